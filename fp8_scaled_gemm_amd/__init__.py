@@ -1,0 +1,211 @@
+"""Python binding of libfp8sg, the MI355X (gfx950) FP8 per-tensor scaled linear
+layer and GradScaler step.
+
+Argument marshalling only: every function forwards torch device tensors as raw
+pointers and sizes to the C ABI declared in include/fp8sg.h (same names, same
+order), on the current torch stream.  All arithmetic runs in the library's HIP
+kernels; torch provides device memory and streams.  There is no fallback: if
+the library is not built, importing it raises.
+"""
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library binds to (one runtime per process)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp8sg.so")
+
+E4M3FN, E5M2 = 0, 1
+OUT_BF16, OUT_F16, OUT_F32 = 0, 1, 2
+SCALE_REC_BYTES = 48
+
+EXPORTS = ("fp8sg_status_string", "fp8sg_version", "fp8_amax", "fp8_quantize", "fp8_gemm",
+           "fp8_scaled_linear_fwd", "fp8_scaled_linear_bwd", "amp_unscale_check",
+           "amp_update_scale")
+
+
+class Fp8sgError(RuntimeError):
+    pass
+
+
+class _Saved(ctypes.Structure):
+    _fields_ = [("x_q", ctypes.c_void_p), ("x_qT", ctypes.c_void_p), ("w_q", ctypes.c_void_p),
+                ("w_qT", ctypes.c_void_p), ("x_sc", ctypes.c_void_p), ("w_sc", ctypes.c_void_p)]
+
+
+class _BwdWs(ctypes.Structure):
+    _fields_ = [("gy_q", ctypes.c_void_p), ("gy_qT", ctypes.c_void_p), ("gy_sc", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libfp8sg.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(or python fp8_scaled_gemm_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, f32, i = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                           ctypes.c_int)
+    L.fp8sg_status_string.argtypes = [i]
+    L.fp8sg_status_string.restype = ctypes.c_char_p
+    L.fp8sg_version.restype = i
+    L.fp8_amax.argtypes = [P, i64, P, P]
+    L.fp8_quantize.argtypes = [P, i64, i64, i, P, P, P, P]
+    L.fp8_gemm.argtypes = [P, i, P, i, P, P, P, i, i64, i64, i64, P]
+    L.fp8_scaled_linear_fwd.argtypes = [P, P, i64, i64, i64, ctypes.POINTER(_Saved), P, i, P]
+    L.fp8_scaled_linear_bwd.argtypes = [P, ctypes.POINTER(_Saved), i64, i64, i64,
+                                        ctypes.POINTER(_BwdWs), P, P, i, P]
+    L.amp_unscale_check.argtypes = [ctypes.POINTER(P), ctypes.POINTER(i64), i32, P, P, P]
+    L.amp_update_scale.argtypes = [P, P, P, f32, f32, i32, P]
+    for name in EXPORTS[2:]:
+        getattr(L, name).restype = i
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().fp8sg_status_string(status).decode()
+        raise Fp8sgError(f"{what}: status {status} ({msg})")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ----------------------------------------------------------------- scale records
+
+class ScaleRec:
+    """A 48-byte device scale record (fp8sg_scale_rec), zero-initialised.
+
+    Fields (after the library has written them): amax, scale32, inv32 (fp32),
+    scale, inv (fp64)."""
+
+    def __init__(self, device="cuda", buf=None):
+        self.buf = buf if buf is not None else torch.zeros(SCALE_REC_BYTES, dtype=torch.uint8,
+                                                          device=device)
+
+    @property
+    def ptr(self):
+        return self.buf.data_ptr()
+
+    def inv_ptr(self):
+        return self.buf.data_ptr() + 24
+
+    def read(self) -> dict:
+        h = self.buf.cpu()
+        f = h[:12].view(torch.float32)
+        u = h[:16].view(torch.int32)
+        d = h[16:32].view(torch.float64)
+        return {"amax": float(f[0]), "scale32": float(f[1]), "inv32": float(f[2]),
+                "amax_bits": int(u[0]) & 0xFFFFFFFF, "scale32_bits": int(u[1]) & 0xFFFFFFFF,
+                "inv32_bits": int(u[2]) & 0xFFFFFFFF, "scale": float(d[0]), "inv": float(d[1]),
+                "_acc": int(u[3]) & 0xFFFFFFFF, "_ticket": int(h[32:36].view(torch.int32)[0])}
+
+
+# ----------------------------------------------------------------- C-ABI calls
+
+def fp8_amax(x: torch.Tensor, rec: ScaleRec, stream=None):
+    """rec.amax = max |x| over a bf16 tensor (any shape, contiguous)."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    _check(lib().fp8_amax(_ptr(x), x.numel(), ctypes.c_void_p(rec.ptr), _stream(stream)),
+           "fp8_amax")
+
+
+def fp8_quantize(x: torch.Tensor, fmt: int, rec: ScaleRec, q: torch.Tensor,
+                 qT: torch.Tensor = None, stream=None):
+    """Scale from rec.amax, then codes q (= x's shape) and optionally qT (transposed)."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    rows, cols = (x.shape[0], x.numel() // max(x.shape[0], 1)) if x.dim() >= 2 else (1, x.numel())
+    assert q.dtype == torch.uint8 and q.numel() == x.numel()
+    if qT is not None:
+        assert qT.dtype == torch.uint8 and qT.numel() == x.numel()
+    _check(lib().fp8_quantize(_ptr(x), rows, cols, fmt, ctypes.c_void_p(rec.ptr), _ptr(q),
+                              _ptr(qT), _stream(stream)), "fp8_quantize")
+
+
+def fp8_gemm(A: torch.Tensor, fa: int, B: torch.Tensor, fb: int, inv_a_ptr: int, inv_b_ptr: int,
+             C: torch.Tensor, out: int, stream=None):
+    """C[M,N] = A[M,K] . B[N,K]^T * fl32(inv_a * inv_b); inv_*_ptr are device double addresses."""
+    M, K = A.shape
+    N, K2 = B.shape
+    assert K == K2 and tuple(C.shape) == (M, N)
+    _check(lib().fp8_gemm(_ptr(A), fa, _ptr(B), fb, ctypes.c_void_p(inv_a_ptr),
+                          ctypes.c_void_p(inv_b_ptr), _ptr(C), out, M, N, K, _stream(stream)),
+           "fp8_gemm")
+
+
+class LinearSaved:
+    """Device buffers the forward pass fills for the backward pass."""
+
+    def __init__(self, M, N, K, device="cuda"):
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.x_q = torch.empty((M, K), **u8)
+        self.x_qT = torch.empty((K, M), **u8)
+        self.w_q = torch.empty((N, K), **u8)
+        self.w_qT = torch.empty((K, N), **u8)
+        self.recs = torch.zeros((2, SCALE_REC_BYTES), **u8)
+        self.x_sc = ScaleRec(buf=self.recs[0])
+        self.w_sc = ScaleRec(buf=self.recs[1])
+
+    def struct(self):
+        return _Saved(self.x_q.data_ptr(), self.x_qT.data_ptr(), self.w_q.data_ptr(),
+                      self.w_qT.data_ptr(), self.x_sc.ptr, self.w_sc.ptr)
+
+
+class LinearBwdWs:
+    def __init__(self, M, N, device="cuda"):
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.gy_q = torch.empty((M, N), **u8)
+        self.gy_qT = torch.empty((N, M), **u8)
+        self.gy_sc = ScaleRec(device=device)
+
+    def struct(self):
+        return _BwdWs(self.gy_q.data_ptr(), self.gy_qT.data_ptr(), self.gy_sc.ptr)
+
+
+def fp8_scaled_linear_fwd(x, w, saved: LinearSaved, y, out: int = OUT_BF16, stream=None):
+    M, K = x.shape
+    N = w.shape[0]
+    s = saved.struct()
+    _check(lib().fp8_scaled_linear_fwd(_ptr(x), _ptr(w), M, N, K, ctypes.byref(s), _ptr(y), out,
+                                       _stream(stream)), "fp8_scaled_linear_fwd")
+
+
+def fp8_scaled_linear_bwd(gy, saved: LinearSaved, ws: LinearBwdWs, gx, gw, out: int = OUT_BF16,
+                          stream=None):
+    M, N = gy.shape
+    K = saved.x_q.shape[1]
+    s = saved.struct()
+    b = ws.struct()
+    _check(lib().fp8_scaled_linear_bwd(_ptr(gy), ctypes.byref(s), M, N, K, ctypes.byref(b),
+                                       _ptr(gx), _ptr(gw), out, _stream(stream)),
+           "fp8_scaled_linear_bwd")
+
+
+def amp_unscale_check(grads, scale: torch.Tensor, found_inf: torch.Tensor, stream=None):
+    """In-place unscale of a list of fp16 gradients and OR of the non-finite flag."""
+    n = len(grads)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[g.data_ptr() for g in grads])
+    numel = (ctypes.c_int64 * max(n, 1))(*[g.numel() for g in grads])
+    for g in grads:
+        assert g.dtype == torch.float16 and g.is_contiguous()
+    _check(lib().amp_unscale_check(ptrs, numel, n, _ptr(scale), _ptr(found_inf),
+                                   _stream(stream)), "amp_unscale_check")
+
+
+def amp_update_scale(scale: torch.Tensor, growth_tracker: torch.Tensor, found_inf: torch.Tensor,
+                     growth_factor=2.0, backoff_factor=0.5, growth_interval=2000, stream=None):
+    _check(lib().amp_update_scale(_ptr(scale), _ptr(growth_tracker), _ptr(found_inf),
+                                  growth_factor, backoff_factor, growth_interval, _stream(stream)),
+           "amp_update_scale")

@@ -1,0 +1,180 @@
+// C-ABI entry points of libfp8sg: argument validation, then kernel launches on
+// the caller's stream.  No device allocation and no host synchronisation.
+//
+// Sources (web pages; cited by title and section):
+//   [FP8-TRAIN]  "FP8训练：量化、自动微分、Torchao" (lzwjava.github.io)
+//   [PT-CH20]    "第20章 量化与混合精度训练" (yangyitao.com, PyTorch book ch. 20)
+#include <stdint.h>
+
+#include "../../include/fp8sg.h"
+#include "launch.hpp"
+
+using namespace fp8sg;
+
+static_assert(sizeof(fp8sg_scale_rec) == 48, "scale record layout");
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool fmt_ok(int f) { return f == FP8SG_E4M3FN || f == FP8SG_E5M2; }
+bool out_ok(int o) { return o == FP8SG_OUT_BF16 || o == FP8SG_OUT_F16 || o == FP8SG_OUT_F32; }
+bool dims16(int64_t v) { return v >= 0 && (v % 16) == 0; }
+bool dims16_pos(int64_t v) { return v > 0 && (v % 16) == 0; }
+fp8sg_status hip_status(hipError_t e) { return e == hipSuccess ? FP8SG_OK : FP8SG_ERR_HIP; }
+hipStream_t S(fp8sg_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+fp8sg_status check_gemm(const void* A, int fa, const void* B, int fb, const void* ia,
+                        const void* ib, const void* C, int out, int64_t M, int64_t N, int64_t K) {
+  if (!A || !B || !ia || !ib || !C) return FP8SG_ERR_NULL;
+  if (!fmt_ok(fa) || !fmt_ok(fb) || !out_ok(out)) return FP8SG_ERR_FORMAT;
+  if (!dims16(M) || !dims16(N) || !dims16(K)) return FP8SG_ERR_SHAPE;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return FP8SG_ERR_ALIGN;
+  return FP8SG_OK;
+}
+
+fp8sg_status check_saved(const fp8_linear_saved* s) {
+  if (!s || !s->x_q || !s->x_qT || !s->w_q || !s->w_qT || !s->x_sc || !s->w_sc) return FP8SG_ERR_NULL;
+  if (!aligned16(s->x_q) || !aligned16(s->x_qT) || !aligned16(s->w_q) || !aligned16(s->w_qT))
+    return FP8SG_ERR_ALIGN;
+  return FP8SG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8sg_status_string(int status) {
+  switch (status) {
+    case FP8SG_OK: return "ok";
+    case FP8SG_ERR_NULL: return "null pointer argument";
+    case FP8SG_ERR_SHAPE: return "invalid size (negative, or not a required multiple of 16)";
+    case FP8SG_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case FP8SG_ERR_FORMAT: return "unknown format or output type";
+    case FP8SG_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int fp8sg_version(void) { return 100; }
+
+fp8sg_status fp8_amax(const uint16_t* x, int64_t n, fp8sg_scale_rec* rec, fp8sg_stream stream) {
+  if (!rec || (n > 0 && !x)) return FP8SG_ERR_NULL;
+  if (n < 0) return FP8SG_ERR_SHAPE;
+  if (!aligned16(x)) return FP8SG_ERR_ALIGN;
+  AmaxArgs a{};
+  a.job[0] = AmaxJob{x, n, rec, 0, amax_blocks_for(n)};
+  a.njobs = 1;
+  return hip_status(launch_amax(a, S(stream)));
+}
+
+fp8sg_status fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, fp8sg_format fmt,
+                          fp8sg_scale_rec* rec, uint8_t* q, uint8_t* qT, fp8sg_stream stream) {
+  if (!rec) return FP8SG_ERR_NULL;
+  if (!fmt_ok(fmt)) return FP8SG_ERR_FORMAT;
+  if (rows < 0 || cols < 0) return FP8SG_ERR_SHAPE;
+  if (rows * cols > 0 && (!x || !q)) return FP8SG_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || (qT && !aligned16(qT))) return FP8SG_ERR_ALIGN;
+  QuantArgs a{};
+  a.job[0] = QuantJob{x, rows, cols, rec, q, qT, 0, 0, 0};
+  a.njobs = 1;
+  return hip_status(launch_quantize(a, fmt, S(stream)));
+}
+
+fp8sg_status fp8_gemm(const uint8_t* A, fp8sg_format fa, const uint8_t* B, fp8sg_format fb,
+                      const double* inv_a, const double* inv_b, void* C, fp8sg_out out,
+                      int64_t M, int64_t N, int64_t Kc, fp8sg_stream stream) {
+  fp8sg_status st = check_gemm(A, fa, B, fb, inv_a, inv_b, C, out, M, N, Kc);
+  if (st != FP8SG_OK) return st;
+  GemmProblem p{A, B, C, inv_a, inv_b, M, N, Kc};
+  return hip_status(launch_gemm(p, fa, fb, out, S(stream)));
+}
+
+// Forward [FP8-TRAIN §4 forward, §6]: one amax launch over x and W, one
+// quantize launch writing codes and transposed copies of both, one GEMM.
+fp8sg_status fp8_scaled_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
+                                   int64_t K, const fp8_linear_saved* saved, void* y,
+                                   fp8sg_out out, fp8sg_stream stream) {
+  if (!x || !w || !y) return FP8SG_ERR_NULL;
+  fp8sg_status st = check_saved(saved);
+  if (st != FP8SG_OK) return st;
+  if (!out_ok(out)) return FP8SG_ERR_FORMAT;
+  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K)) return FP8SG_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return FP8SG_ERR_ALIGN;
+  hipStream_t s = S(stream);
+
+  AmaxArgs am{};
+  am.job[0] = AmaxJob{x, M * K, saved->x_sc, 0, amax_blocks_for(M * K)};
+  am.job[1] = AmaxJob{w, N * K, saved->w_sc, 0, amax_blocks_for(N * K)};
+  am.njobs = 2;
+  hipError_t e = launch_amax(am, s);
+  if (e != hipSuccess) return FP8SG_ERR_HIP;
+
+  QuantArgs qa{};
+  qa.job[0] = QuantJob{x, M, K, saved->x_sc, saved->x_q, saved->x_qT, 0, 0, 0};
+  qa.job[1] = QuantJob{w, N, K, saved->w_sc, saved->w_q, saved->w_qT, 0, 0, 0};
+  qa.njobs = 2;
+  e = launch_quantize(qa, FP8SG_E4M3FN, s);
+  if (e != hipSuccess) return FP8SG_ERR_HIP;
+
+  GemmProblem p{saved->x_q, saved->w_q, y, &saved->x_sc->inv, &saved->w_sc->inv, M, N, K};
+  return hip_status(launch_gemm(p, FP8SG_E4M3FN, FP8SG_E4M3FN, out, s));
+}
+
+// Backward [FP8-TRAIN §4 backward]: gy -> e5m2 codes + transposed copy, then
+// dgrad (gy_q [M,N] x w_qT [K,N]^T) and wgrad (gy_qT [N,M] x x_qT [K,M]^T).
+fp8sg_status fp8_scaled_linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved,
+                                   int64_t M, int64_t N, int64_t K, const fp8_linear_bwd_ws* ws,
+                                   void* gx, void* gw, fp8sg_out out, fp8sg_stream stream) {
+  if (!gy || !ws || !gx || !gw) return FP8SG_ERR_NULL;
+  fp8sg_status st = check_saved(saved);
+  if (st != FP8SG_OK) return st;
+  if (!ws->gy_q || !ws->gy_qT || !ws->gy_sc) return FP8SG_ERR_NULL;
+  if (!out_ok(out)) return FP8SG_ERR_FORMAT;
+  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K)) return FP8SG_ERR_SHAPE;
+  if (!aligned16(gy) || !aligned16(gx) || !aligned16(gw) || !aligned16(ws->gy_q) ||
+      !aligned16(ws->gy_qT))
+    return FP8SG_ERR_ALIGN;
+  hipStream_t s = S(stream);
+
+  AmaxArgs am{};
+  am.job[0] = AmaxJob{gy, M * N, ws->gy_sc, 0, amax_blocks_for(M * N)};
+  am.njobs = 1;
+  hipError_t e = launch_amax(am, s);
+  if (e != hipSuccess) return FP8SG_ERR_HIP;
+
+  QuantArgs qa{};
+  qa.job[0] = QuantJob{gy, M, N, ws->gy_sc, ws->gy_q, ws->gy_qT, 0, 0, 0};
+  qa.njobs = 1;
+  e = launch_quantize(qa, FP8SG_E5M2, s);
+  if (e != hipSuccess) return FP8SG_ERR_HIP;
+
+  GemmProblem dg{ws->gy_q, saved->w_qT, gx, &ws->gy_sc->inv, &saved->w_sc->inv, M, K, N};
+  e = launch_gemm(dg, FP8SG_E5M2, FP8SG_E4M3FN, out, s);
+  if (e != hipSuccess) return FP8SG_ERR_HIP;
+  GemmProblem wg{ws->gy_qT, saved->x_qT, gw, &ws->gy_sc->inv, &saved->x_sc->inv, N, K, M};
+  return hip_status(launch_gemm(wg, FP8SG_E5M2, FP8SG_E4M3FN, out, s));
+}
+
+fp8sg_status amp_unscale_check(uint16_t* const* grads, const int64_t* numel, int32_t ntensors,
+                               const float* scale, int32_t* found_inf, fp8sg_stream stream) {
+  if (!scale || !found_inf) return FP8SG_ERR_NULL;
+  if (ntensors < 0 || ntensors > 8192) return FP8SG_ERR_SHAPE;
+  if (ntensors > 0 && (!grads || !numel)) return FP8SG_ERR_NULL;
+  for (int32_t i = 0; i < ntensors; ++i) {
+    if (numel[i] < 0) return FP8SG_ERR_SHAPE;
+    if (numel[i] > 0 && !grads[i]) return FP8SG_ERR_NULL;
+    if (numel[i] > 0 && !aligned16(grads[i])) return FP8SG_ERR_ALIGN;
+  }
+  return hip_status(launch_unscale_check(grads, numel, ntensors, scale, found_inf, S(stream)));
+}
+
+fp8sg_status amp_update_scale(float* scale, int32_t* growth_tracker, int32_t* found_inf,
+                              float growth_factor, float backoff_factor,
+                              int32_t growth_interval, fp8sg_stream stream) {
+  if (!scale || !growth_tracker || !found_inf) return FP8SG_ERR_NULL;
+  if (growth_interval < 1) return FP8SG_ERR_SHAPE;
+  return hip_status(launch_update_scale(scale, growth_tracker, found_inf, growth_factor,
+                                        backoff_factor, growth_interval, S(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Device-side helpers shared by the fp8sg kernels (gfx950 / CDNA4).
+//
+// Sources (web pages; cited by title and section):
+//   [FP8-TRAIN]  "FP8训练：量化、自动微分、Torchao" (lzwjava.github.io)
+//   [PT-CH20]    "第20章 量化与混合精度训练" (yangyitao.com, PyTorch book ch. 20)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp8sg.h"
+
+namespace fp8sg {
+
+constexpr int kWave = 64;
+
+// Largest finite values of the two FP8 formats [FP8-TRAIN §2, §3 table].
+constexpr float kE4M3Max = 448.0f;
+constexpr float kE5M2Max = 57344.0f;
+// Lower clamp of amax in the scale division; the page names EPS without a value.
+constexpr double kScaleEps = 1e-12;
+
+__device__ __forceinline__ float fmt_max(int fmt) { return fmt == FP8SG_E4M3FN ? kE4M3Max : kE5M2Max; }
+
+// bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Per-tensor scale from the amax word [FP8-TRAIN §2]: s = fp8_max / max(amax, EPS)
+// as an IEEE fp64 division (NaN amax keeps NaN), inverse = 1/s in fp64, both also
+// rounded to fp32.
+struct ScaleVals {
+  double s, inv;
+  float s32, inv32;
+};
+
+__device__ __forceinline__ ScaleVals scale_from_amax(float amax, int fmt) {
+  ScaleVals v;
+  double d = (double)amax;
+  if (d != d) {
+    v.s = d;
+  } else {
+    if (d < kScaleEps) d = kScaleEps;
+    v.s = (double)fmt_max(fmt) / d;
+  }
+  v.inv = 1.0 / v.s;
+  v.s32 = (float)v.s;
+  v.inv32 = (float)v.inv;
+  return v;
+}
+
+// clamp(y, -max, max) that keeps NaN (v_min/v_max return the non-NaN operand).
+__device__ __forceinline__ float clamp_keep_nan(float y, float m) {
+  float c = fminf(fmaxf(y, -m), m);
+  return (y != y) ? y : c;
+}
+
+// Four already-clamped fp32 values -> four FP8 codes (byte i = value i), using
+// gfx950's OCP converts, which round to nearest even.
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  int r;
+  if constexpr (FMT == FP8SG_E4M3FN) {
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  } else {
+    r = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, r, true);
+  }
+  return (uint32_t)r;
+}
+
+// Quantize 8 bf16 values (one 16-byte load) to 8 codes (two dwords)
+// [FP8-TRAIN §2: fl32(x * scale32), clamp, cast].
+template <int FMT>
+__device__ __forceinline__ uint2 quant8(uint4 v, float s32) {
+  constexpr float m = FMT == FP8SG_E4M3FN ? kE4M3Max : kE5M2Max;
+  float f0 = clamp_keep_nan(bf16_lo(v.x) * s32, m), f1 = clamp_keep_nan(bf16_hi(v.x) * s32, m);
+  float f2 = clamp_keep_nan(bf16_lo(v.y) * s32, m), f3 = clamp_keep_nan(bf16_hi(v.y) * s32, m);
+  float f4 = clamp_keep_nan(bf16_lo(v.z) * s32, m), f5 = clamp_keep_nan(bf16_hi(v.z) * s32, m);
+  float f6 = clamp_keep_nan(bf16_lo(v.w) * s32, m), f7 = clamp_keep_nan(bf16_hi(v.w) * s32, m);
+  return make_uint2(cvt4<FMT>(f0, f1, f2, f3), cvt4<FMT>(f4, f5, f6, f7));
+}
+
+template <int FMT>
+__device__ __forceinline__ uint8_t quant1(uint16_t b, float s32) {
+  constexpr float m = FMT == FP8SG_E4M3FN ? kE4M3Max : kE5M2Max;
+  float f = clamp_keep_nan(bf16_lo(b) * s32, m);
+  return (uint8_t)(cvt4<FMT>(f, 0.f, 0.f, 0.f) & 0xFFu);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+}  // namespace fp8sg

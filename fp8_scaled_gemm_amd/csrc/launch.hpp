@@ -1,0 +1,70 @@
+// Host-side launch interface between the C-ABI layer (api.hip) and the kernel
+// translation units.  Kernel arguments travel by value (no device tables), so a
+// launch needs no allocation and no host-to-device copy.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp8sg.h"
+
+namespace fp8sg {
+
+// ---- amax (amax.hip)
+constexpr int kMaxAmaxJobs = 4;
+constexpr int kAmaxMaxBlocksPerJob = 2048;
+
+struct AmaxJob {
+  const uint16_t* x;
+  int64_t n;
+  fp8sg_scale_rec* rec;
+  int32_t block0;   // first block of this job (filled by launch_amax)
+  int32_t nblocks;  // blocks given to this job (amax_blocks_for)
+};
+struct AmaxArgs {
+  AmaxJob job[kMaxAmaxJobs];
+  int32_t njobs;
+};
+int amax_blocks_for(int64_t n);
+hipError_t launch_amax(AmaxArgs args, hipStream_t stream);
+
+// ---- quantize (quantize.hip)
+constexpr int kMaxQuantJobs = 4;
+
+struct QuantJob {
+  const uint16_t* x;
+  int64_t rows, cols;
+  fp8sg_scale_rec* rec;
+  uint8_t* q;
+  uint8_t* qT;      // may be null
+  int32_t block0;   // filled by the launcher
+  int32_t nblocks;
+  int32_t tiles_c;  // tiled path: tiles along cols
+};
+struct QuantArgs {
+  QuantJob job[kMaxQuantJobs];
+  int32_t njobs;
+};
+// All jobs of one launch share the format.  Chooses the tiled kernel (rows and
+// cols multiples of 16 with a transposed copy), the flat kernel (no transposed
+// copy) or the per-element kernel (a transposed copy of an odd shape).
+hipError_t launch_quantize(QuantArgs args, int fmt, hipStream_t stream);
+
+// ---- GEMM (gemm.hip)
+struct GemmProblem {
+  const uint8_t* A;
+  const uint8_t* B;
+  void* C;
+  const double* inv_a;
+  const double* inv_b;
+  int64_t M, N, K;
+};
+hipError_t launch_gemm(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);
+
+// ---- GradScaler (amp.hip)
+hipError_t launch_unscale_check(uint16_t* const* grads, const int64_t* numel, int32_t ntensors,
+                                const float* scale, int32_t* found_inf, hipStream_t stream);
+hipError_t launch_update_scale(float* scale, int32_t* tracker, int32_t* found_inf, float growth,
+                               float backoff, int32_t interval, hipStream_t stream);
+
+}  // namespace fp8sg

@@ -1,0 +1,229 @@
+// Scale + quantize-cast of bf16 tensors to OCP FP8, fused with the transposed
+// copy [FP8-TRAIN §2: scale = fp8_max / amax in fp64, x * scale, clamp, cast;
+// §3: e4m3 for activations and weights, e5m2 for gradients; §4: the backward
+// GEMMs need each operand contiguous along its contraction dimension, which
+// for x, W and gy means a transposed FP8 copy].
+//
+// Every block recomputes the scale from the amax word (two fp64 divisions, a
+// few hundred cycles), so the amax -> scale step needs no launch of its own;
+// the first block of each job also writes the record's scale fields.
+//
+// Tiled path: one 128 x 128 tile per 256-thread block.  The tile is read once
+// with 16-byte loads (8 in flight per thread), quantized in registers, stored
+// row-major with coalesced 8-byte stores, staged in LDS (16 KB, XOR-swizzled
+// so both the row-wise writes and the column-wise reads spread over the
+// banks), transposed in 4x4-byte blocks with byte permutes, and stored to qT
+// with 16-byte stores, 8 lanes per 128-byte row segment.  HBM traffic is the
+// algorithmic 2 B read + 1 B + 1 B written per element.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace fp8sg {
+
+constexpr int kQThreads = 256;
+constexpr int kQTile = 128;
+
+__device__ __forceinline__ const QuantJob& pick_job(const QuantArgs& a, int& lb) {
+  int j = 0;
+#pragma unroll
+  for (int t = 1; t < kMaxQuantJobs; ++t)
+    if (t < a.njobs && (int)blockIdx.x >= a.job[t].block0) j = t;
+  lb = (int)blockIdx.x - a.job[j].block0;
+  return a.job[j];
+}
+
+__device__ __forceinline__ void write_scale_fields(fp8sg_scale_rec* rec, const ScaleVals& v) {
+  rec->scale = v.s;
+  rec->inv = v.inv;
+  rec->scale32 = v.s32;
+  rec->inv32 = v.inv32;
+}
+
+// LDS tile: 128 rows x 32 dwords; dword column x of row r lives at x ^ swz(r).
+__device__ __forceinline__ int swz(int r) { return ((r >> 4) & 3) << 3; }
+
+// 4x4 byte transpose: out[j] byte i = in[i] byte j.
+__device__ __forceinline__ void tr4x4(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3,
+                                      uint32_t& o0, uint32_t& o1, uint32_t& o2, uint32_t& o3) {
+  // v_perm_b32(hi, lo, sel): selector bytes 0-3 pick lo's bytes, 4-7 hi's bytes
+  uint32_t e0 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);  // d0.b0 d1.b0 d0.b1 d1.b1
+  uint32_t e1 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);  // d0.b2 d1.b2 d0.b3 d1.b3
+  uint32_t f0 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+  uint32_t f1 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+  o0 = __builtin_amdgcn_perm(f0, e0, 0x05040100u);  // d0.b0 d1.b0 d2.b0 d3.b0
+  o1 = __builtin_amdgcn_perm(f0, e0, 0x07060302u);  // d0.b1 d1.b1 d2.b1 d3.b1
+  o2 = __builtin_amdgcn_perm(f1, e1, 0x05040100u);
+  o3 = __builtin_amdgcn_perm(f1, e1, 0x07060302u);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
+  int lb;
+  const QuantJob& job = pick_job(args, lb);
+  const int tid = threadIdx.x;
+  const ScaleVals sv = scale_from_amax(job.rec->amax, FMT);
+  if (lb == 0 && tid == 0) write_scale_fields(job.rec, sv);
+
+  const int64_t rows = job.rows, cols = job.cols;
+  const int64_t r_tile = (int64_t)(lb / job.tiles_c) * kQTile;
+  const int64_t c_tile = (int64_t)(lb % job.tiles_c) * kQTile;
+
+  __shared__ uint32_t lds[kQTile * 32];
+
+  // phase 1: 16 lanes per row (8 elements each), 16 rows per pass, 8 passes
+  const int c8 = tid & 15;
+  const int r0 = tid >> 4;
+  const int64_t gc = c_tile + 8 * c8;
+  const bool col_ok = gc < cols;  // cols % 16 == 0: a group of 8 is all in or all out
+  uint4 v[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int64_t gr = r_tile + r0 + 16 * p;
+    v[p] = (col_ok && gr < rows) ? *reinterpret_cast<const uint4*>(job.x + gr * cols + gc)
+                                 : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = r0 + 16 * p;
+    const int64_t gr = r_tile + r;
+    const uint2 c = quant8<FMT>(v[p], sv.s32);
+    if (col_ok && gr < rows) *reinterpret_cast<uint2*>(job.q + gr * cols + gc) = c;
+    *reinterpret_cast<uint2*>(&lds[r * 32 + ((2 * c8) ^ swz(r))]) = c;
+  }
+  __syncthreads();
+
+  // phase 2: lane owns tile columns 4cq..4cq+3 and tile rows 16rq..16rq+15
+  const int cq = tid >> 3;
+  const int rq = tid & 7;
+  uint32_t d[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 16 * rq + i;
+    d[i] = lds[r * 32 + (cq ^ swz(r))];
+  }
+  uint32_t o[4][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    tr4x4(d[4 * b], d[4 * b + 1], d[4 * b + 2], d[4 * b + 3], o[0][b], o[1][b], o[2][b], o[3][b]);
+  const int64_t tr0 = r_tile + 16 * rq;
+  const int64_t tc0 = c_tile + 4 * cq;
+  if (tr0 < rows && tc0 < cols) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<uint4*>(job.qT + (tc0 + j) * rows + tr0) =
+          make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]);
+  }
+}
+
+// Row-major codes only, any element count: grid-stride over 16-byte loads.
+constexpr int kFlatUnroll = 4;
+
+template <int FMT>
+__global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
+  int lb;
+  const QuantJob& job = pick_job(args, lb);
+  const int tid = threadIdx.x;
+  const ScaleVals sv = scale_from_amax(job.rec->amax, FMT);
+  if (lb == 0 && tid == 0) write_scale_fields(job.rec, sv);
+
+  const int64_t n = job.rows * job.cols;
+  const int64_t nvec = n >> 3;
+  const uint4* xv = reinterpret_cast<const uint4*>(job.x);
+  uint2* qv = reinterpret_cast<uint2*>(job.q);
+  const int64_t step = (int64_t)job.nblocks * kQThreads * kFlatUnroll;
+  for (int64_t base = (int64_t)lb * kQThreads * kFlatUnroll + tid; base < nvec; base += step) {
+    uint4 v[kFlatUnroll];
+#pragma unroll
+    for (int u = 0; u < kFlatUnroll; ++u) {
+      const int64_t k = base + (int64_t)u * kQThreads;
+      v[u] = k < nvec ? xv[k] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kFlatUnroll; ++u) {
+      const int64_t k = base + (int64_t)u * kQThreads;
+      if (k < nvec) qv[k] = quant8<FMT>(v[u], sv.s32);
+    }
+  }
+  if (lb == 0 && tid < (int)(n & 7)) {
+    const int64_t i = (nvec << 3) + tid;
+    job.q[i] = quant1<FMT>(job.x[i], sv.s32);
+  }
+}
+
+// Transposed copy of a shape the tiled kernel does not take: one thread per element.
+template <int FMT>
+__global__ __launch_bounds__(kQThreads) void k_quant_elem(QuantArgs args) {
+  int lb;
+  const QuantJob& job = pick_job(args, lb);
+  const int tid = threadIdx.x;
+  const ScaleVals sv = scale_from_amax(job.rec->amax, FMT);
+  if (lb == 0 && tid == 0) write_scale_fields(job.rec, sv);
+  const int64_t n = job.rows * job.cols;
+  for (int64_t i = (int64_t)lb * kQThreads + tid; i < n; i += (int64_t)job.nblocks * kQThreads) {
+    const uint8_t c = quant1<FMT>(job.x[i], sv.s32);
+    job.q[i] = c;
+    const int64_t r = i / job.cols, cc = i - r * job.cols;
+    job.qT[cc * job.rows + r] = c;
+  }
+}
+
+enum QuantPath { kPathTiled, kPathFlat, kPathElem };
+
+static QuantPath path_of(const QuantJob& j) {
+  if (!j.qT) return kPathFlat;
+  if (j.rows % 16 == 0 && j.cols % 16 == 0) return kPathTiled;
+  return kPathElem;
+}
+
+static int blocks_of(QuantJob& j, QuantPath p) {
+  const int64_t n = j.rows * j.cols;
+  int64_t b;
+  if (p == kPathTiled) {
+    const int64_t tr = (j.rows + kQTile - 1) / kQTile, tc = (j.cols + kQTile - 1) / kQTile;
+    j.tiles_c = (int32_t)(tc > 0 ? tc : 1);
+    b = tr * tc;
+  } else if (p == kPathFlat) {
+    const int64_t per = (int64_t)kQThreads * kFlatUnroll;
+    b = ((n >> 3) + per - 1) / per;
+    if (b > 4096) b = 4096;
+  } else {
+    b = (n + kQThreads - 1) / kQThreads;
+    if (b > 4096) b = 4096;
+  }
+  return (int)(b < 1 ? 1 : b);  // one block at least: it writes the scale fields
+}
+
+template <int FMT>
+static hipError_t launch_fmt(QuantArgs a, hipStream_t stream) {
+  // jobs of one launch must take the same path; otherwise split into launches
+  for (int j0 = 0; j0 < a.njobs;) {
+    const QuantPath p = path_of(a.job[j0]);
+    QuantArgs sub{};
+    int total = 0;
+    int j = j0;
+    for (; j < a.njobs && path_of(a.job[j]) == p; ++j) {
+      QuantJob jb = a.job[j];
+      jb.nblocks = blocks_of(jb, p);
+      jb.block0 = total;
+      total += jb.nblocks;
+      sub.job[sub.njobs++] = jb;
+    }
+    if (p == kPathTiled)
+      hipLaunchKernelGGL(k_quant_tiled<FMT>, dim3(total), dim3(kQThreads), 0, stream, sub);
+    else if (p == kPathFlat)
+      hipLaunchKernelGGL(k_quant_flat<FMT>, dim3(total), dim3(kQThreads), 0, stream, sub);
+    else
+      hipLaunchKernelGGL(k_quant_elem<FMT>, dim3(total), dim3(kQThreads), 0, stream, sub);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    j0 = j;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_quantize(QuantArgs args, int fmt, hipStream_t stream) {
+  return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN>(args, stream)
+                             : launch_fmt<FP8SG_E5M2>(args, stream);
+}
+
+}  // namespace fp8sg

@@ -1,0 +1,214 @@
+/*
+ * fp8sg -- FP8 per-tensor dynamically scaled linear layer and GradScaler step
+ * for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operations follow these web pages (cited by title and section):
+ *   [FP8-TRAIN]  "FP8训练：量化、自动微分、Torchao" (lzwjava.github.io)
+ *   [PT-CH20]    "第20章 量化与混合精度训练" (yangyitao.com, PyTorch book ch. 20)
+ *   [AMP-MP]     "从 AMP 到 Mixed Precision" (111qqz.com)
+ *   [AMP-NOTES]  "AMP：Automatic Mixed Precision 技术笔记" (luna-shi.github.io)
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor and state pointers are DEVICE pointers into memory the caller
+ *    owns; the library allocates no device memory on any of these calls.
+ *    Host pointers appear only where a parameter says "host".
+ *  - Element types are passed as their bit patterns: bf16 and fp16 as
+ *    uint16_t, FP8 codes as uint8_t.  Matrices are row-major and contiguous.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    validates its arguments and enqueues kernels on `stream`; it never
+ *    synchronises the host.  Results are ready when the stream's work is.
+ *  - Errors: argument errors are reported before anything is enqueued
+ *    (FP8SG_ERR_NULL, _SHAPE, _ALIGN, _FORMAT).  FP8SG_ERR_HIP means a launch
+ *    failed; kernels already enqueued by the call may have run.  No exception
+ *    crosses the ABI, and there is no global error state besides the return.
+ *  - Device pointers to tensors must be 16-byte aligned (FP8SG_ERR_ALIGN).
+ *  - Calls that share an output or state buffer must not overlap in time.
+ */
+#ifndef FP8SG_H
+#define FP8SG_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define FP8SG_API __attribute__((visibility("default")))
+#else
+#define FP8SG_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8SG_E4M3FN = 0, /* 1|4|3, bias 7, no inf, largest 448 [FP8-TRAIN §2, §3]  */
+  FP8SG_E5M2 = 1    /* 1|5|2, bias 15, IEEE-style inf/NaN, largest 57344 [§3] */
+} fp8sg_format;
+
+typedef enum {
+  FP8SG_OUT_BF16 = 0, /* bf16, round-to-nearest-even (the layer's dtype)  */
+  FP8SG_OUT_F16 = 1,  /* fp16, round-to-nearest-even (fp16 AMP gradients) */
+  FP8SG_OUT_F32 = 2   /* fp32, unrounded epilogue value                   */
+} fp8sg_out;
+
+typedef enum {
+  FP8SG_OK = 0,
+  FP8SG_ERR_NULL = 1,   /* a required pointer is NULL                      */
+  FP8SG_ERR_SHAPE = 2,  /* a size is negative or breaks a multiple-of rule */
+  FP8SG_ERR_ALIGN = 3,  /* a tensor pointer is not 16-byte aligned         */
+  FP8SG_ERR_FORMAT = 4, /* unknown fp8sg_format / fp8sg_out value          */
+  FP8SG_ERR_HIP = 5     /* a HIP launch or runtime call failed             */
+} fp8sg_status;
+
+typedef void* fp8sg_stream; /* hipStream_t */
+
+/*
+ * Per-tensor scale record, 48 bytes of device memory owned by the caller
+ * [FP8-TRAIN §2]: the tensor's absolute maximum, the fp64 scale
+ * fp8_max / max(amax, EPS) with EPS = 1e-12, its fp64 reciprocal (the inverse
+ * the GEMM dequantises with) and both rounded to fp32 (the quantizer
+ * multiplies by scale32).  The two underscore words are the library's own
+ * reduction state: ZERO THE RECORD ONCE before its first use (the library
+ * leaves them zero after every call).
+ */
+typedef struct fp8sg_scale_rec {
+  float amax;        /* max_i |x_i| as fp32; canonical NaN 0x7FC00000 if any NaN */
+  float scale32;     /* (float)scale                                             */
+  float inv32;       /* (float)inv                                               */
+  uint32_t _acc;     /* library-internal, zero between calls                     */
+  double scale;      /* fp8_max / max(amax, EPS), IEEE fp64 division             */
+  double inv;        /* 1.0 / scale, IEEE fp64 division                          */
+  uint32_t _ticket;  /* library-internal, zero between calls                     */
+  uint32_t _pad[3];
+} fp8sg_scale_rec;
+
+/* Human-readable name of a status code (static storage). */
+FP8SG_API const char* fp8sg_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+FP8SG_API int fp8sg_version(void);
+
+/*
+ * amax of a bf16 tensor [FP8-TRAIN §2: x.float().abs().max()].
+ *   x:   n bf16 values (device, 16-byte aligned; may be NULL when n == 0);
+ *        n >= 0, any n.
+ *   rec: scale record (device); writes rec->amax only.  n == 0 gives +0.
+ * A NaN anywhere gives the canonical NaN; +-inf gives +inf.
+ */
+FP8SG_API fp8sg_status fp8_amax(const uint16_t* x, int64_t n, fp8sg_scale_rec* rec, fp8sg_stream stream);
+
+/*
+ * Scale and quantize-cast of a bf16 matrix [FP8-TRAIN §2 (scale in fp64,
+ * x*scale, clamp to +-fp8_max, cast), §3 (e4m3 for activations and weights,
+ * e5m2 for gradients), §4 (the transposed copy the backward GEMMs need)].
+ *   x:    rows x cols bf16, row-major (device, 16-byte aligned).
+ *   fmt:  FP8SG_E4M3FN or FP8SG_E5M2.
+ *   rec:  scale record whose amax was written by fp8_amax on the same
+ *         tensor; this call writes scale, inv, scale32 and inv32.
+ *   q:    rows x cols codes, row-major (device, 16-byte aligned).
+ *   qT:   cols x rows codes = transpose of q (device, 16-byte aligned), or
+ *         NULL to skip the transposed copy.
+ * Each code is enc(clamp(fl32(x * scale32), -max, max)) rounded to nearest
+ * even; NaN inputs give a NaN code.  rows, cols >= 0 (x, q, qT may be NULL
+ * when rows * cols == 0; the record's scale fields are still written).  With qT, rows and cols
+ * that are multiples of 16 take the tiled fast path; other shapes are
+ * handled by a plain per-element kernel.
+ */
+FP8SG_API fp8sg_status fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, fp8sg_format fmt,
+                          fp8sg_scale_rec* rec, uint8_t* q, uint8_t* qT, fp8sg_stream stream);
+
+/*
+ * Scaled FP8 GEMM [FP8-TRAIN §2, §4; AMP-MP "不要忘记 Accumulator Precision"]:
+ *   C[M,N] = out( (sum_k dec(A[m,k]) * dec(B[n,k])) * fl32(inv_a * inv_b) )
+ * with the sum accumulated in fp32 (any order) and the product of the two
+ * fp64 inverse scales rounded once to fp32.
+ *   A:  M x Kc codes of format fa, row-major (contiguous along Kc).
+ *   B:  N x Kc codes of format fb, row-major (contiguous along Kc).
+ *   inv_a, inv_b: device doubles (e.g. &rec->inv).
+ *   C:  M x N of type `out`, row-major.
+ *   M, N, Kc >= 0 and multiples of 16 (FP8SG_ERR_SHAPE otherwise).  Kc == 0
+ *   gives C = 0 * alpha.
+ */
+FP8SG_API fp8sg_status fp8_gemm(const uint8_t* A, fp8sg_format fa, const uint8_t* B, fp8sg_format fb,
+                      const double* inv_a, const double* inv_b, void* C, fp8sg_out out,
+                      int64_t M, int64_t N, int64_t Kc, fp8sg_stream stream);
+
+/*
+ * What the forward pass saves for the backward pass [FP8-TRAIN §6: the
+ * quantized FP8 tensors and their inverse scales, not the bf16 inputs].
+ * All pointers are caller-owned device buffers.
+ */
+typedef struct fp8_linear_saved {
+  uint8_t* x_q;         /* [M,K] e4m3 codes of x                */
+  uint8_t* x_qT;        /* [K,M] transposed copy                */
+  uint8_t* w_q;         /* [N,K] e4m3 codes of W                */
+  uint8_t* w_qT;        /* [K,N] transposed copy                */
+  fp8sg_scale_rec* x_sc;
+  fp8sg_scale_rec* w_sc;
+} fp8_linear_saved;
+
+/* Backward workspace: the quantized gradient and its scale record. */
+typedef struct fp8_linear_bwd_ws {
+  uint8_t* gy_q;        /* [M,N] e5m2 codes of gy               */
+  uint8_t* gy_qT;       /* [N,M] transposed copy                */
+  fp8sg_scale_rec* gy_sc;
+} fp8_linear_bwd_ws;
+
+/*
+ * Forward of the FP8 linear layer y = x @ W^T [FP8-TRAIN §4 forward, §6]:
+ * amax of x and W, fp64 scales, e4m3 quantize-cast with transposed copies,
+ * then the scaled GEMM.
+ *   x: [M,K] bf16, w: [N,K] bf16 (nn.Linear's [out,in]); y: [M,N] of type
+ *   `out` (FP8SG_OUT_BF16 normally).  M, N, K > 0, multiples of 16.
+ */
+FP8SG_API fp8sg_status fp8_scaled_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
+                                   int64_t K, const fp8_linear_saved* saved, void* y,
+                                   fp8sg_out out, fp8sg_stream stream);
+
+/*
+ * Backward of the FP8 linear layer [FP8-TRAIN §4 backward]: gy quantized to
+ * e5m2 (with its transposed copy), then
+ *   dgrad gx[M,K] = gy @ W     from gy_q [M,N] and the saved w_qT [K,N],
+ *   wgrad gW[N,K] = gy^T @ x   from gy_qT [N,M] and the saved x_qT [K,M],
+ * each dequantised by the product of its two inverse scales.
+ *   gy: [M,N] bf16; gx, gw of type `out` (FP8SG_OUT_F16 feeds fp16 AMP).
+ *   `saved` must come from fp8_scaled_linear_fwd with the same M, N, K.
+ */
+FP8SG_API fp8sg_status fp8_scaled_linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved,
+                                   int64_t M, int64_t N, int64_t K, const fp8_linear_bwd_ws* ws,
+                                   void* gx, void* gw, fp8sg_out out, fp8sg_stream stream);
+
+/*
+ * GradScaler unscale + non-finite check over a list of fp16 gradients
+ * [PT-CH20 §20.2.2: unscale the gradients, then check for inf/NaN;
+ *  AMP-NOTES §4 steps 3-4].  In place, for every element:
+ *   g <- fp16_RNE( fl32(g) * fl32(1.0f / *scale) )
+ * and *found_inf is set to 1 if any stored result is inf or NaN (it is never
+ * cleared here: the flag is OR-accumulated over calls).
+ *   grads:  HOST array of ntensors device pointers (each 16-byte aligned).
+ *   numel:  HOST array of ntensors element counts (>= 0, any value).
+ *   scale:  device float, the current loss scale.
+ *   found_inf: device int32.
+ * Up to 8192 tensors per call (FP8SG_ERR_SHAPE beyond).
+ */
+FP8SG_API fp8sg_status amp_unscale_check(uint16_t* const* grads, const int64_t* numel, int32_t ntensors,
+                               const float* scale, int32_t* found_inf, fp8sg_stream stream);
+
+/*
+ * GradScaler.update() [PT-CH20 §20.5.33], on the device:
+ *   if *found_inf: *scale *= backoff_factor; *growth_tracker = 0
+ *   else: ++*growth_tracker; if it reaches growth_interval:
+ *         *scale *= growth_factor; *growth_tracker = 0
+ * then *found_inf is reset to 0, ready for the next step's amp_unscale_check
+ * (the optimizer's skip decision must read it before this call).
+ *   scale: device float; growth_tracker, found_inf: device int32.
+ *   growth_interval >= 1 (FP8SG_ERR_SHAPE otherwise).
+ */
+FP8SG_API fp8sg_status amp_update_scale(float* scale, int32_t* growth_tracker, int32_t* found_inf,
+                              float growth_factor, float backoff_factor,
+                              int32_t growth_interval, fp8sg_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8SG_H */

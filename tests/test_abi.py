@@ -1,0 +1,119 @@
+"""The C-ABI library loads on a machine without a GPU, exports every entry point
+include/fp8sg.h declares, and rejects bad arguments before enqueuing anything.
+
+Only validation paths run here (they return before any HIP call); compute calls
+need a GPU and live in the gpu-marked tests.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_scaled_gemm_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8sg.h")
+
+OK, ENULL, ESHAPE, EALIGN, EFORMAT = 0, 1, 2, 3, 4
+A16 = 0x10000  # fake, never dereferenced: validation fails before any use
+A16B = 0x20000
+MIS = 0x10008  # not 16-byte aligned
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"FP8SG_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    assert syms == sorted(F.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = F.lib()
+    for s in declared_symbols():
+        assert hasattr(L, s), s
+    assert F.lib().fp8sg_version() >= 100
+    for code in range(6):
+        assert F.lib().fp8sg_status_string(code)
+
+
+def test_scale_record_layout_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct fp8sg_scale_rec \{(.*?)\} fp8sg_scale_rec;", text, re.S).group(1)
+    fields = re.findall(r"^\s*(float|double|uint32_t)\s+(\w+)(\[\d+\])?;", body, re.M)
+
+    class Rec(ctypes.Structure):
+        _fields_ = [(n, {"float": ctypes.c_float, "double": ctypes.c_double,
+                         "uint32_t": ctypes.c_uint32}[t] * (int(a[1:-1]) if a else 1))
+                    for t, n, a in fields]
+    assert ctypes.sizeof(Rec) == F.SCALE_REC_BYTES == 48
+    assert Rec.inv.offset == 24  # the binding hands &rec->inv to fp8_gemm
+
+
+def P(v):
+    return ctypes.c_void_p(v)
+
+
+def test_gemm_validation():
+    L = F.lib()
+    g = L.fp8_gemm
+    args = [P(A16), 0, P(A16B), 0, P(A16), P(A16), P(A16B), 0, 16, 16, 16, P(0)]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return g(*a)
+
+    assert call(a0=P(0)) == ENULL
+    assert call(a4=P(0)) == ENULL
+    assert call(a1=7) == EFORMAT
+    assert call(a7=9) == EFORMAT
+    assert call(a8=24) == ESHAPE
+    assert call(a10=8) == ESHAPE
+    assert call(a9=-16) == ESHAPE
+    assert call(a0=P(MIS)) == EALIGN
+    assert call(a6=P(MIS)) == EALIGN
+
+
+def test_linear_and_quant_validation():
+    L = F.lib()
+    s = F._Saved(A16, A16, A16, A16, A16, A16)
+    assert L.fp8_scaled_linear_fwd(P(A16), P(A16), 16, 16, 16, None, P(A16), 0, P(0)) == ENULL
+    assert L.fp8_scaled_linear_fwd(P(A16), P(A16), 16, 15, 16, ctypes.byref(s), P(A16), 0, P(0)) == ESHAPE
+    assert L.fp8_scaled_linear_fwd(P(A16), P(A16), 0, 16, 16, ctypes.byref(s), P(A16), 0, P(0)) == ESHAPE
+    assert L.fp8_scaled_linear_fwd(P(MIS), P(A16), 16, 16, 16, ctypes.byref(s), P(A16), 0, P(0)) == EALIGN
+    assert L.fp8_scaled_linear_fwd(P(A16), P(A16), 16, 16, 16, ctypes.byref(s), P(A16), 5, P(0)) == EFORMAT
+    ws = F._BwdWs(A16, A16, 0)
+    assert L.fp8_scaled_linear_bwd(P(A16), ctypes.byref(s), 16, 16, 16, ctypes.byref(ws), P(A16),
+                                   P(A16), 0, P(0)) == ENULL
+    assert L.fp8_quantize(P(A16), 4, 4, 3, P(A16), P(A16), P(0), P(0)) == EFORMAT
+    assert L.fp8_quantize(P(A16), -1, 4, 0, P(A16), P(A16), P(0), P(0)) == ESHAPE
+    assert L.fp8_quantize(P(A16), 4, 4, 0, P(A16), P(A16), P(MIS), P(0)) == EALIGN
+    assert L.fp8_amax(P(0), 4, P(A16), P(0)) == ENULL
+    assert L.fp8_amax(P(A16), -4, P(A16), P(0)) == ESHAPE
+    assert L.fp8_amax(P(MIS), 4, P(A16), P(0)) == EALIGN
+
+
+def test_amp_validation():
+    L = F.lib()
+    ptrs = (ctypes.c_void_p * 2)(A16, MIS)
+    numel = (ctypes.c_int64 * 2)(8, 8)
+    assert L.amp_unscale_check(ptrs, numel, 2, P(A16), P(A16), P(0)) == EALIGN
+    numel[1] = -1
+    assert L.amp_unscale_check(ptrs, numel, 2, P(A16), P(A16), P(0)) == ESHAPE
+    assert L.amp_unscale_check(ptrs, numel, 2, P(0), P(A16), P(0)) == ENULL
+    assert L.amp_unscale_check(ptrs, numel, 9000, P(A16), P(A16), P(0)) == ESHAPE
+    assert L.amp_update_scale(P(A16), P(A16), P(A16), 2.0, 0.5, 0, P(0)) == ESHAPE
+    assert L.amp_update_scale(P(0), P(A16), P(A16), 2.0, 0.5, 10, P(0)) == ENULL
+
+
+def test_binding_refuses_a_missing_library(monkeypatch, tmp_path):
+    # no fallback path: without the built library the binding raises
+    monkeypatch.setattr(F, "_lib", None)
+    monkeypatch.setattr(F, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        F.lib()
