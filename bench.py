@@ -1,0 +1,283 @@
+"""Benchmark of the FP8 per-tensor scaled linear layer + GradScaler step on one
+MI355X.
+
+One step = the whole hot path on the square 4096 x 4096 x 4096 layer (bf16
+x ~N(0,1) with 0.1% outliers x50, W ~N(0,0.02), gy ~N(0,1e-4), seeded):
+  forward:  amax(x), amax(W) -> fp64 scales -> e4m3 codes + transposed copies
+            -> y = x W^T (bf16)
+  backward: gy carries the loss scale 65536 (fp16 AMP); amax(gy) -> e5m2 codes
+            + transposed copy -> dgrad gx = gy W and wgrad gW = gy^T x (fp16)
+  scaler:   unscale gx, gW in place + non-finite check -> update()
+all through the C ABI on one stream, inputs resident in HBM.
+
+Prints one JSON line.  `value` is the step's GEMM throughput (3 GEMMs,
+2 M N K flops each) in TFLOP/s.  The line also carries, each measured with HIP
+events on the launch stream: every kernel's average duration, the
+quantize/unscale bandwidths (logical bytes, caches flushed between reps), the
+roofline of the dominant kernel (the GEMM) and the oracle's CPU throughput on
+a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 scaled-linear fwd+bwd TFLOP/s + quantize/unscale GB/s (% MI355X peak)"
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+LOSS_SCALE = 65536.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--reps", type=int, default=50, help="launches per kernel timing loop")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-check", action="store_true")
+    p.add_argument("--size", type=int, default=4096, help="M = N = K of the square layer")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events recorded on the stream the kernels are launched on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def run(self, fn, reps, flush=None):
+        torch = self.torch
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        for i in range(reps):
+            if flush is not None:
+                flush()
+            starts[i].record(self.stream)
+            fn()
+            ends[i].record(self.stream)
+        torch.cuda.synchronize()
+        ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+        return {"avg_us": 1e3 * sum(ms) / reps, "median_us": 1e3 * ms[reps // 2],
+                "min_us": 1e3 * ms[0]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_scaled_gemm_amd as F
+    import workloads as W
+    from workloads.configs import SQUARE, Linear
+
+    cfg = SQUARE if args.size == 4096 else Linear(
+        f"square linear {args.size}^3", args.size, args.size, args.size, 2, 1.0, 0.02, 1e-4,
+        1e-3, 50.0)
+    M, N, K = cfg.M, cfg.N, cfg.K
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    F.lib()
+
+    log(f"generating inputs for {cfg.name}")
+    x_h, w_h, gy_h = cfg.x(), cfg.w(), cfg.gy()
+    gy_s_h = W.f32_to_bf16_bits(
+        (gy_h.view(np.uint16).astype(np.uint32) << 16).view(np.float32) * np.float32(LOSS_SCALE)
+    ).reshape(gy_h.shape)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, w, gy = to_dev(x_h), to_dev(w_h), to_dev(gy_s_h)
+    saved = F.LinearSaved(M, N, K, device=dev)
+    ws = F.LinearBwdWs(M, N, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    gx = torch.empty((M, K), dtype=torch.float16, device=dev)
+    gw = torch.empty((N, K), dtype=torch.float16, device=dev)
+    scale = torch.tensor([LOSS_SCALE], dtype=torch.float32, device=dev)
+    tracker = torch.zeros(1, dtype=torch.int32, device=dev)
+    found = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step():
+        F.fp8_scaled_linear_fwd(x, w, saved, y, F.OUT_BF16)
+        F.fp8_scaled_linear_bwd(gy, saved, ws, gx, gw, F.OUT_F16)
+        F.amp_unscale_check([gx, gw], scale, found)
+        F.amp_update_scale(scale, tracker, found, 2.0, 0.5, 2000)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- the timed region: exactly `steps` steps
+    log(f"timing {args.steps} steps")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    gemm_flops = 3 * 2.0 * M * N * K
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    # ---- per-kernel timings on the same stream (same operands as the step)
+    log("per-kernel timings")
+    T = Timer(torch, stream)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush():
+        flush_buf.fill_(1)  # evicts L2 and the 256 MB Infinity Cache
+
+    inv = lambda rec: rec.inv_ptr()
+    kern = {}
+    kern["gemm_fwd_e4m3xe4m3"] = T.run(lambda: F.fp8_gemm(
+        saved.x_q, F.E4M3FN, saved.w_q, F.E4M3FN, inv(saved.x_sc), inv(saved.w_sc), y,
+        F.OUT_BF16), args.reps)
+    kern["gemm_dgrad_e5m2xe4m3"] = T.run(lambda: F.fp8_gemm(
+        ws.gy_q, F.E5M2, saved.w_qT, F.E4M3FN, inv(ws.gy_sc), inv(saved.w_sc), gx,
+        F.OUT_F16), args.reps)
+    kern["gemm_wgrad_e5m2xe4m3"] = T.run(lambda: F.fp8_gemm(
+        ws.gy_qT, F.E5M2, saved.x_qT, F.E4M3FN, inv(ws.gy_sc), inv(saved.x_sc), gw,
+        F.OUT_F16), args.reps)
+    rec = F.ScaleRec(device=dev)
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    qT = torch.empty((K, M), dtype=torch.uint8, device=dev)
+    kern["amax"] = T.run(lambda: F.fp8_amax(x, rec), args.reps, flush)
+    kern["quantize_transpose"] = T.run(lambda: F.fp8_quantize(x, F.E4M3FN, rec, q, qT),
+                                       args.reps, flush)
+    g16 = [torch.empty_like(gx).copy_(gx), torch.empty_like(gw).copy_(gw)]
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    fz = torch.zeros(1, dtype=torch.int32, device=dev)
+    kern["unscale_check"] = T.run(lambda: F.amp_unscale_check(g16, one, fz), args.reps, flush)
+    kern["update_scale"] = T.run(lambda: F.amp_update_scale(scale, tracker, found, 2.0, 0.5,
+                                                            2000), args.reps)
+
+    gemm_avg_us = sum(kern[k]["avg_us"] for k in kern if k.startswith("gemm")) / 3
+    gemm_tflops = 2.0 * M * N * K / (gemm_avg_us * 1e-6) / 1e12
+    n_el = M * K
+    amax_gbps = 2.0 * n_el / (kern["amax"]["avg_us"] * 1e-6) / 1e9
+    quant_gbps = 4.0 * n_el / (kern["quantize_transpose"]["avg_us"] * 1e-6) / 1e9
+    unscale_gbps = 4.0 * (gx.numel() + gw.numel()) / (kern["unscale_check"]["avg_us"] * 1e-6) / 1e9
+    amax_quant_gbps = 6.0 * n_el / ((kern["amax"]["avg_us"] + kern["quantize_transpose"]["avg_us"])
+                                     * 1e-6) / 1e9
+
+    # ---- sampled check of the step's outputs against the oracle
+    check = None
+    if not args.no_check:
+        log("sampled oracle check")
+        check = sampled_check(np, torch, F, x_h, w_h, gy_s_h, saved, ws, y, M, N, K)
+
+    # ---- oracle on the host cores, bounded sample
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("oracle CPU baseline")
+        cpu = cpu_baseline(np, saved, M, N, K)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: FP8 linear fwd+dgrad+wgrad with fused transposed "
+                               "copies + GradScaler unscale/check/update",
+                   "M": M, "N": N, "K": K, "x": "bf16 N(0,1), 0.1% outliers x50",
+                   "W": "bf16 N(0,0.02)", "gy": "bf16 N(0,1e-4) x loss scale 65536",
+                   "y": "bf16", "grads": "fp16", "formats": "e4m3fn x/W, e5m2 gy"},
+        "step_pct_of_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_gemm (3 GEMMs of the step, 2*M*N*K flops per launch)"},
+        "quantize_GBps": round(quant_gbps, 1),
+        "amax_GBps": round(amax_gbps, 1),
+        "amax_plus_quantize_GBps": round(amax_quant_gbps, 1),
+        "unscale_GBps": round(unscale_gbps, 1),
+        "hbm_frac": {"quantize": round(quant_gbps / PEAK_HBM_GBPS, 4),
+                     "amax": round(amax_gbps / PEAK_HBM_GBPS, 4),
+                     "unscale": round(unscale_gbps / PEAK_HBM_GBPS, 4)},
+        "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
+        "wall_s_timed_region": round(wall, 4),
+        "check": check,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def sampled_check(np, torch, F, x_h, w_h, gy_h, saved, ws, y, M, N, K, n_pts=256):
+    """Recompute codes and scales with the oracle from the same host inputs and
+    compare them with the step's device buffers; check sampled GEMM outputs."""
+    import oracle as O
+    from tests.parity import assert_codes_equal, check_gemm_values
+    xq = O.to_fp8(x_h, O.E4M3FN)
+    wq = O.to_fp8(w_h, O.E4M3FN)
+    gq = O.to_fp8(gy_h, O.E5M2)
+    for got, ref, fmt in ((saved.x_q, xq.q, O.E4M3FN), (saved.w_qT, wq.qT, O.E4M3FN),
+                          (ws.gy_qT, gq.qT, O.E5M2)):
+        assert_codes_equal(fmt, got.cpu().numpy(), ref)
+    for rec, sc in ((saved.x_sc, xq.sc), (saved.w_sc, wq.sc), (ws.gy_sc, gq.sc)):
+        r = rec.read()
+        assert r["amax_bits"] == sc.amax_bits and r["inv"] == sc.inv
+    rng = np.random.default_rng(0)
+    ii = rng.integers(0, M, n_pts)
+    jj = rng.integers(0, N, n_pts)
+    c_ref = O.gemm_at(xq.q, O.E4M3FN, wq.q, O.E4M3FN, xq.sc.inv, wq.sc.inv, ii, jj)
+    ad = O.gemm_absdot_at(xq.q, O.E4M3FN, wq.q, O.E4M3FN, xq.sc.inv, wq.sc.inv, ii, jj)
+    y_h = y.view(torch.int16).cpu().numpy().view(np.uint16)[ii, jj]
+    nw = check_gemm_values(O.decode(O.BF16, y_h), c_ref, ad, K, O.BF16, "bench y")
+    return {"codes_and_scales": "bit-exact", "gemm_fwd_samples": n_pts, "ok": True,
+            "max_abs_err_over_max_abs": float(nw)}
+
+
+def cpu_baseline(np, saved, M, N, K, rows=None):
+    """The oracle (plain C, OpenMP) on the host cores: the forward GEMM on a
+    slab of rows, on the step's own FP8 codes.  Throughput in the metric's
+    unit (TFLOP/s)."""
+    import oracle as O
+    A = saved.x_q.cpu().numpy()
+    B = saved.w_q.cpu().numpy()
+    threads = O.num_threads()
+    if rows is None:  # size the slab for about 10 s of wall time on these cores
+        probe = max(1, threads)
+        t = time.perf_counter()
+        O.gemm(A[:probe], O.E4M3FN, B, O.E4M3FN, 1.0, 1.0)
+        per_row = (time.perf_counter() - t) / probe
+        rows = int(min(M, max(probe, 10.0 / max(per_row, 1e-9))))
+        rows = max(threads, rows - rows % max(threads, 1))
+    t = time.perf_counter()
+    O.gemm(A[:rows], O.E4M3FN, B, O.E4M3FN, 1.0, 1.0)
+    dt = time.perf_counter() - t
+    flops = 2.0 * rows * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"forward GEMM on {rows} of {M} rows ({rows}x{N}x{K}, fp32 sequential "
+                      f"accumulation), {dt:.2f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

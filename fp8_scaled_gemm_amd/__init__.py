@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(HERE, "libfp8sg.so")
 
 E4M3FN, E5M2 = 0, 1
 OUT_BF16, OUT_F16, OUT_F32 = 0, 1, 2
-SCALE_REC_BYTES = 48
+AMAX_PARTS = 1024
+SCALE_REC_BYTES = 32 + 4 * AMAX_PARTS
 
 EXPORTS = ("fp8sg_status_string", "fp8sg_version", "fp8_amax", "fp8_quantize", "fp8_gemm",
            "fp8_scaled_linear_fwd", "fp8_scaled_linear_bwd", "amp_unscale_check",
@@ -86,7 +87,7 @@ def _stream(stream):
 # ----------------------------------------------------------------- scale records
 
 class ScaleRec:
-    """A 48-byte device scale record (fp8sg_scale_rec), zero-initialised.
+    """A device scale record (fp8sg_scale_rec, 4128 bytes).
 
     Fields (after the library has written them): amax, scale32, inv32 (fp32),
     scale, inv (fp64)."""
@@ -103,14 +104,14 @@ class ScaleRec:
         return self.buf.data_ptr() + 24
 
     def read(self) -> dict:
-        h = self.buf.cpu()
+        h = self.buf[:32].cpu()
         f = h[:12].view(torch.float32)
         u = h[:16].view(torch.int32)
         d = h[16:32].view(torch.float64)
         return {"amax": float(f[0]), "scale32": float(f[1]), "inv32": float(f[2]),
                 "amax_bits": int(u[0]) & 0xFFFFFFFF, "scale32_bits": int(u[1]) & 0xFFFFFFFF,
                 "inv32_bits": int(u[2]) & 0xFFFFFFFF, "scale": float(d[0]), "inv": float(d[1]),
-                "_acc": int(u[3]) & 0xFFFFFFFF, "_ticket": int(h[32:36].view(torch.int32)[0])}
+                "nparts": int(u[3])}
 
 
 # ----------------------------------------------------------------- C-ABI calls

@@ -11,7 +11,7 @@
 
 using namespace fp8sg;
 
-static_assert(sizeof(fp8sg_scale_rec) == 48, "scale record layout");
+static_assert(sizeof(fp8sg_scale_rec) == 32 + 4 * FP8SG_AMAX_PARTS, "scale record layout");
 
 namespace {
 
@@ -25,9 +25,11 @@ hipStream_t S(fp8sg_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
 fp8sg_status check_gemm(const void* A, int fa, const void* B, int fb, const void* ia,
                         const void* ib, const void* C, int out, int64_t M, int64_t N, int64_t K) {
-  if (!A || !B || !ia || !ib || !C) return FP8SG_ERR_NULL;
   if (!fmt_ok(fa) || !fmt_ok(fb) || !out_ok(out)) return FP8SG_ERR_FORMAT;
   if (!dims16(M) || !dims16(N) || !dims16(K)) return FP8SG_ERR_SHAPE;
+  // zero-sized operands may come with a NULL data pointer
+  if ((M * K > 0 && !A) || (N * K > 0 && !B) || (M * N > 0 && !C) || !ia || !ib)
+    return FP8SG_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return FP8SG_ERR_ALIGN;
   return FP8SG_OK;
 }
@@ -64,7 +66,7 @@ fp8sg_status fp8_amax(const uint16_t* x, int64_t n, fp8sg_scale_rec* rec, fp8sg_
   AmaxArgs a{};
   a.job[0] = AmaxJob{x, n, rec, 0, amax_blocks_for(n)};
   a.njobs = 1;
-  return hip_status(launch_amax(a, S(stream)));
+  return hip_status(launch_amax(a, true, S(stream)));
 }
 
 fp8sg_status fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, fp8sg_format fmt,
@@ -106,7 +108,7 @@ fp8sg_status fp8_scaled_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t
   am.job[0] = AmaxJob{x, M * K, saved->x_sc, 0, amax_blocks_for(M * K)};
   am.job[1] = AmaxJob{w, N * K, saved->w_sc, 0, amax_blocks_for(N * K)};
   am.njobs = 2;
-  hipError_t e = launch_amax(am, s);
+  hipError_t e = launch_amax(am, false, s);
   if (e != hipSuccess) return FP8SG_ERR_HIP;
 
   QuantArgs qa{};
@@ -139,7 +141,7 @@ fp8sg_status fp8_scaled_linear_bwd(const uint16_t* gy, const fp8_linear_saved* s
   AmaxArgs am{};
   am.job[0] = AmaxJob{gy, M * N, ws->gy_sc, 0, amax_blocks_for(M * N)};
   am.njobs = 1;
-  hipError_t e = launch_amax(am, s);
+  hipError_t e = launch_amax(am, false, s);
   if (e != hipSuccess) return FP8SG_ERR_HIP;
 
   QuantArgs qa{};

@@ -98,4 +98,32 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// Block-wide max of one u32 per thread; every thread gets the result.
+template <int NT>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+  __shared__ uint32_t red[NT / kWave];
+  v = wave_max_u32(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) r = red[w] > r ? red[w] : r;
+  return r;
+}
+
+// amax of a tensor from the per-block partial maxima the amax kernel left in
+// its record (fp32 bit patterns of non-negative values, NaN already
+// canonical, so integer max is numeric max).  Called once per block by every
+// thread; every thread gets the result.
+template <int NT>
+__device__ __forceinline__ float amax_from_partials(const fp8sg_scale_rec* rec) {
+  const uint32_t np = rec->_nparts;
+  uint32_t m = 0;
+  for (uint32_t i = threadIdx.x; i < np; i += NT) {
+    const uint32_t v = rec->_part[i];
+    m = v > m ? v : m;
+  }
+  return __uint_as_float(block_max_u32<NT>(m));
+}
+
 }  // namespace fp8sg

@@ -12,21 +12,21 @@ namespace fp8sg {
 
 // ---- amax (amax.hip)
 constexpr int kMaxAmaxJobs = 4;
-constexpr int kAmaxMaxBlocksPerJob = 2048;
 
 struct AmaxJob {
   const uint16_t* x;
   int64_t n;
   fp8sg_scale_rec* rec;
   int32_t block0;   // first block of this job (filled by launch_amax)
-  int32_t nblocks;  // blocks given to this job (amax_blocks_for)
+  int32_t nblocks;  // blocks given to this job (amax_blocks_for, <= FP8SG_AMAX_PARTS)
 };
 struct AmaxArgs {
   AmaxJob job[kMaxAmaxJobs];
   int32_t njobs;
 };
 int amax_blocks_for(int64_t n);
-hipError_t launch_amax(AmaxArgs args, hipStream_t stream);
+// Per-block partial maxima into each job's record; with finalize, also rec->amax.
+hipError_t launch_amax(AmaxArgs args, bool finalize, hipStream_t stream);
 
 // ---- quantize (quantize.hip)
 constexpr int kMaxQuantJobs = 4;

@@ -4,9 +4,10 @@
 // GEMMs need each operand contiguous along its contraction dimension, which
 // for x, W and gy means a transposed FP8 copy].
 //
-// Every block recomputes the scale from the amax word (two fp64 divisions, a
-// few hundred cycles), so the amax -> scale step needs no launch of its own;
-// the first block of each job also writes the record's scale fields.
+// Every block reduces the amax kernel's partial maxima (4 KB, from L2) and
+// recomputes the scale (two fp64 divisions), so the amax -> scale step needs
+// no launch of its own; the first block of each job also writes the record's
+// amax and scale fields.
 //
 // Tiled path: one 128 x 128 tile per 256-thread block.  The tile is read once
 // with 16-byte loads (8 in flight per thread), quantized in registers, stored
@@ -32,7 +33,9 @@ __device__ __forceinline__ const QuantJob& pick_job(const QuantArgs& a, int& lb)
   return a.job[j];
 }
 
-__device__ __forceinline__ void write_scale_fields(fp8sg_scale_rec* rec, const ScaleVals& v) {
+__device__ __forceinline__ void write_scale_fields(fp8sg_scale_rec* rec, float amax,
+                                                   const ScaleVals& v) {
+  rec->amax = amax;
   rec->scale = v.s;
   rec->inv = v.inv;
   rec->scale32 = v.s32;
@@ -61,8 +64,9 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
   int lb;
   const QuantJob& job = pick_job(args, lb);
   const int tid = threadIdx.x;
-  const ScaleVals sv = scale_from_amax(job.rec->amax, FMT);
-  if (lb == 0 && tid == 0) write_scale_fields(job.rec, sv);
+  const float amax = amax_from_partials<kQThreads>(job.rec);
+  const ScaleVals sv = scale_from_amax(amax, FMT);
+  if (lb == 0 && tid == 0) write_scale_fields(job.rec, amax, sv);
 
   const int64_t rows = job.rows, cols = job.cols;
   const int64_t r_tile = (int64_t)(lb / job.tiles_c) * kQTile;
@@ -123,8 +127,9 @@ __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
   int lb;
   const QuantJob& job = pick_job(args, lb);
   const int tid = threadIdx.x;
-  const ScaleVals sv = scale_from_amax(job.rec->amax, FMT);
-  if (lb == 0 && tid == 0) write_scale_fields(job.rec, sv);
+  const float amax = amax_from_partials<kQThreads>(job.rec);
+  const ScaleVals sv = scale_from_amax(amax, FMT);
+  if (lb == 0 && tid == 0) write_scale_fields(job.rec, amax, sv);
 
   const int64_t n = job.rows * job.cols;
   const int64_t nvec = n >> 3;
@@ -156,8 +161,9 @@ __global__ __launch_bounds__(kQThreads) void k_quant_elem(QuantArgs args) {
   int lb;
   const QuantJob& job = pick_job(args, lb);
   const int tid = threadIdx.x;
-  const ScaleVals sv = scale_from_amax(job.rec->amax, FMT);
-  if (lb == 0 && tid == 0) write_scale_fields(job.rec, sv);
+  const float amax = amax_from_partials<kQThreads>(job.rec);
+  const ScaleVals sv = scale_from_amax(amax, FMT);
+  if (lb == 0 && tid == 0) write_scale_fields(job.rec, amax, sv);
   const int64_t n = job.rows * job.cols;
   for (int64_t i = (int64_t)lb * kQThreads + tid; i < n; i += (int64_t)job.nblocks * kQThreads) {
     const uint8_t c = quant1<FMT>(job.x[i], sv.s32);

@@ -61,24 +61,26 @@ typedef enum {
 
 typedef void* fp8sg_stream; /* hipStream_t */
 
+/* Number of per-block partial maxima an amax reduction leaves in a record. */
+#define FP8SG_AMAX_PARTS 1024
+
 /*
- * Per-tensor scale record, 48 bytes of device memory owned by the caller
+ * Per-tensor scale record, 4128 bytes of device memory owned by the caller
  * [FP8-TRAIN §2]: the tensor's absolute maximum, the fp64 scale
  * fp8_max / max(amax, EPS) with EPS = 1e-12, its fp64 reciprocal (the inverse
  * the GEMM dequantises with) and both rounded to fp32 (the quantizer
- * multiplies by scale32).  The two underscore words are the library's own
- * reduction state: ZERO THE RECORD ONCE before its first use (the library
- * leaves them zero after every call).
+ * multiplies by scale32).  The underscore fields hold the amax reduction's
+ * per-block partial maxima, written by fp8_amax and read by fp8_quantize; no
+ * initialisation is needed.
  */
 typedef struct fp8sg_scale_rec {
   float amax;        /* max_i |x_i| as fp32; canonical NaN 0x7FC00000 if any NaN */
   float scale32;     /* (float)scale                                             */
   float inv32;       /* (float)inv                                               */
-  uint32_t _acc;     /* library-internal, zero between calls                     */
+  uint32_t _nparts;  /* library-internal: partial maxima in _part                */
   double scale;      /* fp8_max / max(amax, EPS), IEEE fp64 division             */
   double inv;        /* 1.0 / scale, IEEE fp64 division                          */
-  uint32_t _ticket;  /* library-internal, zero between calls                     */
-  uint32_t _pad[3];
+  uint32_t _part[FP8SG_AMAX_PARTS]; /* library-internal: per-block maxima (fp32 bits) */
 } fp8sg_scale_rec;
 
 /* Human-readable name of a status code (static storage). */
@@ -91,7 +93,8 @@ FP8SG_API int fp8sg_version(void);
  * amax of a bf16 tensor [FP8-TRAIN §2: x.float().abs().max()].
  *   x:   n bf16 values (device, 16-byte aligned; may be NULL when n == 0);
  *        n >= 0, any n.
- *   rec: scale record (device); writes rec->amax only.  n == 0 gives +0.
+ *   rec: scale record (device); writes rec->amax and the partial maxima.
+ *        n == 0 gives +0.
  * A NaN anywhere gives the canonical NaN; +-inf gives +inf.
  */
 FP8SG_API fp8sg_status fp8_amax(const uint16_t* x, int64_t n, fp8sg_scale_rec* rec, fp8sg_stream stream);
@@ -102,8 +105,9 @@ FP8SG_API fp8sg_status fp8_amax(const uint16_t* x, int64_t n, fp8sg_scale_rec* r
  * e5m2 for gradients), §4 (the transposed copy the backward GEMMs need)].
  *   x:    rows x cols bf16, row-major (device, 16-byte aligned).
  *   fmt:  FP8SG_E4M3FN or FP8SG_E5M2.
- *   rec:  scale record whose amax was written by fp8_amax on the same
- *         tensor; this call writes scale, inv, scale32 and inv32.
+ *   rec:  scale record filled by fp8_amax on the same tensor; this call
+ *         reduces its partial maxima and writes amax, scale, inv, scale32 and
+ *         inv32.
  *   q:    rows x cols codes, row-major (device, 16-byte aligned).
  *   qT:   cols x rows codes = transpose of q (device, 16-byte aligned), or
  *         NULL to skip the transposed copy.
@@ -126,7 +130,7 @@ FP8SG_API fp8sg_status fp8_quantize(const uint16_t* x, int64_t rows, int64_t col
  *   inv_a, inv_b: device doubles (e.g. &rec->inv).
  *   C:  M x N of type `out`, row-major.
  *   M, N, Kc >= 0 and multiples of 16 (FP8SG_ERR_SHAPE otherwise).  Kc == 0
- *   gives C = 0 * alpha.
+ *   gives C = 0 * alpha.  A pointer to a zero-sized operand may be NULL.
  */
 FP8SG_API fp8sg_status fp8_gemm(const uint8_t* A, fp8sg_format fa, const uint8_t* B, fp8sg_format fb,
                       const double* inv_a, const double* inv_b, void* C, fp8sg_out out,

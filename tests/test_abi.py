@@ -43,13 +43,14 @@ def test_library_exports_every_declared_symbol():
 def test_scale_record_layout_matches_header():
     text = open(HEADER).read()
     body = re.search(r"typedef struct fp8sg_scale_rec \{(.*?)\} fp8sg_scale_rec;", text, re.S).group(1)
-    fields = re.findall(r"^\s*(float|double|uint32_t)\s+(\w+)(\[\d+\])?;", body, re.M)
+    parts = int(re.search(r"#define FP8SG_AMAX_PARTS (\d+)", text).group(1))
+    assert parts == F.AMAX_PARTS
+    fields = re.findall(r"^\s*(float|double|uint32_t)\s+(\w+)(\[\w+\])?;", body, re.M)
+    ctype = {"float": ctypes.c_float, "double": ctypes.c_double, "uint32_t": ctypes.c_uint32}
 
     class Rec(ctypes.Structure):
-        _fields_ = [(n, {"float": ctypes.c_float, "double": ctypes.c_double,
-                         "uint32_t": ctypes.c_uint32}[t] * (int(a[1:-1]) if a else 1))
-                    for t, n, a in fields]
-    assert ctypes.sizeof(Rec) == F.SCALE_REC_BYTES == 48
+        _fields_ = [(n, ctype[t] * parts) if a else (n, ctype[t]) for t, n, a in fields]
+    assert ctypes.sizeof(Rec) == F.SCALE_REC_BYTES == 32 + 4 * parts
     assert Rec.inv.offset == 24  # the binding hands &rec->inv to fp8_gemm
 
 
@@ -70,6 +71,7 @@ def test_gemm_validation():
 
     assert call(a0=P(0)) == ENULL
     assert call(a4=P(0)) == ENULL
+    assert call(a0=P(0), a4=P(0), a10=0) == ENULL  # Kc == 0 allows NULL A, never NULL scales
     assert call(a1=7) == EFORMAT
     assert call(a7=9) == EFORMAT
     assert call(a8=24) == ESHAPE

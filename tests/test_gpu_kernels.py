@@ -53,7 +53,7 @@ def check_rec(rec: F.ScaleRec, ref: O.Scale, what=""):
         (np.isnan(s_ref).all() and np.isnan(s_got).all()), (what, s_got, s_ref)
     assert r["scale32_bits"] == int(np.array([ref.scale32], np.float32).view(np.uint32)[0]) or np.isnan(ref.scale32)
     assert r["inv32_bits"] == int(np.array([ref.inv32], np.float32).view(np.uint32)[0]) or np.isnan(ref.inv32)
-    assert r["_acc"] == 0 and r["_ticket"] == 0, "reduction state not re-zeroed"
+    assert 1 <= r["nparts"] <= F.AMAX_PARTS
 
 
 # ------------------------------------------------------------------------ amax
@@ -66,8 +66,7 @@ def test_amax_matches_oracle(n):
     torch.cuda.synchronize()
     r = rec.read()
     assert r["amax_bits"] == O.amax_bits(x)
-    assert r["_acc"] == 0 and r["_ticket"] == 0
-    # the same record again (reduction state must have been re-zeroed)
+    # the same record again: nothing left over from the first call may leak in
     y = W.normal_bf16(31, 8, (n,), 0.5)
     F.fp8_amax(dev_bf16(y), rec)
     torch.cuda.synchronize()
