@@ -178,6 +178,233 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel: BM x BN x 128 tiles streamed global -> LDS by the buffer
+// unit (buffer_load_dwordx4 ... lds), two LDS stages, so the next k-tile's
+// loads are in flight while the current one is multiplied, with no VGPR
+// staging.  One load instruction moves 64 lanes x 16 B = 1 KB = 8 rows of a
+// 128-byte k-slice; lane l fills LDS row 8g + l/8, chunk l%8, and fetches the
+// global chunk that belongs there under the swizzle.  The per-block buffer
+// descriptor spans only the block's row panel, so rows past M (or N) read as
+// zero; chunks past K are pointed outside the descriptor and read as zero too.
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16-byte chunk c of LDS row r lives at chunk c ^ swz16(r).  swz16 is a
+// bijection on every aligned group of 8 rows and on the even and the odd rows
+// of every aligned group of 16, so the 16-byte fragment reads hit distinct
+// banks whether the LDS serves 8 lanes x 16 B or 16 lanes x 16 B per cycle.
+__device__ __forceinline__ int swz16(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int lds_off2(int r, int c) { return r * kBK + ((c ^ swz16(r)) << 4); }
+
+// s_waitcnt with vmcnt <= n and the other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+constexpr uint32_t kBufDword3 = 0x00020000u;  // raw buffer, gfx9 data format
+constexpr uint32_t kOob = 0x80000000u;        // offset past any descriptor: reads 0
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over [base, base + bytes), in scalar registers.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = (int)kBufDword3;
+  return r;
+}
+
+// 16 bytes per lane from buffer offset `voff` into LDS at lds + 16 * lane.
+// Written as inline assembly so the compiler does not track these LDS writes:
+// its own wait insertion would otherwise drain every in-flight load before each
+// LDS read.  The k-loop below waits for them explicitly (s_waitcnt vmcnt) and
+// orders LDS reads with compiler barriers.  M0 carries the LDS address; no
+// other code in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Position of this block's tile.  Workgroups are handed to the 8 XCDs round
+// robin (block b on XCD b % 8); renumber so that each XCD gets a run of
+// consecutive tile indices, then walk tiles in groups of kGroupM tile-rows,
+// column by column, so one XCD's tiles form a compact region whose A and B
+// panels its L2 can share.
+constexpr int kGroupM = 4;
+__device__ __forceinline__ void tile_of(int nbm, int nbn, int& tm, int& tn) {
+  const int nb = nbm * nbn;
+  const int b = blockIdx.x;
+  const int q = nb / 8, rem = nb % 8, x = b % 8;
+  const int t = x * q + (x < rem ? x : rem) + b / 8;
+  const int per_group = kGroupM * nbn;
+  const int g = t / per_group, r = t % per_group;
+  const int gm = (nbm - g * kGroupM) < kGroupM ? (nbm - g * kGroupM) : kGroupM;
+  tm = g * kGroupM + r % gm;
+  tn = r / gm;
+}
+
+// The two pipeline stages are separate LDS objects and the k-loop is unrolled
+// by two, so every fragment read names its stage at compile time: the
+// compiler can then prove the reads do not alias the buffer loads still
+// filling the other stage and waits only for the loads of the stage it reads.
+template <int BM, int BN>
+struct LdsStages {
+  static constexpr int kA = BM * kBK, kB = BN * kBK;
+};
+
+template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT>
+__global__ __launch_bounds__(WM* WN* kWave) void k_gemm_lds(GemmProblem p) {
+  constexpr int kNW = WM * WN;
+  constexpr int kTM = BM / WM / 16, kTN = BN / WN / 16;
+  constexpr int kIA = BM / 8 / kNW, kIB = BN / 8 / kNW;  // 1 KB loads per wave per k-tile
+  static_assert(kIA * 8 * kNW == BM && kIB * 8 * kNW == BN, "tile rows / waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * kBK];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int wm = wave / WN, wn = wave % WN;
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int nbm = (int)((M + BM - 1) / BM), nbn = (int)((N + BN - 1) / BN);
+  int tm, tn;
+  tile_of(nbm, nbn, tm, tn);
+  const int64_t bm = (int64_t)tm * BM, bn = (int64_t)tn * BN;
+  const int nk = (int)((K + kBK - 1) / kBK);
+
+  const int64_t rows_a = (M - bm) < BM ? (M - bm) : BM;
+  const int64_t rows_b = (N - bn) < BN ? (N - bn) : BN;
+  const i32x4 ra = make_rsrc(p.A + bm * K, rows_a * K);
+  const i32x4 rb = make_rsrc(p.B + bn * K, rows_b * K);
+
+  // this lane's source offset (before adding k0) and chunk for each load
+  uint32_t offa[kIA], offb[kIB];
+  int chka[kIA], chkb[kIB];
+#pragma unroll
+  for (int i = 0; i < kIA; ++i) {
+    const int r = 8 * (wave * kIA + i) + (lane >> 3);
+    chka[i] = (lane & 7) ^ swz16(r);
+    offa[i] = (uint32_t)(r * K + 16 * chka[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < kIB; ++i) {
+    const int r = 8 * (wave * kIB + i) + (lane >> 3);
+    chkb[i] = (lane & 7) ^ swz16(r);
+    offb[i] = (uint32_t)(r * K + 16 * chkb[i]);
+  }
+  auto issue = [&](int kt, uint8_t* a, uint8_t* b) {
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int i = 0; i < kIA; ++i) {
+      const uint32_t off = (k0 + 16 * chka[i] < K) ? offa[i] + (uint32_t)k0 : kOob;
+      lds_dma16(lds_addr(a + (wave * kIA + i) * 1024), off, ra);
+    }
+#pragma unroll
+    for (int i = 0; i < kIB; ++i) {
+      const uint32_t off = (k0 + 16 * chkb[i] < K) ? offb[i] + (uint32_t)k0 : kOob;
+      lds_dma16(lds_addr(b + (wave * kIB + i) * 1024), off, rb);
+    }
+  };
+
+  v4f acc[kTM][kTN];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int frow = lane & 15;
+  const int fchunk = 2 * (lane >> 4);
+
+  auto compute = [&](const uint8_t* a, const uint8_t* b) {
+    v8i bf[kTN];
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const int r = wn * (BN / WN) + 16 * j + frow;
+      const uint4 lo = *reinterpret_cast<const uint4*>(b + lds_off2(r, fchunk));
+      const uint4 hi = *reinterpret_cast<const uint4*>(b + lds_off2(r, fchunk + 1));
+      bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const int r = wm * (BM / WM) + 16 * i + frow;
+      const uint4 lo = *reinterpret_cast<const uint4*>(a + lds_off2(r, fchunk));
+      const uint4 hi = *reinterpret_cast<const uint4*>(a + lds_off2(r, fchunk + 1));
+      const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], FB, FA,
+                                                                     0, 0, 0, 0);
+    }
+  };
+  // one k-tile from stage (a, b); then, once every wave is done reading it,
+  // refill the stage with tile kt + 2
+  auto step = [&](int kt, uint8_t* a, uint8_t* b) {
+    if (kt + 1 < nk) wait_vmcnt<kIA + kIB>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's share of this tile has landed
+    compiler_fence();
+    compute(a, b);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads have returned
+    __builtin_amdgcn_s_barrier();        // every wave is done reading the stage
+    compiler_fence();
+    if (kt + 2 < nk) issue(kt + 2, a, b);
+  };
+
+  if (nk > 0) issue(0, sA0, sB0);
+  if (nk > 1) issue(1, sA1, sB1);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, sA0, sB0);
+    step(kt + 1, sA1, sB1);
+  }
+  if (kt < nk) step(kt, sA0, sB0);
+
+  const float alpha = (float)(*p.inv_a * *p.inv_b);
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) {
+    const int64_t m = bm + wm * (BM / WM) + 16 * i + (lane & 15);
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const int64_t n = bn + wn * (BN / WN) + 16 * j + 4 * (lane >> 4);
+      if (n >= N) continue;
+      v4f c = acc[i][j];
+      c[0] *= alpha;
+      c[1] *= alpha;
+      c[2] *= alpha;
+      c[3] *= alpha;
+      store4<OUT>(p.C, m * N + n, c);
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT>
+static hipError_t launch_lds(const GemmProblem& p, hipStream_t stream) {
+  auto kern = k_gemm_lds<BM, BN, WM, WN, FA, FB, OUT>;
+  const unsigned nb = (unsigned)(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN));
+  hipLaunchKernelGGL(kern, dim3(nb), dim3(WM * WN * kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT>
 static hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   using Cfg = GemmCfg<BM, BN, WM, WN>;
@@ -196,6 +423,9 @@ static hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
 
 template <int FA, int FB, int OUT>
 static hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
+  // 256 x 256 tiles once there are enough of them to fill the chip
+  const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  if (big >= 128 && p.K * 256 < (1ll << 31)) return launch_lds<256, 256, 2, 4, FA, FB, OUT>(p, stream);
   return launch_cfg<128, 128, 2, 2, FA, FB, OUT>(p, stream);
 }
 

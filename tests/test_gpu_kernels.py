@@ -188,7 +188,9 @@ def random_codes(rng, fmt, shape):
 
 
 GEMM_SHAPES = [(16, 16, 16), (64, 256, 128), (256, 64, 64), (144, 272, 400), (272, 144, 48),
-               (384, 256, 1024), (128, 128, 0), (512, 384, 4096)]
+               (384, 256, 1024), (128, 128, 0), (512, 384, 4096),
+               # large enough for the 256 x 256 LDS-DMA kernel, with ragged M, N and K
+               (4096, 2048, 256), (4000, 2064, 400), (2064, 4000, 1040)]
 
 
 @pytest.mark.parametrize("fa,fb", [(F.E4M3FN, F.E4M3FN), (F.E5M2, F.E4M3FN), (F.E4M3FN, F.E5M2),
