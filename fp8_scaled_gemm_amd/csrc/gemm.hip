@@ -235,6 +235,7 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, i32x4 rsr
                : "s"(lds), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
+
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -277,6 +278,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm_lds(GemmProblem p) {
   constexpr int kTM = BM / WM / 16, kTN = BN / WN / 16;
   constexpr int kIA = BM / 8 / kNW, kIB = BN / 8 / kNW;  // 1 KB loads per wave per k-tile
   static_assert(kIA * 8 * kNW == BM && kIB * 8 * kNW == BN, "tile rows / waves");
+  static_assert(BM % 16 == 0 && BN % 16 == 0, "16-row blocks");
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * kBK];
@@ -297,32 +299,23 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm_lds(GemmProblem p) {
   const i32x4 ra = make_rsrc(p.A + bm * K, rows_a * K);
   const i32x4 rb = make_rsrc(p.B + bn * K, rows_b * K);
 
-  // this lane's source offset (before adding k0) and chunk for each load
-  uint32_t offa[kIA], offb[kIB];
-  int chka[kIA], chkb[kIB];
-#pragma unroll
-  for (int i = 0; i < kIA; ++i) {
-    const int r = 8 * (wave * kIA + i) + (lane >> 3);
-    chka[i] = (lane & 7) ^ swz16(r);
-    offa[i] = (uint32_t)(r * K + 16 * chka[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < kIB; ++i) {
-    const int r = 8 * (wave * kIB + i) + (lane >> 3);
-    chkb[i] = (lane & 7) ^ swz16(r);
-    offb[i] = (uint32_t)(r * K + 16 * chkb[i]);
-  }
-  auto issue = [&](int kt, uint8_t* a, uint8_t* b) {
-    const int k0 = kt * kBK;
+  // LDS row 8g + l/8, chunk l%8 of a k-tile holds global chunk (l%8) ^ swz16(row):
+  // one load instruction moves 8 full 128-byte rows.
+  auto chunk_of = [&](int g) { return (lane & 7) ^ swz16(8 * g + (lane >> 3)); };
+  auto row_of = [&](int g) { return 8 * g + (lane >> 3); };
+  auto issue = [&](int kt, uint8_t* a, uint8_t* b) {  // kt >= nk loads zeros
+    const int k0 = kt < nk ? kt * kBK : (int)K;
 #pragma unroll
     for (int i = 0; i < kIA; ++i) {
-      const uint32_t off = (k0 + 16 * chka[i] < K) ? offa[i] + (uint32_t)k0 : kOob;
-      lds_dma16(lds_addr(a + (wave * kIA + i) * 1024), off, ra);
+      const int g = wave * kIA + i, c = chunk_of(g);
+      const uint32_t off = (k0 + 16 * c < K) ? (uint32_t)(row_of(g) * K + k0 + 16 * c) : kOob;
+      lds_dma16(lds_addr(a + g * 1024), off, ra);
     }
 #pragma unroll
     for (int i = 0; i < kIB; ++i) {
-      const uint32_t off = (k0 + 16 * chkb[i] < K) ? offb[i] + (uint32_t)k0 : kOob;
-      lds_dma16(lds_addr(b + (wave * kIB + i) * 1024), off, rb);
+      const int g = wave * kIB + i, c = chunk_of(g);
+      const uint32_t off = (k0 + 16 * c < K) ? (uint32_t)(row_of(g) * K + k0 + 16 * c) : kOob;
+      lds_dma16(lds_addr(b + g * 1024), off, rb);
     }
   };
 
@@ -332,51 +325,88 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm_lds(GemmProblem p) {
 #pragma unroll
     for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // fragment of 16-row block rb: lane l holds row 16 rb + (l & 15), k bytes
+  // [32 (l >> 4), +32) as two 16-byte chunks (the same k mapping for A and B)
   const int frow = lane & 15;
   const int fchunk = 2 * (lane >> 4);
+  auto frag = [&](const uint8_t* base, int rb) {
+    const int r = 16 * rb + frow;
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + lds_off2(r, fchunk));
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + lds_off2(r, fchunk + 1));
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  const int ra0 = wm * (BM / WM) / 16;  // first 16-row block of this wave's A rows
+  const int rb0 = wn * (BN / WN) / 16;
 
-  auto compute = [&](const uint8_t* a, const uint8_t* b) {
-    v8i bf[kTN];
-#pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      const int r = wn * (BN / WN) + 16 * j + frow;
-      const uint4 lo = *reinterpret_cast<const uint4*>(b + lds_off2(r, fchunk));
-      const uint4 hi = *reinterpret_cast<const uint4*>(b + lds_off2(r, fchunk + 1));
-      bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
+  // Fragments in registers: the kTN B fragments, two A fragments (the one
+  // in use and the one being read), and one more A fragment at the tile
+  // boundary.
+  v8i bf[kTN];
+  v8i af[2];
+  auto mma1 = [&](int i, int j, const v8i& a_frag) {
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], a_frag, acc[i][j], FB,
+                                                                 FA, 0, 0, 0, 0);
+  };
+  constexpr int kHold = 2;  // the last two A fragments x the last two B fragments wait
+  static_assert(kTM >= kHold && kTN >= kHold && kTM % 2 == 0, "tile split");
+
+  // One k-tile whose head fragments (A0, B*) are in registers or in flight.
+  // A fragments are read one step ahead of their MFMAs.  The kHold x kHold
+  // MFMAs that use the last A and the last B fragments are held back past the
+  // barrier: once every wave has finished reading this stage and the next
+  // tile has landed, each wave reads the next tile's A0 and first B
+  // fragments into the registers already free, runs the held-back MFMAs
+  // while those reads are in flight, then reads the remaining B fragments.
+  // The matrix pipe therefore has work queued across the barrier.  Then the
+  // freed stage is refilled with tile kt + 2.
+  auto tile = [&](int kt, const uint8_t* a, const uint8_t* b, const uint8_t* na,
+                  const uint8_t* nb, uint8_t* ra_next, uint8_t* rb_next) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
-      const int r = wm * (BM / WM) + 16 * i + frow;
-      const uint4 lo = *reinterpret_cast<const uint4*>(a + lds_off2(r, fchunk));
-      const uint4 hi = *reinterpret_cast<const uint4*>(a + lds_off2(r, fchunk + 1));
-      const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      if (i + 1 < kTM) af[(i + 1) & 1] = frag(a, ra0 + i + 1);
+      __builtin_amdgcn_sched_barrier(0);  // the read goes out before the MFMAs
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], FB, FA,
-                                                                     0, 0, 0, 0);
+        if (i < kTM - kHold || j < kTN - kHold) mma1(i, j, af[i & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  // one k-tile from stage (a, b); then, once every wave is done reading it,
-  // refill the stage with tile kt + 2
-  auto step = [&](int kt, uint8_t* a, uint8_t* b) {
-    if (kt + 1 < nk) wait_vmcnt<kIA + kIB>(); else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // every wave's share of this tile has landed
+    wait_vmcnt<0>();                     // tile kt + 1 has landed (my part)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): all my reads of this stage returned
+    __builtin_amdgcn_s_barrier();
     compiler_fence();
-    compute(a, b);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads have returned
-    __builtin_amdgcn_s_barrier();        // every wave is done reading the stage
-    compiler_fence();
-    if (kt + 2 < nk) issue(kt + 2, a, b);
+    // branch-free: past the last tile these reads are stale and unused, and
+    // the refill loads zeros
+    const v8i na0 = frag(na, ra0);
+#pragma unroll
+    for (int j = 0; j < kTN - kHold; ++j) bf[j] = frag(nb, rb0 + j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = kTM - kHold; i < kTM; ++i)
+#pragma unroll
+      for (int j = kTN - kHold; j < kTN; ++j) mma1(i, j, af[i & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = kTN - kHold; j < kTN; ++j) bf[j] = frag(nb, rb0 + j);
+    af[0] = na0;
+    issue(kt + 2, ra_next, rb_next);
   };
 
-  if (nk > 0) issue(0, sA0, sB0);
-  if (nk > 1) issue(1, sA1, sB1);
+  // Prologue: load tile 0; once it is in, load tile 1 and read tile 0's head
+  // fragments.
+  issue(0, sA0, sB0);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+  af[0] = frag(sA0, ra0);
+#pragma unroll
+  for (int j = 0; j < kTN; ++j) bf[j] = frag(sB0, rb0 + j);
+  issue(1, sA1, sB1);
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    step(kt, sA0, sB0);
-    step(kt + 1, sA1, sB1);
+    tile(kt, sA0, sB0, sA1, sB1, sA0, sB0);
+    tile(kt + 1, sA1, sB1, sA0, sB0, sA1, sB1);
   }
-  if (kt < nk) step(kt, sA0, sB0);
+  if (kt < nk) tile(kt, sA0, sB0, sA1, sB1, sA0, sB0);
 
   const float alpha = (float)(*p.inv_a * *p.inv_b);
 #pragma unroll
