@@ -409,20 +409,67 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm_lds(GemmProblem p) {
   if (kt < nk) tile(kt, sA0, sB0, sA1, sB1, sA0, sB0);
 
   const float alpha = (float)(*p.inv_a * *p.inv_b);
+  if constexpr (OUT == FP8SG_OUT_F32) {
 #pragma unroll
-  for (int i = 0; i < kTM; ++i) {
-    const int64_t m = bm + wm * (BM / WM) + 16 * i + (lane & 15);
-    if (m >= M) continue;
+    for (int i = 0; i < kTM; ++i) {
+      const int64_t m = bm + wm * (BM / WM) + 16 * i + (lane & 15);
+      if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      const int64_t n = bn + wn * (BN / WN) + 16 * j + 4 * (lane >> 4);
-      if (n >= N) continue;
-      v4f c = acc[i][j];
-      c[0] *= alpha;
-      c[1] *= alpha;
-      c[2] *= alpha;
-      c[3] *= alpha;
-      store4<OUT>(p.C, m * N + n, c);
+      for (int j = 0; j < kTN; ++j) {
+        const int64_t n = bn + wn * (BN / WN) + 16 * j + 4 * (lane >> 4);
+        if (n >= N) continue;
+        v4f c = acc[i][j];
+        c[0] *= alpha;
+        c[1] *= alpha;
+        c[2] *= alpha;
+        c[3] *= alpha;
+        store4<OUT>(p.C, m * N + n, c);
+      }
+    }
+  } else {
+    // 16-bit output: stage the BM x BN tile in the (now idle) LDS stages, then
+    // write it out as whole row segments, 16 bytes per lane.  Row R of the
+    // tile lives in stage array R / 64 (64 rows of 2 * BN bytes each); its
+    // 16-byte chunk c sits at chunk c ^ (R & 31), so both the column-wise
+    // writes of the accumulator layout and the row-wise reads spread over the
+    // banks.
+    static_assert(BM == 256 && BN == 256, "the staged epilogue assumes 256 x 256 tiles");
+    constexpr int kRowBytes = 2 * BN;
+    auto crow = [&](int r) -> uint8_t* {
+      uint8_t* base = r < 64 ? sA0 : r < 128 ? sB0 : r < 192 ? sA1 : sB1;
+      return base + (r & 63) * kRowBytes;
+    };
+    __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing a stage
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const int r = wm * (BM / WM) + 16 * i + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {
+        const int col = wn * (BN / WN) + 16 * j + 4 * (lane >> 4);
+        v4f c = acc[i][j];
+        c[0] *= alpha;
+        c[1] *= alpha;
+        c[2] *= alpha;
+        c[3] *= alpha;
+        const int off = (((col >> 3) ^ (r & 31)) << 4) + (col & 7) * 2;
+        store4<OUT>(crow(r) + off, 0, c);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    constexpr int kChunks = BN / 8;                       // 16-byte chunks per row
+    constexpr int kRowsPerPass = kNW * kWave / kChunks;   // rows written per pass
+    const int cc = threadIdx.x % kChunks;
+#pragma unroll
+    for (int pass = 0; pass < BM / kRowsPerPass; ++pass) {
+      const int r = pass * kRowsPerPass + threadIdx.x / kChunks;
+      const uint4 v = *reinterpret_cast<const uint4*>(crow(r) + ((cc ^ (r & 31)) << 4));
+      const int64_t m = bm + r, n = bn + 8 * cc;
+      if (m < M && n < N)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + m * N + n) = v;
     }
   }
 }
