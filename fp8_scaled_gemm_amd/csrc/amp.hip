@@ -6,7 +6,10 @@
 // kernel arguments (up to kAmpTensorsPerLaunch tensors per launch, no device
 // table to allocate or copy), every block owns 8192 consecutive elements of one
 // tensor and finds its tensor by binary search over the per-tensor block
-// offsets.  Each element is read and written once in place (2 + 2 bytes); the
+// offsets.  A tensor may start anywhere 2-byte aligned (views into a flat
+// gradient bucket): the kernel walks the enclosing 16-byte-aligned span with
+// 16-byte vectors and handles the partial first and last vectors element by
+// element, never writing outside the tensor.  Each element is read and written once in place (2 + 2 bytes); the
 // non-finite test runs on the stored fp16 result, (bits & 0x7FFF) >= 0x7C00,
 // so it costs no extra traffic.  A wave that saw one sets the flag with a
 // plain store of 1 (all writers store the same value).  The scale update is a
@@ -23,8 +26,9 @@ constexpr int kAmpElemsPerBlock = kAmpThreads * 8 * kAmpUnroll;  // 8192
 constexpr int kAmpTensorsPerLaunch = 64;
 
 struct AmpTable {
-  uint16_t* ptr[kAmpTensorsPerLaunch];
-  int64_t numel[kAmpTensorsPerLaunch];
+  uint16_t* ptr[kAmpTensorsPerLaunch];    // 16-byte-aligned base at or below the tensor
+  int64_t numel[kAmpTensorsPerLaunch];    // elements from ptr to the tensor's end
+  int32_t head[kAmpTensorsPerLaunch];     // elements between ptr and the tensor's start (0..7)
   int32_t block0[kAmpTensorsPerLaunch + 1];  // prefix sum of blocks per tensor
   int32_t ntensors;
   const float* scale;
@@ -52,7 +56,8 @@ __global__ __launch_bounds__(kAmpThreads) void k_unscale_check(AmpTable t) {
     if (t.block0[mid] <= b) lo = mid; else hi = mid;
   }
   uint16_t* g = t.ptr[lo];
-  const int64_t n = t.numel[lo];
+  const int64_t n = t.numel[lo];   // the tensor is [first, n) of g
+  const int64_t first = t.head[lo];
   const int64_t base = (int64_t)(b - t.block0[lo]) * kAmpElemsPerBlock;
   const float inv = 1.0f / *t.scale;
   const int tid = threadIdx.x;
@@ -62,20 +67,23 @@ __global__ __launch_bounds__(kAmpThreads) void k_unscale_check(AmpTable t) {
 #pragma unroll
   for (int u = 0; u < kAmpUnroll; ++u) {
     const int64_t e = base + 8 * (int64_t)(u * kAmpThreads + tid);
-    v[u] = (e + 8 <= n) ? *reinterpret_cast<const uint4*>(g + e) : make_uint4(0, 0, 0, 0);
+    v[u] = (e >= first && e + 8 <= n) ? *reinterpret_cast<const uint4*>(g + e)
+                                      : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int u = 0; u < kAmpUnroll; ++u) {
     const int64_t e = base + 8 * (int64_t)(u * kAmpThreads + tid);
-    if (e + 8 <= n) {
+    if (e >= first && e + 8 <= n) {
       uint4 o;
       o.x = unscale2(v[u].x, inv, bad);
       o.y = unscale2(v[u].y, inv, bad);
       o.z = unscale2(v[u].z, inv, bad);
       o.w = unscale2(v[u].w, inv, bad);
       *reinterpret_cast<uint4*>(g + e) = o;
-    } else if (e < n) {
-      for (int64_t i = e; i < n; ++i) {  // the tensor's last, partial vector
+    } else if (e < n && e + 8 > first) {
+      // a partial vector at the tensor's start or end: only its own elements
+      const int64_t i0 = e > first ? e : first, i1 = e + 8 < n ? e + 8 : n;
+      for (int64_t i = i0; i < i1; ++i) {
         const float f = (float)__builtin_bit_cast(_Float16, g[i]) * inv;
         const uint16_t r = __builtin_bit_cast(uint16_t, (_Float16)f);
         bad |= (r & 0x7FFFu) >= 0x7C00u;
@@ -95,9 +103,12 @@ hipError_t launch_unscale_check(uint16_t* const* grads, const int64_t* numel, in
     int32_t total = 0;
     const int32_t cnt = ntensors - t0 < kAmpTensorsPerLaunch ? ntensors - t0 : kAmpTensorsPerLaunch;
     for (int32_t i = 0; i < cnt; ++i) {
-      const int64_t n = numel[t0 + i];
-      tab.ptr[tab.ntensors] = grads[t0 + i];
+      const uintptr_t p = reinterpret_cast<uintptr_t>(grads[t0 + i]);
+      const int32_t head = (int32_t)((p & 15u) >> 1);
+      const int64_t n = numel[t0 + i] > 0 ? numel[t0 + i] + head : 0;  // span from the base
+      tab.ptr[tab.ntensors] = reinterpret_cast<uint16_t*>(p & ~(uintptr_t)15);
       tab.numel[tab.ntensors] = n;
+      tab.head[tab.ntensors] = head;
       tab.block0[tab.ntensors] = total;
       total += (int32_t)((n + kAmpElemsPerBlock - 1) / kAmpElemsPerBlock);
       ++tab.ntensors;

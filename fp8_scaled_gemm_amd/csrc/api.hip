@@ -165,7 +165,7 @@ fp8sg_status amp_unscale_check(uint16_t* const* grads, const int64_t* numel, int
   for (int32_t i = 0; i < ntensors; ++i) {
     if (numel[i] < 0) return FP8SG_ERR_SHAPE;
     if (numel[i] > 0 && !grads[i]) return FP8SG_ERR_NULL;
-    if (numel[i] > 0 && !aligned16(grads[i])) return FP8SG_ERR_ALIGN;
+    if (numel[i] > 0 && (reinterpret_cast<uintptr_t>(grads[i]) & 1u)) return FP8SG_ERR_ALIGN;
   }
   return hip_status(launch_unscale_check(grads, numel, ntensors, scale, found_inf, S(stream)));
 }

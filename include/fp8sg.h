@@ -21,7 +21,8 @@
  *    (FP8SG_ERR_NULL, _SHAPE, _ALIGN, _FORMAT).  FP8SG_ERR_HIP means a launch
  *    failed; kernels already enqueued by the call may have run.  No exception
  *    crosses the ABI, and there is no global error state besides the return.
- *  - Device pointers to tensors must be 16-byte aligned (FP8SG_ERR_ALIGN).
+ *  - Device pointers to tensors must be 16-byte aligned (FP8SG_ERR_ALIGN),
+ *    except the fp16 gradients of amp_unscale_check (2-byte aligned).
  *  - Calls that share an output or state buffer must not overlap in time.
  */
 #ifndef FP8SG_H
@@ -188,7 +189,8 @@ FP8SG_API fp8sg_status fp8_scaled_linear_bwd(const uint16_t* gy, const fp8_linea
  *   g <- fp16_RNE( fl32(g) * fl32(1.0f / *scale) )
  * and *found_inf is set to 1 if any stored result is inf or NaN (it is never
  * cleared here: the flag is OR-accumulated over calls).
- *   grads:  HOST array of ntensors device pointers (each 16-byte aligned).
+ *   grads:  HOST array of ntensors device pointers (each 2-byte aligned;
+ *           views into one flat gradient buffer are fine).
  *   numel:  HOST array of ntensors element counts (>= 0, any value).
  *   scale:  device float, the current loss scale.
  *   found_inf: device int32.

@@ -102,7 +102,7 @@ def test_linear_and_quant_validation():
 
 def test_amp_validation():
     L = F.lib()
-    ptrs = (ctypes.c_void_p * 2)(A16, MIS)
+    ptrs = (ctypes.c_void_p * 2)(A16, A16 + 1)  # fp16 needs 2-byte alignment only
     numel = (ctypes.c_int64 * 2)(8, 8)
     assert L.amp_unscale_check(ptrs, numel, 2, P(A16), P(A16), P(0)) == EALIGN
     numel[1] = -1

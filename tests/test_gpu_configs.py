@@ -1,0 +1,276 @@
+"""GPU parity at the five workloads' full sizes, through the same C-ABI calls
+bench.py times.  FP8 codes (row-major and transposed), amax, scales, non-finite
+flags and scaler state are compared in full, bit-exact; GEMM outputs at
+sampled coordinates, each computed by the oracle one by one, within the bound
+of tests/parity.py."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_scaled_gemm_amd as F
+import oracle as O
+import workloads as W
+from tests.parity import assert_codes_equal, check_gemm_values
+from workloads import configs as C
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def log(msg):
+    print(f"[configs {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def dev16(bits, dtype=torch.bfloat16):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(dtype).to(DEV)
+
+
+def host16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_rec(rec, sc, what):
+    r = rec.read()
+    assert r["amax_bits"] == sc.amax_bits, what
+    assert r["scale"] == sc.scale and r["inv"] == sc.inv, what
+    assert np.float32(r["scale32"]) == sc.scale32 and np.float32(r["inv32"]) == sc.inv32, what
+
+
+def sampled_gemm_check(got_dev, out_fmt, A, fa, B, fb, inv_a, inv_b, n_pts, seed, what):
+    M, N = got_dev.shape
+    rng = np.random.default_rng(seed)
+    ii = rng.integers(0, M, n_pts)
+    jj = rng.integers(0, N, n_pts)
+    # always include the corners (first/last tile, ragged edges)
+    ii = np.concatenate([ii, [0, M - 1, 0, M - 1]])
+    jj = np.concatenate([jj, [0, N - 1, N - 1, 0]])
+    c_ref = O.gemm_at(A, fa, B, fb, inv_a, inv_b, ii, jj)
+    ad = O.gemm_absdot_at(A, fa, B, fb, inv_a, inv_b, ii, jj)
+    got = host16(got_dev)[ii, jj]
+    return check_gemm_values(O.decode(out_fmt, got), c_ref, ad, A.shape[1], out_fmt, what)
+
+
+def run_and_check_linear(x_h, w_h, gy_h, out_bwd, n_pts, seed, what, xq_ref=None):
+    """fwd (bf16 y) + bwd through the C ABI; every code and scale against the
+    oracle, GEMM outputs sampled.  Returns device gradients and the oracle
+    quantizations (so a caller can reuse a shared input's)."""
+    M, K = x_h.shape
+    N = w_h.shape[0]
+    x, w, gy = dev16(x_h), dev16(w_h), dev16(gy_h)
+    saved = F.LinearSaved(M, N, K)
+    ws = F.LinearBwdWs(M, N)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    gdt = torch.float16 if out_bwd == F.OUT_F16 else torch.bfloat16
+    gx = torch.empty((M, K), dtype=gdt, device=DEV)
+    gw = torch.empty((N, K), dtype=gdt, device=DEV)
+    log(f"{what}: GPU fwd+bwd M={M} N={N} K={K}")
+    F.fp8_scaled_linear_fwd(x, w, saved, y, F.OUT_BF16)
+    F.fp8_scaled_linear_bwd(gy, saved, ws, gx, gw, out_bwd)
+    torch.cuda.synchronize()
+    log(f"{what}: oracle quantize")
+    xq = xq_ref if xq_ref is not None else O.to_fp8(x_h, O.E4M3FN)
+    wq = O.to_fp8(w_h, O.E4M3FN)
+    gq = O.to_fp8(gy_h, O.E5M2)
+    for rec, sc, nm in ((saved.x_sc, xq.sc, "x"), (saved.w_sc, wq.sc, "W"), (ws.gy_sc, gq.sc, "gy")):
+        check_rec(rec, sc, f"{what} {nm}")
+    for got, ref, fmt, nm in ((saved.x_q, xq.q, O.E4M3FN, "x_q"), (saved.x_qT, xq.qT, O.E4M3FN, "x_qT"),
+                              (saved.w_q, wq.q, O.E4M3FN, "w_q"), (saved.w_qT, wq.qT, O.E4M3FN, "w_qT"),
+                              (ws.gy_q, gq.q, O.E5M2, "gy_q"), (ws.gy_qT, gq.qT, O.E5M2, "gy_qT")):
+        assert_codes_equal(fmt, got.cpu().numpy(), ref, f"{what} {nm}")
+    log(f"{what}: sampled GEMM outputs")
+    ofmt = O.F16 if out_bwd == F.OUT_F16 else O.BF16
+    sampled_gemm_check(y, O.BF16, xq.q, O.E4M3FN, wq.q, O.E4M3FN, xq.sc.inv, wq.sc.inv, n_pts,
+                       seed, f"{what} fwd")
+    sampled_gemm_check(gx, ofmt, gq.q, O.E5M2, wq.qT, O.E4M3FN, gq.sc.inv, wq.sc.inv, n_pts,
+                       seed + 1, f"{what} dgrad")
+    sampled_gemm_check(gw, ofmt, gq.qT, O.E5M2, xq.qT, O.E4M3FN, gq.sc.inv, xq.sc.inv, n_pts,
+                       seed + 2, f"{what} wgrad")
+    return gx, gw, xq
+
+
+def test_square_layer_with_gradscaler_step():
+    """4096^3 layer exactly as bench.py runs it: bf16 forward, fp16 backward of
+    the loss-scaled gradient, then one unscale/check/update step."""
+    cfg = C.SQUARE
+    x_h, w_h, gy_h = cfg.x(), cfg.w(), cfg.gy()
+    gy_s = W.f32_to_bf16_bits(O.decode(O.BF16, gy_h).astype(np.float32) *
+                              np.float32(C.INIT_SCALE)).reshape(gy_h.shape)
+    gx, gw, _ = run_and_check_linear(x_h, w_h, gy_s, F.OUT_F16, 2048, 20, "square")
+    g_host = [host16(gx), host16(gw)]
+    scale = torch.tensor([C.INIT_SCALE], dtype=torch.float32, device=DEV)
+    tracker = torch.zeros(1, dtype=torch.int32, device=DEV)
+    found = torch.zeros(1, dtype=torch.int32, device=DEV)
+    F.amp_unscale_check([gx, gw], scale, found)
+    f_gpu = int(found.item())
+    F.amp_update_scale(scale, tracker, found, C.GROWTH, C.BACKOFF, C.INTERVAL)
+    torch.cuda.synchronize()
+    f_ref = O.unscale_check(g_host, C.INIT_SCALE, 0)
+    assert f_gpu == f_ref
+    assert_codes_equal(O.F16, host16(gx), g_host[0], "unscaled gx")
+    assert_codes_equal(O.F16, host16(gw), g_host[1], "unscaled gW")
+    st = O.update_scale(O.ScalerState(np.float32(C.INIT_SCALE), 0), f_ref, C.GROWTH, C.BACKOFF,
+                        C.INTERVAL)
+    assert float(scale.item()) == float(st.scale) and int(tracker.item()) == st.tracker
+
+
+def test_mlp_block_three_linears():
+    """Transformer MLP block, tokens 8192, hidden 4096, ffn 14336: gate and up
+    ([14336,4096], sharing x) and down ([4096,14336]), forward and backward."""
+    xq_shared = None
+    for k, name in enumerate(("gate", "up", "down")):
+        lin = C.mlp_linear(name)
+        log(f"generating {lin.name}")
+        x_h, w_h, gy_h = lin.x(), lin.w(), lin.gy()
+        reuse = xq_shared if name == "up" else None
+        _, _, xq = run_and_check_linear(x_h, w_h, gy_h, F.OUT_BF16, 512, 30 + 3 * k, name, reuse)
+        if name == "gate":
+            xq_shared = xq
+        del x_h, w_h, gy_h
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("which", ["activations_e4m3", "gradients_e5m2"])
+def test_quantize_pass_2pow28(which):
+    """amax + scale + quantize-cast of a 268,435,456-element bf16 tensor:
+    magnitudes 10^U(-6,3) to e4m3, and 10^U(-8,-2) to e5m2."""
+    if which == "activations_e4m3":
+        x_h, fmt = C.quant_act(), F.E4M3FN
+    else:
+        x_h, fmt = C.quant_grad(), F.E5M2
+    x = dev16(x_h)
+    rec = F.ScaleRec()
+    q = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+    log(f"{which}: GPU amax + quantize")
+    F.fp8_amax(x, rec)
+    F.fp8_quantize(x, fmt, rec, q)
+    torch.cuda.synchronize()
+    log(f"{which}: oracle")
+    ref = O.to_fp8(x_h, fmt, with_transpose=False)
+    check_rec(rec, ref.sc, which)
+    assert_codes_equal(fmt, q.cpu().numpy(), ref.q, which)
+
+
+def _scaler_reference(sizes, injections, values_finite_ok):
+    """Oracle trajectory of (found, scale, tracker) per step."""
+    inj = {j.step: j for j in injections}
+    st = O.ScalerState(np.float32(C.INIT_SCALE), 0)
+    traj = []
+    for s in range(C.SCALER_STEPS):
+        found = 1 if s in inj else 0
+        if s not in inj:
+            assert values_finite_ok
+        st = O.update_scale(st, found, C.GROWTH, C.BACKOFF, C.SCALER_INTERVAL)
+        traj.append((found, float(st.scale), st.tracker))
+    return traj
+
+
+def test_gradscaler_200_tensors_1000_steps_full_size():
+    """200 fp16 gradients (sizes log-uniform 4K..64M, ~1.7e9 elements), 1000
+    steps with an inf/NaN injected into a random tensor with probability 0.01,
+    growth interval 100.  Each step restores the tensors from a resident copy
+    (values N(0,1e-5) * 65536), injects per the schedule, then runs one
+    amp_unscale_check over all 200 tensors and amp_update_scale.  The
+    found/scale/tracker trajectory must equal the oracle's over all 1000 steps;
+    unscaled values are compared in full at step 0 and sampled at the first
+    injected and the last step."""
+    sizes = C.scaler_sizes()
+    injections = C.injection_schedule(sizes)
+    log(f"scaler: {len(sizes)} tensors, {int(sizes.sum())} elements, {len(injections)} injections")
+    pristine_h = [C.scaler_grad(t, int(n), C.INIT_SCALE) for t, n in enumerate(sizes)]
+    pristine = [dev16(g, torch.float16) for g in pristine_h]
+    work = [torch.empty_like(p) for p in pristine]
+    scale = torch.tensor([C.INIT_SCALE], dtype=torch.float32, device=DEV)
+    tracker = torch.zeros(1, dtype=torch.int32, device=DEV)
+    found = torch.zeros(1, dtype=torch.int32, device=DEV)
+    hist = torch.zeros((C.SCALER_STEPS, 3), dtype=torch.float64, device=DEV)
+    inj = {j.step: j for j in injections}
+    first_inj = injections[0].step if injections else None
+    checks = {}
+    inj_bits = torch.tensor([0], dtype=torch.int16, device=DEV)
+    for s in range(C.SCALER_STEPS):
+        for wv, pv in zip(work, pristine):
+            wv.copy_(pv)
+        if s in inj:
+            j = inj[s]
+            inj_bits.fill_(int(np.array([j.bits], np.uint16).view(np.int16)[0]))
+            work[j.tensor].view(torch.int16)[j.index:j.index + 1].copy_(inj_bits)
+        scale_before = float(scale.item()) if s in (0, first_inj, C.SCALER_STEPS - 1) else None
+        F.amp_unscale_check(work, scale, found)
+        hist[s, 0].copy_(found[0])
+        F.amp_update_scale(scale, tracker, found, C.GROWTH, C.BACKOFF, C.SCALER_INTERVAL)
+        hist[s, 1].copy_(scale[0])
+        hist[s, 2].copy_(tracker[0])
+        if scale_before is not None:
+            torch.cuda.synchronize()
+            checks[s] = scale_before
+            if s == 0:
+                log("scaler: full element-wise check at step 0")
+                ref = [g.copy() for g in pristine_h]
+                f0 = O.unscale_check(ref, scale_before, 0)
+                assert f0 == 0  # every value is finite after unscaling
+                for t, wv in enumerate(work):
+                    assert_codes_equal(O.F16, host16(wv), ref[t], f"step 0 tensor {t}")
+                del ref
+            else:
+                log(f"scaler: sampled check at step {s}")
+                rng = np.random.default_rng(s)
+                for t in rng.choice(len(sizes), 20, replace=False).tolist() + \
+                        ([inj[s].tensor] if s in inj else []):
+                    n = int(sizes[t])
+                    idx = np.unique(np.concatenate([rng.integers(0, n, 5000),
+                                                    [inj[s].index] if (s in inj and inj[s].tensor == t) else []]).astype(np.int64))
+                    src = pristine_h[t][idx].copy()
+                    if s in inj and inj[s].tensor == t:
+                        src[np.searchsorted(idx, inj[s].index)] = inj[s].bits
+                    O.unscale_check([src], scale_before, 0)
+                    got = host16(work[t])[idx]
+                    assert_codes_equal(O.F16, got, src, f"step {s} tensor {t}")
+        if s % 100 == 0:
+            log(f"scaler: step {s}")
+    torch.cuda.synchronize()
+    # the oracle's found flag on the injected tensor at every injected step
+    for j in injections:
+        g = pristine_h[j.tensor].copy()
+        g[j.index] = j.bits
+        assert O.unscale_check([g], C.INIT_SCALE, 0) == 1
+    traj = _scaler_reference(sizes, injections, values_finite_ok=True)
+    h = hist.cpu().numpy()
+    for s in range(C.SCALER_STEPS):
+        assert (int(h[s, 0]), float(h[s, 1]), int(h[s, 2])) == traj[s], f"step {s}"
+    log(f"scaler: trajectory ok, final scale {traj[-1][1]}, tracker {traj[-1][2]}")
+
+
+def test_gradscaler_downsized_every_step_elementwise():
+    """The same run on 200 tensors of 4K..64K elements, values regenerated every
+    step as fp16(N(0,1e-5) * scale_t), compared element by element with the
+    oracle at every one of the 1000 steps."""
+    sizes = C.scaler_sizes(lo=4096, hi=65536)
+    injections = C.injection_schedule(sizes)
+    inj = {j.step: j for j in injections}
+    scale = torch.tensor([C.INIT_SCALE], dtype=torch.float32, device=DEV)
+    tracker = torch.zeros(1, dtype=torch.int32, device=DEV)
+    found = torch.zeros(1, dtype=torch.int32, device=DEV)
+    st = O.ScalerState(np.float32(C.INIT_SCALE), 0)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    flat_dev = torch.empty(int(offs[-1]), dtype=torch.float16, device=DEV)
+    views = [flat_dev[int(offs[t]):int(offs[t + 1])] for t in range(len(sizes))]
+    for s in range(C.SCALER_STEPS):
+        cur = float(st.scale)
+        g = np.concatenate([C.scaler_grad(t, int(n), cur, step=s) for t, n in enumerate(sizes)])
+        if s in inj:
+            g[int(offs[inj[s].tensor]) + inj[s].index] = inj[s].bits
+        flat_dev.copy_(torch.from_numpy(g.view(np.int16)).view(torch.float16).to(DEV))
+        F.amp_unscale_check(views, scale, found)
+        f_gpu = int(found.item())
+        F.amp_update_scale(scale, tracker, found, C.GROWTH, C.BACKOFF, C.SCALER_INTERVAL)
+        ref = [g[int(offs[t]):int(offs[t + 1])].copy() for t in range(len(sizes))]
+        f_ref = O.unscale_check(ref, cur, 0)
+        assert f_gpu == f_ref == (1 if s in inj else 0), f"step {s}"
+        assert_codes_equal(O.F16, host16(flat_dev), np.concatenate(ref), f"step {s}")
+        st = O.update_scale(st, f_ref, C.GROWTH, C.BACKOFF, C.SCALER_INTERVAL)
+        assert float(scale.item()) == float(st.scale) and int(tracker.item()) == st.tracker
+        if s % 200 == 0:
+            log(f"downsized scaler: step {s}, scale {float(st.scale)}")

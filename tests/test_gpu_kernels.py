@@ -376,3 +376,31 @@ def test_small_layer_with_gradscaler_step():
     st = O.update_scale(O.ScalerState(np.float32(INIT_SCALE), 0), f_ref, 2.0, 0.5, INTERVAL)
     assert float(scale.item()) == float(st.scale) == INIT_SCALE
     assert int(tracker.item()) == st.tracker == 1
+
+
+def test_unscale_check_views_into_flat_buffer():
+    """Gradients as views at arbitrary 2-byte offsets of one flat fp16 buffer
+    (a gradient bucket): partial first/last vectors must be handled without
+    touching the neighbours."""
+    rng = np.random.default_rng(39)
+    sizes = [1, 3, 7, 8, 9, 15, 17, 8191, 8193, 20000, 5, 70001]
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    flat_h = W.normal_f16(39, 1, (int(offs[-1]) + 3,), 4.0)
+    flat_h[int(offs[5]) + 2] = 0x7E00  # NaN inside one view
+    flat = dev_f16(flat_h)
+    views = [flat[1 + int(offs[t]):1 + int(offs[t + 1])] for t in range(len(sizes))]
+    # unscale every other view; the others and the guard elements must not change
+    chosen = [v for t, v in enumerate(views) if t % 2 == 1]
+    scale = torch.tensor([8.0], dtype=torch.float32, device=DEV)
+    found = torch.zeros(1, dtype=torch.int32, device=DEV)
+    F.amp_unscale_check(chosen, scale, found)
+    torch.cuda.synchronize()
+    ref = flat_h.copy()
+    f = 0
+    for t in range(len(sizes)):
+        if t % 2 == 1:
+            seg = ref[1 + int(offs[t]):1 + int(offs[t + 1])].copy()
+            f = O.unscale_check([seg], 8.0, f)
+            ref[1 + int(offs[t]):1 + int(offs[t + 1])] = seg
+    assert int(found.item()) == f == 1
+    assert_codes_equal(O.F16, host_u16(flat), ref, "flat buffer")
