@@ -12,10 +12,11 @@ all through the C ABI on one stream, inputs resident in HBM.
 
 Prints one JSON line.  `value` is the step's GEMM throughput (3 GEMMs,
 2 M N K flops each) in TFLOP/s.  The line also carries, each measured with HIP
-events on the launch stream: every kernel's average duration, the
-quantize/unscale bandwidths (logical bytes, caches flushed between reps), the
-roofline of the dominant kernel (the GEMM) and the oracle's CPU throughput on
-a bounded sample of the same workload.
+events on the launch stream: every kernel's average duration with the step's
+operands, the roofline of the dominant kernel (the GEMM), the bandwidth of the
+memory-bound kernels at HBM scale (a 2^28-element quantize pass and a
+200-tensor, ~1.7e9-element unscale pass; logical bytes), and the oracle's CPU
+throughput on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -31,6 +32,15 @@ PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 LOSS_SCALE = 65536.0
 
+# HBM bytes of one 4096^3 GEMM launch from two rocprofv3 --pmc passes of this
+# benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
+# what the same counter reads for a 1 GiB device-to-device copy
+# (bench.py --copy-reference: FETCH_SIZE 524,302 KiB -> x2.0, WRITE_SIZE
+# 1,048,576 KiB -> x1.0).  Valid only for the GEMM source they were taken on;
+# bench.py reports null for any other.
+GEMM_TRAFFIC = {"gemm_src_sha256_16": "94a82b94d1b243a9", "fetch_kib": 49637.0, "write_kib": 33280.0,
+                "fetch_factor": 2.0, "write_factor": 1.0}
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -40,6 +50,10 @@ def parse():
     p.add_argument("--reps", type=int, default=50, help="launches per kernel timing loop")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true")
+    p.add_argument("--no-hbm", action="store_true", help="skip the HBM-scale bandwidth passes")
+    p.add_argument("--copy-reference", action="store_true",
+                   help="only copy 1 GiB device-to-device 5 times (calibrates the HBM byte "
+                        "counters against a transfer of known size)")
     p.add_argument("--size", type=int, default=4096, help="M = N = K of the square layer")
     return p.parse_args()
 
@@ -79,6 +93,15 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_reference:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_reference_bytes": 1 << 30, "copies": 5}), flush=True)
+        return
 
     import fp8_scaled_gemm_amd as F
     import workloads as W
@@ -139,14 +162,9 @@ def main():
     gemm_flops = 3 * 2.0 * M * N * K
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
 
-    # ---- per-kernel timings on the same stream (same operands as the step)
+    # ---- per-kernel timings on the same stream, same operands as the step
     log("per-kernel timings")
     T = Timer(torch, stream)
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-
-    def flush():
-        flush_buf.fill_(1)  # evicts L2 and the 256 MB Infinity Cache
-
     inv = lambda rec: rec.inv_ptr()
     kern = {}
     kern["gemm_fwd_e4m3xe4m3"] = T.run(lambda: F.fp8_gemm(
@@ -161,24 +179,56 @@ def main():
     rec = F.ScaleRec(device=dev)
     q = torch.empty((M, K), dtype=torch.uint8, device=dev)
     qT = torch.empty((K, M), dtype=torch.uint8, device=dev)
-    kern["amax"] = T.run(lambda: F.fp8_amax(x, rec), args.reps, flush)
-    kern["quantize_transpose"] = T.run(lambda: F.fp8_quantize(x, F.E4M3FN, rec, q, qT),
-                                       args.reps, flush)
+    kern["amax_x_standalone"] = T.run(lambda: F.fp8_amax(x, rec), args.reps)
+    kern["quantize_transpose_x"] = T.run(lambda: F.fp8_quantize(x, F.E4M3FN, rec, q, qT),
+                                         args.reps)
     g16 = [torch.empty_like(gx).copy_(gx), torch.empty_like(gw).copy_(gw)]
     one = torch.ones(1, dtype=torch.float32, device=dev)
     fz = torch.zeros(1, dtype=torch.int32, device=dev)
-    kern["unscale_check"] = T.run(lambda: F.amp_unscale_check(g16, one, fz), args.reps, flush)
+    kern["unscale_check_gx_gw"] = T.run(lambda: F.amp_unscale_check(g16, one, fz), args.reps)
     kern["update_scale"] = T.run(lambda: F.amp_update_scale(scale, tracker, found, 2.0, 0.5,
                                                             2000), args.reps)
+    del g16, q, qT
 
     gemm_avg_us = sum(kern[k]["avg_us"] for k in kern if k.startswith("gemm")) / 3
     gemm_tflops = 2.0 * M * N * K / (gemm_avg_us * 1e-6) / 1e12
-    n_el = M * K
-    amax_gbps = 2.0 * n_el / (kern["amax"]["avg_us"] * 1e-6) / 1e9
-    quant_gbps = 4.0 * n_el / (kern["quantize_transpose"]["avg_us"] * 1e-6) / 1e9
-    unscale_gbps = 4.0 * (gx.numel() + gw.numel()) / (kern["unscale_check"]["avg_us"] * 1e-6) / 1e9
-    amax_quant_gbps = 6.0 * n_el / ((kern["amax"]["avg_us"] + kern["quantize_transpose"]["avg_us"])
-                                     * 1e-6) / 1e9
+    traffic = None
+    import hashlib
+    src = os.path.join(ROOT, "fp8_scaled_gemm_amd", "csrc", "gemm.hip")
+    if (M, N, K) == (4096, 4096, 4096) and hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]             == GEMM_TRAFFIC["gemm_src_sha256_16"]:
+        traffic = 1024.0 * (GEMM_TRAFFIC["fetch_kib"] * GEMM_TRAFFIC["fetch_factor"] +
+                            GEMM_TRAFFIC["write_kib"] * GEMM_TRAFFIC["write_factor"])
+
+    # ---- memory-bound kernels at HBM scale (working sets far above the 256 MB
+    # Infinity Cache): amax + e4m3 quantize of a 2^28-element bf16 tensor
+    # (magnitudes 10^U(-6,3)), and unscale + check over 200 fp16 gradients of
+    # log-uniform sizes 4K..64M
+    hbm = {}
+    if not args.no_hbm:
+        from workloads import configs as C
+        log("HBM-scale quantize pass")
+        big = torch.from_numpy(C.quant_act().view(np.int16)).view(torch.bfloat16).to(dev)
+        bq = torch.empty(big.shape, dtype=torch.uint8, device=dev)
+        brec = F.ScaleRec(device=dev)
+        r_amax = T.run(lambda: F.fp8_amax(big, brec), 10)
+        r_quant = T.run(lambda: F.fp8_quantize(big, F.E4M3FN, brec, bq), 10)
+        nb = big.numel()
+        hbm["amax_GBps"] = 2.0 * nb / (r_amax["avg_us"] * 1e-6) / 1e9
+        hbm["quantize_GBps"] = 3.0 * nb / (r_quant["avg_us"] * 1e-6) / 1e9
+        hbm["amax_plus_quantize_GBps"] = 5.0 * nb / ((r_amax["avg_us"] + r_quant["avg_us"]) * 1e-6) / 1e9
+        kern["amax_2p28"] = r_amax
+        kern["quantize_2p28"] = r_quant
+        del big, bq
+        log("HBM-scale unscale pass")
+        sizes = C.scaler_sizes()
+        grads = [(torch.randn(int(n), device=dev) * 0.5).half() for n in sizes]
+        r_un = T.run(lambda: F.amp_unscale_check(grads, one, fz), 10)
+        ng = int(sizes.sum())
+        hbm["unscale_GBps"] = 4.0 * ng / (r_un["avg_us"] * 1e-6) / 1e9
+        hbm["unscale_elements"] = ng
+        kern["unscale_check_200_tensors"] = r_un
+        del grads
+        torch.cuda.empty_cache()
 
     # ---- sampled check of the step's outputs against the oracle
     check = None
@@ -213,15 +263,12 @@ def main():
         "step_pct_of_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch (HBM, counter-measured)",
                      "kernel": "k_gemm (3 GEMMs of the step, 2*M*N*K flops per launch)"},
-        "quantize_GBps": round(quant_gbps, 1),
-        "amax_GBps": round(amax_gbps, 1),
-        "amax_plus_quantize_GBps": round(amax_quant_gbps, 1),
-        "unscale_GBps": round(unscale_gbps, 1),
-        "hbm_frac": {"quantize": round(quant_gbps / PEAK_HBM_GBPS, 4),
-                     "amax": round(amax_gbps / PEAK_HBM_GBPS, 4),
-                     "unscale": round(unscale_gbps / PEAK_HBM_GBPS, 4)},
+        "hbm_scale": {k: (round(v, 1) if isinstance(v, float) else v) for k, v in hbm.items()},
+        "hbm_frac": {k[:-5]: round(v / PEAK_HBM_GBPS, 4) for k, v in hbm.items()
+                     if k.endswith("_GBps")},
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "wall_s_timed_region": round(wall, 4),
         "check": check,
