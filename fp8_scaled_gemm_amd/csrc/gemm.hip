@@ -9,16 +9,16 @@
 // three GEMMs.  Every FP8 x FP8 product is exact in fp32 and the matrix cores
 // accumulate in fp32; only the summation order differs from a sequential loop.
 //
-// Structure: a BM x BN block tile per workgroup, K consumed 128 bytes at a
-// time.  Each k-tile of A and B is fetched with 16-byte global loads into
-// registers while the previous tile is being multiplied, then written to the
-// other half of a double-buffered LDS tile (16-byte chunks XOR-swizzled by row
-// so the fragment reads hit distinct banks).  Each wave owns a (BM/WM) x
-// (BN/WN) sub-tile made of 16x16 blocks and issues
-// v_mfma_f32_16x16x128_f8f6f4 with the operand formats (e4m3 = 0, e5m2 = 1)
-// selected per operand.  The B fragment is passed as the instruction's first
-// source so each lane's four accumulators are four consecutive output
-// columns, stored as one 8-byte (bf16/fp16) or 16-byte (fp32) write.
+// Two kernels, one arithmetic: each wave issues v_mfma_f32_16x16x128_f8f6f4
+// with the operand formats (e4m3 = 0, e5m2 = 1) selected per operand.  The B
+// fragment is passed as the instruction's first source so each lane's four
+// accumulators are four consecutive output columns.  LDS tiles hold 16-byte
+// chunks XOR-swizzled by row so the fragment reads hit distinct banks.
+//   - k_gemm_pingpong: 256 x 256 tiles, for problems with at least 128 of
+//     them (fills the chip).
+//   - k_gemm: 128 x 128 tiles with register-staged loads, for smaller problems.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -60,6 +60,12 @@ __device__ __forceinline__ void store4(void* C, int64_t idx, v4f v) {
   }
 }
 
+// Small-problem kernel: a BM x BN block tile per workgroup, K consumed 128
+// bytes at a time.  Each k-tile of A and B is fetched with 16-byte global loads
+// into registers while the previous tile is being multiplied, then written to
+// the other half of a double-buffered LDS tile.  Each wave owns a (BM/WM) x
+// (BN/WN) sub-tile of 16 x 16 blocks; results are stored as one 8-byte
+// (bf16/fp16) or 16-byte (fp32) write per lane and block.
 template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT>
 __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
   using Cfg = GemmCfg<BM, BN, WM, WN>;
@@ -179,23 +185,22 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile kernel: BM x BN x 128 tiles streamed global -> LDS by the buffer
-// unit (buffer_load_dwordx4 ... lds), two LDS stages, so the next k-tile's
-// loads are in flight while the current one is multiplied, with no VGPR
-// staging.  One load instruction moves 64 lanes x 16 B = 1 KB = 8 rows of a
-// 128-byte k-slice; lane l fills LDS row 8g + l/8, chunk l%8, and fetches the
-// global chunk that belongs there under the swizzle.  The per-block buffer
-// descriptor spans only the block's row panel, so rows past M (or N) read as
-// zero; chunks past K are pointed outside the descriptor and read as zero too.
+// Large-tile kernel helpers.  Operand tiles are streamed global -> LDS by the
+// buffer unit (buffer_load_dwordx4 ... lds), with no VGPR staging.  One load
+// instruction moves 64 lanes x 16 B = 1 KB = 8 rows of a 128-byte k-slice;
+// lane l fills LDS row 8g + l/8, chunk l%8, and fetches the global chunk that
+// belongs there under the swizzle.  The per-block buffer descriptor spans only
+// the block's row panel, so rows past M (or N) read as zero; chunks past K are
+// pointed outside the descriptor and read as zero too.
 // ---------------------------------------------------------------------------
-
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 // 16-byte chunk c of LDS row r lives at chunk c ^ swz16(r).  swz16 is a
 // bijection on every aligned group of 8 rows and on the even and the odd rows
 // of every aligned group of 16, so the 16-byte fragment reads hit distinct
 // banks whether the LDS serves 8 lanes x 16 B or 16 lanes x 16 B per cycle.
-__device__ __forceinline__ int swz16(int r) { return (r ^ (r >> 3)) & 7; }
+// It depends on r & 15 only, so a lane's fragment-read address differs
+// between 16-row blocks by a constant that fits the instruction's offset.
+__device__ __forceinline__ int swz16(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
 __device__ __forceinline__ int lds_off2(int r, int c) { return r * kBK + ((c ^ swz16(r)) << 4); }
 
 // s_waitcnt with vmcnt <= n and the other counters untouched (gfx9 encoding).
@@ -238,9 +243,9 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, i32x4 rsr
 
 #pragma clang diagnostic pop
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)__builtin_amdgcn_readfirstlane(
-      (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+// LDS byte address of a __shared__ array (folds to a constant).
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -263,160 +268,173 @@ __device__ __forceinline__ void tile_of(int nbm, int nbn, int& tm, int& tn) {
   tn = r / gm;
 }
 
-// The two pipeline stages are separate LDS objects and the k-loop is unrolled
-// by two, so every fragment read names its stage at compile time: the
-// compiler can then prove the reads do not alias the buffer loads still
-// filling the other stage and waits only for the loads of the stage it reads.
-template <int BM, int BN>
-struct LdsStages {
-  static constexpr int kA = BM * kBK, kB = BN * kBK;
-};
-
-template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT>
-__global__ __launch_bounds__(WM* WN* kWave) void k_gemm_lds(GemmProblem p) {
-  constexpr int kNW = WM * WN;
-  constexpr int kTM = BM / WM / 16, kTN = BN / WN / 16;
-  constexpr int kIA = BM / 8 / kNW, kIB = BN / 8 / kNW;  // 1 KB loads per wave per k-tile
-  static_assert(kIA * 8 * kNW == BM && kIB * 8 * kNW == BN, "tile rows / waves");
-  static_assert(BM % 16 == 0 && BN % 16 == 0, "16-row blocks");
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * kBK];
+// ---------------------------------------------------------------------------
+// Large-tile kernel: 256 x 256 output tile per workgroup, K consumed 128 bytes
+// at a time, 8 waves in two groups of four (one wave of each group per SIMD).
+// Group g owns output rows [128 g, 128 g + 128); wave q of a group owns
+// columns [64 q, 64 q + 64), i.e. 8 x 4 blocks of 16 x 16.
+//
+// The groups run half a k-tile apart and alternate between
+//   - a memory phase: issue this group's share of the global -> LDS loads,
+//     then read all 12 operand fragments of the next k-tile (8 A, 4 B; 96
+//     VGPRs) from LDS, and
+//   - a compute phase: 32 MFMAs on registers only, nothing to wait for,
+// meeting at a workgroup barrier at every swap.  So each SIMD always has one
+// wave feeding its matrix pipe while the other waits on LDS and memory.
+//
+// LDS (160 KB): A of k-tile t in A stage t % 2, B of k-tile t in B slot
+// t % 3.  Group 0 loads A of t + 1 during its memory phase for t (that stage
+// held A of t - 1, which both groups read before the last swap); group 1
+// loads B of t + 2 during its memory phase for t (that slot held B of t - 1).
+// Each load is waited for (s_waitcnt vmcnt) by the wave that issued it before
+// the swap ahead of the first read, so the barrier publishes it to all waves.
+// ---------------------------------------------------------------------------
+template <int FA, int FB, int OUT, bool RAGGED_K>
+__global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
+  constexpr int BM = 256, BN = 256;
+  constexpr int kTM = 8, kTN = 4;
+  constexpr int kLoads = 256 / 8 / 4;  // 1 KB loads per group wave per operand half-stage: 8
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[256 * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[256 * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[256 * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[256 * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB2[256 * kBK];
+  auto sa = [&](auto i) -> uint8_t* { if constexpr (decltype(i)::value == 0) return sA0; else return sA1; };
+  auto sb = [&](auto i) -> uint8_t* {
+    constexpr int I = decltype(i)::value;
+    if constexpr (I == 0) return sB0;
+    else if constexpr (I == 1) return sB1;
+    else return sB2;
+  };
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int grp = wave >> 2, wq = wave & 3;
   const int64_t M = p.M, N = p.N, K = p.K;
   const int nbm = (int)((M + BM - 1) / BM), nbn = (int)((N + BN - 1) / BN);
   int tm, tn;
   tile_of(nbm, nbn, tm, tn);
   const int64_t bm = (int64_t)tm * BM, bn = (int64_t)tn * BN;
   const int nk = (int)((K + kBK - 1) / kBK);
-
   const int64_t rows_a = (M - bm) < BM ? (M - bm) : BM;
   const int64_t rows_b = (N - bn) < BN ? (N - bn) : BN;
   const i32x4 ra = make_rsrc(p.A + bm * K, rows_a * K);
   const i32x4 rb = make_rsrc(p.B + bn * K, rows_b * K);
 
-  // LDS row 8g + l/8, chunk l%8 of a k-tile holds global chunk (l%8) ^ swz16(row):
-  // one load instruction moves 8 full 128-byte rows.
-  auto chunk_of = [&](int g) { return (lane & 7) ^ swz16(8 * g + (lane >> 3)); };
-  auto row_of = [&](int g) { return 8 * g + (lane >> 3); };
-  auto issue = [&](int kt, uint8_t* a, uint8_t* b) {  // kt >= nk loads zeros
+  // One operand half-stage (256 rows x 128 B) by wave q of a group: rows
+  // [64 q, 64 q + 64), 8 loads of 8 rows.  Lane l of load i fills LDS row
+  // 8 (8 q + i) + l / 8; the swizzle of that row depends only on i & 1, so a
+  // lane needs two offsets (even and odd i) and the rest is scalar.  Only a
+  // ragged last k-tile (RAGGED_K) needs the per-lane test against K.
+  const int lr = lane >> 3;
+  const int cl0 = (lane & 7) ^ swz16(lr), cl1 = (lane & 7) ^ swz16(8 + lr);
+  const uint32_t vo0 = (uint32_t)(lr * K + 16 * cl0), vo1 = (uint32_t)(lr * K + 16 * cl1);
+  auto issue = [&](int kt, uint32_t dst, const i32x4& rs) {  // kt >= nk loads zeros
     const int k0 = kt < nk ? kt * kBK : (int)K;
+    const uint32_t sbase = (uint32_t)(64 * wq * K + k0);
 #pragma unroll
-    for (int i = 0; i < kIA; ++i) {
-      const int g = wave * kIA + i, c = chunk_of(g);
-      const uint32_t off = (k0 + 16 * c < K) ? (uint32_t)(row_of(g) * K + k0 + 16 * c) : kOob;
-      lds_dma16(lds_addr(a + g * 1024), off, ra);
-    }
-#pragma unroll
-    for (int i = 0; i < kIB; ++i) {
-      const int g = wave * kIB + i, c = chunk_of(g);
-      const uint32_t off = (k0 + 16 * c < K) ? (uint32_t)(row_of(g) * K + k0 + 16 * c) : kOob;
-      lds_dma16(lds_addr(b + g * 1024), off, rb);
+    for (int i = 0; i < kLoads; ++i) {
+      uint32_t off = ((i & 1) ? vo1 : vo0) + sbase + (uint32_t)(8 * i * K);
+      if constexpr (RAGGED_K) {
+        if (k0 + 16 * ((i & 1) ? cl1 : cl0) >= K) off = kOob;
+      } else {
+        if (kt >= nk) off = kOob;
+      }
+      lds_dma16(dst + (wq * kLoads + i) * 1024, off, rs);
     }
   };
-
   v4f acc[kTM][kTN];
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
     for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // fragment of 16-row block rb: lane l holds row 16 rb + (l & 15), k bytes
-  // [32 (l >> 4), +32) as two 16-byte chunks (the same k mapping for A and B)
   const int frow = lane & 15;
   const int fchunk = 2 * (lane >> 4);
-  auto frag = [&](const uint8_t* base, int rb) {
-    const int r = 16 * rb + frow;
+  auto frag = [&](const uint8_t* base, int blk) {
+    const int r = 16 * blk + frow;
     const uint4 lo = *reinterpret_cast<const uint4*>(base + lds_off2(r, fchunk));
     const uint4 hi = *reinterpret_cast<const uint4*>(base + lds_off2(r, fchunk + 1));
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
-  const int ra0 = wm * (BM / WM) / 16;  // first 16-row block of this wave's A rows
-  const int rb0 = wn * (BN / WN) / 16;
-
-  // Fragments in registers: the kTN B fragments, two A fragments (the one
-  // in use and the one being read), and one more A fragment at the tile
-  // boundary.
-  v8i bf[kTN];
-  v8i af[2];
-  auto mma1 = [&](int i, int j, const v8i& a_frag) {
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], a_frag, acc[i][j], FB,
-                                                                 FA, 0, 0, 0, 0);
-  };
-  constexpr int kHold = 2;  // the last two A fragments x the last two B fragments wait
-  static_assert(kTM >= kHold && kTN >= kHold && kTM % 2 == 0, "tile split");
-
-  // One k-tile whose head fragments (A0, B*) are in registers or in flight.
-  // A fragments are read one step ahead of their MFMAs.  The kHold x kHold
-  // MFMAs that use the last A and the last B fragments are held back past the
-  // barrier: once every wave has finished reading this stage and the next
-  // tile has landed, each wave reads the next tile's A0 and first B
-  // fragments into the registers already free, runs the held-back MFMAs
-  // while those reads are in flight, then reads the remaining B fragments.
-  // The matrix pipe therefore has work queued across the barrier.  Then the
-  // freed stage is refilled with tile kt + 2.
-  auto tile = [&](int kt, const uint8_t* a, const uint8_t* b, const uint8_t* na,
-                  const uint8_t* nb, uint8_t* ra_next, uint8_t* rb_next) {
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) {
-      if (i + 1 < kTM) af[(i + 1) & 1] = frag(a, ra0 + i + 1);
-      __builtin_amdgcn_sched_barrier(0);  // the read goes out before the MFMAs
-#pragma unroll
-      for (int j = 0; j < kTN; ++j)
-        if (i < kTM - kHold || j < kTN - kHold) mma1(i, j, af[i & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_vmcnt<0>();                     // tile kt + 1 has landed (my part)
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): all my reads of this stage returned
+  const int ra0 = grp * 8, rb0 = wq * 4;
+  v8i af[kTM], bf[kTN];
+  auto barrier = [&]() {
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    // branch-free: past the last tile these reads are stale and unused, and
-    // the refill loads zeros
-    const v8i na0 = frag(na, ra0);
-#pragma unroll
-    for (int j = 0; j < kTN - kHold; ++j) bf[j] = frag(nb, rb0 + j);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = kTM - kHold; i < kTM; ++i)
-#pragma unroll
-      for (int j = kTN - kHold; j < kTN; ++j) mma1(i, j, af[i & 1]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = kTN - kHold; j < kTN; ++j) bf[j] = frag(nb, rb0 + j);
-    af[0] = na0;
-    issue(kt + 2, ra_next, rb_next);
   };
 
-  // Prologue: load tile 0; once it is in, load tile 1 and read tile 0's head
-  // fragments.
-  issue(0, sA0, sB0);
-  wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
-  af[0] = frag(sA0, ra0);
-#pragma unroll
-  for (int j = 0; j < kTN; ++j) bf[j] = frag(sB0, rb0 + j);
-  issue(1, sA1, sB1);
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    tile(kt, sA0, sB0, sA1, sB1, sA0, sB0);
-    tile(kt + 1, sA1, sB1, sA0, sB0, sA1, sB1);
+  // Prologue: group 0 loads A0, group 1 loads B0 and B1.
+  if (grp == 0) {
+    issue(0, lds_u32(sA0), ra);
+    wait_vmcnt<0>();
+  } else {
+    issue(0, lds_u32(sB0), rb);
+    issue(1, lds_u32(sB1), rb);
+    wait_vmcnt<kLoads>();
   }
-  if (kt < nk) tile(kt, sA0, sB0, sA1, sB1, sA0, sB0);
+  barrier();
+  if (grp == 1) barrier();  // group 1 starts half a k-tile later
+
+  // k-tile t: memory phase (loads, then all 12 fragments), swap, compute
+  // phase, swap.  Group 0 loads A of t + 1 (its stage held A of t - 1, read
+  // by both groups before the last swap) and waits for it before the swap
+  // that ends its compute phase.  Group 1 loads B of t + 2 (its slot held B
+  // of t - 1) and, before the swap that ends this memory phase, waits for B of
+  // t + 1, issued one k-tile earlier.
+  auto step = [&](auto pc, int t) {
+    constexpr int P = decltype(pc)::value;  // t % 6
+    const uint8_t* a = sa(std::integral_constant<int, P % 2>{});
+    const uint8_t* b = sb(std::integral_constant<int, P % 3>{});
+    {
+      const uint32_t da = lds_u32(sa(std::integral_constant<int, (P + 1) % 2>{}));
+      const uint32_t db = lds_u32(sb(std::integral_constant<int, (P + 2) % 3>{}));
+      issue(t + 1 + grp, grp ? db : da, grp ? rb : ra);
+    }
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) bf[j] = frag(b, rb0 + j);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) af[i] = frag(a, ra0 + i);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    if (grp == 1) wait_vmcnt<kLoads>();  // B of t + 1 has landed
+    barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], FB,
+                                                                     FA, 0, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp == 0) wait_vmcnt<0>();  // A of t + 1 has landed
+    barrier();
+  };
+  for (int t = 0;;) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (++t == nk) break;
+    step(std::integral_constant<int, 1>{}, t);
+    if (++t == nk) break;
+    step(std::integral_constant<int, 2>{}, t);
+    if (++t == nk) break;
+    step(std::integral_constant<int, 3>{}, t);
+    if (++t == nk) break;
+    step(std::integral_constant<int, 4>{}, t);
+    if (++t == nk) break;
+    step(std::integral_constant<int, 5>{}, t);
+    if (++t == nk) break;
+  }
+  if (grp == 0) barrier();
 
   const float alpha = (float)(*p.inv_a * *p.inv_b);
+  const int wr0 = grp * 128, wc0 = wq * 64;
   if constexpr (OUT == FP8SG_OUT_F32) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
-      const int64_t m = bm + wm * (BM / WM) + 16 * i + (lane & 15);
+      const int64_t m = bm + wr0 + 16 * i + (lane & 15);
       if (m >= M) continue;
 #pragma unroll
       for (int j = 0; j < kTN; ++j) {
-        const int64_t n = bn + wn * (BN / WN) + 16 * j + 4 * (lane >> 4);
+        const int64_t n = bn + wc0 + 16 * j + 4 * (lane >> 4);
         if (n >= N) continue;
         v4f c = acc[i][j];
         c[0] *= alpha;
@@ -427,27 +445,19 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm_lds(GemmProblem p) {
       }
     }
   } else {
-    // 16-bit output: stage the BM x BN tile in the (now idle) LDS stages, then
-    // write it out as whole row segments, 16 bytes per lane.  Row R of the
-    // tile lives in stage array R / 64 (64 rows of 2 * BN bytes each); its
-    // 16-byte chunk c sits at chunk c ^ (R & 31), so both the column-wise
-    // writes of the accumulator layout and the row-wise reads spread over the
-    // banks.
-    static_assert(BM == 256 && BN == 256, "the staged epilogue assumes 256 x 256 tiles");
     constexpr int kRowBytes = 2 * BN;
     auto crow = [&](int r) -> uint8_t* {
-      uint8_t* base = r < 64 ? sA0 : r < 128 ? sB0 : r < 192 ? sA1 : sB1;
+      uint8_t* base = r < 64 ? sA0 : r < 128 ? sA1 : r < 192 ? sB0 : sB1;
       return base + (r & 63) * kRowBytes;
     };
-    __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing a stage
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing a slot
+    barrier();
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
-      const int r = wm * (BM / WM) + 16 * i + (lane & 15);
+      const int r = wr0 + 16 * i + (lane & 15);
 #pragma unroll
       for (int j = 0; j < kTN; ++j) {
-        const int col = wn * (BN / WN) + 16 * j + 4 * (lane >> 4);
+        const int col = wc0 + 16 * j + 4 * (lane >> 4);
         v4f c = acc[i][j];
         c[0] *= alpha;
         c[1] *= alpha;
@@ -457,11 +467,10 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm_lds(GemmProblem p) {
         store4<OUT>(crow(r) + off, 0, c);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-    constexpr int kChunks = BN / 8;                       // 16-byte chunks per row
-    constexpr int kRowsPerPass = kNW * kWave / kChunks;   // rows written per pass
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    barrier();
+    constexpr int kChunks = BN / 8;
+    constexpr int kRowsPerPass = 512 / kChunks;
     const int cc = threadIdx.x % kChunks;
 #pragma unroll
     for (int pass = 0; pass < BM / kRowsPerPass; ++pass) {
@@ -474,11 +483,13 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm_lds(GemmProblem p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT>
-static hipError_t launch_lds(const GemmProblem& p, hipStream_t stream) {
-  auto kern = k_gemm_lds<BM, BN, WM, WN, FA, FB, OUT>;
-  const unsigned nb = (unsigned)(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN));
-  hipLaunchKernelGGL(kern, dim3(nb), dim3(WM * WN * kWave), 0, stream, p);
+template <int FA, int FB, int OUT>
+static hipError_t launch_pingpong(const GemmProblem& p, hipStream_t stream) {
+  const unsigned nb = (unsigned)(((p.M + 255) / 256) * ((p.N + 255) / 256));
+  if (p.K % kBK == 0)
+    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, false>), dim3(nb), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, true>), dim3(nb), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -500,9 +511,10 @@ static hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
 
 template <int FA, int FB, int OUT>
 static hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
-  // 256 x 256 tiles once there are enough of them to fill the chip
+  // 256 x 256 tiles once there are enough of them to fill the chip; the
+  // per-block buffer descriptors address a 256-row panel with 32-bit offsets
   const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (big >= 128 && p.K * 256 < (1ll << 31)) return launch_lds<256, 256, 2, 4, FA, FB, OUT>(p, stream);
+  if (big >= 128 && p.K * 256 < (1ll << 31)) return launch_pingpong<FA, FB, OUT>(p, stream);
   return launch_cfg<128, 128, 2, 2, FA, FB, OUT>(p, stream);
 }
 
