@@ -38,7 +38,7 @@ LOSS_SCALE = 65536.0
 # (bench.py --copy-reference: FETCH_SIZE 524,302 KiB -> x2.0, WRITE_SIZE
 # 1,048,576 KiB -> x1.0).  Valid only for the GEMM source they were taken on;
 # bench.py reports null for any other.
-GEMM_TRAFFIC = {"gemm_src_sha256_16": "94a82b94d1b243a9", "fetch_kib": 49637.0, "write_kib": 33280.0,
+GEMM_TRAFFIC = {"gemm_src_sha256_16": "9085a2c22a5e8a9c", "fetch_kib": 49248.0, "write_kib": 32768.0,
                 "fetch_factor": 2.0, "write_factor": 1.0}
 
 
@@ -265,7 +265,7 @@ def main():
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
                      "traffic_unit": "bytes per launch (HBM, counter-measured)",
-                     "kernel": "k_gemm (3 GEMMs of the step, 2*M*N*K flops per launch)"},
+                     "kernel": "k_gemm_pingpong (3 GEMMs of the step, 2*M*N*K flops per launch)"},
         "hbm_scale": {k: (round(v, 1) if isinstance(v, float) else v) for k, v in hbm.items()},
         "hbm_frac": {k[:-5]: round(v / PEAK_HBM_GBPS, 4) for k, v in hbm.items()
                      if k.endswith("_GBps")},
