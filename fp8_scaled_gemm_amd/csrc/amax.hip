@@ -32,6 +32,7 @@ __device__ __forceinline__ uint32_t pmax(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+template <bool S>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax(AmaxArgs args) {
   int j = 0;
 #pragma unroll
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(AmaxArgs args) {
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) {
       const int64_t k = base + (int64_t)u * kAmaxThreads;
-      v[u] = k < nvec ? xv[k] : make_uint4(0, 0, 0, 0);
+      v[u] = k < nvec ? ld16<S>(xv + k) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) {
@@ -92,11 +93,16 @@ int amax_blocks_for(int64_t n) {
 
 hipError_t launch_amax(AmaxArgs args, bool finalize, hipStream_t stream) {
   int total = 0;
+  int64_t bytes = 0;
   for (int j = 0; j < args.njobs; ++j) {
     args.job[j].block0 = total;
     total += args.job[j].nblocks;
+    bytes += 2 * args.job[j].n;
   }
-  hipLaunchKernelGGL(k_amax, dim3(total), dim3(kAmaxThreads), 0, stream, args);
+  if (bytes >= kStreamBytes)
+    hipLaunchKernelGGL(k_amax<true>, dim3(total), dim3(kAmaxThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL(k_amax<false>, dim3(total), dim3(kAmaxThreads), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !finalize) return e;
   hipLaunchKernelGGL(k_amax_finalize, dim3(args.njobs), dim3(kAmaxThreads), 0, stream, args);

@@ -48,6 +48,7 @@ __device__ __forceinline__ uint32_t unscale2(uint32_t w, float inv, bool& bad) {
   return r;
 }
 
+template <bool S>
 __global__ __launch_bounds__(kAmpThreads) void k_unscale_check(AmpTable t) {
   const int b = blockIdx.x;
   int lo = 0, hi = t.ntensors;  // block0[lo] <= b < block0[hi]
@@ -67,8 +68,7 @@ __global__ __launch_bounds__(kAmpThreads) void k_unscale_check(AmpTable t) {
 #pragma unroll
   for (int u = 0; u < kAmpUnroll; ++u) {
     const int64_t e = base + 8 * (int64_t)(u * kAmpThreads + tid);
-    v[u] = (e >= first && e + 8 <= n) ? *reinterpret_cast<const uint4*>(g + e)
-                                      : make_uint4(0, 0, 0, 0);
+    v[u] = (e >= first && e + 8 <= n) ? ld16<S>(g + e) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int u = 0; u < kAmpUnroll; ++u) {
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kAmpThreads) void k_unscale_check(AmpTable t) {
       o.y = unscale2(v[u].y, inv, bad);
       o.z = unscale2(v[u].z, inv, bad);
       o.w = unscale2(v[u].w, inv, bad);
-      *reinterpret_cast<uint4*>(g + e) = o;
+      st16<S>(g + e, o);
     } else if (e < n && e + 8 > first) {
       // a partial vector at the tensor's start or end: only its own elements
       const int64_t i0 = e > first ? e : first, i1 = e + 8 < n ? e + 8 : n;
@@ -115,7 +115,10 @@ hipError_t launch_unscale_check(uint16_t* const* grads, const int64_t* numel, in
     }
     tab.block0[tab.ntensors] = total;
     if (total == 0) continue;
-    hipLaunchKernelGGL(k_unscale_check, dim3(total), dim3(kAmpThreads), 0, stream, tab);
+    if (4ll * kAmpElemsPerBlock * total >= kStreamBytes)  // 2 B read + 2 B written per element
+      hipLaunchKernelGGL(k_unscale_check<true>, dim3(total), dim3(kAmpThreads), 0, stream, tab);
+    else
+      hipLaunchKernelGGL(k_unscale_check<false>, dim3(total), dim3(kAmpThreads), 0, stream, tab);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -20,6 +20,43 @@ constexpr float kE5M2Max = 57344.0f;
 // Lower clamp of amax in the scale division; the page names EPS without a value.
 constexpr double kScaleEps = 1e-12;
 
+// Streaming (non-temporal) 16- and 8-byte global accesses for data touched
+// once per pass: the caches are told not to keep the lines, which lets a
+// pure stream run at close to the HBM rate (measured on MI355X: reads 3.8 ->
+// 6.7 TB/s, read + write 4.5 -> 6.3 TB/s for 512 MiB passes).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st_stream(void* p, uint2 v) {
+  __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+}
+
+// A pass that moves less than the Infinity Cache (256 MB) keeps ordinary
+// cached accesses: its inputs were usually just written or read by the
+// previous kernel and are still there, and its outputs are read next.
+constexpr int64_t kStreamBytes = 256ll << 20;
+template <bool S>
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  if constexpr (S) return ld_stream(p);
+  else return *reinterpret_cast<const uint4*>(p);
+}
+template <bool S>
+__device__ __forceinline__ void st16(void* p, uint4 v) {
+  if constexpr (S) st_stream(p, v);
+  else *reinterpret_cast<uint4*>(p) = v;
+}
+template <bool S>
+__device__ __forceinline__ void st8(void* p, uint2 v) {
+  if constexpr (S) st_stream(p, v);
+  else *reinterpret_cast<uint2*>(p) = v;
+}
+
 __device__ __forceinline__ float fmt_max(int fmt) { return fmt == FP8SG_E4M3FN ? kE4M3Max : kE5M2Max; }
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.

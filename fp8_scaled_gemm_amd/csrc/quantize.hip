@@ -59,7 +59,7 @@ __device__ __forceinline__ void tr4x4(uint32_t d0, uint32_t d1, uint32_t d2, uin
   o3 = __builtin_amdgcn_perm(f1, e1, 0x07060302u);
 }
 
-template <int FMT>
+template <int FMT, bool S>
 __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
   int lb;
   const QuantJob& job = pick_job(args, lb);
@@ -83,15 +83,14 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int64_t gr = r_tile + r0 + 16 * p;
-    v[p] = (col_ok && gr < rows) ? *reinterpret_cast<const uint4*>(job.x + gr * cols + gc)
-                                 : make_uint4(0, 0, 0, 0);
+    v[p] = (col_ok && gr < rows) ? ld16<S>(job.x + gr * cols + gc) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int r = r0 + 16 * p;
     const int64_t gr = r_tile + r;
     const uint2 c = quant8<FMT>(v[p], sv.s32);
-    if (col_ok && gr < rows) *reinterpret_cast<uint2*>(job.q + gr * cols + gc) = c;
+    if (col_ok && gr < rows) st8<S>(job.q + gr * cols + gc, c);
     *reinterpret_cast<uint2*>(&lds[r * 32 + ((2 * c8) ^ swz(r))]) = c;
   }
   __syncthreads();
@@ -114,15 +113,14 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
   if (tr0 < rows && tc0 < cols) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(job.qT + (tc0 + j) * rows + tr0) =
-          make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]);
+      st16<S>(job.qT + (tc0 + j) * rows + tr0, make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]));
   }
 }
 
 // Row-major codes only, any element count: grid-stride over 16-byte loads.
 constexpr int kFlatUnroll = 4;
 
-template <int FMT>
+template <int FMT, bool S>
 __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
   int lb;
   const QuantJob& job = pick_job(args, lb);
@@ -141,12 +139,12 @@ __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
 #pragma unroll
     for (int u = 0; u < kFlatUnroll; ++u) {
       const int64_t k = base + (int64_t)u * kQThreads;
-      v[u] = k < nvec ? xv[k] : make_uint4(0, 0, 0, 0);
+      v[u] = k < nvec ? ld16<S>(xv + k) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kFlatUnroll; ++u) {
       const int64_t k = base + (int64_t)u * kQThreads;
-      if (k < nvec) qv[k] = quant8<FMT>(v[u], sv.s32);
+      if (k < nvec) st8<S>(qv + k, quant8<FMT>(v[u], sv.s32));
     }
   }
   if (lb == 0 && tid < (int)(n & 7)) {
@@ -206,18 +204,25 @@ static hipError_t launch_fmt(QuantArgs a, hipStream_t stream) {
     const QuantPath p = path_of(a.job[j0]);
     QuantArgs sub{};
     int total = 0;
+    int64_t bytes = 0;  // read + written by this launch
     int j = j0;
     for (; j < a.njobs && path_of(a.job[j]) == p; ++j) {
       QuantJob jb = a.job[j];
       jb.nblocks = blocks_of(jb, p);
       jb.block0 = total;
       total += jb.nblocks;
+      bytes += jb.rows * jb.cols * (jb.qT ? 4 : 3);
       sub.job[sub.njobs++] = jb;
     }
-    if (p == kPathTiled)
-      hipLaunchKernelGGL(k_quant_tiled<FMT>, dim3(total), dim3(kQThreads), 0, stream, sub);
+    const bool stream_pass = bytes >= kStreamBytes;
+    if (p == kPathTiled && stream_pass)
+      hipLaunchKernelGGL((k_quant_tiled<FMT, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
+    else if (p == kPathTiled)
+      hipLaunchKernelGGL((k_quant_tiled<FMT, false>), dim3(total), dim3(kQThreads), 0, stream, sub);
+    else if (p == kPathFlat && stream_pass)
+      hipLaunchKernelGGL((k_quant_flat<FMT, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathFlat)
-      hipLaunchKernelGGL(k_quant_flat<FMT>, dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_flat<FMT, false>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else
       hipLaunchKernelGGL(k_quant_elem<FMT>, dim3(total), dim3(kQThreads), 0, stream, sub);
     hipError_t e = hipGetLastError();
