@@ -195,7 +195,8 @@ def main():
     traffic = None
     import hashlib
     src = os.path.join(ROOT, "fp8_scaled_gemm_amd", "csrc", "gemm.hip")
-    if (M, N, K) == (4096, 4096, 4096) and hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]             == GEMM_TRAFFIC["gemm_src_sha256_16"]:
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if (M, N, K) == (4096, 4096, 4096) and digest == GEMM_TRAFFIC["gemm_src_sha256_16"]:
         traffic = 1024.0 * (GEMM_TRAFFIC["fetch_kib"] * GEMM_TRAFFIC["fetch_factor"] +
                             GEMM_TRAFFIC["write_kib"] * GEMM_TRAFFIC["write_factor"])
 
