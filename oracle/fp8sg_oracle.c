@@ -406,6 +406,55 @@ ORC_API int32_t orc_unscale_check(uint16_t* g, int64_t n, float scale, int32_t f
 }
 
 /* ------------------------------------------------------------------------ */
+/* O-7b Global gradient norm for clipping after unscale [AMP-NOTES §6 and    */
+/*      MP-06 §四: clip_grad_norm_ runs on the unscaled gradients; its norm  */
+/*      is the 2-norm of all gradient elements taken together].  Exact: an   */
+/*      fp16 value is an integer times 2^-24, so its square is an integer    */
+/*      times 2^-48 below 2^80; the squares are summed as 128-bit integers.  */
+/*      out_lohi receives the sum in units of 2^-48 (low, high 64 bits).     */
+/*      Returns 0 if every value is finite, 1 if an infinity was seen and no */
+/*      NaN, 2 if a NaN was seen (the sum is then meaningless).               */
+/* ------------------------------------------------------------------------ */
+
+ORC_API int32_t orc_sumsq_f16(const uint16_t* g, int64_t n, uint64_t* out_lohi) {
+  ensure_init();
+  int nt = orc_num_threads();
+  __int128* part = (__int128*)calloc((size_t)nt, sizeof(__int128));
+  int* kind = (int*)calloc((size_t)nt, sizeof(int));
+#pragma omp parallel num_threads(nt)
+  {
+    int t = omp_get_thread_num();
+    __int128 acc = 0;
+    int k = 0;
+#pragma omp for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+      double v = dec(ORC_F16, g[i]);
+      if (isnan(v)) {
+        k = 2;
+      } else if (isinf(v)) {
+        if (k == 0) k = 1;
+      } else {
+        int64_t m = (int64_t)(fabs(v) * 16777216.0); /* |v| * 2^24, an exact integer */
+        acc += (__int128)m * (__int128)m;
+      }
+    }
+    part[t] = acc;
+    kind[t] = k;
+  }
+  __int128 total = 0;
+  int k = 0;
+  for (int t = 0; t < nt; ++t) {
+    total += part[t];
+    if (kind[t] > k) k = kind[t];
+  }
+  free(part);
+  free(kind);
+  out_lohi[0] = (uint64_t)total;
+  out_lohi[1] = (uint64_t)(total >> 64);
+  return k;
+}
+
+/* ------------------------------------------------------------------------ */
 /* O-8  GradScaler.update() state machine [PT-CH20 §20.5.33]: on a step with */
 /*      inf/NaN multiply the scale by the backoff factor and reset the       */
 /*      tracker; otherwise count the clean step and, once the count reaches  */
