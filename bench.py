@@ -228,7 +228,14 @@ def main():
         hbm["unscale_GBps"] = 4.0 * ng / (r_un["avg_us"] * 1e-6) / 1e9
         hbm["unscale_elements"] = ng
         kern["unscale_check_200_tensors"] = r_un
-        del grads
+        # the same pass with the global gradient norm (sum of squares) fused in
+        nws = torch.empty(F.amp_norm_workspace_len([g.numel() for g in grads]),
+                          dtype=torch.float32, device=dev)
+        nout = torch.empty(2, dtype=torch.float32, device=dev)
+        r_nrm = T.run(lambda: F.amp_unscale_check_norm(grads, one, fz, nws, nout), 10)
+        hbm["unscale_norm_GBps"] = 4.0 * ng / (r_nrm["avg_us"] * 1e-6) / 1e9
+        kern["unscale_check_norm_200_tensors"] = r_nrm
+        del grads, nws
         torch.cuda.empty_cache()
 
     # ---- sampled check of the step's outputs against the oracle

@@ -20,9 +20,9 @@ OUT_BF16, OUT_F16, OUT_F32 = 0, 1, 2
 AMAX_PARTS = 1024
 SCALE_REC_BYTES = 32 + 4 * AMAX_PARTS
 
-EXPORTS = ("fp8sg_status_string", "fp8sg_version", "fp8_amax", "fp8_quantize", "fp8_gemm",
-           "fp8_scaled_linear_fwd", "fp8_scaled_linear_bwd", "amp_unscale_check",
-           "amp_update_scale")
+EXPORTS = ("fp8sg_status_string", "fp8sg_version", "amp_norm_workspace_len", "fp8_amax",
+           "fp8_quantize", "fp8_gemm", "fp8_scaled_linear_fwd", "fp8_scaled_linear_bwd",
+           "amp_unscale_check", "amp_unscale_check_norm", "amp_update_scale")
 
 
 class Fp8sgError(RuntimeError):
@@ -63,7 +63,11 @@ def lib():
                                         ctypes.POINTER(_BwdWs), P, P, i, P]
     L.amp_unscale_check.argtypes = [ctypes.POINTER(P), ctypes.POINTER(i64), i32, P, P, P]
     L.amp_update_scale.argtypes = [P, P, P, f32, f32, i32, P]
-    for name in EXPORTS[2:]:
+    L.amp_norm_workspace_len.argtypes = [ctypes.POINTER(i64), i32]
+    L.amp_norm_workspace_len.restype = i64
+    L.amp_unscale_check_norm.argtypes = [ctypes.POINTER(P), ctypes.POINTER(i64), i32, P, P, P, i64,
+                                         P, P]
+    for name in EXPORTS[3:]:
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -203,6 +207,33 @@ def amp_unscale_check(grads, scale: torch.Tensor, found_inf: torch.Tensor, strea
         assert g.dtype == torch.float16 and g.is_contiguous()
     _check(lib().amp_unscale_check(ptrs, numel, n, _ptr(scale), _ptr(found_inf),
                                    _stream(stream)), "amp_unscale_check")
+
+
+def amp_norm_workspace_len(numels) -> int:
+    """fp32 slots amp_unscale_check_norm needs for tensors of these sizes."""
+    n = len(numels)
+    arr = (ctypes.c_int64 * max(n, 1))(*[int(v) for v in numels])
+    r = lib().amp_norm_workspace_len(arr, n)
+    if r < 0:
+        raise Fp8sgError(f"amp_norm_workspace_len: invalid sizes {list(numels)[:4]}...")
+    return int(r)
+
+
+def amp_unscale_check_norm(grads, scale: torch.Tensor, found_inf: torch.Tensor,
+                           workspace: torch.Tensor, sumsq_norm: torch.Tensor, stream=None):
+    """amp_unscale_check plus (sum of squares, 2-norm) of the unscaled gradients
+    into sumsq_norm (device float32[2]); workspace: device float32 scratch of at
+    least amp_norm_workspace_len([g.numel() for g in grads]) elements."""
+    n = len(grads)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[g.data_ptr() for g in grads])
+    numel = (ctypes.c_int64 * max(n, 1))(*[g.numel() for g in grads])
+    for g in grads:
+        assert g.dtype == torch.float16 and g.is_contiguous()
+    assert workspace.dtype == torch.float32 and sumsq_norm.dtype == torch.float32
+    assert sumsq_norm.numel() >= 2
+    _check(lib().amp_unscale_check_norm(ptrs, numel, n, _ptr(scale), _ptr(found_inf),
+                                        _ptr(workspace), workspace.numel(), _ptr(sumsq_norm),
+                                        _stream(stream)), "amp_unscale_check_norm")
 
 
 def amp_update_scale(scale: torch.Tensor, growth_tracker: torch.Tensor, found_inf: torch.Tensor,

@@ -167,7 +167,36 @@ fp8sg_status amp_unscale_check(uint16_t* const* grads, const int64_t* numel, int
     if (numel[i] > 0 && !grads[i]) return FP8SG_ERR_NULL;
     if (numel[i] > 0 && (reinterpret_cast<uintptr_t>(grads[i]) & 1u)) return FP8SG_ERR_ALIGN;
   }
-  return hip_status(launch_unscale_check(grads, numel, ntensors, scale, found_inf, S(stream)));
+  return hip_status(
+      launch_unscale_check(grads, numel, ntensors, scale, found_inf, nullptr, nullptr, S(stream)));
+}
+
+int64_t amp_norm_workspace_len(const int64_t* numel, int32_t ntensors) {
+  if (ntensors < 0 || ntensors > 8192 || (ntensors > 0 && !numel)) return -1;
+  for (int32_t i = 0; i < ntensors; ++i)
+    if (numel[i] < 0) return -1;
+  return unscale_blocks_bound(numel, ntensors);
+}
+
+fp8sg_status amp_unscale_check_norm(uint16_t* const* grads, const int64_t* numel,
+                                    int32_t ntensors, const float* scale, int32_t* found_inf,
+                                    float* workspace, int64_t workspace_len, float* sumsq_norm,
+                                    fp8sg_stream stream) {
+  if (!scale || !found_inf || !sumsq_norm) return FP8SG_ERR_NULL;
+  if (ntensors < 0 || ntensors > 8192) return FP8SG_ERR_SHAPE;
+  if (ntensors > 0 && (!grads || !numel)) return FP8SG_ERR_NULL;
+  for (int32_t i = 0; i < ntensors; ++i) {
+    if (numel[i] < 0) return FP8SG_ERR_SHAPE;
+    if (numel[i] > 0 && !grads[i]) return FP8SG_ERR_NULL;
+    if (numel[i] > 0 && (reinterpret_cast<uintptr_t>(grads[i]) & 1u)) return FP8SG_ERR_ALIGN;
+  }
+  const int64_t need = norm_slots(grads, numel, ntensors);
+  if (workspace_len < need) return FP8SG_ERR_SHAPE;
+  if (!workspace) return FP8SG_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(sumsq_norm) & 3u) return FP8SG_ERR_ALIGN;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 7u)) return FP8SG_ERR_ALIGN;
+  return hip_status(launch_unscale_check(grads, numel, ntensors, scale, found_inf, workspace,
+                                         sumsq_norm, S(stream)));
 }
 
 fp8sg_status amp_update_scale(float* scale, int32_t* growth_tracker, int32_t* found_inf,

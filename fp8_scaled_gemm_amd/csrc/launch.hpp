@@ -62,8 +62,15 @@ struct GemmProblem {
 hipError_t launch_gemm(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);
 
 // ---- GradScaler (amp.hip)
+// Norm workspace slots of the unscale pass for these tensors (exact; needs the
+// pointers' alignment) and an upper bound that needs only the sizes.
+int64_t norm_slots(uint16_t* const* grads, const int64_t* numel, int32_t ntensors);
+int64_t unscale_blocks_bound(const int64_t* numel, int32_t ntensors);
+// parts == nullptr: unscale + check only; otherwise also one sum-of-squares
+// slot per block in parts and the finalized (sum, norm) in sumsq_norm.
 hipError_t launch_unscale_check(uint16_t* const* grads, const int64_t* numel, int32_t ntensors,
-                                const float* scale, int32_t* found_inf, hipStream_t stream);
+                                const float* scale, int32_t* found_inf, float* parts,
+                                float* sumsq_norm, hipStream_t stream);
 hipError_t launch_update_scale(float* scale, int32_t* tracker, int32_t* found_inf, float growth,
                                float backoff, int32_t interval, hipStream_t stream);
 

@@ -200,6 +200,40 @@ FP8SG_API fp8sg_status amp_unscale_check(uint16_t* const* grads, const int64_t* 
                                const float* scale, int32_t* found_inf, fp8sg_stream stream);
 
 /*
+ * Workspace for amp_unscale_check_norm: the number of fp32 slots it needs
+ * for these element counts: one per block of 8192 elements (blocks counted
+ * with room for any 2-byte alignment of each tensor), rounded up to even, plus
+ * 512 (256 fp64 partial sums).  Host function, no device work;
+ * -1 for invalid arguments (ntensors outside 0..8192, a NULL or negative
+ * numel).
+ */
+FP8SG_API int64_t amp_norm_workspace_len(const int64_t* numel, int32_t ntensors);
+
+/*
+ * amp_unscale_check plus the global 2-norm of the unscaled gradients, in the
+ * same pass [AMP-NOTES §6 and MP-06 §四: gradient clipping must run after
+ * unscale; clip_grad_norm_ takes the 2-norm of all gradient elements
+ * together].  Every stored unscaled value g' contributes g'^2 (exact in fp32
+ * for fp16 values); the squares are summed in fp32 in a fixed order (8 per
+ * 16-byte load, 4 loads per thread, then a fixed tree over each block of 8192
+ * elements) into one slot of `workspace` per block; two small kernels add the
+ * slots in fp64 in a fixed order.  Results are identical from run to run,
+ * within 20 * 2^-24 (relative) of the exact sum of squares.
+ *   workspace: device float[workspace_len], 8-byte aligned, caller-owned
+ *              scratch of at least amp_norm_workspace_len(numel, ntensors)
+ *              slots (FP8SG_ERR_SHAPE if too short); its contents on return
+ *              are unspecified.
+ *   sumsq_norm: device float[2], written: [0] = sum of squares rounded to
+ *              fp32, [1] = its square root (taken in fp64, rounded to fp32).
+ *              Both are inf or NaN when a stored value is (found_inf is set).
+ * The other arguments and the unscale/check behave as in amp_unscale_check.
+ */
+FP8SG_API fp8sg_status amp_unscale_check_norm(uint16_t* const* grads, const int64_t* numel,
+                                    int32_t ntensors, const float* scale, int32_t* found_inf,
+                                    float* workspace, int64_t workspace_len, float* sumsq_norm,
+                                    fp8sg_stream stream);
+
+/*
  * GradScaler.update() [PT-CH20 §20.5.33], on the device:
  *   if *found_inf: *scale *= backoff_factor; *growth_tracker = 0
  *   else: ++*growth_tracker; if it reaches growth_interval:

@@ -113,6 +113,28 @@ def test_amp_validation():
     assert L.amp_update_scale(P(0), P(A16), P(A16), 2.0, 0.5, 10, P(0)) == ENULL
 
 
+def test_norm_workspace_and_validation():
+    L = F.lib()
+    n = (ctypes.c_int64 * 3)(8192, 8193, 0)
+    # ceil((numel + 7) / 8192) blocks per non-empty tensor (2 + 2 + 0), even, + 512
+    assert L.amp_norm_workspace_len(n, 3) == 4 + 512
+    n[2] = -1
+    assert L.amp_norm_workspace_len(n, 3) == -1
+    assert L.amp_norm_workspace_len(n, 9000) == -1
+    ptrs = (ctypes.c_void_p * 2)(A16, A16 + 2)
+    numel = (ctypes.c_int64 * 2)(8192, 8)
+    need = 2 + 512  # the first tensor is aligned (one block), the second needs one more
+    args = lambda ws_len, sn=A16, ws=A16: (ptrs, numel, 2, P(A16), P(A16), P(ws), ws_len, P(sn),
+                                           P(0))
+    assert L.amp_unscale_check_norm(*args(need - 1)) == ESHAPE
+    assert L.amp_unscale_check_norm(*args(need, sn=0)) == ENULL
+    assert L.amp_unscale_check_norm(*args(need, ws=0)) == ENULL
+    assert L.amp_unscale_check_norm(*args(need, ws=A16 + 4)) == EALIGN
+    assert L.amp_unscale_check_norm(*args(need, sn=A16 + 2)) == EALIGN
+    ptrs[1] = A16 + 1
+    assert L.amp_unscale_check_norm(*args(need)) == EALIGN
+
+
 def test_binding_refuses_a_missing_library(monkeypatch, tmp_path):
     # no fallback path: without the built library the binding raises
     monkeypatch.setattr(F, "_lib", None)
