@@ -64,6 +64,9 @@ def lib():
     L.orc_unscale_check.restype = i32
     L.orc_update_scale.argtypes = [P, P, i32, f32, f32, i32]
     L.orc_sumsq_f16.argtypes = [P, i64, ctypes.POINTER(ctypes.c_uint64)]
+    L.orc_hist_amax.argtypes = [P, i32]
+    L.orc_hist_amax.restype = u32
+    L.orc_hist_push.argtypes = [P, i32, u32]
     L.orc_sumsq_f16.restype = i32
     _lib = L
     return L
@@ -177,6 +180,36 @@ def to_fp8(x_bf16: np.ndarray, fmt: int, with_transpose: bool = True) -> Quantiz
     q = quantize(x_bf16, fmt, sc.scale32)
     qT = transpose(q) if (with_transpose and q.ndim == 2) else None
     return Quantized(q, qT, sc)
+
+
+@dataclass
+class DelayedQuantized:
+    """One delayed-scaling cast [PT-CH20 §20.5.9]: codes and their transposed
+    copy, the scale state taken from the history (sc), the current tensor's
+    amax (fp32 bits) and the history after the current amax was pushed."""
+    q: np.ndarray
+    qT: np.ndarray
+    sc: Scale
+    amax_bits: int
+    hist: np.ndarray
+
+
+def hist_amax(hist: np.ndarray) -> int:
+    h = np.ascontiguousarray(hist, dtype=np.float32)
+    return int(lib().orc_hist_amax(_p(h), h.size))
+
+
+def to_fp8_delayed(x_bf16: np.ndarray, fmt: int, hist: np.ndarray,
+                   with_transpose: bool = True) -> DelayedQuantized:
+    """Delayed scaling [PT-CH20 §20.5.9]: scale from the largest amax of the
+    history (earlier steps), cast with it, then push the current amax."""
+    sc = scale_from_amax(hist_amax(hist), fmt)
+    q = quantize(x_bf16, fmt, sc.scale32)
+    qT = transpose(q) if (with_transpose and q.ndim == 2) else None
+    cur = amax_bits(x_bf16)
+    new = np.array(hist, dtype=np.float32, copy=True)
+    lib().orc_hist_push(_p(new), new.size, cur)
+    return DelayedQuantized(q, qT, sc, cur, new)
 
 
 # ---------------------------------------------------------------- GEMM (O-6)

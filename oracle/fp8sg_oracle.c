@@ -382,6 +382,34 @@ ORC_API void orc_gemm_absdot_at(const uint8_t* A, int fa, const uint8_t* B, int 
 }
 
 /* ------------------------------------------------------------------------ */
+/* O-4b Delayed scaling [PT-CH20 §20.5.9: each FP8 op keeps an amax history   */
+/*      of its input; every step takes the scale from the amax of earlier    */
+/*      steps, casts with it, and records the current amax].  The history is */
+/*      a float array, most recent first.  The scale is O-3 applied to the   */
+/*      largest history entry (NaN if any entry is NaN); after the cast the  */
+/*      current amax is pushed in front and the oldest entry drops out.      */
+/* ------------------------------------------------------------------------ */
+
+ORC_API uint32_t orc_hist_amax(const float* hist, int32_t h) {
+  double best = 0.0;
+  for (int32_t i = 0; i < h; ++i) {
+    double v = (double)hist[i];
+    if (isnan(v)) return 0x7FC00000u;
+    if (v > best) best = v;
+  }
+  return f32_bits((float)best);
+}
+
+ORC_API void orc_hist_push(float* hist, int32_t h, uint32_t amax_bits) {
+  for (int32_t i = h - 1; i > 0; --i) hist[i] = hist[i - 1];
+  if (h > 0) {
+    float a;
+    memcpy(&a, &amax_bits, 4);
+    hist[0] = a;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* O-7  GradScaler unscale + non-finite check                                */
 /*      [PT-CH20 §20.2.2: unscale the gradients (divide by the scale), then  */
 /*      check for inf/NaN; AMP-NOTES §4 steps 3-4].  In place on fp16        */
