@@ -162,6 +162,27 @@ def main():
     gemm_flops = 3 * 2.0 * M * N * K
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
 
+    # ---- the same step with delayed scaling of x, W and gy (history of 16)
+    hx, hw, hg = (torch.ones(16, dtype=torch.float32, device=dev) for _ in range(3))
+
+    def step_delayed():
+        F.fp8_scaled_linear_fwd_delayed(x, w, saved, hx, hw, y, F.OUT_BF16)
+        F.fp8_scaled_linear_bwd_delayed(gy, saved, ws, hg, gx, gw, F.OUT_F16)
+        F.amp_unscale_check([gx, gw], scale, found)
+        F.amp_update_scale(scale, tracker, found, 2.0, 0.5, 2000)
+
+    for _ in range(args.warmup):
+        step_delayed()
+    torch.cuda.synchronize()
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for _ in range(args.steps):
+        step_delayed()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    ms_delayed = d0.elapsed_time(d1) / args.steps
+
     # ---- per-kernel timings on the same stream, same operands as the step
     log("per-kernel timings")
     T = Timer(torch, stream)
@@ -219,7 +240,14 @@ def main():
         hbm["amax_plus_quantize_GBps"] = 5.0 * nb / ((r_amax["avg_us"] + r_quant["avg_us"]) * 1e-6) / 1e9
         kern["amax_2p28"] = r_amax
         kern["quantize_2p28"] = r_quant
-        del big, bq
+        # delayed scaling: one pass (scale from the history, current amax reduced
+        # on the way): 2 B read + 1 B written per element
+        amax_big = float(np.array([brec.read()["amax_bits"]], np.uint32).view(np.float32)[0])
+        bh = torch.full((16,), amax_big, dtype=torch.float32, device=dev)
+        r_del = T.run(lambda: F.fp8_quantize_delayed(big, F.E4M3FN, brec, bh, bq), 10)
+        hbm["quantize_delayed_GBps"] = 3.0 * nb / (r_del["avg_us"] * 1e-6) / 1e9
+        kern["quantize_delayed_2p28"] = r_del
+        del big, bq, bh
         log("HBM-scale unscale pass")
         sizes = C.scaler_sizes()
         grads = [(torch.randn(int(n), device=dev) * 0.5).half() for n in sizes]
@@ -269,6 +297,9 @@ def main():
                    "W": "bf16 N(0,0.02)", "gy": "bf16 N(0,1e-4) x loss scale 65536",
                    "y": "bf16", "grads": "fp16", "formats": "e4m3fn x/W, e5m2 gy"},
         "step_pct_of_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "step_delayed_scaling": {"ms_per_step": round(ms_delayed, 4),
+                                 "TFLOPs": round(gemm_flops / (ms_delayed * 1e-3) / 1e12, 2),
+                                 "history": 16},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,

@@ -21,8 +21,10 @@ AMAX_PARTS = 1024
 SCALE_REC_BYTES = 32 + 4 * AMAX_PARTS
 
 EXPORTS = ("fp8sg_status_string", "fp8sg_version", "amp_norm_workspace_len", "fp8_amax",
-           "fp8_quantize", "fp8_gemm", "fp8_scaled_linear_fwd", "fp8_scaled_linear_bwd",
+           "fp8_quantize", "fp8_quantize_delayed", "fp8_gemm", "fp8_scaled_linear_fwd",
+           "fp8_scaled_linear_fwd_delayed", "fp8_scaled_linear_bwd", "fp8_scaled_linear_bwd_delayed",
            "amp_unscale_check", "amp_unscale_check_norm", "amp_update_scale")
+MAX_HISTORY = 1024
 
 
 class Fp8sgError(RuntimeError):
@@ -57,10 +59,15 @@ def lib():
     L.fp8sg_version.restype = i
     L.fp8_amax.argtypes = [P, i64, P, P]
     L.fp8_quantize.argtypes = [P, i64, i64, i, P, P, P, P]
+    L.fp8_quantize_delayed.argtypes = [P, i64, i64, i, P, i32, P, P, P, P]
     L.fp8_gemm.argtypes = [P, i, P, i, P, P, P, i, i64, i64, i64, P]
     L.fp8_scaled_linear_fwd.argtypes = [P, P, i64, i64, i64, ctypes.POINTER(_Saved), P, i, P]
     L.fp8_scaled_linear_bwd.argtypes = [P, ctypes.POINTER(_Saved), i64, i64, i64,
                                         ctypes.POINTER(_BwdWs), P, P, i, P]
+    L.fp8_scaled_linear_fwd_delayed.argtypes = [P, P, i64, i64, i64, ctypes.POINTER(_Saved), P, P,
+                                                i32, P, i, P]
+    L.fp8_scaled_linear_bwd_delayed.argtypes = [P, ctypes.POINTER(_Saved), i64, i64, i64,
+                                                ctypes.POINTER(_BwdWs), P, i32, P, P, i, P]
     L.amp_unscale_check.argtypes = [ctypes.POINTER(P), ctypes.POINTER(i64), i32, P, P, P]
     L.amp_update_scale.argtypes = [P, P, P, f32, f32, i32, P]
     L.amp_norm_workspace_len.argtypes = [ctypes.POINTER(i64), i32]
@@ -139,6 +146,27 @@ def fp8_quantize(x: torch.Tensor, fmt: int, rec: ScaleRec, q: torch.Tensor,
                               _ptr(qT), _stream(stream)), "fp8_quantize")
 
 
+def _hist(h: torch.Tensor):
+    assert h.dtype == torch.float32 and h.is_contiguous() and 1 <= h.numel() <= MAX_HISTORY
+    return h.numel()
+
+
+def fp8_quantize_delayed(x: torch.Tensor, fmt: int, rec: ScaleRec, hist: torch.Tensor,
+                         q: torch.Tensor, qT: torch.Tensor = None, stream=None):
+    """Delayed scaling: scale from the largest entry of the amax history hist
+    (device float32, most recent first), codes q (and qT), then rec.amax =
+    max |x| pushed to the front of hist."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    rows, cols = (x.shape[0], x.numel() // max(x.shape[0], 1)) if x.dim() >= 2 else (1, x.numel())
+    assert q.dtype == torch.uint8 and q.numel() == x.numel()
+    if qT is not None:
+        assert qT.dtype == torch.uint8 and qT.numel() == x.numel()
+    h = _hist(hist)
+    _check(lib().fp8_quantize_delayed(_ptr(x), rows, cols, fmt, _ptr(hist), h,
+                                      ctypes.c_void_p(rec.ptr), _ptr(q), _ptr(qT),
+                                      _stream(stream)), "fp8_quantize_delayed")
+
+
 def fp8_gemm(A: torch.Tensor, fa: int, B: torch.Tensor, fb: int, inv_a_ptr: int, inv_b_ptr: int,
              C: torch.Tensor, out: int, stream=None):
     """C[M,N] = A[M,K] . B[N,K]^T * fl32(inv_a * inv_b); inv_*_ptr are device double addresses."""
@@ -196,6 +224,30 @@ def fp8_scaled_linear_bwd(gy, saved: LinearSaved, ws: LinearBwdWs, gx, gw, out: 
     _check(lib().fp8_scaled_linear_bwd(_ptr(gy), ctypes.byref(s), M, N, K, ctypes.byref(b),
                                        _ptr(gx), _ptr(gw), out, _stream(stream)),
            "fp8_scaled_linear_bwd")
+
+
+def fp8_scaled_linear_fwd_delayed(x, w, saved: LinearSaved, hist_x, hist_w, y,
+                                  out: int = OUT_BF16, stream=None):
+    M, K = x.shape
+    N = w.shape[0]
+    h = _hist(hist_x)
+    assert _hist(hist_w) == h
+    s = saved.struct()
+    _check(lib().fp8_scaled_linear_fwd_delayed(_ptr(x), _ptr(w), M, N, K, ctypes.byref(s),
+                                               _ptr(hist_x), _ptr(hist_w), h, _ptr(y), out,
+                                               _stream(stream)), "fp8_scaled_linear_fwd_delayed")
+
+
+def fp8_scaled_linear_bwd_delayed(gy, saved: LinearSaved, ws: LinearBwdWs, hist_gy, gx, gw,
+                                  out: int = OUT_BF16, stream=None):
+    M, N = gy.shape
+    K = saved.x_q.shape[1]
+    s = saved.struct()
+    b = ws.struct()
+    _check(lib().fp8_scaled_linear_bwd_delayed(_ptr(gy), ctypes.byref(s), M, N, K, ctypes.byref(b),
+                                               _ptr(hist_gy), _hist(hist_gy), _ptr(gx), _ptr(gw),
+                                               out, _stream(stream)),
+           "fp8_scaled_linear_bwd_delayed")
 
 
 def amp_unscale_check(grads, scale: torch.Tensor, found_inf: torch.Tensor, stream=None):

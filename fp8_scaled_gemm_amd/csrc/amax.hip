@@ -25,13 +25,6 @@ namespace fp8sg {
 constexpr int kAmaxThreads = 256;
 constexpr int kAmaxUnroll = 4;  // 16-byte loads in flight per thread per iteration
 
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pmax(uint32_t a, uint32_t b) {
-  us2 r = __builtin_elementwise_max(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b));
-  return __builtin_bit_cast(uint32_t, r);
-}
-
 template <bool S>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax(AmaxArgs args) {
   int j = 0;

@@ -21,6 +21,8 @@ bool out_ok(int o) { return o == FP8SG_OUT_BF16 || o == FP8SG_OUT_F16 || o == FP
 bool dims16(int64_t v) { return v >= 0 && (v % 16) == 0; }
 bool dims16_pos(int64_t v) { return v > 0 && (v % 16) == 0; }
 fp8sg_status hip_status(hipError_t e) { return e == hipSuccess ? FP8SG_OK : FP8SG_ERR_HIP; }
+bool hist_len_ok(int32_t h) { return h >= 1 && h <= FP8SG_MAX_HISTORY; }
+bool hist_ok(const float* h) { return h && (reinterpret_cast<uintptr_t>(h) & 3u) == 0; }
 hipStream_t S(fp8sg_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
 fp8sg_status check_gemm(const void* A, int fa, const void* B, int fb, const void* ia,
@@ -82,6 +84,22 @@ fp8sg_status fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, fp8sg_f
   return hip_status(launch_quantize(a, fmt, S(stream)));
 }
 
+fp8sg_status fp8_quantize_delayed(const uint16_t* x, int64_t rows, int64_t cols,
+                                  fp8sg_format fmt, float* amax_history, int32_t history_len,
+                                  fp8sg_scale_rec* rec, uint8_t* q, uint8_t* qT,
+                                  fp8sg_stream stream) {
+  if (!rec || !amax_history) return FP8SG_ERR_NULL;
+  if (!fmt_ok(fmt)) return FP8SG_ERR_FORMAT;
+  if (rows < 0 || cols < 0 || !hist_len_ok(history_len)) return FP8SG_ERR_SHAPE;
+  if (rows * cols > 0 && (!x || !q)) return FP8SG_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || (qT && !aligned16(qT))) return FP8SG_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(amax_history) & 3u) return FP8SG_ERR_ALIGN;
+  QuantArgs a{};
+  a.job[0] = QuantJob{x, rows, cols, rec, q, qT, 0, 0, 0, amax_history, history_len};
+  a.njobs = 1;
+  return hip_status(launch_quantize(a, fmt, S(stream)));
+}
+
 fp8sg_status fp8_gemm(const uint8_t* A, fp8sg_format fa, const uint8_t* B, fp8sg_format fb,
                       const double* inv_a, const double* inv_b, void* C, fp8sg_out out,
                       int64_t M, int64_t N, int64_t Kc, fp8sg_stream stream) {
@@ -91,29 +109,42 @@ fp8sg_status fp8_gemm(const uint8_t* A, fp8sg_format fa, const uint8_t* B, fp8sg
   return hip_status(launch_gemm(p, fa, fb, out, S(stream)));
 }
 
-// Forward [FP8-TRAIN §4 forward, §6]: one amax launch over x and W, one
-// quantize launch writing codes and transposed copies of both, one GEMM.
-fp8sg_status fp8_scaled_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
-                                   int64_t K, const fp8_linear_saved* saved, void* y,
-                                   fp8sg_out out, fp8sg_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// Forward [FP8-TRAIN §4 forward, §6]: codes and transposed copies of x and W
+// (dynamic: one amax launch over both, then one quantize launch; delayed: one
+// quantize launch that also reduces the current amax, then the history push),
+// then one GEMM.
+fp8sg_status linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K,
+                        const fp8_linear_saved* saved, float* hist_x, float* hist_w,
+                        int32_t hist_len, void* y, fp8sg_out out, fp8sg_stream stream) {
   if (!x || !w || !y) return FP8SG_ERR_NULL;
   fp8sg_status st = check_saved(saved);
   if (st != FP8SG_OK) return st;
   if (!out_ok(out)) return FP8SG_ERR_FORMAT;
   if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K)) return FP8SG_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return FP8SG_ERR_ALIGN;
+  const bool delayed = hist_x || hist_w;
+  if (delayed) {
+    if (!hist_x || !hist_w) return FP8SG_ERR_NULL;
+    if (!hist_len_ok(hist_len)) return FP8SG_ERR_SHAPE;
+    if (!hist_ok(hist_x) || !hist_ok(hist_w)) return FP8SG_ERR_ALIGN;
+  }
   hipStream_t s = S(stream);
-
-  AmaxArgs am{};
-  am.job[0] = AmaxJob{x, M * K, saved->x_sc, 0, amax_blocks_for(M * K)};
-  am.job[1] = AmaxJob{w, N * K, saved->w_sc, 0, amax_blocks_for(N * K)};
-  am.njobs = 2;
-  hipError_t e = launch_amax(am, false, s);
-  if (e != hipSuccess) return FP8SG_ERR_HIP;
-
+  hipError_t e;
+  if (!delayed) {
+    AmaxArgs am{};
+    am.job[0] = AmaxJob{x, M * K, saved->x_sc, 0, amax_blocks_for(M * K)};
+    am.job[1] = AmaxJob{w, N * K, saved->w_sc, 0, amax_blocks_for(N * K)};
+    am.njobs = 2;
+    e = launch_amax(am, false, s);
+    if (e != hipSuccess) return FP8SG_ERR_HIP;
+  }
   QuantArgs qa{};
-  qa.job[0] = QuantJob{x, M, K, saved->x_sc, saved->x_q, saved->x_qT, 0, 0, 0};
-  qa.job[1] = QuantJob{w, N, K, saved->w_sc, saved->w_q, saved->w_qT, 0, 0, 0};
+  qa.job[0] = QuantJob{x, M, K, saved->x_sc, saved->x_q, saved->x_qT, 0, 0, 0, hist_x, hist_len};
+  qa.job[1] = QuantJob{w, N, K, saved->w_sc, saved->w_q, saved->w_qT, 0, 0, 0, hist_w, hist_len};
   qa.njobs = 2;
   e = launch_quantize(qa, FP8SG_E4M3FN, s);
   if (e != hipSuccess) return FP8SG_ERR_HIP;
@@ -124,9 +155,9 @@ fp8sg_status fp8_scaled_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t
 
 // Backward [FP8-TRAIN §4 backward]: gy -> e5m2 codes + transposed copy, then
 // dgrad (gy_q [M,N] x w_qT [K,N]^T) and wgrad (gy_qT [N,M] x x_qT [K,M]^T).
-fp8sg_status fp8_scaled_linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved,
-                                   int64_t M, int64_t N, int64_t K, const fp8_linear_bwd_ws* ws,
-                                   void* gx, void* gw, fp8sg_out out, fp8sg_stream stream) {
+fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64_t M, int64_t N,
+                        int64_t K, const fp8_linear_bwd_ws* ws, float* hist_gy, int32_t hist_len,
+                        void* gx, void* gw, fp8sg_out out, fp8sg_stream stream) {
   if (!gy || !ws || !gx || !gw) return FP8SG_ERR_NULL;
   fp8sg_status st = check_saved(saved);
   if (st != FP8SG_OK) return st;
@@ -136,16 +167,21 @@ fp8sg_status fp8_scaled_linear_bwd(const uint16_t* gy, const fp8_linear_saved* s
   if (!aligned16(gy) || !aligned16(gx) || !aligned16(gw) || !aligned16(ws->gy_q) ||
       !aligned16(ws->gy_qT))
     return FP8SG_ERR_ALIGN;
+  if (hist_gy) {
+    if (!hist_len_ok(hist_len)) return FP8SG_ERR_SHAPE;
+    if (!hist_ok(hist_gy)) return FP8SG_ERR_ALIGN;
+  }
   hipStream_t s = S(stream);
-
-  AmaxArgs am{};
-  am.job[0] = AmaxJob{gy, M * N, ws->gy_sc, 0, amax_blocks_for(M * N)};
-  am.njobs = 1;
-  hipError_t e = launch_amax(am, false, s);
-  if (e != hipSuccess) return FP8SG_ERR_HIP;
-
+  hipError_t e;
+  if (!hist_gy) {
+    AmaxArgs am{};
+    am.job[0] = AmaxJob{gy, M * N, ws->gy_sc, 0, amax_blocks_for(M * N)};
+    am.njobs = 1;
+    e = launch_amax(am, false, s);
+    if (e != hipSuccess) return FP8SG_ERR_HIP;
+  }
   QuantArgs qa{};
-  qa.job[0] = QuantJob{gy, M, N, ws->gy_sc, ws->gy_q, ws->gy_qT, 0, 0, 0};
+  qa.job[0] = QuantJob{gy, M, N, ws->gy_sc, ws->gy_q, ws->gy_qT, 0, 0, 0, hist_gy, hist_len};
   qa.njobs = 1;
   e = launch_quantize(qa, FP8SG_E5M2, s);
   if (e != hipSuccess) return FP8SG_ERR_HIP;
@@ -155,6 +191,39 @@ fp8sg_status fp8_scaled_linear_bwd(const uint16_t* gy, const fp8_linear_saved* s
   if (e != hipSuccess) return FP8SG_ERR_HIP;
   GemmProblem wg{ws->gy_qT, saved->x_qT, gw, &ws->gy_sc->inv, &saved->x_sc->inv, N, K, M};
   return hip_status(launch_gemm(wg, FP8SG_E5M2, FP8SG_E4M3FN, out, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8sg_status fp8_scaled_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
+                                   int64_t K, const fp8_linear_saved* saved, void* y,
+                                   fp8sg_out out, fp8sg_stream stream) {
+  return linear_fwd(x, w, M, N, K, saved, nullptr, nullptr, 0, y, out, stream);
+}
+
+fp8sg_status fp8_scaled_linear_fwd_delayed(const uint16_t* x, const uint16_t* w, int64_t M,
+                                           int64_t N, int64_t K, const fp8_linear_saved* saved,
+                                           float* hist_x, float* hist_w, int32_t history_len,
+                                           void* y, fp8sg_out out, fp8sg_stream stream) {
+  if (!hist_x || !hist_w) return FP8SG_ERR_NULL;
+  return linear_fwd(x, w, M, N, K, saved, hist_x, hist_w, history_len, y, out, stream);
+}
+
+fp8sg_status fp8_scaled_linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved,
+                                   int64_t M, int64_t N, int64_t K, const fp8_linear_bwd_ws* ws,
+                                   void* gx, void* gw, fp8sg_out out, fp8sg_stream stream) {
+  return linear_bwd(gy, saved, M, N, K, ws, nullptr, 0, gx, gw, out, stream);
+}
+
+fp8sg_status fp8_scaled_linear_bwd_delayed(const uint16_t* gy, const fp8_linear_saved* saved,
+                                           int64_t M, int64_t N, int64_t K,
+                                           const fp8_linear_bwd_ws* ws, float* hist_gy,
+                                           int32_t history_len, void* gx, void* gw,
+                                           fp8sg_out out, fp8sg_stream stream) {
+  if (!hist_gy) return FP8SG_ERR_NULL;
+  return linear_bwd(gy, saved, M, N, K, ws, hist_gy, history_len, gx, gw, out, stream);
 }
 
 fp8sg_status amp_unscale_check(uint16_t* const* grads, const int64_t* numel, int32_t ntensors,

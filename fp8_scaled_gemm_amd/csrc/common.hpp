@@ -145,6 +145,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
   uint32_t r = red[0];
 #pragma unroll
   for (int w = 1; w < NT / kWave; ++w) r = red[w] > r ? red[w] : r;
+  __syncthreads();  // the next call may reuse red[]
   return r;
 }
 
@@ -159,6 +160,42 @@ __device__ __forceinline__ float amax_from_partials(const fp8sg_scale_rec* rec) 
   for (uint32_t i = threadIdx.x; i < np; i += NT) {
     const uint32_t v = rec->_part[i];
     m = v > m ? v : m;
+  }
+  return __uint_as_float(block_max_u32<NT>(m));
+}
+
+// |x| max over bf16 pairs: packed 16-bit max of the bit patterns with the sign
+// cleared (integer order = numeric order for non-negative IEEE values, every
+// NaN above +inf).
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pmax(uint32_t a, uint32_t b) {
+  us2 r = __builtin_elementwise_max(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b));
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint32_t absmax8(uint32_t m, uint4 v) {
+  constexpr uint32_t mask = 0x7FFF7FFFu;
+  m = pmax(m, v.x & mask);
+  m = pmax(m, v.y & mask);
+  m = pmax(m, v.z & mask);
+  return pmax(m, v.w & mask);
+}
+// packed pair max -> fp32 bits of the larger magnitude, NaN made canonical
+__device__ __forceinline__ uint32_t absmax_bits(uint32_t m) {
+  const uint32_t code = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
+  const uint32_t bits = code << 16;
+  return bits > 0x7F800000u ? 0x7FC00000u : bits;
+}
+
+// Largest entry of an amax history (fp32, most recent first): NaN if any
+// entry is NaN; negative entries count as 0.  Every thread gets the result.
+template <int NT>
+__device__ __forceinline__ float hist_amax(const float* hist, int32_t h) {
+  uint32_t m = 0;
+  for (int32_t i = threadIdx.x; i < h; i += NT) {
+    uint32_t b = __float_as_uint(hist[i]);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) b = 0x7FC00000u;
+    else if (b >> 31) b = 0;
+    m = b > m ? b : m;
   }
   return __uint_as_float(block_max_u32<NT>(m));
 }

@@ -40,6 +40,8 @@ struct QuantJob {
   int32_t block0;   // filled by the launcher
   int32_t nblocks;
   int32_t tiles_c;  // tiled path: tiles along cols
+  float* hist;      // delayed scaling: amax history (most recent first), or null
+  int32_t hist_len;
 };
 struct QuantArgs {
   QuantJob job[kMaxQuantJobs];

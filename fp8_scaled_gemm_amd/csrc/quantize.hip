@@ -16,6 +16,15 @@
 // banks), transposed in 4x4-byte blocks with byte permutes, and stored to qT
 // with 16-byte stores, 8 lanes per 128-byte row segment.  HBM traffic is the
 // algorithmic 2 B read + 1 B + 1 B written per element.
+//
+// Delayed scaling [PT-CH20 §20.5.9: each FP8 op keeps an amax history of its
+// input; the scale comes from the amax of earlier steps]: with a history the
+// blocks take the scale from the history's largest entry instead of the amax
+// kernel's partials, and each block also reduces |x| over what it loaded and
+// stores the result in its own partial slot of the record (at most
+// FP8SG_AMAX_PARTS blocks per tensor; the tiled blocks then loop over tiles).
+// k_hist_push then reduces those partials into rec->amax and pushes it to the
+// front of the history.  One pass over x instead of two.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -42,6 +51,40 @@ __device__ __forceinline__ void write_scale_fields(fp8sg_scale_rec* rec, float a
   rec->inv32 = v.inv32;
 }
 
+// The scale of a job: from the amax kernel's partials, or (DELAYED) from the
+// largest entry of the job's amax history.
+template <bool DELAYED>
+__device__ __forceinline__ float job_amax(const QuantJob& job) {
+  if constexpr (DELAYED) return hist_amax<kQThreads>(job.hist, job.hist_len);
+  else return amax_from_partials<kQThreads>(job.rec);
+}
+
+// DELAYED: this block's |x| maximum (packed pair max m) into its partial slot.
+template <bool DELAYED>
+__device__ __forceinline__ void store_block_amax(const QuantJob& job, int lb, uint32_t m) {
+  if constexpr (DELAYED) {
+    const uint32_t bits = block_max_u32<kQThreads>(absmax_bits(m));
+    if (threadIdx.x == 0) {
+      job.rec->_part[lb] = bits;
+      if (lb == 0) job.rec->_nparts = (uint32_t)job.nblocks;
+    }
+  }
+}
+
+// DELAYED writes the scale fields only: rec->amax is the current tensor's,
+// published by k_hist_push.
+template <bool DELAYED>
+__device__ __forceinline__ void publish_scale(fp8sg_scale_rec* rec, float amax, const ScaleVals& v) {
+  if constexpr (DELAYED) {
+    rec->scale = v.s;
+    rec->inv = v.inv;
+    rec->scale32 = v.s32;
+    rec->inv32 = v.inv32;
+  } else {
+    write_scale_fields(rec, amax, v);
+  }
+}
+
 // LDS tile: 128 rows x 32 dwords; dword column x of row r lives at x ^ swz(r).
 __device__ __forceinline__ int swz(int r) { return ((r >> 4) & 3) << 3; }
 
@@ -59,75 +102,83 @@ __device__ __forceinline__ void tr4x4(uint32_t d0, uint32_t d1, uint32_t d2, uin
   o3 = __builtin_amdgcn_perm(f1, e1, 0x07060302u);
 }
 
-template <int FMT, bool S>
+template <int FMT, bool S, bool DELAYED>
 __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
   int lb;
   const QuantJob& job = pick_job(args, lb);
   const int tid = threadIdx.x;
-  const float amax = amax_from_partials<kQThreads>(job.rec);
+  const float amax = job_amax<DELAYED>(job);
   const ScaleVals sv = scale_from_amax(amax, FMT);
-  if (lb == 0 && tid == 0) write_scale_fields(job.rec, amax, sv);
+  if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
 
   const int64_t rows = job.rows, cols = job.cols;
-  const int64_t r_tile = (int64_t)(lb / job.tiles_c) * kQTile;
-  const int64_t c_tile = (int64_t)(lb % job.tiles_c) * kQTile;
-
+  const int64_t ntiles = (int64_t)((rows + kQTile - 1) / kQTile) * job.tiles_c;
   __shared__ uint32_t lds[kQTile * 32];
+  uint32_t am = 0;  // DELAYED: packed |x| max of everything this block loaded
 
-  // phase 1: 16 lanes per row (8 elements each), 16 rows per pass, 8 passes
-  const int c8 = tid & 15;
-  const int r0 = tid >> 4;
-  const int64_t gc = c_tile + 8 * c8;
-  const bool col_ok = gc < cols;  // cols % 16 == 0: a group of 8 is all in or all out
-  uint4 v[8];
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int64_t gr = r_tile + r0 + 16 * p;
-    v[p] = (col_ok && gr < rows) ? ld16<S>(job.x + gr * cols + gc) : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int r = r0 + 16 * p;
-    const int64_t gr = r_tile + r;
-    const uint2 c = quant8<FMT>(v[p], sv.s32);
-    if (col_ok && gr < rows) st8<S>(job.q + gr * cols + gc, c);
-    *reinterpret_cast<uint2*>(&lds[r * 32 + ((2 * c8) ^ swz(r))]) = c;
-  }
-  __syncthreads();
+  for (int64_t tile = lb; tile < ntiles; tile += job.nblocks) {
+    const int64_t r_tile = (tile / job.tiles_c) * kQTile;
+    const int64_t c_tile = (tile % job.tiles_c) * kQTile;
 
-  // phase 2: lane owns tile columns 4cq..4cq+3 and tile rows 16rq..16rq+15
-  const int cq = tid >> 3;
-  const int rq = tid & 7;
-  uint32_t d[16];
+    // phase 1: 16 lanes per row (8 elements each), 16 rows per pass, 8 passes
+    const int c8 = tid & 15;
+    const int r0 = tid >> 4;
+    const int64_t gc = c_tile + 8 * c8;
+    const bool col_ok = gc < cols;  // cols % 16 == 0: a group of 8 is all in or all out
+    uint4 v[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = 16 * rq + i;
-    d[i] = lds[r * 32 + (cq ^ swz(r))];
+    for (int p = 0; p < 8; ++p) {
+      const int64_t gr = r_tile + r0 + 16 * p;
+      v[p] = (col_ok && gr < rows) ? ld16<S>(job.x + gr * cols + gc) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int r = r0 + 16 * p;
+      const int64_t gr = r_tile + r;
+      if constexpr (DELAYED) am = absmax8(am, v[p]);
+      const uint2 c = quant8<FMT>(v[p], sv.s32);
+      if (col_ok && gr < rows) st8<S>(job.q + gr * cols + gc, c);
+      *reinterpret_cast<uint2*>(&lds[r * 32 + ((2 * c8) ^ swz(r))]) = c;
+    }
+    __syncthreads();
+
+    // phase 2: lane owns tile columns 4cq..4cq+3 and tile rows 16rq..16rq+15
+    const int cq = tid >> 3;
+    const int rq = tid & 7;
+    uint32_t d[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * rq + i;
+      d[i] = lds[r * 32 + (cq ^ swz(r))];
+    }
+    uint32_t o[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      tr4x4(d[4 * b], d[4 * b + 1], d[4 * b + 2], d[4 * b + 3], o[0][b], o[1][b], o[2][b], o[3][b]);
+    const int64_t tr0 = r_tile + 16 * rq;
+    const int64_t tc0 = c_tile + 4 * cq;
+    if (tr0 < rows && tc0 < cols) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        st16<S>(job.qT + (tc0 + j) * rows + tr0, make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]));
+    }
+    if (tile + job.nblocks < ntiles) __syncthreads();  // the next tile reuses lds
   }
-  uint32_t o[4][4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-    tr4x4(d[4 * b], d[4 * b + 1], d[4 * b + 2], d[4 * b + 3], o[0][b], o[1][b], o[2][b], o[3][b]);
-  const int64_t tr0 = r_tile + 16 * rq;
-  const int64_t tc0 = c_tile + 4 * cq;
-  if (tr0 < rows && tc0 < cols) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      st16<S>(job.qT + (tc0 + j) * rows + tr0, make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]));
-  }
+  store_block_amax<DELAYED>(job, lb, am);
 }
 
 // Row-major codes only, any element count: grid-stride over 16-byte loads.
 constexpr int kFlatUnroll = 4;
 
-template <int FMT, bool S>
+template <int FMT, bool S, bool DELAYED>
 __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
   int lb;
   const QuantJob& job = pick_job(args, lb);
   const int tid = threadIdx.x;
-  const float amax = amax_from_partials<kQThreads>(job.rec);
+  const float amax = job_amax<DELAYED>(job);
   const ScaleVals sv = scale_from_amax(amax, FMT);
-  if (lb == 0 && tid == 0) write_scale_fields(job.rec, amax, sv);
+  if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
+  uint32_t am = 0;
 
   const int64_t n = job.rows * job.cols;
   const int64_t nvec = n >> 3;
@@ -144,30 +195,61 @@ __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
 #pragma unroll
     for (int u = 0; u < kFlatUnroll; ++u) {
       const int64_t k = base + (int64_t)u * kQThreads;
+      if constexpr (DELAYED) am = absmax8(am, v[u]);
       if (k < nvec) st8<S>(qv + k, quant8<FMT>(v[u], sv.s32));
     }
   }
   if (lb == 0 && tid < (int)(n & 7)) {
     const int64_t i = (nvec << 3) + tid;
+    if constexpr (DELAYED) am = pmax(am, (uint32_t)(job.x[i] & 0x7FFFu));
     job.q[i] = quant1<FMT>(job.x[i], sv.s32);
   }
+  store_block_amax<DELAYED>(job, lb, am);
 }
 
 // Transposed copy of a shape the tiled kernel does not take: one thread per element.
-template <int FMT>
+template <int FMT, bool DELAYED>
 __global__ __launch_bounds__(kQThreads) void k_quant_elem(QuantArgs args) {
   int lb;
   const QuantJob& job = pick_job(args, lb);
   const int tid = threadIdx.x;
-  const float amax = amax_from_partials<kQThreads>(job.rec);
+  const float amax = job_amax<DELAYED>(job);
   const ScaleVals sv = scale_from_amax(amax, FMT);
-  if (lb == 0 && tid == 0) write_scale_fields(job.rec, amax, sv);
+  if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
+  uint32_t am = 0;
   const int64_t n = job.rows * job.cols;
   for (int64_t i = (int64_t)lb * kQThreads + tid; i < n; i += (int64_t)job.nblocks * kQThreads) {
+    if constexpr (DELAYED) am = pmax(am, (uint32_t)(job.x[i] & 0x7FFFu));
     const uint8_t c = quant1<FMT>(job.x[i], sv.s32);
     job.q[i] = c;
     const int64_t r = i / job.cols, cc = i - r * job.cols;
     job.qT[cc * job.rows + r] = c;
+  }
+  store_block_amax<DELAYED>(job, lb, am);
+}
+
+// Delayed scaling, after the cast: rec->amax = the current tensor's amax
+// (from the partials the cast left), pushed to the front of the history; the
+// oldest entry drops out.  One block per job.
+__global__ __launch_bounds__(kQThreads) void k_hist_push(QuantArgs args) {
+  const QuantJob& job = args.job[blockIdx.x];
+  const float a = amax_from_partials<kQThreads>(job.rec);
+  constexpr int kMaxPer = FP8SG_MAX_HISTORY / kQThreads;
+  float old[kMaxPer];
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) {
+    const int i = threadIdx.x + k * kQThreads;
+    old[k] = i < job.hist_len ? job.hist[i] : 0.0f;
+  }
+  __syncthreads();  // every entry read before any is overwritten
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) {
+    const int i = threadIdx.x + k * kQThreads;
+    if (i + 1 < job.hist_len) job.hist[i + 1] = old[k];
+  }
+  if (threadIdx.x == 0) {
+    job.hist[0] = a;
+    job.rec->amax = a;
   }
 }
 
@@ -194,10 +276,11 @@ static int blocks_of(QuantJob& j, QuantPath p) {
     b = (n + kQThreads - 1) / kQThreads;
     if (b > 4096) b = 4096;
   }
+  if (j.hist && b > FP8SG_AMAX_PARTS) b = FP8SG_AMAX_PARTS;  // one partial slot per block
   return (int)(b < 1 ? 1 : b);  // one block at least: it writes the scale fields
 }
 
-template <int FMT>
+template <int FMT, bool DELAYED>
 static hipError_t launch_fmt(QuantArgs a, hipStream_t stream) {
   // jobs of one launch must take the same path; otherwise split into launches
   for (int j0 = 0; j0 < a.njobs;) {
@@ -214,27 +297,38 @@ static hipError_t launch_fmt(QuantArgs a, hipStream_t stream) {
       bytes += jb.rows * jb.cols * (jb.qT ? 4 : 3);
       sub.job[sub.njobs++] = jb;
     }
-    const bool stream_pass = bytes >= kStreamBytes;
-    if (p == kPathTiled && stream_pass)
-      hipLaunchKernelGGL((k_quant_tiled<FMT, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
+    const bool st = bytes >= kStreamBytes;
+    if (p == kPathTiled && st)
+      hipLaunchKernelGGL((k_quant_tiled<FMT, true, DELAYED>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathTiled)
-      hipLaunchKernelGGL((k_quant_tiled<FMT, false>), dim3(total), dim3(kQThreads), 0, stream, sub);
-    else if (p == kPathFlat && stream_pass)
-      hipLaunchKernelGGL((k_quant_flat<FMT, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_tiled<FMT, false, DELAYED>), dim3(total), dim3(kQThreads), 0, stream, sub);
+    else if (p == kPathFlat && st)
+      hipLaunchKernelGGL((k_quant_flat<FMT, true, DELAYED>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathFlat)
-      hipLaunchKernelGGL((k_quant_flat<FMT, false>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_flat<FMT, false, DELAYED>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else
-      hipLaunchKernelGGL(k_quant_elem<FMT>, dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_elem<FMT, DELAYED>), dim3(total), dim3(kQThreads), 0, stream, sub);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (DELAYED) {
+      hipLaunchKernelGGL(k_hist_push, dim3(sub.njobs), dim3(kQThreads), 0, stream, sub);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     j0 = j;
   }
   return hipSuccess;
 }
 
 hipError_t launch_quantize(QuantArgs args, int fmt, hipStream_t stream) {
-  return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN>(args, stream)
-                             : launch_fmt<FP8SG_E5M2>(args, stream);
+  // delayed and dynamic jobs are never mixed in one call (the entry points
+  // build the job lists)
+  const bool delayed = args.njobs > 0 && args.job[0].hist;
+  if (delayed)
+    return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN, true>(args, stream)
+                               : launch_fmt<FP8SG_E5M2, true>(args, stream);
+  return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN, false>(args, stream)
+                             : launch_fmt<FP8SG_E5M2, false>(args, stream);
 }
 
 }  // namespace fp8sg

@@ -64,6 +64,8 @@ typedef void* fp8sg_stream; /* hipStream_t */
 
 /* Number of per-block partial maxima an amax reduction leaves in a record. */
 #define FP8SG_AMAX_PARTS 1024
+/* Longest amax history the delayed-scaling entry points take. */
+#define FP8SG_MAX_HISTORY 1024
 
 /*
  * Per-tensor scale record, 4128 bytes of device memory owned by the caller
@@ -181,6 +183,49 @@ FP8SG_API fp8sg_status fp8_scaled_linear_fwd(const uint16_t* x, const uint16_t* 
 FP8SG_API fp8sg_status fp8_scaled_linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved,
                                    int64_t M, int64_t N, int64_t K, const fp8_linear_bwd_ws* ws,
                                    void* gx, void* gw, fp8sg_out out, fp8sg_stream stream);
+
+/*
+ * Delayed scaling [PT-CH20 §20.5.9: each FP8 op keeps an amax history of its
+ * input and takes every step's scale from the amax of earlier steps].
+ * One pass over x instead of fp8_amax + fp8_quantize:
+ *   a   = the largest entry of amax_history[0 .. history_len) (NaN if any
+ *         entry is NaN, negative entries count as 0)
+ *   scale, inv, scale32, inv32 = as fp8_quantize computes them from amax a,
+ *         written to rec
+ *   q (and qT) = the codes of x at that scale, as fp8_quantize
+ *   rec->amax  = max |x| of this x (as fp8_amax), then pushed to the front of
+ *         the history: amax_history[i + 1] = old amax_history[i], and
+ *         amax_history[0] = rec->amax.
+ * Before the first step the caller seeds the history (for example with
+ * fp8_amax of the first tensor, or with the amax it expects).
+ *   amax_history: device float[history_len], 1 <= history_len <=
+ *                 FP8SG_MAX_HISTORY (FP8SG_ERR_SHAPE otherwise), read and
+ *                 updated in place, most recent first.
+ * The other arguments as fp8_quantize.
+ */
+FP8SG_API fp8sg_status fp8_quantize_delayed(const uint16_t* x, int64_t rows, int64_t cols,
+                                  fp8sg_format fmt, float* amax_history, int32_t history_len,
+                                  fp8sg_scale_rec* rec, uint8_t* q, uint8_t* qT,
+                                  fp8sg_stream stream);
+
+/*
+ * fp8_scaled_linear_fwd / fp8_scaled_linear_bwd with delayed scaling of the
+ * operands they quantize [PT-CH20 §20.5.9; FP8-TRAIN §4]: x and W (forward,
+ * histories hist_x and hist_w) and gy (backward, hist_gy) are cast as
+ * fp8_quantize_delayed does, with their histories updated in place; the
+ * GEMMs and everything else are as in the dynamic entry points.  The
+ * backward reuses the codes and inverse scales the forward saved.
+ *   hist_*: device float[history_len], 1 <= history_len <= FP8SG_MAX_HISTORY.
+ */
+FP8SG_API fp8sg_status fp8_scaled_linear_fwd_delayed(const uint16_t* x, const uint16_t* w,
+                                   int64_t M, int64_t N, int64_t K,
+                                   const fp8_linear_saved* saved, float* hist_x, float* hist_w,
+                                   int32_t history_len, void* y, fp8sg_out out,
+                                   fp8sg_stream stream);
+FP8SG_API fp8sg_status fp8_scaled_linear_bwd_delayed(const uint16_t* gy, const fp8_linear_saved* saved,
+                                   int64_t M, int64_t N, int64_t K, const fp8_linear_bwd_ws* ws,
+                                   float* hist_gy, int32_t history_len, void* gx, void* gw,
+                                   fp8sg_out out, fp8sg_stream stream);
 
 /*
  * GradScaler unscale + non-finite check over a list of fp16 gradients

@@ -295,6 +295,23 @@ def linear_bwd(gy_bf16, fwd: FwdResult, out_fmt: int = BF16) -> BwdResult:
     return BwdResult(g, c_gx, c_gw, round_out(c_gx, out_fmt), round_out(c_gw, out_fmt))
 
 
+def linear_fwd_delayed(x_bf16, w_bf16, hist_x, hist_w, out_fmt: int = BF16):
+    """linear_fwd with x and W cast by delayed scaling [PT-CH20 §20.5.9];
+    returns (FwdResult, new hist_x, new hist_w)."""
+    xq = to_fp8_delayed(x_bf16, E4M3FN, hist_x)
+    wq = to_fp8_delayed(w_bf16, E4M3FN, hist_w)
+    c = gemm(xq.q, E4M3FN, wq.q, E4M3FN, xq.sc.inv, wq.sc.inv)
+    return FwdResult(xq, wq, c, round_out(c, out_fmt)), xq.hist, wq.hist
+
+
+def linear_bwd_delayed(gy_bf16, fwd: FwdResult, hist_gy, out_fmt: int = BF16):
+    """linear_bwd with gy cast by delayed scaling; returns (BwdResult, new hist_gy)."""
+    g = to_fp8_delayed(gy_bf16, E5M2, hist_gy)
+    c_gx = gemm(g.q, E5M2, fwd.w.qT, E4M3FN, g.sc.inv, fwd.w.sc.inv)
+    c_gw = gemm(g.qT, E5M2, fwd.x.qT, E4M3FN, g.sc.inv, fwd.x.sc.inv)
+    return BwdResult(g, c_gx, c_gw, round_out(c_gx, out_fmt), round_out(c_gw, out_fmt)), g.hist
+
+
 # ------------------------------------------------------ GradScaler (O-7, O-8)
 
 def unscale_check(grads, scale: float, found: int = 0):

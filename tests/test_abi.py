@@ -113,6 +113,28 @@ def test_amp_validation():
     assert L.amp_update_scale(P(0), P(A16), P(A16), 2.0, 0.5, 10, P(0)) == ENULL
 
 
+def test_delayed_validation():
+    L = F.lib()
+    q = P(A16)
+    # history length 0 and beyond the maximum; a NULL history; a misaligned one
+    assert L.fp8_quantize_delayed(P(A16), 16, 16, 0, P(A16), 0, P(A16), q, q, P(0)) == ESHAPE
+    assert L.fp8_quantize_delayed(P(A16), 16, 16, 0, P(A16), 1025, P(A16), q, q, P(0)) == ESHAPE
+    assert L.fp8_quantize_delayed(P(A16), 16, 16, 0, P(0), 4, P(A16), q, q, P(0)) == ENULL
+    assert L.fp8_quantize_delayed(P(A16), 16, 16, 0, P(A16 + 2), 4, P(A16), q, q, P(0)) == EALIGN
+    assert L.fp8_quantize_delayed(P(A16), 16, 16, 7, P(A16), 4, P(A16), q, q, P(0)) == EFORMAT
+    saved = F._Saved(A16, A16, A16, A16, A16, A16)
+    ws = F._BwdWs(A16, A16, A16)
+    fwd = lambda hx, hw, h: L.fp8_scaled_linear_fwd_delayed(P(A16), P(A16), 16, 16, 16,
+                                                             ctypes.byref(saved), P(hx), P(hw), h,
+                                                             P(A16), 0, P(0))
+    assert fwd(0, A16, 4) == ENULL and fwd(A16, 0, 4) == ENULL
+    assert fwd(A16, A16, 0) == ESHAPE and fwd(A16, A16 + 1, 4) == EALIGN
+    bwd = lambda hg, h: L.fp8_scaled_linear_bwd_delayed(P(A16), ctypes.byref(saved), 16, 16, 16,
+                                                        ctypes.byref(ws), P(hg), h, P(A16), P(A16),
+                                                        0, P(0))
+    assert bwd(0, 4) == ENULL and bwd(A16, 2000) == ESHAPE and bwd(A16 + 2, 4) == EALIGN
+
+
 def test_norm_workspace_and_validation():
     L = F.lib()
     n = (ctypes.c_int64 * 3)(8192, 8193, 0)
