@@ -181,15 +181,21 @@ def fp8_gemm(A: torch.Tensor, fa: int, B: torch.Tensor, fb: int, inv_a_ptr: int,
 class LinearSaved:
     """Device buffers the forward pass fills for the backward pass."""
 
-    def __init__(self, M, N, K, device="cuda"):
-        u8 = dict(dtype=torch.uint8, device=device)
-        self.x_q = torch.empty((M, K), **u8)
-        self.x_qT = torch.empty((K, M), **u8)
-        self.w_q = torch.empty((N, K), **u8)
-        self.w_qT = torch.empty((K, N), **u8)
-        self.recs = torch.zeros((2, SCALE_REC_BYTES), **u8)
+    def __init__(self, M, N, K, device="cuda", tensors=None):
+        if tensors is not None:  # (x_q, x_qT, w_q, w_qT, recs) kept from an earlier forward
+            self.x_q, self.x_qT, self.w_q, self.w_qT, self.recs = tensors
+        else:
+            u8 = dict(dtype=torch.uint8, device=device)
+            self.x_q = torch.empty((M, K), **u8)
+            self.x_qT = torch.empty((K, M), **u8)
+            self.w_q = torch.empty((N, K), **u8)
+            self.w_qT = torch.empty((K, N), **u8)
+            self.recs = torch.zeros((2, SCALE_REC_BYTES), **u8)
         self.x_sc = ScaleRec(buf=self.recs[0])
         self.w_sc = ScaleRec(buf=self.recs[1])
+
+    def tensors(self):
+        return (self.x_q, self.x_qT, self.w_q, self.w_qT, self.recs)
 
     def struct(self):
         return _Saved(self.x_q.data_ptr(), self.x_qT.data_ptr(), self.w_q.data_ptr(),

@@ -1,0 +1,235 @@
+"""PyTorch integration of the FP8 scaled linear layer and the GradScaler step,
+over the C-ABI library: every FP8 cast, GEMM, unscale, check and scale update
+runs in libfp8sg's kernels; this module only allocates buffers, wires
+autograd and walks module trees.
+
+  - Float8Linear / _Fp8LinearFn ["FP8训练：量化、自动微分、Torchao", §6: one
+    autograd node per linear; the forward takes and returns plain bf16, FP8
+    never leaves it; what is saved for the backward pass is the FP8 operands
+    and their inverse scales, not the bf16 inputs].
+  - convert_to_float8_training [same page, §8: post-order walk over the module
+    tree, nn.Linear children replaced in place when module_filter_fn(module,
+    fully qualified name) allows, the new module reusing the original weight
+    tensor].
+  - GradScaler ["第20章 量化与混合精度训练", §20.2.2 and §20.5.33;
+    "AMP：Automatic Mixed Precision 技术笔记", §4 and §6]: scale the loss,
+    unscale fp16 gradients in place with the non-finite check, skip the
+    optimizer step on inf/NaN, update the scale on the device.
+
+Limits of this layer: inputs and weights are bf16 (the quantize kernels read
+bf16); Float8Linear has no bias (the method's linear has none; the default
+filter leaves biased layers alone); leading dimensions of the input are
+flattened into M; M, N, K must be multiples of 16.
+"""
+from typing import Callable, Optional
+
+import torch
+from torch import nn
+
+from . import (LinearBwdWs, LinearSaved, OUT_BF16, ScaleRec, amp_norm_workspace_len,
+               amp_unscale_check, amp_unscale_check_norm, amp_update_scale, fp8_amax,
+               fp8_scaled_linear_bwd, fp8_scaled_linear_bwd_delayed, fp8_scaled_linear_fwd,
+               fp8_scaled_linear_fwd_delayed)
+
+
+def _seed_history(hist: torch.Tensor, x: torch.Tensor):
+    """Delayed scaling needs a history before its first step: its first entry
+    becomes max |x| of the first tensor seen (one amax pass)."""
+    rec = ScaleRec(device=x.device)
+    fp8_amax(x, rec)
+    hist.zero_()
+    hist[:1].copy_(rec.buf[0:4].view(torch.float32))  # the record's amax field
+
+
+class _Fp8LinearFn(torch.autograd.Function):
+    """y = x W^T through the FP8 path; saves the FP8 codes (row-major and
+    transposed) and the two scale records for the backward pass."""
+
+    @staticmethod
+    def forward(ctx, x2d: torch.Tensor, weight: torch.Tensor, mod: "Float8Linear"):
+        M, K = x2d.shape
+        N = weight.shape[0]
+        saved = LinearSaved(M, N, K, device=x2d.device)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x2d.device)
+        if mod.scaling == "delayed":
+            if not mod._seeded_fwd:
+                _seed_history(mod.hist_x, x2d)
+                _seed_history(mod.hist_w, weight)
+                mod._seeded_fwd = True
+            fp8_scaled_linear_fwd_delayed(x2d, weight, saved, mod.hist_x, mod.hist_w, y, OUT_BF16)
+        else:
+            fp8_scaled_linear_fwd(x2d, weight, saved, y, OUT_BF16)
+        ctx.save_for_backward(*saved.tensors())
+        ctx.mod = mod
+        ctx.dims = (M, N, K)
+        return y
+
+    @staticmethod
+    def backward(ctx, gy: torch.Tensor):
+        M, N, K = ctx.dims
+        mod = ctx.mod
+        if gy.dtype != torch.bfloat16:
+            raise TypeError(f"Float8Linear expects bf16 output gradients, got {gy.dtype}")
+        gy = gy.contiguous()
+        saved = LinearSaved(M, N, K, tensors=ctx.saved_tensors)
+        ws = LinearBwdWs(M, N, device=gy.device)
+        gx = torch.empty((M, K), dtype=torch.bfloat16, device=gy.device)
+        gw = torch.empty((N, K), dtype=torch.bfloat16, device=gy.device)
+        if mod.scaling == "delayed":
+            if not mod._seeded_bwd:
+                _seed_history(mod.hist_gy, gy)
+                mod._seeded_bwd = True
+            fp8_scaled_linear_bwd_delayed(gy, saved, ws, mod.hist_gy, gx, gw, OUT_BF16)
+        else:
+            fp8_scaled_linear_bwd(gy, saved, ws, gx, gw, OUT_BF16)
+        return gx, gw, None
+
+
+class Float8Linear(nn.Module):
+    """nn.Linear (no bias) whose forward and backward GEMMs run in FP8 with
+    per-tensor scaling: "dynamic" (scale from the current tensor) or
+    "delayed" (scale from an amax history of history_len earlier steps)."""
+
+    def __init__(self, in_features: int, out_features: int, scaling: str = "dynamic",
+                 history_len: int = 16, device=None):
+        super().__init__()
+        if scaling not in ("dynamic", "delayed"):
+            raise ValueError(f"scaling must be 'dynamic' or 'delayed', not {scaling!r}")
+        self.in_features, self.out_features = in_features, out_features
+        self.scaling = scaling
+        self.weight = nn.Parameter(torch.empty((out_features, in_features), dtype=torch.bfloat16,
+                                               device=device))
+        if scaling == "delayed":
+            for name in ("hist_x", "hist_w", "hist_gy"):
+                self.register_buffer(name, torch.zeros(history_len, dtype=torch.float32,
+                                                       device=device))
+        self._seeded_fwd = self._seeded_bwd = False
+
+    @classmethod
+    def from_float(cls, lin: nn.Linear, scaling: str = "dynamic",
+                   history_len: int = 16) -> "Float8Linear":
+        """A Float8Linear sharing lin's weight tensor (no copy)."""
+        if lin.bias is not None:
+            raise ValueError("Float8Linear has no bias")
+        if lin.weight.dtype != torch.bfloat16:
+            raise TypeError(f"Float8Linear needs a bf16 weight, got {lin.weight.dtype}")
+        with torch.device("meta"):
+            new = cls(lin.in_features, lin.out_features, scaling, history_len)
+        new.weight = lin.weight
+        if scaling == "delayed":
+            for name in ("hist_x", "hist_w", "hist_gy"):
+                setattr(new, name, torch.zeros(history_len, dtype=torch.float32,
+                                               device=lin.weight.device))
+        return new
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.dtype != torch.bfloat16 or self.weight.dtype != torch.bfloat16:
+            raise TypeError("Float8Linear takes bf16 inputs and a bf16 weight")
+        lead = x.shape[:-1]
+        x2d = x.reshape(-1, self.in_features).contiguous()
+        y = _Fp8LinearFn.apply(x2d, self.weight, self)
+        return y.reshape(*lead, self.out_features)
+
+    def extra_repr(self):
+        return f"in_features={self.in_features}, out_features={self.out_features}, " \
+               f"scaling={self.scaling}"
+
+
+def default_module_filter(mod: nn.Linear, fqn: str) -> bool:
+    """Convert a linear layer when the FP8 path can take it: bf16 weight, no
+    bias, in and out features multiples of 16 (vocabulary-sized heads often
+    are not)."""
+    return (mod.bias is None and mod.weight.dtype == torch.bfloat16 and
+            mod.in_features % 16 == 0 and mod.out_features % 16 == 0)
+
+
+def convert_to_float8_training(model: nn.Module,
+                               module_filter_fn: Optional[Callable[[nn.Module, str], bool]] = None,
+                               scaling: str = "dynamic", history_len: int = 16) -> nn.Module:
+    """Replace, in place and post-order, every nn.Linear child that
+    module_filter_fn(child, fully_qualified_name) accepts (default:
+    default_module_filter) with a Float8Linear sharing its weight."""
+    accept = module_filter_fn or default_module_filter
+
+    def walk(mod: nn.Module, prefix: str):
+        for name, child in list(mod.named_children()):
+            fqn = f"{prefix}.{name}" if prefix else name
+            walk(child, fqn)  # children first
+            if isinstance(child, nn.Linear) and accept(child, fqn):
+                setattr(mod, name, Float8Linear.from_float(child, scaling, history_len))
+
+    walk(model, "")
+    return model
+
+
+class GradScaler:
+    """Dynamic loss scaling for fp16 gradients with the scale, growth tracker
+    and non-finite flag kept on the device.  scale(loss) multiplies by the
+    current scale; unscale_(optimizer) unscales the optimizer's gradients in
+    place and checks them (optionally also returning their global 2-norm, for
+    clipping); step(optimizer) runs optimizer.step() unless a gradient was
+    inf/NaN (this reads the flag: one host synchronisation, as in PyTorch's
+    GradScaler); update() applies the halve-on-inf / grow-after-interval rule
+    and clears the flag."""
+
+    def __init__(self, init_scale: float = 2.0 ** 16, growth_factor: float = 2.0,
+                 backoff_factor: float = 0.5, growth_interval: int = 2000, device="cuda"):
+        self._scale = torch.tensor([init_scale], dtype=torch.float32, device=device)
+        self._tracker = torch.zeros(1, dtype=torch.int32, device=device)
+        self._found = torch.zeros(1, dtype=torch.int32, device=device)
+        self.growth_factor, self.backoff_factor = growth_factor, backoff_factor
+        self.growth_interval = growth_interval
+        self._unscaled = set()
+
+    def scale(self, loss: torch.Tensor) -> torch.Tensor:
+        # a 0-dim fp32 factor: torch's promotion keeps the loss's own dtype
+        # unless it is lower, as PyTorch's GradScaler does
+        return loss * self._scale.view(())
+
+    @staticmethod
+    def _grads(optimizer):
+        gs = []
+        for group in optimizer.param_groups:
+            for p in group["params"]:
+                if p.grad is None:
+                    continue
+                if p.grad.dtype != torch.float16 or not p.grad.is_contiguous():
+                    raise TypeError("GradScaler unscales contiguous fp16 gradients only")
+                gs.append(p.grad)
+        return gs
+
+    def unscale_(self, optimizer, with_norm: bool = False):
+        """Unscale and check the optimizer's gradients once per step.  With
+        with_norm, returns a device float32[2]: (sum of squares, 2-norm) of the
+        unscaled gradients taken together."""
+        if id(optimizer) in self._unscaled:
+            raise RuntimeError("unscale_() has already been called on this optimizer this step")
+        grads = self._grads(optimizer)
+        self._unscaled.add(id(optimizer))
+        if not with_norm:
+            amp_unscale_check(grads, self._scale, self._found)
+            return None
+        ws = torch.empty(amp_norm_workspace_len([g.numel() for g in grads]), dtype=torch.float32,
+                         device=self._scale.device)
+        out = torch.empty(2, dtype=torch.float32, device=self._scale.device)
+        amp_unscale_check_norm(grads, self._scale, self._found, ws, out)
+        return out
+
+    def step(self, optimizer, *args, **kwargs):
+        if id(optimizer) not in self._unscaled:
+            self.unscale_(optimizer)
+        if int(self._found.item()) == 0:
+            return optimizer.step(*args, **kwargs)
+        return None
+
+    def update(self):
+        amp_update_scale(self._scale, self._tracker, self._found, self.growth_factor,
+                         self.backoff_factor, self.growth_interval)
+        self._unscaled.clear()
+
+    def get_scale(self) -> float:
+        return float(self._scale.item())
+
+    def state(self):
+        """(scale, growth tracker, non-finite flag), read from the device."""
+        return self.get_scale(), int(self._tracker.item()), int(self._found.item())

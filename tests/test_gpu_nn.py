@@ -1,0 +1,159 @@
+"""GPU tests of the PyTorch integration (fp8_scaled_gemm_amd.nn): Float8Linear
+forward/backward through autograd against the oracle's FP8 linear, delayed
+scaling histories over several steps, and the GradScaler wrapper's
+skip/backoff/growth behaviour and gradient norm against the oracle."""
+import numpy as np
+import pytest
+import torch
+from torch import nn
+
+import fp8_scaled_gemm_amd.nn as FN
+import oracle as O
+import workloads as W
+from tests.parity import assert_codes_equal, check_gemm_values
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def dev_bf16(bits, requires_grad=False):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return t.requires_grad_(requires_grad)
+
+
+def host_u16(t):
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_out(got, c_ref, A, fa, B, ia, ib, K, what):
+    ii, jj = [v.reshape(-1) for v in np.meshgrid(np.arange(c_ref.shape[0]),
+                                                  np.arange(c_ref.shape[1]), indexing="ij")]
+    ad = O.gemm_absdot_at(A, fa, B, O.E4M3FN, ia, ib, ii, jj)
+    check_gemm_values(O.decode(O.BF16, host_u16(got)).reshape(-1), c_ref.reshape(-1), ad, K,
+                      O.BF16, what)
+
+
+def test_float8_linear_autograd_matches_oracle():
+    B, T, K, N = 2, 64, 128, 256
+    x_h = W.normal_bf16(61, 0, (B * T, K), 1.0)
+    w_h = W.normal_bf16(61, 1, (N, K), 0.02)
+    gy_h = W.normal_bf16(61, 2, (B * T, N), 1e-3)
+    lin = nn.Linear(K, N, bias=False, dtype=torch.bfloat16, device=DEV)
+    with torch.no_grad():
+        lin.weight.copy_(dev_bf16(w_h))
+    f8 = FN.Float8Linear.from_float(lin)
+    x = dev_bf16(x_h).reshape(B, T, K).requires_grad_(True)
+    y = f8(x)
+    assert y.shape == (B, T, N) and y.dtype == torch.bfloat16
+    # the autograd node keeps FP8 codes and scale records only, no bf16 input
+    node = y.grad_fn.next_functions[0][0]  # under the reshape back to (B, T, N)
+    assert type(node).__name__ == "_Fp8LinearFnBackward"
+    assert len(node.saved_tensors) == 5 and all(t.dtype == torch.uint8 for t in node.saved_tensors)
+    y.backward(dev_bf16(gy_h).reshape(B, T, N))
+    torch.cuda.synchronize()
+    fw = O.linear_fwd(x_h, w_h)
+    bw = O.linear_bwd(gy_h, fw)
+    check_out(y.reshape(B * T, N), fw.c, fw.x.q, O.E4M3FN, fw.w.q, fw.x.sc.inv, fw.w.sc.inv, K, "y")
+    check_out(x.grad.reshape(B * T, K), bw.c_gx, bw.gy.q, O.E5M2, fw.w.qT, bw.gy.sc.inv,
+              fw.w.sc.inv, N, "gx")
+    check_out(lin.weight.grad, bw.c_gw, bw.gy.qT, O.E5M2, fw.x.qT, bw.gy.sc.inv, fw.x.sc.inv,
+              B * T, "gw")
+    assert f8.weight.grad is lin.weight.grad  # one shared parameter
+
+
+def test_float8_linear_delayed_steps_match_oracle():
+    M, K, N, H = 128, 256, 128, 4
+    lin = nn.Linear(K, N, bias=False, dtype=torch.bfloat16, device=DEV)
+    w_h = W.normal_bf16(62, 1, (N, K), 0.02)
+    with torch.no_grad():
+        lin.weight.copy_(dev_bf16(w_h))
+    f8 = FN.Float8Linear.from_float(lin, scaling="delayed", history_len=H)
+    hx = hw = hg = None
+    for t in range(3):
+        x_h = W.normal_bf16(62, 10 + t, (M, K), 1.0 + 3 * t)
+        gy_h = W.normal_bf16(62, 20 + t, (M, N), 1e-3 * (t + 1))
+        x = dev_bf16(x_h, requires_grad=True)
+        y = f8(x)
+        y.backward(dev_bf16(gy_h))
+        torch.cuda.synchronize()
+        if t == 0:  # the module seeds each history with the first tensor's amax
+            seed = lambda a: np.array([O.bits_to_f32(O.amax_bits(a))] + [0.0] * (H - 1), np.float32)
+            hx, hw, hg = seed(x_h), seed(w_h), seed(gy_h)
+        fw, hx, hw = O.linear_fwd_delayed(x_h, w_h, hx, hw)
+        bw, hg = O.linear_bwd_delayed(gy_h, fw, hg)
+        for got, ref in ((f8.hist_x, hx), (f8.hist_w, hw), (f8.hist_gy, hg)):
+            assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32)), t
+        check_out(y, fw.c, fw.x.q, O.E4M3FN, fw.w.q, fw.x.sc.inv, fw.w.sc.inv, K, f"y {t}")
+        check_out(x.grad, bw.c_gx, bw.gy.q, O.E5M2, fw.w.qT, bw.gy.sc.inv, fw.w.sc.inv, N,
+                  f"gx {t}")
+        lin.weight.grad = None
+
+
+def test_converted_mlp_block_trains():
+    """A SwiGLU block converted by convert_to_float8_training: forward and
+    backward run through the FP8 kernels (the gating itself is torch), and
+    stay within FP8 quantization error of the bf16 block."""
+    torch.manual_seed(0)
+    T, H, Fd = 256, 128, 384
+
+    class MLP(nn.Module):
+        def __init__(self):
+            super().__init__()
+            self.gate = nn.Linear(H, Fd, bias=False, dtype=torch.bfloat16)
+            self.up = nn.Linear(H, Fd, bias=False, dtype=torch.bfloat16)
+            self.down = nn.Linear(Fd, H, bias=False, dtype=torch.bfloat16)
+
+        def forward(self, x):
+            return self.down(torch.nn.functional.silu(self.gate(x)) * self.up(x))
+
+    ref = MLP().to(DEV)
+    for p in ref.parameters():
+        nn.init.normal_(p, 0.0, 0.05)
+    f8 = MLP().to(DEV)
+    f8.load_state_dict(ref.state_dict())
+    FN.convert_to_float8_training(f8)
+    assert all(isinstance(getattr(f8, n), FN.Float8Linear) for n in ("gate", "up", "down"))
+    x = torch.randn(T, H, device=DEV, dtype=torch.bfloat16)
+    y_ref, y8 = ref(x.float().bfloat16()), f8(x)
+    rel = (y8.float() - y_ref.float()).norm() / y_ref.float().norm()
+    assert rel < 0.1, rel
+    y8.float().pow(2).mean().backward()
+    y_ref.float().pow(2).mean().backward()
+    for n in ("gate", "up", "down"):
+        g8, gr = getattr(f8, n).weight.grad.float(), getattr(ref, n).weight.grad.float()
+        assert torch.isfinite(g8).all()
+        assert (g8 - gr).norm() / gr.norm() < 0.2, n
+
+
+def test_grad_scaler_skip_backoff_growth_and_norm():
+    ps = [nn.Parameter(torch.zeros(n, dtype=torch.float16, device=DEV)) for n in (4096, 777, 64)]
+    opt = torch.optim.SGD(ps, lr=1.0)
+    sc = FN.GradScaler(init_scale=1024.0, growth_interval=2)
+    st = O.ScalerState(np.float32(1024.0), 0)
+    for step in range(6):
+        grads = [W.normal_f16(70 + step, i, (p.numel(),), 1e-2 * float(st.scale))
+                 for i, p in enumerate(ps)]
+        if step == 3:
+            grads[1][5] = 0x7C00  # +inf in one gradient
+        for p, g in zip(ps, grads):
+            p.grad = torch.from_numpy(g.view(np.int16)).view(torch.float16).to(DEV)
+        before = [p.detach().clone() for p in ps]
+        norm = sc.unscale_(opt, with_norm=True)
+        sc.step(opt)
+        ref = [g.copy() for g in grads]
+        found = O.unscale_check(ref, st.scale)
+        for p, r in zip(ps, ref):
+            assert np.array_equal(host_u16(p.grad), r)  # unscaled in place, bit-exact
+        s_ref, n_ref = O.grad_norm(ref)
+        n_got = norm.cpu().numpy().astype(np.float64)
+        if found:
+            assert not np.isfinite(n_got[1])
+            assert all(torch.equal(p, b) for p, b in zip(ps, before))  # step skipped
+        else:
+            assert abs(n_got[1] - n_ref) <= 11 * 2.0 ** -24 * n_ref + 1e-12
+            assert not all(torch.equal(p, b) for p, b in zip(ps, before))
+        sc.update()
+        st = O.update_scale(st, found, 2.0, 0.5, 2)
+        assert sc.state() == (float(st.scale), st.tracker, 0), step
+        for p in ps:
+            p.grad = None

@@ -1,0 +1,77 @@
+"""convert_to_float8_training's module surgery ["FP8训练：量化、自动微分、
+Torchao", §8]: post-order walk, nn.Linear children replaced in place when the
+filter accepts (module, fully qualified name), the replacement sharing the
+original weight tensor.  Pure module-tree logic: no kernels run."""
+import torch
+from torch import nn
+
+from fp8_scaled_gemm_amd.nn import Float8Linear, convert_to_float8_training, default_module_filter
+
+
+def lin(i, o, bias=False):
+    return nn.Linear(i, o, bias=bias, dtype=torch.bfloat16)
+
+
+class Block(nn.Module):
+    def __init__(self):
+        super().__init__()
+        self.gate, self.up, self.down = lin(64, 128), lin(64, 128), lin(128, 64)
+        self.router = lin(64, 16)
+        self.norm = nn.LayerNorm(64)
+
+
+class Model(nn.Module):
+    def __init__(self):
+        super().__init__()
+        self.embed = nn.Embedding(100, 64)
+        self.blocks = nn.ModuleList([Block(), Block()])
+        self.proj = lin(64, 64, bias=True)     # biased: the default filter leaves it
+        self.lm_head = lin(64, 100)            # 100 outputs: not a multiple of 16
+
+
+def test_default_filter_converts_what_the_path_takes():
+    m = Model()
+    w = {n: p for n, p in m.named_parameters()}
+    convert_to_float8_training(m)
+    for b in m.blocks:
+        for name in ("gate", "up", "down", "router"):
+            assert isinstance(getattr(b, name), Float8Linear)
+        assert isinstance(b.norm, nn.LayerNorm)
+    assert type(m.proj) is nn.Linear and type(m.lm_head) is nn.Linear
+    # the weights are the original tensors, not copies
+    assert m.blocks[1].down.weight is w["blocks.1.down.weight"]
+    assert m.blocks[0].gate.weight.data_ptr() == w["blocks.0.gate.weight"].data_ptr()
+
+
+def test_filter_sees_fully_qualified_names_post_order():
+    m = Model()
+    seen = []
+
+    def keep_router_out(mod, fqn):
+        seen.append(fqn)
+        return default_module_filter(mod, fqn) and not fqn.endswith("router")
+
+    convert_to_float8_training(m, keep_router_out)
+    assert seen == ["blocks.0.gate", "blocks.0.up", "blocks.0.down", "blocks.0.router",
+                    "blocks.1.gate", "blocks.1.up", "blocks.1.down", "blocks.1.router",
+                    "proj", "lm_head"]
+    assert type(m.blocks[0].router) is nn.Linear and isinstance(m.blocks[0].gate, Float8Linear)
+
+
+def test_delayed_modules_carry_histories():
+    m = Block()
+    convert_to_float8_training(m, scaling="delayed", history_len=8)
+    for name in ("gate", "up", "down", "router"):
+        f = getattr(m, name)
+        assert f.scaling == "delayed"
+        assert all(getattr(f, h).shape == (8,) and getattr(f, h).dtype == torch.float32
+                   for h in ("hist_x", "hist_w", "hist_gy"))
+    assert set(dict(m.named_buffers())) >= {"gate.hist_x", "down.hist_gy"}
+
+
+def test_from_float_refuses_what_the_path_cannot_take():
+    import pytest
+    with pytest.raises(ValueError):
+        Float8Linear.from_float(lin(32, 32, bias=True))
+    with pytest.raises(TypeError):
+        Float8Linear.from_float(nn.Linear(32, 32, bias=False))  # fp32 weight
