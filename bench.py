@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true")
     p.add_argument("--no-hbm", action="store_true", help="skip the HBM-scale bandwidth passes")
+    p.add_argument("--no-mlp", action="store_true",
+                   help="skip the MLP-block timing through the PyTorch layer")
     p.add_argument("--copy-reference", action="store_true",
                    help="only copy 1 GiB device-to-device 5 times (calibrates the HBM byte "
                         "counters against a transfer of known size)")
@@ -266,6 +268,12 @@ def main():
         del grads, nws
         torch.cuda.empty_cache()
 
+    mlp = None
+    if not args.no_mlp:
+        log("MLP block through the PyTorch layer")
+        mlp = mlp_block(torch, F, dev, stream)
+        torch.cuda.empty_cache()
+
     # ---- sampled check of the step's outputs against the oracle
     check = None
     if not args.no_check:
@@ -311,9 +319,70 @@ def main():
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "wall_s_timed_region": round(wall, 4),
         "check": check,
+        "mlp_block": mlp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def mlp_block(torch, F, dev, stream, steps=10, warmup=3):
+    """The transformer MLP block's three FP8 linears (gate, up: 4096 -> 14336;
+    down: 14336 -> 4096; 8192 tokens) trained through Float8Linear and autograd
+    (x shared by gate and up, as in the block), against the same nine GEMMs
+    driven directly through the C-ABI.  Synthetic device data at the
+    workload's shapes and standard deviations."""
+    import fp8_scaled_gemm_amd.nn as FN
+    T, H, Fd = 8192, 4096, 14336
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    shapes = {"gate": (H, Fd), "up": (H, Fd), "down": (Fd, H)}
+    mods = {n: FN.Float8Linear(k, o, device=dev) for n, (k, o) in shapes.items()}
+    for m in mods.values():
+        with torch.no_grad():
+            m.weight.normal_(0.0, 0.02)
+    x = torch.randn(T, H, **bf).requires_grad_(True)
+    h = torch.randn(T, Fd, **bf).requires_grad_(True)
+    gys = {"gate": torch.randn(T, Fd, **bf) * 1e-4, "up": torch.randn(T, Fd, **bf) * 1e-4,
+           "down": torch.randn(T, H, **bf) * 1e-4}
+
+    def autograd_step():
+        for t in [x, h] + [m.weight for m in mods.values()]:
+            t.grad = None
+        outs = [mods["gate"](x), mods["up"](x), mods["down"](h)]
+        torch.autograd.backward(outs, [gys["gate"], gys["up"], gys["down"]])
+
+    direct = {}
+    for n, (k, o) in shapes.items():
+        inp = x if n != "down" else h
+        direct[n] = dict(inp=inp.detach(), w=mods[n].weight.detach(),
+                         saved=F.LinearSaved(T, o, k, device=dev), ws=F.LinearBwdWs(T, o, device=dev),
+                         y=torch.empty(T, o, **bf), gx=torch.empty(T, k, **bf),
+                         gw=torch.empty(o, k, **bf))
+
+    def direct_step():
+        for n, d in direct.items():
+            F.fp8_scaled_linear_fwd(d["inp"], d["w"], d["saved"], d["y"], F.OUT_BF16)
+        for n, d in direct.items():
+            F.fp8_scaled_linear_bwd(gys[n], d["saved"], d["ws"], d["gx"], d["gw"], F.OUT_BF16)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_auto, ms_direct = timed(autograd_step), timed(direct_step)
+    flops = 9 * 2.0 * T * Fd * H
+    return {"workload": "MLP block T=8192 H=4096 F=14336: gate/up/down fwd+dgrad+wgrad",
+            "autograd_ms_per_step": round(ms_auto, 4),
+            "autograd_TFLOPs": round(flops / (ms_auto * 1e-3) / 1e12, 1),
+            "direct_abi_ms_per_step": round(ms_direct, 4),
+            "direct_abi_TFLOPs": round(flops / (ms_direct * 1e-3) / 1e12, 1)}
 
 
 def sampled_check(np, torch, F, x_h, w_h, gy_h, saved, ws, y, M, N, K, n_pts=256):
