@@ -67,6 +67,13 @@ def lib():
     L.orc_hist_amax.argtypes = [P, i32]
     L.orc_hist_amax.restype = u32
     L.orc_hist_push.argtypes = [P, i32, u32]
+    L.orc_amax_rows_bf16.argtypes = [P, i64, i64, P]
+    L.orc_scale_vec.argtypes = [P, i64, ctypes.c_int, P, P, P, P]
+    L.orc_quantize_rows.argtypes = [P, i64, i64, ctypes.c_int, P, P]
+    L.orc_gemm_vec.argtypes = [P, ctypes.c_int, P, ctypes.c_int, i64, i64, i64, P, P, P]
+    L.orc_gemm_vec_at.argtypes = [P, ctypes.c_int, P, ctypes.c_int, i64, P, P, P, P, i64, P]
+    L.orc_gemm_absdot_vec_at.argtypes = [P, ctypes.c_int, P, ctypes.c_int, i64, P, P, P, P, i64,
+                                         P]
     L.orc_sumsq_f16.restype = i32
     _lib = L
     return L
@@ -310,6 +317,125 @@ def linear_bwd_delayed(gy_bf16, fwd: FwdResult, hist_gy, out_fmt: int = BF16):
     c_gx = gemm(g.q, E5M2, fwd.w.qT, E4M3FN, g.sc.inv, fwd.w.sc.inv)
     c_gw = gemm(g.qT, E5M2, fwd.x.qT, E4M3FN, g.sc.inv, fwd.x.sc.inv)
     return BwdResult(g, c_gx, c_gw, round_out(c_gx, out_fmt), round_out(c_gw, out_fmt)), g.hist
+
+
+# ------------------------------------------------------- row-wise scaling (O-4c)
+
+@dataclass
+class RowScales:
+    """Per-row scale state [FP8-TRAIN §1]: amax (fp32 bits), fp64 scale and
+    inverse, and their fp32 roundings, one entry per row."""
+    amax_bits: np.ndarray
+    scale: np.ndarray
+    inv: np.ndarray
+    scale32: np.ndarray
+    inv32: np.ndarray
+
+
+def amax_rows(x2d: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x2d, dtype=np.uint16)
+    out = np.empty(x.shape[0], np.uint32)
+    lib().orc_amax_rows_bf16(_p(x), x.shape[0], x.shape[1], _p(out))
+    return out
+
+
+def row_scales(amax_bits: np.ndarray, fmt: int) -> RowScales:
+    a = np.ascontiguousarray(amax_bits, dtype=np.uint32)
+    n = a.size
+    s, r = np.empty(n, np.float64), np.empty(n, np.float64)
+    s32, r32 = np.empty(n, np.float32), np.empty(n, np.float32)
+    lib().orc_scale_vec(_p(a), n, fmt, _p(s), _p(r), _p(s32), _p(r32))
+    return RowScales(a, s, r, s32, r32)
+
+
+def quantize_rows(x2d: np.ndarray, fmt: int, scale32: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x2d, dtype=np.uint16)
+    s32 = np.ascontiguousarray(scale32, dtype=np.float32)
+    q = np.empty(x.shape, np.uint8)
+    lib().orc_quantize_rows(_p(x), x.shape[0], x.shape[1], fmt, _p(s32), _p(q))
+    return q
+
+
+@dataclass
+class RowwiseQuantized:
+    """Row-wise cast of a [R, C] tensor: codes q with one scale per row, and
+    the transposed copy qT [C, R] with one scale per column of the tensor
+    (per row of qT), as a GEMM contracting over R needs."""
+    q: np.ndarray
+    qT: np.ndarray
+    rows: RowScales
+    cols: RowScales
+
+
+def to_fp8_rowwise(x2d: np.ndarray, fmt: int, with_transpose: bool = True) -> RowwiseQuantized:
+    x = np.ascontiguousarray(x2d, dtype=np.uint16)
+    rows = row_scales(amax_rows(x), fmt)
+    q = quantize_rows(x, fmt, rows.scale32)
+    if not with_transpose:
+        return RowwiseQuantized(q, None, rows, None)
+    xT = np.ascontiguousarray(x.T)
+    cols = row_scales(amax_rows(xT), fmt)
+    return RowwiseQuantized(q, quantize_rows(xT, fmt, cols.scale32), rows, cols)
+
+
+def _f64(v):
+    return np.ascontiguousarray(v, dtype=np.float64)
+
+
+def gemm_vec(A, fa, B, fb, inv_a, inv_b) -> np.ndarray:
+    """C[M,N] (fp32) = (A . B^T) * fl32(inv_a[i] * inv_b[j]), fp32 accumulation."""
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    ia, ib = _f64(inv_a), _f64(inv_b)
+    M, Kc = A.shape
+    N = B.shape[0]
+    assert B.shape[1] == Kc and ia.size == M and ib.size == N
+    C = np.empty((M, N), np.float32)
+    lib().orc_gemm_vec(_p(A), fa, _p(B), fb, M, N, Kc, _p(ia), _p(ib), _p(C))
+    return C
+
+
+def gemm_vec_at(A, fa, B, fb, inv_a, inv_b, ii, jj) -> np.ndarray:
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    ia, ib = _f64(inv_a), _f64(inv_b)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    out = np.empty(ii.shape, np.float32)
+    lib().orc_gemm_vec_at(_p(A), fa, _p(B), fb, A.shape[1], _p(ia), _p(ib), _p(ii), _p(jj),
+                          ii.size, _p(out))
+    return out
+
+
+def gemm_absdot_vec_at(A, fa, B, fb, inv_a, inv_b, ii, jj) -> np.ndarray:
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    ia, ib = _f64(inv_a), _f64(inv_b)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    out = np.empty(ii.shape, np.float64)
+    lib().orc_gemm_absdot_vec_at(_p(A), fa, _p(B), fb, A.shape[1], _p(ia), _p(ib), _p(ii),
+                                 _p(jj), ii.size, _p(out))
+    return out
+
+
+def linear_fwd_rowwise(x_bf16, w_bf16, out_fmt: int = BF16) -> FwdResult:
+    """linear_fwd with row-wise scaling of every operand: x by rows (and by
+    columns for its transposed copy), W likewise."""
+    xq = to_fp8_rowwise(x_bf16, E4M3FN)
+    wq = to_fp8_rowwise(w_bf16, E4M3FN)
+    c = gemm_vec(xq.q, E4M3FN, wq.q, E4M3FN, xq.rows.inv, wq.rows.inv)
+    return FwdResult(xq, wq, c, round_out(c, out_fmt))
+
+
+def linear_bwd_rowwise(gy_bf16, fwd: FwdResult, out_fmt: int = BF16) -> BwdResult:
+    """dgrad = gy_q (rows of gy) . W_qT (columns of W); wgrad = gy_qT (columns
+    of gy) . x_qT (columns of x): every scale lies along a non-contraction
+    dimension."""
+    g = to_fp8_rowwise(gy_bf16, E5M2)
+    c_gx = gemm_vec(g.q, E5M2, fwd.w.qT, E4M3FN, g.rows.inv, fwd.w.cols.inv)
+    c_gw = gemm_vec(g.qT, E5M2, fwd.x.qT, E4M3FN, g.cols.inv, fwd.x.cols.inv)
+    return BwdResult(g, c_gx, c_gw, round_out(c_gx, out_fmt), round_out(c_gw, out_fmt))
 
 
 # ------------------------------------------------------ GradScaler (O-7, O-8)

@@ -382,6 +382,89 @@ ORC_API void orc_gemm_absdot_at(const uint8_t* A, int fa, const uint8_t* B, int 
 }
 
 /* ------------------------------------------------------------------------ */
+/* O-4c Row-wise scaling [FP8-TRAIN §1: each row has its own scale factor,    */
+/*      which must be carried through the accumulation].  Every row of a     */
+/*      [rows, cols] tensor gets O-2's amax over that row alone, O-3's scale */
+/*      from it and O-4's cast with it.  A GEMM of row-scaled operands       */
+/*      applies alpha[i][j] = fl32(inv_a[i] * inv_b[j]) to the fp32 sum:     */
+/*      each scale is constant along the contraction, so it factors out of   */
+/*      the dot product.                                                     */
+/* ------------------------------------------------------------------------ */
+
+ORC_API void orc_amax_rows_bf16(const uint16_t* x, int64_t rows, int64_t cols, uint32_t* out) {
+  ensure_init();
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    double best = 0.0;
+    int nan = 0;
+    for (int64_t c = 0; c < cols; ++c) {
+      double v = fabs(dec(ORC_BF16, x[r * cols + c]));
+      if (isnan(v)) nan = 1;
+      else if (v > best) best = v;
+    }
+    out[r] = nan ? 0x7FC00000u : f32_bits((float)best);
+  }
+}
+
+ORC_API void orc_scale_vec(const uint32_t* amax_bits, int64_t n, int fi, double* scale,
+                           double* inv, float* scale32, float* inv32) {
+  for (int64_t i = 0; i < n; ++i)
+    orc_scale(amax_bits[i], fi, scale + i, inv + i, scale32 + i, inv32 + i);
+}
+
+ORC_API void orc_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, int fi,
+                               const float* scale32, uint8_t* q) {
+  ensure_init();
+  float m = (float)orc_fp8_max(fi);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      float xf = (float)dec(ORC_BF16, x[r * cols + c]);
+      float y = xf * scale32[r];
+      if (!isnan(y)) {
+        if (y > m) y = m;
+        if (y < -m) y = -m;
+      }
+      q[r * cols + c] = (uint8_t)enc(fi, (double)y);
+    }
+}
+
+ORC_API void orc_gemm_vec(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t M,
+                          int64_t N, int64_t Kc, const double* inv_a, const double* inv_b,
+                          float* C) {
+  ensure_init();
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t j = 0; j < N; ++j)
+      C[i * N + j] = gemm_one(A + i * Kc, fa, B + j * Kc, fb, Kc, (float)(inv_a[i] * inv_b[j]));
+}
+
+ORC_API void orc_gemm_vec_at(const uint8_t* A, int fa, const uint8_t* B, int fb, int64_t Kc,
+                             const double* inv_a, const double* inv_b, const int64_t* ii,
+                             const int64_t* jj, int64_t npts, float* out) {
+  ensure_init();
+#pragma omp parallel for schedule(static)
+  for (int64_t p = 0; p < npts; ++p)
+    out[p] = gemm_one(A + ii[p] * Kc, fa, B + jj[p] * Kc, fb, Kc,
+                      (float)(inv_a[ii[p]] * inv_b[jj[p]]));
+}
+
+ORC_API void orc_gemm_absdot_vec_at(const uint8_t* A, int fa, const uint8_t* B, int fb,
+                                    int64_t Kc, const double* inv_a, const double* inv_b,
+                                    const int64_t* ii, const int64_t* jj, int64_t npts,
+                                    double* out) {
+  ensure_init();
+#pragma omp parallel for schedule(static)
+  for (int64_t p = 0; p < npts; ++p) {
+    const uint8_t* ar = A + ii[p] * Kc;
+    const uint8_t* br = B + jj[p] * Kc;
+    double s = 0.0;
+    for (int64_t k = 0; k < Kc; ++k) s += fabs(dec(fa, ar[k]) * dec(fb, br[k]));
+    out[p] = s * fabs((double)(float)(inv_a[ii[p]] * inv_b[jj[p]]));
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* O-4b Delayed scaling [PT-CH20 §20.5.9: each FP8 op keeps an amax history   */
 /*      of its input; every step takes the scale from the amax of earlier    */
 /*      steps, casts with it, and records the current amax].  The history is */
