@@ -36,9 +36,11 @@ LOSS_SCALE = 65536.0
 # benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
 # what the same counter reads for a 1 GiB device-to-device copy
 # (bench.py --copy-reference: FETCH_SIZE 524,302 KiB -> x2.0, WRITE_SIZE
-# 1,048,576 KiB -> x1.0).  Valid only for the GEMM source they were taken on;
-# bench.py reports null for any other.
-GEMM_TRAFFIC = {"gemm_src_sha256_16": "9085a2c22a5e8a9c", "fetch_kib": 49248.0, "write_kib": 32768.0,
+# 1,048,576 KiB -> x1.0).  Valid only for the GEMM kernel source they were
+# taken on (the kernel templates, since moved to gemm_kernels.hpp unchanged:
+# the per-tensor instantiations assemble to the same instructions); bench.py
+# reports null for any other.
+GEMM_TRAFFIC = {"gemm_src_sha256_16": "109131220fee30f2", "fetch_kib": 49248.0, "write_kib": 32768.0,
                 "fetch_factor": 2.0, "write_factor": 1.0}
 
 
@@ -217,7 +219,7 @@ def main():
     gemm_tflops = 2.0 * M * N * K / (gemm_avg_us * 1e-6) / 1e12
     traffic = None
     import hashlib
-    src = os.path.join(ROOT, "fp8_scaled_gemm_amd", "csrc", "gemm.hip")
+    src = os.path.join(ROOT, "fp8_scaled_gemm_amd", "csrc", "gemm_kernels.hpp")
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     if (M, N, K) == (4096, 4096, 4096) and digest == GEMM_TRAFFIC["gemm_src_sha256_16"]:
         traffic = 1024.0 * (GEMM_TRAFFIC["fetch_kib"] * GEMM_TRAFFIC["fetch_factor"] +

@@ -1,5 +1,6 @@
-"""Python binding of libfp8sg, the MI355X (gfx950) FP8 per-tensor scaled linear
-layer and GradScaler step.
+"""Python binding of libfp8sg, the MI355X (gfx950) FP8 scaled linear layer
+(per-tensor dynamic or delayed scaling, or row-wise scaling) and GradScaler
+step.
 
 Argument marshalling only: every function forwards torch device tensors as raw
 pointers and sizes to the C ABI declared in include/fp8sg.h (same names, same
@@ -23,7 +24,9 @@ SCALE_REC_BYTES = 32 + 4 * AMAX_PARTS
 EXPORTS = ("fp8sg_status_string", "fp8sg_version", "amp_norm_workspace_len", "fp8_amax",
            "fp8_quantize", "fp8_quantize_delayed", "fp8_gemm", "fp8_scaled_linear_fwd",
            "fp8_scaled_linear_fwd_delayed", "fp8_scaled_linear_bwd", "fp8_scaled_linear_bwd_delayed",
-           "amp_unscale_check", "amp_unscale_check_norm", "amp_update_scale")
+           "amp_unscale_check", "amp_unscale_check_norm", "amp_update_scale",
+           "fp8_quantize_rowwise", "fp8_gemm_rowwise", "fp8_scaled_linear_fwd_rowwise",
+           "fp8_scaled_linear_bwd_rowwise")
 MAX_HISTORY = 1024
 
 
@@ -38,6 +41,17 @@ class _Saved(ctypes.Structure):
 
 class _BwdWs(ctypes.Structure):
     _fields_ = [("gy_q", ctypes.c_void_p), ("gy_qT", ctypes.c_void_p), ("gy_sc", ctypes.c_void_p)]
+
+
+class _SavedRW(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x_q", "x_qT", "w_q", "w_qT", "x_row_amax", "x_row_inv", "x_col_amax", "x_col_inv",
+        "w_row_amax", "w_row_inv", "w_col_amax", "w_col_inv")]
+
+
+class _BwdWsRW(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "gy_q", "gy_qT", "gy_row_amax", "gy_row_inv", "gy_col_amax", "gy_col_inv")]
 
 
 _lib = None
@@ -74,6 +88,12 @@ def lib():
     L.amp_norm_workspace_len.restype = i64
     L.amp_unscale_check_norm.argtypes = [ctypes.POINTER(P), ctypes.POINTER(i64), i32, P, P, P, i64,
                                          P, P]
+    L.fp8_quantize_rowwise.argtypes = [P, i64, i64, i, P, P, P, P, P, P, P]
+    L.fp8_gemm_rowwise.argtypes = [P, i, P, i, P, P, P, i, i64, i64, i64, P]
+    L.fp8_scaled_linear_fwd_rowwise.argtypes = [P, P, i64, i64, i64, ctypes.POINTER(_SavedRW), P,
+                                                i, P]
+    L.fp8_scaled_linear_bwd_rowwise.argtypes = [P, ctypes.POINTER(_SavedRW), i64, i64, i64,
+                                                ctypes.POINTER(_BwdWsRW), P, P, i, P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = i
     _lib = L
@@ -254,6 +274,104 @@ def fp8_scaled_linear_bwd_delayed(gy, saved: LinearSaved, ws: LinearBwdWs, hist_
                                                _ptr(hist_gy), _hist(hist_gy), _ptr(gx), _ptr(gw),
                                                out, _stream(stream)),
            "fp8_scaled_linear_bwd_delayed")
+
+
+# ----------------------------------------------------------------- row-wise
+
+class RowScalesDev:
+    """A row-wise scale-vector pair: amax float32[n], inv float64[n]."""
+
+    def __init__(self, n, device="cuda", amax=None, inv=None):
+        self.amax = amax if amax is not None else torch.empty(n, dtype=torch.float32, device=device)
+        self.inv = inv if inv is not None else torch.empty(n, dtype=torch.float64, device=device)
+
+
+def fp8_quantize_rowwise(x: torch.Tensor, fmt: int, rows_sc: RowScalesDev, q: torch.Tensor,
+                         cols_sc: RowScalesDev = None, qT: torch.Tensor = None, stream=None):
+    """Row-wise cast of a [rows, cols] bf16 matrix: q with one scale per row
+    (rows_sc), and with qT the transposed copy with one scale per column
+    (cols_sc)."""
+    rows, cols = x.shape
+    ca = cols_sc.amax if cols_sc is not None else None
+    ci = cols_sc.inv if cols_sc is not None else None
+    _check(lib().fp8_quantize_rowwise(_ptr(x), rows, cols, fmt, _ptr(rows_sc.amax),
+                                      _ptr(rows_sc.inv), _ptr(q), _ptr(ca), _ptr(ci), _ptr(qT),
+                                      _stream(stream)), "fp8_quantize_rowwise")
+
+
+def fp8_gemm_rowwise(A: torch.Tensor, fa: int, B: torch.Tensor, fb: int, inv_a: torch.Tensor,
+                     inv_b: torch.Tensor, C: torch.Tensor, out: int, stream=None):
+    """C[M,N] = A[M,K] . B[N,K]^T * fl32(inv_a[m] * inv_b[n]) (float64 vectors)."""
+    M, K = A.shape
+    N, K2 = B.shape
+    assert K == K2 and tuple(C.shape) == (M, N)
+    _check(lib().fp8_gemm_rowwise(_ptr(A), fa, _ptr(B), fb, _ptr(inv_a), _ptr(inv_b), _ptr(C),
+                                  out, M, N, K, _stream(stream)), "fp8_gemm_rowwise")
+
+
+class LinearSavedRW:
+    """Device buffers the row-wise forward fills for the backward pass: codes
+    of x and W by rows and (transposed) by columns, with their scale vectors."""
+
+    NAMES = ("x_q", "x_qT", "w_q", "w_qT", "x_row_amax", "x_row_inv", "x_col_amax", "x_col_inv",
+             "w_row_amax", "w_row_inv", "w_col_amax", "w_col_inv")
+
+    def __init__(self, M, N, K, device="cuda", tensors=None):
+        if tensors is None:
+            u8 = dict(dtype=torch.uint8, device=device)
+            f32 = dict(dtype=torch.float32, device=device)
+            f64 = dict(dtype=torch.float64, device=device)
+            tensors = (torch.empty((M, K), **u8), torch.empty((K, M), **u8),
+                       torch.empty((N, K), **u8), torch.empty((K, N), **u8),
+                       torch.empty(M, **f32), torch.empty(M, **f64),
+                       torch.empty(K, **f32), torch.empty(K, **f64),
+                       torch.empty(N, **f32), torch.empty(N, **f64),
+                       torch.empty(K, **f32), torch.empty(K, **f64))
+        for n, t in zip(self.NAMES, tensors):
+            setattr(self, n, t)
+
+    def tensors(self):
+        return tuple(getattr(self, n) for n in self.NAMES)
+
+    def struct(self):
+        return _SavedRW(*[getattr(self, n).data_ptr() for n in self.NAMES])
+
+
+class LinearBwdWsRW:
+    NAMES = ("gy_q", "gy_qT", "gy_row_amax", "gy_row_inv", "gy_col_amax", "gy_col_inv")
+
+    def __init__(self, M, N, device="cuda"):
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.gy_q = torch.empty((M, N), **u8)
+        self.gy_qT = torch.empty((N, M), **u8)
+        self.gy_row_amax = torch.empty(M, dtype=torch.float32, device=device)
+        self.gy_row_inv = torch.empty(M, dtype=torch.float64, device=device)
+        self.gy_col_amax = torch.empty(N, dtype=torch.float32, device=device)
+        self.gy_col_inv = torch.empty(N, dtype=torch.float64, device=device)
+
+    def struct(self):
+        return _BwdWsRW(*[getattr(self, n).data_ptr() for n in self.NAMES])
+
+
+def fp8_scaled_linear_fwd_rowwise(x, w, saved: LinearSavedRW, y, out: int = OUT_BF16,
+                                  stream=None):
+    M, K = x.shape
+    N = w.shape[0]
+    s = saved.struct()
+    _check(lib().fp8_scaled_linear_fwd_rowwise(_ptr(x), _ptr(w), M, N, K, ctypes.byref(s),
+                                               _ptr(y), out, _stream(stream)),
+           "fp8_scaled_linear_fwd_rowwise")
+
+
+def fp8_scaled_linear_bwd_rowwise(gy, saved: LinearSavedRW, ws: LinearBwdWsRW, gx, gw,
+                                  out: int = OUT_BF16, stream=None):
+    M, N = gy.shape
+    K = saved.x_q.shape[1]
+    s = saved.struct()
+    b = ws.struct()
+    _check(lib().fp8_scaled_linear_bwd_rowwise(_ptr(gy), ctypes.byref(s), M, N, K,
+                                               ctypes.byref(b), _ptr(gx), _ptr(gw), out,
+                                               _stream(stream)), "fp8_scaled_linear_bwd_rowwise")
 
 
 def amp_unscale_check(grads, scale: torch.Tensor, found_inf: torch.Tensor, stream=None):

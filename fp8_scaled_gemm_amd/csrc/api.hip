@@ -24,6 +24,14 @@ fp8sg_status hip_status(hipError_t e) { return e == hipSuccess ? FP8SG_OK : FP8S
 bool hist_len_ok(int32_t h) { return h >= 1 && h <= FP8SG_MAX_HISTORY; }
 bool hist_ok(const float* h) { return h && (reinterpret_cast<uintptr_t>(h) & 3u) == 0; }
 hipStream_t S(fp8sg_stream s) { return reinterpret_cast<hipStream_t>(s); }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// A scale-vector pair (amax float[n], inv double[n]) of a row-wise cast.
+fp8sg_status check_vec(const float* amax, const double* inv, int64_t n) {
+  if (n > 0 && (!amax || !inv)) return FP8SG_ERR_NULL;
+  if (!aligned(amax, 4) || !aligned(inv, 8)) return FP8SG_ERR_ALIGN;
+  return FP8SG_OK;
+}
 
 fp8sg_status check_gemm(const void* A, int fa, const void* B, int fb, const void* ia,
                         const void* ib, const void* C, int out, int64_t M, int64_t N, int64_t K) {
@@ -109,9 +117,51 @@ fp8sg_status fp8_gemm(const uint8_t* A, fp8sg_format fa, const uint8_t* B, fp8sg
   return hip_status(launch_gemm(p, fa, fb, out, S(stream)));
 }
 
+fp8sg_status fp8_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols, fp8sg_format fmt,
+                                  float* row_amax, double* row_inv, uint8_t* q, float* col_amax,
+                                  double* col_inv, uint8_t* qT, fp8sg_stream stream) {
+  if (!fmt_ok(fmt)) return FP8SG_ERR_FORMAT;
+  if (!dims16(rows) || !dims16(cols)) return FP8SG_ERR_SHAPE;
+  if (rows * cols > 0 && (!x || !q)) return FP8SG_ERR_NULL;
+  fp8sg_status st = check_vec(row_amax, row_inv, rows);
+  if (st != FP8SG_OK) return st;
+  const bool with_t = col_amax || col_inv || qT;
+  if (with_t) {
+    st = check_vec(col_amax, col_inv, cols);
+    if (st != FP8SG_OK) return st;
+    if (rows * cols > 0 && !qT) return FP8SG_ERR_NULL;
+  }
+  if (!aligned16(x) || !aligned16(q) || !aligned16(qT)) return FP8SG_ERR_ALIGN;
+  RowwiseArgs a{x, rows, cols, row_amax, row_inv, q, col_amax, col_inv, qT, 0};
+  return hip_status(launch_rowwise(a, fmt, S(stream)));
+}
+
+fp8sg_status fp8_gemm_rowwise(const uint8_t* A, fp8sg_format fa, const uint8_t* B, fp8sg_format fb,
+                              const double* inv_a, const double* inv_b, void* C, fp8sg_out out,
+                              int64_t M, int64_t N, int64_t Kc, fp8sg_stream stream) {
+  fp8sg_status st = check_gemm(A, fa, B, fb, inv_a, inv_b, C, out, M, N, Kc);
+  if (st != FP8SG_OK) return st;
+  if (!aligned(inv_a, 8) || !aligned(inv_b, 8)) return FP8SG_ERR_ALIGN;
+  GemmProblem p{A, B, C, inv_a, inv_b, M, N, Kc};
+  return hip_status(launch_gemm_rowwise(p, fa, fb, out, S(stream)));
+}
+
 }  // extern "C"
 
 namespace {
+
+fp8sg_status check_saved_rw(const fp8_linear_saved_rw* s, int64_t M, int64_t N, int64_t K) {
+  if (!s || !s->x_q || !s->x_qT || !s->w_q || !s->w_qT) return FP8SG_ERR_NULL;
+  if (!aligned16(s->x_q) || !aligned16(s->x_qT) || !aligned16(s->w_q) || !aligned16(s->w_qT))
+    return FP8SG_ERR_ALIGN;
+  const fp8sg_status sts[4] = {check_vec(s->x_row_amax, s->x_row_inv, M),
+                               check_vec(s->x_col_amax, s->x_col_inv, K),
+                               check_vec(s->w_row_amax, s->w_row_inv, N),
+                               check_vec(s->w_col_amax, s->w_col_inv, K)};
+  for (fp8sg_status st : sts)
+    if (st != FP8SG_OK) return st;
+  return FP8SG_OK;
+}
 
 // Forward [FP8-TRAIN §4 forward, §6]: codes and transposed copies of x and W
 // (dynamic: one amax launch over both, then one quantize launch; delayed: one
@@ -224,6 +274,60 @@ fp8sg_status fp8_scaled_linear_bwd_delayed(const uint16_t* gy, const fp8_linear_
                                            fp8sg_out out, fp8sg_stream stream) {
   if (!hist_gy) return FP8SG_ERR_NULL;
   return linear_bwd(gy, saved, M, N, K, ws, hist_gy, history_len, gx, gw, out, stream);
+}
+
+// Row-wise forward [FP8-TRAIN §1, §4 forward]: x and W cast with one scale per
+// row (codes for this GEMM) and one per column (transposed copies for the
+// backward GEMMs), then y = x_q . w_q^T scaled by x_row_inv[m] * w_row_inv[n].
+fp8sg_status fp8_scaled_linear_fwd_rowwise(const uint16_t* x, const uint16_t* w, int64_t M,
+                                           int64_t N, int64_t K, const fp8_linear_saved_rw* saved,
+                                           void* y, fp8sg_out out, fp8sg_stream stream) {
+  if (!x || !w || !y) return FP8SG_ERR_NULL;
+  if (!out_ok(out)) return FP8SG_ERR_FORMAT;
+  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K)) return FP8SG_ERR_SHAPE;
+  fp8sg_status st = check_saved_rw(saved, M, N, K);
+  if (st != FP8SG_OK) return st;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return FP8SG_ERR_ALIGN;
+  hipStream_t s = S(stream);
+  const fp8_linear_saved_rw& v = *saved;
+  RowwiseArgs ax{x, M, K, v.x_row_amax, v.x_row_inv, v.x_q, v.x_col_amax, v.x_col_inv, v.x_qT, 0};
+  if (launch_rowwise(ax, FP8SG_E4M3FN, s) != hipSuccess) return FP8SG_ERR_HIP;
+  RowwiseArgs aw{w, N, K, v.w_row_amax, v.w_row_inv, v.w_q, v.w_col_amax, v.w_col_inv, v.w_qT, 0};
+  if (launch_rowwise(aw, FP8SG_E4M3FN, s) != hipSuccess) return FP8SG_ERR_HIP;
+  GemmProblem p{v.x_q, v.w_q, y, v.x_row_inv, v.w_row_inv, M, N, K};
+  return hip_status(launch_gemm_rowwise(p, FP8SG_E4M3FN, FP8SG_E4M3FN, out, s));
+}
+
+// Row-wise backward [FP8-TRAIN §1, §4 backward]: gy cast by rows and by
+// columns (e5m2); dgrad from gy_q (rows of gy) and w_qT (columns of W), wgrad
+// from gy_qT (columns of gy) and x_qT (columns of x): every scale lies along a
+// dimension the GEMM does not contract.
+fp8sg_status fp8_scaled_linear_bwd_rowwise(const uint16_t* gy, const fp8_linear_saved_rw* saved,
+                                           int64_t M, int64_t N, int64_t K,
+                                           const fp8_linear_bwd_ws_rw* ws, void* gx, void* gw,
+                                           fp8sg_out out, fp8sg_stream stream) {
+  if (!gy || !ws || !gx || !gw) return FP8SG_ERR_NULL;
+  if (!out_ok(out)) return FP8SG_ERR_FORMAT;
+  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K)) return FP8SG_ERR_SHAPE;
+  fp8sg_status st = check_saved_rw(saved, M, N, K);
+  if (st != FP8SG_OK) return st;
+  if (!ws->gy_q || !ws->gy_qT) return FP8SG_ERR_NULL;
+  st = check_vec(ws->gy_row_amax, ws->gy_row_inv, M);
+  if (st != FP8SG_OK) return st;
+  st = check_vec(ws->gy_col_amax, ws->gy_col_inv, N);
+  if (st != FP8SG_OK) return st;
+  if (!aligned16(gy) || !aligned16(gx) || !aligned16(gw) || !aligned16(ws->gy_q) ||
+      !aligned16(ws->gy_qT))
+    return FP8SG_ERR_ALIGN;
+  hipStream_t s = S(stream);
+  const fp8_linear_saved_rw& v = *saved;
+  RowwiseArgs ag{gy, M, N, ws->gy_row_amax, ws->gy_row_inv, ws->gy_q, ws->gy_col_amax,
+                 ws->gy_col_inv, ws->gy_qT, 0};
+  if (launch_rowwise(ag, FP8SG_E5M2, s) != hipSuccess) return FP8SG_ERR_HIP;
+  GemmProblem dg{ws->gy_q, v.w_qT, gx, ws->gy_row_inv, v.w_col_inv, M, K, N};
+  if (launch_gemm_rowwise(dg, FP8SG_E5M2, FP8SG_E4M3FN, out, s) != hipSuccess) return FP8SG_ERR_HIP;
+  GemmProblem wg{ws->gy_qT, v.x_qT, gw, ws->gy_col_inv, v.x_col_inv, N, K, M};
+  return hip_status(launch_gemm_rowwise(wg, FP8SG_E5M2, FP8SG_E4M3FN, out, s));
 }
 
 fp8sg_status amp_unscale_check(uint16_t* const* grads, const int64_t* numel, int32_t ntensors,

@@ -1,538 +1,11 @@
-// Scaled FP8 GEMM on gfx950 matrix cores:
-//   C[M,N] = out( (sum_k dec(A[m,k]) * dec(B[n,k])) * fl32(inv_a * inv_b) )
-// [FP8-TRAIN §2 (dequantise by the product of the two inverse scales), §4 (the
-// forward, dgrad and wgrad products), AMP-MP "不要忘记 Accumulator Precision"
-// (low-precision multiply, fp32 accumulate)].
-//
-// Both operands are contiguous along the contraction (the quantizer writes the
-// transposed copies the backward GEMMs need), so one kernel form serves all
-// three GEMMs.  Every FP8 x FP8 product is exact in fp32 and the matrix cores
-// accumulate in fp32; only the summation order differs from a sequential loop.
-//
-// Two kernels, one arithmetic: each wave issues v_mfma_f32_16x16x128_f8f6f4
-// with the operand formats (e4m3 = 0, e5m2 = 1) selected per operand.  The B
-// fragment is passed as the instruction's first source so each lane's four
-// accumulators are four consecutive output columns.  LDS tiles hold 16-byte
-// chunks XOR-swizzled by row so the fragment reads hit distinct banks.
-//   - k_gemm_pingpong: 256 x 256 tiles, for problems with at least 128 of
-//     them (fills the chip).
-//   - k_gemm: 128 x 128 tiles with register-staged loads, for smaller problems.
-#include <type_traits>
-
-#include "common.hpp"
-#include "launch.hpp"
+// Scaled FP8 GEMM with per-tensor inverse scales: the instantiations of the
+// kernels in gemm_kernels.hpp for alpha = fl32(inv_a * inv_b).
+#include "gemm_kernels.hpp"
 
 namespace fp8sg {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-constexpr int kBK = 128;  // bytes (= FP8 elements) of K per tile
-
-template <int BM, int BN, int WM, int WN>
-struct GemmCfg {
-  static constexpr int kThreads = WM * WN * kWave;
-  static constexpr int kTM = BM / WM / 16;  // 16-row MFMA blocks per wave
-  static constexpr int kTN = BN / WN / 16;
-  static constexpr int kChunksA = BM * (kBK / 16);  // 16-byte chunks per k-tile
-  static constexpr int kChunksB = BN * (kBK / 16);
-  static constexpr int kLoadsA = kChunksA / kThreads;
-  static constexpr int kLoadsB = kChunksB / kThreads;
-  static constexpr int kLdsBytes = 2 * (BM + BN) * kBK;
-  static_assert(kChunksA % kThreads == 0 && kChunksB % kThreads == 0, "tile/threads");
-};
-
-// byte offset of 16-byte chunk c of row r inside a [rows][128 B] LDS tile
-__device__ __forceinline__ int lds_off(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4); }
-
-template <int OUT>
-__device__ __forceinline__ void store4(void* C, int64_t idx, v4f v) {
-  if constexpr (OUT == FP8SG_OUT_F32) {
-    *reinterpret_cast<v4f*>(reinterpret_cast<float*>(C) + idx) = v;
-  } else if constexpr (OUT == FP8SG_OUT_BF16) {
-    typedef __bf16 b4 __attribute__((ext_vector_type(4)));
-    b4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-    *reinterpret_cast<b4*>(reinterpret_cast<uint16_t*>(C) + idx) = h;
-  } else {
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    h4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-    *reinterpret_cast<h4*>(reinterpret_cast<uint16_t*>(C) + idx) = h;
-  }
-}
-
-// Small-problem kernel: a BM x BN block tile per workgroup, K consumed 128
-// bytes at a time.  Each k-tile of A and B is fetched with 16-byte global loads
-// into registers while the previous tile is being multiplied, then written to
-// the other half of a double-buffered LDS tile.  Each wave owns a (BM/WM) x
-// (BN/WN) sub-tile of 16 x 16 blocks; results are stored as one 8-byte
-// (bf16/fp16) or 16-byte (fp32) write per lane and block.
-template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT>
-__global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
-  using Cfg = GemmCfg<BM, BN, WM, WN>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* As = smem;                  // [2][BM][128]
-  uint8_t* Bs = smem + 2 * BM * kBK;   // [2][BN][128]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int wm = wave / WN, wn = wave % WN;
-  const int64_t bm = (int64_t)blockIdx.y * BM;
-  const int64_t bn = (int64_t)blockIdx.x * BN;
-  const int64_t M = p.M, N = p.N, K = p.K;
-  const int nk = (int)((K + kBK - 1) / kBK);
-
-  // global -> register prefetch of one k-tile
-  uint4 ra[Cfg::kLoadsA], rb[Cfg::kLoadsB];
-  auto load_tile = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * kBK;
-#pragma unroll
-    for (int i = 0; i < Cfg::kLoadsA; ++i) {
-      const int c = tid + i * Cfg::kThreads;
-      const int r = c >> 3, kc = c & 7;
-      const int64_t gr = bm + r, gk = k0 + 16 * kc;
-      ra[i] = (gr < M && gk < K) ? *reinterpret_cast<const uint4*>(p.A + gr * K + gk)
-                                 : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg::kLoadsB; ++i) {
-      const int c = tid + i * Cfg::kThreads;
-      const int r = c >> 3, kc = c & 7;
-      const int64_t gr = bn + r, gk = k0 + 16 * kc;
-      rb[i] = (gr < N && gk < K) ? *reinterpret_cast<const uint4*>(p.B + gr * K + gk)
-                                 : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint8_t* a = As + buf * BM * kBK;
-    uint8_t* b = Bs + buf * BN * kBK;
-#pragma unroll
-    for (int i = 0; i < Cfg::kLoadsA; ++i) {
-      const int c = tid + i * Cfg::kThreads;
-      *reinterpret_cast<uint4*>(a + lds_off(c >> 3, c & 7)) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg::kLoadsB; ++i) {
-      const int c = tid + i * Cfg::kThreads;
-      *reinterpret_cast<uint4*>(b + lds_off(c >> 3, c & 7)) = rb[i];
-    }
-  };
-
-  v4f acc[Cfg::kTM][Cfg::kTN];
-#pragma unroll
-  for (int i = 0; i < Cfg::kTM; ++i)
-#pragma unroll
-    for (int j = 0; j < Cfg::kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // fragment of a 16 x 128 block: lane holds row (lane & 15), K bytes
-  // [32 * (lane >> 4), +32) as two 16-byte chunks.  A and B use the same K
-  // mapping, so the products pair up correctly whatever order the
-  // instruction sums them in.
-  const int frow = lane & 15;
-  const int fchunk = 2 * (lane >> 4);
-
-  if (nk > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
-    const uint8_t* a = As + buf * BM * kBK;
-    const uint8_t* b = Bs + buf * BN * kBK;
-    v8i bf[Cfg::kTN];
-#pragma unroll
-    for (int j = 0; j < Cfg::kTN; ++j) {
-      const int r = wn * (BN / WN) + 16 * j + frow;
-      const uint4 lo = *reinterpret_cast<const uint4*>(b + lds_off(r, fchunk));
-      const uint4 hi = *reinterpret_cast<const uint4*>(b + lds_off(r, fchunk + 1));
-      bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg::kTM; ++i) {
-      const int r = wm * (BM / WM) + 16 * i + frow;
-      const uint4 lo = *reinterpret_cast<const uint4*>(a + lds_off(r, fchunk));
-      const uint4 hi = *reinterpret_cast<const uint4*>(a + lds_off(r, fchunk + 1));
-      const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-      for (int j = 0; j < Cfg::kTN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], FB, FA,
-                                                                     0, 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds C[m][n..n+3] of each 16x16 block
-  const float alpha = (float)(*p.inv_a * *p.inv_b);
-#pragma unroll
-  for (int i = 0; i < Cfg::kTM; ++i) {
-    const int64_t m = bm + wm * (BM / WM) + 16 * i + (lane & 15);
-    if (m >= M) continue;
-#pragma unroll
-    for (int j = 0; j < Cfg::kTN; ++j) {
-      const int64_t n = bn + wn * (BN / WN) + 16 * j + 4 * (lane >> 4);
-      if (n >= N) continue;  // N % 16 == 0: the four columns are all in or all out
-      v4f c = acc[i][j];
-      c[0] *= alpha;
-      c[1] *= alpha;
-      c[2] *= alpha;
-      c[3] *= alpha;
-      store4<OUT>(p.C, m * N + n, c);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Large-tile kernel helpers.  Operand tiles are streamed global -> LDS by the
-// buffer unit (buffer_load_dwordx4 ... lds), with no VGPR staging.  One load
-// instruction moves 64 lanes x 16 B = 1 KB = 8 rows of a 128-byte k-slice;
-// lane l fills LDS row 8g + l/8, chunk l%8, and fetches the global chunk that
-// belongs there under the swizzle.  The per-block buffer descriptor spans only
-// the block's row panel, so rows past M (or N) read as zero; chunks past K are
-// pointed outside the descriptor and read as zero too.
-// ---------------------------------------------------------------------------
-
-// 16-byte chunk c of LDS row r lives at chunk c ^ swz16(r).  swz16 is a
-// bijection on every aligned group of 8 rows and on the even and the odd rows
-// of every aligned group of 16, so the 16-byte fragment reads hit distinct
-// banks whether the LDS serves 8 lanes x 16 B or 16 lanes x 16 B per cycle.
-// It depends on r & 15 only, so a lane's fragment-read address differs
-// between 16-row blocks by a constant that fits the instruction's offset.
-__device__ __forceinline__ int swz16(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
-__device__ __forceinline__ int lds_off2(int r, int c) { return r * kBK + ((c ^ swz16(r)) << 4); }
-
-// s_waitcnt with vmcnt <= n and the other counters untouched (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-constexpr uint32_t kBufDword3 = 0x00020000u;  // raw buffer, gfx9 data format
-constexpr uint32_t kOob = 0x80000000u;        // offset past any descriptor: reads 0
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor over [base, base + bytes), in scalar registers.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));  // stride 0
-  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-  r[3] = (int)kBufDword3;
-  return r;
-}
-
-// 16 bytes per lane from buffer offset `voff` into LDS at lds + 16 * lane.
-// Written as inline assembly so the compiler does not track these LDS writes:
-// its own wait insertion would otherwise drain every in-flight load before each
-// LDS read.  The k-loop below waits for them explicitly (s_waitcnt vmcnt) and
-// orders LDS reads with compiler barriers.  M0 carries the LDS address; no
-// other code in these kernels uses M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, i32x4 rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-
-#pragma clang diagnostic pop
-
-// LDS byte address of a __shared__ array (folds to a constant).
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-
-// Position of this block's tile.  Workgroups are handed to the 8 XCDs round
-// robin (block b on XCD b % 8); renumber so that each XCD gets a run of
-// consecutive tile indices, then walk tiles in groups of kGroupM tile-rows,
-// column by column, so one XCD's tiles form a compact region whose A and B
-// panels its L2 can share.
-constexpr int kGroupM = 4;
-__device__ __forceinline__ void tile_of(int nbm, int nbn, int& tm, int& tn) {
-  const int nb = nbm * nbn;
-  const int b = blockIdx.x;
-  const int q = nb / 8, rem = nb % 8, x = b % 8;
-  const int t = x * q + (x < rem ? x : rem) + b / 8;
-  const int per_group = kGroupM * nbn;
-  const int g = t / per_group, r = t % per_group;
-  const int gm = (nbm - g * kGroupM) < kGroupM ? (nbm - g * kGroupM) : kGroupM;
-  tm = g * kGroupM + r % gm;
-  tn = r / gm;
-}
-
-// ---------------------------------------------------------------------------
-// Large-tile kernel: 256 x 256 output tile per workgroup, K consumed 128 bytes
-// at a time, 8 waves in two groups of four (one wave of each group per SIMD).
-// Group g owns output rows [128 g, 128 g + 128); wave q of a group owns
-// columns [64 q, 64 q + 64), i.e. 8 x 4 blocks of 16 x 16.
-//
-// The groups run half a k-tile apart and alternate between
-//   - a memory phase: issue this group's share of the global -> LDS loads,
-//     then read all 12 operand fragments of the next k-tile (8 A, 4 B; 96
-//     VGPRs) from LDS, and
-//   - a compute phase: 32 MFMAs on registers only, nothing to wait for,
-// meeting at a workgroup barrier at every swap.  So each SIMD always has one
-// wave feeding its matrix pipe while the other waits on LDS and memory.
-//
-// LDS (160 KB): A of k-tile t in A stage t % 2, B of k-tile t in B slot
-// t % 3.  Group 0 loads A of t + 1 during its memory phase for t (that stage
-// held A of t - 1, which both groups read before the last swap); group 1
-// loads B of t + 2 during its memory phase for t (that slot held B of t - 1).
-// Each load is waited for (s_waitcnt vmcnt) by the wave that issued it before
-// the swap ahead of the first read, so the barrier publishes it to all waves.
-// ---------------------------------------------------------------------------
-template <int FA, int FB, int OUT, bool RAGGED_K>
-__global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
-  constexpr int BM = 256, BN = 256;
-  constexpr int kTM = 8, kTN = 4;
-  constexpr int kLoads = 256 / 8 / 4;  // 1 KB loads per group wave per operand half-stage: 8
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[256 * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[256 * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[256 * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[256 * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB2[256 * kBK];
-  auto sa = [&](auto i) -> uint8_t* { if constexpr (decltype(i)::value == 0) return sA0; else return sA1; };
-  auto sb = [&](auto i) -> uint8_t* {
-    constexpr int I = decltype(i)::value;
-    if constexpr (I == 0) return sB0;
-    else if constexpr (I == 1) return sB1;
-    else return sB2;
-  };
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int grp = wave >> 2, wq = wave & 3;
-  const int64_t M = p.M, N = p.N, K = p.K;
-  const int nbm = (int)((M + BM - 1) / BM), nbn = (int)((N + BN - 1) / BN);
-  int tm, tn;
-  tile_of(nbm, nbn, tm, tn);
-  const int64_t bm = (int64_t)tm * BM, bn = (int64_t)tn * BN;
-  const int nk = (int)((K + kBK - 1) / kBK);
-  const int64_t rows_a = (M - bm) < BM ? (M - bm) : BM;
-  const int64_t rows_b = (N - bn) < BN ? (N - bn) : BN;
-  const i32x4 ra = make_rsrc(p.A + bm * K, rows_a * K);
-  const i32x4 rb = make_rsrc(p.B + bn * K, rows_b * K);
-
-  // One operand half-stage (256 rows x 128 B) by wave q of a group: rows
-  // [64 q, 64 q + 64), 8 loads of 8 rows.  Lane l of load i fills LDS row
-  // 8 (8 q + i) + l / 8; the swizzle of that row depends only on i & 1, so a
-  // lane needs two offsets (even and odd i) and the rest is scalar.  Only a
-  // ragged last k-tile (RAGGED_K) needs the per-lane test against K.
-  const int lr = lane >> 3;
-  const int cl0 = (lane & 7) ^ swz16(lr), cl1 = (lane & 7) ^ swz16(8 + lr);
-  const uint32_t vo0 = (uint32_t)(lr * K + 16 * cl0), vo1 = (uint32_t)(lr * K + 16 * cl1);
-  auto issue = [&](int kt, uint32_t dst, const i32x4& rs) {  // kt >= nk loads zeros
-    const int k0 = kt < nk ? kt * kBK : (int)K;
-    const uint32_t sbase = (uint32_t)(64 * wq * K + k0);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      uint32_t off = ((i & 1) ? vo1 : vo0) + sbase + (uint32_t)(8 * i * K);
-      if constexpr (RAGGED_K) {
-        if (k0 + 16 * ((i & 1) ? cl1 : cl0) >= K) off = kOob;
-      } else {
-        if (kt >= nk) off = kOob;
-      }
-      lds_dma16(dst + (wq * kLoads + i) * 1024, off, rs);
-    }
-  };
-  v4f acc[kTM][kTN];
-#pragma unroll
-  for (int i = 0; i < kTM; ++i)
-#pragma unroll
-    for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  const int frow = lane & 15;
-  const int fchunk = 2 * (lane >> 4);
-  auto frag = [&](const uint8_t* base, int blk) {
-    const int r = 16 * blk + frow;
-    const uint4 lo = *reinterpret_cast<const uint4*>(base + lds_off2(r, fchunk));
-    const uint4 hi = *reinterpret_cast<const uint4*>(base + lds_off2(r, fchunk + 1));
-    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  };
-  const int ra0 = grp * 8, rb0 = wq * 4;
-  v8i af[kTM], bf[kTN];
-  auto barrier = [&]() {
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-  };
-
-  // Prologue: group 0 loads A0, group 1 loads B0 and B1.
-  if (grp == 0) {
-    issue(0, lds_u32(sA0), ra);
-    wait_vmcnt<0>();
-  } else {
-    issue(0, lds_u32(sB0), rb);
-    issue(1, lds_u32(sB1), rb);
-    wait_vmcnt<kLoads>();
-  }
-  barrier();
-  if (grp == 1) barrier();  // group 1 starts half a k-tile later
-
-  // k-tile t: memory phase (loads, then all 12 fragments), swap, compute
-  // phase, swap.  Group 0 loads A of t + 1 (its stage held A of t - 1, read
-  // by both groups before the last swap) and waits for it before the swap
-  // that ends its compute phase.  Group 1 loads B of t + 2 (its slot held B
-  // of t - 1) and, before the swap that ends this memory phase, waits for B of
-  // t + 1, issued one k-tile earlier.
-  auto step = [&](auto pc, int t) {
-    constexpr int P = decltype(pc)::value;  // t % 6
-    const uint8_t* a = sa(std::integral_constant<int, P % 2>{});
-    const uint8_t* b = sb(std::integral_constant<int, P % 3>{});
-    {
-      const uint32_t da = lds_u32(sa(std::integral_constant<int, (P + 1) % 2>{}));
-      const uint32_t db = lds_u32(sb(std::integral_constant<int, (P + 2) % 3>{}));
-      issue(t + 1 + grp, grp ? db : da, grp ? rb : ra);
-    }
-#pragma unroll
-    for (int j = 0; j < kTN; ++j) bf[j] = frag(b, rb0 + j);
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) af[i] = frag(a, ra0 + i);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    if (grp == 1) wait_vmcnt<kLoads>();  // B of t + 1 has landed
-    barrier();
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kTN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], FB,
-                                                                     FA, 0, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (grp == 0) wait_vmcnt<0>();  // A of t + 1 has landed
-    barrier();
-  };
-  for (int t = 0;;) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (++t == nk) break;
-    step(std::integral_constant<int, 1>{}, t);
-    if (++t == nk) break;
-    step(std::integral_constant<int, 2>{}, t);
-    if (++t == nk) break;
-    step(std::integral_constant<int, 3>{}, t);
-    if (++t == nk) break;
-    step(std::integral_constant<int, 4>{}, t);
-    if (++t == nk) break;
-    step(std::integral_constant<int, 5>{}, t);
-    if (++t == nk) break;
-  }
-  if (grp == 0) barrier();
-
-  const float alpha = (float)(*p.inv_a * *p.inv_b);
-  const int wr0 = grp * 128, wc0 = wq * 64;
-  if constexpr (OUT == FP8SG_OUT_F32) {
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) {
-      const int64_t m = bm + wr0 + 16 * i + (lane & 15);
-      if (m >= M) continue;
-#pragma unroll
-      for (int j = 0; j < kTN; ++j) {
-        const int64_t n = bn + wc0 + 16 * j + 4 * (lane >> 4);
-        if (n >= N) continue;
-        v4f c = acc[i][j];
-        c[0] *= alpha;
-        c[1] *= alpha;
-        c[2] *= alpha;
-        c[3] *= alpha;
-        store4<OUT>(p.C, m * N + n, c);
-      }
-    }
-  } else {
-    constexpr int kRowBytes = 2 * BN;
-    auto crow = [&](int r) -> uint8_t* {
-      uint8_t* base = r < 64 ? sA0 : r < 128 ? sA1 : r < 192 ? sB0 : sB1;
-      return base + (r & 63) * kRowBytes;
-    };
-    __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing a slot
-    barrier();
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) {
-      const int r = wr0 + 16 * i + (lane & 15);
-#pragma unroll
-      for (int j = 0; j < kTN; ++j) {
-        const int col = wc0 + 16 * j + 4 * (lane >> 4);
-        v4f c = acc[i][j];
-        c[0] *= alpha;
-        c[1] *= alpha;
-        c[2] *= alpha;
-        c[3] *= alpha;
-        const int off = (((col >> 3) ^ (r & 31)) << 4) + (col & 7) * 2;
-        store4<OUT>(crow(r) + off, 0, c);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    barrier();
-    constexpr int kChunks = BN / 8;
-    constexpr int kRowsPerPass = 512 / kChunks;
-    const int cc = threadIdx.x % kChunks;
-#pragma unroll
-    for (int pass = 0; pass < BM / kRowsPerPass; ++pass) {
-      const int r = pass * kRowsPerPass + threadIdx.x / kChunks;
-      const uint4 v = *reinterpret_cast<const uint4*>(crow(r) + ((cc ^ (r & 31)) << 4));
-      const int64_t m = bm + r, n = bn + 8 * cc;
-      if (m < M && n < N)
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + m * N + n) = v;
-    }
-  }
-}
-
-template <int FA, int FB, int OUT>
-static hipError_t launch_pingpong(const GemmProblem& p, hipStream_t stream) {
-  const unsigned nb = (unsigned)(((p.M + 255) / 256) * ((p.N + 255) / 256));
-  if (p.K % kBK == 0)
-    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, false>), dim3(nb), dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, true>), dim3(nb), dim3(512), 0, stream, p);
-  return hipGetLastError();
-}
-
-template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT>
-static hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
-  using Cfg = GemmCfg<BM, BN, WM, WN>;
-  auto kern = k_gemm<BM, BN, WM, WN, FA, FB, OUT>;
-  static bool attr_set = false;
-  if (!attr_set && Cfg::kLdsBytes > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
-  hipLaunchKernelGGL(kern, grid, dim3(Cfg::kThreads), Cfg::kLdsBytes, stream, p);
-  return hipGetLastError();
-}
-
-template <int FA, int FB, int OUT>
-static hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
-  // 256 x 256 tiles once there are enough of them to fill the chip; the
-  // per-block buffer descriptors address a 256-row panel with 32-bit offsets
-  const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (big >= 128 && p.K * 256 < (1ll << 31)) return launch_pingpong<FA, FB, OUT>(p, stream);
-  return launch_cfg<128, 128, 2, 2, FA, FB, OUT>(p, stream);
-}
-
-template <int FA, int FB>
-static hipError_t launch_out(const GemmProblem& p, int out, hipStream_t stream) {
-  switch (out) {
-    case FP8SG_OUT_BF16: return launch_tiles<FA, FB, FP8SG_OUT_BF16>(p, stream);
-    case FP8SG_OUT_F16: return launch_tiles<FA, FB, FP8SG_OUT_F16>(p, stream);
-    default: return launch_tiles<FA, FB, FP8SG_OUT_F32>(p, stream);
-  }
-}
-
 hipError_t launch_gemm(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream) {
-  if (p.M == 0 || p.N == 0) return hipSuccess;
-  if (fa == FP8SG_E4M3FN && fb == FP8SG_E4M3FN) return launch_out<0, 0>(p, out, stream);
-  if (fa == FP8SG_E5M2 && fb == FP8SG_E4M3FN) return launch_out<1, 0>(p, out, stream);
-  if (fa == FP8SG_E4M3FN && fb == FP8SG_E5M2) return launch_out<0, 1>(p, out, stream);
-  return launch_out<1, 1>(p, out, stream);
+  return launch_gemm_any<false>(p, fa, fb, out, stream);
 }
 
 }  // namespace fp8sg

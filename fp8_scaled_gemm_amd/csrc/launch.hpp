@@ -62,6 +62,24 @@ struct GemmProblem {
   int64_t M, N, K;
 };
 hipError_t launch_gemm(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);
+// Row-wise scaling (gemm_rowwise.hip): inv_a points to M doubles, inv_b to N;
+// element (m, n) is scaled by fl32(inv_a[m] * inv_b[n]).
+hipError_t launch_gemm_rowwise(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);
+
+// ---- row-wise quantize (rowwise.hip)
+struct RowwiseArgs {
+  const uint16_t* x;
+  int64_t rows, cols;  // multiples of 16
+  float* row_amax;     // [rows]
+  double* row_inv;     // [rows]
+  uint8_t* q;          // [rows, cols], codes with the row scales
+  float* col_amax;     // [cols] (with qT)
+  double* col_inv;     // [cols] (with qT)
+  uint8_t* qT;         // [cols, rows], codes with the column scales; may be null
+  int32_t tiles_c;     // filled by the launcher
+};
+// Three launches: zero the amax vectors, reduce them, cast.
+hipError_t launch_rowwise(const RowwiseArgs& a, int fmt, hipStream_t stream);
 
 // ---- GradScaler (amp.hip)
 // Norm workspace slots of the unscale pass for these tensors (exact; needs the

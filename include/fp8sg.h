@@ -228,6 +228,96 @@ FP8SG_API fp8sg_status fp8_scaled_linear_bwd_delayed(const uint16_t* gy, const f
                                    fp8sg_out out, fp8sg_stream stream);
 
 /*
+ * Row-wise scaling [FP8-TRAIN §1: instead of one scale per tensor, each row
+ * gets its own scale factor, which the accumulation has to carry through].
+ * For a rows x cols bf16 matrix x and each row i:
+ *   row_amax[i] = max_j |x[i,j]|   (fp32; canonical NaN if the row has a NaN)
+ *   s_i = fp8_max / max(row_amax[i], EPS) in fp64, row_inv[i] = 1.0 / s_i
+ *   q[i,j] = enc(clamp(fl32(x[i,j] * fl32(s_i)), -max, max))
+ * i.e. each row is cast exactly as fp8_quantize casts a one-row tensor.  With
+ * qT, the same per column j (col_amax[j], col_inv[j]) and
+ *   qT[j,i] = the code of x[i,j] at column j's scale,
+ * the row-wise cast of x^T: the operand a GEMM contracting over the rows of x
+ * needs (its codes differ from the transpose of q).
+ *   x: rows x cols bf16, row-major; rows, cols >= 0 and multiples of 16.
+ *   row_amax: device float[rows] (4-byte aligned), row_inv: device
+ *   double[rows] (8-byte aligned), both written; q: rows x cols codes.
+ *   qT: cols x rows codes; col_amax: float[cols], col_inv: double[cols],
+ *   written.  All three NULL skips the transposed cast; otherwise all three
+ *   are required (qT may be NULL when rows * cols == 0).
+ * Three kernels on `stream` (zero the maxima, reduce them, cast).  An empty
+ * dimension leaves the other one's maxima 0 (scale of amax 0).
+ */
+FP8SG_API fp8sg_status fp8_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols,
+                                  fp8sg_format fmt, float* row_amax, double* row_inv,
+                                  uint8_t* q, float* col_amax, double* col_inv, uint8_t* qT,
+                                  fp8sg_stream stream);
+
+/*
+ * Scaled FP8 GEMM with row-wise scales [FP8-TRAIN §1]: as fp8_gemm, with
+ * element (m, n) scaled by fl32(inv_a[m] * inv_b[n]):
+ *   C[m,n] = out( (sum_k dec(A[m,k]) * dec(B[n,k])) * fl32(inv_a[m] * inv_b[n]) )
+ * (each scale is constant along the contraction, so it factors out of the sum).
+ *   inv_a: device double[M], inv_b: device double[N], 8-byte aligned.
+ * The other arguments as fp8_gemm.
+ */
+FP8SG_API fp8sg_status fp8_gemm_rowwise(const uint8_t* A, fp8sg_format fa, const uint8_t* B,
+                              fp8sg_format fb, const double* inv_a, const double* inv_b,
+                              void* C, fp8sg_out out, int64_t M, int64_t N, int64_t Kc,
+                              fp8sg_stream stream);
+
+/*
+ * What the row-wise forward saves [FP8-TRAIN §1, §6]: codes and scale vectors
+ * of x [M,K] and W [N,K], by rows (the forward GEMM) and by columns (the
+ * transposed copies the backward GEMMs contract).  Caller-owned device
+ * buffers; amax vectors 4-byte, inverse vectors 8-byte, codes 16-byte aligned.
+ */
+typedef struct fp8_linear_saved_rw {
+  uint8_t* x_q;        /* [M,K] codes, one scale per row of x     */
+  uint8_t* x_qT;       /* [K,M] codes, one scale per column of x  */
+  uint8_t* w_q;        /* [N,K] codes, one scale per row of W     */
+  uint8_t* w_qT;       /* [K,N] codes, one scale per column of W  */
+  float* x_row_amax;   /* [M] */
+  double* x_row_inv;   /* [M] */
+  float* x_col_amax;   /* [K] */
+  double* x_col_inv;   /* [K] */
+  float* w_row_amax;   /* [N] */
+  double* w_row_inv;   /* [N] */
+  float* w_col_amax;   /* [K] */
+  double* w_col_inv;   /* [K] */
+} fp8_linear_saved_rw;
+
+/* Row-wise backward workspace: gy [M,N] cast by rows and by columns. */
+typedef struct fp8_linear_bwd_ws_rw {
+  uint8_t* gy_q;       /* [M,N] e5m2 codes, one scale per row     */
+  uint8_t* gy_qT;      /* [N,M] e5m2 codes, one scale per column  */
+  float* gy_row_amax;  /* [M] */
+  double* gy_row_inv;  /* [M] */
+  float* gy_col_amax;  /* [N] */
+  double* gy_col_inv;  /* [N] */
+} fp8_linear_bwd_ws_rw;
+
+/*
+ * The FP8 linear layer with row-wise scaling [FP8-TRAIN §1, §4].
+ * Forward: x and W cast as fp8_quantize_rowwise (e4m3, with transposed
+ * copies), then y = x_q . w_q^T scaled by x_row_inv[m] * w_row_inv[n].
+ * Backward: gy cast the same way in e5m2, then
+ *   gx[M,K] = gy_q . w_qT^T     scaled by gy_row_inv[m] * w_col_inv[k]
+ *   gW[N,K] = gy_qT . x_qT^T    scaled by gy_col_inv[n] * x_col_inv[k]
+ * so every scale lies along a dimension its GEMM does not contract.
+ * Shapes, outputs and errors as fp8_scaled_linear_fwd / _bwd; `saved` must
+ * come from the row-wise forward with the same M, N, K.
+ */
+FP8SG_API fp8sg_status fp8_scaled_linear_fwd_rowwise(const uint16_t* x, const uint16_t* w,
+                                   int64_t M, int64_t N, int64_t K,
+                                   const fp8_linear_saved_rw* saved, void* y, fp8sg_out out,
+                                   fp8sg_stream stream);
+FP8SG_API fp8sg_status fp8_scaled_linear_bwd_rowwise(const uint16_t* gy,
+                                   const fp8_linear_saved_rw* saved, int64_t M, int64_t N,
+                                   int64_t K, const fp8_linear_bwd_ws_rw* ws, void* gx, void* gw,
+                                   fp8sg_out out, fp8sg_stream stream);
+
+/*
  * GradScaler unscale + non-finite check over a list of fp16 gradients
  * [PT-CH20 §20.2.2: unscale the gradients, then check for inf/NaN;
  *  AMP-NOTES §4 steps 3-4].  In place, for every element:

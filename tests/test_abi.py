@@ -157,6 +157,39 @@ def test_norm_workspace_and_validation():
     assert L.amp_unscale_check_norm(*args(need)) == EALIGN
 
 
+def test_rowwise_validation():
+    L = F.lib()
+    q = P(A16)
+    quant = lambda rows=16, cols=32, fmt=0, ra=A16, ri=A16, ca=A16, ci=A16, qT=A16, x=A16: \
+        L.fp8_quantize_rowwise(P(x), rows, cols, fmt, P(ra), P(ri), q, P(ca), P(ci), P(qT), P(0))
+    assert quant(fmt=2) == EFORMAT
+    assert quant(rows=8) == ESHAPE and quant(cols=-16) == ESHAPE
+    assert quant(x=0) == ENULL and quant(ra=0) == ENULL and quant(ci=0) == ENULL
+    assert quant(ra=A16 + 2) == EALIGN and quant(ri=A16 + 4) == EALIGN
+    assert quant(ca=A16 + 1) == EALIGN and quant(qT=MIS) == EALIGN
+    g = lambda ia=A16, ib=A16, M=16: L.fp8_gemm_rowwise(P(A16), 0, P(A16B), 1, P(ia), P(ib),
+                                                        P(A16B), 0, M, 16, 32, P(0))
+    assert g(ia=0) == ENULL and g(M=17) == ESHAPE and g(ib=A16 + 4) == EALIGN
+    s = F._SavedRW(*([A16] * 12))
+    ws = F._BwdWsRW(*([A16] * 6))
+    fwd = lambda s, M=16: L.fp8_scaled_linear_fwd_rowwise(P(A16), P(A16), M, 16, 32,
+                                                          ctypes.byref(s), P(A16), 0, P(0))
+    bwd = lambda s, ws: L.fp8_scaled_linear_bwd_rowwise(P(A16), ctypes.byref(s), 16, 16, 32,
+                                                        ctypes.byref(ws), P(A16), P(A16), 0, P(0))
+    assert fwd(s, M=0) == ESHAPE
+    for i, name in enumerate(F.LinearSavedRW.NAMES):
+        bad = F._SavedRW(*([A16] * 12))
+        setattr(bad, name, 0)
+        assert fwd(bad) == ENULL, name
+        setattr(bad, name, A16 + 2)
+        assert fwd(bad) == EALIGN, name
+        assert bwd(bad, ws) in (ENULL, EALIGN) and bwd(bad, ws) == EALIGN, name
+    for name in F.LinearBwdWsRW.NAMES:
+        bad = F._BwdWsRW(*([A16] * 6))
+        setattr(bad, name, 0)
+        assert bwd(s, bad) == ENULL, name
+
+
 def test_binding_refuses_a_missing_library(monkeypatch, tmp_path):
     # no fallback path: without the built library the binding raises
     monkeypatch.setattr(F, "_lib", None)
