@@ -187,6 +187,30 @@ def main():
     torch.cuda.synchronize()
     ms_delayed = d0.elapsed_time(d1) / args.steps
 
+    # ---- the same step with row-wise scaling (one scale per row of every
+    # operand along its non-contraction dimension)
+    saved_rw = F.LinearSavedRW(M, N, K, device=dev)
+    ws_rw = F.LinearBwdWsRW(M, N, device=dev)
+    y_rw, gx_rw, gw_rw = torch.empty_like(y), torch.empty_like(gx), torch.empty_like(gw)
+
+    def step_rowwise():
+        F.fp8_scaled_linear_fwd_rowwise(x, w, saved_rw, y_rw, F.OUT_BF16)
+        F.fp8_scaled_linear_bwd_rowwise(gy, saved_rw, ws_rw, gx_rw, gw_rw, F.OUT_F16)
+        F.amp_unscale_check([gx_rw, gw_rw], scale, found)
+        F.amp_update_scale(scale, tracker, found, 2.0, 0.5, 2000)
+
+    for _ in range(args.warmup):
+        step_rowwise()
+    torch.cuda.synchronize()
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for _ in range(args.steps):
+        step_rowwise()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    ms_rowwise = r0.elapsed_time(r1) / args.steps
+
     # ---- per-kernel timings on the same stream, same operands as the step
     log("per-kernel timings")
     T = Timer(torch, stream)
@@ -213,9 +237,16 @@ def main():
     kern["unscale_check_gx_gw"] = T.run(lambda: F.amp_unscale_check(g16, one, fz), args.reps)
     kern["update_scale"] = T.run(lambda: F.amp_update_scale(scale, tracker, found, 2.0, 0.5,
                                                             2000), args.reps)
-    del g16, q, qT
+    rs, cs = F.RowScalesDev(M, device=dev), F.RowScalesDev(K, device=dev)
+    kern["quantize_rowwise_transpose_x"] = T.run(
+        lambda: F.fp8_quantize_rowwise(x, F.E4M3FN, rs, q, cs, qT), args.reps)
+    kern["gemm_rowwise_fwd_e4m3xe4m3"] = T.run(lambda: F.fp8_gemm_rowwise(
+        saved_rw.x_q, F.E4M3FN, saved_rw.w_q, F.E4M3FN, saved_rw.x_row_inv, saved_rw.w_row_inv,
+        y_rw, F.OUT_BF16), args.reps)
+    del g16, q, qT, rs, cs
 
-    gemm_avg_us = sum(kern[k]["avg_us"] for k in kern if k.startswith("gemm")) / 3
+    gemm_avg_us = sum(kern[k]["avg_us"] for k in kern if k.startswith("gemm_")
+                      and "rowwise" not in k) / 3
     gemm_tflops = 2.0 * M * N * K / (gemm_avg_us * 1e-6) / 1e12
     traffic = None
     import hashlib
@@ -251,7 +282,17 @@ def main():
         r_del = T.run(lambda: F.fp8_quantize_delayed(big, F.E4M3FN, brec, bh, bq), 10)
         hbm["quantize_delayed_GBps"] = 3.0 * nb / (r_del["avg_us"] * 1e-6) / 1e9
         kern["quantize_delayed_2p28"] = r_del
-        del big, bq, bh
+        # row-wise: amax pass (2 B/elem) + cast with the transposed copy
+        # (2 B read + 2 B written), the tensor as a 16384 x 16384 matrix
+        side = 1 << 14
+        big2 = big.view(side, side)
+        bqT = torch.empty((side, side), dtype=torch.uint8, device=dev)
+        brs, bcs = F.RowScalesDev(side, device=dev), F.RowScalesDev(side, device=dev)
+        r_rw = T.run(lambda: F.fp8_quantize_rowwise(big2, F.E4M3FN, brs, bq.view(side, side), bcs,
+                                                     bqT), 10)
+        hbm["quantize_rowwise_transpose_GBps"] = 6.0 * nb / (r_rw["avg_us"] * 1e-6) / 1e9
+        kern["quantize_rowwise_transpose_2p28"] = r_rw
+        del big, bq, bh, big2, bqT
         log("HBM-scale unscale pass")
         sizes = C.scaler_sizes()
         grads = [(torch.randn(int(n), device=dev) * 0.5).half() for n in sizes]
@@ -280,7 +321,10 @@ def main():
     check = None
     if not args.no_check:
         log("sampled oracle check")
+        step()  # the delayed-scaling step shares these buffers: restore the dynamic step's
+        torch.cuda.synchronize()
         check = sampled_check(np, torch, F, x_h, w_h, gy_s_h, saved, ws, y, M, N, K)
+        check["rowwise"] = sampled_check_rowwise(np, torch, x_h, w_h, saved_rw, y_rw, M, N, K)
 
     # ---- oracle on the host cores, bounded sample
     cpu = None
@@ -310,6 +354,8 @@ def main():
         "step_delayed_scaling": {"ms_per_step": round(ms_delayed, 4),
                                  "TFLOPs": round(gemm_flops / (ms_delayed * 1e-3) / 1e12, 2),
                                  "history": 16},
+        "step_rowwise_scaling": {"ms_per_step": round(ms_rowwise, 4),
+                                 "TFLOPs": round(gemm_flops / (ms_rowwise * 1e-3) / 1e12, 2)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
@@ -409,6 +455,30 @@ def sampled_check(np, torch, F, x_h, w_h, gy_h, saved, ws, y, M, N, K, n_pts=256
     y_h = y.view(torch.int16).cpu().numpy().view(np.uint16)[ii, jj]
     nw = check_gemm_values(O.decode(O.BF16, y_h), c_ref, ad, K, O.BF16, "bench y")
     return {"codes_and_scales": "bit-exact", "gemm_fwd_samples": n_pts, "ok": True,
+            "max_abs_err_over_max_abs": float(nw)}
+
+
+def sampled_check_rowwise(np, torch, x_h, w_h, saved, y, M, N, K, n_pts=256):
+    """The row-wise step's forward: codes and scale vectors of x and W against
+    the oracle's row-wise cast, sampled outputs of y."""
+    import oracle as O
+    from tests.parity import assert_codes_equal, check_gemm_values
+    xq = O.to_fp8_rowwise(x_h, O.E4M3FN)
+    wq = O.to_fp8_rowwise(w_h, O.E4M3FN)
+    for got, ref in ((saved.x_q, xq.q), (saved.x_qT, xq.qT), (saved.w_q, wq.q),
+                     (saved.w_qT, wq.qT)):
+        assert_codes_equal(O.E4M3FN, got.cpu().numpy(), ref)
+    for got, ref in ((saved.x_row_inv, xq.rows.inv), (saved.x_col_inv, xq.cols.inv),
+                     (saved.w_row_inv, wq.rows.inv), (saved.w_col_inv, wq.cols.inv)):
+        assert np.array_equal(got.cpu().numpy().view(np.uint64), ref.view(np.uint64))
+    rng = np.random.default_rng(1)
+    ii = rng.integers(0, M, n_pts)
+    jj = rng.integers(0, N, n_pts)
+    c_ref = O.gemm_vec_at(xq.q, O.E4M3FN, wq.q, O.E4M3FN, xq.rows.inv, wq.rows.inv, ii, jj)
+    ad = O.gemm_absdot_vec_at(xq.q, O.E4M3FN, wq.q, O.E4M3FN, xq.rows.inv, wq.rows.inv, ii, jj)
+    y_h = y.view(torch.int16).cpu().numpy().view(np.uint16)[ii, jj]
+    nw = check_gemm_values(O.decode(O.BF16, y_h), c_ref, ad, K, O.BF16, "bench y rowwise")
+    return {"codes_and_scale_vectors": "bit-exact", "gemm_fwd_samples": n_pts, "ok": True,
             "max_abs_err_over_max_abs": float(nw)}
 
 

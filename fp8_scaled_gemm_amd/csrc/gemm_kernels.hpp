@@ -76,20 +76,36 @@ __device__ __forceinline__ void store4(void* C, int64_t idx, v4f v) {
 // inverse scale per row of A and of B, and element (m, n) is multiplied by
 // fl32(inv_a[m] * inv_b[n]) [FP8-TRAIN §1: each row's scale is carried
 // through the accumulation; constant along K, it factors out of the sum].
-template <bool RW>
+// A lane owns rows m0 + 16 i + (lane & 15) and columns n0 + 16 j + 4 (lane >> 4)
+// + e of its wave's TM x TN blocks; the row-wise factors it needs are loaded
+// once, after the main loop (rows and columns past M and N get 0, never stored).
+template <bool RW, int TM, int TN>
 struct Alpha {
-  const double* ia;
-  const double* ib;
   float a;
-  __device__ explicit Alpha(const GemmProblem& p) : ia(p.inv_a), ib(p.inv_b), a(0.f) {
-    if constexpr (!RW) a = (float)(*p.inv_a * *p.inv_b);
-  }
-  // c holds C[m][n .. n+3]; rows/columns past M/N get 0 (never stored)
-  __device__ void apply(v4f& c, int64_t m, int64_t n, int64_t M, int64_t N) const {
+  double ia[RW ? TM : 1];
+  double ib[RW ? TN : 1][4];
+  __device__ Alpha(const GemmProblem& p, int64_t m0, int64_t n0, int lane) {
     if constexpr (RW) {
-      const double am = m < M ? ia[m] : 0.0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c[e] *= (float)(am * (n + e < N ? ib[n + e] : 0.0));
+      for (int i = 0; i < TM; ++i) {
+        const int64_t m = m0 + 16 * i + (lane & 15);
+        ia[i] = m < p.M ? p.inv_a[m] : 0.0;
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t n = n0 + 16 * j + 4 * (lane >> 4);  // N % 16 == 0: all four in or out
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ib[j][e] = n < p.N ? p.inv_b[n + e] : 0.0;
+      }
+    } else {
+      a = (float)(*p.inv_a * *p.inv_b);
+    }
+  }
+  // c holds C[m][n .. n+3] of block (i, j)
+  __device__ void apply(v4f& c, int i, int j) const {
+    if constexpr (RW) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] *= (float)(ia[i] * ib[j][e]);
     } else {
       c[0] *= a;
       c[1] *= a;
@@ -198,7 +214,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
   }
 
   // epilogue: lane holds C[m][n..n+3] of each 16x16 block
-  const Alpha<RW> alpha(p);
+  const Alpha<RW, Cfg::kTM, Cfg::kTN> alpha(p, bm + wm * (BM / WM), bn + wn * (BN / WN), lane);
 #pragma unroll
   for (int i = 0; i < Cfg::kTM; ++i) {
     const int64_t m = bm + wm * (BM / WM) + 16 * i + (lane & 15);
@@ -208,7 +224,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
       const int64_t n = bn + wn * (BN / WN) + 16 * j + 4 * (lane >> 4);
       if (n >= N) continue;  // N % 16 == 0: the four columns are all in or all out
       v4f c = acc[i][j];
-      alpha.apply(c, m, n, M, N);
+      alpha.apply(c, i, j);
       store4<OUT>(p.C, m * N + n, c);
     }
   }
@@ -455,8 +471,8 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
   }
   if (grp == 0) barrier();
 
-  const Alpha<RW> alpha(p);
   const int wr0 = grp * 128, wc0 = wq * 64;
+  const Alpha<RW, kTM, kTN> alpha(p, bm + wr0, bn + wc0, lane);
   if constexpr (OUT == FP8SG_OUT_F32) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
@@ -467,7 +483,7 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
         const int64_t n = bn + wc0 + 16 * j + 4 * (lane >> 4);
         if (n >= N) continue;
         v4f c = acc[i][j];
-        alpha.apply(c, m, n, M, N);
+        alpha.apply(c, i, j);
         store4<OUT>(p.C, m * N + n, c);
       }
     }
@@ -486,7 +502,7 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
       for (int j = 0; j < kTN; ++j) {
         const int col = wc0 + 16 * j + 4 * (lane >> 4);
         v4f c = acc[i][j];
-        alpha.apply(c, bm + r, bn + col, M, N);
+        alpha.apply(c, i, j);
         const int off = (((col >> 3) ^ (r & 31)) << 4) + (col & 7) * 2;
         store4<OUT>(crow(r) + off, 0, c);
       }

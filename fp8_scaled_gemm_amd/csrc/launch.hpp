@@ -78,7 +78,8 @@ struct RowwiseArgs {
   uint8_t* qT;         // [cols, rows], codes with the column scales; may be null
   int32_t tiles_c;     // filled by the launcher
 };
-// Three launches: zero the amax vectors, reduce them, cast.
+// Three launches: per-tile partial maxima (stored in q's memory), their
+// reduction into the amax / inverse-scale vectors, the cast.
 hipError_t launch_rowwise(const RowwiseArgs& a, int fmt, hipStream_t stream);
 
 // ---- GradScaler (amp.hip)

@@ -85,23 +85,6 @@ __device__ __forceinline__ void publish_scale(fp8sg_scale_rec* rec, float amax, 
   }
 }
 
-// LDS tile: 128 rows x 32 dwords; dword column x of row r lives at x ^ swz(r).
-__device__ __forceinline__ int swz(int r) { return ((r >> 4) & 3) << 3; }
-
-// 4x4 byte transpose: out[j] byte i = in[i] byte j.
-__device__ __forceinline__ void tr4x4(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3,
-                                      uint32_t& o0, uint32_t& o1, uint32_t& o2, uint32_t& o3) {
-  // v_perm_b32(hi, lo, sel): selector bytes 0-3 pick lo's bytes, 4-7 hi's bytes
-  uint32_t e0 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);  // d0.b0 d1.b0 d0.b1 d1.b1
-  uint32_t e1 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);  // d0.b2 d1.b2 d0.b3 d1.b3
-  uint32_t f0 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
-  uint32_t f1 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
-  o0 = __builtin_amdgcn_perm(f0, e0, 0x05040100u);  // d0.b0 d1.b0 d2.b0 d3.b0
-  o1 = __builtin_amdgcn_perm(f0, e0, 0x07060302u);  // d0.b1 d1.b1 d2.b1 d3.b1
-  o2 = __builtin_amdgcn_perm(f1, e1, 0x05040100u);
-  o3 = __builtin_amdgcn_perm(f1, e1, 0x07060302u);
-}
-
 template <int FMT, bool S, bool DELAYED>
 __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
   int lb;

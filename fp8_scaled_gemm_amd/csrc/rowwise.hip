@@ -3,23 +3,29 @@
 // accumulation].  For a GEMM C = A . B^T contracting over K, A gets one scale
 // per row (over its K entries) and B one per row; both are constant along the
 // contraction, so they factor out of the dot product and the epilogue applies
-// alpha[m][n] = fl32(inv_a[m] * inv_b[n]) (gemm.hip, ROWWISE epilogue).  The
-// backward GEMMs contract over the other dimension of each operand, so the
-// transposed FP8 copy of a tensor is cast with one scale per column of the
-// tensor (= per row of the copy): its codes differ from the row-major ones.
+// alpha[m][n] = fl32(inv_a[m] * inv_b[n]) (gemm_rowwise.hip).  The backward
+// GEMMs contract over the other dimension of each operand, so the transposed
+// FP8 copy of a tensor is cast with one scale per column of the tensor (= per
+// row of the copy): its codes differ from the row-major ones.
 //
-// Two passes over x, as with per-tensor dynamic scaling:
-//   k_rw_amax:  per 128 x 128 tile, the maximum |x| of each row (16-lane
-//               shuffles) and of each column (shuffles, then LDS across the
-//               four waves), merged into the caller's amax vectors with
-//               unsigned atomic max on the fp32 bits (exact and order-free:
-//               non-negative IEEE values order like their bit patterns, NaN
-//               canonical above +inf).  The vectors start at zero (k_rw_zero).
-//   k_rw_quant: per tile, the 128 row scales and 128 column scales (fp64, as
-//               for a tensor) into LDS; codes with the row scales stored
-//               directly, codes with the column scales staged in LDS and
-//               stored transposed.  The blocks of the first tile column
-//               (row) also write the row (column) inverse scales.
+// Three kernels, two passes over x:
+//   k_rw_amax:   per 128 x 128 tile, the maximum |x| of each of its rows
+//                (16-lane shuffles) and of each of its columns (shuffles, then
+//                LDS across the four waves), stored as fp32 bits (NaN
+//                canonical) into partial-maximum arrays.  The arrays live in
+//                the caller's q buffer, which the cast overwrites afterwards:
+//                no workspace and no atomics.
+//   k_rw_reduce: one lane per row (column): the maximum over its partials
+//                (unsigned max of the bits: non-negative IEEE values order
+//                like their bit patterns, NaN canonical above +inf), then the
+//                amax and inverse-scale vectors.
+//   k_rw_quant:  per tile, the 128 row scales and 128 column scales (fp64, as
+//                for a tensor) into LDS; codes with the row scales stored
+//                directly, codes with the column scales staged in LDS and
+//                stored transposed.
+// Passes that move 256 MiB or more load x with non-temporal loads; the code
+// stores stay cached (the 8 and 16-byte pieces of one 128-byte line come from
+// different lanes and are merged in L2; written around it they cost more).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -28,45 +34,82 @@ namespace fp8sg {
 constexpr int kRwThreads = 256;
 constexpr int kRwTile = 128;
 
-__global__ __launch_bounds__(kRwThreads) void k_rw_zero(float* a, int64_t na, float* b, int64_t nb) {
-  const int64_t i = (int64_t)blockIdx.x * kRwThreads + threadIdx.x;
-  if (i < na) a[i] = 0.0f;
-  if (b && i < nb) b[i] = 0.0f;
+// Partial maxima (fp32 bits) in the q buffer:
+//   prow[ct * rows + r] = max |x[r, c]| over column tile ct
+//   pcol[rt * cols + c] = max |x[r, c]| over row tile rt
+// 4 (rows * tiles_c + cols * tiles_r) bytes <= rows * cols for rows, cols >= 16.
+struct RwParts {
+  uint32_t* prow;
+  uint32_t* pcol;
+};
+__device__ __forceinline__ RwParts rw_parts(const RowwiseArgs& a) {
+  uint32_t* base = reinterpret_cast<uint32_t*>(a.q);
+  return {base, base + a.rows * a.tiles_c};
+}
+__host__ __device__ inline int64_t rw_tiles(int64_t n) { return (n + kRwTile - 1) / kRwTile; }
+
+// Block b -> tile (rt, ct): groups of 8 row tiles, walked down the rows first,
+// so 64 consecutive blocks cover 8 x 8 tiles and both the row-major and the
+// transposed stores of blocks in flight together form 1 KiB runs (a single
+// row band would put all transposed stores of the moment at one power-of-two
+// stride).
+__device__ __forceinline__ void rw_tile_of(int64_t b, int64_t tiles_r, int64_t tiles_c,
+                                           int64_t& rt, int64_t& ct) {
+  constexpr int64_t G = 8;
+  const int64_t per = G * tiles_c, g = b / per, first = g * G;
+  const int64_t gs = tiles_r - first < G ? tiles_r - first : G;
+  const int64_t w = b - g * per;
+  rt = first + w % gs;
+  ct = w / gs;
 }
 
-// the larger of the two bf16 magnitudes packed in m, as fp32 bits (NaN canonical)
-__device__ __forceinline__ uint32_t pair_bits(uint32_t m) { return absmax_bits(m); }
+// packed bf16 pair maximum (16-bit unsigned) -> the two fp32 bit patterns, NaN canonical
+__device__ __forceinline__ void unpack_max(uint32_t d, uint32_t& lo, uint32_t& hi) {
+  lo = (d & 0xFFFFu) << 16;
+  hi = d & 0xFFFF0000u;
+  lo = lo > 0x7F800000u ? 0x7FC00000u : lo;
+  hi = hi > 0x7F800000u ? 0x7FC00000u : hi;
+}
 
-template <bool WITH_T>
+template <bool WITH_T, bool S>
 __global__ __launch_bounds__(kRwThreads) void k_rw_amax(RowwiseArgs a) {
   const int tid = threadIdx.x;
   const int64_t rows = a.rows, cols = a.cols;
-  const int64_t r_tile = (int64_t)(blockIdx.x / a.tiles_c) * kRwTile;
-  const int64_t c_tile = (int64_t)(blockIdx.x % a.tiles_c) * kRwTile;
+  int64_t rt, ct;
+  rw_tile_of(blockIdx.x, rw_tiles(a.rows), a.tiles_c, rt, ct);
+  const int64_t r_tile = rt * kRwTile, c_tile = ct * kRwTile;
+  const RwParts pp = rw_parts(a);
   const int c8 = tid & 15, r0 = tid >> 4;
   const int64_t gc = c_tile + 8 * c8;
   const bool col_ok = gc < cols;  // cols % 16 == 0: a group of 8 is all in or all out
+  __shared__ uint32_t srow[kRwTile];
+  __shared__ uint4 red[kRwThreads / kWave][16];
+
+  uint4 v[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int64_t gr = r_tile + r0 + 16 * p;
+    v[p] = (col_ok && gr < rows) ? ld16<S>(a.x + gr * cols + gc) : make_uint4(0, 0, 0, 0);
+  }
   constexpr uint32_t mask = 0x7FFF7FFFu;
   uint4 cm = make_uint4(0, 0, 0, 0);  // column maxima, two columns per dword
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    const int64_t gr = r_tile + r0 + 16 * p;
-    const uint4 v = (col_ok && gr < rows) ? *reinterpret_cast<const uint4*>(a.x + gr * cols + gc)
-                                          : make_uint4(0, 0, 0, 0);
-    uint32_t b = pair_bits(absmax8(0u, v));  // this thread's 8 values of row gr
+    uint32_t b = absmax_bits(absmax8(0u, v[p]));  // this thread's 8 values of row r0 + 16p
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) {  // the 16 lanes of a row are consecutive
       const uint32_t o = (uint32_t)__shfl_xor((int)b, off, kWave);
       b = o > b ? o : b;
     }
-    if (c8 == 0 && gr < rows) atomicMax(reinterpret_cast<unsigned int*>(a.row_amax) + gr, b);
+    if (c8 == 0) srow[r0 + 16 * p] = b;
     if constexpr (WITH_T) {
-      cm.x = pmax(cm.x, v.x & mask);
-      cm.y = pmax(cm.y, v.y & mask);
-      cm.z = pmax(cm.z, v.z & mask);
-      cm.w = pmax(cm.w, v.w & mask);
+      cm.x = pmax(cm.x, v[p].x & mask);
+      cm.y = pmax(cm.y, v[p].y & mask);
+      cm.z = pmax(cm.z, v[p].z & mask);
+      cm.w = pmax(cm.w, v[p].w & mask);
     }
   }
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
   if constexpr (WITH_T) {
     // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same 8 columns
 #pragma unroll
@@ -76,29 +119,81 @@ __global__ __launch_bounds__(kRwThreads) void k_rw_amax(RowwiseArgs a) {
       cm.z = pmax(cm.z, (uint32_t)__shfl_xor((int)cm.z, off, kWave));
       cm.w = pmax(cm.w, (uint32_t)__shfl_xor((int)cm.w, off, kWave));
     }
-    __shared__ uint4 red[kRwThreads / kWave][16];
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
     if (lane < 16) red[wave][lane] = cm;
-    __syncthreads();
-    if (tid < 16 && col_ok) {
-      uint4 m = red[0][tid];
+  }
+  __syncthreads();
+  // the tile's 128 row maxima: 32 lanes, 4 consecutive rows each
+  if (tid < kRwTile / 4) {
+    const int64_t gr = r_tile + 4 * tid;
+    if (gr < rows)  // rows % 16 == 0: four rows are all in or all out
+      *reinterpret_cast<uint4*>(pp.prow + ct * rows + gr) =
+          *reinterpret_cast<const uint4*>(&srow[4 * tid]);
+  }
+  if constexpr (WITH_T) {
+    if (tid >= kWave && tid < kWave + 16) {
+      const int c = tid - kWave;
+      const int64_t gcc = c_tile + 8 * c;
+      if (gcc < cols) {
+        uint4 m = red[0][c];
 #pragma unroll
-      for (int w = 1; w < kRwThreads / kWave; ++w) {
-        m.x = pmax(m.x, red[w][tid].x);
-        m.y = pmax(m.y, red[w][tid].y);
-        m.z = pmax(m.z, red[w][tid].z);
-        m.w = pmax(m.w, red[w][tid].w);
+        for (int w = 1; w < kRwThreads / kWave; ++w) {
+          m.x = pmax(m.x, red[w][c].x);
+          m.y = pmax(m.y, red[w][c].y);
+          m.z = pmax(m.z, red[w][c].z);
+          m.w = pmax(m.w, red[w][c].w);
+        }
+        uint4 o0, o1;
+        unpack_max(m.x, o0.x, o0.y);
+        unpack_max(m.y, o0.z, o0.w);
+        unpack_max(m.z, o1.x, o1.y);
+        unpack_max(m.w, o1.z, o1.w);
+        uint32_t* dst = pp.pcol + rt * cols + gcc;
+        *reinterpret_cast<uint4*>(dst) = o0;
+        *reinterpret_cast<uint4*>(dst + 4) = o1;
       }
-      unsigned int* ca = reinterpret_cast<unsigned int*>(a.col_amax) + gc;
-      const uint32_t d[4] = {m.x, m.y, m.z, m.w};
+    }
+  }
+}
+
+// One lane per row (then per column, with a transposed copy), 64 per block;
+// the four waves split the partials and meet in LDS.
+template <int FMT>
+__global__ __launch_bounds__(kRwThreads) void k_rw_reduce(RowwiseArgs a) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int64_t rows = a.rows, ncols = a.qT ? a.cols : 0;
+  const int64_t idx = (int64_t)blockIdx.x * kWave + lane;
+  const RwParts pp = rw_parts(a);
+  const bool is_row = idx < rows;
+  const uint32_t* src = is_row ? pp.prow + idx : pp.pcol + (idx - rows);
+  const int64_t stride = is_row ? rows : a.cols;
+  const int64_t nt = idx < rows + ncols ? (is_row ? a.tiles_c : rw_tiles(rows)) : 0;
+  constexpr int kWaves = kRwThreads / kWave;
+  constexpr int kUnroll = 8;
+  uint32_t m = 0;
+  for (int64_t t0 = wave; t0 < nt; t0 += kWaves * kUnroll) {
+    uint32_t u[kUnroll];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t lo = (d[k] & 0xFFFFu) << 16, hi = d[k] & 0xFFFF0000u;
-        lo = lo > 0x7F800000u ? 0x7FC00000u : lo;
-        hi = hi > 0x7F800000u ? 0x7FC00000u : hi;
-        atomicMax(ca + 2 * k, lo);
-        atomicMax(ca + 2 * k + 1, hi);
-      }
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t t = t0 + (int64_t)kWaves * k;
+      u[k] = t < nt ? src[t * stride] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) m = u[k] > m ? u[k] : m;
+  }
+  __shared__ uint32_t red[kWaves][kWave];
+  red[wave][lane] = m;
+  __syncthreads();
+  if (wave == 0 && nt > 0) {
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = red[w][lane] > m ? red[w][lane] : m;
+    const float amax = __uint_as_float(m);
+    const double inv = scale_from_amax(amax, FMT).inv;
+    if (is_row) {
+      a.row_amax[idx] = amax;
+      a.row_inv[idx] = inv;
+    } else {
+      a.col_amax[idx - rows] = amax;
+      a.col_inv[idx - rows] = inv;
     }
   }
 }
@@ -114,54 +209,34 @@ __device__ __forceinline__ uint2 quant8v(uint4 v, const float* s) {
   return make_uint2(cvt4<FMT>(f0, f1, f2, f3), cvt4<FMT>(f4, f5, f6, f7));
 }
 
-// LDS tile for the transposed store: dword column x of row r at x ^ rw_swz(r)
-__device__ __forceinline__ int rw_swz(int r) { return ((r >> 4) & 3) << 3; }
-
-__device__ __forceinline__ void rw_tr4x4(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3,
-                                         uint32_t& o0, uint32_t& o1, uint32_t& o2, uint32_t& o3) {
-  const uint32_t e0 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
-  const uint32_t e1 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);
-  const uint32_t f0 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
-  const uint32_t f1 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
-  o0 = __builtin_amdgcn_perm(f0, e0, 0x05040100u);
-  o1 = __builtin_amdgcn_perm(f0, e0, 0x07060302u);
-  o2 = __builtin_amdgcn_perm(f1, e1, 0x05040100u);
-  o3 = __builtin_amdgcn_perm(f1, e1, 0x07060302u);
-}
-
-template <int FMT, bool WITH_T>
+template <int FMT, bool WITH_T, bool S>
 __global__ __launch_bounds__(kRwThreads) void k_rw_quant(RowwiseArgs a) {
   const int tid = threadIdx.x;
   const int64_t rows = a.rows, cols = a.cols;
-  const int64_t r_tile = (int64_t)(blockIdx.x / a.tiles_c) * kRwTile;
-  const int64_t c_tile = (int64_t)(blockIdx.x % a.tiles_c) * kRwTile;
+  int64_t rt, ct;
+  rw_tile_of(blockIdx.x, rw_tiles(a.rows), a.tiles_c, rt, ct);
+  const int64_t r_tile = rt * kRwTile, c_tile = ct * kRwTile;
   __shared__ float srow[kRwTile], scol[kRwTile];
   __shared__ uint32_t lds[kRwTile * 32];
-
-  if (tid < kRwTile) {
-    const int64_t gr = r_tile + tid;
-    float s = 0.0f;
-    if (gr < rows) {
-      const ScaleVals sv = scale_from_amax(a.row_amax[gr], FMT);
-      s = sv.s32;
-      if (c_tile == 0) a.row_inv[gr] = sv.inv;
-    }
-    srow[tid] = s;
-  } else if (WITH_T) {
-    const int64_t gc = c_tile + (tid - kRwTile);
-    float s = 0.0f;
-    if (gc < cols) {
-      const ScaleVals sv = scale_from_amax(a.col_amax[gc], FMT);
-      s = sv.s32;
-      if (r_tile == 0) a.col_inv[gc] = sv.inv;
-    }
-    scol[tid - kRwTile] = s;
-  }
-  __syncthreads();
 
   const int c8 = tid & 15, r0 = tid >> 4;
   const int64_t gc = c_tile + 8 * c8;
   const bool col_ok = gc < cols;
+  uint4 v[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int64_t gr = r_tile + r0 + 16 * p;
+    v[p] = (col_ok && gr < rows) ? ld16<S>(a.x + gr * cols + gc) : make_uint4(0, 0, 0, 0);
+  }
+  if (tid < kRwTile) {
+    const int64_t gr = r_tile + tid;
+    srow[tid] = gr < rows ? scale_from_amax(a.row_amax[gr], FMT).s32 : 0.0f;
+  } else if (WITH_T) {
+    const int64_t gcc = c_tile + (tid - kRwTile);
+    scol[tid - kRwTile] = gcc < cols ? scale_from_amax(a.col_amax[gcc], FMT).s32 : 0.0f;
+  }
+  __syncthreads();
+
   float sc[8];
   if constexpr (WITH_T) {
 #pragma unroll
@@ -171,12 +246,9 @@ __global__ __launch_bounds__(kRwThreads) void k_rw_quant(RowwiseArgs a) {
   for (int p = 0; p < 8; ++p) {
     const int r = r0 + 16 * p;
     const int64_t gr = r_tile + r;
-    const uint4 v = (col_ok && gr < rows) ? *reinterpret_cast<const uint4*>(a.x + gr * cols + gc)
-                                          : make_uint4(0, 0, 0, 0);
-    if (col_ok && gr < rows)
-      *reinterpret_cast<uint2*>(a.q + gr * cols + gc) = quant8<FMT>(v, srow[r]);
+    if (col_ok && gr < rows) st8<false>(a.q + gr * cols + gc, quant8<FMT>(v[p], srow[r]));
     if constexpr (WITH_T)
-      *reinterpret_cast<uint2*>(&lds[r * 32 + ((2 * c8) ^ rw_swz(r))]) = quant8v<FMT>(v, sc);
+      *reinterpret_cast<uint2*>(&lds[r * 32 + ((2 * c8) ^ swz(r))]) = quant8v<FMT>(v[p], sc);
   }
   if constexpr (WITH_T) {
     __syncthreads();
@@ -185,41 +257,50 @@ __global__ __launch_bounds__(kRwThreads) void k_rw_quant(RowwiseArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 16 * rq + i;
-      d[i] = lds[r * 32 + (cq ^ rw_swz(r))];
+      d[i] = lds[r * 32 + (cq ^ swz(r))];
     }
     uint32_t o[4][4];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
-      rw_tr4x4(d[4 * b], d[4 * b + 1], d[4 * b + 2], d[4 * b + 3], o[0][b], o[1][b], o[2][b], o[3][b]);
+      tr4x4(d[4 * b], d[4 * b + 1], d[4 * b + 2], d[4 * b + 3], o[0][b], o[1][b], o[2][b], o[3][b]);
     const int64_t tr0 = r_tile + 16 * rq, tc0 = c_tile + 4 * cq;
     if (tr0 < rows && tc0 < cols) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(a.qT + (tc0 + j) * rows + tr0) =
-            make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]);
+        st16<false>(a.qT + (tc0 + j) * rows + tr0, make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]));
     }
   }
 }
 
-template <int FMT>
-static hipError_t launch_rw_fmt(RowwiseArgs a, hipStream_t stream) {
+template <int FMT, bool S>
+static hipError_t launch_rw_passes(const RowwiseArgs& a, int64_t nb, hipStream_t stream) {
   const bool with_t = a.qT != nullptr;
-  const int64_t nz = a.rows > a.cols ? a.rows : a.cols;
-  hipLaunchKernelGGL(k_rw_zero, dim3((unsigned)((nz + kRwThreads - 1) / kRwThreads)), dim3(kRwThreads),
-                     0, stream, a.row_amax, a.rows, with_t ? a.col_amax : nullptr, a.cols);
+  if (with_t) hipLaunchKernelGGL((k_rw_amax<true, S>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream, a);
+  else hipLaunchKernelGGL((k_rw_amax<false, S>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  a.tiles_c = (int32_t)((a.cols + kRwTile - 1) / kRwTile);
-  const int64_t nb = ((a.rows + kRwTile - 1) / kRwTile) * a.tiles_c;
-  if (with_t) hipLaunchKernelGGL(k_rw_amax<true>, dim3((unsigned)nb), dim3(kRwThreads), 0, stream, a);
-  else hipLaunchKernelGGL(k_rw_amax<false>, dim3((unsigned)nb), dim3(kRwThreads), 0, stream, a);
+  const int64_t nred = (a.rows + (with_t ? a.cols : 0) + kWave - 1) / kWave;
+  hipLaunchKernelGGL(k_rw_reduce<FMT>, dim3((unsigned)nred), dim3(kRwThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (with_t)
-    hipLaunchKernelGGL((k_rw_quant<FMT, true>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_rw_quant<FMT, true, S>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((k_rw_quant<FMT, false>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_rw_quant<FMT, false, S>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_rw_fmt(RowwiseArgs a, hipStream_t stream) {
+  a.tiles_c = (int32_t)rw_tiles(a.cols);
+  const int64_t tiles_r = rw_tiles(a.rows);
+  // the partial maxima must fit in q (they do for rows, cols >= 16)
+  const int64_t part_bytes = 4 * (a.rows * a.tiles_c + (a.qT ? a.cols * tiles_r : 0));
+  if (part_bytes > a.rows * a.cols) return hipErrorInvalidValue;
+  const int64_t nb = tiles_r * a.tiles_c;
+  const int64_t bytes = a.rows * a.cols * (a.qT ? 4 : 3);  // the cast's traffic
+  return bytes >= kStreamBytes ? launch_rw_passes<FMT, true>(a, nb, stream)
+                               : launch_rw_passes<FMT, false>(a, nb, stream);
 }
 
 // An empty dimension: the other dimension's rows (columns) are empty, so

@@ -245,8 +245,9 @@ FP8SG_API fp8sg_status fp8_scaled_linear_bwd_delayed(const uint16_t* gy, const f
  *   qT: cols x rows codes; col_amax: float[cols], col_inv: double[cols],
  *   written.  All three NULL skips the transposed cast; otherwise all three
  *   are required (qT may be NULL when rows * cols == 0).
- * Three kernels on `stream` (zero the maxima, reduce them, cast).  An empty
- * dimension leaves the other one's maxima 0 (scale of amax 0).
+ * Three kernels on `stream`: per-tile partial maxima (kept in q's memory,
+ * which the cast then overwrites), their reduction into the vectors, the
+ * cast.  An empty dimension leaves the other one's maxima 0 (scale of amax 0).
  */
 FP8SG_API fp8sg_status fp8_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols,
                                   fp8sg_format fmt, float* row_amax, double* row_inv,
