@@ -6,7 +6,7 @@ autograd and walks module trees.
   - Float8Linear / _Fp8LinearFn ["FP8训练：量化、自动微分、Torchao", §6: one
     autograd node per linear; the forward takes and returns plain bf16, FP8
     never leaves it; what is saved for the backward pass is the FP8 operands
-    and their inverse scales, not the bf16 inputs].
+    and their inverse scales, not the bf16 inputs; §1 for row-wise scaling].
   - convert_to_float8_training [same page, §8: post-order walk over the module
     tree, nn.Linear children replaced in place when module_filter_fn(module,
     fully qualified name) allows, the new module reusing the original weight
@@ -26,10 +26,13 @@ from typing import Callable, Optional
 import torch
 from torch import nn
 
-from . import (LinearBwdWs, LinearSaved, OUT_BF16, ScaleRec, amp_norm_workspace_len,
-               amp_unscale_check, amp_unscale_check_norm, amp_update_scale, fp8_amax,
-               fp8_scaled_linear_bwd, fp8_scaled_linear_bwd_delayed, fp8_scaled_linear_fwd,
-               fp8_scaled_linear_fwd_delayed)
+from . import (LinearBwdWs, LinearBwdWsRW, LinearSaved, LinearSavedRW, OUT_BF16, ScaleRec,
+               amp_norm_workspace_len, amp_unscale_check, amp_unscale_check_norm,
+               amp_update_scale, fp8_amax, fp8_scaled_linear_bwd, fp8_scaled_linear_bwd_delayed,
+               fp8_scaled_linear_bwd_rowwise, fp8_scaled_linear_fwd, fp8_scaled_linear_fwd_delayed,
+               fp8_scaled_linear_fwd_rowwise)
+
+SCALINGS = ("dynamic", "delayed", "rowwise")
 
 
 def _seed_history(hist: torch.Tensor, x: torch.Tensor):
@@ -43,14 +46,22 @@ def _seed_history(hist: torch.Tensor, x: torch.Tensor):
 
 class _Fp8LinearFn(torch.autograd.Function):
     """y = x W^T through the FP8 path; saves the FP8 codes (row-major and
-    transposed) and the two scale records for the backward pass."""
+    transposed) and the scale records (per-tensor) or scale vectors (row-wise)
+    for the backward pass."""
 
     @staticmethod
     def forward(ctx, x2d: torch.Tensor, weight: torch.Tensor, mod: "Float8Linear"):
         M, K = x2d.shape
         N = weight.shape[0]
-        saved = LinearSaved(M, N, K, device=x2d.device)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x2d.device)
+        ctx.mod = mod
+        ctx.dims = (M, N, K)
+        if mod.scaling == "rowwise":
+            saved = LinearSavedRW(M, N, K, device=x2d.device)
+            fp8_scaled_linear_fwd_rowwise(x2d, weight, saved, y, OUT_BF16)
+            ctx.save_for_backward(*saved.tensors())
+            return y
+        saved = LinearSaved(M, N, K, device=x2d.device)
         if mod.scaling == "delayed":
             if not mod._seeded_fwd:
                 _seed_history(mod.hist_x, x2d)
@@ -60,8 +71,6 @@ class _Fp8LinearFn(torch.autograd.Function):
         else:
             fp8_scaled_linear_fwd(x2d, weight, saved, y, OUT_BF16)
         ctx.save_for_backward(*saved.tensors())
-        ctx.mod = mod
-        ctx.dims = (M, N, K)
         return y
 
     @staticmethod
@@ -71,10 +80,15 @@ class _Fp8LinearFn(torch.autograd.Function):
         if gy.dtype != torch.bfloat16:
             raise TypeError(f"Float8Linear expects bf16 output gradients, got {gy.dtype}")
         gy = gy.contiguous()
-        saved = LinearSaved(M, N, K, tensors=ctx.saved_tensors)
-        ws = LinearBwdWs(M, N, device=gy.device)
         gx = torch.empty((M, K), dtype=torch.bfloat16, device=gy.device)
         gw = torch.empty((N, K), dtype=torch.bfloat16, device=gy.device)
+        if mod.scaling == "rowwise":
+            saved = LinearSavedRW(M, N, K, tensors=ctx.saved_tensors)
+            fp8_scaled_linear_bwd_rowwise(gy, saved, LinearBwdWsRW(M, N, device=gy.device), gx, gw,
+                                          OUT_BF16)
+            return gx, gw, None
+        saved = LinearSaved(M, N, K, tensors=ctx.saved_tensors)
+        ws = LinearBwdWs(M, N, device=gy.device)
         if mod.scaling == "delayed":
             if not mod._seeded_bwd:
                 _seed_history(mod.hist_gy, gy)
@@ -87,14 +101,16 @@ class _Fp8LinearFn(torch.autograd.Function):
 
 class Float8Linear(nn.Module):
     """nn.Linear (no bias) whose forward and backward GEMMs run in FP8 with
-    per-tensor scaling: "dynamic" (scale from the current tensor) or
-    "delayed" (scale from an amax history of history_len earlier steps)."""
+    per-tensor scaling, "dynamic" (scale from the current tensor) or
+    "delayed" (scale from an amax history of history_len earlier steps), or
+    with "rowwise" scaling (one scale per row of every operand along the
+    dimension its GEMM does not contract)."""
 
     def __init__(self, in_features: int, out_features: int, scaling: str = "dynamic",
                  history_len: int = 16, device=None):
         super().__init__()
-        if scaling not in ("dynamic", "delayed"):
-            raise ValueError(f"scaling must be 'dynamic' or 'delayed', not {scaling!r}")
+        if scaling not in SCALINGS:
+            raise ValueError(f"scaling must be one of {SCALINGS}, not {scaling!r}")
         self.in_features, self.out_features = in_features, out_features
         self.scaling = scaling
         self.weight = nn.Parameter(torch.empty((out_features, in_features), dtype=torch.bfloat16,

@@ -89,7 +89,42 @@ def test_float8_linear_delayed_steps_match_oracle():
         lin.weight.grad = None
 
 
-def test_converted_mlp_block_trains():
+def test_float8_linear_rowwise_autograd_matches_oracle():
+    M, K, N = 192, 160, 272
+    rng_rows = lambda seed, r, c, lo, hi: W.f32_to_bf16_bits(
+        (W.normal_f32(seed, 0, r * c, 1.0).reshape(r, c) *
+         (10.0 ** (lo + (hi - lo) * W.uniform(seed, 1, r)))[:, None]).astype(np.float32)).reshape(r, c)
+    x_h = rng_rows(63, M, K, -3, 2)
+    w_h = W.normal_bf16(63, 5, (N, K), 0.02)
+    gy_h = rng_rows(64, M, N, -6, -2)
+    lin = nn.Linear(K, N, bias=False, dtype=torch.bfloat16, device=DEV)
+    with torch.no_grad():
+        lin.weight.copy_(dev_bf16(w_h))
+    f8 = FN.Float8Linear.from_float(lin, scaling="rowwise")
+    x = dev_bf16(x_h, requires_grad=True)
+    y = f8(x)
+    node = y.grad_fn.next_functions[0][0]
+    # codes (4) and the amax / inverse-scale vectors (8): no bf16 input kept
+    assert len(node.saved_tensors) == 12
+    assert all(t.dtype in (torch.uint8, torch.float32, torch.float64) for t in node.saved_tensors)
+    y.backward(dev_bf16(gy_h))
+    torch.cuda.synchronize()
+    fw = O.linear_fwd_rowwise(x_h, w_h)
+    bw = O.linear_bwd_rowwise(gy_h, fw)
+    for got, ref, A, fa, B, ia, ib, Kc, what in (
+            (y, fw.c, fw.x.q, O.E4M3FN, fw.w.q, fw.x.rows.inv, fw.w.rows.inv, K, "y"),
+            (x.grad, bw.c_gx, bw.gy.q, O.E5M2, fw.w.qT, bw.gy.rows.inv, fw.w.cols.inv, N, "gx"),
+            (lin.weight.grad, bw.c_gw, bw.gy.qT, O.E5M2, fw.x.qT, bw.gy.cols.inv, fw.x.cols.inv, M,
+             "gw")):
+        ii, jj = [v.reshape(-1) for v in np.meshgrid(np.arange(ref.shape[0]),
+                                                      np.arange(ref.shape[1]), indexing="ij")]
+        ad = O.gemm_absdot_vec_at(A, fa, B, O.E4M3FN, ia, ib, ii, jj)
+        check_gemm_values(O.decode(O.BF16, host_u16(got)).reshape(-1), ref.reshape(-1), ad, Kc,
+                          O.BF16, what)
+
+
+@pytest.mark.parametrize("scaling", FN.SCALINGS)
+def test_converted_mlp_block_trains(scaling):
     """A SwiGLU block converted by convert_to_float8_training: forward and
     backward run through the FP8 kernels (the gating itself is torch), and
     stay within FP8 quantization error of the bf16 block."""
@@ -111,7 +146,7 @@ def test_converted_mlp_block_trains():
         nn.init.normal_(p, 0.0, 0.05)
     f8 = MLP().to(DEV)
     f8.load_state_dict(ref.state_dict())
-    FN.convert_to_float8_training(f8)
+    FN.convert_to_float8_training(f8, scaling=scaling)
     assert all(isinstance(getattr(f8, n), FN.Float8Linear) for n in ("gate", "up", "down"))
     x = torch.randn(T, H, device=DEV, dtype=torch.bfloat16)
     y_ref, y8 = ref(x.float().bfloat16()), f8(x)

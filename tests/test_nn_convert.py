@@ -75,3 +75,16 @@ def test_from_float_refuses_what_the_path_cannot_take():
         Float8Linear.from_float(lin(32, 32, bias=True))
     with pytest.raises(TypeError):
         Float8Linear.from_float(nn.Linear(32, 32, bias=False))  # fp32 weight
+
+
+def test_scaling_modes():
+    for scaling in ("dynamic", "delayed", "rowwise"):
+        m = convert_to_float8_training(Model(), scaling=scaling)
+        assert m.blocks[0].gate.scaling == scaling
+        assert hasattr(m.blocks[0].gate, "hist_x") == (scaling == "delayed")
+    try:
+        Float8Linear(16, 16, scaling="blockwise")
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("unknown scaling accepted")
