@@ -26,7 +26,7 @@ EXPORTS = ("fp8sg_status_string", "fp8sg_version", "amp_norm_workspace_len", "fp
            "fp8_scaled_linear_fwd_delayed", "fp8_scaled_linear_bwd", "fp8_scaled_linear_bwd_delayed",
            "amp_unscale_check", "amp_unscale_check_norm", "amp_update_scale",
            "fp8_quantize_rowwise", "fp8_gemm_rowwise", "fp8_scaled_linear_fwd_rowwise",
-           "fp8_scaled_linear_bwd_rowwise")
+           "fp8_scaled_linear_bwd_rowwise", "fp8_scaled_linear_bwd_unscale")
 MAX_HISTORY = 1024
 
 
@@ -94,6 +94,8 @@ def lib():
                                                 i, P]
     L.fp8_scaled_linear_bwd_rowwise.argtypes = [P, ctypes.POINTER(_SavedRW), i64, i64, i64,
                                                 ctypes.POINTER(_BwdWsRW), P, P, i, P]
+    L.fp8_scaled_linear_bwd_unscale.argtypes = [P, ctypes.POINTER(_Saved), i64, i64, i64,
+                                                ctypes.POINTER(_BwdWs), P, P, P, P, P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = i
     _lib = L
@@ -250,6 +252,19 @@ def fp8_scaled_linear_bwd(gy, saved: LinearSaved, ws: LinearBwdWs, gx, gw, out: 
     _check(lib().fp8_scaled_linear_bwd(_ptr(gy), ctypes.byref(s), M, N, K, ctypes.byref(b),
                                        _ptr(gx), _ptr(gw), out, _stream(stream)),
            "fp8_scaled_linear_bwd")
+
+
+def fp8_scaled_linear_bwd_unscale(gy, saved: LinearSaved, ws: LinearBwdWs, scale, found_inf,
+                                  gx, gw, stream=None):
+    """fp8_scaled_linear_bwd into fp16 gx, gw with the GradScaler unscale and
+    non-finite check fused into the GEMM epilogues."""
+    M, N = gy.shape
+    K = saved.x_q.shape[1]
+    s = saved.struct()
+    b = ws.struct()
+    _check(lib().fp8_scaled_linear_bwd_unscale(_ptr(gy), ctypes.byref(s), M, N, K, ctypes.byref(b),
+                                               _ptr(scale), _ptr(found_inf), _ptr(gx), _ptr(gw),
+                                               _stream(stream)), "fp8_scaled_linear_bwd_unscale")
 
 
 def fp8_scaled_linear_fwd_delayed(x, w, saved: LinearSaved, hist_x, hist_w, y,

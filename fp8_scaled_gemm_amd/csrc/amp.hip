@@ -53,8 +53,8 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 template <bool NORM>
 __device__ __forceinline__ uint32_t unscale2(uint32_t w, float inv, bool& bad, float& ss) {
   const h2 h = __builtin_bit_cast(h2, w);
-  const float a = (float)h[0] * inv;
-  const float b = (float)h[1] * inv;
+  const float a = fp32_value((float)h[0] * inv);
+  const float b = fp32_value((float)h[1] * inv);
   const h2 o = h2{(_Float16)a, (_Float16)b};
   const uint32_t r = __builtin_bit_cast(uint32_t, o);
   bad |= ((r & 0x7FFFu) >= 0x7C00u) | (((r >> 16) & 0x7FFFu) >= 0x7C00u);
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kAmpThreads) void k_unscale_check(AmpTable t) {
       // a partial vector at the tensor's start or end: only its own elements
       const int64_t i0 = e > first ? e : first, i1 = e + 8 < n ? e + 8 : n;
       for (int64_t i = i0; i < i1; ++i) {
-        const float f = (float)__builtin_bit_cast(_Float16, g[i]) * inv;
+        const float f = fp32_value((float)__builtin_bit_cast(_Float16, g[i]) * inv);
         const _Float16 o = (_Float16)f;
         const uint16_t r = __builtin_bit_cast(uint16_t, o);
         bad |= (r & 0x7FFFu) >= 0x7C00u;

@@ -207,7 +207,8 @@ fp8sg_status linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t
 // dgrad (gy_q [M,N] x w_qT [K,N]^T) and wgrad (gy_qT [N,M] x x_qT [K,M]^T).
 fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64_t M, int64_t N,
                         int64_t K, const fp8_linear_bwd_ws* ws, float* hist_gy, int32_t hist_len,
-                        void* gx, void* gw, fp8sg_out out, fp8sg_stream stream) {
+                        void* gx, void* gw, fp8sg_out out, fp8sg_stream stream,
+                        const float* amp_scale = nullptr, int32_t* found_inf = nullptr) {
   if (!gy || !ws || !gx || !gw) return FP8SG_ERR_NULL;
   fp8sg_status st = check_saved(saved);
   if (st != FP8SG_OK) return st;
@@ -236,10 +237,17 @@ fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64
   e = launch_quantize(qa, FP8SG_E5M2, s);
   if (e != hipSuccess) return FP8SG_ERR_HIP;
 
-  GemmProblem dg{ws->gy_q, saved->w_qT, gx, &ws->gy_sc->inv, &saved->w_sc->inv, M, K, N};
+  GemmProblem dg{ws->gy_q, saved->w_qT, gx, &ws->gy_sc->inv, &saved->w_sc->inv, M, K, N,
+                 amp_scale, found_inf};
+  GemmProblem wg{ws->gy_qT, saved->x_qT, gw, &ws->gy_sc->inv, &saved->x_sc->inv, N, K, M,
+                 amp_scale, found_inf};
+  if (amp_scale) {  // fp16 gradients unscaled and checked in the GEMM epilogues
+    e = launch_gemm_unscale(dg, s);
+    if (e != hipSuccess) return FP8SG_ERR_HIP;
+    return hip_status(launch_gemm_unscale(wg, s));
+  }
   e = launch_gemm(dg, FP8SG_E5M2, FP8SG_E4M3FN, out, s);
   if (e != hipSuccess) return FP8SG_ERR_HIP;
-  GemmProblem wg{ws->gy_qT, saved->x_qT, gw, &ws->gy_sc->inv, &saved->x_sc->inv, N, K, M};
   return hip_status(launch_gemm(wg, FP8SG_E5M2, FP8SG_E4M3FN, out, s));
 }
 
@@ -265,6 +273,17 @@ fp8sg_status fp8_scaled_linear_bwd(const uint16_t* gy, const fp8_linear_saved* s
                                    int64_t M, int64_t N, int64_t K, const fp8_linear_bwd_ws* ws,
                                    void* gx, void* gw, fp8sg_out out, fp8sg_stream stream) {
   return linear_bwd(gy, saved, M, N, K, ws, nullptr, 0, gx, gw, out, stream);
+}
+
+fp8sg_status fp8_scaled_linear_bwd_unscale(const uint16_t* gy, const fp8_linear_saved* saved,
+                                           int64_t M, int64_t N, int64_t K,
+                                           const fp8_linear_bwd_ws* ws, const float* scale,
+                                           int32_t* found_inf, uint16_t* gx, uint16_t* gw,
+                                           fp8sg_stream stream) {
+  if (!scale || !found_inf) return FP8SG_ERR_NULL;
+  if (!aligned(scale, 4) || !aligned(found_inf, 4)) return FP8SG_ERR_ALIGN;
+  return linear_bwd(gy, saved, M, N, K, ws, nullptr, 0, gx, gw, FP8SG_OUT_F16, stream, scale,
+                    found_inf);
 }
 
 fp8sg_status fp8_scaled_linear_bwd_delayed(const uint16_t* gy, const fp8_linear_saved* saved,

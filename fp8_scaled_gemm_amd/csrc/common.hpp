@@ -86,6 +86,15 @@ __device__ __forceinline__ ScaleVals scale_from_amax(float amax, int fmt) {
   return v;
 }
 
+// Keeps x as an fp32 value: an fp16 conversion that follows rounds this fp32
+// value (two roundings, as the definition fl32 then fp16 has it), instead of
+// being folded with the multiply that produced x into one mixed-precision
+// instruction (v_fma_mixlo_f16) that rounds the exact product once.
+__device__ __forceinline__ float fp32_value(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // clamp(y, -max, max) that keeps NaN (v_min/v_max return the non-NaN operand).
 __device__ __forceinline__ float clamp_keep_nan(float y, float m) {
   float c = fminf(fmaxf(y, -m), m);

@@ -50,6 +50,31 @@ struct GemmCfg {
 // byte offset of 16-byte chunk c of row r inside a [rows][128 B] LDS tile
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4); }
 
+// The unscale step fused into an fp16 epilogue: the GradScaler's rounding
+// sequence on the stored value, h = fp16(c), g = fp16(fl32(h) * inv_s); bad
+// records an inf/NaN g (as the standalone unscale pass checks stored values).
+struct Unscale {
+  float inv_s;
+  bool bad;
+  __device__ explicit Unscale(const GemmProblem& p) : inv_s(0.f), bad(false) {}
+  __device__ void load(const GemmProblem& p) { inv_s = 1.0f / *p.amp_scale; }
+  __device__ uint2 apply(v4f c, bool live) {
+    uint16_t r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const _Float16 h = (_Float16)fp32_value(c[e]);
+      const _Float16 g = (_Float16)fp32_value((float)h * inv_s);
+      r[e] = __builtin_bit_cast(uint16_t, g);
+      bad |= live && (r[e] & 0x7FFFu) >= 0x7C00u;
+    }
+    return make_uint2((uint32_t)r[0] | ((uint32_t)r[1] << 16), (uint32_t)r[2] | ((uint32_t)r[3] << 16));
+  }
+  // one plain store of 1 per wave that saw a non-finite value
+  __device__ void flag(const GemmProblem& p, int lane) const {
+    if (__ballot(bad) != 0 && lane == 0) *p.found_inf = 1;
+  }
+};
+
 template <int OUT>
 __device__ __forceinline__ void store4(void* C, int64_t idx, v4f v) {
   if constexpr (OUT == FP8SG_OUT_F32) {
@@ -60,17 +85,12 @@ __device__ __forceinline__ void store4(void* C, int64_t idx, v4f v) {
     *reinterpret_cast<b4*>(reinterpret_cast<uint16_t*>(C) + idx) = h;
   } else {
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    h4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    h4 h = {(_Float16)fp32_value(v[0]), (_Float16)fp32_value(v[1]), (_Float16)fp32_value(v[2]),
+            (_Float16)fp32_value(v[3])};
     *reinterpret_cast<h4*>(reinterpret_cast<uint16_t*>(C) + idx) = h;
   }
 }
 
-// Small-problem kernel: a BM x BN block tile per workgroup, K consumed 128
-// bytes at a time.  Each k-tile of A and B is fetched with 16-byte global loads
-// into registers while the previous tile is being multiplied, then written to
-// the other half of a double-buffered LDS tile.  Each wave owns a (BM/WM) x
-// (BN/WN) sub-tile of 16 x 16 blocks; results are stored as one 8-byte
-// (bf16/fp16) or 16-byte (fp32) write per lane and block.
 // The epilogue factor.  Per-tensor scaling: alpha = fl32(inv_a * inv_b), one
 // value [FP8-TRAIN §2].  Row-wise scaling (RW): inv_a and inv_b point to one
 // inverse scale per row of A and of B, and element (m, n) is multiplied by
@@ -115,6 +135,12 @@ struct Alpha {
   }
 };
 
+// Small-problem kernel: a BM x BN block tile per workgroup, K consumed 128
+// bytes at a time.  Each k-tile of A and B is fetched with 16-byte global loads
+// into registers while the previous tile is being multiplied, then written to
+// the other half of a double-buffered LDS tile.  Each wave owns a (BM/WM) x
+// (BN/WN) sub-tile of 16 x 16 blocks; results are stored as one 8-byte
+// (bf16/fp16) or 16-byte (fp32) write per lane and block.
 template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW>
 __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
   using Cfg = GemmCfg<BM, BN, WM, WN>;
@@ -215,6 +241,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
 
   // epilogue: lane holds C[m][n..n+3] of each 16x16 block
   const Alpha<RW, Cfg::kTM, Cfg::kTN> alpha(p, bm + wm * (BM / WM), bn + wn * (BN / WN), lane);
+  Unscale us(p);
+  if constexpr (OUT == kOutF16Unscale) us.load(p);
 #pragma unroll
   for (int i = 0; i < Cfg::kTM; ++i) {
     const int64_t m = bm + wm * (BM / WM) + 16 * i + (lane & 15);
@@ -225,9 +253,13 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
       if (n >= N) continue;  // N % 16 == 0: the four columns are all in or all out
       v4f c = acc[i][j];
       alpha.apply(c, i, j);
-      store4<OUT>(p.C, m * N + n, c);
+      if constexpr (OUT == kOutF16Unscale)
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + m * N + n) = us.apply(c, true);
+      else
+        store4<OUT>(p.C, m * N + n, c);
     }
   }
+  if constexpr (OUT == kOutF16Unscale) us.flag(p, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -493,6 +525,8 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
       uint8_t* base = r < 64 ? sA0 : r < 128 ? sA1 : r < 192 ? sB0 : sB1;
       return base + (r & 63) * kRowBytes;
     };
+    Unscale us(p);
+    if constexpr (OUT == kOutF16Unscale) us.load(p);
     __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing a slot
     barrier();
 #pragma unroll
@@ -504,9 +538,13 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
         v4f c = acc[i][j];
         alpha.apply(c, i, j);
         const int off = (((col >> 3) ^ (r & 31)) << 4) + (col & 7) * 2;
-        store4<OUT>(crow(r) + off, 0, c);
+        if constexpr (OUT == kOutF16Unscale)
+          *reinterpret_cast<uint2*>(crow(r) + off) = us.apply(c, bm + r < M && bn + col < N);
+        else
+          store4<OUT>(crow(r) + off, 0, c);
       }
     }
+    if constexpr (OUT == kOutF16Unscale) us.flag(p, lane);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     barrier();
     constexpr int kChunks = BN / 8;

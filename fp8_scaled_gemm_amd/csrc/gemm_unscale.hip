@@ -1,0 +1,16 @@
+// The backward GEMMs (e5m2 gradient codes x e4m3 codes) with the GradScaler's
+// unscale and non-finite check fused into the fp16 epilogue [PT-CH20 §20.2.2:
+// unscale the gradients, then check them for inf/NaN]: the kernels of
+// gemm_kernels.hpp instantiated for the kOutF16Unscale output mode.  The
+// stored values and the flag are those of an fp16 GEMM followed by the
+// standalone unscale pass over its output.
+#include "gemm_kernels.hpp"
+
+namespace fp8sg {
+
+hipError_t launch_gemm_unscale(const GemmProblem& p, hipStream_t stream) {
+  if (p.M == 0 || p.N == 0) return hipSuccess;
+  return launch_tiles<FP8SG_E5M2, FP8SG_E4M3FN, kOutF16Unscale, false>(p, stream);
+}
+
+}  // namespace fp8sg

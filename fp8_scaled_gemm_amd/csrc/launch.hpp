@@ -60,11 +60,20 @@ struct GemmProblem {
   const double* inv_a;
   const double* inv_b;
   int64_t M, N, K;
+  const float* amp_scale;  // kOutF16Unscale only: the GradScaler's loss scale
+  int32_t* found_inf;      // kOutF16Unscale only: set to 1 on a non-finite output
 };
+// Internal output mode next to fp8sg_out: fp16 output h = fp16(acc * alpha),
+// then unscaled in the epilogue as the GradScaler does it, g = fp16(fl32(h) *
+// fl32(1 / *amp_scale)), with found_inf set when a stored g is inf or NaN.
+constexpr int kOutF16Unscale = 3;
 hipError_t launch_gemm(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);
 // Row-wise scaling (gemm_rowwise.hip): inv_a points to M doubles, inv_b to N;
 // element (m, n) is scaled by fl32(inv_a[m] * inv_b[n]).
 hipError_t launch_gemm_rowwise(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);
+// The backward GEMMs (e5m2 x e4m3) with the kOutF16Unscale epilogue
+// (gemm_unscale.hip).
+hipError_t launch_gemm_unscale(const GemmProblem& p, hipStream_t stream);
 
 // ---- row-wise quantize (rowwise.hip)
 struct RowwiseArgs {

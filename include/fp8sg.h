@@ -185,6 +185,27 @@ FP8SG_API fp8sg_status fp8_scaled_linear_bwd(const uint16_t* gy, const fp8_linea
                                    void* gx, void* gw, fp8sg_out out, fp8sg_stream stream);
 
 /*
+ * fp8_scaled_linear_bwd with fp16 gradients and the GradScaler's unscale and
+ * non-finite check fused into the two GEMM epilogues [PT-CH20 §20.2.2: unscale
+ * the gradients, then check them for inf/NaN; FP8-TRAIN §4 backward].  The
+ * results are those of
+ *   fp8_scaled_linear_bwd(gy, saved, M, N, K, ws, gx, gw, FP8SG_OUT_F16)
+ *   amp_unscale_check({gx, gw}, {M*K, N*K}, 2, scale, found_inf)
+ * bit for bit: each element is stored as fp16(fl32(h) * fl32(1.0f / *scale))
+ * with h = fp16(acc * alpha), and *found_inf is set to 1 (never cleared) if a
+ * stored value is inf or NaN.  The separate pass over gx and gW (4 B per
+ * element) is saved.
+ *   scale: device float, the current loss scale; found_inf: device int32.
+ *   gx: [M,K] fp16, gw: [N,K] fp16 (bit patterns).
+ * The other arguments as fp8_scaled_linear_bwd.
+ */
+FP8SG_API fp8sg_status fp8_scaled_linear_bwd_unscale(const uint16_t* gy,
+                                   const fp8_linear_saved* saved, int64_t M, int64_t N, int64_t K,
+                                   const fp8_linear_bwd_ws* ws, const float* scale,
+                                   int32_t* found_inf, uint16_t* gx, uint16_t* gw,
+                                   fp8sg_stream stream);
+
+/*
  * Delayed scaling [PT-CH20 §20.5.9: each FP8 op keeps an amax history of its
  * input and takes every step's scale from the amax of earlier steps].
  * One pass over x instead of fp8_amax + fp8_quantize:

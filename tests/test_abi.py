@@ -190,6 +190,18 @@ def test_rowwise_validation():
         assert bwd(s, bad) == ENULL, name
 
 
+def test_fused_unscale_validation():
+    L = F.lib()
+    s = F._Saved(A16, A16, A16, A16, A16, A16)
+    ws = F._BwdWs(A16, A16, A16)
+    call = lambda scale=A16, found=A16, gx=A16, M=16: L.fp8_scaled_linear_bwd_unscale(
+        P(A16), ctypes.byref(s), M, 16, 16, ctypes.byref(ws), P(scale), P(found), P(gx), P(A16),
+        P(0))
+    assert call(scale=0) == ENULL and call(found=0) == ENULL and call(gx=0) == ENULL
+    assert call(scale=A16 + 2) == EALIGN and call(found=A16 + 1) == EALIGN
+    assert call(gx=MIS) == EALIGN and call(M=8) == ESHAPE
+
+
 def test_binding_refuses_a_missing_library(monkeypatch, tmp_path):
     # no fallback path: without the built library the binding raises
     monkeypatch.setattr(F, "_lib", None)
