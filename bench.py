@@ -32,15 +32,14 @@ PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 LOSS_SCALE = 65536.0
 
-# HBM bytes of one 4096^3 GEMM launch from two rocprofv3 --pmc passes of this
-# benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
+# HBM bytes of one 4096^3 GEMM launch (mean over the step's three: forward,
+# and dgrad/wgrad with the unscale epilogue) from two rocprofv3 --pmc passes of
+# this benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
 # what the same counter reads for a 1 GiB device-to-device copy
 # (bench.py --copy-reference: FETCH_SIZE 524,302 KiB -> x2.0, WRITE_SIZE
 # 1,048,576 KiB -> x1.0).  Valid only for the GEMM kernel source they were
-# taken on (the kernel templates, since moved to gemm_kernels.hpp unchanged:
-# the per-tensor instantiations assemble to the same instructions); bench.py
-# reports null for any other.
-GEMM_TRAFFIC = {"gemm_src_sha256_16": "109131220fee30f2", "fetch_kib": 49248.0, "write_kib": 32768.0,
+# taken on; bench.py reports null for any other.
+GEMM_TRAFFIC = {"gemm_src_sha256_16": "86b636081dc4422e", "fetch_kib": 49275.5, "write_kib": 32768.0,
                 "fetch_factor": 2.0, "write_factor": 1.0}
 
 
@@ -72,20 +71,22 @@ class Timer:
     def __init__(self, torch, stream):
         self.torch, self.stream = torch, stream
 
-    def run(self, fn, reps, flush=None):
+    def run(self, fn, reps):
+        """Average time of fn over reps back-to-back calls: one event pair around
+        the whole loop on the launch stream, after 3 untimed calls, so per-launch
+        dispatch latency is not counted (it is hidden between back-to-back
+        kernels, as in the step).  Matches the kernel-trace durations."""
         torch = self.torch
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-        for i in range(reps):
-            if flush is not None:
-                flush()
-            starts[i].record(self.stream)
+        for _ in range(3):
             fn()
-            ends[i].record(self.stream)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(self.stream)
+        for _ in range(reps):
+            fn()
+        t1.record(self.stream)
         torch.cuda.synchronize()
-        ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-        return {"avg_us": 1e3 * sum(ms) / reps, "median_us": 1e3 * ms[reps // 2],
-                "min_us": 1e3 * ms[0]}
+        return {"avg_us": 1e3 * t0.elapsed_time(t1) / reps}
 
 
 def main():
@@ -247,11 +248,16 @@ def main():
     kern["gemm_fwd_e4m3xe4m3"] = T.run(lambda: F.fp8_gemm(
         saved.x_q, F.E4M3FN, saved.w_q, F.E4M3FN, inv(saved.x_sc), inv(saved.w_sc), y,
         F.OUT_BF16), args.reps)
-    kern["gemm_dgrad_e5m2xe4m3"] = T.run(lambda: F.fp8_gemm(
+    # dgrad and wgrad as the step runs them: fp16 out, unscaled and checked in the epilogue
+    fz0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    kern["gemm_dgrad_e5m2xe4m3"] = T.run(lambda: F.fp8_gemm_unscale(
+        ws.gy_q, F.E5M2, saved.w_qT, F.E4M3FN, inv(ws.gy_sc), inv(saved.w_sc), scale, fz0,
+        gx), args.reps)
+    kern["gemm_wgrad_e5m2xe4m3"] = T.run(lambda: F.fp8_gemm_unscale(
+        ws.gy_qT, F.E5M2, saved.x_qT, F.E4M3FN, inv(ws.gy_sc), inv(saved.x_sc), scale, fz0,
+        gw), args.reps)
+    kern["gemm_dgrad_plain_f16"] = T.run(lambda: F.fp8_gemm(
         ws.gy_q, F.E5M2, saved.w_qT, F.E4M3FN, inv(ws.gy_sc), inv(saved.w_sc), gx,
-        F.OUT_F16), args.reps)
-    kern["gemm_wgrad_e5m2xe4m3"] = T.run(lambda: F.fp8_gemm(
-        ws.gy_qT, F.E5M2, saved.x_qT, F.E4M3FN, inv(ws.gy_sc), inv(saved.x_sc), gw,
         F.OUT_F16), args.reps)
     rec = F.ScaleRec(device=dev)
     q = torch.empty((M, K), dtype=torch.uint8, device=dev)
@@ -278,8 +284,8 @@ def main():
         y_rw, F.OUT_BF16), args.reps)
     del g16, q, qT, rs, cs
 
-    gemm_avg_us = sum(kern[k]["avg_us"] for k in kern if k.startswith("gemm_")
-                      and "rowwise" not in k) / 3
+    gemm_avg_us = sum(kern[k]["avg_us"] for k in ("gemm_fwd_e4m3xe4m3", "gemm_dgrad_e5m2xe4m3",
+                                                  "gemm_wgrad_e5m2xe4m3")) / 3
     gemm_tflops = 2.0 * M * N * K / (gemm_avg_us * 1e-6) / 1e12
     traffic = None
     import hashlib

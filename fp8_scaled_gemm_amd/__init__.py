@@ -26,7 +26,7 @@ EXPORTS = ("fp8sg_status_string", "fp8sg_version", "amp_norm_workspace_len", "fp
            "fp8_scaled_linear_fwd_delayed", "fp8_scaled_linear_bwd", "fp8_scaled_linear_bwd_delayed",
            "amp_unscale_check", "amp_unscale_check_norm", "amp_update_scale",
            "fp8_quantize_rowwise", "fp8_gemm_rowwise", "fp8_scaled_linear_fwd_rowwise",
-           "fp8_scaled_linear_bwd_rowwise", "fp8_scaled_linear_bwd_unscale")
+           "fp8_scaled_linear_bwd_rowwise", "fp8_scaled_linear_bwd_unscale", "fp8_gemm_unscale")
 MAX_HISTORY = 1024
 
 
@@ -94,6 +94,7 @@ def lib():
                                                 i, P]
     L.fp8_scaled_linear_bwd_rowwise.argtypes = [P, ctypes.POINTER(_SavedRW), i64, i64, i64,
                                                 ctypes.POINTER(_BwdWsRW), P, P, i, P]
+    L.fp8_gemm_unscale.argtypes = [P, i, P, i, P, P, P, P, P, i64, i64, i64, P]
     L.fp8_scaled_linear_bwd_unscale.argtypes = [P, ctypes.POINTER(_Saved), i64, i64, i64,
                                                 ctypes.POINTER(_BwdWs), P, P, P, P, P]
     for name in EXPORTS[3:]:
@@ -198,6 +199,18 @@ def fp8_gemm(A: torch.Tensor, fa: int, B: torch.Tensor, fb: int, inv_a_ptr: int,
     _check(lib().fp8_gemm(_ptr(A), fa, _ptr(B), fb, ctypes.c_void_p(inv_a_ptr),
                           ctypes.c_void_p(inv_b_ptr), _ptr(C), out, M, N, K, _stream(stream)),
            "fp8_gemm")
+
+
+def fp8_gemm_unscale(A: torch.Tensor, fa: int, B: torch.Tensor, fb: int, inv_a_ptr: int,
+                     inv_b_ptr: int, scale: torch.Tensor, found_inf: torch.Tensor, C: torch.Tensor,
+                     stream=None):
+    """fp8_gemm into fp16 C with the GradScaler unscale and check in the epilogue."""
+    M, K = A.shape
+    N, K2 = B.shape
+    assert K == K2 and tuple(C.shape) == (M, N) and C.dtype == torch.float16
+    _check(lib().fp8_gemm_unscale(_ptr(A), fa, _ptr(B), fb, ctypes.c_void_p(inv_a_ptr),
+                                  ctypes.c_void_p(inv_b_ptr), _ptr(scale), _ptr(found_inf), _ptr(C),
+                                  M, N, K, _stream(stream)), "fp8_gemm_unscale")
 
 
 class LinearSaved:

@@ -146,6 +146,18 @@ fp8sg_status fp8_gemm_rowwise(const uint8_t* A, fp8sg_format fa, const uint8_t* 
   return hip_status(launch_gemm_rowwise(p, fa, fb, out, S(stream)));
 }
 
+fp8sg_status fp8_gemm_unscale(const uint8_t* A, fp8sg_format fa, const uint8_t* B, fp8sg_format fb,
+                              const double* inv_a, const double* inv_b, const float* scale,
+                              int32_t* found_inf, uint16_t* C, int64_t M, int64_t N, int64_t Kc,
+                              fp8sg_stream stream) {
+  fp8sg_status st = check_gemm(A, fa, B, fb, inv_a, inv_b, C, FP8SG_OUT_F16, M, N, Kc);
+  if (st != FP8SG_OK) return st;
+  if (!scale || !found_inf) return FP8SG_ERR_NULL;
+  if (!aligned(scale, 4) || !aligned(found_inf, 4)) return FP8SG_ERR_ALIGN;
+  GemmProblem p{A, B, C, inv_a, inv_b, M, N, Kc, scale, found_inf};
+  return hip_status(launch_gemm_unscale(p, fa, fb, S(stream)));
+}
+
 }  // extern "C"
 
 namespace {
@@ -242,9 +254,9 @@ fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64
   GemmProblem wg{ws->gy_qT, saved->x_qT, gw, &ws->gy_sc->inv, &saved->x_sc->inv, N, K, M,
                  amp_scale, found_inf};
   if (amp_scale) {  // fp16 gradients unscaled and checked in the GEMM epilogues
-    e = launch_gemm_unscale(dg, s);
+    e = launch_gemm_unscale(dg, FP8SG_E5M2, FP8SG_E4M3FN, s);
     if (e != hipSuccess) return FP8SG_ERR_HIP;
-    return hip_status(launch_gemm_unscale(wg, s));
+    return hip_status(launch_gemm_unscale(wg, FP8SG_E5M2, FP8SG_E4M3FN, s));
   }
   e = launch_gemm(dg, FP8SG_E5M2, FP8SG_E4M3FN, out, s);
   if (e != hipSuccess) return FP8SG_ERR_HIP;

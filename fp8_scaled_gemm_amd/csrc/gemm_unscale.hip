@@ -1,5 +1,6 @@
-// The backward GEMMs (e5m2 gradient codes x e4m3 codes) with the GradScaler's
-// unscale and non-finite check fused into the fp16 epilogue [PT-CH20 §20.2.2:
+// The scaled GEMM with the GradScaler's unscale and non-finite check fused
+// into the fp16 epilogue (used by the backward GEMMs, e5m2 gradient codes x
+// e4m3 codes) [PT-CH20 §20.2.2:
 // unscale the gradients, then check them for inf/NaN]: the kernels of
 // gemm_kernels.hpp instantiated for the kOutF16Unscale output mode.  The
 // stored values and the flag are those of an fp16 GEMM followed by the
@@ -8,9 +9,12 @@
 
 namespace fp8sg {
 
-hipError_t launch_gemm_unscale(const GemmProblem& p, hipStream_t stream) {
+hipError_t launch_gemm_unscale(const GemmProblem& p, int fa, int fb, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  return launch_tiles<FP8SG_E5M2, FP8SG_E4M3FN, kOutF16Unscale, false>(p, stream);
+  if (fa == FP8SG_E4M3FN && fb == FP8SG_E4M3FN) return launch_tiles<0, 0, kOutF16Unscale, false>(p, stream);
+  if (fa == FP8SG_E5M2 && fb == FP8SG_E4M3FN) return launch_tiles<1, 0, kOutF16Unscale, false>(p, stream);
+  if (fa == FP8SG_E4M3FN && fb == FP8SG_E5M2) return launch_tiles<0, 1, kOutF16Unscale, false>(p, stream);
+  return launch_tiles<1, 1, kOutF16Unscale, false>(p, stream);
 }
 
 }  // namespace fp8sg

@@ -71,9 +71,8 @@ hipError_t launch_gemm(const GemmProblem& p, int fa, int fb, int out, hipStream_
 // Row-wise scaling (gemm_rowwise.hip): inv_a points to M doubles, inv_b to N;
 // element (m, n) is scaled by fl32(inv_a[m] * inv_b[n]).
 hipError_t launch_gemm_rowwise(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);
-// The backward GEMMs (e5m2 x e4m3) with the kOutF16Unscale epilogue
-// (gemm_unscale.hip).
-hipError_t launch_gemm_unscale(const GemmProblem& p, hipStream_t stream);
+// The kOutF16Unscale epilogue (gemm_unscale.hip); p.amp_scale and p.found_inf set.
+hipError_t launch_gemm_unscale(const GemmProblem& p, int fa, int fb, hipStream_t stream);
 
 // ---- row-wise quantize (rowwise.hip)
 struct RowwiseArgs {

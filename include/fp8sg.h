@@ -140,6 +140,21 @@ FP8SG_API fp8sg_status fp8_gemm(const uint8_t* A, fp8sg_format fa, const uint8_t
                       int64_t M, int64_t N, int64_t Kc, fp8sg_stream stream);
 
 /*
+ * fp8_gemm into fp16 with the GradScaler's unscale and non-finite check
+ * fused into the epilogue [PT-CH20 §20.2.2; FP8-TRAIN §4]: each element is
+ *   h = fp16(acc * fl32(inv_a * inv_b)),  C = fp16(fl32(h) * fl32(1.0f / *scale))
+ * (both fp16 roundings to nearest even, as fp8_gemm with FP8SG_OUT_F16 followed
+ * by amp_unscale_check on C), and *found_inf is set to 1 (never cleared) if a
+ * stored C element is inf or NaN.
+ *   scale: device float (4-byte aligned); found_inf: device int32.
+ *   C: M x N fp16 bit patterns.  The other arguments as fp8_gemm.
+ */
+FP8SG_API fp8sg_status fp8_gemm_unscale(const uint8_t* A, fp8sg_format fa, const uint8_t* B,
+                              fp8sg_format fb, const double* inv_a, const double* inv_b,
+                              const float* scale, int32_t* found_inf, uint16_t* C, int64_t M,
+                              int64_t N, int64_t Kc, fp8sg_stream stream);
+
+/*
  * What the forward pass saves for the backward pass [FP8-TRAIN §6: the
  * quantized FP8 tensors and their inverse scales, not the bf16 inputs].
  * All pointers are caller-owned device buffers.

@@ -202,6 +202,14 @@ def test_fused_unscale_validation():
     assert call(gx=MIS) == EALIGN and call(M=8) == ESHAPE
 
 
+def test_gemm_unscale_validation():
+    g = lambda scale=A16, found=A16, C=A16B, M=16, fa=0: F.lib().fp8_gemm_unscale(
+        P(A16), fa, P(A16B), 1, P(A16), P(A16), P(scale), P(found), P(C), M, 16, 32, P(0))
+    assert g(scale=0) == ENULL and g(found=0) == ENULL and g(C=0) == ENULL
+    assert g(M=24) == ESHAPE and g(fa=5) == EFORMAT
+    assert g(C=MIS) == EALIGN and g(scale=A16 + 1) == EALIGN
+
+
 def test_binding_refuses_a_missing_library(monkeypatch, tmp_path):
     # no fallback path: without the built library the binding raises
     monkeypatch.setattr(F, "_lib", None)

@@ -137,3 +137,31 @@ def test_fused_unscale_never_clears_the_flag():
     gy_h = W.normal_bf16(84, 2, (M, N), 1e-4 * 65536.0)
     _, outs = run_both(x_h, w_h, gy_h, 65536.0, found0=1)
     assert outs[True][2] == outs[False][2] == 1
+
+
+@pytest.mark.parametrize("fa,fb", [(F.E4M3FN, F.E4M3FN), (F.E5M2, F.E4M3FN), (F.E4M3FN, F.E5M2),
+                                   (F.E5M2, F.E5M2)])
+@pytest.mark.parametrize("shape", [(144, 272, 400), (2064, 4000, 1040)])
+def test_gemm_unscale_is_gemm_then_unscale(fa, fb, shape):
+    """fp8_gemm_unscale = fp8_gemm (fp16 out) followed by amp_unscale_check on
+    its output, bit for bit, flag included."""
+    M, N, K = shape
+    rng = np.random.default_rng(M + 7 * N + K + 10 * fa + fb)
+    A = rng.integers(0, 256, (M, K), dtype=np.int64).astype(np.uint8)
+    B = rng.integers(0, 256, (N, K), dtype=np.int64).astype(np.uint8)
+    A[~np.isfinite(O.decode(fa, A))] = 0
+    B[~np.isfinite(O.decode(fb, B))] = 0
+    Ad, Bd = torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV)
+    inv = torch.tensor([2.0 ** -9 / 3.0, 0.37 / 448.0 * 2.0 ** -14], dtype=torch.float64,
+                       device=DEV)
+    scale = torch.tensor([49152.0], dtype=torch.float32, device=DEV)
+    C1 = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    C2 = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    f1 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    f2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    F.fp8_gemm_unscale(Ad, fa, Bd, fb, inv.data_ptr(), inv.data_ptr() + 8, scale, f1, C1)
+    F.fp8_gemm(Ad, fa, Bd, fb, inv.data_ptr(), inv.data_ptr() + 8, C2, F.OUT_F16)
+    F.amp_unscale_check([C2], scale, f2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(C1), host_u16(C2))
+    assert int(f1.item()) == int(f2.item())
