@@ -94,6 +94,11 @@ __device__ __forceinline__ float fp32_value(float x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2 fp32_value(f32x2 x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // clamp(y, -max, max) that keeps NaN (v_min/v_max return the non-NaN operand).
 __device__ __forceinline__ float clamp_keep_nan(float y, float m) {

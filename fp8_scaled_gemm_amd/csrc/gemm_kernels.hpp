@@ -51,26 +51,34 @@ struct GemmCfg {
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4); }
 
 // The unscale step fused into an fp16 epilogue: the GradScaler's rounding
-// sequence on the stored value, h = fp16(c), g = fp16(fl32(h) * inv_s); bad
-// records an inf/NaN g (as the standalone unscale pass checks stored values).
+// sequence on the stored value, h = fp16(c), g = fp16(fl32(h) * inv_s), in
+// packed conversions.  mx keeps the largest |g| bit pattern seen per 16-bit
+// half; a half at 0x7C00 or above is inf/NaN (the standalone unscale pass's
+// check on stored values).  Every element of the tile is checked, also rows
+// and columns past M and N: their accumulators are exact zeros (the operand
+// loads there are zero-filled), so they can only be non-finite when alpha
+// is, and then every element in range is non-finite too.
 struct Unscale {
   float inv_s;
-  bool bad;
-  __device__ explicit Unscale(const GemmProblem& p) : inv_s(0.f), bad(false) {}
+  uint32_t mx;
+  __device__ Unscale() : inv_s(0.f), mx(0u) {}
   __device__ void load(const GemmProblem& p) { inv_s = 1.0f / *p.amp_scale; }
-  __device__ uint2 apply(v4f c, bool live) {
-    uint16_t r[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const _Float16 h = (_Float16)fp32_value(c[e]);
-      const _Float16 g = (_Float16)fp32_value((float)h * inv_s);
-      r[e] = __builtin_bit_cast(uint16_t, g);
-      bad |= live && (r[e] & 0x7FFFu) >= 0x7C00u;
-    }
-    return make_uint2((uint32_t)r[0] | ((uint32_t)r[1] << 16), (uint32_t)r[2] | ((uint32_t)r[3] << 16));
+  // two elements: fp16 pair of fp16(fl32(fp16(c) * inv_s)), as packed bits
+  __device__ uint32_t pair(f32x2 c) const {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 h = __builtin_convertvector(fp32_value(c), f16x2);
+    const f32x2 u = __builtin_convertvector(h, f32x2);
+    const f32x2 v = {u[0] * inv_s, u[1] * inv_s};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(fp32_value(v), f16x2));
+  }
+  __device__ uint2 apply(v4f c) {
+    const uint2 r = make_uint2(pair(f32x2{c[0], c[1]}), pair(f32x2{c[2], c[3]}));
+    mx = pmax(mx, pmax(r.x & 0x7FFF7FFFu, r.y & 0x7FFF7FFFu));
+    return r;
   }
   // one plain store of 1 per wave that saw a non-finite value
   __device__ void flag(const GemmProblem& p, int lane) const {
+    const bool bad = (mx & 0xFFFFu) >= 0x7C00u || (mx >> 16) >= 0x7C00u;
     if (__ballot(bad) != 0 && lane == 0) *p.found_inf = 1;
   }
 };
@@ -241,7 +249,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
 
   // epilogue: lane holds C[m][n..n+3] of each 16x16 block
   const Alpha<RW, Cfg::kTM, Cfg::kTN> alpha(p, bm + wm * (BM / WM), bn + wn * (BN / WN), lane);
-  Unscale us(p);
+  Unscale us;
   if constexpr (OUT == kOutF16Unscale) us.load(p);
 #pragma unroll
   for (int i = 0; i < Cfg::kTM; ++i) {
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
       v4f c = acc[i][j];
       alpha.apply(c, i, j);
       if constexpr (OUT == kOutF16Unscale)
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + m * N + n) = us.apply(c, true);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + m * N + n) = us.apply(c);
       else
         store4<OUT>(p.C, m * N + n, c);
     }
@@ -525,7 +533,7 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
       uint8_t* base = r < 64 ? sA0 : r < 128 ? sA1 : r < 192 ? sB0 : sB1;
       return base + (r & 63) * kRowBytes;
     };
-    Unscale us(p);
+    Unscale us;
     if constexpr (OUT == kOutF16Unscale) us.load(p);
     __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing a slot
     barrier();
@@ -539,7 +547,7 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
         alpha.apply(c, i, j);
         const int off = (((col >> 3) ^ (r & 31)) << 4) + (col & 7) * 2;
         if constexpr (OUT == kOutF16Unscale)
-          *reinterpret_cast<uint2*>(crow(r) + off) = us.apply(c, bm + r < M && bn + col < N);
+          *reinterpret_cast<uint2*>(crow(r) + off) = us.apply(c);
         else
           store4<OUT>(crow(r) + off, 0, c);
       }
