@@ -274,3 +274,157 @@ def test_gradscaler_downsized_every_step_elementwise():
         assert float(scale.item()) == float(st.scale) and int(tracker.item()) == st.tracker
         if s % 200 == 0:
             log(f"downsized scaler: step {s}, scale {float(st.scale)}")
+
+
+# ---- the square layer in the other configurations bench.py times
+
+def square_inputs():
+    cfg = C.SQUARE
+    x_h, w_h, gy_h = cfg.x(), cfg.w(), cfg.gy()
+    gy_s = W.f32_to_bf16_bits(O.decode(O.BF16, gy_h).astype(np.float32) *
+                              np.float32(C.INIT_SCALE)).reshape(gy_h.shape)
+    return x_h, w_h, gy_s
+
+
+def sampled_vec_check(got_dev, out_fmt, A, fa, B, fb, ia, ib, n_pts, seed, what, post=1.0):
+    """Sampled outputs against the oracle's vector-scaled GEMM (post scales
+    the reference, e.g. by 1/loss scale for unscaled gradients)."""
+    M, N = got_dev.shape
+    rng = np.random.default_rng(seed)
+    ii = np.concatenate([rng.integers(0, M, n_pts), [0, M - 1, 0, M - 1]])
+    jj = np.concatenate([rng.integers(0, N, n_pts), [0, N - 1, N - 1, 0]])
+    ia = np.broadcast_to(np.asarray(ia, np.float64), (A.shape[0],))
+    ib = np.broadcast_to(np.asarray(ib, np.float64), (B.shape[0],))
+    c_ref = O.gemm_vec_at(A, fa, B, fb, ia, ib, ii, jj).astype(np.float64) * post
+    ad = O.gemm_absdot_vec_at(A, fa, B, fb, ia, ib, ii, jj) * post
+    got = host16(got_dev)[ii, jj]
+    return check_gemm_values(O.decode(out_fmt, got), c_ref, ad, A.shape[1], out_fmt, what)
+
+
+def test_square_layer_fused_unscale_step():
+    """The step bench.py times: bf16 forward, fp16 backward with the unscale
+    and check fused into the GEMM epilogues, update.  Against the oracle
+    (codes, scales, sampled unscaled gradients, flag, scaler state) and bit
+    for bit against the unfused backward + unscale pass."""
+    x_h, w_h, gy_s = square_inputs()
+    M, K = x_h.shape
+    N = w_h.shape[0]
+    x, w, gy = dev16(x_h), dev16(w_h), dev16(gy_s)
+    saved = F.LinearSaved(M, N, K)
+    ws = F.LinearBwdWs(M, N)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    gx = torch.empty((M, K), dtype=torch.float16, device=DEV)
+    gw = torch.empty((N, K), dtype=torch.float16, device=DEV)
+    scale = torch.tensor([C.INIT_SCALE], dtype=torch.float32, device=DEV)
+    tracker = torch.zeros(1, dtype=torch.int32, device=DEV)
+    found = torch.zeros(1, dtype=torch.int32, device=DEV)
+    log("fused step: GPU")
+    F.fp8_scaled_linear_fwd(x, w, saved, y, F.OUT_BF16)
+    F.fp8_scaled_linear_bwd_unscale(gy, saved, ws, scale, found, gx, gw)
+    f_gpu = int(found.item())
+    F.amp_update_scale(scale, tracker, found, C.GROWTH, C.BACKOFF, C.INTERVAL)
+    torch.cuda.synchronize()
+    # the unfused pair on the same saved state
+    gx2 = torch.empty_like(gx)
+    gw2 = torch.empty_like(gw)
+    ws2 = F.LinearBwdWs(M, N)
+    found2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    one_scale = torch.tensor([C.INIT_SCALE], dtype=torch.float32, device=DEV)
+    F.fp8_scaled_linear_bwd(gy, saved, ws2, gx2, gw2, F.OUT_F16)
+    F.amp_unscale_check([gx2, gw2], one_scale, found2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host16(gx), host16(gx2)) and np.array_equal(host16(gw), host16(gw2))
+    assert f_gpu == int(found2.item()) == 0
+    log("fused step: oracle")
+    xq, wq = O.to_fp8(x_h, O.E4M3FN), O.to_fp8(w_h, O.E4M3FN)
+    gq = O.to_fp8(gy_s, O.E5M2)
+    for rec, sc, nm in ((saved.x_sc, xq.sc, "x"), (saved.w_sc, wq.sc, "W"), (ws.gy_sc, gq.sc, "gy")):
+        check_rec(rec, sc, f"fused {nm}")
+    assert_codes_equal(O.E5M2, ws.gy_q.cpu().numpy(), gq.q, "gy_q")
+    assert_codes_equal(O.E5M2, ws.gy_qT.cpu().numpy(), gq.qT, "gy_qT")
+    inv_s = float(np.float32(1.0) / np.float32(C.INIT_SCALE))
+    sampled_vec_check(gx, O.F16, gq.q, O.E5M2, wq.qT, O.E4M3FN, gq.sc.inv, wq.sc.inv, 2048, 40,
+                      "fused dgrad", inv_s)
+    sampled_vec_check(gw, O.F16, gq.qT, O.E5M2, xq.qT, O.E4M3FN, gq.sc.inv, xq.sc.inv, 2048, 41,
+                      "fused wgrad", inv_s)
+    st = O.update_scale(O.ScalerState(np.float32(C.INIT_SCALE), 0), 0, C.GROWTH, C.BACKOFF,
+                        C.INTERVAL)
+    assert float(scale.item()) == float(st.scale) and int(tracker.item()) == st.tracker
+
+
+def test_square_layer_delayed_steps():
+    """bench.py's delayed-scaling step: histories of 16 starting at 1.0, three
+    steps on the same tensors; histories, codes and scales bit-exact every
+    step, sampled GEMM outputs of the last."""
+    x_h, w_h, gy_s = square_inputs()
+    M, K = x_h.shape
+    N = w_h.shape[0]
+    x, w, gy = dev16(x_h), dev16(w_h), dev16(gy_s)
+    saved = F.LinearSaved(M, N, K)
+    ws = F.LinearBwdWs(M, N)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    gx = torch.empty((M, K), dtype=torch.float16, device=DEV)
+    gw = torch.empty((N, K), dtype=torch.float16, device=DEV)
+    hx, hw, hg = (torch.ones(16, dtype=torch.float32, device=DEV) for _ in range(3))
+    rhx = rhw = rhg = np.ones(16, np.float32)
+    for step in range(3):
+        log(f"delayed step {step}")
+        F.fp8_scaled_linear_fwd_delayed(x, w, saved, hx, hw, y, F.OUT_BF16)
+        F.fp8_scaled_linear_bwd_delayed(gy, saved, ws, hg, gx, gw, F.OUT_F16)
+        torch.cuda.synchronize()
+        xq = O.to_fp8_delayed(x_h, O.E4M3FN, rhx)
+        wq = O.to_fp8_delayed(w_h, O.E4M3FN, rhw)
+        gq = O.to_fp8_delayed(gy_s, O.E5M2, rhg)
+        rhx, rhw, rhg = xq.hist, wq.hist, gq.hist
+        for got, ref, nm in ((hx, rhx, "hist_x"), (hw, rhw, "hist_w"), (hg, rhg, "hist_gy")):
+            assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32)), (nm, step)
+        for rec, sc, nm in ((saved.x_sc, xq.sc, "x"), (saved.w_sc, wq.sc, "W"), (ws.gy_sc, gq.sc, "gy")):
+            r = rec.read()
+            assert r["scale"] == sc.scale and r["inv"] == sc.inv, (nm, step)
+        for got, ref, fmt, nm in ((saved.x_q, xq.q, O.E4M3FN, "x_q"), (saved.w_qT, wq.qT, O.E4M3FN, "w_qT"),
+                                  (ws.gy_qT, gq.qT, O.E5M2, "gy_qT")):
+            assert_codes_equal(fmt, got.cpu().numpy(), ref, f"{nm} step {step}")
+    sampled_gemm_check(y, O.BF16, xq.q, O.E4M3FN, wq.q, O.E4M3FN, xq.sc.inv, wq.sc.inv, 1024, 50,
+                       "delayed fwd")
+    sampled_gemm_check(gx, O.F16, gq.q, O.E5M2, wq.qT, O.E4M3FN, gq.sc.inv, wq.sc.inv, 1024, 51,
+                       "delayed dgrad")
+    sampled_gemm_check(gw, O.F16, gq.qT, O.E5M2, xq.qT, O.E4M3FN, gq.sc.inv, xq.sc.inv, 1024, 52,
+                       "delayed wgrad")
+
+
+def test_square_layer_rowwise():
+    """bench.py's row-wise step: codes and scale vectors of x, W and gy (by
+    rows and by columns) bit-exact, sampled GEMM outputs of all three."""
+    x_h, w_h, gy_s = square_inputs()
+    M, K = x_h.shape
+    N = w_h.shape[0]
+    saved = F.LinearSavedRW(M, N, K)
+    ws = F.LinearBwdWsRW(M, N)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    gx = torch.empty((M, K), dtype=torch.float16, device=DEV)
+    gw = torch.empty((N, K), dtype=torch.float16, device=DEV)
+    log("row-wise: GPU")
+    F.fp8_scaled_linear_fwd_rowwise(dev16(x_h), dev16(w_h), saved, y, F.OUT_BF16)
+    F.fp8_scaled_linear_bwd_rowwise(dev16(gy_s), saved, ws, gx, gw, F.OUT_F16)
+    torch.cuda.synchronize()
+    log("row-wise: oracle")
+    xq, wq = O.to_fp8_rowwise(x_h, O.E4M3FN), O.to_fp8_rowwise(w_h, O.E4M3FN)
+    gq = O.to_fp8_rowwise(gy_s, O.E5M2)
+    for got, ref, fmt, nm in ((saved.x_q, xq.q, O.E4M3FN, "x_q"), (saved.x_qT, xq.qT, O.E4M3FN, "x_qT"),
+                              (saved.w_q, wq.q, O.E4M3FN, "w_q"), (saved.w_qT, wq.qT, O.E4M3FN, "w_qT"),
+                              (ws.gy_q, gq.q, O.E5M2, "gy_q"), (ws.gy_qT, gq.qT, O.E5M2, "gy_qT")):
+        assert_codes_equal(fmt, got.cpu().numpy(), ref, f"row-wise {nm}")
+    for amax, inv, ref, nm in ((saved.x_row_amax, saved.x_row_inv, xq.rows, "x rows"),
+                               (saved.x_col_amax, saved.x_col_inv, xq.cols, "x cols"),
+                               (saved.w_row_amax, saved.w_row_inv, wq.rows, "w rows"),
+                               (saved.w_col_amax, saved.w_col_inv, wq.cols, "w cols"),
+                               (ws.gy_row_amax, ws.gy_row_inv, gq.rows, "gy rows"),
+                               (ws.gy_col_amax, ws.gy_col_inv, gq.cols, "gy cols")):
+        assert np.array_equal(amax.cpu().numpy().view(np.uint32), ref.amax_bits), nm
+        assert np.array_equal(inv.cpu().numpy().view(np.uint64), ref.inv.view(np.uint64)), nm
+    sampled_vec_check(y, O.BF16, xq.q, O.E4M3FN, wq.q, O.E4M3FN, xq.rows.inv, wq.rows.inv, 1024,
+                      60, "row-wise fwd")
+    sampled_vec_check(gx, O.F16, gq.q, O.E5M2, wq.qT, O.E4M3FN, gq.rows.inv, wq.cols.inv, 1024,
+                      61, "row-wise dgrad")
+    sampled_vec_check(gw, O.F16, gq.qT, O.E5M2, xq.qT, O.E4M3FN, gq.cols.inv, xq.cols.inv, 1024,
+                      62, "row-wise wgrad")
