@@ -18,7 +18,8 @@ def _bits(t):
     return t.contiguous().view(torch.uint8) if t.dtype != torch.uint8 else t
 
 
-def test_step_graph_replay_matches_eager():
+@pytest.mark.parametrize("fused", [False, True])
+def test_step_graph_replay_matches_eager(fused):
     M, N, K = 512, 768, 384
     x = torch.from_numpy(W.normal_bf16(41, 0, (M, K), 1.0).view(np.int16)).view(
         torch.bfloat16).to(DEV)
@@ -37,8 +38,11 @@ def test_step_graph_replay_matches_eager():
 
     def step():
         F.fp8_scaled_linear_fwd(x, w, saved, y, F.OUT_BF16)
-        F.fp8_scaled_linear_bwd(gy, saved, ws, gx, gw, F.OUT_F16)
-        F.amp_unscale_check([gx, gw], scale, found)
+        if fused:  # unscale + check in the backward GEMMs' epilogues
+            F.fp8_scaled_linear_bwd_unscale(gy, saved, ws, scale, found, gx, gw)
+        else:
+            F.fp8_scaled_linear_bwd(gy, saved, ws, gx, gw, F.OUT_F16)
+            F.amp_unscale_check([gx, gw], scale, found)
         # growth factor 1: the tracker counts and resets, the scale (and so every
         # output) stays that of the eager reference step
         F.amp_update_scale(scale, tracker, found, 1.0, 0.5, 3)
