@@ -39,7 +39,7 @@ LOSS_SCALE = 65536.0
 # (bench.py --copy-reference: FETCH_SIZE 524,302 KiB -> x2.0, WRITE_SIZE
 # 1,048,576 KiB -> x1.0).  Valid only for the GEMM kernel source they were
 # taken on; bench.py reports null for any other.
-GEMM_TRAFFIC = {"gemm_src_sha256_16": "86b636081dc4422e", "fetch_kib": 49275.5, "write_kib": 32768.0,
+GEMM_TRAFFIC = {"gemm_src_sha256_16": "0193c4865902cae6", "fetch_kib": 49267.5, "write_kib": 32768.0,
                 "fetch_factor": 2.0, "write_factor": 1.0}
 
 
