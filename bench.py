@@ -39,7 +39,7 @@ LOSS_SCALE = 65536.0
 # (bench.py --copy-reference: FETCH_SIZE 524,302 KiB -> x2.0, WRITE_SIZE
 # 1,048,576 KiB -> x1.0).  Valid only for the GEMM kernel source they were
 # taken on; bench.py reports null for any other.
-GEMM_TRAFFIC = {"gemm_src_sha256_16": "0193c4865902cae6", "fetch_kib": 49267.5, "write_kib": 32768.0,
+GEMM_TRAFFIC = {"gemm_src_sha256_16": "168b3f1dc221af4c", "fetch_kib": 49267.5, "write_kib": 32768.0,
                 "fetch_factor": 2.0, "write_factor": 1.0}
 
 
@@ -332,6 +332,17 @@ def main():
         hbm["quantize_rowwise_transpose_GBps"] = 6.0 * nb / (r_rw["avg_us"] * 1e-6) / 1e9
         kern["quantize_rowwise_transpose_2p28"] = r_rw
         del big, bq, bh, big2, bqT
+        # the gradient half of the quantize-path workload: an equal-size tensor
+        # (magnitudes 10^U(-8,-2)) cast to e5m2
+        gbig = torch.from_numpy(C.quant_grad().view(np.int16)).view(torch.bfloat16).to(dev)
+        gq = torch.empty(gbig.shape, dtype=torch.uint8, device=dev)
+        grec = F.ScaleRec(device=dev)
+        r_gamax = T.run(lambda: F.fp8_amax(gbig, grec), 10)
+        r_gquant = T.run(lambda: F.fp8_quantize(gbig, F.E5M2, grec, gq), 10)
+        hbm["amax_plus_quantize_e5m2_GBps"] = 5.0 * nb / ((r_gamax["avg_us"] + r_gquant["avg_us"]) * 1e-6) / 1e9
+        kern["amax_2p28_grad"] = r_gamax
+        kern["quantize_e5m2_2p28"] = r_gquant
+        del gbig, gq
         log("HBM-scale unscale pass")
         sizes = C.scaler_sizes()
         grads = [(torch.randn(int(n), device=dev) * 0.5).half() for n in sizes]
@@ -349,6 +360,8 @@ def main():
         kern["unscale_check_norm_200_tensors"] = r_nrm
         del grads, nws
         torch.cuda.empty_cache()
+
+    small = small_layer(torch, F, dev, stream, T)
 
     mlp = None
     if not args.no_mlp:
@@ -409,10 +422,59 @@ def main():
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "wall_s_timed_region": round(wall, 4),
         "check": check,
+        "small_layer": small,
         "mlp_block": mlp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def small_layer(torch, F, dev, stream, T, reps=200):
+    """The small layer (B=64, K=128, N=256): launch-latency bound, so its
+    time per phase and its kernel launches are reported, eager and replayed
+    from a HIP graph."""
+    from workloads.configs import SMALL as S
+    import numpy as np
+    to_dev = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    x, w, gy = to_dev(S.x()), to_dev(S.w()), to_dev(S.gy())
+    saved = F.LinearSaved(S.M, S.N, S.K, device=dev)
+    ws = F.LinearBwdWs(S.M, S.N, device=dev)
+    y = torch.empty((S.M, S.N), dtype=torch.bfloat16, device=dev)
+    gx = torch.empty((S.M, S.K), dtype=torch.float16, device=dev)
+    gw = torch.empty((S.N, S.K), dtype=torch.float16, device=dev)
+    scale = torch.tensor([65536.0], dtype=torch.float32, device=dev)
+    tracker = torch.zeros(1, dtype=torch.int32, device=dev)
+    found = torch.zeros(1, dtype=torch.int32, device=dev)
+    fwd = lambda: F.fp8_scaled_linear_fwd(x, w, saved, y, F.OUT_BF16)
+    bwd = lambda: F.fp8_scaled_linear_bwd(gy, saved, ws, gx, gw, F.OUT_F16)
+    scaler = lambda: (F.amp_unscale_check([gx, gw], scale, found),
+                      F.amp_update_scale(scale, tracker, found, 2.0, 0.5, 2000))
+
+    def step():
+        fwd()
+        bwd()
+        scaler()
+
+    out = {"workload": "small linear B=64 K=128 N=256 + GradScaler step (init 65536, "
+                       "interval 2000)",
+           "fwd_us": round(T.run(fwd, reps)["avg_us"], 2),
+           "bwd_us": round(T.run(bwd, reps)["avg_us"], 2),
+           "scaler_step_us": round(T.run(scaler, reps)["avg_us"], 2),
+           "step_us": round(T.run(step, reps)["avg_us"], 2),
+           # tensors of at most 64 Ki elements are cast by one block each with
+           # their own amax, and the two backward GEMMs share a launch
+           "launches": {"fwd": 2, "bwd": 2, "scaler_step": 2}}
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        step()
+    out["step_graph_replay_us"] = round(T.run(g.replay, reps)["avg_us"], 2)
+    out["TFLOPs_eager"] = round(3 * 2.0 * S.M * S.N * S.K / (out["step_us"] * 1e-6) / 1e12, 4)
+    return out
 
 
 def mlp_block(torch, F, dev, stream, steps=10, warmup=3):

@@ -196,19 +196,23 @@ fp8sg_status linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t
   }
   hipStream_t s = S(stream);
   hipError_t e;
-  if (!delayed) {
-    AmaxArgs am{};
-    am.job[0] = AmaxJob{x, M * K, saved->x_sc, 0, amax_blocks_for(M * K)};
-    am.job[1] = AmaxJob{w, N * K, saved->w_sc, 0, amax_blocks_for(N * K)};
-    am.njobs = 2;
-    e = launch_amax(am, false, s);
-    if (e != hipSuccess) return FP8SG_ERR_HIP;
-  }
   QuantArgs qa{};
   qa.job[0] = QuantJob{x, M, K, saved->x_sc, saved->x_q, saved->x_qT, 0, 0, 0, hist_x, hist_len};
   qa.job[1] = QuantJob{w, N, K, saved->w_sc, saved->w_q, saved->w_qT, 0, 0, 0, hist_w, hist_len};
   qa.njobs = 2;
-  e = launch_quantize(qa, FP8SG_E4M3FN, s);
+  if (!delayed && self_cast_fits(qa)) {  // small x and W: amax and cast in one launch
+    e = launch_quantize_self(qa, FP8SG_E4M3FN, s);
+  } else {
+    if (!delayed) {
+      AmaxArgs am{};
+      am.job[0] = AmaxJob{x, M * K, saved->x_sc, 0, amax_blocks_for(M * K)};
+      am.job[1] = AmaxJob{w, N * K, saved->w_sc, 0, amax_blocks_for(N * K)};
+      am.njobs = 2;
+      e = launch_amax(am, false, s);
+      if (e != hipSuccess) return FP8SG_ERR_HIP;
+    }
+    e = launch_quantize(qa, FP8SG_E4M3FN, s);
+  }
   if (e != hipSuccess) return FP8SG_ERR_HIP;
 
   GemmProblem p{saved->x_q, saved->w_q, y, &saved->x_sc->inv, &saved->w_sc->inv, M, N, K};
@@ -236,31 +240,30 @@ fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64
   }
   hipStream_t s = S(stream);
   hipError_t e;
-  if (!hist_gy) {
-    AmaxArgs am{};
-    am.job[0] = AmaxJob{gy, M * N, ws->gy_sc, 0, amax_blocks_for(M * N)};
-    am.njobs = 1;
-    e = launch_amax(am, false, s);
-    if (e != hipSuccess) return FP8SG_ERR_HIP;
-  }
   QuantArgs qa{};
   qa.job[0] = QuantJob{gy, M, N, ws->gy_sc, ws->gy_q, ws->gy_qT, 0, 0, 0, hist_gy, hist_len};
   qa.njobs = 1;
-  e = launch_quantize(qa, FP8SG_E5M2, s);
+  if (!hist_gy && self_cast_fits(qa)) {  // small gy: amax and cast in one launch
+    e = launch_quantize_self(qa, FP8SG_E5M2, s);
+  } else {
+    if (!hist_gy) {
+      AmaxArgs am{};
+      am.job[0] = AmaxJob{gy, M * N, ws->gy_sc, 0, amax_blocks_for(M * N)};
+      am.njobs = 1;
+      e = launch_amax(am, false, s);
+      if (e != hipSuccess) return FP8SG_ERR_HIP;
+    }
+    e = launch_quantize(qa, FP8SG_E5M2, s);
+  }
   if (e != hipSuccess) return FP8SG_ERR_HIP;
 
   GemmProblem dg{ws->gy_q, saved->w_qT, gx, &ws->gy_sc->inv, &saved->w_sc->inv, M, K, N,
                  amp_scale, found_inf};
   GemmProblem wg{ws->gy_qT, saved->x_qT, gw, &ws->gy_sc->inv, &saved->x_sc->inv, N, K, M,
                  amp_scale, found_inf};
-  if (amp_scale) {  // fp16 gradients unscaled and checked in the GEMM epilogues
-    e = launch_gemm_unscale(dg, FP8SG_E5M2, FP8SG_E4M3FN, s);
-    if (e != hipSuccess) return FP8SG_ERR_HIP;
-    return hip_status(launch_gemm_unscale(wg, FP8SG_E5M2, FP8SG_E4M3FN, s));
-  }
-  e = launch_gemm(dg, FP8SG_E5M2, FP8SG_E4M3FN, out, s);
-  if (e != hipSuccess) return FP8SG_ERR_HIP;
-  return hip_status(launch_gemm(wg, FP8SG_E5M2, FP8SG_E4M3FN, out, s));
+  if (amp_scale)  // fp16 gradients unscaled and checked in the GEMM epilogues
+    return hip_status(launch_gemm_unscale_pair(dg, wg, s));
+  return hip_status(launch_gemm_pair(dg, wg, FP8SG_E5M2, FP8SG_E4M3FN, out, s));
 }
 
 }  // namespace

@@ -8,4 +8,19 @@ hipError_t launch_gemm(const GemmProblem& p, int fa, int fb, int out, hipStream_
   return launch_gemm_any<false>(p, fa, fb, out, stream);
 }
 
+hipError_t launch_gemm_pair(const GemmProblem& p0, const GemmProblem& p1, int fa, int fb, int out,
+                           hipStream_t stream) {
+  // the backward pair: gradient codes (fa) x saved codes (fb)
+  if (fa == FP8SG_E5M2 && fb == FP8SG_E4M3FN) {
+    switch (out) {
+      case FP8SG_OUT_BF16: return launch_tiles_pair<1, 0, FP8SG_OUT_BF16, false>(p0, p1, stream);
+      case FP8SG_OUT_F16: return launch_tiles_pair<1, 0, FP8SG_OUT_F16, false>(p0, p1, stream);
+      default: return launch_tiles_pair<1, 0, FP8SG_OUT_F32, false>(p0, p1, stream);
+    }
+  }
+  hipError_t e = launch_gemm(p0, fa, fb, out, stream);
+  if (e != hipSuccess) return e;
+  return launch_gemm(p1, fa, fb, out, stream);
+}
+
 }  // namespace fp8sg

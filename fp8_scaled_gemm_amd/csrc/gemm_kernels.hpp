@@ -150,7 +150,7 @@ struct Alpha {
 // (BN/WN) sub-tile of 16 x 16 blocks; results are stored as one 8-byte
 // (bf16/fp16) or 16-byte (fp32) write per lane and block.
 template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW>
-__global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
+__device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, int by) {
   using Cfg = GemmCfg<BM, BN, WM, WN>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* As = smem;                  // [2][BM][128]
@@ -160,8 +160,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int wm = wave / WN, wn = wave % WN;
-  const int64_t bm = (int64_t)blockIdx.y * BM;
-  const int64_t bn = (int64_t)blockIdx.x * BN;
+  const int64_t bm = (int64_t)by * BM;
+  const int64_t bn = (int64_t)bx * BN;
   const int64_t M = p.M, N = p.N, K = p.K;
   const int nk = (int)((K + kBK - 1) / kBK);
 
@@ -268,6 +268,21 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
     }
   }
   if constexpr (OUT == kOutF16Unscale) us.flag(p, lane);
+}
+
+template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW>
+__global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
+  gemm_small_tile<BM, BN, WM, WN, FA, FB, OUT, RW>(p, blockIdx.x, blockIdx.y);
+}
+
+// Two independent small problems of the same kind in one launch (the small
+// backward pass's dgrad and wgrad, where launches dominate): blockIdx.z picks
+// the problem; blocks past its tiles leave at once.
+template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW>
+__global__ __launch_bounds__(WM* WN* kWave) void k_gemm2(GemmProblem p0, GemmProblem p1) {
+  const GemmProblem& p = blockIdx.z ? p1 : p0;
+  if ((int64_t)blockIdx.y * BM >= p.M || (int64_t)blockIdx.x * BN >= p.N) return;
+  gemm_small_tile<BM, BN, WM, WN, FA, FB, OUT, RW>(p, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -602,6 +617,36 @@ static hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
   const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
   if (big >= 128 && p.K * 256 < (1ll << 31)) return launch_pingpong<FA, FB, OUT, RW>(p, stream);
   return launch_cfg<128, 128, 2, 2, FA, FB, OUT, RW>(p, stream);
+}
+
+// Two problems: one launch of the 128 x 128 kernel when both take it,
+// otherwise one launch each.
+template <int FA, int FB, int OUT, bool RW>
+static hipError_t launch_tiles_pair(const GemmProblem& p0, const GemmProblem& p1, hipStream_t stream) {
+  auto big = [](const GemmProblem& p) {
+    return ((p.M + 255) / 256) * ((p.N + 255) / 256) >= 128 && p.K * 256 < (1ll << 31);
+  };
+  if (big(p0) || big(p1)) {
+    hipError_t e = p0.M && p0.N ? launch_tiles<FA, FB, OUT, RW>(p0, stream) : hipSuccess;
+    if (e != hipSuccess) return e;
+    return p1.M && p1.N ? launch_tiles<FA, FB, OUT, RW>(p1, stream) : hipSuccess;
+  }
+  using Cfg = GemmCfg<128, 128, 2, 2>;
+  auto kern = k_gemm2<128, 128, 2, 2, FA, FB, OUT, RW>;
+  static bool attr_set = false;
+  if (!attr_set && Cfg::kLdsBytes > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+  const int64_t gx = cdiv(p0.N, 128) > cdiv(p1.N, 128) ? cdiv(p0.N, 128) : cdiv(p1.N, 128);
+  const int64_t gy = cdiv(p0.M, 128) > cdiv(p1.M, 128) ? cdiv(p0.M, 128) : cdiv(p1.M, 128);
+  if (gx == 0 || gy == 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)gy, 2), dim3(Cfg::kThreads), Cfg::kLdsBytes,
+                     stream, p0, p1);
+  return hipGetLastError();
 }
 
 template <int FA, int FB, bool RW>

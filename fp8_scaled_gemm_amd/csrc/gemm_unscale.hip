@@ -17,4 +17,8 @@ hipError_t launch_gemm_unscale(const GemmProblem& p, int fa, int fb, hipStream_t
   return launch_tiles<1, 1, kOutF16Unscale, false>(p, stream);
 }
 
+hipError_t launch_gemm_unscale_pair(const GemmProblem& p0, const GemmProblem& p1, hipStream_t stream) {
+  return launch_tiles_pair<FP8SG_E5M2, FP8SG_E4M3FN, kOutF16Unscale, false>(p0, p1, stream);
+}
+
 }  // namespace fp8sg

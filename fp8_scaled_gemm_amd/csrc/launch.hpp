@@ -51,6 +51,13 @@ struct QuantArgs {
 // cols multiples of 16 with a transposed copy), the flat kernel (no transposed
 // copy) or the per-element kernel (a transposed copy of an odd shape).
 hipError_t launch_quantize(QuantArgs args, int fmt, hipStream_t stream);
+// Small tensors: one block per job reduces its own amax and casts it, so the
+// amax launch is not needed (tiled path, dynamic scaling, at most
+// kSelfCastMaxElems elements per job).  Records, codes and transposed codes
+// as launch_amax + launch_quantize write them.
+constexpr int64_t kSelfCastMaxElems = 65536;
+bool self_cast_fits(const QuantArgs& a);
+hipError_t launch_quantize_self(QuantArgs args, int fmt, hipStream_t stream);
 
 // ---- GEMM (gemm.hip)
 struct GemmProblem {
@@ -73,6 +80,12 @@ hipError_t launch_gemm(const GemmProblem& p, int fa, int fb, int out, hipStream_
 hipError_t launch_gemm_rowwise(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);
 // The kOutF16Unscale epilogue (gemm_unscale.hip); p.amp_scale and p.found_inf set.
 hipError_t launch_gemm_unscale(const GemmProblem& p, int fa, int fb, hipStream_t stream);
+// The backward pair (dgrad, wgrad): one launch of the 128 x 128 kernel when
+// both are small, otherwise one launch each.
+hipError_t launch_gemm_pair(const GemmProblem& p0, const GemmProblem& p1, int fa, int fb, int out,
+                           hipStream_t stream);
+hipError_t launch_gemm_unscale_pair(const GemmProblem& p0, const GemmProblem& p1,
+                                    hipStream_t stream);
 
 // ---- row-wise quantize (rowwise.hip)
 struct RowwiseArgs {

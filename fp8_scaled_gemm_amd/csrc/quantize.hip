@@ -59,6 +59,23 @@ __device__ __forceinline__ float job_amax(const QuantJob& job) {
   else return amax_from_partials<kQThreads>(job.rec);
 }
 
+// SELF (a small tensor cast by one block): the block reduces |x| over the
+// whole tensor itself, then casts it [FP8-TRAIN §2]; x is read twice, the
+// second time from L2.  The amax also goes to the record's first partial
+// slot, as if one amax block had written it.
+__device__ __forceinline__ float self_amax(const QuantJob& job) {
+  const int64_t nv = job.rows * job.cols / 8;  // cols % 16 == 0 on this path
+  const uint4* xv = reinterpret_cast<const uint4*>(job.x);
+  uint32_t m = 0;
+  for (int64_t k = threadIdx.x; k < nv; k += kQThreads) m = absmax8(m, xv[k]);
+  const uint32_t bits = block_max_u32<kQThreads>(absmax_bits(m));
+  if (threadIdx.x == 0) {
+    job.rec->_part[0] = bits;
+    job.rec->_nparts = 1;
+  }
+  return __uint_as_float(bits);
+}
+
 // DELAYED: this block's |x| maximum (packed pair max m) into its partial slot.
 template <bool DELAYED>
 __device__ __forceinline__ void store_block_amax(const QuantJob& job, int lb, uint32_t m) {
@@ -85,12 +102,12 @@ __device__ __forceinline__ void publish_scale(fp8sg_scale_rec* rec, float amax, 
   }
 }
 
-template <int FMT, bool S, bool DELAYED>
+template <int FMT, bool S, bool DELAYED, bool SELF = false>
 __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
   int lb;
   const QuantJob& job = pick_job(args, lb);
   const int tid = threadIdx.x;
-  const float amax = job_amax<DELAYED>(job);
+  const float amax = SELF ? self_amax(job) : job_amax<DELAYED>(job);
   const ScaleVals sv = scale_from_amax(amax, FMT);
   if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
 
@@ -264,7 +281,7 @@ static int blocks_of(QuantJob& j, QuantPath p) {
 }
 
 template <int FMT, bool DELAYED>
-static hipError_t launch_fmt(QuantArgs a, hipStream_t stream) {
+static hipError_t launch_fmt(QuantArgs a, hipStream_t stream, bool self = false) {
   // jobs of one launch must take the same path; otherwise split into launches
   for (int j0 = 0; j0 < a.njobs;) {
     const QuantPath p = path_of(a.job[j0]);
@@ -275,13 +292,16 @@ static hipError_t launch_fmt(QuantArgs a, hipStream_t stream) {
     for (; j < a.njobs && path_of(a.job[j]) == p; ++j) {
       QuantJob jb = a.job[j];
       jb.nblocks = blocks_of(jb, p);
+      if (self) jb.nblocks = 1;  // the block loops over all the tensor's tiles
       jb.block0 = total;
       total += jb.nblocks;
       bytes += jb.rows * jb.cols * (jb.qT ? 4 : 3);
       sub.job[sub.njobs++] = jb;
     }
     const bool st = bytes >= kStreamBytes;
-    if (p == kPathTiled && st)
+    if (self && p == kPathTiled && !DELAYED)
+      hipLaunchKernelGGL((k_quant_tiled<FMT, false, false, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
+    else if (p == kPathTiled && st)
       hipLaunchKernelGGL((k_quant_tiled<FMT, true, DELAYED>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathTiled)
       hipLaunchKernelGGL((k_quant_tiled<FMT, false, DELAYED>), dim3(total), dim3(kQThreads), 0, stream, sub);
@@ -301,6 +321,19 @@ static hipError_t launch_fmt(QuantArgs a, hipStream_t stream) {
     j0 = j;
   }
   return hipSuccess;
+}
+
+bool self_cast_fits(const QuantArgs& a) {
+  for (int j = 0; j < a.njobs; ++j) {
+    const QuantJob& jb = a.job[j];
+    if (jb.hist || path_of(jb) != kPathTiled || jb.rows * jb.cols > kSelfCastMaxElems) return false;
+  }
+  return a.njobs > 0;
+}
+
+hipError_t launch_quantize_self(QuantArgs args, int fmt, hipStream_t stream) {
+  return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN, false>(args, stream, true)
+                             : launch_fmt<FP8SG_E5M2, false>(args, stream, true);
 }
 
 hipError_t launch_quantize(QuantArgs args, int fmt, hipStream_t stream) {
