@@ -28,6 +28,8 @@ EXPORTS = ("fp8sg_status_string", "fp8sg_version", "amp_norm_workspace_len", "fp
            "fp8_quantize_rowwise", "fp8_gemm_rowwise", "fp8_scaled_linear_fwd_rowwise",
            "fp8_scaled_linear_bwd_rowwise", "fp8_scaled_linear_bwd_unscale", "fp8_gemm_unscale")
 MAX_HISTORY = 1024
+MAX_DIM = 1 << 29     # largest matrix dimension an entry point takes
+MAX_ELEMS = 1 << 35   # largest tensor, in elements
 
 
 class Fp8sgError(RuntimeError):

@@ -211,41 +211,55 @@ int64_t unscale_blocks_bound(const int64_t* numel, int32_t ntensors) {
 hipError_t launch_unscale_check(uint16_t* const* grads, const int64_t* numel, int32_t ntensors,
                                 const float* scale, int32_t* found_inf, float* parts,
                                 float* sumsq_norm, hipStream_t stream) {
+  // A launch takes up to kAmpTensorsPerLaunch tensors and kAmpMaxBlocks
+  // blocks; a tensor of at most FP8SG_MAX_ELEMS elements always fits alone.
+  constexpr int32_t kAmpMaxBlocks = 1 << 23;
+  static_assert(FP8SG_MAX_ELEMS / kAmpElemsPerBlock + 1 <= kAmpMaxBlocks, "one tensor per launch");
   int64_t part0 = 0;
-  for (int32_t t0 = 0; t0 < ntensors; t0 += kAmpTensorsPerLaunch) {
-    AmpTable tab{};
-    tab.scale = scale;
-    tab.found_inf = found_inf;
-    tab.parts = parts;
-    tab.part0 = part0;
-    int32_t total = 0;
-    const int32_t cnt = ntensors - t0 < kAmpTensorsPerLaunch ? ntensors - t0 : kAmpTensorsPerLaunch;
-    for (int32_t i = 0; i < cnt; ++i) {
-      const uintptr_t p = reinterpret_cast<uintptr_t>(grads[t0 + i]);
-      const int32_t head = (int32_t)((p & 15u) >> 1);
-      const int64_t n = numel[t0 + i] > 0 ? numel[t0 + i] + head : 0;  // span from the base
-      tab.ptr[tab.ntensors] = reinterpret_cast<uint16_t*>(p & ~(uintptr_t)15);
-      tab.numel[tab.ntensors] = n;
-      tab.head[tab.ntensors] = head;
-      tab.block0[tab.ntensors] = total;
-      total += (int32_t)((n + kAmpElemsPerBlock - 1) / kAmpElemsPerBlock);
-      ++tab.ntensors;
-    }
+  AmpTable tab{};
+  int32_t total = 0;
+  auto flush = [&]() -> hipError_t {
     tab.block0[tab.ntensors] = total;
-    if (total == 0) continue;
-    const bool stream_pass = 4ll * kAmpElemsPerBlock * total >= kStreamBytes;  // 2 B in + 2 B out
-    if (parts && stream_pass)
-      hipLaunchKernelGGL((k_unscale_check<true, true>), dim3(total), dim3(kAmpThreads), 0, stream, tab);
-    else if (parts)
-      hipLaunchKernelGGL((k_unscale_check<false, true>), dim3(total), dim3(kAmpThreads), 0, stream, tab);
-    else if (stream_pass)
-      hipLaunchKernelGGL((k_unscale_check<true, false>), dim3(total), dim3(kAmpThreads), 0, stream, tab);
-    else
-      hipLaunchKernelGGL((k_unscale_check<false, false>), dim3(total), dim3(kAmpThreads), 0, stream, tab);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    part0 += total;
+    if (total > 0) {
+      tab.scale = scale;
+      tab.found_inf = found_inf;
+      tab.parts = parts;
+      tab.part0 = part0;
+      const bool stream_pass = 4ll * kAmpElemsPerBlock * total >= kStreamBytes;  // 2 B in + 2 B out
+      if (parts && stream_pass)
+        hipLaunchKernelGGL((k_unscale_check<true, true>), dim3(total), dim3(kAmpThreads), 0, stream, tab);
+      else if (parts)
+        hipLaunchKernelGGL((k_unscale_check<false, true>), dim3(total), dim3(kAmpThreads), 0, stream, tab);
+      else if (stream_pass)
+        hipLaunchKernelGGL((k_unscale_check<true, false>), dim3(total), dim3(kAmpThreads), 0, stream, tab);
+      else
+        hipLaunchKernelGGL((k_unscale_check<false, false>), dim3(total), dim3(kAmpThreads), 0, stream, tab);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      part0 += total;
+    }
+    tab = AmpTable{};
+    total = 0;
+    return hipSuccess;
+  };
+  for (int32_t i = 0; i < ntensors; ++i) {
+    const uintptr_t p = reinterpret_cast<uintptr_t>(grads[i]);
+    const int32_t head = (int32_t)((p & 15u) >> 1);
+    const int64_t n = numel[i] > 0 ? numel[i] + head : 0;  // span from the base
+    const int32_t nb = (int32_t)((n + kAmpElemsPerBlock - 1) / kAmpElemsPerBlock);
+    if (tab.ntensors == kAmpTensorsPerLaunch || total + (int64_t)nb > kAmpMaxBlocks) {
+      const hipError_t e = flush();
+      if (e != hipSuccess) return e;
+    }
+    tab.ptr[tab.ntensors] = reinterpret_cast<uint16_t*>(p & ~(uintptr_t)15);
+    tab.numel[tab.ntensors] = n;
+    tab.head[tab.ntensors] = head;
+    tab.block0[tab.ntensors] = total;
+    total += nb;
+    ++tab.ntensors;
   }
+  const hipError_t ef = flush();
+  if (ef != hipSuccess) return ef;
   if (parts) {
     double* part64 = reinterpret_cast<double*>(parts + ((part0 + 1) & ~int64_t(1)));
     hipLaunchKernelGGL(k_norm_partial, dim3(kNormGroups), dim3(kAmpThreads), 0, stream, parts,

@@ -26,6 +26,15 @@ bool hist_ok(const float* h) { return h && (reinterpret_cast<uintptr_t>(h) & 3u)
 hipStream_t S(fp8sg_stream s) { return reinterpret_cast<hipStream_t>(s); }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Size limits: an a x b tensor has at most FP8SG_MAX_ELEMS elements (tested
+// without forming an overflowing product); a matrix dimension of a row-wise
+// cast or a GEMM is at most FP8SG_MAX_DIM.
+bool elems_ok(int64_t a, int64_t b) {
+  return a >= 0 && b >= 0 && (a == 0 || b <= FP8SG_MAX_ELEMS / a);
+}
+bool mat_ok(int64_t r, int64_t c) { return r <= FP8SG_MAX_DIM && c <= FP8SG_MAX_DIM && elems_ok(r, c); }
+bool gemm_ok(int64_t M, int64_t N, int64_t K) { return mat_ok(M, K) && mat_ok(N, K) && mat_ok(M, N); }
+
 // A scale-vector pair (amax float[n], inv double[n]) of a row-wise cast.
 fp8sg_status check_vec(const float* amax, const double* inv, int64_t n) {
   if (n > 0 && (!amax || !inv)) return FP8SG_ERR_NULL;
@@ -36,17 +45,19 @@ fp8sg_status check_vec(const float* amax, const double* inv, int64_t n) {
 fp8sg_status check_gemm(const void* A, int fa, const void* B, int fb, const void* ia,
                         const void* ib, const void* C, int out, int64_t M, int64_t N, int64_t K) {
   if (!fmt_ok(fa) || !fmt_ok(fb) || !out_ok(out)) return FP8SG_ERR_FORMAT;
-  if (!dims16(M) || !dims16(N) || !dims16(K)) return FP8SG_ERR_SHAPE;
+  if (!dims16(M) || !dims16(N) || !dims16(K) || !gemm_ok(M, N, K)) return FP8SG_ERR_SHAPE;
   // zero-sized operands may come with a NULL data pointer
   if ((M * K > 0 && !A) || (N * K > 0 && !B) || (M * N > 0 && !C) || !ia || !ib)
     return FP8SG_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return FP8SG_ERR_ALIGN;
+  if (!aligned(ia, 8) || !aligned(ib, 8)) return FP8SG_ERR_ALIGN;
   return FP8SG_OK;
 }
 
 fp8sg_status check_saved(const fp8_linear_saved* s) {
   if (!s || !s->x_q || !s->x_qT || !s->w_q || !s->w_qT || !s->x_sc || !s->w_sc) return FP8SG_ERR_NULL;
-  if (!aligned16(s->x_q) || !aligned16(s->x_qT) || !aligned16(s->w_q) || !aligned16(s->w_qT))
+  if (!aligned16(s->x_q) || !aligned16(s->x_qT) || !aligned16(s->w_q) || !aligned16(s->w_qT) ||
+      !aligned(s->x_sc, 8) || !aligned(s->w_sc, 8))
     return FP8SG_ERR_ALIGN;
   return FP8SG_OK;
 }
@@ -59,8 +70,8 @@ const char* fp8sg_status_string(int status) {
   switch (status) {
     case FP8SG_OK: return "ok";
     case FP8SG_ERR_NULL: return "null pointer argument";
-    case FP8SG_ERR_SHAPE: return "invalid size (negative, or not a required multiple of 16)";
-    case FP8SG_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case FP8SG_ERR_SHAPE: return "invalid size (negative, above the size limits, or not a required multiple of 16)";
+    case FP8SG_ERR_ALIGN: return "pointer not aligned (16 bytes for tensors, 8 for records and fp64 vectors, 4 for scalars)";
     case FP8SG_ERR_FORMAT: return "unknown format or output type";
     case FP8SG_ERR_HIP: return "HIP launch or runtime error";
     default: return "unknown status";
@@ -71,8 +82,8 @@ int fp8sg_version(void) { return 100; }
 
 fp8sg_status fp8_amax(const uint16_t* x, int64_t n, fp8sg_scale_rec* rec, fp8sg_stream stream) {
   if (!rec || (n > 0 && !x)) return FP8SG_ERR_NULL;
-  if (n < 0) return FP8SG_ERR_SHAPE;
-  if (!aligned16(x)) return FP8SG_ERR_ALIGN;
+  if (n < 0 || n > FP8SG_MAX_ELEMS) return FP8SG_ERR_SHAPE;
+  if (!aligned16(x) || !aligned(rec, 8)) return FP8SG_ERR_ALIGN;
   AmaxArgs a{};
   a.job[0] = AmaxJob{x, n, rec, 0, amax_blocks_for(n)};
   a.njobs = 1;
@@ -83,9 +94,10 @@ fp8sg_status fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, fp8sg_f
                           fp8sg_scale_rec* rec, uint8_t* q, uint8_t* qT, fp8sg_stream stream) {
   if (!rec) return FP8SG_ERR_NULL;
   if (!fmt_ok(fmt)) return FP8SG_ERR_FORMAT;
-  if (rows < 0 || cols < 0) return FP8SG_ERR_SHAPE;
+  if (!elems_ok(rows, cols)) return FP8SG_ERR_SHAPE;
   if (rows * cols > 0 && (!x || !q)) return FP8SG_ERR_NULL;
-  if (!aligned16(x) || !aligned16(q) || (qT && !aligned16(qT))) return FP8SG_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(q) || (qT && !aligned16(qT)) || !aligned(rec, 8))
+    return FP8SG_ERR_ALIGN;
   QuantArgs a{};
   a.job[0] = QuantJob{x, rows, cols, rec, q, qT, 0, 0, 0};
   a.njobs = 1;
@@ -98,9 +110,10 @@ fp8sg_status fp8_quantize_delayed(const uint16_t* x, int64_t rows, int64_t cols,
                                   fp8sg_stream stream) {
   if (!rec || !amax_history) return FP8SG_ERR_NULL;
   if (!fmt_ok(fmt)) return FP8SG_ERR_FORMAT;
-  if (rows < 0 || cols < 0 || !hist_len_ok(history_len)) return FP8SG_ERR_SHAPE;
+  if (!elems_ok(rows, cols) || !hist_len_ok(history_len)) return FP8SG_ERR_SHAPE;
   if (rows * cols > 0 && (!x || !q)) return FP8SG_ERR_NULL;
-  if (!aligned16(x) || !aligned16(q) || (qT && !aligned16(qT))) return FP8SG_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(q) || (qT && !aligned16(qT)) || !aligned(rec, 8))
+    return FP8SG_ERR_ALIGN;
   if (reinterpret_cast<uintptr_t>(amax_history) & 3u) return FP8SG_ERR_ALIGN;
   QuantArgs a{};
   a.job[0] = QuantJob{x, rows, cols, rec, q, qT, 0, 0, 0, amax_history, history_len};
@@ -121,7 +134,7 @@ fp8sg_status fp8_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols,
                                   float* row_amax, double* row_inv, uint8_t* q, float* col_amax,
                                   double* col_inv, uint8_t* qT, fp8sg_stream stream) {
   if (!fmt_ok(fmt)) return FP8SG_ERR_FORMAT;
-  if (!dims16(rows) || !dims16(cols)) return FP8SG_ERR_SHAPE;
+  if (!dims16(rows) || !dims16(cols) || !mat_ok(rows, cols)) return FP8SG_ERR_SHAPE;
   if (rows * cols > 0 && (!x || !q)) return FP8SG_ERR_NULL;
   fp8sg_status st = check_vec(row_amax, row_inv, rows);
   if (st != FP8SG_OK) return st;
@@ -141,7 +154,6 @@ fp8sg_status fp8_gemm_rowwise(const uint8_t* A, fp8sg_format fa, const uint8_t* 
                               int64_t M, int64_t N, int64_t Kc, fp8sg_stream stream) {
   fp8sg_status st = check_gemm(A, fa, B, fb, inv_a, inv_b, C, out, M, N, Kc);
   if (st != FP8SG_OK) return st;
-  if (!aligned(inv_a, 8) || !aligned(inv_b, 8)) return FP8SG_ERR_ALIGN;
   GemmProblem p{A, B, C, inv_a, inv_b, M, N, Kc};
   return hip_status(launch_gemm_rowwise(p, fa, fb, out, S(stream)));
 }
@@ -186,7 +198,8 @@ fp8sg_status linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t
   fp8sg_status st = check_saved(saved);
   if (st != FP8SG_OK) return st;
   if (!out_ok(out)) return FP8SG_ERR_FORMAT;
-  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K)) return FP8SG_ERR_SHAPE;
+  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K) || !gemm_ok(M, N, K))
+    return FP8SG_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return FP8SG_ERR_ALIGN;
   const bool delayed = hist_x || hist_w;
   if (delayed) {
@@ -230,9 +243,10 @@ fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64
   if (st != FP8SG_OK) return st;
   if (!ws->gy_q || !ws->gy_qT || !ws->gy_sc) return FP8SG_ERR_NULL;
   if (!out_ok(out)) return FP8SG_ERR_FORMAT;
-  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K)) return FP8SG_ERR_SHAPE;
+  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K) || !gemm_ok(M, N, K))
+    return FP8SG_ERR_SHAPE;
   if (!aligned16(gy) || !aligned16(gx) || !aligned16(gw) || !aligned16(ws->gy_q) ||
-      !aligned16(ws->gy_qT))
+      !aligned16(ws->gy_qT) || !aligned(ws->gy_sc, 8))
     return FP8SG_ERR_ALIGN;
   if (hist_gy) {
     if (!hist_len_ok(hist_len)) return FP8SG_ERR_SHAPE;
@@ -318,7 +332,8 @@ fp8sg_status fp8_scaled_linear_fwd_rowwise(const uint16_t* x, const uint16_t* w,
                                            void* y, fp8sg_out out, fp8sg_stream stream) {
   if (!x || !w || !y) return FP8SG_ERR_NULL;
   if (!out_ok(out)) return FP8SG_ERR_FORMAT;
-  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K)) return FP8SG_ERR_SHAPE;
+  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K) || !gemm_ok(M, N, K))
+    return FP8SG_ERR_SHAPE;
   fp8sg_status st = check_saved_rw(saved, M, N, K);
   if (st != FP8SG_OK) return st;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return FP8SG_ERR_ALIGN;
@@ -342,7 +357,8 @@ fp8sg_status fp8_scaled_linear_bwd_rowwise(const uint16_t* gy, const fp8_linear_
                                            fp8sg_out out, fp8sg_stream stream) {
   if (!gy || !ws || !gx || !gw) return FP8SG_ERR_NULL;
   if (!out_ok(out)) return FP8SG_ERR_FORMAT;
-  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K)) return FP8SG_ERR_SHAPE;
+  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K) || !gemm_ok(M, N, K))
+    return FP8SG_ERR_SHAPE;
   fp8sg_status st = check_saved_rw(saved, M, N, K);
   if (st != FP8SG_OK) return st;
   if (!ws->gy_q || !ws->gy_qT) return FP8SG_ERR_NULL;
@@ -369,8 +385,9 @@ fp8sg_status amp_unscale_check(uint16_t* const* grads, const int64_t* numel, int
   if (!scale || !found_inf) return FP8SG_ERR_NULL;
   if (ntensors < 0 || ntensors > 8192) return FP8SG_ERR_SHAPE;
   if (ntensors > 0 && (!grads || !numel)) return FP8SG_ERR_NULL;
+  if (!aligned(scale, 4) || !aligned(found_inf, 4)) return FP8SG_ERR_ALIGN;
   for (int32_t i = 0; i < ntensors; ++i) {
-    if (numel[i] < 0) return FP8SG_ERR_SHAPE;
+    if (numel[i] < 0 || numel[i] > FP8SG_MAX_ELEMS) return FP8SG_ERR_SHAPE;
     if (numel[i] > 0 && !grads[i]) return FP8SG_ERR_NULL;
     if (numel[i] > 0 && (reinterpret_cast<uintptr_t>(grads[i]) & 1u)) return FP8SG_ERR_ALIGN;
   }
@@ -381,7 +398,7 @@ fp8sg_status amp_unscale_check(uint16_t* const* grads, const int64_t* numel, int
 int64_t amp_norm_workspace_len(const int64_t* numel, int32_t ntensors) {
   if (ntensors < 0 || ntensors > 8192 || (ntensors > 0 && !numel)) return -1;
   for (int32_t i = 0; i < ntensors; ++i)
-    if (numel[i] < 0) return -1;
+    if (numel[i] < 0 || numel[i] > FP8SG_MAX_ELEMS) return -1;
   return unscale_blocks_bound(numel, ntensors);
 }
 
@@ -392,8 +409,9 @@ fp8sg_status amp_unscale_check_norm(uint16_t* const* grads, const int64_t* numel
   if (!scale || !found_inf || !sumsq_norm) return FP8SG_ERR_NULL;
   if (ntensors < 0 || ntensors > 8192) return FP8SG_ERR_SHAPE;
   if (ntensors > 0 && (!grads || !numel)) return FP8SG_ERR_NULL;
+  if (!aligned(scale, 4) || !aligned(found_inf, 4)) return FP8SG_ERR_ALIGN;
   for (int32_t i = 0; i < ntensors; ++i) {
-    if (numel[i] < 0) return FP8SG_ERR_SHAPE;
+    if (numel[i] < 0 || numel[i] > FP8SG_MAX_ELEMS) return FP8SG_ERR_SHAPE;
     if (numel[i] > 0 && !grads[i]) return FP8SG_ERR_NULL;
     if (numel[i] > 0 && (reinterpret_cast<uintptr_t>(grads[i]) & 1u)) return FP8SG_ERR_ALIGN;
   }
@@ -401,7 +419,7 @@ fp8sg_status amp_unscale_check_norm(uint16_t* const* grads, const int64_t* numel
   if (workspace_len < need) return FP8SG_ERR_SHAPE;
   if (!workspace) return FP8SG_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(sumsq_norm) & 3u) return FP8SG_ERR_ALIGN;
-  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 7u)) return FP8SG_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(workspace) & 7u) return FP8SG_ERR_ALIGN;
   return hip_status(launch_unscale_check(grads, numel, ntensors, scale, found_inf, workspace,
                                          sumsq_norm, S(stream)));
 }
@@ -411,6 +429,8 @@ fp8sg_status amp_update_scale(float* scale, int32_t* growth_tracker, int32_t* fo
                               int32_t growth_interval, fp8sg_stream stream) {
   if (!scale || !growth_tracker || !found_inf) return FP8SG_ERR_NULL;
   if (growth_interval < 1) return FP8SG_ERR_SHAPE;
+  if (!aligned(scale, 4) || !aligned(growth_tracker, 4) || !aligned(found_inf, 4))
+    return FP8SG_ERR_ALIGN;
   return hip_status(launch_update_scale(scale, growth_tracker, found_inf, growth_factor,
                                         backoff_factor, growth_interval, S(stream)));
 }

@@ -268,6 +268,7 @@ static int blocks_of(QuantJob& j, QuantPath p) {
     const int64_t tr = (j.rows + kQTile - 1) / kQTile, tc = (j.cols + kQTile - 1) / kQTile;
     j.tiles_c = (int32_t)(tc > 0 ? tc : 1);
     b = tr * tc;
+    if (b > (1 << 20)) b = 1 << 20;  // the blocks stride over the tiles
   } else if (p == kPathFlat) {
     const int64_t per = (int64_t)kQThreads * kFlatUnroll;
     b = ((n >> 3) + per - 1) / per;

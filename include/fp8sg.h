@@ -22,7 +22,9 @@
  *    failed; kernels already enqueued by the call may have run.  No exception
  *    crosses the ABI, and there is no global error state besides the return.
  *  - Device pointers to tensors must be 16-byte aligned (FP8SG_ERR_ALIGN),
- *    except the fp16 gradients of amp_unscale_check (2-byte aligned).
+ *    except the fp16 gradients of amp_unscale_check (2-byte aligned); scale
+ *    records 8-byte aligned; fp32 and int32 scalars 4-byte aligned.
+ *  - Sizes are bounded by FP8SG_MAX_DIM and FP8SG_MAX_ELEMS (below).
  *  - Calls that share an output or state buffer must not overlap in time.
  */
 #ifndef FP8SG_H
@@ -54,8 +56,11 @@ typedef enum {
 typedef enum {
   FP8SG_OK = 0,
   FP8SG_ERR_NULL = 1,   /* a required pointer is NULL                      */
-  FP8SG_ERR_SHAPE = 2,  /* a size is negative or breaks a multiple-of rule */
-  FP8SG_ERR_ALIGN = 3,  /* a tensor pointer is not 16-byte aligned         */
+  FP8SG_ERR_SHAPE = 2,  /* a size is negative, above the size limits below
+                           or breaks a multiple-of rule                     */
+  FP8SG_ERR_ALIGN = 3,  /* a pointer lacks the alignment its call needs:
+                           16 bytes for tensors, 8 for scale records and
+                           fp64 vectors, 4 for fp32/int32 scalars           */
   FP8SG_ERR_FORMAT = 4, /* unknown fp8sg_format / fp8sg_out value          */
   FP8SG_ERR_HIP = 5     /* a HIP launch or runtime call failed             */
 } fp8sg_status;
@@ -66,6 +71,18 @@ typedef void* fp8sg_stream; /* hipStream_t */
 #define FP8SG_AMAX_PARTS 1024
 /* Longest amax history the delayed-scaling entry points take. */
 #define FP8SG_MAX_HISTORY 1024
+
+/*
+ * Size limits, checked by every entry point (FP8SG_ERR_SHAPE beyond them).
+ * A matrix dimension (rows and cols of a row-wise cast, M, N, Kc of a GEMM or
+ * linear layer) is at most FP8SG_MAX_DIM; every tensor an entry point reads
+ * or writes holds at most FP8SG_MAX_ELEMS elements (64 GiB of bf16).  The
+ * launch grids and 32-bit per-launch block counts are sized for these.
+ * fp8_amax, fp8_quantize, fp8_quantize_delayed and the amp_* calls bound only
+ * the element count.
+ */
+#define FP8SG_MAX_DIM (1LL << 29)
+#define FP8SG_MAX_ELEMS (1LL << 35)
 
 /*
  * Per-tensor scale record, 4128 bytes of device memory owned by the caller

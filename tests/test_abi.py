@@ -216,3 +216,55 @@ def test_binding_refuses_a_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(F, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         F.lib()
+
+
+def test_size_limits():
+    """Sizes beyond FP8SG_MAX_DIM / FP8SG_MAX_ELEMS are refused before any
+    launch, products included (no int64 overflow on the way)."""
+    text = open(HEADER).read()
+    assert int(re.search(r"#define FP8SG_MAX_DIM \(1LL << (\d+)\)", text).group(1)) == 29 == \
+        F.MAX_DIM.bit_length() - 1
+    assert int(re.search(r"#define FP8SG_MAX_ELEMS \(1LL << (\d+)\)", text).group(1)) == 35 == \
+        F.MAX_ELEMS.bit_length() - 1
+    L = F.lib()
+    D, E = F.MAX_DIM, F.MAX_ELEMS
+    g = lambda M, N, K: L.fp8_gemm(P(A16), 0, P(A16B), 0, P(A16), P(A16), P(A16B), 0, M, N, K, P(0))
+    assert g(D + 16, 16, 16) == ESHAPE and g(16, 16, D + 16) == ESHAPE
+    assert g(1 << 20, 1 << 20, 16) == ESHAPE      # C has 2^40 elements
+    assert g(1 << 62, 1 << 62, 1 << 62) == ESHAPE  # products that overflow int64
+    assert L.fp8_amax(P(A16), E + 1, P(A16), P(0)) == ESHAPE
+    assert L.fp8_quantize(P(A16), 1 << 20, 1 << 16, 0, P(A16), P(A16), P(0), P(0)) == ESHAPE
+    assert L.fp8_quantize(P(A16), 1 << 62, 4, 0, P(A16), P(A16), P(0), P(0)) == ESHAPE
+    rw = lambda r, c: L.fp8_quantize_rowwise(P(A16), r, c, 0, P(A16), P(A16), P(A16), P(0), P(0),
+                                             P(0), P(0))
+    assert rw(16, D + 16) == ESHAPE and rw(1 << 20, 1 << 20) == ESHAPE
+    s = F._Saved(A16, A16, A16, A16, A16, A16)
+    fwd = lambda M, N, K: L.fp8_scaled_linear_fwd(P(A16), P(A16), M, N, K, ctypes.byref(s), P(A16),
+                                                  0, P(0))
+    assert fwd(16, 16, D + 16) == ESHAPE and fwd(1 << 20, 1 << 20, 16) == ESHAPE
+    ptrs = (ctypes.c_void_p * 1)(A16)
+    numel = (ctypes.c_int64 * 1)(E + 1)
+    assert L.amp_unscale_check(ptrs, numel, 1, P(A16), P(A16), P(0)) == ESHAPE
+    assert L.amp_norm_workspace_len(numel, 1) == -1
+
+
+def test_record_and_scalar_alignment():
+    """Scale records and fp64 inverses need 8 bytes, fp32/int32 scalars 4."""
+    L = F.lib()
+    assert L.fp8_amax(P(A16), 16, P(A16 + 4), P(0)) == EALIGN
+    assert L.fp8_quantize(P(A16), 4, 4, 0, P(A16 + 4), P(A16), P(0), P(0)) == EALIGN
+    assert L.fp8_gemm(P(A16), 0, P(A16B), 0, P(A16 + 4), P(A16), P(A16B), 0, 16, 16, 16,
+                      P(0)) == EALIGN
+    s = F._Saved(A16, A16, A16, A16, A16 + 4, A16)
+    assert L.fp8_scaled_linear_fwd(P(A16), P(A16), 16, 16, 16, ctypes.byref(s), P(A16), 0,
+                                   P(0)) == EALIGN
+    s = F._Saved(A16, A16, A16, A16, A16, A16)
+    ws = F._BwdWs(A16, A16, A16 + 4)
+    assert L.fp8_scaled_linear_bwd(P(A16), ctypes.byref(s), 16, 16, 16, ctypes.byref(ws), P(A16),
+                                   P(A16), 0, P(0)) == EALIGN
+    ptrs = (ctypes.c_void_p * 1)(A16)
+    numel = (ctypes.c_int64 * 1)(8)
+    assert L.amp_unscale_check(ptrs, numel, 1, P(A16 + 2), P(A16), P(0)) == EALIGN
+    assert L.amp_unscale_check(ptrs, numel, 1, P(A16), P(A16 + 1), P(0)) == EALIGN
+    for a in ((A16 + 2, A16, A16), (A16, A16 + 2, A16), (A16, A16, A16 + 1)):
+        assert L.amp_update_scale(P(a[0]), P(a[1]), P(a[2]), 2.0, 0.5, 10, P(0)) == EALIGN
