@@ -215,6 +215,21 @@ __device__ __forceinline__ float hist_amax(const float* hist, int32_t h) {
 }
 
 // Transposed stores of 128 x 128 code tiles (quantize.hip, rowwise.hip).
+// Tile t of a tiles_r x tiles_c grid, walked in groups of 8 row tiles: down
+// the 8 rows of a group first, then across its columns.  64 consecutive tiles
+// cover 8 x 8, so the transposed copies' stores of neighbouring blocks land in
+// adjacent 128-byte pieces of the same rows (a single row band would spread
+// them over 128 rows at one power-of-two stride).
+__host__ __device__ inline void tile_grouped(int64_t t, int64_t tiles_r, int64_t tiles_c,
+                                             int64_t& rt, int64_t& ct) {
+  constexpr int64_t G = 8;
+  const int64_t per = G * tiles_c, g = t / per, first = g * G;
+  const int64_t gs = tiles_r - first < G ? tiles_r - first : G;
+  const int64_t w = t - g * per;
+  rt = first + w % gs;
+  ct = w / gs;
+}
+
 // LDS tile: 128 rows x 32 dwords; dword column x of row r lives at x ^ swz(r).
 __device__ __forceinline__ int swz(int r) { return ((r >> 4) & 3) << 3; }
 

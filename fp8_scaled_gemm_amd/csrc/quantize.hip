@@ -9,13 +9,16 @@
 // no launch of its own; the first block of each job also writes the record's
 // amax and scale fields.
 //
-// Tiled path: one 128 x 128 tile per 256-thread block.  The tile is read once
-// with 16-byte loads (8 in flight per thread), quantized in registers, stored
+// Tiled path: one 128 x 128 tile per 256-thread block (blocks stride over the
+// tiles when there are more tiles than blocks).  The tile is read once with
+// 16-byte loads (8 in flight per thread), quantized in registers, stored
 // row-major with coalesced 8-byte stores, staged in LDS (16 KB, XOR-swizzled
 // so both the row-wise writes and the column-wise reads spread over the
 // banks), transposed in 4x4-byte blocks with byte permutes, and stored to qT
-// with 16-byte stores, 8 lanes per 128-byte row segment.  HBM traffic is the
-// algorithmic 2 B read + 1 B + 1 B written per element.
+// with 16-byte stores, 8 lanes per 128-byte row segment.  Tiles are walked in
+// groups of 8 row tiles (tile_grouped), so the transposed stores of blocks in
+// flight together form runs longer than one tile's 128 bytes.  HBM traffic is
+// the algorithmic 2 B read + 1 B + 1 B written per element.
 //
 // Delayed scaling [PT-CH20 §20.5.9: each FP8 op keeps an amax history of its
 // input; the scale comes from the amax of earlier steps]: with a history the
@@ -112,13 +115,15 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
   if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
 
   const int64_t rows = job.rows, cols = job.cols;
-  const int64_t ntiles = (int64_t)((rows + kQTile - 1) / kQTile) * job.tiles_c;
+  const int64_t tiles_r = (rows + kQTile - 1) / kQTile;
+  const int64_t ntiles = tiles_r * job.tiles_c;
   __shared__ uint32_t lds[kQTile * 32];
   uint32_t am = 0;  // DELAYED: packed |x| max of everything this block loaded
 
   for (int64_t tile = lb; tile < ntiles; tile += job.nblocks) {
-    const int64_t r_tile = (tile / job.tiles_c) * kQTile;
-    const int64_t c_tile = (tile % job.tiles_c) * kQTile;
+    int64_t rt, ct;
+    tile_grouped(tile, tiles_r, job.tiles_c, rt, ct);
+    const int64_t r_tile = rt * kQTile, c_tile = ct * kQTile;
 
     // phase 1: 16 lanes per row (8 elements each), 16 rows per pass, 8 passes
     const int c8 = tid & 15;

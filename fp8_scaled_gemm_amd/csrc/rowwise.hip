@@ -48,21 +48,6 @@ __device__ __forceinline__ RwParts rw_parts(const RowwiseArgs& a) {
 }
 __host__ __device__ inline int64_t rw_tiles(int64_t n) { return (n + kRwTile - 1) / kRwTile; }
 
-// Block b -> tile (rt, ct): groups of 8 row tiles, walked down the rows first,
-// so 64 consecutive blocks cover 8 x 8 tiles and both the row-major and the
-// transposed stores of blocks in flight together form 1 KiB runs (a single
-// row band would put all transposed stores of the moment at one power-of-two
-// stride).
-__device__ __forceinline__ void rw_tile_of(int64_t b, int64_t tiles_r, int64_t tiles_c,
-                                           int64_t& rt, int64_t& ct) {
-  constexpr int64_t G = 8;
-  const int64_t per = G * tiles_c, g = b / per, first = g * G;
-  const int64_t gs = tiles_r - first < G ? tiles_r - first : G;
-  const int64_t w = b - g * per;
-  rt = first + w % gs;
-  ct = w / gs;
-}
-
 // packed bf16 pair maximum (16-bit unsigned) -> the two fp32 bit patterns, NaN canonical
 __device__ __forceinline__ void unpack_max(uint32_t d, uint32_t& lo, uint32_t& hi) {
   lo = (d & 0xFFFFu) << 16;
@@ -76,7 +61,7 @@ __global__ __launch_bounds__(kRwThreads) void k_rw_amax(RowwiseArgs a) {
   const int tid = threadIdx.x;
   const int64_t rows = a.rows, cols = a.cols;
   int64_t rt, ct;
-  rw_tile_of(blockIdx.x, rw_tiles(a.rows), a.tiles_c, rt, ct);
+  tile_grouped(blockIdx.x, rw_tiles(a.rows), a.tiles_c, rt, ct);
   const int64_t r_tile = rt * kRwTile, c_tile = ct * kRwTile;
   const RwParts pp = rw_parts(a);
   const int c8 = tid & 15, r0 = tid >> 4;
@@ -214,7 +199,7 @@ __global__ __launch_bounds__(kRwThreads) void k_rw_quant(RowwiseArgs a) {
   const int tid = threadIdx.x;
   const int64_t rows = a.rows, cols = a.cols;
   int64_t rt, ct;
-  rw_tile_of(blockIdx.x, rw_tiles(a.rows), a.tiles_c, rt, ct);
+  tile_grouped(blockIdx.x, rw_tiles(a.rows), a.tiles_c, rt, ct);
   const int64_t r_tile = rt * kRwTile, c_tile = ct * kRwTile;
   __shared__ float srow[kRwTile], scol[kRwTile];
   __shared__ uint32_t lds[kRwTile * 32];
