@@ -112,12 +112,56 @@ def _check(status: int, what: str):
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    """Device address of a tensor (NULL for None); host tensors are refused."""
+    if t is None:
+        return ctypes.c_void_p(0)
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must be device tensors")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+_OUT_DTYPE = {OUT_BF16: torch.bfloat16, OUT_F16: torch.float16, OUT_F32: torch.float32}
+
+
+def _need(t, name, dtype, shape=None, numel=None, min_numel=None):
+    """Refuses a tensor the library would read or write out of bounds.  The C
+    ABI sees pointers and sizes only, so dtype, shape and contiguity are
+    checked here, before any call (TypeError / ValueError); _ptr checks the
+    device when the arguments are marshalled."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected at least {min_numel}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _need_rec(rec, name):
+    if not isinstance(rec, ScaleRec):
+        raise TypeError(f"{name}: expected a ScaleRec")
+    _need(rec.buf, name, torch.uint8, min_numel=SCALE_REC_BYTES)
+
+
+def _need_2d(t, name):
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{name}: expected a 2-D tensor")
+    return t.shape
+
+
+def _need_scaler(scale, found_inf):
+    _need(scale, "scale", torch.float32, min_numel=1)
+    _need(found_inf, "found_inf", torch.int32, min_numel=1)
 
 
 # ----------------------------------------------------------------- scale records
@@ -154,25 +198,33 @@ class ScaleRec:
 
 def fp8_amax(x: torch.Tensor, rec: ScaleRec, stream=None):
     """rec.amax = max |x| over a bf16 tensor (any shape, contiguous)."""
-    assert x.dtype == torch.bfloat16 and x.is_contiguous()
-    _check(lib().fp8_amax(_ptr(x), x.numel(), ctypes.c_void_p(rec.ptr), _stream(stream)),
+    _need(x, "x", torch.bfloat16)
+    _need_rec(rec, "rec")
+    _check(lib().fp8_amax(_ptr(x), x.numel(), _ptr(rec.buf), _stream(stream)),
            "fp8_amax")
 
 
 def fp8_quantize(x: torch.Tensor, fmt: int, rec: ScaleRec, q: torch.Tensor,
                  qT: torch.Tensor = None, stream=None):
     """Scale from rec.amax, then codes q (= x's shape) and optionally qT (transposed)."""
-    assert x.dtype == torch.bfloat16 and x.is_contiguous()
-    rows, cols = (x.shape[0], x.numel() // max(x.shape[0], 1)) if x.dim() >= 2 else (1, x.numel())
-    assert q.dtype == torch.uint8 and q.numel() == x.numel()
-    if qT is not None:
-        assert qT.dtype == torch.uint8 and qT.numel() == x.numel()
-    _check(lib().fp8_quantize(_ptr(x), rows, cols, fmt, ctypes.c_void_p(rec.ptr), _ptr(q),
+    rows, cols = _quant_args(x, rec, q, qT)
+    _check(lib().fp8_quantize(_ptr(x), rows, cols, fmt, _ptr(rec.buf), _ptr(q),
                               _ptr(qT), _stream(stream)), "fp8_quantize")
 
 
-def _hist(h: torch.Tensor):
-    assert h.dtype == torch.float32 and h.is_contiguous() and 1 <= h.numel() <= MAX_HISTORY
+def _quant_args(x, rec, q, qT):
+    _need(x, "x", torch.bfloat16)
+    _need_rec(rec, "rec")
+    _need(q, "q", torch.uint8, numel=x.numel())
+    if qT is not None:
+        _need(qT, "qT", torch.uint8, numel=x.numel())
+    return (x.shape[0], x.numel() // max(x.shape[0], 1)) if x.dim() >= 2 else (1, x.numel())
+
+
+def _hist(h: torch.Tensor, name="hist"):
+    _need(h, name, torch.float32)
+    if not 1 <= h.numel() <= MAX_HISTORY:
+        raise ValueError(f"{name}: history length {h.numel()} outside 1..{MAX_HISTORY}")
     return h.numel()
 
 
@@ -181,23 +233,26 @@ def fp8_quantize_delayed(x: torch.Tensor, fmt: int, rec: ScaleRec, hist: torch.T
     """Delayed scaling: scale from the largest entry of the amax history hist
     (device float32, most recent first), codes q (and qT), then rec.amax =
     max |x| pushed to the front of hist."""
-    assert x.dtype == torch.bfloat16 and x.is_contiguous()
-    rows, cols = (x.shape[0], x.numel() // max(x.shape[0], 1)) if x.dim() >= 2 else (1, x.numel())
-    assert q.dtype == torch.uint8 and q.numel() == x.numel()
-    if qT is not None:
-        assert qT.dtype == torch.uint8 and qT.numel() == x.numel()
+    rows, cols = _quant_args(x, rec, q, qT)
     h = _hist(hist)
     _check(lib().fp8_quantize_delayed(_ptr(x), rows, cols, fmt, _ptr(hist), h,
-                                      ctypes.c_void_p(rec.ptr), _ptr(q), _ptr(qT),
+                                      _ptr(rec.buf), _ptr(q), _ptr(qT),
                                       _stream(stream)), "fp8_quantize_delayed")
+
+
+def _gemm_args(A, B, C, c_dtype):
+    M, K = _need_2d(A, "A")
+    N, K2 = _need_2d(B, "B")
+    _need(A, "A", torch.uint8)
+    _need(B, "B", torch.uint8, shape=(N, K))
+    _need(C, "C", c_dtype, shape=(M, N))
+    return M, N, K
 
 
 def fp8_gemm(A: torch.Tensor, fa: int, B: torch.Tensor, fb: int, inv_a_ptr: int, inv_b_ptr: int,
              C: torch.Tensor, out: int, stream=None):
     """C[M,N] = A[M,K] . B[N,K]^T * fl32(inv_a * inv_b); inv_*_ptr are device double addresses."""
-    M, K = A.shape
-    N, K2 = B.shape
-    assert K == K2 and tuple(C.shape) == (M, N)
+    M, N, K = _gemm_args(A, B, C, _OUT_DTYPE.get(out))
     _check(lib().fp8_gemm(_ptr(A), fa, _ptr(B), fb, ctypes.c_void_p(inv_a_ptr),
                           ctypes.c_void_p(inv_b_ptr), _ptr(C), out, M, N, K, _stream(stream)),
            "fp8_gemm")
@@ -207,9 +262,8 @@ def fp8_gemm_unscale(A: torch.Tensor, fa: int, B: torch.Tensor, fb: int, inv_a_p
                      inv_b_ptr: int, scale: torch.Tensor, found_inf: torch.Tensor, C: torch.Tensor,
                      stream=None):
     """fp8_gemm into fp16 C with the GradScaler unscale and check in the epilogue."""
-    M, K = A.shape
-    N, K2 = B.shape
-    assert K == K2 and tuple(C.shape) == (M, N) and C.dtype == torch.float16
+    M, N, K = _gemm_args(A, B, C, torch.float16)
+    _need_scaler(scale, found_inf)
     _check(lib().fp8_gemm_unscale(_ptr(A), fa, _ptr(B), fb, ctypes.c_void_p(inv_a_ptr),
                                   ctypes.c_void_p(inv_b_ptr), _ptr(scale), _ptr(found_inf), _ptr(C),
                                   M, N, K, _stream(stream)), "fp8_gemm_unscale")
@@ -234,9 +288,17 @@ class LinearSaved:
     def tensors(self):
         return (self.x_q, self.x_qT, self.w_q, self.w_qT, self.recs)
 
+    def check(self, M, N, K):
+        """The buffers must fit a layer of these sizes."""
+        for t, name, shape in ((self.x_q, "saved.x_q", (M, K)), (self.x_qT, "saved.x_qT", (K, M)),
+                               (self.w_q, "saved.w_q", (N, K)), (self.w_qT, "saved.w_qT", (K, N))):
+            _need(t, name, torch.uint8, shape=shape)
+        _need_rec(self.x_sc, "saved.x_sc")
+        _need_rec(self.w_sc, "saved.w_sc")
+
     def struct(self):
-        return _Saved(self.x_q.data_ptr(), self.x_qT.data_ptr(), self.w_q.data_ptr(),
-                      self.w_qT.data_ptr(), self.x_sc.ptr, self.w_sc.ptr)
+        return _Saved(*[_ptr(t).value for t in (self.x_q, self.x_qT, self.w_q, self.w_qT,
+                                                  self.x_sc.buf, self.w_sc.buf)])
 
 
 class LinearBwdWs:
@@ -246,13 +308,37 @@ class LinearBwdWs:
         self.gy_qT = torch.empty((N, M), **u8)
         self.gy_sc = ScaleRec(device=device)
 
+    def check(self, M, N):
+        _need(self.gy_q, "ws.gy_q", torch.uint8, shape=(M, N))
+        _need(self.gy_qT, "ws.gy_qT", torch.uint8, shape=(N, M))
+        _need_rec(self.gy_sc, "ws.gy_sc")
+
     def struct(self):
-        return _BwdWs(self.gy_q.data_ptr(), self.gy_qT.data_ptr(), self.gy_sc.ptr)
+        return _BwdWs(*[_ptr(t).value for t in (self.gy_q, self.gy_qT, self.gy_sc.buf)])
+
+
+def _fwd_args(x, w, y, out):
+    M, K = _need_2d(x, "x")
+    N, _ = _need_2d(w, "w")
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.bfloat16, shape=(N, K))
+    _need(y, "y", _OUT_DTYPE.get(out), shape=(M, N))
+    return M, N, K
+
+
+def _bwd_args(gy, saved, gx, gw, out):
+    M, N = _need_2d(gy, "gy")
+    _need(gy, "gy", torch.bfloat16)
+    K = _need_2d(saved.x_q, "saved.x_q")[1]
+    dt = _OUT_DTYPE.get(out)
+    _need(gx, "gx", dt, shape=(M, K))
+    _need(gw, "gw", dt, shape=(N, K))
+    return M, N, K
 
 
 def fp8_scaled_linear_fwd(x, w, saved: LinearSaved, y, out: int = OUT_BF16, stream=None):
-    M, K = x.shape
-    N = w.shape[0]
+    M, N, K = _fwd_args(x, w, y, out)
+    saved.check(M, N, K)
     s = saved.struct()
     _check(lib().fp8_scaled_linear_fwd(_ptr(x), _ptr(w), M, N, K, ctypes.byref(s), _ptr(y), out,
                                        _stream(stream)), "fp8_scaled_linear_fwd")
@@ -260,8 +346,9 @@ def fp8_scaled_linear_fwd(x, w, saved: LinearSaved, y, out: int = OUT_BF16, stre
 
 def fp8_scaled_linear_bwd(gy, saved: LinearSaved, ws: LinearBwdWs, gx, gw, out: int = OUT_BF16,
                           stream=None):
-    M, N = gy.shape
-    K = saved.x_q.shape[1]
+    M, N, K = _bwd_args(gy, saved, gx, gw, out)
+    saved.check(M, N, K)
+    ws.check(M, N)
     s = saved.struct()
     b = ws.struct()
     _check(lib().fp8_scaled_linear_bwd(_ptr(gy), ctypes.byref(s), M, N, K, ctypes.byref(b),
@@ -273,8 +360,10 @@ def fp8_scaled_linear_bwd_unscale(gy, saved: LinearSaved, ws: LinearBwdWs, scale
                                   gx, gw, stream=None):
     """fp8_scaled_linear_bwd into fp16 gx, gw with the GradScaler unscale and
     non-finite check fused into the GEMM epilogues."""
-    M, N = gy.shape
-    K = saved.x_q.shape[1]
+    M, N, K = _bwd_args(gy, saved, gx, gw, OUT_F16)
+    _need_scaler(scale, found_inf)
+    saved.check(M, N, K)
+    ws.check(M, N)
     s = saved.struct()
     b = ws.struct()
     _check(lib().fp8_scaled_linear_bwd_unscale(_ptr(gy), ctypes.byref(s), M, N, K, ctypes.byref(b),
@@ -284,10 +373,11 @@ def fp8_scaled_linear_bwd_unscale(gy, saved: LinearSaved, ws: LinearBwdWs, scale
 
 def fp8_scaled_linear_fwd_delayed(x, w, saved: LinearSaved, hist_x, hist_w, y,
                                   out: int = OUT_BF16, stream=None):
-    M, K = x.shape
-    N = w.shape[0]
-    h = _hist(hist_x)
-    assert _hist(hist_w) == h
+    M, N, K = _fwd_args(x, w, y, out)
+    h = _hist(hist_x, "hist_x")
+    if _hist(hist_w, "hist_w") != h:
+        raise ValueError("hist_x and hist_w must have the same length")
+    saved.check(M, N, K)
     s = saved.struct()
     _check(lib().fp8_scaled_linear_fwd_delayed(_ptr(x), _ptr(w), M, N, K, ctypes.byref(s),
                                                _ptr(hist_x), _ptr(hist_w), h, _ptr(y), out,
@@ -296,12 +386,14 @@ def fp8_scaled_linear_fwd_delayed(x, w, saved: LinearSaved, hist_x, hist_w, y,
 
 def fp8_scaled_linear_bwd_delayed(gy, saved: LinearSaved, ws: LinearBwdWs, hist_gy, gx, gw,
                                   out: int = OUT_BF16, stream=None):
-    M, N = gy.shape
-    K = saved.x_q.shape[1]
+    M, N, K = _bwd_args(gy, saved, gx, gw, out)
+    saved.check(M, N, K)
+    ws.check(M, N)
     s = saved.struct()
     b = ws.struct()
     _check(lib().fp8_scaled_linear_bwd_delayed(_ptr(gy), ctypes.byref(s), M, N, K, ctypes.byref(b),
-                                               _ptr(hist_gy), _hist(hist_gy), _ptr(gx), _ptr(gw),
+                                               _ptr(hist_gy), _hist(hist_gy, "hist_gy"), _ptr(gx),
+                                               _ptr(gw),
                                                out, _stream(stream)),
            "fp8_scaled_linear_bwd_delayed")
 
@@ -316,12 +408,25 @@ class RowScalesDev:
         self.inv = inv if inv is not None else torch.empty(n, dtype=torch.float64, device=device)
 
 
+def _need_vec(sc, name, n):
+    if not isinstance(sc, RowScalesDev):
+        raise TypeError(f"{name}: expected a RowScalesDev")
+    _need(sc.amax, name + ".amax", torch.float32, numel=n)
+    _need(sc.inv, name + ".inv", torch.float64, numel=n)
+
+
 def fp8_quantize_rowwise(x: torch.Tensor, fmt: int, rows_sc: RowScalesDev, q: torch.Tensor,
                          cols_sc: RowScalesDev = None, qT: torch.Tensor = None, stream=None):
     """Row-wise cast of a [rows, cols] bf16 matrix: q with one scale per row
     (rows_sc), and with qT the transposed copy with one scale per column
     (cols_sc)."""
-    rows, cols = x.shape
+    rows, cols = _need_2d(x, "x")
+    _need(x, "x", torch.bfloat16)
+    _need(q, "q", torch.uint8, shape=(rows, cols))
+    _need_vec(rows_sc, "rows_sc", rows)
+    if cols_sc is not None or qT is not None:
+        _need_vec(cols_sc, "cols_sc", cols)
+        _need(qT, "qT", torch.uint8, shape=(cols, rows))
     ca = cols_sc.amax if cols_sc is not None else None
     ci = cols_sc.inv if cols_sc is not None else None
     _check(lib().fp8_quantize_rowwise(_ptr(x), rows, cols, fmt, _ptr(rows_sc.amax),
@@ -332,9 +437,9 @@ def fp8_quantize_rowwise(x: torch.Tensor, fmt: int, rows_sc: RowScalesDev, q: to
 def fp8_gemm_rowwise(A: torch.Tensor, fa: int, B: torch.Tensor, fb: int, inv_a: torch.Tensor,
                      inv_b: torch.Tensor, C: torch.Tensor, out: int, stream=None):
     """C[M,N] = A[M,K] . B[N,K]^T * fl32(inv_a[m] * inv_b[n]) (float64 vectors)."""
-    M, K = A.shape
-    N, K2 = B.shape
-    assert K == K2 and tuple(C.shape) == (M, N)
+    M, N, K = _gemm_args(A, B, C, _OUT_DTYPE.get(out))
+    _need(inv_a, "inv_a", torch.float64, numel=M)
+    _need(inv_b, "inv_b", torch.float64, numel=N)
     _check(lib().fp8_gemm_rowwise(_ptr(A), fa, _ptr(B), fb, _ptr(inv_a), _ptr(inv_b), _ptr(C),
                                   out, M, N, K, _stream(stream)), "fp8_gemm_rowwise")
 
@@ -363,8 +468,15 @@ class LinearSavedRW:
     def tensors(self):
         return tuple(getattr(self, n) for n in self.NAMES)
 
+    def check(self, M, N, K):
+        shapes = ((M, K), (K, M), (N, K), (K, N), (M,), (M,), (K,), (K,), (N,), (N,), (K,), (K,))
+        for n, shape in zip(self.NAMES, shapes):
+            dt = torch.uint8 if len(shape) == 2 else (
+                torch.float32 if n.endswith("amax") else torch.float64)
+            _need(getattr(self, n), "saved." + n, dt, shape=shape)
+
     def struct(self):
-        return _SavedRW(*[getattr(self, n).data_ptr() for n in self.NAMES])
+        return _SavedRW(*[_ptr(getattr(self, n)).value for n in self.NAMES])
 
 
 class LinearBwdWsRW:
@@ -379,14 +491,20 @@ class LinearBwdWsRW:
         self.gy_col_amax = torch.empty(N, dtype=torch.float32, device=device)
         self.gy_col_inv = torch.empty(N, dtype=torch.float64, device=device)
 
+    def check(self, M, N):
+        shapes = ((M, N), (N, M), (M,), (M,), (N,), (N,))
+        dts = (torch.uint8, torch.uint8, torch.float32, torch.float64, torch.float32, torch.float64)
+        for n, shape, dt in zip(self.NAMES, shapes, dts):
+            _need(getattr(self, n), "ws." + n, dt, shape=shape)
+
     def struct(self):
-        return _BwdWsRW(*[getattr(self, n).data_ptr() for n in self.NAMES])
+        return _BwdWsRW(*[_ptr(getattr(self, n)).value for n in self.NAMES])
 
 
 def fp8_scaled_linear_fwd_rowwise(x, w, saved: LinearSavedRW, y, out: int = OUT_BF16,
                                   stream=None):
-    M, K = x.shape
-    N = w.shape[0]
+    M, N, K = _fwd_args(x, w, y, out)
+    saved.check(M, N, K)
     s = saved.struct()
     _check(lib().fp8_scaled_linear_fwd_rowwise(_ptr(x), _ptr(w), M, N, K, ctypes.byref(s),
                                                _ptr(y), out, _stream(stream)),
@@ -395,8 +513,9 @@ def fp8_scaled_linear_fwd_rowwise(x, w, saved: LinearSavedRW, y, out: int = OUT_
 
 def fp8_scaled_linear_bwd_rowwise(gy, saved: LinearSavedRW, ws: LinearBwdWsRW, gx, gw,
                                   out: int = OUT_BF16, stream=None):
-    M, N = gy.shape
-    K = saved.x_q.shape[1]
+    M, N, K = _bwd_args(gy, saved, gx, gw, out)
+    saved.check(M, N, K)
+    ws.check(M, N)
     s = saved.struct()
     b = ws.struct()
     _check(lib().fp8_scaled_linear_bwd_rowwise(_ptr(gy), ctypes.byref(s), M, N, K,
@@ -404,13 +523,20 @@ def fp8_scaled_linear_bwd_rowwise(gy, saved: LinearSavedRW, ws: LinearBwdWsRW, g
                                                _stream(stream)), "fp8_scaled_linear_bwd_rowwise")
 
 
+def _grad_list(grads):
+    grads = list(grads)
+    for i, g in enumerate(grads):
+        _need(g, f"grads[{i}]", torch.float16)
+    n = len(grads)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(g).value for g in grads])
+    numel = (ctypes.c_int64 * max(n, 1))(*[g.numel() for g in grads])
+    return ptrs, numel, n
+
+
 def amp_unscale_check(grads, scale: torch.Tensor, found_inf: torch.Tensor, stream=None):
     """In-place unscale of a list of fp16 gradients and OR of the non-finite flag."""
-    n = len(grads)
-    ptrs = (ctypes.c_void_p * max(n, 1))(*[g.data_ptr() for g in grads])
-    numel = (ctypes.c_int64 * max(n, 1))(*[g.numel() for g in grads])
-    for g in grads:
-        assert g.dtype == torch.float16 and g.is_contiguous()
+    ptrs, numel, n = _grad_list(grads)
+    _need_scaler(scale, found_inf)
     _check(lib().amp_unscale_check(ptrs, numel, n, _ptr(scale), _ptr(found_inf),
                                    _stream(stream)), "amp_unscale_check")
 
@@ -430,13 +556,10 @@ def amp_unscale_check_norm(grads, scale: torch.Tensor, found_inf: torch.Tensor,
     """amp_unscale_check plus (sum of squares, 2-norm) of the unscaled gradients
     into sumsq_norm (device float32[2]); workspace: device float32 scratch of at
     least amp_norm_workspace_len([g.numel() for g in grads]) elements."""
-    n = len(grads)
-    ptrs = (ctypes.c_void_p * max(n, 1))(*[g.data_ptr() for g in grads])
-    numel = (ctypes.c_int64 * max(n, 1))(*[g.numel() for g in grads])
-    for g in grads:
-        assert g.dtype == torch.float16 and g.is_contiguous()
-    assert workspace.dtype == torch.float32 and sumsq_norm.dtype == torch.float32
-    assert sumsq_norm.numel() >= 2
+    ptrs, numel, n = _grad_list(grads)
+    _need_scaler(scale, found_inf)
+    _need(workspace, "workspace", torch.float32)
+    _need(sumsq_norm, "sumsq_norm", torch.float32, min_numel=2)
     _check(lib().amp_unscale_check_norm(ptrs, numel, n, _ptr(scale), _ptr(found_inf),
                                         _ptr(workspace), workspace.numel(), _ptr(sumsq_norm),
                                         _stream(stream)), "amp_unscale_check_norm")
@@ -444,6 +567,8 @@ def amp_unscale_check_norm(grads, scale: torch.Tensor, found_inf: torch.Tensor,
 
 def amp_update_scale(scale: torch.Tensor, growth_tracker: torch.Tensor, found_inf: torch.Tensor,
                      growth_factor=2.0, backoff_factor=0.5, growth_interval=2000, stream=None):
+    _need_scaler(scale, found_inf)
+    _need(growth_tracker, "growth_tracker", torch.int32, min_numel=1)
     _check(lib().amp_update_scale(_ptr(scale), _ptr(growth_tracker), _ptr(found_inf),
                                   growth_factor, backoff_factor, growth_interval, _stream(stream)),
            "amp_update_scale")

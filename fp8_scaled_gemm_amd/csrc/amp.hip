@@ -3,15 +3,16 @@
 // found; §20.5.33: the update() state machine; AMP-NOTES §4 steps 3-6].
 //
 // Unscale + check is one multi-tensor pass: the tensor list travels in the
-// kernel arguments (up to kAmpTensorsPerLaunch tensors per launch, no device
-// table to allocate or copy), every block owns 8192 consecutive elements of one
-// tensor and finds its tensor by binary search over the per-tensor block
-// offsets.  A tensor may start anywhere 2-byte aligned (views into a flat
-// gradient bucket): the kernel walks the enclosing 16-byte-aligned span with
-// 16-byte vectors and handles the partial first and last vectors element by
-// element, never writing outside the tensor.  Each element is read and written once in place (2 + 2 bytes); the
-// non-finite test runs on the stored fp16 result, (bits & 0x7FFF) >= 0x7C00,
-// so it costs no extra traffic.  A wave that saw one sets the flag with a
+// kernel arguments (up to kAmpTensorsPerLaunch tensors and 2^23 blocks per
+// launch, no device table to allocate or copy), every block owns 8192
+// consecutive elements of one tensor and finds its tensor by binary search over
+// the per-tensor block offsets.  A tensor may start anywhere 2-byte aligned
+// (views into a flat gradient bucket): the kernel walks the enclosing
+// 16-byte-aligned span with 16-byte vectors and handles the partial first and
+// last vectors element by element, never writing outside the tensor.  Each
+// element is read and written once in place (2 + 2 bytes); the non-finite test
+// runs on the stored fp16 result, (bits & 0x7FFF) >= 0x7C00, so it costs no
+// extra traffic.  A wave that saw one sets the flag with a
 // plain store of 1 (all writers store the same value).  The scale update is a
 // single-lane kernel that keeps scale, tracker and flag on the device, so the
 // step never synchronises the host.

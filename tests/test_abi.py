@@ -268,3 +268,48 @@ def test_record_and_scalar_alignment():
     assert L.amp_unscale_check(ptrs, numel, 1, P(A16), P(A16 + 1), P(0)) == EALIGN
     for a in ((A16 + 2, A16, A16), (A16, A16 + 2, A16), (A16, A16, A16 + 1)):
         assert L.amp_update_scale(P(a[0]), P(a[1]), P(a[2]), 2.0, 0.5, 10, P(0)) == EALIGN
+
+
+def test_binding_refuses_mismatched_buffers():
+    """The library sees pointers only, so the binding checks dtype, shape,
+    contiguity and device before any call (here on CPU tensors, which never
+    reach the library)."""
+    import torch
+    u8, bf = torch.uint8, torch.bfloat16
+    A = torch.zeros(32, 64, dtype=u8)
+    B = torch.zeros(16, 64, dtype=u8)
+    with pytest.raises(ValueError, match="shape"):
+        F.fp8_gemm(A, 0, torch.zeros(16, 48, dtype=u8), 0, 0, 0, torch.zeros(32, 16, dtype=bf),
+                   F.OUT_BF16)
+    with pytest.raises(ValueError, match="shape"):
+        F.fp8_gemm(A, 0, B, 0, 0, 0, torch.zeros(16, 32, dtype=bf), F.OUT_BF16)
+    with pytest.raises(TypeError, match="dtype"):
+        F.fp8_gemm(A, 0, B, 0, 0, 0, torch.zeros(32, 16, dtype=torch.float16), F.OUT_BF16)
+    with pytest.raises(ValueError, match="contiguous"):
+        F.fp8_gemm(A, 0, B, 0, 0, 0, torch.zeros(16, 32, dtype=bf).t(), F.OUT_BF16)
+    with pytest.raises(ValueError, match="device"):
+        F.fp8_gemm(A, 0, B, 0, 0, 0, torch.zeros(32, 16, dtype=bf), F.OUT_BF16)
+    M, N, K = 32, 16, 64
+    x, w = torch.zeros(M, K, dtype=bf), torch.zeros(N, K, dtype=bf)
+    saved = F.LinearSaved(M, N, K, device="cpu")
+    with pytest.raises(ValueError, match="shape"):
+        F.fp8_scaled_linear_fwd(x, w, saved, torch.zeros(M, K, dtype=bf))
+    with pytest.raises(ValueError, match="saved.x_qT"):
+        F.fp8_scaled_linear_fwd(x, w, F.LinearSaved(M, N, K // 2, device="cpu",
+                                                    tensors=(saved.x_q, saved.x_q.t().contiguous()[:K // 2],
+                                                             saved.w_q, saved.w_qT, saved.recs)),
+                                torch.zeros(M, N, dtype=bf))
+    ws = F.LinearBwdWs(M, N + 16, device="cpu")
+    with pytest.raises(ValueError, match="ws.gy_q"):
+        F.fp8_scaled_linear_bwd(torch.zeros(M, N, dtype=bf), saved, ws, torch.zeros(M, K, dtype=bf),
+                                torch.zeros(N, K, dtype=bf))
+    with pytest.raises(TypeError, match="grads"):
+        F.amp_unscale_check([torch.zeros(8, dtype=torch.float32)], torch.ones(1),
+                            torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="history"):
+        F.fp8_quantize_delayed(x, 0, F.ScaleRec(device="cpu"), torch.zeros(0),
+                               torch.zeros(M, K, dtype=u8))
+    rs = F.RowScalesDev(M, device="cpu")
+    with pytest.raises(ValueError, match="cols_sc.amax"):
+        F.fp8_quantize_rowwise(x, 0, rs, torch.zeros(M, K, dtype=u8), F.RowScalesDev(K - 16, device="cpu"),
+                               torch.zeros(K, M, dtype=u8))
