@@ -140,6 +140,18 @@ __device__ __forceinline__ uint8_t quant1(uint16_t b, float s32) {
   return (uint8_t)(cvt4<FMT>(f, 0.f, 0.f, 0.f) & 0xFFu);
 }
 
+// Maximum over the 16 lanes of a DPP row (lanes 16k .. 16k + 15), in every lane
+// of the row: pairs (quad_perm 1,0,3,2), quads (2,3,0,1), half rows
+// (row_half_mirror), rows (row_mirror).  All 64 lanes must be active.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  auto mx = [](uint32_t a, int b) { return (uint32_t)b > a ? (uint32_t)b : a; };
+  v = mx(v, __builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = mx(v, __builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = mx(v, __builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = mx(v, __builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  return v;
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {

@@ -10,9 +10,9 @@
 //
 // Three kernels, two passes over x:
 //   k_rw_amax:   per 128 x 128 tile, the maximum |x| of each of its rows
-//                (16-lane shuffles) and of each of its columns (shuffles, then
-//                LDS across the four waves), stored as fp32 bits (NaN
-//                canonical) into partial-maximum arrays.  The arrays live in
+//                (DPP reductions over the row's 16 lanes) and of each of its
+//                columns (shuffles, then LDS across the four waves), stored
+//                as fp32 bits (NaN canonical) into partial-maximum arrays.  The arrays live in
 //                the caller's q buffer, which the cast overwrites afterwards:
 //                no workspace and no atomics.
 //   k_rw_reduce: one lane per row (column): the maximum over its partials
@@ -80,12 +80,8 @@ __global__ __launch_bounds__(kRwThreads) void k_rw_amax(RowwiseArgs a) {
   uint4 cm = make_uint4(0, 0, 0, 0);  // column maxima, two columns per dword
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    uint32_t b = absmax_bits(absmax8(0u, v[p]));  // this thread's 8 values of row r0 + 16p
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) {  // the 16 lanes of a row are consecutive
-      const uint32_t o = (uint32_t)__shfl_xor((int)b, off, kWave);
-      b = o > b ? o : b;
-    }
+    // this thread's 8 values of row r0 + 16p; the row's 16 lanes form one DPP row
+    const uint32_t b = row16_max(absmax_bits(absmax8(0u, v[p])));
     if (c8 == 0) srow[r0 + 16 * p] = b;
     if constexpr (WITH_T) {
       cm.x = pmax(cm.x, v[p].x & mask);
