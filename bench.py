@@ -480,8 +480,9 @@ def small_layer(torch, F, dev, stream, T, reps=200):
 def mlp_block(torch, F, dev, stream, steps=10, warmup=3):
     """The transformer MLP block's three FP8 linears (gate, up: 4096 -> 14336;
     down: 14336 -> 4096; 8192 tokens) trained through Float8Linear and autograd
-    (x shared by gate and up, as in the block), against the same nine GEMMs
-    driven directly through the C-ABI.  Synthetic device data at the
+    (x shared by gate and up, as in the block; each module casts its own input),
+    against the same nine GEMMs driven directly through the C-ABI, where x is
+    reduced and cast once for gate and up.  Synthetic device data at the
     workload's shapes and standard deviations."""
     import fp8_scaled_gemm_amd.nn as FN
     T, H, Fd = 8192, 4096, 14336
@@ -509,10 +510,23 @@ def mlp_block(torch, F, dev, stream, steps=10, warmup=3):
                          saved=F.LinearSaved(T, o, k, device=dev), ws=F.LinearBwdWs(T, o, device=dev),
                          y=torch.empty(T, o, **bf), gx=torch.empty(T, k, **bf),
                          gw=torch.empty(o, k, **bf))
+    # up shares gate's input: its saved x codes, transposed codes and scale
+    # record are gate's, so x is reduced and cast once per step
+    g_sv, u = direct["gate"]["saved"], direct["up"]
+    u["saved"] = F.LinearSaved(T, Fd, H, tensors=(g_sv.x_q, g_sv.x_qT, u["saved"].w_q,
+                                                  u["saved"].w_qT, u["saved"].recs))
+    u["saved"].x_sc = g_sv.x_sc
 
     def direct_step():
         for n, d in direct.items():
-            F.fp8_scaled_linear_fwd(d["inp"], d["w"], d["saved"], d["y"], F.OUT_BF16)
+            if n == "up":  # W_up alone: amax, cast (+ transposed copy), GEMM on gate's x codes
+                sv = d["saved"]
+                F.fp8_amax(d["w"], sv.w_sc)
+                F.fp8_quantize(d["w"], F.E4M3FN, sv.w_sc, sv.w_q, sv.w_qT)
+                F.fp8_gemm(sv.x_q, F.E4M3FN, sv.w_q, F.E4M3FN, sv.x_sc.inv_ptr(), sv.w_sc.inv_ptr(),
+                           d["y"], F.OUT_BF16)
+            else:
+                F.fp8_scaled_linear_fwd(d["inp"], d["w"], d["saved"], d["y"], F.OUT_BF16)
         for n, d in direct.items():
             F.fp8_scaled_linear_bwd(gys[n], d["saved"], d["ws"], d["gx"], d["gw"], F.OUT_BF16)
 

@@ -132,6 +132,41 @@ def test_mlp_block_three_linears():
         torch.cuda.empty_cache()
 
 
+def test_shared_input_linear_is_the_full_linear():
+    """The MLP block's up projection on gate's cast of x (bench.py's direct
+    path: W_up alone is reduced and cast, its GEMM reads gate's x codes, its
+    backward gate's transposed x codes and record) gives the same bits as a
+    full fp8_scaled_linear_fwd/bwd of (x, W_up)."""
+    M, K, N = 512, 1024, 768
+    x = dev16(W.normal_bf16(91, 0, (M, K), 1.0))
+    wg = dev16(W.normal_bf16(91, 1, (N, K), 0.02))
+    wu = dev16(W.normal_bf16(91, 2, (N, K), 0.02))
+    gy = dev16(W.normal_bf16(91, 3, (M, N), 1e-4))
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    outs = []
+    for shared in (False, True):
+        y, gx, gw = torch.empty(M, N, **bf), torch.empty(M, K, **bf), torch.empty(N, K, **bf)
+        ws = F.LinearBwdWs(M, N)
+        if shared:
+            sg = F.LinearSaved(M, N, K)
+            F.fp8_scaled_linear_fwd(x, wg, sg, torch.empty(M, N, **bf))
+            own = F.LinearSaved(M, N, K)
+            su = F.LinearSaved(M, N, K, tensors=(sg.x_q, sg.x_qT, own.w_q, own.w_qT, own.recs))
+            su.x_sc = sg.x_sc
+            F.fp8_amax(wu, su.w_sc)
+            F.fp8_quantize(wu, F.E4M3FN, su.w_sc, su.w_q, su.w_qT)
+            F.fp8_gemm(su.x_q, F.E4M3FN, su.w_q, F.E4M3FN, su.x_sc.inv_ptr(), su.w_sc.inv_ptr(),
+                       y, F.OUT_BF16)
+        else:
+            su = F.LinearSaved(M, N, K)
+            F.fp8_scaled_linear_fwd(x, wu, su, y)
+        F.fp8_scaled_linear_bwd(gy, su, ws, gx, gw)
+        torch.cuda.synchronize()
+        outs.append([host16(t) for t in (y, gx, gw)])
+    for a, b, nm in zip(outs[0], outs[1], ("y", "gx", "gW")):
+        assert np.array_equal(a, b), nm
+
+
 @pytest.mark.parametrize("which", ["activations_e4m3", "gradients_e5m2"])
 def test_quantize_pass_2pow28(which):
     """amax + scale + quantize-cast of a 268,435,456-element bf16 tensor:
