@@ -200,8 +200,7 @@ def main():
 
     def step_delayed():
         F.fp8_scaled_linear_fwd_delayed(x, w, saved, hx, hw, y, F.OUT_BF16)
-        F.fp8_scaled_linear_bwd_delayed(gy, saved, ws, hg, gx, gw, F.OUT_F16)
-        F.amp_unscale_check([gx, gw], scale, found)
+        F.fp8_scaled_linear_bwd_delayed_unscale(gy, saved, ws, hg, scale, found, gx, gw)
         F.amp_update_scale(scale, tracker, found, 2.0, 0.5, 2000)
 
     for _ in range(args.warmup):
@@ -224,8 +223,7 @@ def main():
 
     def step_rowwise():
         F.fp8_scaled_linear_fwd_rowwise(x, w, saved_rw, y_rw, F.OUT_BF16)
-        F.fp8_scaled_linear_bwd_rowwise(gy, saved_rw, ws_rw, gx_rw, gw_rw, F.OUT_F16)
-        F.amp_unscale_check([gx_rw, gw_rw], scale, found)
+        F.fp8_scaled_linear_bwd_rowwise_unscale(gy, saved_rw, ws_rw, scale, found, gx_rw, gw_rw)
         F.amp_update_scale(scale, tracker, found, 2.0, 0.5, 2000)
 
     for _ in range(args.warmup):

@@ -26,7 +26,8 @@ EXPORTS = ("fp8sg_status_string", "fp8sg_version", "amp_norm_workspace_len", "fp
            "fp8_scaled_linear_fwd_delayed", "fp8_scaled_linear_bwd", "fp8_scaled_linear_bwd_delayed",
            "amp_unscale_check", "amp_unscale_check_norm", "amp_update_scale",
            "fp8_quantize_rowwise", "fp8_gemm_rowwise", "fp8_scaled_linear_fwd_rowwise",
-           "fp8_scaled_linear_bwd_rowwise", "fp8_scaled_linear_bwd_unscale", "fp8_gemm_unscale")
+           "fp8_scaled_linear_bwd_rowwise", "fp8_scaled_linear_bwd_unscale", "fp8_gemm_unscale",
+           "fp8_scaled_linear_bwd_delayed_unscale", "fp8_scaled_linear_bwd_rowwise_unscale")
 MAX_HISTORY = 1024
 MAX_DIM = 1 << 29     # largest matrix dimension an entry point takes
 MAX_ELEMS = 1 << 35   # largest tensor, in elements
@@ -99,6 +100,11 @@ def lib():
     L.fp8_gemm_unscale.argtypes = [P, i, P, i, P, P, P, P, P, i64, i64, i64, P]
     L.fp8_scaled_linear_bwd_unscale.argtypes = [P, ctypes.POINTER(_Saved), i64, i64, i64,
                                                 ctypes.POINTER(_BwdWs), P, P, P, P, P]
+    L.fp8_scaled_linear_bwd_delayed_unscale.argtypes = [P, ctypes.POINTER(_Saved), i64, i64, i64,
+                                                        ctypes.POINTER(_BwdWs), P, i32, P, P, P,
+                                                        P, P]
+    L.fp8_scaled_linear_bwd_rowwise_unscale.argtypes = [P, ctypes.POINTER(_SavedRW), i64, i64, i64,
+                                                        ctypes.POINTER(_BwdWsRW), P, P, P, P, P]
     for name in EXPORTS[3:]:
         getattr(L, name).restype = i
     _lib = L
@@ -398,6 +404,22 @@ def fp8_scaled_linear_bwd_delayed(gy, saved: LinearSaved, ws: LinearBwdWs, hist_
            "fp8_scaled_linear_bwd_delayed")
 
 
+def fp8_scaled_linear_bwd_delayed_unscale(gy, saved: LinearSaved, ws: LinearBwdWs, hist_gy,
+                                          scale, found_inf, gx, gw, stream=None):
+    """fp8_scaled_linear_bwd_delayed into fp16 gx, gw with the GradScaler
+    unscale and non-finite check fused into the GEMM epilogues."""
+    M, N, K = _bwd_args(gy, saved, gx, gw, OUT_F16)
+    _need_scaler(scale, found_inf)
+    h = _hist(hist_gy, "hist_gy")
+    saved.check(M, N, K)
+    ws.check(M, N)
+    s = saved.struct()
+    b = ws.struct()
+    _check(lib().fp8_scaled_linear_bwd_delayed_unscale(
+        _ptr(gy), ctypes.byref(s), M, N, K, ctypes.byref(b), _ptr(hist_gy), h, _ptr(scale),
+        _ptr(found_inf), _ptr(gx), _ptr(gw), _stream(stream)), "fp8_scaled_linear_bwd_delayed_unscale")
+
+
 # ----------------------------------------------------------------- row-wise
 
 class RowScalesDev:
@@ -521,6 +543,21 @@ def fp8_scaled_linear_bwd_rowwise(gy, saved: LinearSavedRW, ws: LinearBwdWsRW, g
     _check(lib().fp8_scaled_linear_bwd_rowwise(_ptr(gy), ctypes.byref(s), M, N, K,
                                                ctypes.byref(b), _ptr(gx), _ptr(gw), out,
                                                _stream(stream)), "fp8_scaled_linear_bwd_rowwise")
+
+
+def fp8_scaled_linear_bwd_rowwise_unscale(gy, saved: LinearSavedRW, ws: LinearBwdWsRW, scale,
+                                          found_inf, gx, gw, stream=None):
+    """fp8_scaled_linear_bwd_rowwise into fp16 gx, gw with the GradScaler
+    unscale and non-finite check fused into the GEMM epilogues."""
+    M, N, K = _bwd_args(gy, saved, gx, gw, OUT_F16)
+    _need_scaler(scale, found_inf)
+    saved.check(M, N, K)
+    ws.check(M, N)
+    s = saved.struct()
+    b = ws.struct()
+    _check(lib().fp8_scaled_linear_bwd_rowwise_unscale(
+        _ptr(gy), ctypes.byref(s), M, N, K, ctypes.byref(b), _ptr(scale), _ptr(found_inf),
+        _ptr(gx), _ptr(gw), _stream(stream)), "fp8_scaled_linear_bwd_rowwise_unscale")
 
 
 def _grad_list(grads):

@@ -276,8 +276,42 @@ fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64
   GemmProblem wg{ws->gy_qT, saved->x_qT, gw, &ws->gy_sc->inv, &saved->x_sc->inv, N, K, M,
                  amp_scale, found_inf};
   if (amp_scale)  // fp16 gradients unscaled and checked in the GEMM epilogues
-    return hip_status(launch_gemm_unscale_pair(dg, wg, s));
+    return hip_status(launch_gemm_unscale_pair(dg, wg, false, s));
   return hip_status(launch_gemm_pair(dg, wg, FP8SG_E5M2, FP8SG_E4M3FN, out, s));
+}
+
+// Row-wise backward [FP8-TRAIN §1, §4 backward]: gy cast by rows and by
+// columns (e5m2); dgrad from gy_q (rows of gy) and w_qT (columns of W), wgrad
+// from gy_qT (columns of gy) and x_qT (columns of x): every scale lies along a
+// dimension the GEMM does not contract.  With amp_scale the fp16 gradients are
+// unscaled and checked in the GEMM epilogues.
+fp8sg_status linear_bwd_rw(const uint16_t* gy, const fp8_linear_saved_rw* saved, int64_t M,
+                                  int64_t N, int64_t K, const fp8_linear_bwd_ws_rw* ws, void* gx,
+                                  void* gw, fp8sg_out out, fp8sg_stream stream,
+                                  const float* amp_scale = nullptr, int32_t* found_inf = nullptr) {
+  if (!gy || !ws || !gx || !gw) return FP8SG_ERR_NULL;
+  if (!out_ok(out)) return FP8SG_ERR_FORMAT;
+  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K) || !gemm_ok(M, N, K))
+    return FP8SG_ERR_SHAPE;
+  fp8sg_status st = check_saved_rw(saved, M, N, K);
+  if (st != FP8SG_OK) return st;
+  if (!ws->gy_q || !ws->gy_qT) return FP8SG_ERR_NULL;
+  st = check_vec(ws->gy_row_amax, ws->gy_row_inv, M);
+  if (st != FP8SG_OK) return st;
+  st = check_vec(ws->gy_col_amax, ws->gy_col_inv, N);
+  if (st != FP8SG_OK) return st;
+  if (!aligned16(gy) || !aligned16(gx) || !aligned16(gw) || !aligned16(ws->gy_q) ||
+      !aligned16(ws->gy_qT))
+    return FP8SG_ERR_ALIGN;
+  hipStream_t s = S(stream);
+  const fp8_linear_saved_rw& v = *saved;
+  RowwiseArgs ag{gy, M, N, ws->gy_row_amax, ws->gy_row_inv, ws->gy_q, ws->gy_col_amax,
+                 ws->gy_col_inv, ws->gy_qT, 0};
+  if (launch_rowwise(ag, FP8SG_E5M2, s) != hipSuccess) return FP8SG_ERR_HIP;
+  GemmProblem dg{ws->gy_q, v.w_qT, gx, ws->gy_row_inv, v.w_col_inv, M, K, N, amp_scale, found_inf};
+  GemmProblem wg{ws->gy_qT, v.x_qT, gw, ws->gy_col_inv, v.x_col_inv, N, K, M, amp_scale, found_inf};
+  if (amp_scale) return hip_status(launch_gemm_unscale_pair(dg, wg, true, s));
+  return hip_status(launch_gemm_rowwise_pair(dg, wg, out, s));
 }
 
 }  // namespace
@@ -324,6 +358,19 @@ fp8sg_status fp8_scaled_linear_bwd_delayed(const uint16_t* gy, const fp8_linear_
   return linear_bwd(gy, saved, M, N, K, ws, hist_gy, history_len, gx, gw, out, stream);
 }
 
+fp8sg_status fp8_scaled_linear_bwd_delayed_unscale(const uint16_t* gy,
+                                                   const fp8_linear_saved* saved, int64_t M,
+                                                   int64_t N, int64_t K,
+                                                   const fp8_linear_bwd_ws* ws, float* hist_gy,
+                                                   int32_t history_len, const float* scale,
+                                                   int32_t* found_inf, uint16_t* gx, uint16_t* gw,
+                                                   fp8sg_stream stream) {
+  if (!hist_gy || !scale || !found_inf) return FP8SG_ERR_NULL;
+  if (!aligned(scale, 4) || !aligned(found_inf, 4)) return FP8SG_ERR_ALIGN;
+  return linear_bwd(gy, saved, M, N, K, ws, hist_gy, history_len, gx, gw, FP8SG_OUT_F16, stream,
+                    scale, found_inf);
+}
+
 // Row-wise forward [FP8-TRAIN §1, §4 forward]: x and W cast with one scale per
 // row (codes for this GEMM) and one per column (transposed copies for the
 // backward GEMMs), then y = x_q . w_q^T scaled by x_row_inv[m] * w_row_inv[n].
@@ -347,37 +394,23 @@ fp8sg_status fp8_scaled_linear_fwd_rowwise(const uint16_t* x, const uint16_t* w,
   return hip_status(launch_gemm_rowwise(p, FP8SG_E4M3FN, FP8SG_E4M3FN, out, s));
 }
 
-// Row-wise backward [FP8-TRAIN §1, §4 backward]: gy cast by rows and by
-// columns (e5m2); dgrad from gy_q (rows of gy) and w_qT (columns of W), wgrad
-// from gy_qT (columns of gy) and x_qT (columns of x): every scale lies along a
-// dimension the GEMM does not contract.
 fp8sg_status fp8_scaled_linear_bwd_rowwise(const uint16_t* gy, const fp8_linear_saved_rw* saved,
                                            int64_t M, int64_t N, int64_t K,
                                            const fp8_linear_bwd_ws_rw* ws, void* gx, void* gw,
                                            fp8sg_out out, fp8sg_stream stream) {
-  if (!gy || !ws || !gx || !gw) return FP8SG_ERR_NULL;
-  if (!out_ok(out)) return FP8SG_ERR_FORMAT;
-  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K) || !gemm_ok(M, N, K))
-    return FP8SG_ERR_SHAPE;
-  fp8sg_status st = check_saved_rw(saved, M, N, K);
-  if (st != FP8SG_OK) return st;
-  if (!ws->gy_q || !ws->gy_qT) return FP8SG_ERR_NULL;
-  st = check_vec(ws->gy_row_amax, ws->gy_row_inv, M);
-  if (st != FP8SG_OK) return st;
-  st = check_vec(ws->gy_col_amax, ws->gy_col_inv, N);
-  if (st != FP8SG_OK) return st;
-  if (!aligned16(gy) || !aligned16(gx) || !aligned16(gw) || !aligned16(ws->gy_q) ||
-      !aligned16(ws->gy_qT))
-    return FP8SG_ERR_ALIGN;
-  hipStream_t s = S(stream);
-  const fp8_linear_saved_rw& v = *saved;
-  RowwiseArgs ag{gy, M, N, ws->gy_row_amax, ws->gy_row_inv, ws->gy_q, ws->gy_col_amax,
-                 ws->gy_col_inv, ws->gy_qT, 0};
-  if (launch_rowwise(ag, FP8SG_E5M2, s) != hipSuccess) return FP8SG_ERR_HIP;
-  GemmProblem dg{ws->gy_q, v.w_qT, gx, ws->gy_row_inv, v.w_col_inv, M, K, N};
-  if (launch_gemm_rowwise(dg, FP8SG_E5M2, FP8SG_E4M3FN, out, s) != hipSuccess) return FP8SG_ERR_HIP;
-  GemmProblem wg{ws->gy_qT, v.x_qT, gw, ws->gy_col_inv, v.x_col_inv, N, K, M};
-  return hip_status(launch_gemm_rowwise(wg, FP8SG_E5M2, FP8SG_E4M3FN, out, s));
+  return linear_bwd_rw(gy, saved, M, N, K, ws, gx, gw, out, stream);
+}
+
+fp8sg_status fp8_scaled_linear_bwd_rowwise_unscale(const uint16_t* gy,
+                                                   const fp8_linear_saved_rw* saved, int64_t M,
+                                                   int64_t N, int64_t K,
+                                                   const fp8_linear_bwd_ws_rw* ws,
+                                                   const float* scale, int32_t* found_inf,
+                                                   uint16_t* gx, uint16_t* gw,
+                                                   fp8sg_stream stream) {
+  if (!scale || !found_inf) return FP8SG_ERR_NULL;
+  if (!aligned(scale, 4) || !aligned(found_inf, 4)) return FP8SG_ERR_ALIGN;
+  return linear_bwd_rw(gy, saved, M, N, K, ws, gx, gw, FP8SG_OUT_F16, stream, scale, found_inf);
 }
 
 fp8sg_status amp_unscale_check(uint16_t* const* grads, const int64_t* numel, int32_t ntensors,

@@ -84,7 +84,11 @@ hipError_t launch_gemm_unscale(const GemmProblem& p, int fa, int fb, hipStream_t
 // both are small, otherwise one launch each.
 hipError_t launch_gemm_pair(const GemmProblem& p0, const GemmProblem& p1, int fa, int fb, int out,
                            hipStream_t stream);
-hipError_t launch_gemm_unscale_pair(const GemmProblem& p0, const GemmProblem& p1,
+// The backward pair with the fused unscale; rowwise selects the row-wise
+// epilogue factors (GemmProblem's inverse pointers are then vectors).
+hipError_t launch_gemm_unscale_pair(const GemmProblem& p0, const GemmProblem& p1, bool rowwise,
+                                    hipStream_t stream);
+hipError_t launch_gemm_rowwise_pair(const GemmProblem& p0, const GemmProblem& p1, int out,
                                     hipStream_t stream);
 
 // ---- row-wise quantize (rowwise.hip)

@@ -281,6 +281,23 @@ FP8SG_API fp8sg_status fp8_scaled_linear_bwd_delayed(const uint16_t* gy, const f
                                    fp8sg_out out, fp8sg_stream stream);
 
 /*
+ * fp8_scaled_linear_bwd_delayed with fp16 gradients and the GradScaler's
+ * unscale and non-finite check fused into the GEMM epilogues [PT-CH20 §20.5.9,
+ * §20.2.2]: bit for bit
+ *   fp8_scaled_linear_bwd_delayed(..., gx, gw, FP8SG_OUT_F16)
+ *   amp_unscale_check({gx, gw}, {M*K, N*K}, 2, scale, found_inf)
+ * as fp8_scaled_linear_bwd_unscale is for the dynamic backward.
+ *   scale: device float; found_inf: device int32 (set, never cleared);
+ *   gx: [M,K] fp16, gw: [N,K] fp16.
+ * The other arguments as fp8_scaled_linear_bwd_delayed.
+ */
+FP8SG_API fp8sg_status fp8_scaled_linear_bwd_delayed_unscale(const uint16_t* gy,
+                                   const fp8_linear_saved* saved, int64_t M, int64_t N, int64_t K,
+                                   const fp8_linear_bwd_ws* ws, float* hist_gy,
+                                   int32_t history_len, const float* scale, int32_t* found_inf,
+                                   uint16_t* gx, uint16_t* gw, fp8sg_stream stream);
+
+/*
  * Row-wise scaling [FP8-TRAIN §1: instead of one scale per tensor, each row
  * gets its own scale factor, which the accumulation has to carry through].
  * For a rows x cols bf16 matrix x and each row i:
@@ -370,6 +387,24 @@ FP8SG_API fp8sg_status fp8_scaled_linear_bwd_rowwise(const uint16_t* gy,
                                    const fp8_linear_saved_rw* saved, int64_t M, int64_t N,
                                    int64_t K, const fp8_linear_bwd_ws_rw* ws, void* gx, void* gw,
                                    fp8sg_out out, fp8sg_stream stream);
+
+/*
+ * fp8_scaled_linear_bwd_rowwise with fp16 gradients and the GradScaler's
+ * unscale and non-finite check fused into the GEMM epilogues [FP8-TRAIN §1;
+ * PT-CH20 §20.2.2]: each element is stored as
+ * fp16(fl32(h) * fl32(1.0f / *scale)) with h = fp16(acc * fl32(inv_a[m] *
+ * inv_b[n])), bit for bit
+ *   fp8_scaled_linear_bwd_rowwise(..., gx, gw, FP8SG_OUT_F16)
+ *   amp_unscale_check({gx, gw}, {M*K, N*K}, 2, scale, found_inf).
+ *   scale: device float; found_inf: device int32 (set, never cleared);
+ *   gx: [M,K] fp16, gw: [N,K] fp16.
+ * The other arguments as fp8_scaled_linear_bwd_rowwise.
+ */
+FP8SG_API fp8sg_status fp8_scaled_linear_bwd_rowwise_unscale(const uint16_t* gy,
+                                   const fp8_linear_saved_rw* saved, int64_t M, int64_t N,
+                                   int64_t K, const fp8_linear_bwd_ws_rw* ws, const float* scale,
+                                   int32_t* found_inf, uint16_t* gx, uint16_t* gw,
+                                   fp8sg_stream stream);
 
 /*
  * GradScaler unscale + non-finite check over a list of fp16 gradients

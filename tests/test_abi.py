@@ -313,3 +313,23 @@ def test_binding_refuses_mismatched_buffers():
     with pytest.raises(ValueError, match="cols_sc.amax"):
         F.fp8_quantize_rowwise(x, 0, rs, torch.zeros(M, K, dtype=u8), F.RowScalesDev(K - 16, device="cpu"),
                                torch.zeros(K, M, dtype=u8))
+
+
+def test_delayed_and_rowwise_fused_unscale_validation():
+    L = F.lib()
+    s = F._Saved(A16, A16, A16, A16, A16, A16)
+    ws = F._BwdWs(A16, A16, A16)
+    d = lambda hist=A16, h=4, scale=A16, found=A16, M=16: L.fp8_scaled_linear_bwd_delayed_unscale(
+        P(A16), ctypes.byref(s), M, 16, 16, ctypes.byref(ws), P(hist), h, P(scale), P(found),
+        P(A16), P(A16), P(0))
+    assert d(hist=0) == ENULL and d(scale=0) == ENULL and d(found=0) == ENULL
+    assert d(h=0) == ESHAPE and d(M=8) == ESHAPE
+    assert d(hist=A16 + 2) == EALIGN and d(scale=A16 + 2) == EALIGN and d(found=A16 + 1) == EALIGN
+    srw = F._SavedRW(*([A16] * 12))
+    wrw = F._BwdWsRW(*([A16] * 6))
+    r = lambda scale=A16, found=A16, gx=A16, M=16: L.fp8_scaled_linear_bwd_rowwise_unscale(
+        P(A16), ctypes.byref(srw), M, 16, 32, ctypes.byref(wrw), P(scale), P(found), P(gx),
+        P(A16), P(0))
+    assert r(scale=0) == ENULL and r(found=0) == ENULL and r(gx=0) == ENULL
+    assert r(M=24) == ESHAPE and r(M=0) == ESHAPE
+    assert r(scale=A16 + 1) == EALIGN and r(gx=MIS) == EALIGN

@@ -165,3 +165,91 @@ def test_gemm_unscale_is_gemm_then_unscale(fa, fb, shape):
     torch.cuda.synchronize()
     assert np.array_equal(host_u16(C1), host_u16(C2))
     assert int(f1.item()) == int(f2.item())
+
+
+def run_both_delayed(x_h, w_h, gy_h, scale_val, hist_len=4):
+    """Delayed scaling: the fused backward and the unfused pair from the same
+    forward state and the same gy history."""
+    M, K = x_h.shape
+    N = w_h.shape[0]
+    x, w, gy = dev_bf16(x_h), dev_bf16(w_h), dev_bf16(gy_h)
+    saved = F.LinearSaved(M, N, K)
+    hx = torch.full((hist_len,), 3.0, dtype=torch.float32, device=DEV)
+    hw = torch.full((hist_len,), 0.05, dtype=torch.float32, device=DEV)
+    F.fp8_scaled_linear_fwd_delayed(x, w, saved, hx, hw, torch.empty((M, N), dtype=torch.bfloat16,
+                                                                      device=DEV))
+    # gy's history: its own amax (the delayed scale then equals the dynamic one)
+    gy_amax = float(np.abs(O.decode(O.BF16, gy_h).astype(np.float64)).max())
+    hg0 = torch.full((hist_len,), gy_amax, dtype=torch.float32, device=DEV)
+    scale = torch.tensor([scale_val], dtype=torch.float32, device=DEV)
+    outs = {}
+    for fused in (True, False):
+        ws = F.LinearBwdWs(M, N)
+        hg = hg0.clone()
+        gx = torch.full((M, K), 7.0, dtype=torch.float16, device=DEV)
+        gw = torch.full((N, K), 7.0, dtype=torch.float16, device=DEV)
+        found = torch.zeros(1, dtype=torch.int32, device=DEV)
+        if fused:
+            F.fp8_scaled_linear_bwd_delayed_unscale(gy, saved, ws, hg, scale, found, gx, gw)
+        else:
+            F.fp8_scaled_linear_bwd_delayed(gy, saved, ws, hg, gx, gw, F.OUT_F16)
+            F.amp_unscale_check([gx, gw], scale, found)
+        torch.cuda.synchronize()
+        outs[fused] = (host_u16(gx), host_u16(gw), int(found.item()), hg.cpu().numpy(),
+                       ws.gy_q.cpu().numpy(), ws.gy_qT.cpu().numpy())
+    return outs
+
+
+def run_both_rowwise(x_h, w_h, gy_h, scale_val):
+    M, K = x_h.shape
+    N = w_h.shape[0]
+    x, w, gy = dev_bf16(x_h), dev_bf16(w_h), dev_bf16(gy_h)
+    saved = F.LinearSavedRW(M, N, K)
+    F.fp8_scaled_linear_fwd_rowwise(x, w, saved, torch.empty((M, N), dtype=torch.bfloat16,
+                                                             device=DEV))
+    scale = torch.tensor([scale_val], dtype=torch.float32, device=DEV)
+    outs = {}
+    for fused in (True, False):
+        ws = F.LinearBwdWsRW(M, N)
+        gx = torch.full((M, K), 7.0, dtype=torch.float16, device=DEV)
+        gw = torch.full((N, K), 7.0, dtype=torch.float16, device=DEV)
+        found = torch.zeros(1, dtype=torch.int32, device=DEV)
+        if fused:
+            F.fp8_scaled_linear_bwd_rowwise_unscale(gy, saved, ws, scale, found, gx, gw)
+        else:
+            F.fp8_scaled_linear_bwd_rowwise(gy, saved, ws, gx, gw, F.OUT_F16)
+            F.amp_unscale_check([gx, gw], scale, found)
+        torch.cuda.synchronize()
+        outs[fused] = (host_u16(gx), host_u16(gw), int(found.item()),
+                       ws.gy_row_inv.cpu().numpy(), ws.gy_q.cpu().numpy(), ws.gy_qT.cpu().numpy())
+    return outs
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("scale", [65536.0, 1000.0])
+@pytest.mark.parametrize("mode", ["delayed", "rowwise"])
+def test_delayed_and_rowwise_fused_unscale_are_the_unfused_pair(mode, shape, scale):
+    """Delayed and row-wise scaling: the fused backward stores the unfused
+    pair's bits (gradients, flag, gy codes and gy's history or scale vector)."""
+    M, N, K = shape
+    x_h = W.normal_bf16(85, 0, (M, K), 1.0, 0.001, 50.0)
+    w_h = W.normal_bf16(85, 1, (N, K), 0.02)
+    gy_h = W.normal_bf16(85, 2, (M, N), 1e-4 * scale)
+    outs = (run_both_delayed if mode == "delayed" else run_both_rowwise)(x_h, w_h, gy_h, scale)
+    for i, what in enumerate(("gx", "gw", "found", "gy state", "gy_q", "gy_qT")):
+        a, b = outs[True][i], outs[False][i]
+        assert np.array_equal(a, b) if isinstance(a, np.ndarray) else a == b, what
+    assert outs[True][2] == 0
+
+
+@pytest.mark.parametrize("mode", ["delayed", "rowwise"])
+def test_delayed_and_rowwise_fused_unscale_flag_overflow(mode):
+    M, N, K = 256, 512, 384
+    x_h = W.normal_bf16(86, 0, (M, K), 1.0)
+    w_h = W.normal_bf16(86, 1, (N, K), 0.02)
+    gy_h = W.normal_bf16(86, 2, (M, N), 1e-4 * 65536.0)
+    outs = (run_both_delayed if mode == "delayed" else run_both_rowwise)(x_h, w_h, gy_h, 2.0 ** -12)
+    assert outs[True][2] == outs[False][2] == 1
+    for i in (0, 1):
+        assert np.array_equal(outs[True][i], outs[False][i])
+    assert np.any((outs[True][1] & 0x7FFF) == 0x7C00)
