@@ -387,9 +387,8 @@ fp8sg_status fp8_scaled_linear_fwd_rowwise(const uint16_t* x, const uint16_t* w,
   hipStream_t s = S(stream);
   const fp8_linear_saved_rw& v = *saved;
   RowwiseArgs ax{x, M, K, v.x_row_amax, v.x_row_inv, v.x_q, v.x_col_amax, v.x_col_inv, v.x_qT, 0};
-  if (launch_rowwise(ax, FP8SG_E4M3FN, s) != hipSuccess) return FP8SG_ERR_HIP;
   RowwiseArgs aw{w, N, K, v.w_row_amax, v.w_row_inv, v.w_q, v.w_col_amax, v.w_col_inv, v.w_qT, 0};
-  if (launch_rowwise(aw, FP8SG_E4M3FN, s) != hipSuccess) return FP8SG_ERR_HIP;
+  if (launch_rowwise2(ax, aw, FP8SG_E4M3FN, s) != hipSuccess) return FP8SG_ERR_HIP;
   GemmProblem p{v.x_q, v.w_q, y, v.x_row_inv, v.w_row_inv, M, N, K};
   return hip_status(launch_gemm_rowwise(p, FP8SG_E4M3FN, FP8SG_E4M3FN, out, s));
 }

@@ -106,6 +106,10 @@ struct RowwiseArgs {
 // Three launches: per-tile partial maxima (stored in q's memory), their
 // reduction into the amax / inverse-scale vectors, the cast.
 hipError_t launch_rowwise(const RowwiseArgs& a, int fmt, hipStream_t stream);
+// Two casts in the same three launches (x and W of a layer); falls back to
+// one cast after the other when either is empty or only one has a qT.
+hipError_t launch_rowwise2(const RowwiseArgs& a0, const RowwiseArgs& a1, int fmt,
+                           hipStream_t stream);
 
 // ---- GradScaler (amp.hip)
 // Norm workspace slots of the unscale pass for these tensors (exact; needs the

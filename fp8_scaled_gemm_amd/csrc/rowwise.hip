@@ -48,6 +48,19 @@ __device__ __forceinline__ RwParts rw_parts(const RowwiseArgs& a) {
 }
 __host__ __device__ inline int64_t rw_tiles(int64_t n) { return (n + kRwTile - 1) / kRwTile; }
 
+// One launch covers up to two tensors of the same kind (x and W of a layer):
+// blocks [0, block0[1]) work on job 0, the rest on job 1.
+struct RwJobs {
+  RowwiseArgs job[2];
+  int32_t block0[2];
+  int32_t njobs;
+};
+__device__ __forceinline__ const RowwiseArgs& rw_job(const RwJobs& J, int64_t& b) {
+  const int j = (J.njobs > 1 && (int)blockIdx.x >= J.block0[1]) ? 1 : 0;
+  b = (int64_t)blockIdx.x - J.block0[j];
+  return J.job[j];
+}
+
 // packed bf16 pair maximum (16-bit unsigned) -> the two fp32 bit patterns, NaN canonical
 __device__ __forceinline__ void unpack_max(uint32_t d, uint32_t& lo, uint32_t& hi) {
   lo = (d & 0xFFFFu) << 16;
@@ -57,11 +70,13 @@ __device__ __forceinline__ void unpack_max(uint32_t d, uint32_t& lo, uint32_t& h
 }
 
 template <bool WITH_T, bool S>
-__global__ __launch_bounds__(kRwThreads) void k_rw_amax(RowwiseArgs a) {
+__global__ __launch_bounds__(kRwThreads) void k_rw_amax(RwJobs J) {
+  int64_t b;
+  const RowwiseArgs& a = rw_job(J, b);
   const int tid = threadIdx.x;
   const int64_t rows = a.rows, cols = a.cols;
   int64_t rt, ct;
-  tile_grouped(blockIdx.x, rw_tiles(a.rows), a.tiles_c, rt, ct);
+  tile_grouped(b, rw_tiles(a.rows), a.tiles_c, rt, ct);
   const int64_t r_tile = rt * kRwTile, c_tile = ct * kRwTile;
   const RwParts pp = rw_parts(a);
   const int c8 = tid & 15, r0 = tid >> 4;
@@ -139,10 +154,12 @@ __global__ __launch_bounds__(kRwThreads) void k_rw_amax(RowwiseArgs a) {
 // One lane per row (then per column, with a transposed copy), 64 per block;
 // the four waves split the partials and meet in LDS.
 template <int FMT>
-__global__ __launch_bounds__(kRwThreads) void k_rw_reduce(RowwiseArgs a) {
+__global__ __launch_bounds__(kRwThreads) void k_rw_reduce(RwJobs J) {
+  int64_t b;
+  const RowwiseArgs& a = rw_job(J, b);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int64_t rows = a.rows, ncols = a.qT ? a.cols : 0;
-  const int64_t idx = (int64_t)blockIdx.x * kWave + lane;
+  const int64_t idx = b * kWave + lane;
   const RwParts pp = rw_parts(a);
   const bool is_row = idx < rows;
   const uint32_t* src = is_row ? pp.prow + idx : pp.pcol + (idx - rows);
@@ -191,11 +208,13 @@ __device__ __forceinline__ uint2 quant8v(uint4 v, const float* s) {
 }
 
 template <int FMT, bool WITH_T, bool S>
-__global__ __launch_bounds__(kRwThreads) void k_rw_quant(RowwiseArgs a) {
+__global__ __launch_bounds__(kRwThreads) void k_rw_quant(RwJobs J) {
+  int64_t b;
+  const RowwiseArgs& a = rw_job(J, b);
   const int tid = threadIdx.x;
   const int64_t rows = a.rows, cols = a.cols;
   int64_t rt, ct;
-  tile_grouped(blockIdx.x, rw_tiles(a.rows), a.tiles_c, rt, ct);
+  tile_grouped(b, rw_tiles(a.rows), a.tiles_c, rt, ct);
   const int64_t r_tile = rt * kRwTile, c_tile = ct * kRwTile;
   __shared__ float srow[kRwTile], scol[kRwTile];
   __shared__ uint32_t lds[kRwTile * 32];
@@ -253,35 +272,61 @@ __global__ __launch_bounds__(kRwThreads) void k_rw_quant(RowwiseArgs a) {
   }
 }
 
-template <int FMT, bool S>
-static hipError_t launch_rw_passes(const RowwiseArgs& a, int64_t nb, hipStream_t stream) {
-  const bool with_t = a.qT != nullptr;
-  if (with_t) hipLaunchKernelGGL((k_rw_amax<true, S>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream, a);
-  else hipLaunchKernelGGL((k_rw_amax<false, S>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream, a);
+// Blocks of a job: tiles for the amax and cast passes, 64 rows (columns) per
+// block for the reduction.
+static int64_t rw_tile_blocks(const RowwiseArgs& a) { return rw_tiles(a.rows) * a.tiles_c; }
+static int64_t rw_reduce_blocks(const RowwiseArgs& a) {
+  return (a.rows + (a.qT ? a.cols : 0) + kWave - 1) / kWave;
+}
+
+static RwJobs rw_jobs(const RowwiseArgs* a, int n, int64_t (*blocks)(const RowwiseArgs&),
+                      int64_t& total) {
+  RwJobs J{};
+  J.njobs = n;
+  total = 0;
+  for (int j = 0; j < n; ++j) {
+    J.job[j] = a[j];
+    J.block0[j] = (int32_t)total;
+    total += blocks(a[j]);
+  }
+  return J;
+}
+
+template <int FMT, bool S, bool WITH_T>
+static hipError_t launch_rw_passes(const RowwiseArgs* a, int n, hipStream_t stream) {
+  int64_t nb, nred;
+  const RwJobs Jt = rw_jobs(a, n, rw_tile_blocks, nb);
+  const RwJobs Jr = rw_jobs(a, n, rw_reduce_blocks, nred);
+  hipLaunchKernelGGL((k_rw_amax<WITH_T, S>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream, Jt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t nred = (a.rows + (with_t ? a.cols : 0) + kWave - 1) / kWave;
-  hipLaunchKernelGGL(k_rw_reduce<FMT>, dim3((unsigned)nred), dim3(kRwThreads), 0, stream, a);
+  hipLaunchKernelGGL(k_rw_reduce<FMT>, dim3((unsigned)nred), dim3(kRwThreads), 0, stream, Jr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (with_t)
-    hipLaunchKernelGGL((k_rw_quant<FMT, true, S>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_rw_quant<FMT, false, S>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream, a);
+  hipLaunchKernelGGL((k_rw_quant<FMT, WITH_T, S>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream,
+                     Jt);
   return hipGetLastError();
 }
 
+// One or two non-empty casts with the same transposed-copy choice.
 template <int FMT>
-static hipError_t launch_rw_fmt(RowwiseArgs a, hipStream_t stream) {
-  a.tiles_c = (int32_t)rw_tiles(a.cols);
-  const int64_t tiles_r = rw_tiles(a.rows);
-  // the partial maxima must fit in q (they do for rows, cols >= 16)
-  const int64_t part_bytes = 4 * (a.rows * a.tiles_c + (a.qT ? a.cols * tiles_r : 0));
-  if (part_bytes > a.rows * a.cols) return hipErrorInvalidValue;
-  const int64_t nb = tiles_r * a.tiles_c;
-  const int64_t bytes = a.rows * a.cols * (a.qT ? 4 : 3);  // the cast's traffic
-  return bytes >= kStreamBytes ? launch_rw_passes<FMT, true>(a, nb, stream)
-                               : launch_rw_passes<FMT, false>(a, nb, stream);
+static hipError_t launch_rw_fmt(const RowwiseArgs* in, int n, hipStream_t stream) {
+  RowwiseArgs a[2];
+  int64_t bytes = 0;  // the cast's traffic
+  for (int j = 0; j < n; ++j) {
+    a[j] = in[j];
+    a[j].tiles_c = (int32_t)rw_tiles(a[j].cols);
+    // the partial maxima must fit in q (they do for rows, cols >= 16)
+    const int64_t part_bytes =
+        4 * (a[j].rows * a[j].tiles_c + (a[j].qT ? a[j].cols * rw_tiles(a[j].rows) : 0));
+    if (part_bytes > a[j].rows * a[j].cols) return hipErrorInvalidValue;
+    bytes += a[j].rows * a[j].cols * (a[j].qT ? 4 : 3);
+  }
+  const bool st = bytes >= kStreamBytes;
+  if (a[0].qT) return st ? launch_rw_passes<FMT, true, true>(a, n, stream)
+                         : launch_rw_passes<FMT, false, true>(a, n, stream);
+  return st ? launch_rw_passes<FMT, true, false>(a, n, stream)
+            : launch_rw_passes<FMT, false, false>(a, n, stream);
 }
 
 // An empty dimension: the other dimension's rows (columns) are empty, so
@@ -316,8 +361,27 @@ hipError_t launch_rowwise(const RowwiseArgs& a, int fmt, hipStream_t stream) {
   if (a.rows == 0 || a.cols == 0)
     return fmt == FP8SG_E4M3FN ? launch_rw_empty<FP8SG_E4M3FN>(a, stream)
                                : launch_rw_empty<FP8SG_E5M2>(a, stream);
-  return fmt == FP8SG_E4M3FN ? launch_rw_fmt<FP8SG_E4M3FN>(a, stream)
-                             : launch_rw_fmt<FP8SG_E5M2>(a, stream);
+  return fmt == FP8SG_E4M3FN ? launch_rw_fmt<FP8SG_E4M3FN>(&a, 1, stream)
+                             : launch_rw_fmt<FP8SG_E5M2>(&a, 1, stream);
+}
+
+hipError_t launch_rowwise2(const RowwiseArgs& a0, const RowwiseArgs& a1, int fmt,
+                           hipStream_t stream) {
+  // one grid must stay below 2^32 threads: at most 2^23 blocks of 256
+  auto blocks = [](const RowwiseArgs& a) {
+    const int64_t t = rw_tiles(a.rows) * rw_tiles(a.cols);
+    const int64_t r = (a.rows + a.cols + kWave - 1) / kWave;
+    return t > r ? t : r;
+  };
+  const bool together = a0.rows && a0.cols && a1.rows && a1.cols && !a0.qT == !a1.qT &&
+                        blocks(a0) + blocks(a1) <= (int64_t(1) << 23);
+  if (!together) {
+    const hipError_t e = launch_rowwise(a0, fmt, stream);
+    return e != hipSuccess ? e : launch_rowwise(a1, fmt, stream);
+  }
+  const RowwiseArgs a[2] = {a0, a1};
+  return fmt == FP8SG_E4M3FN ? launch_rw_fmt<FP8SG_E4M3FN>(a, 2, stream)
+                             : launch_rw_fmt<FP8SG_E5M2>(a, 2, stream);
 }
 
 }  // namespace fp8sg
