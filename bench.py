@@ -453,24 +453,34 @@ def small_layer(torch, F, dev, stream, T, reps=200):
         bwd()
         scaler()
 
+    def step_fused():  # unscale + check in the backward epilogues: update only after it
+        fwd()
+        F.fp8_scaled_linear_bwd_unscale(gy, saved, ws, scale, found, gx, gw)
+        F.amp_update_scale(scale, tracker, found, 2.0, 0.5, 2000)
+
+    def replay_us(fn):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(g):
+            fn()
+        return round(T.run(g.replay, reps)["avg_us"], 2)
+
     out = {"workload": "small linear B=64 K=128 N=256 + GradScaler step (init 65536, "
                        "interval 2000)",
            "fwd_us": round(T.run(fwd, reps)["avg_us"], 2),
            "bwd_us": round(T.run(bwd, reps)["avg_us"], 2),
            "scaler_step_us": round(T.run(scaler, reps)["avg_us"], 2),
            "step_us": round(T.run(step, reps)["avg_us"], 2),
+           "step_fused_unscale_us": round(T.run(step_fused, reps)["avg_us"], 2),
            # tensors of at most 64 Ki elements are cast by one block each with
            # their own amax, and the two backward GEMMs share a launch
-           "launches": {"fwd": 2, "bwd": 2, "scaler_step": 2}}
-    g = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()
-    torch.cuda.current_stream().wait_stream(side)
-    with torch.cuda.graph(g):
-        step()
-    out["step_graph_replay_us"] = round(T.run(g.replay, reps)["avg_us"], 2)
+           "launches": {"fwd": 2, "bwd": 2, "scaler_step": 2, "step_fused_unscale": 5}}
+    out["step_graph_replay_us"] = replay_us(step)
+    out["step_fused_unscale_graph_replay_us"] = replay_us(step_fused)
     out["TFLOPs_eager"] = round(3 * 2.0 * S.M * S.N * S.K / (out["step_us"] * 1e-6) / 1e12, 4)
     return out
 
