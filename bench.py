@@ -168,17 +168,26 @@ def main():
 
     # ---- the timed region: exactly `steps` steps
     log(f"timing {args.steps} steps")
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    # events also every `chunk` steps (recording one does not synchronise):
+    # the median and minimum chunk give the spread inside the timed region
+    chunk = max(1, args.steps // 10)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range((args.steps + chunk - 1) // chunk + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
-    t1.record(stream)
+        if (i + 1) % chunk == 0 or i + 1 == args.steps:
+            marks[(i + chunk) // chunk].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    t0, t1 = marks[0], marks[-1]
     ms_per_step = t0.elapsed_time(t1) / args.steps
+    per_chunk = sorted(marks[k].elapsed_time(marks[k + 1]) / min(chunk, args.steps - k * chunk)
+                       for k in range(len(marks) - 1))
+    spread = {"chunks": len(per_chunk), "steps_per_chunk": chunk,
+              "median_ms_per_step": round(per_chunk[len(per_chunk) // 2], 4),
+              "min_ms_per_step": round(per_chunk[0], 4)}
     gemm_flops = 3 * 2.0 * M * N * K
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -402,6 +411,7 @@ def main():
                    "W": "bf16 N(0,0.02)", "gy": "bf16 N(0,1e-4) x loss scale 65536",
                    "y": "bf16", "grads": "fp16", "formats": "e4m3fn x/W, e5m2 gy"},
         "step_pct_of_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "step_spread": spread,
         "step_unfused_unscale": {"ms_per_step": round(ms_unfused, 4),
                                  "TFLOPs": round(gemm_flops / (ms_unfused * 1e-3) / 1e12, 2)},
         "step_delayed_scaling": {"ms_per_step": round(ms_delayed, 4),

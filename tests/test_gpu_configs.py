@@ -188,6 +188,39 @@ def test_quantize_pass_2pow28(which):
     assert_codes_equal(fmt, q.cpu().numpy(), ref.q, which)
 
 
+@pytest.mark.parametrize("delayed", [False, True])
+def test_quantize_flat_past_one_pass_per_block(delayed):
+    """A flat cast of 2^29 + 13 elements: more 16-byte vectors than the flat
+    kernel's one-pass blocks cover, so blocks stride (dynamic: 65,536 blocks;
+    delayed: 1,024), plus a 5-element tail.  Codes and record bit-exact."""
+    n = (1 << 29) + 13
+    x_h = W.logmag_bf16(87, 0, (n,), -4.0, 2.0)
+    x = dev16(x_h)
+    rec = F.ScaleRec()
+    q = torch.empty(n, dtype=torch.uint8, device=DEV)
+    log(f"flat cast n={n} delayed={delayed}: GPU")
+    if delayed:
+        hist = torch.full((4,), 37.0, dtype=torch.float32, device=DEV)
+        F.fp8_quantize_delayed(x, F.E4M3FN, rec, hist, q)
+    else:
+        F.fp8_amax(x, rec)
+        F.fp8_quantize(x, F.E4M3FN, rec, q)
+    torch.cuda.synchronize()
+    log("oracle")
+    if delayed:
+        ref = O.to_fp8_delayed(x_h, O.E4M3FN, np.full(4, 37.0, np.float32), with_transpose=False)
+        r = rec.read()
+        assert r["amax_bits"] == ref.amax_bits  # the current amax, pushed to the history
+        assert r["scale"] == ref.sc.scale and r["inv"] == ref.sc.inv
+        assert np.array_equal(hist.cpu().numpy(), ref.hist)
+        ref_q = ref.q
+    else:
+        ref = O.to_fp8(x_h, O.E4M3FN, with_transpose=False)
+        check_rec(rec, ref.sc, "flat")
+        ref_q = ref.q
+    assert_codes_equal(O.E4M3FN, q.cpu().numpy(), ref_q, "flat striding")
+
+
 def _scaler_reference(sizes, injections, values_finite_ok):
     """Oracle trajectory of (found, scale, tracker) per step."""
     inj = {j.step: j for j in injections}
