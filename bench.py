@@ -92,7 +92,7 @@ class Timer:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "fp8sg runs on one GPU (no multi-GPU path); --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 

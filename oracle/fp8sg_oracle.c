@@ -263,7 +263,7 @@ ORC_API uint32_t orc_amax_bf16(const uint16_t* x, int64_t n) {
 /*      consumes].                                                           */
 /* ------------------------------------------------------------------------ */
 
-/* EPS is named but not given on the page; 1e-12 is this build's reading. */
+/* EPS is named but not given on the page; the reading taken here is 1e-12. */
 #define ORC_EPS 1e-12
 
 ORC_API double orc_fp8_max(int fi) {
