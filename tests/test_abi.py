@@ -333,3 +333,25 @@ def test_delayed_and_rowwise_fused_unscale_validation():
     assert r(scale=0) == ENULL and r(found=0) == ENULL and r(gx=0) == ENULL
     assert r(M=24) == ESHAPE and r(M=0) == ESHAPE
     assert r(scale=A16 + 1) == EALIGN and r(gx=MIS) == EALIGN
+
+
+def test_buffer_checks_are_cached_per_buffer_set():
+    """A LinearSaved/LinearBwdWs validated once is not re-checked while its
+    buffers and sizes stay the same, and is checked again when one changes."""
+    import torch
+    M, N, K = 32, 16, 64
+    saved = F.LinearSaved(M, N, K, device="cpu")
+    saved.check(M, N, K)
+    saved.check(M, N, K)  # cached
+    saved.x_q = torch.zeros(M, K + 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="saved.x_q"):
+        saved.check(M, N, K)
+    saved.x_q = torch.zeros(M, K, dtype=torch.uint8)
+    saved.check(M, N, K)
+    with pytest.raises(ValueError, match="saved.x_q"):
+        saved.check(M, N, K + 16)  # other sizes: checked again
+    ws = F.LinearBwdWs(M, N, device="cpu")
+    ws.check(M, N)
+    ws.gy_qT = torch.zeros(N, M, dtype=torch.int8)
+    with pytest.raises(TypeError, match="ws.gy_qT"):
+        ws.check(M, N)
