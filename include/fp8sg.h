@@ -133,9 +133,9 @@ FP8SG_API fp8sg_status fp8_amax(const uint16_t* x, int64_t n, fp8sg_scale_rec* r
  *         NULL to skip the transposed copy.
  * Each code is enc(clamp(fl32(x * scale32), -max, max)) rounded to nearest
  * even; NaN inputs give a NaN code.  rows, cols >= 0 (x, q, qT may be NULL
- * when rows * cols == 0; the record's scale fields are still written).  With qT, rows and cols
- * that are multiples of 16 take the tiled fast path; other shapes are
- * handled by a plain per-element kernel.
+ * when rows * cols == 0; the record's scale fields are still written).  With
+ * qT, rows and cols that are multiples of 16 take the tiled fast path; other
+ * shapes are handled by a plain per-element kernel.
  */
 FP8SG_API fp8sg_status fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, fp8sg_format fmt,
                           fp8sg_scale_rec* rec, uint8_t* q, uint8_t* qT, fp8sg_stream stream);
@@ -147,7 +147,7 @@ FP8SG_API fp8sg_status fp8_quantize(const uint16_t* x, int64_t rows, int64_t col
  * fp64 inverse scales rounded once to fp32.
  *   A:  M x Kc codes of format fa, row-major (contiguous along Kc).
  *   B:  N x Kc codes of format fb, row-major (contiguous along Kc).
- *   inv_a, inv_b: device doubles (e.g. &rec->inv).
+ *   inv_a, inv_b: device doubles, 8-byte aligned (e.g. &rec->inv).
  *   C:  M x N of type `out`, row-major.
  *   M, N, Kc >= 0 and multiples of 16 (FP8SG_ERR_SHAPE otherwise).  Kc == 0
  *   gives C = 0 * alpha.  A pointer to a zero-sized operand may be NULL.
