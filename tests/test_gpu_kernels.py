@@ -224,6 +224,27 @@ def test_gemm_matches_oracle(fa, fb, shape, out):
     check_gemm_values(g, c_ref, absdot, K, OUT_FMT[out], f"{shape} {fa}{fb} out{out}")
 
 
+@pytest.mark.parametrize("shape", [(32, 48, (1 << 20) + 16), (272, 16, 65536 + 48)])
+def test_gemm_long_contraction(shape):
+    """A contraction of a million FP8 products (8,192 k-tiles of 128 plus a
+    ragged 16): every output against the oracle's sequential fp32 sum."""
+    M, N, K = shape
+    rng = np.random.default_rng(K)
+    A = random_codes(rng, F.E4M3FN, (M, K))
+    B = random_codes(rng, F.E5M2, (N, K))
+    inv = np.array([2.0 ** -9, 2.0 ** -12], np.float64)
+    invd = torch.from_numpy(inv).to(DEV)
+    C = out_tensor((M, N), F.OUT_F32)
+    F.fp8_gemm(dev_u8(A), F.E4M3FN, dev_u8(B), F.E5M2, invd.data_ptr(), invd.data_ptr() + 8, C,
+               F.OUT_F32)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy().astype(np.float64)
+    ii, jj = [v.reshape(-1) for v in np.meshgrid(np.arange(M), np.arange(N), indexing="ij")]
+    c_ref = O.gemm_at(A, F.E4M3FN, B, F.E5M2, inv[0], inv[1], ii, jj)
+    absdot = O.gemm_absdot_at(A, F.E4M3FN, B, F.E5M2, inv[0], inv[1], ii, jj)
+    check_gemm_values(got[ii, jj], c_ref, absdot, K, OUT_FMT[F.OUT_F32], f"long K {shape}")
+
+
 # ------------------------------------------------------------------ GradScaler
 
 AMP_SIZES = [0, 1, 7, 8, 9, 8191, 8192, 8193, 70_000, 123_457]
