@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true")
     p.add_argument("--no-hbm", action="store_true", help="skip the HBM-scale bandwidth passes")
+    p.add_argument("--no-vendor", action="store_true",
+                   help="skip timing the vendor library's FP8 GEMM for comparison")
     p.add_argument("--no-mlp", action="store_true",
                    help="skip the MLP-block timing through the PyTorch layer")
     p.add_argument("--copy-reference", action="store_true",
@@ -291,6 +293,31 @@ def main():
         y_rw, F.OUT_BF16), args.reps)
     del g16, q, qT, rs, cs
 
+    # ---- the vendor library's FP8 GEMM (hipBLASLt through torch._scaled_mm) on
+    # the forward's codes and inverse scales: context for the GEMM's roofline
+    # fraction, timed the same way; not part of the step
+    vendor = None
+    if not args.no_vendor:
+        try:
+            a8 = saved.x_q.view(torch.float8_e4m3fn)
+            b8 = saved.w_q.view(torch.float8_e4m3fn).t()  # [K, N], column-major
+            sa = torch.tensor([saved.x_sc.read()["inv32"]], dtype=torch.float32, device=dev)
+            sb = torch.tensor([saved.w_sc.read()["inv32"]], dtype=torch.float32, device=dev)
+            mm = lambda: torch._scaled_mm(a8, b8, scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+            v_us = T.run(mm, args.reps)["avg_us"]
+            ref = mm().float()
+            ours = y.float()
+            vendor = {"library": "hipBLASLt via torch._scaled_mm (e4m3fn x e4m3fn -> bf16)",
+                      "gemm_us": round(v_us, 2),
+                      "TFLOPs": round(2.0 * M * N * K / (v_us * 1e-6) / 1e12, 1),
+                      "ours_fwd_gemm_us": round(kern["gemm_fwd_e4m3xe4m3"]["avg_us"], 2),
+                      "speedup_ours_over_vendor": round(
+                          v_us / kern["gemm_fwd_e4m3xe4m3"]["avg_us"], 3),
+                      "max_abs_diff_over_max_abs": float((ref - ours).abs().max() /
+                                                         ours.abs().max())}
+        except Exception as e:  # an unsupported layout or dtype on this torch build
+            vendor = {"error": f"{type(e).__name__}: {e}"[:200]}
+
     gemm_avg_us = sum(kern[k]["avg_us"] for k in ("gemm_fwd_e4m3xe4m3", "gemm_dgrad_e5m2xe4m3",
                                                   "gemm_wgrad_e5m2xe4m3")) / 3
     gemm_tflops = 2.0 * M * N * K / (gemm_avg_us * 1e-6) / 1e12
@@ -424,6 +451,7 @@ def main():
                      "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
                      "traffic_unit": "bytes per launch (HBM, counter-measured)",
                      "kernel": "k_gemm_pingpong (3 GEMMs of the step, 2*M*N*K flops per launch)"},
+        "vendor_gemm": vendor,
         "hbm_scale": {k: (round(v, 1) if isinstance(v, float) else v) for k, v in hbm.items()},
         "hbm_frac": {k[:-5]: round(v / PEAK_HBM_GBPS, 4) for k, v in hbm.items()
                      if k.endswith("_GBps")},
