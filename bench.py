@@ -52,8 +52,6 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true")
     p.add_argument("--no-hbm", action="store_true", help="skip the HBM-scale bandwidth passes")
-    p.add_argument("--no-clock", action="store_true",
-                   help="skip sampling the GPU clock and power with amd-smi during steps")
     p.add_argument("--no-vendor", action="store_true",
                    help="skip timing the vendor library's FP8 GEMM for comparison")
     p.add_argument("--no-mlp", action="store_true",
@@ -295,12 +293,6 @@ def main():
         y_rw, F.OUT_BF16), args.reps)
     del g16, q, qT, rs, cs
 
-    # ---- the shader clock and board power under load (amd-smi, read while
-    # steps run): the GEMM's rate is bounded by this clock
-    clocks = None
-    if not args.no_clock:
-        clocks = sample_clocks(torch, step)
-
     # ---- the vendor library's FP8 GEMM (hipBLASLt through torch._scaled_mm) on
     # the forward's codes and inverse scales: context for the GEMM's roofline
     # fraction, timed the same way; not part of the step
@@ -460,7 +452,6 @@ def main():
                      "traffic_unit": "bytes per launch (HBM, counter-measured)",
                      "kernel": "k_gemm_pingpong (3 GEMMs of the step, 2*M*N*K flops per launch)"},
         "vendor_gemm": vendor,
-        "clock_under_load": clocks,
         "hbm_scale": {k: (round(v, 1) if isinstance(v, float) else v) for k, v in hbm.items()},
         "hbm_frac": {k[:-5]: round(v / PEAK_HBM_GBPS, 4) for k, v in hbm.items()
                      if k.endswith("_GBps")},
@@ -472,39 +463,6 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-
-
-def sample_clocks(torch, step):
-    """Read the XCD clocks and socket power with amd-smi (a child process) while
-    steps keep the GPU busy: steps are enqueued until the tool has answered.
-    None if amd-smi is unavailable; an error entry if its output is unexpected."""
-    import shutil
-    import subprocess
-    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
-    if not os.path.exists(exe):
-        return None
-    for _ in range(50):  # the GPU is busy before the tool starts
-        step()
-    proc = subprocess.Popen([exe, "metric", "-g", "0", "--clock", "--power", "--json"],
-                            stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
-    t_end = time.perf_counter() + 20.0
-    while proc.poll() is None and time.perf_counter() < t_end:
-        for _ in range(10):
-            step()
-    try:
-        out, _ = proc.communicate(timeout=5)
-        torch.cuda.synchronize()
-        d = json.loads(out)
-        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
-        mhz = [g["clock"][k]["clk"]["value"] for k in g["clock"] if k.startswith("gfx_")]
-        return {"source": "amd-smi metric, read while steps run back to back",
-                "gfx_clock_mhz_mean": round(sum(mhz) / len(mhz), 1),
-                "gfx_clock_mhz_min": min(mhz), "gfx_clock_mhz_max": max(mhz),
-                "xcds": len(mhz), "socket_power_w": g["power"]["socket_power"]["value"]}
-    except Exception as e:  # the tool's output format or a time-out
-        proc.kill()
-        torch.cuda.synchronize()
-        return {"error": f"{type(e).__name__}: {e}"[:200]}
 
 
 def small_layer(torch, F, dev, stream, T, reps=200):
