@@ -9,11 +9,12 @@
 // Stages: per-thread grid-stride loop over 16-byte loads (4 in flight) ->
 // wavefront shuffle -> LDS across the block's waves -> one plain store of the
 // block's maximum into its own slot of the record (at most FP8SG_AMAX_PARTS
-// blocks).  No atomics and no fences: same-address device-scope atomics from
-// thousands of blocks serialise at one memory channel, which made an
-// atomic-max design several times slower than the loads.  The consumer
-// reduces the slots: the quantize kernel does it at the start of every block
-// (4 KB from L2), and the standalone entry point adds a one-block finalize.
+// blocks; the first block zeroes the slots past the block count).  No atomics
+// and no fences: same-address device-scope atomics from thousands of blocks
+// serialise at one memory channel, which made an atomic-max design several
+// times slower than the loads.  The consumer reduces the slots: every block
+// of the quantize kernel loads all of them (4 KB) together with its first
+// tile, and the standalone entry point adds a one-block finalize.
 //
 // Several tensors can share one launch (the forward pass reduces x and W
 // together): each job owns a contiguous range of blocks.
@@ -66,6 +67,10 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(AmaxArgs args) {
     job.rec->_part[lb] = bits;
     if (lb == 0) job.rec->_nparts = (uint32_t)job.nblocks;
   }
+  // the slots past the block count read as zero, so a consumer may take all
+  // of them without reading the count first
+  if (lb == 0)
+    for (int i = job.nblocks + tid; i < FP8SG_AMAX_PARTS; i += kAmaxThreads) job.rec->_part[i] = 0;
 }
 
 // Standalone amax: publish rec->amax from the partial maxima (one block per job).

@@ -190,6 +190,29 @@ __device__ __forceinline__ float amax_from_partials(const fp8sg_scale_rec* rec) 
   return __uint_as_float(block_max_u32<NT>(m));
 }
 
+// The same maximum as a cast block takes it: all FP8SG_AMAX_PARTS slots (the
+// amax kernel zeroes the slots past its block count; zero never raises the
+// maximum), a fixed number of loads per thread that depend on no other load.
+// A block issues them before its data loads and then waits for them alone
+// (the vector memory counter retires loads in order), so the partials' round
+// trip overlaps the data's instead of preceding it.
+template <int NT>
+struct PartialLoads {
+  static constexpr int kPer = FP8SG_AMAX_PARTS / NT;
+  static_assert(FP8SG_AMAX_PARTS % NT == 0, "slots split evenly over the threads");
+  uint32_t v[kPer];
+  __device__ __forceinline__ void issue(const fp8sg_scale_rec* rec) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) v[k] = rec->_part[threadIdx.x + k * NT];
+  }
+  __device__ __forceinline__ float reduce() const {
+    uint32_t m = v[0];
+#pragma unroll
+    for (int k = 1; k < kPer; ++k) m = v[k] > m ? v[k] : m;
+    return __uint_as_float(block_max_u32<NT>(m));
+  }
+};
+
 // |x| max over bf16 pairs: packed 16-bit max of the bit patterns with the sign
 // cleared (integer order = numeric order for non-negative IEEE values, every
 // NaN above +inf).
@@ -232,15 +255,21 @@ __device__ __forceinline__ float hist_amax(const float* hist, int32_t h) {
 // cover 8 x 8, so the transposed copies' stores of neighbouring blocks land in
 // adjacent 128-byte pieces of the same rows (a single row band would spread
 // them over 128 rows at one power-of-two stride).
+// In 32-bit arithmetic (64-bit division is a long software loop): with rows,
+// cols <= FP8SG_MAX_DIM and rows * cols <= FP8SG_MAX_ELEMS there are fewer
+// than 2^24 tiles and 8 * tiles_c < 2^26.
 __host__ __device__ inline void tile_grouped(int64_t t, int64_t tiles_r, int64_t tiles_c,
                                              int64_t& rt, int64_t& ct) {
-  constexpr int64_t G = 8;
-  const int64_t per = G * tiles_c, g = t / per, first = g * G;
-  const int64_t gs = tiles_r - first < G ? tiles_r - first : G;
-  const int64_t w = t - g * per;
+  constexpr uint32_t G = 8;
+  const uint32_t t32 = (uint32_t)t, tr = (uint32_t)tiles_r;
+  const uint32_t per = G * (uint32_t)tiles_c, g = t32 / per, first = g * G;
+  const uint32_t gs = tr - first < G ? tr - first : G;
+  const uint32_t w = t32 - g * per;
   rt = first + w % gs;
   ct = w / gs;
 }
+static_assert((FP8SG_MAX_ELEMS >> 14) + 2 * (FP8SG_MAX_DIM >> 7) + 1 < (1ll << 24),
+              "tile counts fit 32-bit arithmetic");
 
 // LDS tile: 128 rows x 32 dwords; dword column x of row r lives at x ^ swz(r).
 __device__ __forceinline__ int swz(int r) { return ((r >> 4) & 3) << 3; }

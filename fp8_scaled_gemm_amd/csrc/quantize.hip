@@ -4,10 +4,10 @@
 // GEMMs need each operand contiguous along its contraction dimension, which
 // for x, W and gy means a transposed FP8 copy].
 //
-// Every block reduces the amax kernel's partial maxima (4 KB, from L2) and
-// recomputes the scale (two fp64 divisions), so the amax -> scale step needs
-// no launch of its own; the first block of each job also writes the record's
-// amax and scale fields.
+// Every block reduces the amax kernel's partial maxima (all 1024 slots, 4 KB,
+// loaded together with its first tile) and recomputes the scale (two fp64
+// divisions), so the amax -> scale step needs no launch of its own; the first
+// block of each job also writes the record's amax and scale fields.
 //
 // Tiled path: one 128 x 128 tile per 256-thread block (blocks stride over the
 // tiles when there are more tiles than blocks).  The tile is read once with
@@ -107,35 +107,63 @@ __device__ __forceinline__ void publish_scale(fp8sg_scale_rec* rec, float amax, 
 
 template <int FMT, bool S, bool DELAYED, bool SELF = false>
 __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
+  constexpr bool kParts = !DELAYED && !SELF;  // scale from the amax kernel's partials
   int lb;
   const QuantJob& job = pick_job(args, lb);
   const int tid = threadIdx.x;
-  const float amax = SELF ? self_amax(job) : job_amax<DELAYED>(job);
-  const ScaleVals sv = scale_from_amax(amax, FMT);
-  if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
-
   const int64_t rows = job.rows, cols = job.cols;
   const int64_t tiles_r = (rows + kQTile - 1) / kQTile;
   const int64_t ntiles = tiles_r * job.tiles_c;
   __shared__ uint32_t lds[kQTile * 32];
   uint32_t am = 0;  // DELAYED: packed |x| max of everything this block loaded
 
+  // phase 1 layout: 16 lanes per row (8 elements each), 16 rows per pass, 8 passes
+  const int c8 = tid & 15;
+  const int r0 = tid >> 4;
+  uint4 v[8];
+  // The one block of an empty tensor has no tile: it loads from its record
+  // (valid memory, nothing stored), so that no branch precedes the first
+  // loads.  A branch there makes the wait for the partials wait for the
+  // tile's loads too (the wait count is taken from the path without them).
+  const bool has_tile = lb < ntiles;
+  const uint16_t* const x = has_tile ? job.x : reinterpret_cast<const uint16_t*>(job.rec);
+  const int64_t tr_any = tiles_r > 0 ? tiles_r : 1;
+  auto load = [&](int64_t tile) {
+    int64_t rt, ct;
+    tile_grouped(tile, tr_any, job.tiles_c, rt, ct);
+    const int64_t gc = ct * kQTile + 8 * c8;
+    const bool col_ok = gc < cols;  // cols % 16 == 0: a group of 8 is all in or all out
+    // Every load is issued, with no branch between them: a lane outside a
+    // ragged tile loads the tensor's first 8 elements instead.  Those codes
+    // are never stored (rows and cols are multiples of 16, so each 8-column
+    // group and each 16-row group of qT is all in or all out), and a delayed
+    // amax over them is unchanged (they are elements of x).
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int64_t gr = rt * kQTile + r0 + 16 * p;
+      v[p] = ld16<S>(x + ((col_ok && gr < rows) ? gr * cols + gc : 0));
+    }
+  };
+  // partials, then the first tile, all in flight before the scale is derived
+  float amax;
+  if constexpr (kParts) {
+    PartialLoads<kQThreads> parts;
+    parts.issue(job.rec);
+    load(has_tile ? lb : 0);
+    amax = parts.reduce();
+  } else {
+    amax = SELF ? self_amax(job) : job_amax<DELAYED>(job);
+  }
+  const ScaleVals sv = scale_from_amax(amax, FMT);
+  if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
+
   for (int64_t tile = lb; tile < ntiles; tile += job.nblocks) {
     int64_t rt, ct;
     tile_grouped(tile, tiles_r, job.tiles_c, rt, ct);
     const int64_t r_tile = rt * kQTile, c_tile = ct * kQTile;
-
-    // phase 1: 16 lanes per row (8 elements each), 16 rows per pass, 8 passes
-    const int c8 = tid & 15;
-    const int r0 = tid >> 4;
     const int64_t gc = c_tile + 8 * c8;
-    const bool col_ok = gc < cols;  // cols % 16 == 0: a group of 8 is all in or all out
-    uint4 v[8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int64_t gr = r_tile + r0 + 16 * p;
-      v[p] = (col_ok && gr < rows) ? ld16<S>(job.x + gr * cols + gc) : make_uint4(0, 0, 0, 0);
-    }
+    const bool col_ok = gc < cols;
+    if (!kParts || tile != lb) load(tile);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int r = r0 + 16 * p;
@@ -186,24 +214,41 @@ __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
   int lb;
   const QuantJob& job = pick_job(args, lb);
   const int tid = threadIdx.x;
-  const float amax = job_amax<DELAYED>(job);
-  const ScaleVals sv = scale_from_amax(amax, FMT);
-  if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
   uint32_t am = 0;
 
   const int64_t n = job.rows * job.cols;
   const int64_t nvec = n >> 3;
-  const uint4* xv = reinterpret_cast<const uint4*>(job.x);
+  // an empty tensor's block loads from its record, as in the tiled kernel
+  const uint4* const xv = reinterpret_cast<const uint4*>(
+      nvec > 0 ? static_cast<const void*>(job.x) : static_cast<const void*>(job.rec));
   uint2* qv = reinterpret_cast<uint2*>(job.q);
   constexpr int kFlatUnroll = flat_unroll<DELAYED>();
   const int64_t step = (int64_t)job.nblocks * kQThreads * kFlatUnroll;
-  for (int64_t base = (int64_t)lb * kQThreads * kFlatUnroll + tid; base < nvec; base += step) {
-    uint4 v[kFlatUnroll];
+  uint4 v[kFlatUnroll];
+  // branch-free as in the tiled kernel: past the end a lane loads vector 0
+  // (stored nowhere; an element of x, so a delayed amax is unchanged)
+  auto load = [&](int64_t base) {
 #pragma unroll
     for (int u = 0; u < kFlatUnroll; ++u) {
       const int64_t k = base + (int64_t)u * kQThreads;
-      v[u] = k < nvec ? ld16<S>(xv + k) : make_uint4(0, 0, 0, 0);
+      v[u] = ld16<S>(xv + (k < nvec ? k : 0));
     }
+  };
+  // as in the tiled kernel: partials, then the first loads, then the scale
+  const int64_t base0 = (int64_t)lb * kQThreads * kFlatUnroll + tid;
+  float amax;
+  if constexpr (!DELAYED) {
+    PartialLoads<kQThreads> parts;
+    parts.issue(job.rec);
+    load(base0);
+    amax = parts.reduce();
+  } else {
+    amax = job_amax<DELAYED>(job);
+  }
+  const ScaleVals sv = scale_from_amax(amax, FMT);
+  if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
+  for (int64_t base = base0; base < nvec; base += step) {
+    if (DELAYED || base != base0) load(base);
 #pragma unroll
     for (int u = 0; u < kFlatUnroll; ++u) {
       const int64_t k = base + (int64_t)u * kQThreads;

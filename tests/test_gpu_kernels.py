@@ -122,6 +122,31 @@ def test_quantize_matches_oracle(fmt, shape, with_t):
         assert_codes_equal(fmt, qT.cpu().numpy(), ref.qT, f"qT {shape}")
 
 
+@pytest.mark.parametrize("with_t", [True, False])
+def test_quantize_reused_record(with_t):
+    """One record for a large tensor (all partial-maximum slots written, large
+    amax), then for small ones (a few slots): the cast takes every slot, so the
+    slots past the small tensor's count must not keep the large amax."""
+    rec = F.ScaleRec()
+    big = W.normal_bf16(35, 1, (4096, 2048), 1.0, 0.002, 500.0)
+    bd = dev_bf16(big).reshape(big.shape)
+    F.fp8_amax(bd, rec)
+    F.fp8_quantize(bd, F.E4M3FN, rec, torch.empty(big.shape, dtype=torch.uint8, device=DEV))
+    for shape in [(256, 272), (16, 16), (0, 16)]:
+        x = W.normal_bf16(35, shape[0] + 2, shape, 0.01)
+        ref = O.to_fp8(x, F.E4M3FN, with_transpose=True)
+        xd = dev_bf16(x).reshape(shape)
+        q = torch.empty(shape, dtype=torch.uint8, device=DEV)
+        qT = torch.empty(shape[::-1], dtype=torch.uint8, device=DEV) if with_t else None
+        F.fp8_amax(xd, rec)
+        F.fp8_quantize(xd, F.E4M3FN, rec, q, qT)
+        torch.cuda.synchronize()
+        check_rec(rec, ref.sc, str(shape))
+        assert_codes_equal(F.E4M3FN, q.cpu().numpy(), ref.q, f"q {shape}")
+        if with_t:
+            assert_codes_equal(F.E4M3FN, qT.cpu().numpy(), ref.qT, f"qT {shape}")
+
+
 def finite_bf16_upto(limit):
     """Every finite bf16 pattern with |x| <= limit, both signs."""
     allp = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
