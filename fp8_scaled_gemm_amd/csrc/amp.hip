@@ -84,12 +84,19 @@ __global__ __launch_bounds__(kAmpThreads) void k_unscale_check(AmpTable t) {
   bool bad = false;
   float ssu[kAmpUnroll] = {};  // norm: one running sum per load of the thread
 
+  // All loads issued with no branch between them (a branch or a select here
+  // makes the compiler wait for the first loads before issuing the rest): a
+  // lane without a whole vector of the tensor loads the 16-byte chunk at g,
+  // which holds the tensor's first element (every block's tensor is
+  // non-empty), and never uses it.
   uint4 v[kAmpUnroll];
 #pragma unroll
   for (int u = 0; u < kAmpUnroll; ++u) {
     const int64_t e = base + 8 * (int64_t)(u * kAmpThreads + tid);
-    v[u] = (e >= first && e + 8 <= n) ? ld16<S>(g + e) : make_uint4(0, 0, 0, 0);
+    v[u] = ld16<S>(g + ((e >= first && e + 8 <= n) ? e : 0));
   }
+#pragma unroll
+  for (int u = 0; u < kAmpUnroll; ++u) keep_loaded(v[u]);
 #pragma unroll
   for (int u = 0; u < kAmpUnroll; ++u) {
     const int64_t e = base + 8 * (int64_t)(u * kAmpThreads + tid);

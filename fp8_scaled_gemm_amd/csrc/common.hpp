@@ -41,6 +41,13 @@ __device__ __forceinline__ void st_stream(void* p, uint2 v) {
 // cached accesses: its inputs were usually just written or read by the
 // previous kernel and are still there, and its outputs are read next.
 constexpr int64_t kStreamBytes = 256ll << 20;
+// An empty use of a loaded value (no instruction): the compiler may not sink
+// the load into a later conditional use, where it would be issued only after
+// the work before that use.
+__device__ __forceinline__ void keep_loaded(const uint4& v) {
+  asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+}
+
 template <bool S>
 __device__ __forceinline__ uint4 ld16(const void* p) {
   if constexpr (S) return ld_stream(p);
