@@ -98,7 +98,7 @@ def test_amax_special_values(special):
 # -------------------------------------------------------------------- quantize
 
 SHAPES = [(16, 16), (128, 128), (144, 272), (272, 144), (256, 4096), (4096, 48), (37, 53),
-          (1, 1000), (1000, 1), (1, 17), (0, 16), (16, 0)]
+          (1, 1000), (1000, 1), (1, 17), (0, 16), (16, 0), (1, 5), (7, 1)]
 
 
 @pytest.mark.parametrize("fmt", [F.E4M3FN, F.E5M2])
