@@ -278,6 +278,16 @@ __host__ __device__ inline void tile_grouped(int64_t t, int64_t tiles_r, int64_t
 static_assert((FP8SG_MAX_ELEMS >> 14) + 2 * (FP8SG_MAX_DIM >> 7) + 1 < (1ll << 24),
               "tile counts fit 32-bit arithmetic");
 
+// Block -> first tile of a cast that streams from HBM: block b runs on XCD
+// b % 8 (round-robin dispatch), and each XCD takes a contiguous eighth of the
+// n first tiles, so the transposed stores of tiles that are neighbours in
+// tile_grouped order leave through the same L2 (16384^2 with transposed copy:
+// 218 -> 205 us; cached sizes gain nothing).  A bijection on [0, n).
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t n) {
+  const int64_t q = n / 8, rem = n % 8, x = b % 8;
+  return x * q + (x < rem ? x : rem) + b / 8;
+}
+
 // LDS tile: 128 rows x 32 dwords; dword column x of row r lives at x ^ swz(r).
 __device__ __forceinline__ int swz(int r) { return ((r >> 4) & 3) << 3; }
 

@@ -125,7 +125,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
   // (valid memory, nothing stored), so that no branch precedes the first
   // loads.  A branch there makes the wait for the partials wait for the
   // tile's loads too (the wait count is taken from the path without them).
-  const bool has_tile = lb < ntiles;
+  const int64_t t0 = S ? xcd_contiguous(lb, job.nblocks) : lb;  // this block's first tile
+  const bool has_tile = t0 < ntiles;
   const uint16_t* const x = has_tile ? job.x : reinterpret_cast<const uint16_t*>(job.rec);
   const int64_t tr_any = tiles_r > 0 ? tiles_r : 1;
   auto load = [&](int64_t tile) {
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
   if constexpr (kParts) {
     PartialLoads<kQThreads> parts;
     parts.issue(job.rec);
-    load(has_tile ? lb : 0);
+    load(has_tile ? t0 : 0);
     amax = parts.reduce();
   } else {
     amax = SELF ? self_amax(job) : job_amax<DELAYED>(job);
@@ -157,13 +158,13 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
   const ScaleVals sv = scale_from_amax(amax, FMT);
   if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
 
-  for (int64_t tile = lb; tile < ntiles; tile += job.nblocks) {
+  for (int64_t tile = t0; tile < ntiles; tile += job.nblocks) {
     int64_t rt, ct;
     tile_grouped(tile, tiles_r, job.tiles_c, rt, ct);
     const int64_t r_tile = rt * kQTile, c_tile = ct * kQTile;
     const int64_t gc = c_tile + 8 * c8;
     const bool col_ok = gc < cols;
-    if (!kParts || tile != lb) load(tile);
+    if (!kParts || tile != t0) load(tile);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int r = r0 + 16 * p;

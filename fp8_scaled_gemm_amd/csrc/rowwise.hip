@@ -213,6 +213,8 @@ __global__ __launch_bounds__(kRwThreads) void k_rw_quant(RwJobs J) {
   const RowwiseArgs& a = rw_job(J, b);
   const int tid = threadIdx.x;
   const int64_t rows = a.rows, cols = a.cols;
+  // one block per tile; streaming with a transposed copy, XCD-contiguous order
+  if constexpr (S && WITH_T) b = xcd_contiguous(b, rw_tiles(a.rows) * a.tiles_c);
   int64_t rt, ct;
   tile_grouped(b, rw_tiles(a.rows), a.tiles_c, rt, ct);
   const int64_t r_tile = rt * kRwTile, c_tile = ct * kRwTile;

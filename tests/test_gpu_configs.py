@@ -188,6 +188,38 @@ def test_quantize_pass_2pow28(which):
     assert_codes_equal(fmt, q.cpu().numpy(), ref.q, which)
 
 
+@pytest.mark.parametrize("rowwise", [False, True])
+def test_quantize_transposed_streaming_size(rowwise):
+    """The cast with its transposed copy at a size that streams from HBM
+    (16400 x 16400, 1.08 GB moved): ragged edge tiles and 129^2 = 16641 tiles,
+    not a multiple of the 8 XCDs the streaming block order splits them over."""
+    side = 16400
+    x_h = W.normal_bf16(36, 1, (side, side), 1.0, 0.001, 50.0)
+    x = dev16(x_h).reshape(side, side)
+    q = torch.empty((side, side), dtype=torch.uint8, device=DEV)
+    qT = torch.empty((side, side), dtype=torch.uint8, device=DEV)
+    log(f"rowwise={rowwise}: GPU cast")
+    if rowwise:
+        rs, cs = F.RowScalesDev(side), F.RowScalesDev(side)
+        F.fp8_quantize_rowwise(x, F.E4M3FN, rs, q, cs, qT)
+    else:
+        rec = F.ScaleRec()
+        F.fp8_amax(x, rec)
+        F.fp8_quantize(x, F.E4M3FN, rec, q, qT)
+    torch.cuda.synchronize()
+    log(f"rowwise={rowwise}: oracle")
+    if rowwise:
+        ref = O.to_fp8_rowwise(x_h, F.E4M3FN)
+        for got, want, nm in ((rs, ref.rows, "rows"), (cs, ref.cols, "cols")):
+            assert np.array_equal(got.amax.cpu().numpy().view(np.uint32), want.amax_bits), nm
+            assert np.array_equal(got.inv.cpu().numpy().view(np.uint64), want.inv.view(np.uint64)), nm
+    else:
+        ref = O.to_fp8(x_h, F.E4M3FN, with_transpose=True)
+        check_rec(rec, ref.sc, "per-tensor")
+    assert_codes_equal(F.E4M3FN, q.cpu().numpy(), ref.q, "q")
+    assert_codes_equal(F.E4M3FN, qT.cpu().numpy(), ref.qT, "qT")
+
+
 @pytest.mark.parametrize("delayed", [False, True])
 def test_quantize_flat_past_one_pass_per_block(delayed):
     """A flat cast of 2^29 + 13 elements: more 16-byte vectors than the flat
