@@ -6,7 +6,7 @@
 // NaN-propagating (every NaN pattern sits above +inf).  Two bf16 lanes per
 // dword are reduced together with packed 16-bit max.
 //
-// Stages: per-thread grid-stride loop over 16-byte loads (4 in flight) ->
+// Stages: per-thread grid-stride loop over 16-byte loads (8 in flight) ->
 // wavefront shuffle -> LDS across the block's waves -> one plain store of the
 // block's maximum into its own slot of the record (at most FP8SG_AMAX_PARTS
 // blocks; the first block zeroes the slots past the block count).  No atomics
@@ -24,7 +24,7 @@
 namespace fp8sg {
 
 constexpr int kAmaxThreads = 256;
-constexpr int kAmaxUnroll = 4;  // 16-byte loads in flight per thread per iteration
+constexpr int kAmaxUnroll = 8;  // 16-byte loads in flight per thread per iteration
 
 template <bool S>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax(AmaxArgs args) {
@@ -43,10 +43,12 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(AmaxArgs args) {
   uint32_t m = 0;
   for (int64_t base = (int64_t)lb * kAmaxThreads * kAmaxUnroll + tid; base < nvec; base += step) {
     uint4 v[kAmaxUnroll];
+    // branch-free: past the end a lane loads vector 0 again, an element of x
+    // (inside this loop nvec > 0), which leaves the maximum unchanged
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) {
       const int64_t k = base + (int64_t)u * kAmaxThreads;
-      v[u] = k < nvec ? ld16<S>(xv + k) : make_uint4(0, 0, 0, 0);
+      v[u] = ld16<S>(xv + (k < nvec ? k : 0));
     }
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) {
