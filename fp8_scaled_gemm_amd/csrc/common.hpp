@@ -256,6 +256,34 @@ __device__ __forceinline__ float hist_amax(const float* hist, int32_t h) {
   return __uint_as_float(block_max_u32<NT>(m));
 }
 
+// The same maximum with loads a block can issue ahead of its data loads (as
+// PartialLoads): FP8SG_MAX_HISTORY / NT per thread, an index past the history
+// reading entry 0 again (h >= 1), which cannot change the maximum.
+template <int NT>
+struct HistLoads {
+  static constexpr int kPer = FP8SG_MAX_HISTORY / NT;
+  static_assert(FP8SG_MAX_HISTORY % NT == 0, "entries split evenly over the threads");
+  uint32_t v[kPer];
+  __device__ __forceinline__ void issue(const float* hist, int32_t h) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int32_t i = (int32_t)threadIdx.x + k * NT;
+      v[k] = __float_as_uint(hist[i < h ? i : 0]);
+    }
+  }
+  __device__ __forceinline__ float reduce() const {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      uint32_t b = v[k];
+      if ((b & 0x7FFFFFFFu) > 0x7F800000u) b = 0x7FC00000u;
+      else if (b >> 31) b = 0;
+      m = b > m ? b : m;
+    }
+    return __uint_as_float(block_max_u32<NT>(m));
+  }
+};
+
 // Transposed stores of 128 x 128 code tiles (quantize.hip, rowwise.hip).
 // Tile t of a tiles_r x tiles_c grid, walked in groups of 8 row tiles: down
 // the 8 rows of a group first, then across its columns.  64 consecutive tiles

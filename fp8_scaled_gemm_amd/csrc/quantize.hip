@@ -145,15 +145,21 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
       v[p] = ld16<S>(x + ((col_ok && gr < rows) ? gr * cols + gc : 0));
     }
   };
-  // partials, then the first tile, all in flight before the scale is derived
+  // partials (or the history), then the first tile, all in flight before
+  // the scale is derived
   float amax;
   if constexpr (kParts) {
     PartialLoads<kQThreads> parts;
     parts.issue(job.rec);
     load(has_tile ? t0 : 0);
     amax = parts.reduce();
+  } else if constexpr (DELAYED) {
+    HistLoads<kQThreads> hl;
+    hl.issue(job.hist, job.hist_len);
+    load(has_tile ? t0 : 0);
+    amax = hl.reduce();
   } else {
-    amax = SELF ? self_amax(job) : job_amax<DELAYED>(job);
+    amax = self_amax(job);
   }
   const ScaleVals sv = scale_from_amax(amax, FMT);
   if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
     const int64_t r_tile = rt * kQTile, c_tile = ct * kQTile;
     const int64_t gc = c_tile + 8 * c8;
     const bool col_ok = gc < cols;
-    if (!kParts || tile != t0) load(tile);
+    if (SELF || tile != t0) load(tile);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int r = r0 + 16 * p;
@@ -244,12 +250,15 @@ __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
     load(base0);
     amax = parts.reduce();
   } else {
-    amax = job_amax<DELAYED>(job);
+    HistLoads<kQThreads> hl;
+    hl.issue(job.hist, job.hist_len);
+    load(base0);
+    amax = hl.reduce();
   }
   const ScaleVals sv = scale_from_amax(amax, FMT);
   if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
   for (int64_t base = base0; base < nvec; base += step) {
-    if (DELAYED || base != base0) load(base);
+    if (base != base0) load(base);
 #pragma unroll
     for (int u = 0; u < kFlatUnroll; ++u) {
       const int64_t k = base + (int64_t)u * kQThreads;
