@@ -70,7 +70,20 @@ __device__ __forceinline__ float self_amax(const QuantJob& job) {
   const int64_t nv = job.rows * job.cols / 8;  // cols % 16 == 0 on this path
   const uint4* xv = reinterpret_cast<const uint4*>(job.x);
   uint32_t m = 0;
-  for (int64_t k = threadIdx.x; k < nv; k += kQThreads) m = absmax8(m, xv[k]);
+  // eight loads in flight per thread (one at a time made a 32 Ki-element
+  // tensor 16 dependent round trips); past the end a lane rereads vector 0,
+  // an element of x, which leaves the maximum unchanged
+  constexpr int kU = 8;
+  for (int64_t k0 = threadIdx.x; k0 < nv; k0 += (int64_t)kQThreads * kU) {
+    uint4 t[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t k = k0 + (int64_t)u * kQThreads;
+      t[u] = xv[k < nv ? k : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) m = absmax8(m, t[u]);
+  }
   const uint32_t bits = block_max_u32<kQThreads>(absmax_bits(m));
   if (threadIdx.x == 0) {
     job.rec->_part[0] = bits;
