@@ -101,6 +101,10 @@ __device__ __forceinline__ void store_block_amax(const QuantJob& job, int lb, ui
       job.rec->_part[lb] = bits;
       if (lb == 0) job.rec->_nparts = (uint32_t)job.nblocks;
     }
+    // as the amax kernel: the slots past the block count read as zero
+    if (lb == 0)
+      for (int i = job.nblocks + (int)threadIdx.x; i < FP8SG_AMAX_PARTS; i += kQThreads)
+        job.rec->_part[i] = 0;
   }
 }
 
@@ -313,14 +317,18 @@ __global__ __launch_bounds__(kQThreads) void k_quant_elem(QuantArgs args) {
 // oldest entry drops out.  One block per job.
 __global__ __launch_bounds__(kQThreads) void k_hist_push(QuantArgs args) {
   const QuantJob& job = args.job[blockIdx.x];
-  const float a = amax_from_partials<kQThreads>(job.rec);
+  // all partial slots and the history entries are loaded together (an index
+  // past the history rereads entry 0; such values are never written back)
+  PartialLoads<kQThreads> parts;
+  parts.issue(job.rec);
   constexpr int kMaxPer = FP8SG_MAX_HISTORY / kQThreads;
   float old[kMaxPer];
 #pragma unroll
   for (int k = 0; k < kMaxPer; ++k) {
     const int i = threadIdx.x + k * kQThreads;
-    old[k] = i < job.hist_len ? job.hist[i] : 0.0f;
+    old[k] = job.hist[i < job.hist_len ? i : 0];
   }
+  const float a = parts.reduce();
   __syncthreads();  // every entry read before any is overwritten
 #pragma unroll
   for (int k = 0; k < kMaxPer; ++k) {

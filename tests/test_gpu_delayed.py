@@ -156,3 +156,26 @@ def test_delayed_at_the_quantize_workload_size():
     torch.cuda.synchronize()
     ref = O.to_fp8_delayed(x, O.E4M3FN, hist_h, with_transpose=False)
     check_step(rec, hist, q, None, ref, O.E4M3FN, "2^28")
+
+
+@pytest.mark.parametrize("transposed", [True, False])
+def test_delayed_record_reused_after_a_larger_tensor(transposed):
+    """A record whose partial slots a larger tensor filled (all 1024, large
+    amax), then delayed casts of small tensors (a few slots): the amax pushed
+    to the history takes every slot, so the ones past the small cast's block
+    count must not keep the large tensor's maxima."""
+    rec = F.ScaleRec(device=DEV)
+    big = W.normal_bf16(41, 0, (4096, 2048), 1.0, 0.002, 500.0)
+    F.fp8_amax(dev16(big).reshape(big.shape), rec)
+    shape = (272, 144)
+    hist_h = np.full(4, 0.5, np.float32)
+    hist = torch.from_numpy(hist_h.copy()).to(DEV)
+    q = torch.empty(shape, dtype=torch.uint8, device=DEV)
+    qT = torch.empty(shape[::-1], dtype=torch.uint8, device=DEV) if transposed else None
+    for t in range(3):
+        x = W.normal_bf16(41, t + 1, shape, 0.01)
+        F.fp8_quantize_delayed(dev16(x).reshape(shape), O.E4M3FN, rec, hist, q, qT)
+        torch.cuda.synchronize()
+        ref = O.to_fp8_delayed(x, O.E4M3FN, hist_h, with_transpose=transposed)
+        check_step(rec, hist, q, qT, ref, O.E4M3FN, f"reused record, step {t}")
+        hist_h = ref.hist
