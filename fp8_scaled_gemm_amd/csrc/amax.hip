@@ -78,7 +78,9 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(AmaxArgs args) {
 // Standalone amax: publish rec->amax from the partial maxima (one block per job).
 __global__ __launch_bounds__(kAmaxThreads) void k_amax_finalize(AmaxArgs args) {
   fp8sg_scale_rec* rec = args.job[blockIdx.x].rec;
-  const float a = amax_from_partials<kAmaxThreads>(rec);
+  PartialLoads<kAmaxThreads> parts;  // every slot at once (unused ones are zero)
+  parts.issue(rec);
+  const float a = parts.reduce();
   if (threadIdx.x == 0) rec->amax = a;
 }
 
