@@ -27,7 +27,8 @@ EXPORTS = ("fp8sg_status_string", "fp8sg_version", "amp_norm_workspace_len", "fp
            "amp_unscale_check", "amp_unscale_check_norm", "amp_update_scale",
            "fp8_quantize_rowwise", "fp8_gemm_rowwise", "fp8_scaled_linear_fwd_rowwise",
            "fp8_scaled_linear_bwd_rowwise", "fp8_scaled_linear_bwd_unscale", "fp8_gemm_unscale",
-           "fp8_scaled_linear_bwd_delayed_unscale", "fp8_scaled_linear_bwd_rowwise_unscale")
+           "fp8_scaled_linear_bwd_delayed_unscale", "fp8_scaled_linear_bwd_rowwise_unscale",
+           "fp8_quantize_from_amax")
 MAX_HISTORY = 1024
 MAX_DIM = 1 << 29     # largest matrix dimension an entry point takes
 MAX_ELEMS = 1 << 35   # largest tensor, in elements
@@ -77,6 +78,7 @@ def lib():
     L.fp8_amax.argtypes = [P, i64, P, P]
     L.fp8_quantize.argtypes = [P, i64, i64, i, P, P, P, P]
     L.fp8_quantize_delayed.argtypes = [P, i64, i64, i, P, i32, P, P, P, P]
+    L.fp8_quantize_from_amax.argtypes = [P, i64, i64, i, P, P, P, P, P]
     L.fp8_gemm.argtypes = [P, i, P, i, P, P, P, i, i64, i64, i64, P]
     L.fp8_scaled_linear_fwd.argtypes = [P, P, i64, i64, i64, ctypes.POINTER(_Saved), P, i, P]
     L.fp8_scaled_linear_bwd.argtypes = [P, ctypes.POINTER(_Saved), i64, i64, i64,
@@ -231,6 +233,17 @@ def fp8_quantize(x: torch.Tensor, fmt: int, rec: ScaleRec, q: torch.Tensor,
     rows, cols = _quant_args(x, rec, q, qT)
     _check(lib().fp8_quantize(_ptr(x), rows, cols, fmt, _ptr(rec.buf), _ptr(q),
                               _ptr(qT), _stream(stream)), "fp8_quantize")
+
+
+def fp8_quantize_from_amax(x: torch.Tensor, fmt: int, amax: torch.Tensor, rec: ScaleRec,
+                           q: torch.Tensor, qT: torch.Tensor = None, stream=None):
+    """Scale from the caller's amax (a one-element device float32 tensor), then
+    codes q (= x's shape) and optionally qT; rec receives amax and the scales."""
+    rows, cols = _quant_args(x, rec, q, qT)
+    _need(amax, "amax", torch.float32, numel=1)
+    _check(lib().fp8_quantize_from_amax(_ptr(x), rows, cols, fmt, _ptr(amax), _ptr(rec.buf),
+                                        _ptr(q), _ptr(qT), _stream(stream)),
+           "fp8_quantize_from_amax")
 
 
 def _quant_args(x, rec, q, qT):

@@ -104,6 +104,22 @@ fp8sg_status fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, fp8sg_f
   return hip_status(launch_quantize(a, fmt, S(stream)));
 }
 
+fp8sg_status fp8_quantize_from_amax(const uint16_t* x, int64_t rows, int64_t cols,
+                                    fp8sg_format fmt, const float* amax, fp8sg_scale_rec* rec,
+                                    uint8_t* q, uint8_t* qT, fp8sg_stream stream) {
+  if (!rec || !amax) return FP8SG_ERR_NULL;
+  if (!fmt_ok(fmt)) return FP8SG_ERR_FORMAT;
+  if (!elems_ok(rows, cols)) return FP8SG_ERR_SHAPE;
+  if (rows * cols > 0 && (!x || !q)) return FP8SG_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || (qT && !aligned16(qT)) || !aligned(rec, 8) ||
+      !aligned(amax, 4))
+    return FP8SG_ERR_ALIGN;
+  QuantArgs a{};
+  a.job[0] = QuantJob{x, rows, cols, rec, q, qT, 0, 0, 0, nullptr, 0, amax};
+  a.njobs = 1;
+  return hip_status(launch_quantize(a, fmt, S(stream)));
+}
+
 fp8sg_status fp8_quantize_delayed(const uint16_t* x, int64_t rows, int64_t cols,
                                   fp8sg_format fmt, float* amax_history, int32_t history_len,
                                   fp8sg_scale_rec* rec, uint8_t* q, uint8_t* qT,

@@ -510,19 +510,21 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
     if (grp == 0) wait_vmcnt<0>();  // A of t + 1 has landed
     barrier();
   };
-  for (int t = 0;;) {
+  // the launcher sends Kc == 0 to the small kernel; the guard keeps an empty
+  // contraction from entering the loop whatever the caller
+  for (int t = 0; t < nk;) {
     step(std::integral_constant<int, 0>{}, t);
-    if (++t == nk) break;
+    if (++t >= nk) break;
     step(std::integral_constant<int, 1>{}, t);
-    if (++t == nk) break;
+    if (++t >= nk) break;
     step(std::integral_constant<int, 2>{}, t);
-    if (++t == nk) break;
+    if (++t >= nk) break;
     step(std::integral_constant<int, 3>{}, t);
-    if (++t == nk) break;
+    if (++t >= nk) break;
     step(std::integral_constant<int, 4>{}, t);
-    if (++t == nk) break;
+    if (++t >= nk) break;
     step(std::integral_constant<int, 5>{}, t);
-    if (++t == nk) break;
+    ++t;
   }
   if (grp == 0) barrier();
 
@@ -615,7 +617,8 @@ static hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
   // 256 x 256 tiles once there are enough of them to fill the chip; the
   // per-block buffer descriptors address a 256-row panel with 32-bit offsets
   const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (big >= 128 && p.K * 256 < (1ll << 31)) return launch_pingpong<FA, FB, OUT, RW>(p, stream);
+  if (big >= 128 && p.K > 0 && p.K * 256 < (1ll << 31))
+    return launch_pingpong<FA, FB, OUT, RW>(p, stream);
   return launch_cfg<128, 128, 2, 2, FA, FB, OUT, RW>(p, stream);
 }
 
@@ -624,7 +627,7 @@ static hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
 template <int FA, int FB, int OUT, bool RW>
 static hipError_t launch_tiles_pair(const GemmProblem& p0, const GemmProblem& p1, hipStream_t stream) {
   auto big = [](const GemmProblem& p) {
-    return ((p.M + 255) / 256) * ((p.N + 255) / 256) >= 128 && p.K * 256 < (1ll << 31);
+    return ((p.M + 255) / 256) * ((p.N + 255) / 256) >= 128 && p.K > 0 && p.K * 256 < (1ll << 31);
   };
   if (big(p0) || big(p1)) {
     hipError_t e = p0.M && p0.N ? launch_tiles<FA, FB, OUT, RW>(p0, stream) : hipSuccess;

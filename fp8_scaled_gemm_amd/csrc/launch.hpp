@@ -42,6 +42,7 @@ struct QuantJob {
   int32_t tiles_c;  // tiled path: tiles along cols
   float* hist;      // delayed scaling: amax history (most recent first), or null
   int32_t hist_len;
+  const float* amax_in;  // the caller's amax (device fp32), or null; never with hist
 };
 struct QuantArgs {
   QuantJob job[kMaxQuantJobs];

@@ -54,11 +54,24 @@ __device__ __forceinline__ void write_scale_fields(fp8sg_scale_rec* rec, float a
   rec->inv32 = v.inv32;
 }
 
-// The scale of a job: from the amax kernel's partials, or (DELAYED) from the
-// largest entry of the job's amax history.
-template <bool DELAYED>
+// Where a job's scale comes from: the amax kernel's partials in its record,
+// the largest entry of its amax history (delayed scaling), or an amax the
+// caller supplies in device memory (taken as one history entry: NaN stays
+// NaN, a negative value counts as 0).
+enum ScaleSrc { kSrcParts = 0, kSrcHist = 1, kSrcGiven = 2 };
+// The scale source's loads, issued ahead of the first tile's loads.
+template <int SRC>
+__device__ __forceinline__ const float* src_entries(const QuantJob& job, int32_t& n) {
+  n = SRC == kSrcHist ? job.hist_len : 1;
+  return SRC == kSrcHist ? job.hist : job.amax_in;
+}
+
+// The scale of a job: from the amax kernel's partials, the history or the
+// caller's amax.
+template <int SRC>
 __device__ __forceinline__ float job_amax(const QuantJob& job) {
-  if constexpr (DELAYED) return hist_amax<kQThreads>(job.hist, job.hist_len);
+  if constexpr (SRC == kSrcHist) return hist_amax<kQThreads>(job.hist, job.hist_len);
+  else if constexpr (SRC == kSrcGiven) return hist_amax<kQThreads>(job.amax_in, 1);
   else return amax_from_partials<kQThreads>(job.rec);
 }
 
@@ -122,9 +135,10 @@ __device__ __forceinline__ void publish_scale(fp8sg_scale_rec* rec, float amax, 
   }
 }
 
-template <int FMT, bool S, bool DELAYED, bool SELF = false>
+template <int FMT, bool S, int SRC, bool SELF = false>
 __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
-  constexpr bool kParts = !DELAYED && !SELF;  // scale from the amax kernel's partials
+  constexpr bool DELAYED = SRC == kSrcHist;
+  constexpr bool kParts = SRC == kSrcParts && !SELF;  // scale from the amax kernel's partials
   int lb;
   const QuantJob& job = pick_job(args, lb);
   const int tid = threadIdx.x;
@@ -170,9 +184,11 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
     parts.issue(job.rec);
     load(has_tile ? t0 : 0);
     amax = parts.reduce();
-  } else if constexpr (DELAYED) {
+  } else if constexpr (SRC != kSrcParts) {
+    int32_t ne;
+    const float* src = src_entries<SRC>(job, ne);
     HistLoads<kQThreads> hl;
-    hl.issue(job.hist, job.hist_len);
+    hl.issue(src, ne);
     load(has_tile ? t0 : 0);
     amax = hl.reduce();
   } else {
@@ -229,12 +245,13 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
 // (up to kFlatMaxBlocks blocks; 2^28 elements at 6.5 TB/s against 6.1 with
 // 4096 striding blocks); delayed scaling has at most FP8SG_AMAX_PARTS blocks,
 // which stride with 8 loads in flight per thread.
-template <bool DELAYED>
-constexpr int flat_unroll() { return DELAYED ? 8 : 4; }
+template <int SRC>
+constexpr int flat_unroll() { return SRC == kSrcHist ? 8 : 4; }
 constexpr int64_t kFlatMaxBlocks = 65536;
 
-template <int FMT, bool S, bool DELAYED>
+template <int FMT, bool S, int SRC>
 __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
+  constexpr bool DELAYED = SRC == kSrcHist;
   int lb;
   const QuantJob& job = pick_job(args, lb);
   const int tid = threadIdx.x;
@@ -246,7 +263,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
   const uint4* const xv = reinterpret_cast<const uint4*>(
       nvec > 0 ? static_cast<const void*>(job.x) : static_cast<const void*>(job.rec));
   uint2* qv = reinterpret_cast<uint2*>(job.q);
-  constexpr int kFlatUnroll = flat_unroll<DELAYED>();
+  constexpr int kFlatUnroll = flat_unroll<SRC>();
   const int64_t step = (int64_t)job.nblocks * kQThreads * kFlatUnroll;
   uint4 v[kFlatUnroll];
   // branch-free as in the tiled kernel: past the end a lane loads vector 0
@@ -261,14 +278,16 @@ __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
   // as in the tiled kernel: partials, then the first loads, then the scale
   const int64_t base0 = (int64_t)lb * kQThreads * kFlatUnroll + tid;
   float amax;
-  if constexpr (!DELAYED) {
+  if constexpr (SRC == kSrcParts) {
     PartialLoads<kQThreads> parts;
     parts.issue(job.rec);
     load(base0);
     amax = parts.reduce();
   } else {
+    int32_t ne;
+    const float* src = src_entries<SRC>(job, ne);
     HistLoads<kQThreads> hl;
-    hl.issue(job.hist, job.hist_len);
+    hl.issue(src, ne);
     load(base0);
     amax = hl.reduce();
   }
@@ -292,12 +311,13 @@ __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
 }
 
 // Transposed copy of a shape the tiled kernel does not take: one thread per element.
-template <int FMT, bool DELAYED>
+template <int FMT, int SRC>
 __global__ __launch_bounds__(kQThreads) void k_quant_elem(QuantArgs args) {
+  constexpr bool DELAYED = SRC == kSrcHist;
   int lb;
   const QuantJob& job = pick_job(args, lb);
   const int tid = threadIdx.x;
-  const float amax = job_amax<DELAYED>(job);
+  const float amax = job_amax<SRC>(job);
   const ScaleVals sv = scale_from_amax(amax, FMT);
   if (lb == 0 && tid == 0) publish_scale<DELAYED>(job.rec, amax, sv);
   uint32_t am = 0;
@@ -358,7 +378,7 @@ static int blocks_of(QuantJob& j, QuantPath p) {
     b = tr * tc;
     if (b > (1 << 20)) b = 1 << 20;  // the blocks stride over the tiles
   } else if (p == kPathFlat) {
-    const int64_t per = (int64_t)kQThreads * (j.hist ? flat_unroll<true>() : flat_unroll<false>());
+    const int64_t per = (int64_t)kQThreads * (j.hist ? flat_unroll<kSrcHist>() : flat_unroll<kSrcParts>());
     b = ((n >> 3) + per - 1) / per;
     if (b > kFlatMaxBlocks) b = kFlatMaxBlocks;
   } else {
@@ -369,8 +389,9 @@ static int blocks_of(QuantJob& j, QuantPath p) {
   return (int)(b < 1 ? 1 : b);  // one block at least: it writes the scale fields
 }
 
-template <int FMT, bool DELAYED>
+template <int FMT, int SRC>
 static hipError_t launch_fmt(QuantArgs a, hipStream_t stream, bool self = false) {
+  constexpr bool DELAYED = SRC == kSrcHist;
   // jobs of one launch must take the same path; otherwise split into launches
   for (int j0 = 0; j0 < a.njobs;) {
     const QuantPath p = path_of(a.job[j0]);
@@ -388,18 +409,18 @@ static hipError_t launch_fmt(QuantArgs a, hipStream_t stream, bool self = false)
       sub.job[sub.njobs++] = jb;
     }
     const bool st = bytes >= kStreamBytes;
-    if (self && p == kPathTiled && !DELAYED)
-      hipLaunchKernelGGL((k_quant_tiled<FMT, false, false, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
+    if (self && p == kPathTiled && SRC == kSrcParts)
+      hipLaunchKernelGGL((k_quant_tiled<FMT, false, kSrcParts, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathTiled && st)
-      hipLaunchKernelGGL((k_quant_tiled<FMT, true, DELAYED>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_tiled<FMT, true, SRC>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathTiled)
-      hipLaunchKernelGGL((k_quant_tiled<FMT, false, DELAYED>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_tiled<FMT, false, SRC>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathFlat && st)
-      hipLaunchKernelGGL((k_quant_flat<FMT, true, DELAYED>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_flat<FMT, true, SRC>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathFlat)
-      hipLaunchKernelGGL((k_quant_flat<FMT, false, DELAYED>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_flat<FMT, false, SRC>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else
-      hipLaunchKernelGGL((k_quant_elem<FMT, DELAYED>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_elem<FMT, SRC>), dim3(total), dim3(kQThreads), 0, stream, sub);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (DELAYED) {
@@ -421,19 +442,23 @@ bool self_cast_fits(const QuantArgs& a) {
 }
 
 hipError_t launch_quantize_self(QuantArgs args, int fmt, hipStream_t stream) {
-  return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN, false>(args, stream, true)
-                             : launch_fmt<FP8SG_E5M2, false>(args, stream, true);
+  return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN, kSrcParts>(args, stream, true)
+                             : launch_fmt<FP8SG_E5M2, kSrcParts>(args, stream, true);
 }
 
 hipError_t launch_quantize(QuantArgs args, int fmt, hipStream_t stream) {
-  // delayed and dynamic jobs are never mixed in one call (the entry points
-  // build the job lists)
+  // jobs with different scale sources are never mixed in one call (the entry
+  // points build the job lists)
   const bool delayed = args.njobs > 0 && args.job[0].hist;
+  const bool given = args.njobs > 0 && args.job[0].amax_in;
   if (delayed)
-    return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN, true>(args, stream)
-                               : launch_fmt<FP8SG_E5M2, true>(args, stream);
-  return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN, false>(args, stream)
-                             : launch_fmt<FP8SG_E5M2, false>(args, stream);
+    return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN, kSrcHist>(args, stream)
+                               : launch_fmt<FP8SG_E5M2, kSrcHist>(args, stream);
+  if (given)
+    return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN, kSrcGiven>(args, stream)
+                               : launch_fmt<FP8SG_E5M2, kSrcGiven>(args, stream);
+  return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN, kSrcParts>(args, stream)
+                             : launch_fmt<FP8SG_E5M2, kSrcParts>(args, stream);
 }
 
 }  // namespace fp8sg

@@ -125,9 +125,12 @@ FP8SG_API fp8sg_status fp8_amax(const uint16_t* x, int64_t n, fp8sg_scale_rec* r
  * e5m2 for gradients), §4 (the transposed copy the backward GEMMs need)].
  *   x:    rows x cols bf16, row-major (device, 16-byte aligned).
  *   fmt:  FP8SG_E4M3FN or FP8SG_E5M2.
- *   rec:  scale record filled by fp8_amax on the same tensor; this call
- *         reduces its partial maxima and writes amax, scale, inv, scale32 and
- *         inv32.
+ *   rec:  scale record filled by fp8_amax on this same tensor x, with no other
+ *         call on rec in between; this call reduces the partial maxima fp8_amax
+ *         left there and writes amax, scale, inv, scale32 and inv32.  The
+ *         partials are the only input the scale is taken from: a record
+ *         reduced over another tensor gives that tensor's scale, without an
+ *         error.  A caller holding the amax itself uses fp8_quantize_from_amax.
  *   q:    rows x cols codes, row-major (device, 16-byte aligned).
  *   qT:   cols x rows codes = transpose of q (device, 16-byte aligned), or
  *         NULL to skip the transposed copy.
@@ -139,6 +142,24 @@ FP8SG_API fp8sg_status fp8_amax(const uint16_t* x, int64_t n, fp8sg_scale_rec* r
  */
 FP8SG_API fp8sg_status fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, fp8sg_format fmt,
                           fp8sg_scale_rec* rec, uint8_t* q, uint8_t* qT, fp8sg_stream stream);
+
+/*
+ * fp8_quantize with the amax supplied by the caller [FP8-TRAIN §2: the scale
+ * is fp8_max / amax in fp64, then x * scale, clamp, cast].  The scale, inverse
+ * and codes are those fp8_quantize computes from a record whose amax is *amax;
+ * nothing is read from rec before it is written, so rec needs no fp8_amax.
+ * This is the call for an amax that was combined outside this tensor: the
+ * maximum over the shards of a tensor split across devices (a MAX all-reduce of
+ * the shards' fp8_amax results) or an amax the caller tracks itself.
+ *   amax: device float (4-byte aligned), read on `stream`.  NaN gives the NaN
+ *         scale; a negative value counts as 0.  rec->amax receives the value
+ *         used (canonical NaN, or +0 for a negative input).
+ *   rec:  scale record (device): amax, scale, inv, scale32 and inv32 written.
+ * The other arguments, layouts and the transposed copy as fp8_quantize.
+ */
+FP8SG_API fp8sg_status fp8_quantize_from_amax(const uint16_t* x, int64_t rows, int64_t cols,
+                                    fp8sg_format fmt, const float* amax, fp8sg_scale_rec* rec,
+                                    uint8_t* q, uint8_t* qT, fp8sg_stream stream);
 
 /*
  * Scaled FP8 GEMM [FP8-TRAIN §2, §4; AMP-MP "不要忘记 Accumulator Precision"]:

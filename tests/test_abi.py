@@ -95,6 +95,15 @@ def test_linear_and_quant_validation():
     assert L.fp8_quantize(P(A16), 4, 4, 3, P(A16), P(A16), P(0), P(0)) == EFORMAT
     assert L.fp8_quantize(P(A16), -1, 4, 0, P(A16), P(A16), P(0), P(0)) == ESHAPE
     assert L.fp8_quantize(P(A16), 4, 4, 0, P(A16), P(A16), P(MIS), P(0)) == EALIGN
+    qa = L.fp8_quantize_from_amax
+    assert qa(P(A16), 4, 4, 0, P(0), P(A16), P(A16), P(0), P(0)) == ENULL       # no amax
+    assert qa(P(A16), 4, 4, 0, P(A16), P(0), P(A16), P(0), P(0)) == ENULL       # no record
+    assert qa(P(0), 4, 4, 0, P(A16), P(A16), P(A16), P(0), P(0)) == ENULL       # no x
+    assert qa(P(A16), 4, 4, 2, P(A16), P(A16), P(A16), P(0), P(0)) == EFORMAT
+    assert qa(P(A16), -4, 4, 0, P(A16), P(A16), P(A16), P(0), P(0)) == ESHAPE
+    assert qa(P(A16), 4, 4, 0, P(A16 + 2), P(A16), P(A16), P(0), P(0)) == EALIGN  # amax 4-byte
+    assert qa(P(A16), 4, 4, 0, P(A16), P(A16 + 4), P(A16), P(0), P(0)) == EALIGN  # record 8-byte
+    assert qa(P(A16), 4, 4, 0, P(A16), P(A16), P(A16), P(MIS), P(0)) == EALIGN   # qT 16-byte
     assert L.fp8_amax(P(0), 4, P(A16), P(0)) == ENULL
     assert L.fp8_amax(P(A16), -4, P(A16), P(0)) == ESHAPE
     assert L.fp8_amax(P(MIS), 4, P(A16), P(0)) == EALIGN

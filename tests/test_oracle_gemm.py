@@ -20,6 +20,90 @@ UNIT = {O.E4M3FN: 9, O.E5M2: 16}  # value = integer * 2^-UNIT
 U = 2.0 ** -24
 
 
+def round_binary(x: Fraction, p: int, emin: int) -> Fraction:
+    """x rounded to the nearest binary floating-point number with p significant
+    bits and smallest normal exponent emin, ties to even (IEEE 754
+    roundTiesToEven; no overflow handling: the values here stay in range)."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    assert Fraction(2) ** e <= a < Fraction(2) ** (e + 1)
+    ulp = Fraction(2) ** (max(e, emin) - (p - 1))
+    q, r = divmod(a, ulp)
+    if r * 2 > ulp or (r * 2 == ulp and q % 2 == 1):
+        q += 1
+    return sign * q * ulp
+
+
+def fl64(x: Fraction) -> Fraction:
+    return round_binary(x, 53, -1022)
+
+
+def fl32(x: Fraction) -> Fraction:
+    return round_binary(x, 24, -126)
+
+
+def alpha_reading(inv_a: float, inv_b: float) -> float:
+    """The epilogue factor as read from FP8-TRAIN §2 (dequantise by the product of
+    the two inverse scales): the fp64 product of the two fp64 inverses, rounded
+    to fp32 -- here from the exact rational product, two roundings by hand."""
+    return float(fl32(fl64(Fraction(inv_a) * Fraction(inv_b))))
+
+
+def test_round_binary_against_hardware_casts():
+    # the hand rounding agrees with numpy's IEEE casts on random doubles
+    rng = np.random.default_rng(17)
+    for v in np.exp(rng.uniform(-60.0, 60.0, 2000)) * rng.choice([-1.0, 1.0], 2000):
+        assert float(fl32(Fraction(float(v)))) == float(np.float32(v))
+    for a, b in rng.uniform(-1e3, 1e3, (500, 2)):
+        assert float(fl64(Fraction(float(a)) * Fraction(float(b)))) == float(a) * float(b)
+
+
+def inverse_pairs(n, seed):
+    """Inverse scales as the quantizer makes them, inv = 1 / (fp8_max / amax),
+    from amax values across the workloads' range."""
+    rng = np.random.default_rng(seed)
+    amax = np.exp(rng.uniform(np.log(1e-6), np.log(1e4), (n, 2)))
+    fmax = np.array([448.0, 57344.0])
+    return 1.0 / (fmax / amax)
+
+
+def test_gemm_alpha_is_rounded_fp64_product():
+    """orc_gemm_alpha = fl32(fl64(inv_a * inv_b)), checked against exact rational
+    arithmetic on pairs where the other plausible reading, fl32(fl32(inv_a) *
+    fl32(inv_b)) (rounding each inverse to fp32 first), gives a different value:
+    a swapped rounding order fails here."""
+    differ = 0
+    for inv_a, inv_b in inverse_pairs(4000, 23):
+        inv_a, inv_b = float(inv_a), float(inv_b)
+        ref = alpha_reading(inv_a, inv_b)
+        assert float(O.gemm_alpha(inv_a, inv_b)) == ref, (inv_a, inv_b)
+        alt = float(fl32(fl32(Fraction(inv_a)) * fl32(Fraction(inv_b))))
+        differ += alt != ref
+        # the single correct rounding of the exact product: the same value
+        # unless the fp64 step lands on an fp32 midpoint (never for these pairs)
+        assert float(fl32(Fraction(inv_a) * Fraction(inv_b))) == ref
+    assert differ > 500  # the pin separates the readings on many pairs
+
+
+def test_gemm_alpha_double_rounding_case():
+    """A product whose fp64 rounding lands exactly on an fp32 midpoint: the exact
+    product of these two doubles lies just above 1 + 2^-24, the midpoint between
+    1 and 1 + 2^-23, and within half an fp64 ulp of it, so its fp64 rounding is
+    the midpoint and ties to even give 1.0; rounding the exact product once would
+    give 1 + 2^-23.  The reading (fp64 product, then fp32) decides this case."""
+    a, b = 1.3184808436607272, 0.7584486831285095
+    mid = Fraction(1) + Fraction(1, 2 ** 24)
+    exact = Fraction(a) * Fraction(b)
+    assert mid < exact < mid + Fraction(1, 2 ** 53)
+    assert float(O.gemm_alpha(a, b)) == alpha_reading(a, b) == 1.0
+    assert float(fl32(exact)) == 1.0 + 2.0 ** -23
+
+
 def int_codes(fmt, codes):
     """Exact integer numerators of the codes' values (finite codes only)."""
     v = O.decode(fmt, codes)
@@ -45,9 +129,11 @@ def test_gemm_exact_integer_bound(fa, fb, M, N, K):
     rng = np.random.default_rng(M * 1000 + K)
     A = random_codes(rng, fa, (M, K))
     B = random_codes(rng, fb, (N, K))
-    inv_a, inv_b = 0.37, 2.0 ** -5
+    # inverses that are not powers of two, so the epilogue factor's rounding
+    # matters; alpha comes from exact arithmetic, not from the oracle
+    inv_a, inv_b = 0.37, 1.0 / (448.0 / 3.3)
     C = O.gemm(A, fa, B, fb, inv_a, inv_b)
-    alpha = float(O.gemm_alpha(inv_a, inv_b))
+    alpha = alpha_reading(inv_a, inv_b)
     ia, ib = int_codes(fa, A), int_codes(fb, B)
     den = 2 ** (UNIT[fa] + UNIT[fb])
     gam = K * U / (1 - K * U)
