@@ -510,9 +510,12 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
     if (grp == 0) wait_vmcnt<0>();  // A of t + 1 has landed
     barrier();
   };
-  // the launcher sends Kc == 0 to the small kernel; the guard keeps an empty
-  // contraction from entering the loop whatever the caller
-  for (int t = 0; t < nk;) {
+  // The launcher sends Kc == 0 to the small kernel.  Should an empty
+  // contraction arrive here anyway, the >= test ends the loop after one step
+  // over k-tile 0, whose loads all lie past K and read as zeros.  (This loop
+  // shape keeps the accumulators in registers; a test at the top of the loop,
+  // or a branch around it, made the compiler spill them.)
+  for (int t = 0;;) {
     step(std::integral_constant<int, 0>{}, t);
     if (++t >= nk) break;
     step(std::integral_constant<int, 1>{}, t);
@@ -524,7 +527,7 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
     step(std::integral_constant<int, 4>{}, t);
     if (++t >= nk) break;
     step(std::integral_constant<int, 5>{}, t);
-    ++t;
+    if (++t >= nk) break;
   }
   if (grp == 0) barrier();
 
