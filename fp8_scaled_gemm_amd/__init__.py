@@ -28,7 +28,7 @@ EXPORTS = ("fp8sg_status_string", "fp8sg_version", "amp_norm_workspace_len", "fp
            "fp8_quantize_rowwise", "fp8_gemm_rowwise", "fp8_scaled_linear_fwd_rowwise",
            "fp8_scaled_linear_bwd_rowwise", "fp8_scaled_linear_bwd_unscale", "fp8_gemm_unscale",
            "fp8_scaled_linear_bwd_delayed_unscale", "fp8_scaled_linear_bwd_rowwise_unscale",
-           "fp8_quantize_from_amax")
+           "fp8_quantize_from_amax", "amp_unscale_check_norm_noalloc")
 MAX_HISTORY = 1024
 MAX_DIM = 1 << 29     # largest matrix dimension an entry point takes
 MAX_ELEMS = 1 << 35   # largest tensor, in elements
@@ -91,6 +91,8 @@ def lib():
     L.amp_update_scale.argtypes = [P, P, P, f32, f32, i32, P]
     L.amp_norm_workspace_len.argtypes = [ctypes.POINTER(i64), i32]
     L.amp_norm_workspace_len.restype = i64
+    L.amp_unscale_check_norm_noalloc.argtypes = [ctypes.POINTER(P), ctypes.POINTER(i64), i32, P,
+                                                 P, P, P]
     L.amp_unscale_check_norm.argtypes = [ctypes.POINTER(P), ctypes.POINTER(i64), i32, P, P, P, i64,
                                          P, P]
     L.fp8_quantize_rowwise.argtypes = [P, i64, i64, i, P, P, P, P, P, P, P]
@@ -671,6 +673,22 @@ def amp_unscale_check_norm(grads, scale: torch.Tensor, found_inf: torch.Tensor,
     _check(lib().amp_unscale_check_norm(ptrs, numel, n, _ptr(scale), _ptr(found_inf),
                                         _ptr(workspace), workspace.numel(), _ptr(sumsq_norm),
                                         _stream(stream)), "amp_unscale_check_norm")
+
+
+NOALLOC_NORM_SLOTS = 1 << 20  # FP8SG_NOALLOC_NORM_SLOTS
+
+
+def amp_unscale_check_norm_noalloc(grads, scale: torch.Tensor, found_inf: torch.Tensor,
+                                   sumsq_norm: torch.Tensor, stream=None):
+    """amp_unscale_check_norm without a workspace: the library's fixed scratch
+    array (one per GPU) holds the partial sums; nothing is allocated.  Calls
+    that overlap in time on one GPU race."""
+    ptrs, numel, n = _grad_list(grads)
+    _need_scaler(scale, found_inf)
+    _need(sumsq_norm, "sumsq_norm", torch.float32, min_numel=2)
+    _check(lib().amp_unscale_check_norm_noalloc(ptrs, numel, n, _ptr(scale), _ptr(found_inf),
+                                                _ptr(sumsq_norm), _stream(stream)),
+           "amp_unscale_check_norm_noalloc")
 
 
 def amp_update_scale(scale: torch.Tensor, growth_tracker: torch.Tensor, found_inf: torch.Tensor,

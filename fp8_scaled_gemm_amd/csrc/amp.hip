@@ -24,6 +24,8 @@
 // 16-byte load in turn, the thread's 4 load sums in turn, a fixed tree over
 // the block; one slot per block of a caller workspace; two small kernels add
 // the slots in fp64 in a fixed order.  The result is the same on every run.
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -277,6 +279,37 @@ hipError_t launch_unscale_check(uint16_t* const* grads, const int64_t* numel, in
     hipLaunchKernelGGL(k_norm_finalize, dim3(1), dim3(kAmpThreads), 0, stream, part64, sumsq_norm);
     return hipGetLastError();
   }
+  return hipSuccess;
+}
+
+// Scratch of the norm pass for callers that cannot allocate: a fixed device
+// array in place of the caller's workspace, one copy per GPU, held until the
+// process ends.  Its address on a device comes from hipGetSymbolAddress, taken
+// once per device with that device current; host code uses only that address
+// (the array's name in host code is not a device address).  Every slot the
+// pass reads was written earlier in the same call (the per-block slots by the
+// unscale kernel, the fp64 partials by the first sum kernel), so nothing needs
+// clearing between calls; calls that overlap in time on one GPU share it and
+// race.
+static __device__ __align__(256) float scratch[kNoAllocNormSlots];
+
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static float* g_scratch[kMaxScratchDevices] = {};
+
+hipError_t norm_scratch(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch[dev];
   return hipSuccess;
 }
 

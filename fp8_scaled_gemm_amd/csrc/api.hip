@@ -472,6 +472,28 @@ fp8sg_status amp_unscale_check_norm(uint16_t* const* grads, const int64_t* numel
                                          sumsq_norm, S(stream)));
 }
 
+fp8sg_status amp_unscale_check_norm_noalloc(uint16_t* const* grads, const int64_t* numel,
+                                            int32_t ntensors, const float* scale,
+                                            int32_t* found_inf, float* sumsq_norm,
+                                            fp8sg_stream stream) {
+  if (!scale || !found_inf || !sumsq_norm) return FP8SG_ERR_NULL;
+  if (ntensors < 0 || ntensors > 8192) return FP8SG_ERR_SHAPE;
+  if (ntensors > 0 && (!grads || !numel)) return FP8SG_ERR_NULL;
+  if (!aligned(scale, 4) || !aligned(found_inf, 4)) return FP8SG_ERR_ALIGN;
+  for (int32_t i = 0; i < ntensors; ++i) {
+    if (numel[i] < 0 || numel[i] > FP8SG_MAX_ELEMS) return FP8SG_ERR_SHAPE;
+    if (numel[i] > 0 && !grads[i]) return FP8SG_ERR_NULL;
+    if (numel[i] > 0 && (reinterpret_cast<uintptr_t>(grads[i]) & 1u)) return FP8SG_ERR_ALIGN;
+  }
+  if (norm_slots(grads, numel, ntensors) > kNoAllocNormSlots) return FP8SG_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(sumsq_norm) & 3u) return FP8SG_ERR_ALIGN;
+  float* ws = nullptr;
+  const hipError_t e = norm_scratch(&ws);
+  if (e != hipSuccess) return FP8SG_ERR_HIP;
+  return hip_status(launch_unscale_check(grads, numel, ntensors, scale, found_inf, ws,
+                                         sumsq_norm, S(stream)));
+}
+
 fp8sg_status amp_update_scale(float* scale, int32_t* growth_tracker, int32_t* found_inf,
                               float growth_factor, float backoff_factor,
                               int32_t growth_interval, fp8sg_stream stream) {

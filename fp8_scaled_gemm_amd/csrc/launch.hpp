@@ -122,6 +122,11 @@ int64_t unscale_blocks_bound(const int64_t* numel, int32_t ntensors);
 hipError_t launch_unscale_check(uint16_t* const* grads, const int64_t* numel, int32_t ntensors,
                                 const float* scale, int32_t* found_inf, float* parts,
                                 float* sumsq_norm, hipStream_t stream);
+// The norm pass's scratch for amp_unscale_check_norm_noalloc: a static device
+// array of kNoAllocNormSlots floats (4 MiB) per GPU; *out is its address on the
+// current device (looked up once per device).
+constexpr int64_t kNoAllocNormSlots = FP8SG_NOALLOC_NORM_SLOTS;
+hipError_t norm_scratch(float** out);
 hipError_t launch_update_scale(float* scale, int32_t* tracker, int32_t* found_inf, float growth,
                                float backoff, int32_t interval, hipStream_t stream);
 

@@ -479,6 +479,28 @@ FP8SG_API fp8sg_status amp_unscale_check_norm(uint16_t* const* grads, const int6
                                     fp8sg_stream stream);
 
 /*
+ * amp_unscale_check_norm for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight training loops, harnesses that forbid
+ * hipMalloc): the same pass and the same results, bit for bit, with the norm's
+ * per-block partial sums kept in a fixed scratch array inside the library
+ * instead of a caller workspace.  The call allocates nothing.
+ *   The scratch holds FP8SG_NOALLOC_NORM_SLOTS fp32 slots (4 MiB, enough for
+ *   about 8.5e9 gradient elements); a call whose tensors need more slots than
+ *   that (amp_norm_workspace_len) returns FP8SG_ERR_SHAPE before any launch.
+ *   Each GPU the library runs this call on holds its own copy of the array
+ *   until the process ends; it is located on the device current on the
+ *   calling thread, which must be the device of `stream`.
+ *   Calls on one GPU share the array: calls that may overlap in time on one
+ *   GPU (other streams, other threads) race and must be serialised by the
+ *   caller.  Nothing of a previous call's contents is read.
+ * The other arguments and the results as amp_unscale_check_norm.
+ */
+#define FP8SG_NOALLOC_NORM_SLOTS (1LL << 20)
+FP8SG_API fp8sg_status amp_unscale_check_norm_noalloc(uint16_t* const* grads, const int64_t* numel,
+                                    int32_t ntensors, const float* scale, int32_t* found_inf,
+                                    float* sumsq_norm, fp8sg_stream stream);
+
+/*
  * GradScaler.update() [PT-CH20 §20.5.33], on the device:
  *   if *found_inf: *scale *= backoff_factor; *growth_tracker = 0
  *   else: ++*growth_tracker; if it reaches growth_interval:

@@ -58,6 +58,27 @@ def P(v):
     return ctypes.c_void_p(v)
 
 
+def test_noalloc_norm_validation():
+    """amp_unscale_check_norm_noalloc refuses, before any launch, a list that
+    needs more than the scratch's FP8SG_NOALLOC_NORM_SLOTS slots, and bad
+    arguments (fake pointers: validation returns before any use)."""
+    L = F.lib()
+    f = L.amp_unscale_check_norm_noalloc
+    n = 11 * 10 ** 9 // 8  # 8 tensors of 1.375e9 elements: about 1.34e6 blocks
+    ptrs = (ctypes.c_void_p * 8)(*([A16] * 8))
+    big = (ctypes.c_int64 * 8)(*([n] * 8))
+    assert f(ptrs, big, 8, P(A16), P(A16), P(A16), P(0)) == ESHAPE
+    assert F.amp_norm_workspace_len([n] * 8) > F.NOALLOC_NORM_SLOTS
+    one = (ctypes.c_int64 * 1)(1000)
+    assert f(ptrs, one, 1, P(0), P(A16), P(A16), P(0)) == ENULL        # scale
+    assert f(ptrs, one, 1, P(A16), P(A16), P(0), P(0)) == ENULL        # sumsq_norm
+    assert f(ptrs, one, 1, P(A16 + 2), P(A16), P(A16), P(0)) == EALIGN  # scale 4-byte
+    assert f(ptrs, one, 1, P(A16), P(A16), P(A16 + 2), P(0)) == EALIGN  # sumsq_norm 4-byte
+    assert f(ptrs, one, -1, P(A16), P(A16), P(A16), P(0)) == ESHAPE
+    odd = (ctypes.c_void_p * 1)(A16 + 1)
+    assert f(odd, one, 1, P(A16), P(A16), P(A16), P(0)) == EALIGN      # fp16 needs 2-byte
+
+
 def test_gemm_validation():
     L = F.lib()
     g = L.fp8_gemm
