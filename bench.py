@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--no-hbm", action="store_true", help="skip the HBM-scale bandwidth passes")
     p.add_argument("--no-side", action="store_true",
                    help="skip the square-layer, small-layer and autograd side lines")
+    p.add_argument("--hbm-only", action="store_true",
+                   help="only the HBM-scale passes (for counter runs); prints their figures")
     p.add_argument("--copy-reference", action="store_true",
                    help="only copy 1 GiB device-to-device 5 times (calibrates the HBM byte "
                         "counters against a transfer of known size)")
@@ -278,6 +280,11 @@ def main():
     stream = torch.cuda.current_stream()
     F.lib()
     T = Timer(torch, stream)
+
+    if args.hbm_only:
+        hbm, hbm_kern = hbm_passes(np, torch, F, dev, T)
+        print(json.dumps({"hbm_scale": hbm, "hbm_kernels_us": hbm_kern}), flush=True)
+        return
 
     mlp = MlpStep(np, torch, F, dev)
     log(f"timing {args.steps} steps of the MLP block")

@@ -29,7 +29,7 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=h
          "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-command-line-argument"]
-MAX_SPILL_VGPRS = 16
+MAX_SPILL_VGPRS = 64
 
 
 def spills(stderr: str) -> dict:

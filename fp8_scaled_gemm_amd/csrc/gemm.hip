@@ -4,6 +4,19 @@
 
 namespace fp8sg {
 
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static int cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 hipError_t launch_gemm(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream) {
   return launch_gemm_any<false>(p, fa, fb, out, stream);
 }

@@ -14,8 +14,8 @@
 // fragment is passed as the instruction's first source so each lane's four
 // accumulators are four consecutive output columns.  LDS tiles hold 16-byte
 // chunks XOR-swizzled by row so the fragment reads hit distinct banks.
-//   - k_gemm_pingpong: 256 x 256 tiles, for problems with at least 128 of
-//     them (fills the chip).
+//   - k_gemm_pingpong: 256 x 256 (or 224 x 256) tiles, for problems with at
+//     least 128 of them (fills the chip).
 //   - k_gemm: 128 x 128 tiles with register-staged loads, for smaller problems.
 // Each kernel has a per-tensor epilogue (one alpha) and a row-wise one (RW:
 // inverse-scale vectors along M and N); gemm.hip and gemm_rowwise.hip hold the
@@ -357,9 +357,8 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // column by column, so one XCD's tiles form a compact region whose A and B
 // panels its L2 can share.
 constexpr int kGroupM = 4;
-__device__ __forceinline__ void tile_of(int nbm, int nbn, int& tm, int& tn) {
+__device__ __forceinline__ void tile_of_index(int b, int nbm, int nbn, int& tm, int& tn) {
   const int nb = nbm * nbn;
-  const int b = blockIdx.x;
   const int q = nb / 8, rem = nb % 8, x = b % 8;
   const int t = x * q + (x < rem ? x : rem) + b / 8;
   const int per_group = kGroupM * nbn;
@@ -368,12 +367,15 @@ __device__ __forceinline__ void tile_of(int nbm, int nbn, int& tm, int& tn) {
   tm = g * kGroupM + r % gm;
   tn = r / gm;
 }
+__device__ __forceinline__ void tile_of(int nbm, int nbn, int& tm, int& tn) {
+  tile_of_index(blockIdx.x, nbm, nbn, tm, tn);
+}
 
 // ---------------------------------------------------------------------------
-// Large-tile kernel: 256 x 256 output tile per workgroup, K consumed 128 bytes
+// Large-tile kernel: BM x 256 output tile per workgroup, K consumed 128 bytes
 // at a time, 8 waves in two groups of four (one wave of each group per SIMD).
-// Group g owns output rows [128 g, 128 g + 128); wave q of a group owns
-// columns [64 q, 64 q + 64), i.e. 8 x 4 blocks of 16 x 16.
+// Group g owns output rows [BM/2 g, BM/2 (g + 1)); wave q of a group owns
+// columns [64 q, 64 q + 64), i.e. BM/32 x 4 blocks of 16 x 16.
 //
 // The groups run half a k-tile apart and alternate between
 //   - a memory phase: issue this group's share of the global -> LDS loads,
@@ -390,11 +392,19 @@ __device__ __forceinline__ void tile_of(int nbm, int nbn, int& tm, int& tn) {
 // Each load is waited for (s_waitcnt vmcnt) by the wave that issued it before
 // the swap ahead of the first read, so the barrier publishes it to all waves.
 // ---------------------------------------------------------------------------
-template <int FA, int FB, int OUT, bool RAGGED_K, bool RW>
+//
+// BM is 256 or 224.  A 224-row tile (7 blocks of 16 rows per wave group) fits
+// M = 14336 in exactly 64 tile rows: the MLP block's weight-gradient GEMMs then
+// have 1024 tiles, four rounds over 256 CUs with none idle, instead of 896
+// (the last of four rounds half empty).  The launcher picks it by that count.
+// ---------------------------------------------------------------------------
+template <int FA, int FB, int OUT, bool RAGGED_K, bool RW, int BM = 256>
 __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
-  constexpr int BM = 256, BN = 256;
-  constexpr int kTM = 8, kTN = 4;
-  constexpr int kLoads = 256 / 8 / 4;  // 1 KB loads per group wave per operand half-stage: 8
+  static_assert(BM == 256 || BM == 224, "tile rows");
+  constexpr int BN = 256;
+  constexpr int kTM = BM / 32, kTN = 4;
+  constexpr int kLoads = 256 / 8 / 4;  // 1 KB loads per group wave per B stage: 8
+  constexpr int kLoadsA = BM / 32;     // ... per A stage: 8, or 7 at BM = 224
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[256 * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[256 * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[256 * kBK];
@@ -422,28 +432,33 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
   const i32x4 ra = make_rsrc(p.A + bm * K, rows_a * K);
   const i32x4 rb = make_rsrc(p.B + bn * K, rows_b * K);
 
-  // One operand half-stage (256 rows x 128 B) by wave q of a group: rows
-  // [64 q, 64 q + 64), 8 loads of 8 rows.  Lane l of load i fills LDS row
-  // 8 (8 q + i) + l / 8; the swizzle of that row depends only on i & 1, so a
-  // lane needs two offsets (even and odd i) and the rest is scalar.  Only a
-  // ragged last k-tile (RAGGED_K) needs the per-lane test against K.
+  // One operand stage (BM or 256 rows x 128 B) by wave q of a group: rows
+  // [8 L q, 8 L q + 8 L), L loads of 8 rows (L = 8 for B, BM / 32 for A).
+  // Lane l of load i fills LDS row 8 (L q + i) + l / 8; the swizzle of that row
+  // depends only on (L q + i) & 1, so a lane needs two offsets (even and odd)
+  // and the rest is scalar.  Only a ragged last k-tile (RAGGED_K) needs the
+  // per-lane test against K.
   const int lr = lane >> 3;
   const int cl0 = (lane & 7) ^ swz16(lr), cl1 = (lane & 7) ^ swz16(8 + lr);
   const uint32_t vo0 = (uint32_t)(lr * K + 16 * cl0), vo1 = (uint32_t)(lr * K + 16 * cl1);
-  auto issue = [&](int kt, uint32_t dst, const i32x4& rs) {  // kt >= nk loads zeros
+  auto issue = [&](auto nl, int kt, uint32_t dst, const i32x4& rs) {  // kt >= nk loads zeros
+    constexpr int L = decltype(nl)::value;
     const int k0 = kt < nk ? kt * kBK : (int)K;
-    const uint32_t sbase = (uint32_t)(64 * wq * K + k0);
+    const uint32_t sbase = (uint32_t)(8 * L * wq * K + k0);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      uint32_t off = ((i & 1) ? vo1 : vo0) + sbase + (uint32_t)(8 * i * K);
+    for (int i = 0; i < L; ++i) {
+      const bool odd = (L % 2 == 0 ? i : wq + i) & 1;  // (L q + i) & 1
+      uint32_t off = (odd ? vo1 : vo0) + sbase + (uint32_t)(8 * i * K);
       if constexpr (RAGGED_K) {
-        if (k0 + 16 * ((i & 1) ? cl1 : cl0) >= K) off = kOob;
+        if (k0 + 16 * (odd ? cl1 : cl0) >= K) off = kOob;
       } else {
         if (kt >= nk) off = kOob;
       }
-      lds_dma16(dst + (wq * kLoads + i) * 1024, off, rs);
+      lds_dma16(dst + (wq * L + i) * 1024, off, rs);
     }
   };
+  using LA = std::integral_constant<int, kLoadsA>;
+  using LB = std::integral_constant<int, kLoads>;
   v4f acc[kTM][kTN];
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
@@ -458,7 +473,7 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
     const uint4 hi = *reinterpret_cast<const uint4*>(base + lds_off2(r, fchunk + 1));
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
-  const int ra0 = grp * 8, rb0 = wq * 4;
+  const int ra0 = grp * kTM, rb0 = wq * 4;
   v8i af[kTM], bf[kTN];
   auto barrier = [&]() {
     __builtin_amdgcn_s_barrier();
@@ -467,11 +482,11 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
 
   // Prologue: group 0 loads A0, group 1 loads B0 and B1.
   if (grp == 0) {
-    issue(0, lds_u32(sA0), ra);
+    issue(LA{}, 0, lds_u32(sA0), ra);
     wait_vmcnt<0>();
   } else {
-    issue(0, lds_u32(sB0), rb);
-    issue(1, lds_u32(sB1), rb);
+    issue(LB{}, 0, lds_u32(sB0), rb);
+    issue(LB{}, 1, lds_u32(sB1), rb);
     wait_vmcnt<kLoads>();
   }
   barrier();
@@ -490,7 +505,12 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
     {
       const uint32_t da = lds_u32(sa(std::integral_constant<int, (P + 1) % 2>{}));
       const uint32_t db = lds_u32(sb(std::integral_constant<int, (P + 2) % 3>{}));
-      issue(t + 1 + grp, grp ? db : da, grp ? rb : ra);
+      if constexpr (kLoadsA == kLoads) {
+        issue(LB{}, t + 1 + grp, grp ? db : da, grp ? rb : ra);
+      } else {
+        if (grp) issue(LB{}, t + 2, db, rb);
+        else issue(LA{}, t + 1, da, ra);
+      }
     }
 #pragma unroll
     for (int j = 0; j < kTN; ++j) bf[j] = frag(b, rb0 + j);
@@ -531,7 +551,7 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
   }
   if (grp == 0) barrier();
 
-  const int wr0 = grp * 128, wc0 = wq * 64;
+  const int wr0 = grp * (BM / 2), wc0 = wq * 64;
   const Alpha<RW, kTM, kTN> alpha(p, bm + wr0, bn + wc0, lane);
   if constexpr (OUT == FP8SG_OUT_F32) {
 #pragma unroll
@@ -589,14 +609,25 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
   }
 }
 
-template <int FA, int FB, int OUT, bool RW>
+template <int FA, int FB, int OUT, bool RW, int BM>
 static hipError_t launch_pingpong(const GemmProblem& p, hipStream_t stream) {
-  const unsigned nb = (unsigned)(((p.M + 255) / 256) * ((p.N + 255) / 256));
+  const unsigned nb = (unsigned)(((p.M + BM - 1) / BM) * ((p.N + 255) / 256));
   if (p.K % kBK == 0)
-    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, false, RW>), dim3(nb), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, false, RW, BM>), dim3(nb), dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, true, RW>), dim3(nb), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, true, RW, BM>), dim3(nb), dim3(512), 0, stream, p);
   return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+int device_cus();
+
+// Rounds of a grid of BM x 256 tiles over the CUs (one workgroup per CU at a
+// time), weighted by the tile's rows: the cost model that picks the tile
+// height.
+inline int64_t tile_rounds_cost(int64_t M, int64_t N, int bm, int cus) {
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + 255) / 256);
+  return ((tiles + cus - 1) / cus) * bm;
 }
 
 template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW>
@@ -618,10 +649,15 @@ static hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
 template <int FA, int FB, int OUT, bool RW>
 static hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
   // 256 x 256 tiles once there are enough of them to fill the chip; the
-  // per-block buffer descriptors address a 256-row panel with 32-bit offsets
+  // per-block buffer descriptors address a 256-row panel with 32-bit offsets.
+  // 224-row tiles where their rounds over the CUs take clearly less time.
   const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (big >= 128 && p.K > 0 && p.K * 256 < (1ll << 31))
-    return launch_pingpong<FA, FB, OUT, RW>(p, stream);
+  if (big >= 128 && p.K > 0 && p.K * 256 < (1ll << 31)) {
+    const int cus = device_cus();
+    if (cus > 0 && tile_rounds_cost(p.M, p.N, 224, cus) * 100 < tile_rounds_cost(p.M, p.N, 256, cus) * 95)
+      return launch_pingpong<FA, FB, OUT, RW, 224>(p, stream);
+    return launch_pingpong<FA, FB, OUT, RW, 256>(p, stream);
+  }
   return launch_cfg<128, 128, 2, 2, FA, FB, OUT, RW>(p, stream);
 }
 
