@@ -46,7 +46,8 @@ GEMM_SRC = os.path.join(ROOT, "fp8_scaled_gemm_amd", "csrc", "gemm_kernels.hpp")
 # device-to-device copy (bench.py --copy-reference: FETCH_SIZE x2.0,
 # WRITE_SIZE x1.0).  Valid only for the GEMM kernel source they were taken on
 # (its hash); bench.py reports null for any other.
-GEMM_TRAFFIC = None
+GEMM_TRAFFIC = {"gemm_src_sha256_16": "27fceaac0f51a6d4", "fetch_kib": 353490.3,
+                "write_kib": 136533.3, "fetch_factor": 2.0, "write_factor": 1.0}
 
 
 def parse():
@@ -368,7 +369,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": gemm_traffic(),
-                     "traffic_unit": "HBM bytes per launch (mean over the 9 GEMMs, counter-measured)",
+                     "traffic_unit": "bytes per launch from L2 to the memory fabric (Infinity Cache "
+                                     "or HBM), mean over the 9 GEMMs, counter-measured",
                      "kernel": "k_gemm_pingpong: the step's 9 GEMMs, 2*M*N*K flops each, "
                                "sum of flops / sum of mean launch times"},
         "gemms": {k: {"us": round(v, 2), "TFLOPs": round(gemm_fl[k] / (v * 1e-6) / 1e12, 1),
