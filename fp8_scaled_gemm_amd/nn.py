@@ -16,6 +16,14 @@ autograd and walks module trees.
     unscale fp16 gradients in place with the non-finite check, skip the
     optimizer step on inf/NaN, update the scale on the device.
 
+Dynamic scaling runs through two registered operators, fp8sg::scaled_linear_fwd
+and fp8sg::scaled_linear_bwd (torch.library custom ops with shape-only fake
+implementations and an autograd formula), so torch.compile keeps each FP8 linear
+as one opaque call in its graph (the same page, §7: the compiler sees the FP8
+linear as an opaque call and optimises around it) instead of tracing into the
+library calls.  Delayed and row-wise scaling use an autograd.Function in eager
+mode; a module keeps its backward scratch (the quantized gradient) across steps.
+
 Limits of this layer: inputs and weights are bf16 (the quantize kernels read
 bf16); Float8Linear has no bias (the method's linear has none; the default
 filter leaves biased layers alone); leading dimensions of the input are
@@ -26,7 +34,8 @@ from typing import Callable, Optional
 import torch
 from torch import nn
 
-from . import (LinearBwdWs, LinearBwdWsRW, LinearSaved, LinearSavedRW, OUT_BF16, ScaleRec,
+from . import (LinearBwdWs, LinearBwdWsRW, LinearSaved, LinearSavedRW, OUT_BF16, SCALE_REC_BYTES,
+               ScaleRec,
                amp_norm_workspace_len, amp_unscale_check, amp_unscale_check_norm,
                amp_update_scale, fp8_amax, fp8_scaled_linear_bwd, fp8_scaled_linear_bwd_delayed,
                fp8_scaled_linear_bwd_rowwise, fp8_scaled_linear_fwd, fp8_scaled_linear_fwd_delayed,
@@ -44,10 +53,69 @@ def _seed_history(hist: torch.Tensor, x: torch.Tensor):
     hist[:1].copy_(rec.buf[0:4].view(torch.float32))  # the record's amax field
 
 
+# ---------------------------------------------------------------- custom ops
+# The dynamic-scaling linear as two operators.  The forward returns y and the
+# state the backward needs (codes, transposed codes, the two scale records),
+# all fresh outputs; nothing is mutated.
+
+@torch.library.custom_op("fp8sg::scaled_linear_fwd", mutates_args=())
+def _op_fwd(x: torch.Tensor, w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor,
+                                                         torch.Tensor, torch.Tensor, torch.Tensor]:
+    M, K = x.shape
+    N = w.shape[0]
+    saved = LinearSaved(M, N, K, device=x.device)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    fp8_scaled_linear_fwd(x, w, saved, y, OUT_BF16)
+    return (y, *saved.tensors())
+
+
+@_op_fwd.register_fake
+def _op_fwd_fake(x, w):
+    M, K = x.shape
+    N = w.shape[0]
+    u8 = dict(dtype=torch.uint8, device=x.device)
+    return (x.new_empty((M, N), dtype=torch.bfloat16), x.new_empty((M, K), **u8),
+            x.new_empty((K, M), **u8), x.new_empty((N, K), **u8), x.new_empty((K, N), **u8),
+            x.new_empty((2, SCALE_REC_BYTES), **u8))
+
+
+@torch.library.custom_op("fp8sg::scaled_linear_bwd", mutates_args=())
+def _op_bwd(gy: torch.Tensor, x_q: torch.Tensor, x_qT: torch.Tensor, w_q: torch.Tensor,
+            w_qT: torch.Tensor, recs: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    M, N = gy.shape
+    K = x_q.shape[1]
+    saved = LinearSaved(M, N, K, tensors=(x_q, x_qT, w_q, w_qT, recs))
+    gx = torch.empty((M, K), dtype=torch.bfloat16, device=gy.device)
+    gw = torch.empty((N, K), dtype=torch.bfloat16, device=gy.device)
+    fp8_scaled_linear_bwd(gy, saved, LinearBwdWs(M, N, device=gy.device), gx, gw, OUT_BF16)
+    return gx, gw
+
+
+@_op_bwd.register_fake
+def _op_bwd_fake(gy, x_q, x_qT, w_q, w_qT, recs):
+    M, N = gy.shape
+    K = x_q.shape[1]
+    return (gy.new_empty((M, K), dtype=torch.bfloat16), gy.new_empty((N, K), dtype=torch.bfloat16))
+
+
+def _op_setup(ctx, inputs, output):
+    ctx.save_for_backward(*output[1:])
+
+
+def _op_backward(ctx, gy, *_unused):
+    if gy.dtype != torch.bfloat16:
+        raise TypeError(f"Float8Linear expects bf16 output gradients, got {gy.dtype}")
+    gx, gw = torch.ops.fp8sg.scaled_linear_bwd(gy.contiguous(), *ctx.saved_tensors)
+    return gx, gw
+
+
+_op_fwd.register_autograd(_op_backward, setup_context=_op_setup)
+
+
 class _Fp8LinearFn(torch.autograd.Function):
-    """y = x W^T through the FP8 path; saves the FP8 codes (row-major and
-    transposed) and the scale records (per-tensor) or scale vectors (row-wise)
-    for the backward pass."""
+    """y = x W^T through the FP8 path with delayed or row-wise scaling; saves
+    the FP8 codes (row-major and transposed) and the scale records (delayed) or
+    scale vectors (row-wise) for the backward pass."""
 
     @staticmethod
     def forward(ctx, x2d: torch.Tensor, weight: torch.Tensor, mod: "Float8Linear"):
@@ -84,11 +152,11 @@ class _Fp8LinearFn(torch.autograd.Function):
         gw = torch.empty((N, K), dtype=torch.bfloat16, device=gy.device)
         if mod.scaling == "rowwise":
             saved = LinearSavedRW(M, N, K, tensors=ctx.saved_tensors)
-            fp8_scaled_linear_bwd_rowwise(gy, saved, LinearBwdWsRW(M, N, device=gy.device), gx, gw,
-                                          OUT_BF16)
+            fp8_scaled_linear_bwd_rowwise(gy, saved, mod._bwd_scratch(M, N, gy.device, True), gx,
+                                          gw, OUT_BF16)
             return gx, gw, None
         saved = LinearSaved(M, N, K, tensors=ctx.saved_tensors)
-        ws = LinearBwdWs(M, N, device=gy.device)
+        ws = mod._bwd_scratch(M, N, gy.device, False)
         if mod.scaling == "delayed":
             if not mod._seeded_bwd:
                 _seed_history(mod.hist_gy, gy)
@@ -120,6 +188,17 @@ class Float8Linear(nn.Module):
                 self.register_buffer(name, torch.zeros(history_len, dtype=torch.float32,
                                                        device=device))
         self._seeded_fwd = self._seeded_bwd = False
+        self._ws = None
+
+    def _bwd_scratch(self, M, N, device, rowwise):
+        """The quantized gradient of the backward pass, kept across steps (its
+        contents are written and consumed inside one backward call on the
+        current stream, so calls on one stream can share it)."""
+        key = (M, N, str(device), rowwise)
+        if self._ws is None or self._ws[0] != key:
+            ws = LinearBwdWsRW(M, N, device=device) if rowwise else LinearBwdWs(M, N, device=device)
+            self._ws = (key, ws)
+        return self._ws[1]
 
     @classmethod
     def from_float(cls, lin: nn.Linear, scaling: str = "dynamic",
@@ -132,6 +211,7 @@ class Float8Linear(nn.Module):
         with torch.device("meta"):
             new = cls(lin.in_features, lin.out_features, scaling, history_len)
         new.weight = lin.weight
+        new._ws = None
         if scaling == "delayed":
             for name in ("hist_x", "hist_w", "hist_gy"):
                 setattr(new, name, torch.zeros(history_len, dtype=torch.float32,
@@ -143,7 +223,10 @@ class Float8Linear(nn.Module):
             raise TypeError("Float8Linear takes bf16 inputs and a bf16 weight")
         lead = x.shape[:-1]
         x2d = x.reshape(-1, self.in_features).contiguous()
-        y = _Fp8LinearFn.apply(x2d, self.weight, self)
+        if self.scaling == "dynamic":
+            y = torch.ops.fp8sg.scaled_linear_fwd(x2d, self.weight)[0]
+        else:
+            y = _Fp8LinearFn.apply(x2d, self.weight, self)
         return y.reshape(*lead, self.out_features)
 
     def extra_repr(self):
@@ -151,12 +234,20 @@ class Float8Linear(nn.Module):
                f"scaling={self.scaling}"
 
 
+# Layers kept in high precision by name [FP8-TRAIN §8: the output head and the
+# MoE router, where FP8 costs more convergence than it saves time]: the last
+# component of the fully qualified name.
+HIGH_PRECISION_NAMES = ("lm_head", "output", "router")
+
+
 def default_module_filter(mod: nn.Linear, fqn: str) -> bool:
-    """Convert a linear layer when the FP8 path can take it: bf16 weight, no
-    bias, in and out features multiples of 16 (vocabulary-sized heads often
-    are not)."""
+    """Convert a linear layer when the FP8 path can take it (bf16 weight, no
+    bias, in and out features multiples of 16) and its name does not mark it as
+    the output head or a MoE router."""
+    last = fqn.rsplit(".", 1)[-1]
     return (mod.bias is None and mod.weight.dtype == torch.bfloat16 and
-            mod.in_features % 16 == 0 and mod.out_features % 16 == 0)
+            mod.in_features % 16 == 0 and mod.out_features % 16 == 0 and
+            last not in HIGH_PRECISION_NAMES)
 
 
 def convert_to_float8_training(model: nn.Module,
@@ -166,16 +257,20 @@ def convert_to_float8_training(model: nn.Module,
     module_filter_fn(child, fully_qualified_name) accepts (default:
     default_module_filter) with a Float8Linear sharing its weight."""
     accept = module_filter_fn or default_module_filter
-
-    def walk(mod: nn.Module, prefix: str):
-        for name, child in list(mod.named_children()):
-            fqn = f"{prefix}.{name}" if prefix else name
-            walk(child, fqn)  # children first
-            if isinstance(child, nn.Linear) and accept(child, fqn):
-                setattr(mod, name, Float8Linear.from_float(child, scaling, history_len))
-
-    walk(model, "")
+    # every (parent, attribute, module, dotted path) below the root, each
+    # module after all of its own descendants; the swaps are made after the
+    # walk, so it never iterates over a tree it is changing
+    edges = list(_descendants_post_order(model, ()))
+    for parent, attr, child, path in edges:
+        if type(child) is nn.Linear and accept(child, ".".join(path)):
+            setattr(parent, attr, Float8Linear.from_float(child, scaling, history_len))
     return model
+
+
+def _descendants_post_order(mod: nn.Module, path: tuple):
+    for attr, child in mod.named_children():
+        yield from _descendants_post_order(child, path + (attr,))
+        yield mod, attr, child, path + (attr,)
 
 
 class GradScaler:

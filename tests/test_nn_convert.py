@@ -34,8 +34,10 @@ def test_default_filter_converts_what_the_path_takes():
     w = {n: p for n, p in m.named_parameters()}
     convert_to_float8_training(m)
     for b in m.blocks:
-        for name in ("gate", "up", "down", "router"):
+        for name in ("gate", "up", "down"):
             assert isinstance(getattr(b, name), Float8Linear)
+        # a MoE router stays in high precision by name (the page's section 8)
+        assert type(b.router) is nn.Linear
         assert isinstance(b.norm, nn.LayerNorm)
     assert type(m.proj) is nn.Linear and type(m.lm_head) is nn.Linear
     # the weights are the original tensors, not copies
@@ -61,12 +63,21 @@ def test_filter_sees_fully_qualified_names_post_order():
 def test_delayed_modules_carry_histories():
     m = Block()
     convert_to_float8_training(m, scaling="delayed", history_len=8)
-    for name in ("gate", "up", "down", "router"):
+    for name in ("gate", "up", "down"):
         f = getattr(m, name)
         assert f.scaling == "delayed"
         assert all(getattr(f, h).shape == (8,) and getattr(f, h).dtype == torch.float32
                    for h in ("hist_x", "hist_w", "hist_gy"))
     assert set(dict(m.named_buffers())) >= {"gate.hist_x", "down.hist_gy"}
+
+
+def test_default_filter_keeps_output_head_and_router_by_name():
+    # sizes the path takes, names that mark the layers kept in high precision
+    assert default_module_filter(lin(64, 128), "blocks.3.mlp.up")
+    assert not default_module_filter(lin(64, 128), "lm_head")
+    assert not default_module_filter(lin(64, 128), "model.output")
+    assert not default_module_filter(lin(64, 16), "layers.2.moe.router")
+    assert default_module_filter(lin(64, 16), "layers.2.router_proj.weight_like")  # last part only
 
 
 def test_from_float_refuses_what_the_path_cannot_take():
@@ -88,3 +99,30 @@ def test_scaling_modes():
         pass
     else:
         raise AssertionError("unknown scaling accepted")
+
+
+def test_dynamo_captures_the_fp8_linear_as_one_op():
+    """torch.compile with fullgraph traces a converted MLP without a graph
+    break; the captured graph holds the fp8sg::scaled_linear_fwd operator (an
+    opaque call) for each linear.  Tracing only: the backend records the graph
+    and never runs it (no GPU here)."""
+    graphs = []
+
+    def record(gm, example_inputs):
+        graphs.append(gm)
+        return lambda *args: (torch.zeros(32, 64, dtype=torch.bfloat16),)
+
+    class Mlp(nn.Module):
+        def __init__(self):
+            super().__init__()
+            self.up, self.down = lin(64, 128), lin(128, 64)
+
+        def forward(self, x):
+            return self.down(torch.relu(self.up(x)))
+
+    m = convert_to_float8_training(Mlp())
+    torch._dynamo.reset()
+    torch.compile(m, backend=record, fullgraph=True)(torch.empty(32, 64, dtype=torch.bfloat16))
+    assert len(graphs) == 1
+    targets = [str(n.target) for n in graphs[0].graph.nodes if n.op == "call_function"]
+    assert sum("fp8sg.scaled_linear_fwd" in t for t in targets) == 2, targets
