@@ -49,6 +49,9 @@ def lib():
     L.orc_encode_f32_array.argtypes = [ctypes.c_int, P, i64, P]
     L.orc_amax_bf16.argtypes = [P, i64]
     L.orc_amax_bf16.restype = u32
+    L.orc_amax_in.argtypes = [ctypes.c_int, P, i64]
+    L.orc_amax_in.restype = u32
+    L.orc_quantize_in.argtypes = [ctypes.c_int, P, i64, ctypes.c_int, f32, P]
     L.orc_fp8_max.argtypes = [ctypes.c_int]
     L.orc_fp8_max.restype = f64
     L.orc_scale.argtypes = [u32, ctypes.c_int, P, P, P, P]
@@ -124,10 +127,11 @@ def fp8_max(fmt: int) -> float:
 
 # ------------------------------------------------------- amax / scale (O-2, O-3)
 
-def amax_bits(x_bf16: np.ndarray) -> int:
-    """fp32 bit pattern of max|x| over a bf16 tensor (given as uint16 codes)."""
+def amax_bits(x_bf16: np.ndarray, in_fmt: int = None) -> int:
+    """fp32 bit pattern of max|x| over a bf16 tensor (given as uint16 codes),
+    or an fp16 one with in_fmt=F16."""
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
-    return int(lib().orc_amax_bf16(_p(x), x.size))
+    return int(lib().orc_amax_in(BF16 if in_fmt is None else in_fmt, _p(x), x.size))
 
 
 def bits_to_f32(b: int) -> float:
@@ -157,10 +161,12 @@ def scale_from_amax(a_bits: int, fmt: int) -> Scale:
 
 # ------------------------------------------------------ quantize (O-4, O-5)
 
-def quantize(x_bf16: np.ndarray, fmt: int, scale32) -> np.ndarray:
+def quantize(x_bf16: np.ndarray, fmt: int, scale32, in_fmt: int = None) -> np.ndarray:
+    """Codes of a bf16 tensor (or an fp16 one with in_fmt=F16)."""
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     q = np.empty(x.shape, np.uint8)
-    lib().orc_quantize(_p(x), x.size, fmt, float(np.float32(scale32)), _p(q))
+    lib().orc_quantize_in(BF16 if in_fmt is None else in_fmt, _p(x), x.size, fmt,
+                          float(np.float32(scale32)), _p(q))
     return q
 
 
@@ -181,10 +187,12 @@ class Quantized:
     sc: Scale
 
 
-def to_fp8(x_bf16: np.ndarray, fmt: int, with_transpose: bool = True) -> Quantized:
-    """amax -> fp64 scale -> fp32 multiply, clamp, cast  [FP8-TRAIN §2]."""
-    sc = scale_from_amax(amax_bits(x_bf16), fmt)
-    q = quantize(x_bf16, fmt, sc.scale32)
+def to_fp8(x_bf16: np.ndarray, fmt: int, with_transpose: bool = True,
+           in_fmt: int = None) -> Quantized:
+    """amax -> fp64 scale -> fp32 multiply, clamp, cast  [FP8-TRAIN §2].  The
+    input is bf16 codes, or fp16 codes with in_fmt=F16."""
+    sc = scale_from_amax(amax_bits(x_bf16, in_fmt), fmt)
+    q = quantize(x_bf16, fmt, sc.scale32, in_fmt)
     qT = transpose(q) if (with_transpose and q.ndim == 2) else None
     return Quantized(q, qT, sc)
 

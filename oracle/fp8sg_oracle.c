@@ -233,7 +233,7 @@ static uint32_t f32_bits(float v) { uint32_t b; memcpy(&b, &v, 4); return b; }
  * the result NaN (torch's max propagates NaN), written as the canonical
  * 0x7FC00000; an all-zero or empty tensor gives +0.
  */
-ORC_API uint32_t orc_amax_bf16(const uint16_t* x, int64_t n) {
+ORC_API uint32_t orc_amax_in(int in_fi, const uint16_t* x, int64_t n) {
   ensure_init();
   double best = 0.0;
   int any_nan = 0;
@@ -243,7 +243,7 @@ ORC_API uint32_t orc_amax_bf16(const uint16_t* x, int64_t n) {
     int nn = 0;
 #pragma omp for schedule(static) nowait
     for (int64_t i = 0; i < n; ++i) {
-      double v = fabs(dec(ORC_BF16, x[i]));
+      double v = fabs(dec(in_fi, x[i]));
       if (isnan(v)) nn = 1;
       else if (v > b) b = v;
     }
@@ -254,8 +254,12 @@ ORC_API uint32_t orc_amax_bf16(const uint16_t* x, int64_t n) {
     }
   }
   if (any_nan) return 0x7FC00000u;
-  return f32_bits((float)best); /* a bf16 magnitude is exact in fp32 */
+  return f32_bits((float)best); /* a bf16 or fp16 magnitude is exact in fp32 */
 }
+
+/* The layer's tensors are bf16 (FP8-TRAIN §6); fp16 inputs (an fp16 model
+   under loss scaling) go through the same definition with the fp16 decode. */
+ORC_API uint32_t orc_amax_bf16(const uint16_t* x, int64_t n) { return orc_amax_in(ORC_BF16, x, n); }
 
 /* ------------------------------------------------------------------------ */
 /* O-3  scale = fp8_max / max(amax, EPS) in fp64; inverse = 1/scale          */
@@ -298,12 +302,13 @@ ORC_API void orc_scale(uint32_t amax_bits, int fi, double* scale, double* inv,
 /*      activations and weights, e5m2 for gradients].                        */
 /* ------------------------------------------------------------------------ */
 
-ORC_API void orc_quantize(const uint16_t* x, int64_t n, int fi, float scale32, uint8_t* q) {
+ORC_API void orc_quantize_in(int in_fi, const uint16_t* x, int64_t n, int fi, float scale32,
+                             uint8_t* q) {
   ensure_init();
   float m = (float)orc_fp8_max(fi);
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) {
-    float xf = (float)dec(ORC_BF16, x[i]);
+    float xf = (float)dec(in_fi, x[i]);
     float y = xf * scale32; /* fp32 product: fp32 tensor times a 0-dim scale */
     if (!isnan(y)) {
       if (y > m) y = m;
@@ -311,6 +316,10 @@ ORC_API void orc_quantize(const uint16_t* x, int64_t n, int fi, float scale32, u
     }
     q[i] = (uint8_t)enc(fi, (double)y);
   }
+}
+
+ORC_API void orc_quantize(const uint16_t* x, int64_t n, int fi, float scale32, uint8_t* q) {
+  orc_quantize_in(ORC_BF16, x, n, fi, scale32, q);
 }
 
 /* O-5  transposed copy: qT[c][r] = q[r][c]  [FP8-TRAIN §4: the column-major

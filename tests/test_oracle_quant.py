@@ -151,3 +151,69 @@ def test_scale_direction_trap():
     ratio = np.median(np.abs(wrong) / np.maximum(np.abs(fw.c), 1e-30))
     factor = (fw.x.sc.scale * fw.w.sc.scale) ** 2
     assert abs(ratio / factor - 1) < 1e-5
+
+
+# ----------------------------------------------- fp16 inputs (an fp16 model)
+
+def f16_tensor(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16)).view(torch.float16)
+
+
+def torch_chain_f16(x_bits, fmt, eps=1e-12):
+    """The page's to_fp8 chain on an fp16 tensor, executed by torch on the CPU."""
+    x = f16_tensor(x_bits)
+    fmax = torch.finfo(TORCH_FP8[fmt]).max
+    amax = x.float().abs().max()
+    scale = torch.full((), fmax, dtype=torch.float64) / amax.double().clamp(min=eps)
+    q = (x.float() * scale).clamp(-fmax, fmax).to(TORCH_FP8[fmt])
+    return float(amax), float(scale), float(scale.reciprocal()), q.view(torch.uint8).numpy()
+
+
+def f16_inputs():
+    yield "normal", W.normal_f16(13, 1, (97, 131), 1.0)
+    yield "grads_scaled", W.normal_f16(13, 2, (64, 200), 1e-4 * 65536.0)
+    yield "small", W.normal_f16(13, 3, (50, 77), 1e-5)  # fp16 subnormals among them
+    yield "wide", W.normal_f16(13, 4, (4096,), 2000.0)
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3FN, O.E5M2])
+def test_f16_input_quantize_matches_torch_chain(fmt):
+    for name, x in f16_inputs():
+        amax, s, inv, q_ref = torch_chain_f16(x, fmt)
+        qz = O.to_fp8(x, fmt, with_transpose=False, in_fmt=O.F16)
+        assert O.bits_to_f32(qz.sc.amax_bits) == amax, name
+        assert qz.sc.scale == s and qz.sc.inv == inv, name
+        assert np.array_equal(qz.q.reshape(-1), q_ref.reshape(-1)), name
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3FN, O.E5M2])
+def test_f16_and_bf16_inputs_of_the_same_values_cast_alike(fmt):
+    """Values representable in both formats (8 significant bits or fewer, in the
+    common exponent range) give the same amax, scale and codes whichever
+    format carries them: a wrong fp16 decode breaks this."""
+    rng = np.random.default_rng(14)
+    mant = rng.integers(128, 256, 3000).astype(np.float64)   # 8 significant bits
+    expo = rng.integers(-14, 8, 3000).astype(np.float64)  # fp16 normal range
+    sign = rng.choice([-1.0, 1.0], 3000)
+    v = (sign * mant * 2.0 ** (expo - 7)).astype(np.float32)
+    f16 = v.astype(np.float16)
+    assert np.array_equal(f16.astype(np.float32), v)        # exact in fp16
+    b16 = W.f32_to_bf16_bits(v)
+    assert np.array_equal((b16.astype(np.uint32) << 16).view(np.float32), v)  # exact in bf16
+    a = O.to_fp8(f16.view(np.uint16), fmt, with_transpose=False, in_fmt=O.F16)
+    b = O.to_fp8(b16, fmt, with_transpose=False)
+    assert a.sc.amax_bits == b.sc.amax_bits and a.sc.scale == b.sc.scale
+    assert np.array_equal(a.q, b.q)
+
+
+def test_f16_amax_special_values():
+    x = W.normal_f16(15, 1, (1000,), 3.0)
+    ref = np.abs(x.view(np.float16).astype(np.float32)).max()
+    assert O.bits_to_f32(O.amax_bits(x, O.F16)) == ref
+    y = x.copy()
+    y[5] = 0xFC00  # -inf
+    assert O.bits_to_f32(O.amax_bits(y, O.F16)) == np.inf
+    y[7] = 0x7E01  # NaN
+    assert O.amax_bits(y, O.F16) == 0x7FC00000
+    assert O.amax_bits(np.array([0x8000, 0x0000, 0x0001], np.uint16), O.F16) == \
+        int(np.float32(2.0 ** -24).view(np.uint32))  # smallest fp16 subnormal
