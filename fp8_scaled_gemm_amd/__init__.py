@@ -28,7 +28,8 @@ EXPORTS = ("fp8sg_status_string", "fp8sg_version", "amp_norm_workspace_len", "fp
            "fp8_quantize_rowwise", "fp8_gemm_rowwise", "fp8_scaled_linear_fwd_rowwise",
            "fp8_scaled_linear_bwd_rowwise", "fp8_scaled_linear_bwd_unscale", "fp8_gemm_unscale",
            "fp8_scaled_linear_bwd_delayed_unscale", "fp8_scaled_linear_bwd_rowwise_unscale",
-           "fp8_quantize_from_amax", "amp_unscale_check_norm_noalloc")
+           "fp8_quantize_from_amax", "amp_unscale_check_norm_noalloc", "fp8_amax_f16",
+           "fp8_quantize_f16")
 MAX_HISTORY = 1024
 MAX_DIM = 1 << 29     # largest matrix dimension an entry point takes
 MAX_ELEMS = 1 << 35   # largest tensor, in elements
@@ -79,6 +80,8 @@ def lib():
     L.fp8_quantize.argtypes = [P, i64, i64, i, P, P, P, P]
     L.fp8_quantize_delayed.argtypes = [P, i64, i64, i, P, i32, P, P, P, P]
     L.fp8_quantize_from_amax.argtypes = [P, i64, i64, i, P, P, P, P, P]
+    L.fp8_amax_f16.argtypes = [P, i64, P, P]
+    L.fp8_quantize_f16.argtypes = [P, i64, i64, i, P, P, P, P]
     L.fp8_gemm.argtypes = [P, i, P, i, P, P, P, i, i64, i64, i64, P]
     L.fp8_scaled_linear_fwd.argtypes = [P, P, i64, i64, i64, ctypes.POINTER(_Saved), P, i, P]
     L.fp8_scaled_linear_bwd.argtypes = [P, ctypes.POINTER(_Saved), i64, i64, i64,
@@ -235,6 +238,27 @@ def fp8_quantize(x: torch.Tensor, fmt: int, rec: ScaleRec, q: torch.Tensor,
     rows, cols = _quant_args(x, rec, q, qT)
     _check(lib().fp8_quantize(_ptr(x), rows, cols, fmt, _ptr(rec.buf), _ptr(q),
                               _ptr(qT), _stream(stream)), "fp8_quantize")
+
+
+def fp8_amax_f16(x: torch.Tensor, rec: ScaleRec, stream=None):
+    """rec.amax = max |x| over an fp16 tensor (any shape, contiguous)."""
+    _need(x, "x", torch.float16)
+    _need_rec(rec, "rec")
+    _check(lib().fp8_amax_f16(_ptr(x), x.numel(), _ptr(rec.buf), _stream(stream)), "fp8_amax_f16")
+
+
+def fp8_quantize_f16(x: torch.Tensor, fmt: int, rec: ScaleRec, q: torch.Tensor,
+                     qT: torch.Tensor = None, stream=None):
+    """fp8_quantize for an fp16 tensor: scale from rec.amax (fp8_amax_f16), codes q
+    (and the transposed codes qT)."""
+    _need(x, "x", torch.float16)
+    _need_rec(rec, "rec")
+    _need(q, "q", torch.uint8, numel=x.numel())
+    if qT is not None:
+        _need(qT, "qT", torch.uint8, numel=x.numel())
+    rows, cols = (x.shape[0], x.numel() // max(x.shape[0], 1)) if x.dim() >= 2 else (1, x.numel())
+    _check(lib().fp8_quantize_f16(_ptr(x), rows, cols, fmt, _ptr(rec.buf), _ptr(q), _ptr(qT),
+                                  _stream(stream)), "fp8_quantize_f16")
 
 
 def fp8_quantize_from_amax(x: torch.Tensor, fmt: int, amax: torch.Tensor, rec: ScaleRec,

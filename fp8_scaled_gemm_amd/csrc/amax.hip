@@ -1,4 +1,4 @@
-// amax = max_i |x_i| over bf16 tensors [FP8-TRAIN §2: x.float().abs().max()].
+// amax = max_i |x_i| over bf16 (or fp16) tensors [FP8-TRAIN §2: x.float().abs().max()].
 //
 // One pass over HBM, 2 bytes per element.  |x| is compared as the unsigned
 // integer bits & 0x7FFF: for non-negative IEEE values (inf and NaN included)
@@ -26,7 +26,7 @@ namespace fp8sg {
 constexpr int kAmaxThreads = 256;
 constexpr int kAmaxUnroll = 8;  // 16-byte loads in flight per thread per iteration
 
-template <bool S>
+template <bool S, bool F16 = false>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax(AmaxArgs args) {
   int j = 0;
 #pragma unroll
@@ -61,10 +61,8 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(AmaxArgs args) {
   // elements past the last full 16-byte vector
   if (lb == 0 && tid < (int)(job.n & 7)) m = pmax(m, (uint32_t)(job.x[(nvec << 3) + tid] & 0x7FFFu));
 
-  const uint32_t code = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
-  uint32_t bits = code << 16;                  // the bf16 magnitude as fp32 bits
-  if (bits > 0x7F800000u) bits = 0x7FC00000u;  // any NaN -> canonical NaN
-  bits = block_max_u32<kAmaxThreads>(bits);
+  // the largest magnitude as fp32 bits, any NaN canonical
+  const uint32_t bits = block_max_u32<kAmaxThreads>(absmax_bits<F16>(m));
   if (tid == 0) {
     job.rec->_part[lb] = bits;
     if (lb == 0) job.rec->_nparts = (uint32_t)job.nblocks;
@@ -101,7 +99,12 @@ hipError_t launch_amax(AmaxArgs args, bool finalize, hipStream_t stream) {
     total += args.job[j].nblocks;
     bytes += 2 * args.job[j].n;
   }
-  if (bytes >= kStreamBytes)
+  const bool st = bytes >= kStreamBytes;
+  if (args.in_f16 && st)
+    hipLaunchKernelGGL((k_amax<true, true>), dim3(total), dim3(kAmaxThreads), 0, stream, args);
+  else if (args.in_f16)
+    hipLaunchKernelGGL((k_amax<false, true>), dim3(total), dim3(kAmaxThreads), 0, stream, args);
+  else if (st)
     hipLaunchKernelGGL(k_amax<true>, dim3(total), dim3(kAmaxThreads), 0, stream, args);
   else
     hipLaunchKernelGGL(k_amax<false>, dim3(total), dim3(kAmaxThreads), 0, stream, args);

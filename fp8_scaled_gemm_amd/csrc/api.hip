@@ -104,6 +104,32 @@ fp8sg_status fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, fp8sg_f
   return hip_status(launch_quantize(a, fmt, S(stream)));
 }
 
+fp8sg_status fp8_amax_f16(const uint16_t* x, int64_t n, fp8sg_scale_rec* rec, fp8sg_stream stream) {
+  if (!rec || (n > 0 && !x)) return FP8SG_ERR_NULL;
+  if (n < 0 || n > FP8SG_MAX_ELEMS) return FP8SG_ERR_SHAPE;
+  if (!aligned16(x) || !aligned(rec, 8)) return FP8SG_ERR_ALIGN;
+  AmaxArgs a{};
+  a.job[0] = AmaxJob{x, n, rec, 0, amax_blocks_for(n)};
+  a.njobs = 1;
+  a.in_f16 = 1;
+  return hip_status(launch_amax(a, true, S(stream)));
+}
+
+fp8sg_status fp8_quantize_f16(const uint16_t* x, int64_t rows, int64_t cols, fp8sg_format fmt,
+                              fp8sg_scale_rec* rec, uint8_t* q, uint8_t* qT, fp8sg_stream stream) {
+  if (!rec) return FP8SG_ERR_NULL;
+  if (!fmt_ok(fmt)) return FP8SG_ERR_FORMAT;
+  if (!elems_ok(rows, cols)) return FP8SG_ERR_SHAPE;
+  if (rows * cols > 0 && (!x || !q)) return FP8SG_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || (qT && !aligned16(qT)) || !aligned(rec, 8))
+    return FP8SG_ERR_ALIGN;
+  QuantArgs a{};
+  a.job[0] = QuantJob{x, rows, cols, rec, q, qT, 0, 0, 0};
+  a.njobs = 1;
+  a.in_f16 = 1;
+  return hip_status(launch_quantize(a, fmt, S(stream)));
+}
+
 fp8sg_status fp8_quantize_from_amax(const uint16_t* x, int64_t rows, int64_t cols,
                                     fp8sg_format fmt, const float* amax, fp8sg_scale_rec* rec,
                                     uint8_t* q, uint8_t* qT, fp8sg_stream stream) {

@@ -128,22 +128,36 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
   return (uint32_t)r;
 }
 
-// Quantize 8 bf16 values (one 16-byte load) to 8 codes (two dwords)
+// The 16-bit input of a cast as fp32 (exact): bf16, the layer's dtype, or
+// fp16 (F16: an fp16 model under loss scaling).  lo/hi: the element in the
+// low / high half of a dword.
+template <bool F16>
+__device__ __forceinline__ float in_lo(uint32_t w) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+  else return bf16_lo(w);
+}
+template <bool F16>
+__device__ __forceinline__ float in_hi(uint32_t w) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  else return bf16_hi(w);
+}
+
+// Quantize 8 inputs (one 16-byte load) to 8 codes (two dwords)
 // [FP8-TRAIN §2: fl32(x * scale32), clamp, cast].
-template <int FMT>
+template <int FMT, bool F16 = false>
 __device__ __forceinline__ uint2 quant8(uint4 v, float s32) {
   constexpr float m = FMT == FP8SG_E4M3FN ? kE4M3Max : kE5M2Max;
-  float f0 = clamp_keep_nan(bf16_lo(v.x) * s32, m), f1 = clamp_keep_nan(bf16_hi(v.x) * s32, m);
-  float f2 = clamp_keep_nan(bf16_lo(v.y) * s32, m), f3 = clamp_keep_nan(bf16_hi(v.y) * s32, m);
-  float f4 = clamp_keep_nan(bf16_lo(v.z) * s32, m), f5 = clamp_keep_nan(bf16_hi(v.z) * s32, m);
-  float f6 = clamp_keep_nan(bf16_lo(v.w) * s32, m), f7 = clamp_keep_nan(bf16_hi(v.w) * s32, m);
+  float f0 = clamp_keep_nan(in_lo<F16>(v.x) * s32, m), f1 = clamp_keep_nan(in_hi<F16>(v.x) * s32, m);
+  float f2 = clamp_keep_nan(in_lo<F16>(v.y) * s32, m), f3 = clamp_keep_nan(in_hi<F16>(v.y) * s32, m);
+  float f4 = clamp_keep_nan(in_lo<F16>(v.z) * s32, m), f5 = clamp_keep_nan(in_hi<F16>(v.z) * s32, m);
+  float f6 = clamp_keep_nan(in_lo<F16>(v.w) * s32, m), f7 = clamp_keep_nan(in_hi<F16>(v.w) * s32, m);
   return make_uint2(cvt4<FMT>(f0, f1, f2, f3), cvt4<FMT>(f4, f5, f6, f7));
 }
 
-template <int FMT>
+template <int FMT, bool F16 = false>
 __device__ __forceinline__ uint8_t quant1(uint16_t b, float s32) {
   constexpr float m = FMT == FP8SG_E4M3FN ? kE4M3Max : kE5M2Max;
-  float f = clamp_keep_nan(bf16_lo(b) * s32, m);
+  float f = clamp_keep_nan(in_lo<F16>(b) * s32, m);
   return (uint8_t)(cvt4<FMT>(f, 0.f, 0.f, 0.f) & 0xFFu);
 }
 
@@ -236,10 +250,16 @@ __device__ __forceinline__ uint32_t absmax8(uint32_t m, uint4 v) {
   return pmax(m, v.w & mask);
 }
 // packed pair max -> fp32 bits of the larger magnitude, NaN made canonical
+template <bool F16 = false>
 __device__ __forceinline__ uint32_t absmax_bits(uint32_t m) {
   const uint32_t code = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
-  const uint32_t bits = code << 16;
-  return bits > 0x7F800000u ? 0x7FC00000u : bits;
+  if constexpr (F16) {  // fp16 magnitude: exact in fp32; inf stays inf
+    if (code > 0x7C00u) return 0x7FC00000u;
+    return __float_as_uint((float)__builtin_bit_cast(_Float16, (uint16_t)code));
+  } else {
+    const uint32_t bits = code << 16;
+    return bits > 0x7F800000u ? 0x7FC00000u : bits;
+  }
 }
 
 // Largest entry of an amax history (fp32, most recent first): NaN if any

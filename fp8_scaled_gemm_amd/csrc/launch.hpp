@@ -23,6 +23,7 @@ struct AmaxJob {
 struct AmaxArgs {
   AmaxJob job[kMaxAmaxJobs];
   int32_t njobs;
+  int32_t in_f16;  // inputs are fp16 (default: bf16)
 };
 int amax_blocks_for(int64_t n);
 // Per-block partial maxima into each job's record; with finalize, also rec->amax.
@@ -47,6 +48,7 @@ struct QuantJob {
 struct QuantArgs {
   QuantJob job[kMaxQuantJobs];
   int32_t njobs;
+  int32_t in_f16;  // inputs are fp16 (default: bf16); dynamic scaling only
 };
 // All jobs of one launch share the format.  Chooses the tiled kernel (rows and
 // cols multiples of 16 with a transposed copy), the flat kernel (no transposed

@@ -1,4 +1,4 @@
-// Scale + quantize-cast of bf16 tensors to OCP FP8, fused with the transposed
+// Scale + quantize-cast of bf16 (or fp16) tensors to OCP FP8, fused with the transposed
 // copy [FP8-TRAIN §2: scale = fp8_max / amax in fp64, x * scale, clamp, cast;
 // §3: e4m3 for activations and weights, e5m2 for gradients; §4: the backward
 // GEMMs need each operand contiguous along its contraction dimension, which
@@ -135,8 +135,9 @@ __device__ __forceinline__ void publish_scale(fp8sg_scale_rec* rec, float amax, 
   }
 }
 
-template <int FMT, bool S, int SRC, bool SELF = false>
+template <int FMT, bool S, int SRC, bool SELF = false, bool F16 = false>
 __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
+  static_assert(!F16 || (SRC == kSrcParts && !SELF), "fp16 inputs: dynamic casts only");
   constexpr bool DELAYED = SRC == kSrcHist;
   constexpr bool kParts = SRC == kSrcParts && !SELF;  // scale from the amax kernel's partials
   int lb;
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
       const int r = r0 + 16 * p;
       const int64_t gr = r_tile + r;
       if constexpr (DELAYED) am = absmax8(am, v[p]);
-      const uint2 c = quant8<FMT>(v[p], sv.s32);
+      const uint2 c = quant8<FMT, F16>(v[p], sv.s32);
       if (col_ok && gr < rows) st8<S>(job.q + gr * cols + gc, c);
       *reinterpret_cast<uint2*>(&lds[r * 32 + ((2 * c8) ^ swz(r))]) = c;
     }
@@ -249,8 +250,9 @@ template <int SRC>
 constexpr int flat_unroll() { return SRC == kSrcHist ? 8 : 4; }
 constexpr int64_t kFlatMaxBlocks = 65536;
 
-template <int FMT, bool S, int SRC>
+template <int FMT, bool S, int SRC, bool F16 = false>
 __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
+  static_assert(!F16 || SRC == kSrcParts, "fp16 inputs: dynamic casts only");
   constexpr bool DELAYED = SRC == kSrcHist;
   int lb;
   const QuantJob& job = pick_job(args, lb);
@@ -299,20 +301,21 @@ __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
     for (int u = 0; u < kFlatUnroll; ++u) {
       const int64_t k = base + (int64_t)u * kQThreads;
       if constexpr (DELAYED) am = absmax8(am, v[u]);
-      if (k < nvec) st8<S>(qv + k, quant8<FMT>(v[u], sv.s32));
+      if (k < nvec) st8<S>(qv + k, quant8<FMT, F16>(v[u], sv.s32));
     }
   }
   if (lb == 0 && tid < (int)(n & 7)) {
     const int64_t i = (nvec << 3) + tid;
     if constexpr (DELAYED) am = pmax(am, (uint32_t)(job.x[i] & 0x7FFFu));
-    job.q[i] = quant1<FMT>(job.x[i], sv.s32);
+    job.q[i] = quant1<FMT, F16>(job.x[i], sv.s32);
   }
   store_block_amax<DELAYED>(job, lb, am);
 }
 
 // Transposed copy of a shape the tiled kernel does not take: one thread per element.
-template <int FMT, int SRC>
+template <int FMT, int SRC, bool F16 = false>
 __global__ __launch_bounds__(kQThreads) void k_quant_elem(QuantArgs args) {
+  static_assert(!F16 || SRC == kSrcParts, "fp16 inputs: dynamic casts only");
   constexpr bool DELAYED = SRC == kSrcHist;
   int lb;
   const QuantJob& job = pick_job(args, lb);
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_elem(QuantArgs args) {
   const int64_t n = job.rows * job.cols;
   for (int64_t i = (int64_t)lb * kQThreads + tid; i < n; i += (int64_t)job.nblocks * kQThreads) {
     if constexpr (DELAYED) am = pmax(am, (uint32_t)(job.x[i] & 0x7FFFu));
-    const uint8_t c = quant1<FMT>(job.x[i], sv.s32);
+    const uint8_t c = quant1<FMT, F16>(job.x[i], sv.s32);
     job.q[i] = c;
     const int64_t r = i / job.cols, cc = i - r * job.cols;
     job.qT[cc * job.rows + r] = c;
@@ -389,7 +392,7 @@ static int blocks_of(QuantJob& j, QuantPath p) {
   return (int)(b < 1 ? 1 : b);  // one block at least: it writes the scale fields
 }
 
-template <int FMT, int SRC>
+template <int FMT, int SRC, bool F16 = false>
 static hipError_t launch_fmt(QuantArgs a, hipStream_t stream, bool self = false) {
   constexpr bool DELAYED = SRC == kSrcHist;
   // jobs of one launch must take the same path; otherwise split into launches
@@ -409,18 +412,18 @@ static hipError_t launch_fmt(QuantArgs a, hipStream_t stream, bool self = false)
       sub.job[sub.njobs++] = jb;
     }
     const bool st = bytes >= kStreamBytes;
-    if (self && p == kPathTiled && SRC == kSrcParts)
+    if (self && p == kPathTiled && SRC == kSrcParts && !F16)
       hipLaunchKernelGGL((k_quant_tiled<FMT, false, kSrcParts, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathTiled && st)
-      hipLaunchKernelGGL((k_quant_tiled<FMT, true, SRC>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_tiled<FMT, true, SRC, false, F16>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathTiled)
-      hipLaunchKernelGGL((k_quant_tiled<FMT, false, SRC>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_tiled<FMT, false, SRC, false, F16>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathFlat && st)
-      hipLaunchKernelGGL((k_quant_flat<FMT, true, SRC>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_flat<FMT, true, SRC, F16>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathFlat)
-      hipLaunchKernelGGL((k_quant_flat<FMT, false, SRC>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_flat<FMT, false, SRC, F16>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else
-      hipLaunchKernelGGL((k_quant_elem<FMT, SRC>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      hipLaunchKernelGGL((k_quant_elem<FMT, SRC, F16>), dim3(total), dim3(kQThreads), 0, stream, sub);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (DELAYED) {
@@ -451,6 +454,9 @@ hipError_t launch_quantize(QuantArgs args, int fmt, hipStream_t stream) {
   // points build the job lists)
   const bool delayed = args.njobs > 0 && args.job[0].hist;
   const bool given = args.njobs > 0 && args.job[0].amax_in;
+  if (args.in_f16)  // fp16 inputs: dynamic scaling from the amax kernel's partials
+    return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN, kSrcParts, true>(args, stream)
+                               : launch_fmt<FP8SG_E5M2, kSrcParts, true>(args, stream);
   if (delayed)
     return fmt == FP8SG_E4M3FN ? launch_fmt<FP8SG_E4M3FN, kSrcHist>(args, stream)
                                : launch_fmt<FP8SG_E5M2, kSrcHist>(args, stream);

@@ -24,8 +24,14 @@ linear as an opaque call and optimises around it) instead of tracing into the
 library calls.  Delayed and row-wise scaling use an autograd.Function in eager
 mode; a module keeps its backward scratch (the quantized gradient) across steps.
 
-Limits of this layer: inputs and weights are bf16 (the quantize kernels read
-bf16); Float8Linear has no bias (the method's linear has none; the default
+An fp16 model under loss scaling [PT-CH20 §20.2.2] uses fp16 layers
+(Float8Linear with an fp16 weight): fp16 inputs are cast by the fp16-input
+kernels, outputs and gradients are fp16, and with a GradScaler attached the
+weight gradient leaves the wgrad GEMM unscaled and checked (the scaler's
+unscale_ then skips it); the input gradient keeps the loss scale for the layers
+below.
+
+Limits of this layer: inputs and weights are bf16 or fp16; Float8Linear has no bias (the method's linear has none; the default
 filter leaves biased layers alone); leading dimensions of the input are
 flattened into M; M, N, K must be multiples of 16.
 """
@@ -34,10 +40,11 @@ from typing import Callable, Optional
 import torch
 from torch import nn
 
-from . import (LinearBwdWs, LinearBwdWsRW, LinearSaved, LinearSavedRW, OUT_BF16, SCALE_REC_BYTES,
-               ScaleRec,
+from . import (E4M3FN, E5M2, LinearBwdWs, LinearBwdWsRW, LinearSaved, LinearSavedRW, OUT_BF16,
+               OUT_F16, SCALE_REC_BYTES, ScaleRec,
                amp_norm_workspace_len, amp_unscale_check, amp_unscale_check_norm,
-               amp_update_scale, fp8_amax, fp8_scaled_linear_bwd, fp8_scaled_linear_bwd_delayed,
+               amp_update_scale, fp8_amax, fp8_amax_f16, fp8_gemm, fp8_gemm_unscale,
+               fp8_quantize_f16, fp8_scaled_linear_bwd, fp8_scaled_linear_bwd_delayed,
                fp8_scaled_linear_bwd_rowwise, fp8_scaled_linear_fwd, fp8_scaled_linear_fwd_delayed,
                fp8_scaled_linear_fwd_rowwise)
 
@@ -167,21 +174,82 @@ class _Fp8LinearFn(torch.autograd.Function):
         return gx, gw, None
 
 
+class _Fp8LinearF16Fn(torch.autograd.Function):
+    """y = x W^T for an fp16 model under loss scaling [PT-CH20 §20.2.2; FP8-TRAIN
+    §2, §4]: fp16 x and W cast to e4m3, the GEMMs in FP8, fp16 y and
+    gradients.  The output gradient carries the loss scale; the input gradient
+    keeps it (it flows to the layers below), the weight gradient leaves the
+    wgrad GEMM unscaled and checked when a GradScaler is attached (its scale and
+    non-finite flag), and the scaler then skips that gradient in unscale_."""
+
+    @staticmethod
+    def forward(ctx, x2d: torch.Tensor, weight: torch.Tensor, mod: "Float8Linear"):
+        M, K = x2d.shape
+        N = weight.shape[0]
+        saved = LinearSaved(M, N, K, device=x2d.device)
+        fp8_amax_f16(x2d, saved.x_sc)
+        fp8_quantize_f16(x2d, E4M3FN, saved.x_sc, saved.x_q, saved.x_qT)
+        fp8_amax_f16(weight, saved.w_sc)
+        fp8_quantize_f16(weight, E4M3FN, saved.w_sc, saved.w_q, saved.w_qT)
+        y = torch.empty((M, N), dtype=torch.float16, device=x2d.device)
+        fp8_gemm(saved.x_q, E4M3FN, saved.w_q, E4M3FN, saved.x_sc.inv_ptr(), saved.w_sc.inv_ptr(), y,
+                 OUT_F16)
+        ctx.mod = mod
+        ctx.dims = (M, N, K)
+        ctx.save_for_backward(*saved.tensors())
+        return y
+
+    @staticmethod
+    def backward(ctx, gy: torch.Tensor):
+        M, N, K = ctx.dims
+        mod = ctx.mod
+        if gy.dtype != torch.float16:
+            raise TypeError(f"an fp16 Float8Linear expects fp16 output gradients, got {gy.dtype}")
+        gy = gy.contiguous()
+        saved = LinearSaved(M, N, K, tensors=ctx.saved_tensors)
+        ws = mod._bwd_scratch(M, N, gy.device, False)
+        fp8_amax_f16(gy, ws.gy_sc)
+        fp8_quantize_f16(gy, E5M2, ws.gy_sc, ws.gy_q, ws.gy_qT)
+        gx = torch.empty((M, K), dtype=torch.float16, device=gy.device)
+        fp8_gemm(ws.gy_q, E5M2, saved.w_qT, E4M3FN, ws.gy_sc.inv_ptr(), saved.w_sc.inv_ptr(), gx,
+                 OUT_F16)
+        gw = torch.empty((N, K), dtype=torch.float16, device=gy.device)
+        scaler = mod.grad_scaler
+        if scaler is not None:
+            fp8_gemm_unscale(ws.gy_qT, E5M2, saved.x_qT, E4M3FN, ws.gy_sc.inv_ptr(),
+                             saved.x_sc.inv_ptr(), scaler._scale, scaler._found, gw)
+            scaler._mark_unscaled(mod.weight)
+        else:
+            fp8_gemm(ws.gy_qT, E5M2, saved.x_qT, E4M3FN, ws.gy_sc.inv_ptr(), saved.x_sc.inv_ptr(),
+                     gw, OUT_F16)
+        return gx, gw, None
+
+
 class Float8Linear(nn.Module):
     """nn.Linear (no bias) whose forward and backward GEMMs run in FP8 with
     per-tensor scaling, "dynamic" (scale from the current tensor) or
     "delayed" (scale from an amax history of history_len earlier steps), or
     with "rowwise" scaling (one scale per row of every operand along the
-    dimension its GEMM does not contract)."""
+    dimension its GEMM does not contract).
+
+    dtype torch.float16 makes an fp16 layer for an fp16 model under loss
+    scaling (dynamic scaling): fp16 inputs, weight, output and gradients; with
+    attach_grad_scaler(scaler), its weight gradient is unscaled and checked in
+    the wgrad GEMM's epilogue."""
 
     def __init__(self, in_features: int, out_features: int, scaling: str = "dynamic",
-                 history_len: int = 16, device=None):
+                 history_len: int = 16, device=None, dtype=torch.bfloat16):
         super().__init__()
         if scaling not in SCALINGS:
             raise ValueError(f"scaling must be one of {SCALINGS}, not {scaling!r}")
+        if dtype not in (torch.bfloat16, torch.float16):
+            raise TypeError(f"Float8Linear takes bf16 or fp16, not {dtype}")
+        if dtype == torch.float16 and scaling != "dynamic":
+            raise ValueError("an fp16 Float8Linear uses dynamic scaling")
         self.in_features, self.out_features = in_features, out_features
         self.scaling = scaling
-        self.weight = nn.Parameter(torch.empty((out_features, in_features), dtype=torch.bfloat16,
+        self.grad_scaler = None
+        self.weight = nn.Parameter(torch.empty((out_features, in_features), dtype=dtype,
                                                device=device))
         if scaling == "delayed":
             for name in ("hist_x", "hist_w", "hist_gy"):
@@ -200,16 +268,26 @@ class Float8Linear(nn.Module):
             self._ws = (key, ws)
         return self._ws[1]
 
+    def attach_grad_scaler(self, scaler: "GradScaler") -> "Float8Linear":
+        """fp16 layers: unscale and check the weight gradient in the wgrad GEMM
+        with this scaler's scale and flag (the scaler's unscale_ then skips it)."""
+        if self.weight.dtype != torch.float16:
+            raise TypeError("the fused unscale serves fp16 layers (fp16 gradients)")
+        self.grad_scaler = scaler
+        return self
+
     @classmethod
     def from_float(cls, lin: nn.Linear, scaling: str = "dynamic",
                    history_len: int = 16) -> "Float8Linear":
-        """A Float8Linear sharing lin's weight tensor (no copy)."""
+        """A Float8Linear sharing lin's weight tensor (no copy); an fp16 weight
+        makes an fp16 layer."""
         if lin.bias is not None:
             raise ValueError("Float8Linear has no bias")
-        if lin.weight.dtype != torch.bfloat16:
-            raise TypeError(f"Float8Linear needs a bf16 weight, got {lin.weight.dtype}")
+        if lin.weight.dtype not in (torch.bfloat16, torch.float16):
+            raise TypeError(f"Float8Linear needs a bf16 or fp16 weight, got {lin.weight.dtype}")
         with torch.device("meta"):
-            new = cls(lin.in_features, lin.out_features, scaling, history_len)
+            new = cls(lin.in_features, lin.out_features, scaling, history_len,
+                      dtype=lin.weight.dtype)
         new.weight = lin.weight
         new._ws = None
         if scaling == "delayed":
@@ -219,11 +297,13 @@ class Float8Linear(nn.Module):
         return new
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        if x.dtype != torch.bfloat16 or self.weight.dtype != torch.bfloat16:
-            raise TypeError("Float8Linear takes bf16 inputs and a bf16 weight")
+        if x.dtype != self.weight.dtype:
+            raise TypeError(f"Float8Linear takes inputs of its weight's dtype {self.weight.dtype}")
         lead = x.shape[:-1]
         x2d = x.reshape(-1, self.in_features).contiguous()
-        if self.scaling == "dynamic":
+        if self.weight.dtype == torch.float16:
+            y = _Fp8LinearF16Fn.apply(x2d, self.weight, self)
+        elif self.scaling == "dynamic":
             y = torch.ops.fp8sg.scaled_linear_fwd(x2d, self.weight)[0]
         else:
             y = _Fp8LinearFn.apply(x2d, self.weight, self)
@@ -245,17 +325,20 @@ def default_module_filter(mod: nn.Linear, fqn: str) -> bool:
     bias, in and out features multiples of 16) and its name does not mark it as
     the output head or a MoE router."""
     last = fqn.rsplit(".", 1)[-1]
-    return (mod.bias is None and mod.weight.dtype == torch.bfloat16 and
+    return (mod.bias is None and mod.weight.dtype in (torch.bfloat16, torch.float16) and
             mod.in_features % 16 == 0 and mod.out_features % 16 == 0 and
             last not in HIGH_PRECISION_NAMES)
 
 
 def convert_to_float8_training(model: nn.Module,
                                module_filter_fn: Optional[Callable[[nn.Module, str], bool]] = None,
-                               scaling: str = "dynamic", history_len: int = 16) -> nn.Module:
+                               scaling: str = "dynamic", history_len: int = 16,
+                               grad_scaler: Optional["GradScaler"] = None) -> nn.Module:
     """Replace, in place and post-order, every nn.Linear child that
     module_filter_fn(child, fully_qualified_name) accepts (default:
-    default_module_filter) with a Float8Linear sharing its weight."""
+    default_module_filter) with a Float8Linear sharing its weight.  With
+    grad_scaler, the fp16 layers unscale and check their weight gradients in
+    the wgrad GEMM's epilogue with that scaler."""
     accept = module_filter_fn or default_module_filter
     # every (parent, attribute, module, dotted path) below the root, each
     # module after all of its own descendants; the swaps are made after the
@@ -263,7 +346,10 @@ def convert_to_float8_training(model: nn.Module,
     edges = list(_descendants_post_order(model, ()))
     for parent, attr, child, path in edges:
         if type(child) is nn.Linear and accept(child, ".".join(path)):
-            setattr(parent, attr, Float8Linear.from_float(child, scaling, history_len))
+            new = Float8Linear.from_float(child, scaling, history_len)
+            if grad_scaler is not None and new.weight.dtype == torch.float16:
+                new.attach_grad_scaler(grad_scaler)
+            setattr(parent, attr, new)
     return model
 
 
@@ -291,18 +377,23 @@ class GradScaler:
         self.growth_factor, self.backoff_factor = growth_factor, backoff_factor
         self.growth_interval = growth_interval
         self._unscaled = set()
+        self._pre_unscaled = set()  # parameters whose gradient a layer unscaled this step
 
     def scale(self, loss: torch.Tensor) -> torch.Tensor:
         # a 0-dim fp32 factor: torch's promotion keeps the loss's own dtype
         # unless it is lower, as PyTorch's GradScaler does
         return loss * self._scale.view(())
 
-    @staticmethod
-    def _grads(optimizer):
+    def _mark_unscaled(self, param):
+        """An fp16 Float8Linear wrote param's gradient already unscaled and
+        checked (wgrad epilogue): unscale_ leaves it alone this step."""
+        self._pre_unscaled.add(id(param))
+
+    def _grads(self, optimizer):
         gs = []
         for group in optimizer.param_groups:
             for p in group["params"]:
-                if p.grad is None:
+                if p.grad is None or id(p) in self._pre_unscaled:
                     continue
                 if p.grad.dtype != torch.float16 or not p.grad.is_contiguous():
                     raise TypeError("GradScaler unscales contiguous fp16 gradients only")
@@ -337,6 +428,7 @@ class GradScaler:
         amp_update_scale(self._scale, self._tracker, self._found, self.growth_factor,
                          self.backoff_factor, self.growth_interval)
         self._unscaled.clear()
+        self._pre_unscaled.clear()
 
     def get_scale(self) -> float:
         return float(self._scale.item())

@@ -144,6 +144,20 @@ FP8SG_API fp8sg_status fp8_quantize(const uint16_t* x, int64_t rows, int64_t col
                           fp8sg_scale_rec* rec, uint8_t* q, uint8_t* qT, fp8sg_stream stream);
 
 /*
+ * fp8_amax and fp8_quantize for fp16 tensors: the same definitions [FP8-TRAIN
+ * §2] with an fp16 input (x as fp16 bit patterns, decoded exactly to fp32), for
+ * a model kept in fp16 under loss scaling [PT-CH20 §20.2.2].  The record,
+ * codes, transposed codes, limits and errors are as for the bf16 calls; a NaN
+ * anywhere gives the canonical NaN amax, +-inf gives +inf.  The record pairs
+ * the two calls as it pairs fp8_amax and fp8_quantize.
+ */
+FP8SG_API fp8sg_status fp8_amax_f16(const uint16_t* x, int64_t n, fp8sg_scale_rec* rec,
+                                    fp8sg_stream stream);
+FP8SG_API fp8sg_status fp8_quantize_f16(const uint16_t* x, int64_t rows, int64_t cols,
+                                        fp8sg_format fmt, fp8sg_scale_rec* rec, uint8_t* q,
+                                        uint8_t* qT, fp8sg_stream stream);
+
+/*
  * fp8_quantize with the amax supplied by the caller [FP8-TRAIN §2: the scale
  * is fp8_max / amax in fp64, then x * scale, clamp, cast].  The scale, inverse
  * and codes are those fp8_quantize computes from a record whose amax is *amax;

@@ -85,3 +85,21 @@ def decode_out(out_fmt, arr):
     if out_fmt is None:
         return np.asarray(arr, np.float64)
     return O.decode(out_fmt, arr)
+
+
+def check_unscaled_values(got_f16, c_ref, absdot, K, loss_scale, what=""):
+    """fp16 gradients unscaled in a GEMM epilogue, g = fp16(fl32(h) / S) with
+    h = fp16(c) and a power-of-two loss scale S, against the oracle's GEMM value
+    c (fp32, before the unscale): S * g is h exactly unless g is an fp16
+    subnormal (then within S * 2^-25).  Bound: the summation bound above, one
+    fp16 ulp of the value, and that subnormal step."""
+    got = np.asarray(decode_out(O.F16, got_f16), np.float64).reshape(-1) * loss_scale
+    c_ref = np.asarray(c_ref, np.float64).reshape(-1)
+    absdot = np.asarray(absdot, np.float64).reshape(-1)
+    err = np.abs(got - c_ref)
+    bound = ((GROUP_ALIGN + 2.0 * gamma(K)) * absdot + 2.0 * U32 * np.abs(c_ref)
+             + ulp_at(O.F16, c_ref) + loss_scale * 2.0 ** -25)
+    bad = np.nonzero(~(err <= bound))[0]
+    assert bad.size == 0, f"{what}: {bad.size} unscaled values outside the bound, first {bad[:4]}"
+    scale = np.abs(c_ref).max() if c_ref.size else 0.0
+    return float(err.max() / scale) if scale > 0 else 0.0

@@ -58,6 +58,19 @@ def P(v):
     return ctypes.c_void_p(v)
 
 
+def test_f16_cast_validation():
+    L = F.lib()
+    assert L.fp8_amax_f16(P(A16), 16, P(0), P(0)) == ENULL
+    assert L.fp8_amax_f16(P(0), 16, P(A16), P(0)) == ENULL
+    assert L.fp8_amax_f16(P(A16), -1, P(A16), P(0)) == ESHAPE
+    assert L.fp8_amax_f16(P(MIS), 16, P(A16), P(0)) == EALIGN
+    q = L.fp8_quantize_f16
+    assert q(P(A16), 4, 4, 7, P(A16), P(A16), P(0), P(0)) == EFORMAT
+    assert q(P(A16), -1, 4, 0, P(A16), P(A16), P(0), P(0)) == ESHAPE
+    assert q(P(A16), 4, 4, 0, P(0), P(A16), P(0), P(0)) == ENULL
+    assert q(P(A16), 4, 4, 0, P(A16), P(A16), P(MIS), P(0)) == EALIGN
+
+
 def test_noalloc_norm_validation():
     """amp_unscale_check_norm_noalloc refuses, before any launch, a list that
     needs more than the scratch's FP8SG_NOALLOC_NORM_SLOTS slots, and bad

@@ -243,3 +243,98 @@ def test_backward_scratch_is_kept_across_steps():
         f8(x).backward(torch.randn(64, 256, dtype=torch.bfloat16, device=DEV))
         ids.append(id(f8._ws[1]))
     assert len(set(ids)) == 1
+
+
+def dev_f16(bits, requires_grad=False):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.float16).to(DEV)
+    return t.requires_grad_(requires_grad)
+
+
+def test_fp16_float8_linear_with_grad_scaler_matches_oracle():
+    """An fp16 layer under loss scaling [PT-CH20 §20.2.2]: fp16 x and W cast
+    by the fp16-input kernels, fp16 y; the output gradient carries the loss
+    scale S, the input gradient keeps it, the weight gradient leaves the wgrad
+    GEMM unscaled and checked with the attached scaler's scale, and the
+    scaler's unscale_ leaves that gradient alone.  Every output against the
+    oracle's composition."""
+    from tests.parity import check_unscaled_values
+    M, K, N, S = 192, 256, 160, 1024.0
+    x_h = W.normal_f16(91, 1, (M, K), 1.0)
+    w_h = W.normal_f16(91, 2, (N, K), 0.02)
+    gy_h = W.normal_f16(91, 3, (M, N), 1e-3 * S)   # carries the loss scale
+    lin = nn.Linear(K, N, bias=False, dtype=torch.float16, device=DEV)
+    with torch.no_grad():
+        lin.weight.copy_(dev_f16(w_h))
+    scaler = FN.GradScaler(init_scale=S, device=DEV)
+    f8 = FN.Float8Linear.from_float(lin).attach_grad_scaler(scaler)
+    x = dev_f16(x_h, requires_grad=True)
+    y = f8(x)
+    assert y.dtype == torch.float16
+    y.backward(dev_f16(gy_h))
+    torch.cuda.synchronize()
+    xq = O.to_fp8(x_h, O.E4M3FN, in_fmt=O.F16)
+    wq = O.to_fp8(w_h, O.E4M3FN, in_fmt=O.F16)
+    gq = O.to_fp8(gy_h, O.E5M2, in_fmt=O.F16)
+    full = lambda a, b: [v.reshape(-1) for v in np.meshgrid(np.arange(a), np.arange(b), indexing="ij")]
+    # y: fp16 forward output
+    ii, jj = full(M, N)
+    c = O.gemm(xq.q, O.E4M3FN, wq.q, O.E4M3FN, xq.sc.inv, wq.sc.inv)
+    ad = O.gemm_absdot_at(xq.q, O.E4M3FN, wq.q, O.E4M3FN, xq.sc.inv, wq.sc.inv, ii, jj)
+    check_gemm_values(O.decode(O.F16, host_u16(y)).reshape(-1), c.reshape(-1), ad, K, O.F16, "y")
+    # gx: fp16, still carrying S
+    ii, jj = full(M, K)
+    c = O.gemm(gq.q, O.E5M2, wq.qT, O.E4M3FN, gq.sc.inv, wq.sc.inv)
+    ad = O.gemm_absdot_at(gq.q, O.E5M2, wq.qT, O.E4M3FN, gq.sc.inv, wq.sc.inv, ii, jj)
+    check_gemm_values(O.decode(O.F16, host_u16(x.grad)).reshape(-1), c.reshape(-1), ad, N, O.F16,
+                      "gx")
+    # gW: unscaled by S in the epilogue
+    ii, jj = full(N, K)
+    c = O.gemm(gq.qT, O.E5M2, xq.qT, O.E4M3FN, gq.sc.inv, xq.sc.inv)
+    ad = O.gemm_absdot_at(gq.qT, O.E5M2, xq.qT, O.E4M3FN, gq.sc.inv, xq.sc.inv, ii, jj)
+    gw_bits = host_u16(lin.weight.grad).copy()
+    check_unscaled_values(gw_bits, c, ad, M, S, "gW")
+    # the scaler: no non-finite value, unscale_ leaves the layer's gradient alone
+    opt = torch.optim.SGD([lin.weight], lr=0.0)
+    scaler.unscale_(opt)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(lin.weight.grad), gw_bits)
+    assert scaler.state()[2] == 0
+    scaler.step(opt)
+    scaler.update()
+    assert scaler.state()[:2] == (S, 1)
+
+
+def test_fp16_two_layer_model_skips_on_overflow():
+    """A two-layer fp16 model converted with a GradScaler: a loss scale that
+    overflows an fp16 weight gradient sets the flag in the wgrad epilogue, the
+    optimizer step is skipped, the scale halves; with a sane scale the next step
+    is taken."""
+    torch.manual_seed(3)
+    K, F_, T = 128, 256, 64
+    model = nn.Sequential(nn.Linear(K, F_, bias=False), nn.ReLU(),
+                          nn.Linear(F_, K, bias=False)).to(DEV, torch.float16)
+    scaler = FN.GradScaler(init_scale=2.0 ** 30, device=DEV)
+    FN.convert_to_float8_training(model, grad_scaler=scaler)
+    assert all(isinstance(m, FN.Float8Linear) and m.grad_scaler is scaler
+               for m in (model[0], model[2]))
+    opt = torch.optim.SGD(model.parameters(), lr=1e-2)
+    x = torch.randn(T, K, dtype=torch.float16, device=DEV)
+    before = [p.detach().clone() for p in model.parameters()]
+    loss = model(x).float().square().mean()
+    scaler.scale(loss).backward()
+    scaler.step(opt)
+    torch.cuda.synchronize()
+    assert scaler.state()[2] == 1  # overflow seen
+    assert all(torch.equal(a, b) for a, b in zip(before, model.parameters()))  # step skipped
+    scaler.update()
+    assert scaler.get_scale() == 2.0 ** 29
+    # a scale that keeps the gradients finite: the step is taken
+    scaler._scale.fill_(256.0)
+    opt.zero_grad(set_to_none=True)
+    loss = model(x).float().square().mean()
+    scaler.scale(loss).backward()
+    scaler.step(opt)
+    torch.cuda.synchronize()
+    assert scaler.state()[2] == 0
+    scaler.update()
+    assert any(not torch.equal(a, b) for a, b in zip(before, model.parameters()))
