@@ -305,17 +305,20 @@ struct HistLoads {
 };
 
 // Transposed stores of 128 x 128 code tiles (quantize.hip, rowwise.hip).
-// Tile t of a tiles_r x tiles_c grid, walked in groups of 8 row tiles: down
-// the 8 rows of a group first, then across its columns.  64 consecutive tiles
-// cover 8 x 8, so the transposed copies' stores of neighbouring blocks land in
-// adjacent 128-byte pieces of the same rows (a single row band would spread
-// them over 128 rows at one power-of-two stride).
+// Tile t of a tiles_r x tiles_c grid, walked in groups of 2 row tiles: down
+// the 2 rows of a group first, then across its columns.  The blocks in flight
+// together then cover a short, wide band: their row-major stores and loads
+// form long runs in each row, and their transposed stores land in pairs of
+// adjacent 128-byte pieces.  Measured at HBM scale against groups of 1, 4, 8,
+// 16 and 32 rows and a diagonal and a hashed walk, 2 rows was fastest or
+// near it on every shape (16384^2: 206 -> 199 us; 8192 x 14336: 96 -> 89 us;
+// 8192 x 28672: 197 -> 178 us against 8-row groups).
 // In 32-bit arithmetic (64-bit division is a long software loop): with rows,
 // cols <= FP8SG_MAX_DIM and rows * cols <= FP8SG_MAX_ELEMS there are fewer
 // than 2^24 tiles and 8 * tiles_c < 2^26.
 __host__ __device__ inline void tile_grouped(int64_t t, int64_t tiles_r, int64_t tiles_c,
                                              int64_t& rt, int64_t& ct) {
-  constexpr uint32_t G = 8;
+  constexpr uint32_t G = 2;
   const uint32_t t32 = (uint32_t)t, tr = (uint32_t)tiles_r;
   const uint32_t per = G * (uint32_t)tiles_c, g = t32 / per, first = g * G;
   const uint32_t gs = tr - first < G ? tr - first : G;

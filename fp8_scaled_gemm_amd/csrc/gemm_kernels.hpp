@@ -397,10 +397,20 @@ __device__ __forceinline__ void tile_of(int nbm, int nbn, int& tm, int& tn) {
 // M = 14336 in exactly 64 tile rows: the MLP block's weight-gradient GEMMs then
 // have 1024 tiles, four rounds over 256 CUs with none idle, instead of 896
 // (the last of four rounds half empty).  The launcher picks it by that count.
+//
+// TR (transposed roles): the launcher swaps the operands, so the kernel forms
+// C^T = B A^T with 224-row tiles along the original N (p.M and p.N are the
+// original N and M, p.A and p.B the original B and A) and writes C itself:
+// the MFMA takes the A-slot fragment first, so a lane's four accumulators are
+// again four consecutive columns of C, and the epilogue stages each tile
+// transposed.  That fits N = 14336 in 64 tiles when M = 4096 does not fit 224
+// (the MLP block's down-projection weight gradient: 1024 tiles, four full
+// rounds, instead of 896 tiles of 256 x 256).
 // ---------------------------------------------------------------------------
-template <int FA, int FB, int OUT, bool RAGGED_K, bool RW, int BM = 256>
+template <int FA, int FB, int OUT, bool RAGGED_K, bool RW, int BM = 256, bool TR = false>
 __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
   static_assert(BM == 256 || BM == 224, "tile rows");
+  static_assert(!(TR && RW), "transposed roles: per-tensor scaling only");
   constexpr int BN = 256;
   constexpr int kTM = BM / 32, kTN = 4;
   constexpr int kLoads = 256 / 8 / 4;  // 1 KB loads per group wave per B stage: 8
@@ -524,8 +534,10 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], FB,
-                                                                     FA, 0, 0, 0, 0);
+        acc[i][j] = TR ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], FA,
+                                                                          FB, 0, 0, 0, 0)
+                       : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], FB,
+                                                                          FA, 0, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (grp == 0) wait_vmcnt<0>();  // A of t + 1 has landed
     barrier();
@@ -553,18 +565,32 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
 
   const int wr0 = grp * (BM / 2), wc0 = wq * 64;
   const Alpha<RW, kTM, kTN> alpha(p, bm + wr0, bn + wc0, lane);
+  // Block (i, j) of this lane, in the C tile: row r, columns col .. col + 3.
+  // The C tile is BM x 256 (rows along p.M), or 256 x BM under TR (rows along
+  // p.N, which is then the original M); C's rows are c_rows long.
+  auto tile_rc = [&](int i, int j, int& r, int& col) {
+    if constexpr (TR) {
+      r = wc0 + 16 * j + (lane & 15);
+      col = wr0 + 16 * i + 4 * (lane >> 4);
+    } else {
+      r = wr0 + 16 * i + (lane & 15);
+      col = wc0 + 16 * j + 4 * (lane >> 4);
+    }
+  };
+  const int64_t c_rows = TR ? N : M, c_cols = TR ? M : N;
+  const int64_t row0 = TR ? bn : bm, col0 = TR ? bm : bn;
   if constexpr (OUT == FP8SG_OUT_F32) {
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
-      const int64_t m = bm + wr0 + 16 * i + (lane & 15);
-      if (m >= M) continue;
 #pragma unroll
       for (int j = 0; j < kTN; ++j) {
-        const int64_t n = bn + wc0 + 16 * j + 4 * (lane >> 4);
-        if (n >= N) continue;
+        int r, col;
+        tile_rc(i, j, r, col);
+        const int64_t m = row0 + r, n = col0 + col;
+        if (m >= c_rows || n >= c_cols) continue;
         v4f c = acc[i][j];
         alpha.apply(c, i, j);
-        store4<OUT>(p.C, m * N + n, c);
+        store4<OUT>(p.C, m * c_cols + n, c);
       }
     }
   } else {
@@ -579,10 +605,10 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
     barrier();
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
-      const int r = wr0 + 16 * i + (lane & 15);
 #pragma unroll
       for (int j = 0; j < kTN; ++j) {
-        const int col = wc0 + 16 * j + 4 * (lane >> 4);
+        int r, col;
+        tile_rc(i, j, r, col);
         v4f c = acc[i][j];
         alpha.apply(c, i, j);
         const int off = (((col >> 3) ^ (r & 31)) << 4) + (col & 7) * 2;
@@ -595,27 +621,29 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
     if constexpr (OUT == kOutF16Unscale) us.flag(p, lane);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     barrier();
-    constexpr int kChunks = BN / 8;
-    constexpr int kRowsPerPass = 512 / kChunks;
-    const int cc = threadIdx.x % kChunks;
+    // the staged tile, 16-byte chunks of 8 columns: BM rows x 32 chunks, or
+    // under TR 256 rows x BM / 8 chunks (28 at BM = 224)
+    constexpr int kChunks = TR ? BM / 8 : BN / 8;
 #pragma unroll
-    for (int pass = 0; pass < BM / kRowsPerPass; ++pass) {
-      const int r = pass * kRowsPerPass + threadIdx.x / kChunks;
+    for (int pass = 0; pass < BM / 16; ++pass) {
+      const int id = pass * 512 + (int)threadIdx.x;
+      const int r = id / kChunks, cc = id % kChunks;
       const uint4 v = *reinterpret_cast<const uint4*>(crow(r) + ((cc ^ (r & 31)) << 4));
-      const int64_t m = bm + r, n = bn + 8 * cc;
-      if (m < M && n < N)
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + m * N + n) = v;
+      const int64_t m = row0 + r, n = col0 + 8 * cc;
+      if (m < c_rows && n < c_cols)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + m * c_cols + n) = v;
     }
   }
 }
 
-template <int FA, int FB, int OUT, bool RW, int BM>
+// TR: p is the problem with its operands swapped (see k_gemm_pingpong).
+template <int FA, int FB, int OUT, bool RW, int BM, bool TR = false>
 static hipError_t launch_pingpong(const GemmProblem& p, hipStream_t stream) {
   const unsigned nb = (unsigned)(((p.M + BM - 1) / BM) * ((p.N + 255) / 256));
   if (p.K % kBK == 0)
-    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, false, RW, BM>), dim3(nb), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, false, RW, BM, TR>), dim3(nb), dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, true, RW, BM>), dim3(nb), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, true, RW, BM, TR>), dim3(nb), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -650,12 +678,29 @@ template <int FA, int FB, int OUT, bool RW>
 static hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
   // 256 x 256 tiles once there are enough of them to fill the chip; the
   // per-block buffer descriptors address a 256-row panel with 32-bit offsets.
-  // 224-row tiles where their rounds over the CUs take clearly less time.
+  // 224-row tiles (along M, or along N with the operands' roles swapped)
+  // where their rounds over the CUs take clearly less time.
   const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
   if (big >= 128 && p.K > 0 && p.K * 256 < (1ll << 31)) {
     const int cus = device_cus();
-    if (cus > 0 && tile_rounds_cost(p.M, p.N, 224, cus) * 100 < tile_rounds_cost(p.M, p.N, 256, cus) * 95)
-      return launch_pingpong<FA, FB, OUT, RW, 224>(p, stream);
+    if (cus > 0) {
+      const int64_t c256 = tile_rounds_cost(p.M, p.N, 256, cus);
+      const int64_t c224 = tile_rounds_cost(p.M, p.N, 224, cus);
+      if constexpr (!RW) {
+        const int64_t c224t = tile_rounds_cost(p.N, p.M, 224, cus);
+        if (c224t * 100 < (c224 < c256 ? c224 : c256) * 95) {
+          GemmProblem q = p;
+          q.A = p.B;
+          q.B = p.A;
+          q.inv_a = p.inv_b;
+          q.inv_b = p.inv_a;
+          q.M = p.N;
+          q.N = p.M;
+          return launch_pingpong<FB, FA, OUT, RW, 224, true>(q, stream);
+        }
+      }
+      if (c224 * 100 < c256 * 95) return launch_pingpong<FA, FB, OUT, RW, 224>(p, stream);
+    }
     return launch_pingpong<FA, FB, OUT, RW, 256>(p, stream);
   }
   return launch_cfg<128, 128, 2, 2, FA, FB, OUT, RW>(p, stream);

@@ -16,9 +16,9 @@
 // so both the row-wise writes and the column-wise reads spread over the
 // banks), transposed in 4x4-byte blocks with byte permutes, and stored to qT
 // with 16-byte stores, 8 lanes per 128-byte row segment.  Tiles are walked in
-// groups of 8 row tiles (tile_grouped), so the transposed stores of blocks in
-// flight together form runs longer than one tile's 128 bytes.  HBM traffic is
-// the algorithmic 2 B read + 1 B + 1 B written per element.
+// groups of 2 row tiles (tile_grouped): the blocks in flight together cover a
+// short, wide band of the tensor.  HBM traffic is the algorithmic 2 B read +
+// 1 B + 1 B written per element.
 //
 // Delayed scaling [PT-CH20 §20.5.9: each FP8 op keeps an amax history of its
 // input; the scale comes from the amax of earlier steps]: with a history the

@@ -3,7 +3,9 @@ workloads' own operands; the epilogue factor's rounding; empty contractions at
 the 256 x 256 kernel's sizes.
 
 The square layer (4096^3: forward, dgrad, wgrad) and the MLP block's down
-projection (8192 x 4096 x 14336) run on the 256 x 256 LDS-DMA kernel.  Their
+projection (8192 x 4096 x 14336) run on the 256 x 256 LDS-DMA kernel; the down
+projection's weight gradient (4096 x 14336 x 8192) on its 224-row form with the
+operands' roles swapped.  Their
 codes come from the library's own casts (checked bit for bit against the
 oracle's), their fp32 outputs are compared element by element with the
 oracle's sequential fp32 GEMM: the elementwise bound of tests/parity.py, the
@@ -107,6 +109,53 @@ def test_mlp_down_projection_every_output():
     check_rec(saved.w_sc, wq.sc, "W_down")
     c = gemm_f32(saved.x_q, F.E4M3FN, saved.w_q, F.E4M3FN, saved.x_sc.inv_ptr(), saved.w_sc.inv_ptr())
     check_full(c, host_u16(y), xq.q, O.E4M3FN, wq.q, O.E4M3FN, xq.sc.inv, wq.sc.inv, "down fwd")
+
+
+def test_mlp_down_wgrad_every_output():
+    """The MLP block's down-projection weight gradient, gW = gy^T h: M=4096,
+    N=14336, Kc=8192.  The launcher runs it with the operands' roles swapped
+    (1024 tiles of 224 along N, each written transposed); the codes come from
+    the library's casts of gy and h (checked against the oracle's), and all
+    58.7 M fp32 outputs are compared with the oracle's; the fused-unscale fp16
+    output, as the backward writes it, against the same reference."""
+    from workloads.configs import mlp_linear
+    from tests.parity import check_unscaled_values
+    from bench import loss_scaled, LOSS_SCALE
+    L = mlp_linear("down")
+    T, H, Fd = L.M, L.N, L.K  # h [T, Fd], W [H, Fd], gy [T, H]
+    h_h, gy_h = L.x(), loss_scaled(np, L.gy())
+    rec_h, rec_g = F.ScaleRec(), F.ScaleRec()
+    h_q = torch.empty((T, Fd), dtype=torch.uint8, device=DEV)
+    h_qT = torch.empty((Fd, T), dtype=torch.uint8, device=DEV)
+    g_q = torch.empty((T, H), dtype=torch.uint8, device=DEV)
+    g_qT = torch.empty((H, T), dtype=torch.uint8, device=DEV)
+    hd, gd = dev_bf16(h_h).reshape(T, Fd), dev_bf16(gy_h).reshape(T, H)
+    F.fp8_amax(hd, rec_h)
+    F.fp8_quantize(hd, F.E4M3FN, rec_h, h_q, h_qT)
+    F.fp8_amax(gd, rec_g)
+    F.fp8_quantize(gd, F.E5M2, rec_g, g_q, g_qT)
+    torch.cuda.synchronize()
+    hq, gq = O.to_fp8(h_h, O.E4M3FN), O.to_fp8(gy_h, O.E5M2)
+    assert_codes_equal(O.E4M3FN, h_qT.cpu().numpy(), hq.qT, "h^T codes")
+    assert_codes_equal(O.E5M2, g_qT.cpu().numpy(), gq.qT, "gy^T codes")
+    check_rec(rec_h, hq.sc, "h")
+    check_rec(rec_g, gq.sc, "gy")
+    del h_q, g_q
+    # gW = gy^T h: A = gy_qT [H, T], B = h_qT [Fd, T]
+    c = gemm_f32(g_qT, F.E5M2, h_qT, F.E4M3FN, rec_g.inv_ptr(), rec_h.inv_ptr())
+    scale = torch.tensor([LOSS_SCALE], dtype=torch.float32, device=DEV)
+    found = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gw = torch.empty((H, Fd), dtype=torch.float16, device=DEV)
+    F.fp8_gemm_unscale(g_qT, F.E5M2, h_qT, F.E4M3FN, rec_g.inv_ptr(), rec_h.inv_ptr(), scale, found, gw)
+    torch.cuda.synchronize()
+    assert int(found.item()) == 0
+    c_ref = O.gemm(gq.qT, O.E5M2, hq.qT, O.E4M3FN, gq.sc.inv, hq.sc.inv)
+    ii, jj = every(H, Fd)
+    absdot = O.gemm_absdot_at(gq.qT, O.E5M2, hq.qT, O.E4M3FN, gq.sc.inv, hq.sc.inv, ii, jj)
+    nw = check_gemm_values(c.reshape(-1), c_ref.reshape(-1), absdot, T, None, "down wgrad fp32")
+    assert nw <= 1e-3
+    check_unscaled_values(host_u16(gw).reshape(-1), c_ref.reshape(-1), absdot, T, LOSS_SCALE,
+                          "down wgrad fp16 unscaled")
 
 
 def alpha_pairs(n, seed):

@@ -141,7 +141,7 @@ def test_fused_unscale_never_clears_the_flag():
 
 @pytest.mark.parametrize("fa,fb", [(F.E4M3FN, F.E4M3FN), (F.E5M2, F.E4M3FN), (F.E4M3FN, F.E5M2),
                                    (F.E5M2, F.E5M2)])
-@pytest.mark.parametrize("shape", [(144, 272, 400), (2064, 4000, 1040)])
+@pytest.mark.parametrize("shape", [(144, 272, 400), (2064, 4000, 1040), (912, 13072, 400)])
 def test_gemm_unscale_is_gemm_then_unscale(fa, fb, shape):
     """fp8_gemm_unscale = fp8_gemm (fp16 out) followed by amp_unscale_check on
     its output, bit for bit, flag included."""

@@ -218,7 +218,10 @@ GEMM_SHAPES = [(16, 16, 16), (64, 256, 128), (256, 64, 64), (144, 272, 400), (27
                (4096, 2048, 256), (4000, 2064, 400), (2064, 4000, 1040),
                # 224 x 256 tiles (their rounds over the CUs are cheaper here):
                # ragged M, N and K, and M a multiple of 224
-               (4000, 4112, 400), (14000, 2048, 256), (7168, 2560, 128)]
+               (4000, 4112, 400), (14000, 2048, 256), (7168, 2560, 128),
+               # the operands' roles swapped (224-row tiles along N, the tile
+               # written transposed): ragged M, N and K
+               (912, 13072, 400)]
 
 
 @pytest.mark.parametrize("fa,fb", [(F.E4M3FN, F.E4M3FN), (F.E5M2, F.E4M3FN), (F.E4M3FN, F.E5M2),
