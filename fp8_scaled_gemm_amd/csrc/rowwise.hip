@@ -24,8 +24,9 @@
 //                directly, codes with the column scales staged in LDS and
 //                stored transposed.
 // Passes that move 256 MiB or more load x with non-temporal loads; the code
-// stores stay cached (the 8 and 16-byte pieces of one 128-byte line come from
-// different lanes and are merged in L2; written around it they cost more).
+// stores are non-temporal only once the codes alone are that large (16384^2
+// with transposed copy: 313 -> 299 us for the three passes; 8192 x 14336,
+// 235 MB of codes, is faster with cached stores: 120 against 135 us).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -207,7 +208,7 @@ __device__ __forceinline__ uint2 quant8v(uint4 v, const float* s) {
   return make_uint2(cvt4<FMT>(f0, f1, f2, f3), cvt4<FMT>(f4, f5, f6, f7));
 }
 
-template <int FMT, bool WITH_T, bool S>
+template <int FMT, bool WITH_T, bool S, bool SS>
 __global__ __launch_bounds__(kRwThreads) void k_rw_quant(RwJobs J) {
   int64_t b;
   const RowwiseArgs& a = rw_job(J, b);
@@ -228,7 +229,9 @@ __global__ __launch_bounds__(kRwThreads) void k_rw_quant(RwJobs J) {
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int64_t gr = r_tile + r0 + 16 * p;
-    v[p] = (col_ok && gr < rows) ? ld16<S>(a.x + gr * cols + gc) : make_uint4(0, 0, 0, 0);
+    // branch-free: a lane outside a ragged tile loads x's first 8 elements;
+    // their codes land only in rows and 16-row groups that are never stored
+    v[p] = ld16<S>(a.x + ((col_ok && gr < rows) ? gr * cols + gc : 0));
   }
   if (tid < kRwTile) {
     const int64_t gr = r_tile + tid;
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(kRwThreads) void k_rw_quant(RwJobs J) {
   for (int p = 0; p < 8; ++p) {
     const int r = r0 + 16 * p;
     const int64_t gr = r_tile + r;
-    if (col_ok && gr < rows) st8<false>(a.q + gr * cols + gc, quant8<FMT>(v[p], srow[r]));
+    if (col_ok && gr < rows) st8<SS>(a.q + gr * cols + gc, quant8<FMT>(v[p], srow[r]));
     if constexpr (WITH_T)
       *reinterpret_cast<uint2*>(&lds[r * 32 + ((2 * c8) ^ swz(r))]) = quant8v<FMT>(v[p], sc);
   }
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(kRwThreads) void k_rw_quant(RwJobs J) {
     if (tr0 < rows && tc0 < cols) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        st16<false>(a.qT + (tc0 + j) * rows + tr0, make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]));
+        st16<SS>(a.qT + (tc0 + j) * rows + tr0, make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]));
     }
   }
 }
@@ -294,7 +297,7 @@ static RwJobs rw_jobs(const RowwiseArgs* a, int n, int64_t (*blocks)(const Rowwi
   return J;
 }
 
-template <int FMT, bool S, bool WITH_T>
+template <int FMT, bool S, bool WITH_T, bool SS = false>
 static hipError_t launch_rw_passes(const RowwiseArgs* a, int n, hipStream_t stream) {
   int64_t nb, nred;
   const RwJobs Jt = rw_jobs(a, n, rw_tile_blocks, nb);
@@ -305,7 +308,7 @@ static hipError_t launch_rw_passes(const RowwiseArgs* a, int n, hipStream_t stre
   hipLaunchKernelGGL(k_rw_reduce<FMT>, dim3((unsigned)nred), dim3(kRwThreads), 0, stream, Jr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_rw_quant<FMT, WITH_T, S>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream,
+  hipLaunchKernelGGL((k_rw_quant<FMT, WITH_T, S, SS>), dim3((unsigned)nb), dim3(kRwThreads), 0, stream,
                      Jt);
   return hipGetLastError();
 }
@@ -314,7 +317,8 @@ static hipError_t launch_rw_passes(const RowwiseArgs* a, int n, hipStream_t stre
 template <int FMT>
 static hipError_t launch_rw_fmt(const RowwiseArgs* in, int n, hipStream_t stream) {
   RowwiseArgs a[2];
-  int64_t bytes = 0;  // the cast's traffic
+  int64_t bytes = 0;    // the cast's traffic
+  int64_t written = 0;  // its codes
   for (int j = 0; j < n; ++j) {
     a[j] = in[j];
     a[j].tiles_c = (int32_t)rw_tiles(a[j].cols);
@@ -323,8 +327,10 @@ static hipError_t launch_rw_fmt(const RowwiseArgs* in, int n, hipStream_t stream
         4 * (a[j].rows * a[j].tiles_c + (a[j].qT ? a[j].cols * rw_tiles(a[j].rows) : 0));
     if (part_bytes > a[j].rows * a[j].cols) return hipErrorInvalidValue;
     bytes += a[j].rows * a[j].cols * (a[j].qT ? 4 : 3);
+    written += a[j].rows * a[j].cols * (a[j].qT ? 2 : 1);
   }
   const bool st = bytes >= kStreamBytes;
+  if (a[0].qT && written >= kStreamBytes) return launch_rw_passes<FMT, true, true, true>(a, n, stream);
   if (a[0].qT) return st ? launch_rw_passes<FMT, true, true>(a, n, stream)
                          : launch_rw_passes<FMT, false, true>(a, n, stream);
   return st ? launch_rw_passes<FMT, true, false>(a, n, stream)
