@@ -63,6 +63,8 @@ def parse():
                    help="skip the square-layer, small-layer and autograd side lines")
     p.add_argument("--hbm-only", action="store_true",
                    help="only the HBM-scale passes (for counter runs); prints their figures")
+    p.add_argument("--square-only", action="store_true",
+                   help="only the square 4096^3 layer's side line (for counter runs)")
     p.add_argument("--copy-reference", action="store_true",
                    help="only copy 1 GiB device-to-device 5 times (calibrates the HBM byte "
                         "counters against a transfer of known size)")
@@ -285,6 +287,9 @@ def main():
     if args.hbm_only:
         hbm, hbm_kern = hbm_passes(np, torch, F, dev, T)
         print(json.dumps({"hbm_scale": hbm, "hbm_kernels_us": hbm_kern}), flush=True)
+        return
+    if args.square_only:
+        print(json.dumps({"square_layer": square_layer(np, torch, F, dev, stream, T, args)}), flush=True)
         return
 
     mlp = MlpStep(np, torch, F, dev)
