@@ -29,7 +29,7 @@ EXPORTS = ("fp8sg_status_string", "fp8sg_version", "amp_norm_workspace_len", "fp
            "fp8_scaled_linear_bwd_rowwise", "fp8_scaled_linear_bwd_unscale", "fp8_gemm_unscale",
            "fp8_scaled_linear_bwd_delayed_unscale", "fp8_scaled_linear_bwd_rowwise_unscale",
            "fp8_quantize_from_amax", "amp_unscale_check_norm_noalloc", "fp8_amax_f16",
-           "fp8_quantize_f16")
+           "fp8_quantize_f16", "fp8_gemm_kmajor", "fp8_gemm_kmajor_unscale")
 MAX_HISTORY = 1024
 MAX_DIM = 1 << 29     # largest matrix dimension an entry point takes
 MAX_ELEMS = 1 << 35   # largest tensor, in elements
@@ -83,6 +83,8 @@ def lib():
     L.fp8_amax_f16.argtypes = [P, i64, P, P]
     L.fp8_quantize_f16.argtypes = [P, i64, i64, i, P, P, P, P]
     L.fp8_gemm.argtypes = [P, i, P, i, P, P, P, i, i64, i64, i64, P]
+    L.fp8_gemm_kmajor.argtypes = [P, i, i32, P, i, i32, P, P, P, i, i64, i64, i64, P]
+    L.fp8_gemm_kmajor_unscale.argtypes = [P, i, i32, P, i, i32, P, P, P, P, P, i64, i64, i64, P]
     L.fp8_scaled_linear_fwd.argtypes = [P, P, i64, i64, i64, ctypes.POINTER(_Saved), P, i, P]
     L.fp8_scaled_linear_bwd.argtypes = [P, ctypes.POINTER(_Saved), i64, i64, i64,
                                         ctypes.POINTER(_BwdWs), P, P, i, P]
@@ -329,18 +331,55 @@ def fp8_gemm_unscale(A: torch.Tensor, fa: int, B: torch.Tensor, fb: int, inv_a_p
                                   M, N, K, _stream(stream)), "fp8_gemm_unscale")
 
 
-class LinearSaved:
-    """Device buffers the forward pass fills for the backward pass."""
+def _kmajor_args(A, a_kmajor, B, b_kmajor, C, c_dtype):
+    """Shapes of a GEMM whose operands may be stored contraction-major."""
+    a0, a1 = _need_2d(A, "A")
+    b0, b1 = _need_2d(B, "B")
+    M, K = (a1, a0) if a_kmajor else (a0, a1)
+    N = b1 if b_kmajor else b0
+    _need(A, "A", torch.uint8)
+    _need(B, "B", torch.uint8, shape=(K, N) if b_kmajor else (N, K))
+    _need(C, "C", c_dtype, shape=(M, N))
+    return M, N, K
 
-    def __init__(self, M, N, K, device="cuda", tensors=None):
+
+def fp8_gemm_kmajor(A: torch.Tensor, fa: int, a_kmajor: bool, B: torch.Tensor, fb: int,
+                    b_kmajor: bool, inv_a_ptr: int, inv_b_ptr: int, C: torch.Tensor, out: int,
+                    stream=None):
+    """fp8_gemm with A given as A^T [K, M] (a_kmajor) and/or B as B^T [K, N]
+    (b_kmajor), read in that layout: the backward GEMMs on row-major codes."""
+    M, N, K = _kmajor_args(A, a_kmajor, B, b_kmajor, C, _OUT_DTYPE.get(out))
+    _check(lib().fp8_gemm_kmajor(_ptr(A), fa, int(bool(a_kmajor)), _ptr(B), fb, int(bool(b_kmajor)),
+                                 ctypes.c_void_p(inv_a_ptr), ctypes.c_void_p(inv_b_ptr), _ptr(C), out,
+                                 M, N, K, _stream(stream)), "fp8_gemm_kmajor")
+
+
+def fp8_gemm_kmajor_unscale(A: torch.Tensor, fa: int, a_kmajor: bool, B: torch.Tensor, fb: int,
+                            b_kmajor: bool, inv_a_ptr: int, inv_b_ptr: int, scale: torch.Tensor,
+                            found_inf: torch.Tensor, C: torch.Tensor, stream=None):
+    """fp8_gemm_unscale with contraction-major operands (as fp8_gemm_kmajor)."""
+    M, N, K = _kmajor_args(A, a_kmajor, B, b_kmajor, C, torch.float16)
+    _need_scaler(scale, found_inf)
+    _check(lib().fp8_gemm_kmajor_unscale(_ptr(A), fa, int(bool(a_kmajor)), _ptr(B), fb,
+                                         int(bool(b_kmajor)), ctypes.c_void_p(inv_a_ptr),
+                                         ctypes.c_void_p(inv_b_ptr), _ptr(scale), _ptr(found_inf),
+                                         _ptr(C), M, N, K, _stream(stream)), "fp8_gemm_kmajor_unscale")
+
+
+class LinearSaved:
+    """Device buffers the forward pass fills for the backward pass.  With
+    transposed=False no transposed copies are kept (x_qT and w_qT are None):
+    the backward GEMMs read x_q and w_q contraction-major."""
+
+    def __init__(self, M, N, K, device="cuda", tensors=None, transposed=True):
         if tensors is not None:  # (x_q, x_qT, w_q, w_qT, recs) kept from an earlier forward
             self.x_q, self.x_qT, self.w_q, self.w_qT, self.recs = tensors
         else:
             u8 = dict(dtype=torch.uint8, device=device)
             self.x_q = torch.empty((M, K), **u8)
-            self.x_qT = torch.empty((K, M), **u8)
+            self.x_qT = torch.empty((K, M), **u8) if transposed else None
             self.w_q = torch.empty((N, K), **u8)
-            self.w_qT = torch.empty((K, N), **u8)
+            self.w_qT = torch.empty((K, N), **u8) if transposed else None
             self.recs = torch.zeros((2, SCALE_REC_BYTES), **u8)
         self.x_sc = ScaleRec(buf=self.recs[0])
         self.w_sc = ScaleRec(buf=self.recs[1])
@@ -355,9 +394,12 @@ class LinearSaved:
                id(self.w_sc), id(self.x_sc.buf), id(self.w_sc.buf))
         if self.__dict__.get("_ok") == key:
             return
+        if (self.x_qT is None) != (self.w_qT is None):
+            raise Fp8sgError("saved.x_qT and saved.w_qT: both tensors or both None")
         for t, name, shape in ((self.x_q, "saved.x_q", (M, K)), (self.x_qT, "saved.x_qT", (K, M)),
                                (self.w_q, "saved.w_q", (N, K)), (self.w_qT, "saved.w_qT", (K, N))):
-            _need(t, name, torch.uint8, shape=shape)
+            if t is not None or name in ("saved.x_q", "saved.w_q"):
+                _need(t, name, torch.uint8, shape=shape)
         _need_rec(self.x_sc, "saved.x_sc")
         _need_rec(self.w_sc, "saved.w_sc")
         self._ok = key
@@ -375,10 +417,13 @@ class LinearSaved:
 
 
 class LinearBwdWs:
-    def __init__(self, M, N, device="cuda"):
+    """The backward's gradient codes; with transposed=False no transposed copy
+    (for a LinearSaved without transposed copies)."""
+
+    def __init__(self, M, N, device="cuda", transposed=True):
         u8 = dict(dtype=torch.uint8, device=device)
         self.gy_q = torch.empty((M, N), **u8)
-        self.gy_qT = torch.empty((N, M), **u8)
+        self.gy_qT = torch.empty((N, M), **u8) if transposed else None
         self.gy_sc = ScaleRec(device=device)
 
     def check(self, M, N):
@@ -386,7 +431,8 @@ class LinearBwdWs:
         if self.__dict__.get("_ok") == key:
             return
         _need(self.gy_q, "ws.gy_q", torch.uint8, shape=(M, N))
-        _need(self.gy_qT, "ws.gy_qT", torch.uint8, shape=(N, M))
+        if self.gy_qT is not None:
+            _need(self.gy_qT, "ws.gy_qT", torch.uint8, shape=(N, M))
         _need_rec(self.gy_sc, "ws.gy_sc")
         self._ok = key
 

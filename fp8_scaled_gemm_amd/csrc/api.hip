@@ -54,8 +54,11 @@ fp8sg_status check_gemm(const void* A, int fa, const void* B, int fb, const void
   return FP8SG_OK;
 }
 
+// x_qT and w_qT are both given (the backward GEMMs read the transposed
+// copies) or both null (they read the row-major codes, contraction-major).
 fp8sg_status check_saved(const fp8_linear_saved* s) {
-  if (!s || !s->x_q || !s->x_qT || !s->w_q || !s->w_qT || !s->x_sc || !s->w_sc) return FP8SG_ERR_NULL;
+  if (!s || !s->x_q || !s->w_q || !s->x_sc || !s->w_sc) return FP8SG_ERR_NULL;
+  if (!s->x_qT != !s->w_qT) return FP8SG_ERR_NULL;
   if (!aligned16(s->x_q) || !aligned16(s->x_qT) || !aligned16(s->w_q) || !aligned16(s->w_qT) ||
       !aligned(s->x_sc, 8) || !aligned(s->w_sc, 8))
     return FP8SG_ERR_ALIGN;
@@ -172,6 +175,29 @@ fp8sg_status fp8_gemm(const uint8_t* A, fp8sg_format fa, const uint8_t* B, fp8sg
   return hip_status(launch_gemm(p, fa, fb, out, S(stream)));
 }
 
+fp8sg_status fp8_gemm_kmajor(const uint8_t* A, fp8sg_format fa, int32_t a_kmajor, const uint8_t* B,
+                             fp8sg_format fb, int32_t b_kmajor, const double* inv_a,
+                             const double* inv_b, void* C, fp8sg_out out, int64_t M, int64_t N,
+                             int64_t Kc, fp8sg_stream stream) {
+  fp8sg_status st = check_gemm(A, fa, B, fb, inv_a, inv_b, C, out, M, N, Kc);
+  if (st != FP8SG_OK) return st;
+  GemmProblem p{A, B, C, inv_a, inv_b, M, N, Kc};
+  return hip_status(launch_gemm_km(p, fa, fb, out, a_kmajor != 0, b_kmajor != 0, S(stream)));
+}
+
+fp8sg_status fp8_gemm_kmajor_unscale(const uint8_t* A, fp8sg_format fa, int32_t a_kmajor,
+                                     const uint8_t* B, fp8sg_format fb, int32_t b_kmajor,
+                                     const double* inv_a, const double* inv_b,
+                                     const float* amp_scale, int32_t* found_inf, uint16_t* C,
+                                     int64_t M, int64_t N, int64_t Kc, fp8sg_stream stream) {
+  fp8sg_status st = check_gemm(A, fa, B, fb, inv_a, inv_b, C, FP8SG_OUT_F16, M, N, Kc);
+  if (st != FP8SG_OK) return st;
+  if (!amp_scale || !found_inf) return FP8SG_ERR_NULL;
+  if (!aligned(amp_scale, 4) || !aligned(found_inf, 4)) return FP8SG_ERR_ALIGN;
+  GemmProblem p{A, B, C, inv_a, inv_b, M, N, Kc, amp_scale, found_inf};
+  return hip_status(launch_gemm_km(p, fa, fb, kOutF16Unscale, a_kmajor != 0, b_kmajor != 0, S(stream)));
+}
+
 fp8sg_status fp8_quantize_rowwise(const uint16_t* x, int64_t rows, int64_t cols, fp8sg_format fmt,
                                   float* row_amax, double* row_inv, uint8_t* q, float* col_amax,
                                   double* col_inv, uint8_t* qT, fp8sg_stream stream) {
@@ -283,7 +309,10 @@ fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64
   if (!gy || !ws || !gx || !gw) return FP8SG_ERR_NULL;
   fp8sg_status st = check_saved(saved);
   if (st != FP8SG_OK) return st;
-  if (!ws->gy_q || !ws->gy_qT || !ws->gy_sc) return FP8SG_ERR_NULL;
+  // without transposed copies (saved and workspace alike), the backward GEMMs
+  // read the row-major codes contraction-major
+  const bool kmajor = !saved->x_qT;
+  if (!ws->gy_q || !ws->gy_sc || (!ws->gy_qT != kmajor)) return FP8SG_ERR_NULL;
   if (!out_ok(out)) return FP8SG_ERR_FORMAT;
   if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K) || !gemm_ok(M, N, K))
     return FP8SG_ERR_SHAPE;
@@ -313,6 +342,15 @@ fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64
   }
   if (e != hipSuccess) return FP8SG_ERR_HIP;
 
+  if (kmajor) {
+    // dgrad: gy codes [M, N] x W codes [N, K] (contraction-major B); wgrad:
+    // gy codes as A^T [M, N] x x codes as B^T [M, K]
+    GemmProblem dg{ws->gy_q, saved->w_q, gx, &ws->gy_sc->inv, &saved->w_sc->inv, M, K, N,
+                   amp_scale, found_inf};
+    GemmProblem wg{ws->gy_q, saved->x_q, gw, &ws->gy_sc->inv, &saved->x_sc->inv, N, K, M,
+                   amp_scale, found_inf};
+    return hip_status(launch_gemm_km_pair(dg, wg, amp_scale ? kOutF16Unscale : (int)out, s));
+  }
   GemmProblem dg{ws->gy_q, saved->w_qT, gx, &ws->gy_sc->inv, &saved->w_sc->inv, M, K, N,
                  amp_scale, found_inf};
   GemmProblem wg{ws->gy_qT, saved->x_qT, gw, &ws->gy_sc->inv, &saved->x_sc->inv, N, K, M,

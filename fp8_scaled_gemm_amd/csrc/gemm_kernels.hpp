@@ -149,8 +149,14 @@ struct Alpha {
 // the other half of a double-buffered LDS tile.  Each wave owns a (BM/WM) x
 // (BN/WN) sub-tile of 16 x 16 blocks; results are stored as one 8-byte
 // (bf16/fp16) or 16-byte (fp32) write per lane and block.
-template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW>
+// TA / TB: the operand is stored contraction-major (A^T [K, M], B^T [K, N]);
+// its k-tile is staged as 128 rows of 128 bytes (one per k, the tile's 128
+// output rows or columns) and its fragments are read with ds_read_b64_tr_b8,
+// as in the large-tile kernel below.
+template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW, bool TA = false,
+          bool TB = false>
 __device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, int by) {
+  static_assert(!(TA || TB) || (BM == 128 && BN == 128), "contraction-major: 128 x 128 tiles");
   using Cfg = GemmCfg<BM, BN, WM, WN>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* As = smem;                  // [2][BM][128]
@@ -167,23 +173,38 @@ __device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, in
 
   // global -> register prefetch of one k-tile
   uint4 ra[Cfg::kLoadsA], rb[Cfg::kLoadsB];
+  // chunk c of a k-tile: LDS row c / 8, 16-byte chunk c % 8; a row-major
+  // operand's row is an output row (column) and the chunk 16 k values, a
+  // contraction-major one's row is a k and the chunk 16 output rows (columns)
   auto load_tile = [&](int kt) {
     const int64_t k0 = (int64_t)kt * kBK;
 #pragma unroll
     for (int i = 0; i < Cfg::kLoadsA; ++i) {
       const int c = tid + i * Cfg::kThreads;
       const int r = c >> 3, kc = c & 7;
-      const int64_t gr = bm + r, gk = k0 + 16 * kc;
-      ra[i] = (gr < M && gk < K) ? *reinterpret_cast<const uint4*>(p.A + gr * K + gk)
-                                 : make_uint4(0, 0, 0, 0);
+      if constexpr (TA) {
+        const int64_t gk = k0 + r, gm = bm + 16 * kc;
+        ra[i] = (gk < K && gm < M) ? *reinterpret_cast<const uint4*>(p.A + gk * M + gm)
+                                   : make_uint4(0, 0, 0, 0);
+      } else {
+        const int64_t gr = bm + r, gk = k0 + 16 * kc;
+        ra[i] = (gr < M && gk < K) ? *reinterpret_cast<const uint4*>(p.A + gr * K + gk)
+                                   : make_uint4(0, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < Cfg::kLoadsB; ++i) {
       const int c = tid + i * Cfg::kThreads;
       const int r = c >> 3, kc = c & 7;
-      const int64_t gr = bn + r, gk = k0 + 16 * kc;
-      rb[i] = (gr < N && gk < K) ? *reinterpret_cast<const uint4*>(p.B + gr * K + gk)
-                                 : make_uint4(0, 0, 0, 0);
+      if constexpr (TB) {
+        const int64_t gk = k0 + r, gn = bn + 16 * kc;
+        rb[i] = (gk < K && gn < N) ? *reinterpret_cast<const uint4*>(p.B + gk * N + gn)
+                                   : make_uint4(0, 0, 0, 0);
+      } else {
+        const int64_t gr = bn + r, gk = k0 + 16 * kc;
+        rb[i] = (gr < N && gk < K) ? *reinterpret_cast<const uint4*>(p.B + gr * K + gk)
+                                   : make_uint4(0, 0, 0, 0);
+      }
     }
   };
   auto store_tile = [&](int buf) {
@@ -213,6 +234,21 @@ __device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, in
   // instruction sums them in.
   const int frow = lane & 15;
   const int fchunk = 2 * (lane >> 4);
+  // fragment of output block blk from a contraction-major k-tile (128 rows
+  // of 128 B): four transposed 8-byte reads
+  typedef int v2i_t __attribute__((ext_vector_type(2)));
+  auto frag_t = [&](const uint8_t* base, int blk) {
+    v8i out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 32 * (lane >> 4) + 8 * r + (frow >> 1);
+      const v2i_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) v2i_t*)(base + lds_off(row, blk) + 8 * (frow & 1)));
+      out[2 * r] = t.x;
+      out[2 * r + 1] = t.y;
+    }
+    return out;
+  };
 
   if (nk > 0) {
     load_tile(0);
@@ -227,17 +263,26 @@ __device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, in
     v8i bf[Cfg::kTN];
 #pragma unroll
     for (int j = 0; j < Cfg::kTN; ++j) {
-      const int r = wn * (BN / WN) + 16 * j + frow;
-      const uint4 lo = *reinterpret_cast<const uint4*>(b + lds_off(r, fchunk));
-      const uint4 hi = *reinterpret_cast<const uint4*>(b + lds_off(r, fchunk + 1));
-      bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      if constexpr (TB) {
+        bf[j] = frag_t(b, wn * (BN / WN) / 16 + j);
+      } else {
+        const int r = wn * (BN / WN) + 16 * j + frow;
+        const uint4 lo = *reinterpret_cast<const uint4*>(b + lds_off(r, fchunk));
+        const uint4 hi = *reinterpret_cast<const uint4*>(b + lds_off(r, fchunk + 1));
+        bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
     }
 #pragma unroll
     for (int i = 0; i < Cfg::kTM; ++i) {
-      const int r = wm * (BM / WM) + 16 * i + frow;
-      const uint4 lo = *reinterpret_cast<const uint4*>(a + lds_off(r, fchunk));
-      const uint4 hi = *reinterpret_cast<const uint4*>(a + lds_off(r, fchunk + 1));
-      const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      v8i af;
+      if constexpr (TA) {
+        af = frag_t(a, wm * (BM / WM) / 16 + i);
+      } else {
+        const int r = wm * (BM / WM) + 16 * i + frow;
+        const uint4 lo = *reinterpret_cast<const uint4*>(a + lds_off(r, fchunk));
+        const uint4 hi = *reinterpret_cast<const uint4*>(a + lds_off(r, fchunk + 1));
+        af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
 #pragma unroll
       for (int j = 0; j < Cfg::kTN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], FB, FA,
@@ -270,19 +315,28 @@ __device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, in
   if constexpr (OUT == kOutF16Unscale) us.flag(p, lane);
 }
 
-template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW>
+template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW, bool TA = false,
+          bool TB = false>
 __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(GemmProblem p) {
-  gemm_small_tile<BM, BN, WM, WN, FA, FB, OUT, RW>(p, blockIdx.x, blockIdx.y);
+  gemm_small_tile<BM, BN, WM, WN, FA, FB, OUT, RW, TA, TB>(p, blockIdx.x, blockIdx.y);
 }
 
 // Two independent small problems of the same kind in one launch (the small
 // backward pass's dgrad and wgrad, where launches dominate): blockIdx.z picks
 // the problem; blocks past its tiles leave at once.
-template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW>
+template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW, bool TA0 = false,
+          bool TB0 = false, bool TA1 = false, bool TB1 = false>
 __global__ __launch_bounds__(WM* WN* kWave) void k_gemm2(GemmProblem p0, GemmProblem p1) {
   const GemmProblem& p = blockIdx.z ? p1 : p0;
   if ((int64_t)blockIdx.y * BM >= p.M || (int64_t)blockIdx.x * BN >= p.N) return;
-  gemm_small_tile<BM, BN, WM, WN, FA, FB, OUT, RW>(p, blockIdx.x, blockIdx.y);
+  if constexpr (TA0 == TA1 && TB0 == TB1) {
+    gemm_small_tile<BM, BN, WM, WN, FA, FB, OUT, RW, TA0, TB0>(p, blockIdx.x, blockIdx.y);
+  } else {
+    if (blockIdx.z)
+      gemm_small_tile<BM, BN, WM, WN, FA, FB, OUT, RW, TA1, TB1>(p, blockIdx.x, blockIdx.y);
+    else
+      gemm_small_tile<BM, BN, WM, WN, FA, FB, OUT, RW, TA0, TB0>(p, blockIdx.x, blockIdx.y);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -339,6 +393,17 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voff, i32x4 rsr
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+// The same with the offset split into a per-lane part and a wave-uniform
+// part, added inside the statement: the sum lives only here, so the compiler
+// keeps no per-load offset registers across the k-loop.  vbase + sbase stays
+// below 2^32 (vbase < 2^31, sbase <= kOob).
+__device__ __forceinline__ void lds_dma16_split(uint32_t lds, uint32_t vbase, uint32_t sbase, i32x4 rsrc) {
+  uint32_t tmp;
+  asm volatile("v_add_u32 %0, %1, %2\n\ts_mov_b32 m0, %3\n\ts_nop 1\n\tbuffer_load_dwordx4 %0, %4, 0 offen lds"
+               : "=&v"(tmp)
+               : "s"(sbase), "v"(vbase), "s"(lds), "s"(rsrc)
                : "memory", "m0");
 }
 
@@ -407,10 +472,26 @@ __device__ __forceinline__ void tile_of(int nbm, int nbn, int& tm, int& tn) {
 // (the MLP block's down-projection weight gradient: 1024 tiles, four full
 // rounds, instead of 896 tiles of 256 x 256).
 // ---------------------------------------------------------------------------
-template <int FA, int FB, int OUT, bool RAGGED_K, bool RW, int BM = 256, bool TR = false>
+//
+// TA / TB (operands stored contraction-major): A is given as A^T [K, M] (or B
+// as B^T [K, N]) row-major, i.e. the FP8 codes of a tensor in its own layout
+// where the GEMM contracts over its rows -- the backward GEMMs' operands,
+// without a transposed copy.  Such an operand's k-tile is staged as 128 LDS
+// rows (one per k) of 256 bytes (the tile's output rows or columns), 16-byte
+// chunk q of row r at position q ^ (r & 7), and each fragment is gathered
+// with four ds_read_b64_tr_b8: in every group of 16 lanes the 8-byte reads
+// of lanes 2i and 2i + 1 form row i of an 8 x 16 byte matrix and lane j
+// receives its column j, so lane j of group g, pointing at row
+// 32 g + 8 r + j / 2, chunk half j & 1, receives k = 32 g + 8 r .. + 7 of its
+// output row or column.  Rows past K fall outside the buffer descriptor and
+// read as zero (no ragged-K test); columns past M or N are pointed outside.
+// ---------------------------------------------------------------------------
+template <int FA, int FB, int OUT, bool RAGGED_K, bool RW, int BM = 256, bool TR = false,
+          bool TA = false, bool TB = false>
 __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
   static_assert(BM == 256 || BM == 224, "tile rows");
   static_assert(!(TR && RW), "transposed roles: per-tensor scaling only");
+  static_assert(!(RW && (TA || TB)), "contraction-major operands: per-tensor scaling only");
   constexpr int BN = 256;
   constexpr int kTM = BM / 32, kTN = 4;
   constexpr int kLoads = 256 / 8 / 4;  // 1 KB loads per group wave per B stage: 8
@@ -439,8 +520,10 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
   const int nk = (int)((K + kBK - 1) / kBK);
   const int64_t rows_a = (M - bm) < BM ? (M - bm) : BM;
   const int64_t rows_b = (N - bn) < BN ? (N - bn) : BN;
-  const i32x4 ra = make_rsrc(p.A + bm * K, rows_a * K);
-  const i32x4 rb = make_rsrc(p.B + bn * K, rows_b * K);
+  // a contraction-major operand's descriptor starts at the tile's first
+  // column and ends with row K - 1
+  const i32x4 ra = TA ? make_rsrc(p.A + bm, K * M - bm) : make_rsrc(p.A + bm * K, rows_a * K);
+  const i32x4 rb = TB ? make_rsrc(p.B + bn, K * N - bn) : make_rsrc(p.B + bn * K, rows_b * K);
 
   // One operand stage (BM or 256 rows x 128 B) by wave q of a group: rows
   // [8 L q, 8 L q + 8 L), L loads of 8 rows (L = 8 for B, BM / 32 for A).
@@ -467,8 +550,40 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
       lds_dma16(dst + (wq * L + i) * 1024, off, rs);
     }
   };
-  using LA = std::integral_constant<int, kLoadsA>;
+  // A contraction-major operand's stage (128 rows of 256 B) by wave q of a
+  // group: 8 loads of 4 rows, rows 32 q + 4 i + l / 16, LDS position l % 16;
+  // the row's swizzle (4 i + l / 16) & 7 takes two values per lane (i even or
+  // odd), so a lane needs two offsets and the rest is scalar.  `ld` is the
+  // stored row length (M or N), `ncols` that of the tile's columns left.
+  const int lr4 = lane >> 4, lp = lane & 15;
+  auto t_off = [&](int sw, int64_t ld, int64_t ncols) -> uint32_t {
+    const int q = lp ^ sw;
+    return 16 * q < ncols ? (uint32_t)(lr4 * ld + 16 * q) : 0x7FFFFFF0u;
+  };
+  const uint32_t ta0 = TA ? t_off(lr4, M, M - bm) : 0u, ta1 = TA ? t_off(4 + lr4, M, M - bm) : 0u;
+  const uint32_t tb0 = TB ? t_off(lr4, N, N - bn) : 0u, tb1 = TB ? t_off(4 + lr4, N, N - bn) : 0u;
+  // (a load's 4 rows lie all below K or all past it, K being a multiple of
+  // 16; past it the scalar part is the outside offset, so no row offset can
+  // exceed (K - 4) * ld < 2^31)
+  auto issue_t = [&](int kt, uint32_t dst, const i32x4& rs, int64_t ld, uint32_t v0, uint32_t v1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t row = (int64_t)kt * kBK + 32 * wq + 4 * i;
+      const uint32_t sb = kt < nk && row < K ? (uint32_t)(row * ld) : kOob;
+      lds_dma16_split(dst + (wq * 8 + i) * 1024, (i & 1) ? v1 : v0, sb, rs);
+    }
+  };
+  using LA = std::integral_constant<int, TA ? 8 : kLoadsA>;
   using LB = std::integral_constant<int, kLoads>;
+  // this group's loads of operand A (group 0) or B (group 1) for k-tile kt
+  auto issue_a = [&](int kt, uint32_t dst) {
+    if constexpr (TA) issue_t(kt, dst, ra, M, ta0, ta1);
+    else issue(LA{}, kt, dst, ra);
+  };
+  auto issue_b = [&](int kt, uint32_t dst) {
+    if constexpr (TB) issue_t(kt, dst, rb, N, tb0, tb1);
+    else issue(LB{}, kt, dst, rb);
+  };
   v4f acc[kTM][kTN];
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
@@ -483,6 +598,27 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
     const uint4 hi = *reinterpret_cast<const uint4*>(base + lds_off2(r, fchunk + 1));
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
+  // fragment of output block blk (16 rows or columns) from a contraction-major
+  // stage: four transposed 8-byte reads (see above).  The lane reads rows
+  // 32 g + 8 r + lp / 2, all with swizzle lp / 2, so its addresses are
+  // t_base + r * 2048 + ((blk ^ lp / 2) << 4).  The XOR differs per block and
+  // lane; `sx` (lp / 2 << 4) is passed through an empty asm statement once per
+  // memory phase so the compiler recomputes the XORs there instead of keeping
+  // one address register per block live across the k-loop.
+  typedef int v2i_t __attribute__((ext_vector_type(2)));
+  const uint32_t t_base = (uint32_t)((32 * lr4 + (lp >> 1)) * 256 + 8 * (lp & 1));
+  auto frag_t = [&](const uint8_t* base, int blk, uint32_t sx) {
+    v8i out;
+    const uint32_t a0 = lds_u32(base) + t_base + (((uint32_t)blk << 4) ^ sx);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const v2i_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) v2i_t*)(uintptr_t)(a0 + 2048 * r));
+      out[2 * r] = t.x;
+      out[2 * r + 1] = t.y;
+    }
+    return out;
+  };
   const int ra0 = grp * kTM, rb0 = wq * 4;
   v8i af[kTM], bf[kTN];
   auto barrier = [&]() {
@@ -492,11 +628,11 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
 
   // Prologue: group 0 loads A0, group 1 loads B0 and B1.
   if (grp == 0) {
-    issue(LA{}, 0, lds_u32(sA0), ra);
+    issue_a(0, lds_u32(sA0));
     wait_vmcnt<0>();
   } else {
-    issue(LB{}, 0, lds_u32(sB0), rb);
-    issue(LB{}, 1, lds_u32(sB1), rb);
+    issue_b(0, lds_u32(sB0));
+    issue_b(1, lds_u32(sB1));
     wait_vmcnt<kLoads>();
   }
   barrier();
@@ -515,17 +651,21 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
     {
       const uint32_t da = lds_u32(sa(std::integral_constant<int, (P + 1) % 2>{}));
       const uint32_t db = lds_u32(sb(std::integral_constant<int, (P + 2) % 3>{}));
-      if constexpr (kLoadsA == kLoads) {
-        issue(LB{}, t + 1 + grp, grp ? db : da, grp ? rb : ra);
+      if constexpr (LA::value == kLoads && TA == TB) {
+        if constexpr (TA) issue_t(t + 1 + grp, grp ? db : da, grp ? rb : ra, grp ? N : M,
+                                  grp ? tb0 : ta0, grp ? tb1 : ta1);
+        else issue(LB{}, t + 1 + grp, grp ? db : da, grp ? rb : ra);
       } else {
-        if (grp) issue(LB{}, t + 2, db, rb);
-        else issue(LA{}, t + 1, da, ra);
+        if (grp) issue_b(t + 2, db);
+        else issue_a(t + 1, da);
       }
     }
+    uint32_t sx = (uint32_t)(lp >> 1) << 4;
+    if constexpr (TA || TB) asm volatile("" : "+v"(sx));
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) bf[j] = frag(b, rb0 + j);
+    for (int j = 0; j < kTN; ++j) bf[j] = TB ? frag_t(b, rb0 + j, sx) : frag(b, rb0 + j);
 #pragma unroll
-    for (int i = 0; i < kTM; ++i) af[i] = frag(a, ra0 + i);
+    for (int i = 0; i < kTM; ++i) af[i] = TA ? frag_t(a, ra0 + i, sx) : frag(a, ra0 + i);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     if (grp == 1) wait_vmcnt<kLoads>();  // B of t + 1 has landed
     barrier();
@@ -637,13 +777,16 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
 }
 
 // TR: p is the problem with its operands swapped (see k_gemm_pingpong).
-template <int FA, int FB, int OUT, bool RW, int BM, bool TR = false>
+template <int FA, int FB, int OUT, bool RW, int BM, bool TR = false, bool TA = false, bool TB = false>
 static hipError_t launch_pingpong(const GemmProblem& p, hipStream_t stream) {
   const unsigned nb = (unsigned)(((p.M + BM - 1) / BM) * ((p.N + 255) / 256));
-  if (p.K % kBK == 0)
-    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, false, RW, BM, TR>), dim3(nb), dim3(512), 0, stream, p);
+  // a ragged K needs a per-lane test only for a row-major operand
+  if (p.K % kBK == 0 || (TA && TB))
+    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, false, RW, BM, TR, TA, TB>), dim3(nb), dim3(512), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, true, RW, BM, TR>), dim3(nb), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_pingpong<FA, FB, OUT, true, RW, BM, TR, TA, TB>), dim3(nb), dim3(512), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
@@ -658,10 +801,10 @@ inline int64_t tile_rounds_cost(int64_t M, int64_t N, int bm, int cus) {
   return ((tiles + cus - 1) / cus) * bm;
 }
 
-template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW>
+template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW, bool TA = false, bool TB = false>
 static hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   using Cfg = GemmCfg<BM, BN, WM, WN>;
-  auto kern = k_gemm<BM, BN, WM, WN, FA, FB, OUT, RW>;
+  auto kern = k_gemm<BM, BN, WM, WN, FA, FB, OUT, RW, TA, TB>;
   static bool attr_set = false;
   if (!attr_set && Cfg::kLdsBytes > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -674,19 +817,28 @@ static hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int FA, int FB, int OUT, bool RW>
+// The large-tile kernel addresses each operand through a buffer descriptor
+// with 32-bit offsets: a row-major operand's 256-row panel, or a
+// contraction-major operand's whole K rows (its per-lane "outside" offset is
+// just below 2^31).
+template <bool TA, bool TB>
+inline bool big_tiles_fit(const GemmProblem& p) {
+  const int64_t lim = (1ll << 31) - 256;
+  return p.K > 0 && (TA ? p.K * p.M < lim : p.K * 256 < lim) && (TB ? p.K * p.N < lim : p.K * 256 < lim);
+}
+
+template <int FA, int FB, int OUT, bool RW, bool TA = false, bool TB = false>
 static hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
-  // 256 x 256 tiles once there are enough of them to fill the chip; the
-  // per-block buffer descriptors address a 256-row panel with 32-bit offsets.
+  // 256 x 256 tiles once there are enough of them to fill the chip.
   // 224-row tiles (along M, or along N with the operands' roles swapped)
   // where their rounds over the CUs take clearly less time.
   const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (big >= 128 && p.K > 0 && p.K * 256 < (1ll << 31)) {
+  if (big >= 128 && big_tiles_fit<TA, TB>(p)) {
     const int cus = device_cus();
     if (cus > 0) {
       const int64_t c256 = tile_rounds_cost(p.M, p.N, 256, cus);
       const int64_t c224 = tile_rounds_cost(p.M, p.N, 224, cus);
-      if constexpr (!RW) {
+      if constexpr (!RW && TA == TB) {
         const int64_t c224t = tile_rounds_cost(p.N, p.M, 224, cus);
         if (c224t * 100 < (c224 < c256 ? c224 : c256) * 95) {
           GemmProblem q = p;
@@ -696,30 +848,30 @@ static hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
           q.inv_b = p.inv_a;
           q.M = p.N;
           q.N = p.M;
-          return launch_pingpong<FB, FA, OUT, RW, 224, true>(q, stream);
+          return launch_pingpong<FB, FA, OUT, RW, 224, true, TB, TA>(q, stream);
         }
       }
-      if (c224 * 100 < c256 * 95) return launch_pingpong<FA, FB, OUT, RW, 224>(p, stream);
+      if (c224 * 100 < c256 * 95) return launch_pingpong<FA, FB, OUT, RW, 224, false, TA, TB>(p, stream);
     }
-    return launch_pingpong<FA, FB, OUT, RW, 256>(p, stream);
+    return launch_pingpong<FA, FB, OUT, RW, 256, false, TA, TB>(p, stream);
   }
-  return launch_cfg<128, 128, 2, 2, FA, FB, OUT, RW>(p, stream);
+  return launch_cfg<128, 128, 2, 2, FA, FB, OUT, RW, TA, TB>(p, stream);
 }
 
 // Two problems: one launch of the 128 x 128 kernel when both take it,
 // otherwise one launch each.
-template <int FA, int FB, int OUT, bool RW>
+template <int FA, int FB, int OUT, bool RW, bool TA0 = false, bool TB0 = false, bool TA1 = false,
+          bool TB1 = false>
 static hipError_t launch_tiles_pair(const GemmProblem& p0, const GemmProblem& p1, hipStream_t stream) {
-  auto big = [](const GemmProblem& p) {
-    return ((p.M + 255) / 256) * ((p.N + 255) / 256) >= 128 && p.K > 0 && p.K * 256 < (1ll << 31);
-  };
-  if (big(p0) || big(p1)) {
-    hipError_t e = p0.M && p0.N ? launch_tiles<FA, FB, OUT, RW>(p0, stream) : hipSuccess;
+  auto big0 = ((p0.M + 255) / 256) * ((p0.N + 255) / 256) >= 128 && big_tiles_fit<TA0, TB0>(p0);
+  auto big1 = ((p1.M + 255) / 256) * ((p1.N + 255) / 256) >= 128 && big_tiles_fit<TA1, TB1>(p1);
+  if (big0 || big1) {
+    hipError_t e = p0.M && p0.N ? launch_tiles<FA, FB, OUT, RW, TA0, TB0>(p0, stream) : hipSuccess;
     if (e != hipSuccess) return e;
-    return p1.M && p1.N ? launch_tiles<FA, FB, OUT, RW>(p1, stream) : hipSuccess;
+    return p1.M && p1.N ? launch_tiles<FA, FB, OUT, RW, TA1, TB1>(p1, stream) : hipSuccess;
   }
   using Cfg = GemmCfg<128, 128, 2, 2>;
-  auto kern = k_gemm2<128, 128, 2, 2, FA, FB, OUT, RW>;
+  auto kern = k_gemm2<128, 128, 2, 2, FA, FB, OUT, RW, TA0, TB0, TA1, TB1>;
   static bool attr_set = false;
   if (!attr_set && Cfg::kLdsBytes > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -736,22 +888,22 @@ static hipError_t launch_tiles_pair(const GemmProblem& p0, const GemmProblem& p1
   return hipGetLastError();
 }
 
-template <int FA, int FB, bool RW>
+template <int FA, int FB, bool RW, bool TA = false, bool TB = false>
 static hipError_t launch_out(const GemmProblem& p, int out, hipStream_t stream) {
   switch (out) {
-    case FP8SG_OUT_BF16: return launch_tiles<FA, FB, FP8SG_OUT_BF16, RW>(p, stream);
-    case FP8SG_OUT_F16: return launch_tiles<FA, FB, FP8SG_OUT_F16, RW>(p, stream);
-    default: return launch_tiles<FA, FB, FP8SG_OUT_F32, RW>(p, stream);
+    case FP8SG_OUT_BF16: return launch_tiles<FA, FB, FP8SG_OUT_BF16, RW, TA, TB>(p, stream);
+    case FP8SG_OUT_F16: return launch_tiles<FA, FB, FP8SG_OUT_F16, RW, TA, TB>(p, stream);
+    default: return launch_tiles<FA, FB, FP8SG_OUT_F32, RW, TA, TB>(p, stream);
   }
 }
 
-template <bool RW>
+template <bool RW, bool TA = false, bool TB = false>
 static hipError_t launch_gemm_any(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  if (fa == FP8SG_E4M3FN && fb == FP8SG_E4M3FN) return launch_out<0, 0, RW>(p, out, stream);
-  if (fa == FP8SG_E5M2 && fb == FP8SG_E4M3FN) return launch_out<1, 0, RW>(p, out, stream);
-  if (fa == FP8SG_E4M3FN && fb == FP8SG_E5M2) return launch_out<0, 1, RW>(p, out, stream);
-  return launch_out<1, 1, RW>(p, out, stream);
+  if (fa == FP8SG_E4M3FN && fb == FP8SG_E4M3FN) return launch_out<0, 0, RW, TA, TB>(p, out, stream);
+  if (fa == FP8SG_E5M2 && fb == FP8SG_E4M3FN) return launch_out<1, 0, RW, TA, TB>(p, out, stream);
+  if (fa == FP8SG_E4M3FN && fb == FP8SG_E5M2) return launch_out<0, 1, RW, TA, TB>(p, out, stream);
+  return launch_out<1, 1, RW, TA, TB>(p, out, stream);
 }
 
 }  // namespace fp8sg

@@ -78,6 +78,15 @@ struct GemmProblem {
 // fl32(1 / *amp_scale)), with found_inf set when a stored g is inf or NaN.
 constexpr int kOutF16Unscale = 3;
 hipError_t launch_gemm(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);
+// Contraction-major operands (gemm_km*.hip): ta / tb mean A is stored as
+// A^T [K, M] / B as B^T [K, N], row-major; out may be kOutF16Unscale.  The
+// pair is a linear layer's backward without transposed copies: dgrad
+// (gy codes, W codes as B^T) and wgrad (gy codes as A^T, x codes as B^T),
+// e5m2 x e4m3.
+hipError_t launch_gemm_km(const GemmProblem& p, int fa, int fb, int out, bool ta, bool tb,
+                          hipStream_t stream);
+hipError_t launch_gemm_km_pair(const GemmProblem& dgrad, const GemmProblem& wgrad, int out,
+                               hipStream_t stream);
 // Row-wise scaling (gemm_rowwise.hip): inv_a points to M doubles, inv_b to N;
 // element (m, n) is scaled by fl32(inv_a[m] * inv_b[n]).
 hipError_t launch_gemm_rowwise(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);

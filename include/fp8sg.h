@@ -207,15 +207,47 @@ FP8SG_API fp8sg_status fp8_gemm_unscale(const uint8_t* A, fp8sg_format fa, const
                               int64_t N, int64_t Kc, fp8sg_stream stream);
 
 /*
+ * Scaled FP8 GEMM with contraction-major operands [FP8-TRAIN §4 backward: the
+ * dgrad and wgrad products contract x, W and gy over their other dimension].
+ * As fp8_gemm, except that with a_kmajor != 0 A is stored as A^T: Kc x M
+ * codes, row-major (contiguous along M); with b_kmajor != 0 B is stored as
+ * B^T: Kc x N, row-major.  The kernels read such an operand in its own layout
+ * (LDS transpose reads), so the backward GEMMs of a linear layer can use the
+ * row-major codes of x, W and gy instead of transposed copies:
+ *   dgrad gx = gy W:   fp8_gemm_kmajor(gy_q, e5m2, 0, w_q, e4m3, 1, ..., M, K, N)
+ *   wgrad gW = gy^T x: fp8_gemm_kmajor(gy_q, e5m2, 1, x_q, e4m3, 1, ..., N, K, M)
+ * The products and their summation order are those of fp8_gemm on the
+ * transposed copies, so the results are the same bits.  Shapes, alignment,
+ * errors and the unscale variant's extra arguments as fp8_gemm and
+ * fp8_gemm_unscale.
+ */
+FP8SG_API fp8sg_status fp8_gemm_kmajor(const uint8_t* A, fp8sg_format fa, int32_t a_kmajor,
+                                       const uint8_t* B, fp8sg_format fb, int32_t b_kmajor,
+                                       const double* inv_a, const double* inv_b, void* C,
+                                       fp8sg_out out, int64_t M, int64_t N, int64_t Kc,
+                                       fp8sg_stream stream);
+FP8SG_API fp8sg_status fp8_gemm_kmajor_unscale(const uint8_t* A, fp8sg_format fa, int32_t a_kmajor,
+                                               const uint8_t* B, fp8sg_format fb, int32_t b_kmajor,
+                                               const double* inv_a, const double* inv_b,
+                                               const float* scale, int32_t* found_inf, uint16_t* C,
+                                               int64_t M, int64_t N, int64_t Kc,
+                                               fp8sg_stream stream);
+
+/*
  * What the forward pass saves for the backward pass [FP8-TRAIN §6: the
  * quantized FP8 tensors and their inverse scales, not the bf16 inputs].
- * All pointers are caller-owned device buffers.
+ * All pointers are caller-owned device buffers.  x_qT and w_qT are both given
+ * or both NULL: NULL means no transposed copies are made, and the backward
+ * GEMMs read x_q and w_q contraction-major (fp8_gemm_kmajor); the workspace's
+ * gy_qT must then be NULL too (FP8SG_ERR_NULL otherwise).  Both forms give
+ * the same results bit for bit; without the copies each cast writes 1 B per
+ * element instead of 2 and the buffers are not needed.
  */
 typedef struct fp8_linear_saved {
   uint8_t* x_q;         /* [M,K] e4m3 codes of x                */
-  uint8_t* x_qT;        /* [K,M] transposed copy                */
+  uint8_t* x_qT;        /* [K,M] transposed copy, or NULL       */
   uint8_t* w_q;         /* [N,K] e4m3 codes of W                */
-  uint8_t* w_qT;        /* [K,N] transposed copy                */
+  uint8_t* w_qT;        /* [K,N] transposed copy, or NULL       */
   fp8sg_scale_rec* x_sc;
   fp8sg_scale_rec* w_sc;
 } fp8_linear_saved;
@@ -223,7 +255,7 @@ typedef struct fp8_linear_saved {
 /* Backward workspace: the quantized gradient and its scale record. */
 typedef struct fp8_linear_bwd_ws {
   uint8_t* gy_q;        /* [M,N] e5m2 codes of gy               */
-  uint8_t* gy_qT;       /* [N,M] transposed copy                */
+  uint8_t* gy_qT;       /* [N,M] transposed copy, or NULL (with the saved copies NULL) */
   fp8sg_scale_rec* gy_sc;
 } fp8_linear_bwd_ws;
 

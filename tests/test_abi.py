@@ -245,6 +245,39 @@ def test_fused_unscale_validation():
     assert call(gx=MIS) == EALIGN and call(M=8) == ESHAPE
 
 
+def test_kmajor_validation():
+    """The contraction-major GEMMs validate as fp8_gemm does; a linear layer's
+    transposed copies are both given or both NULL, the backward workspace's
+    gy_qT with them."""
+    L = F.lib()
+    g = L.fp8_gemm_kmajor
+    args = [P(A16), 0, 1, P(A16B), 0, 1, P(A16), P(A16), P(A16B), 0, 16, 32, 48, P(0)]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return g(*a)
+
+    assert call(a0=P(0)) == ENULL and call(a3=P(0)) == ENULL and call(a6=P(0)) == ENULL
+    assert call(a1=7) == EFORMAT and call(a9=9) == EFORMAT
+    assert call(a10=24) == ESHAPE and call(a12=-16) == ESHAPE
+    assert call(a0=P(MIS)) == EALIGN and call(a8=P(MIS)) == EALIGN
+    u = lambda scale=A16, found=A16, C=A16B, M=16: L.fp8_gemm_kmajor_unscale(
+        P(A16), 1, 1, P(A16B), 0, 1, P(A16), P(A16), P(scale), P(found), P(C), M, 16, 32, P(0))
+    assert u(scale=0) == ENULL and u(found=0) == ENULL and u(C=0) == ENULL
+    assert u(M=24) == ESHAPE and u(scale=A16 + 1) == EALIGN
+    one = F._Saved(A16, 0, A16, A16, A16, A16)       # x_qT NULL, w_qT given
+    assert L.fp8_scaled_linear_fwd(P(A16), P(A16), 16, 16, 16, ctypes.byref(one), P(A16), 0,
+                                   P(0)) == ENULL
+    none = F._Saved(A16, 0, A16, 0, A16, A16)        # no transposed copies
+    both = F._Saved(A16, A16, A16, A16, A16, A16)
+    ws_t, ws_n = F._BwdWs(A16, A16, A16), F._BwdWs(A16, 0, A16)
+    bwd = lambda s, ws: L.fp8_scaled_linear_bwd(P(A16), ctypes.byref(s), 16, 16, 16,
+                                                ctypes.byref(ws), P(A16), P(A16), 0, P(0))
+    assert bwd(none, ws_t) == ENULL and bwd(both, ws_n) == ENULL
+
+
 def test_gemm_unscale_validation():
     g = lambda scale=A16, found=A16, C=A16B, M=16, fa=0: F.lib().fp8_gemm_unscale(
         P(A16), fa, P(A16B), 1, P(A16), P(A16), P(scale), P(found), P(C), M, 16, 32, P(0))
