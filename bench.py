@@ -5,12 +5,13 @@ One step = the whole hot path on the transformer MLP block (tokens T=8192,
 hidden H=4096, ffn F=14336; gate and up W [14336,4096], down W [4096,14336];
 bf16 activations x, h ~N(0,1), weights ~N(0,0.02), gradients ~N(0,1e-4), all
 seeded; fp16 AMP with loss scale 65536):
-  forward:  amax -> fp64 scale -> e4m3 codes + transposed copies of x (once,
-            shared by gate and up), h and the three weights -> y = x W^T (bf16)
-            for gate, up, down
-  backward: each linear's gradient (carrying the loss scale) amax -> e5m2 codes
-            + transposed copy -> dgrad gx = gy W and wgrad gW = gy^T x in fp16,
-            unscaled and checked for inf/NaN in the GEMM epilogues
+  forward:  amax -> fp64 scale -> e4m3 codes of x (once, shared by gate and
+            up), h and the three weights -> y = x W^T (bf16) for gate, up, down
+  backward: each linear's gradient (carrying the loss scale) amax -> e5m2
+            codes -> dgrad gx = gy W and wgrad gW = gy^T x in fp16, the GEMMs
+            reading W, x and gy codes contraction-major (no transposed copies;
+            --transposed-copies casts them and reads them row-major), unscaled
+            and checked for inf/NaN in the GEMM epilogues
   scaler:   update() of the loss scale on the device
 all through the C ABI on one stream, inputs resident in HBM.
 
@@ -65,6 +66,9 @@ def parse():
                    help="only the HBM-scale passes (for counter runs); prints their figures")
     p.add_argument("--square-only", action="store_true",
                    help="only the square 4096^3 layer's side line (for counter runs)")
+    p.add_argument("--transposed-copies", action="store_true",
+                   help="MLP step with transposed code copies that the backward GEMMs read "
+                        "row-major (default: no copies, the codes read contraction-major)")
     p.add_argument("--copy-reference", action="store_true",
                    help="only copy 1 GiB device-to-device 5 times (calibrates the HBM byte "
                         "counters against a transfer of known size)")
@@ -154,9 +158,9 @@ class MlpStep:
 
     NAMES = ("gate", "up", "down")
 
-    def __init__(self, np, torch, F, dev):
+    def __init__(self, np, torch, F, dev, transposed=False):
         from workloads.configs import mlp_linear, MLP_T, MLP_H, MLP_F
-        self.F, self.torch = F, torch
+        self.F, self.torch, self.transposed = F, torch, transposed
         self.T, self.H, self.Fd = MLP_T, MLP_H, MLP_F
         self.lin = {n: mlp_linear(n) for n in self.NAMES}
         log("generating the MLP block's inputs")
@@ -173,8 +177,8 @@ class MlpStep:
         self.saved, self.ws, self.y, self.gx, self.gw = {}, {}, {}, {}, {}
         for n in self.NAMES:
             L = self.lin[n]
-            self.saved[n] = F.LinearSaved(L.M, L.N, L.K, device=dev)
-            self.ws[n] = F.LinearBwdWs(L.M, L.N, device=dev)
+            self.saved[n] = F.LinearSaved(L.M, L.N, L.K, device=dev, transposed=transposed)
+            self.ws[n] = F.LinearBwdWs(L.M, L.N, device=dev, transposed=transposed)
             self.y[n] = torch.empty((L.M, L.N), **bf)
             self.gx[n] = torch.empty((L.M, L.K), **f16)
             self.gw[n] = torch.empty((L.N, L.K), **f16)
@@ -221,17 +225,28 @@ class MlpStep:
             out.append((f"{n}_fwd {L.M}x{L.N}x{L.K}", fl, lambda sv=sv, n=n: F.fp8_gemm(
                 sv.x_q, F.E4M3FN, sv.w_q, F.E4M3FN, sv.x_sc.inv_ptr(), sv.w_sc.inv_ptr(),
                 self.y[n], F.OUT_BF16)))
-            out.append((f"{n}_dgrad {L.M}x{L.K}x{L.N}", fl, lambda sv=sv, ws=ws, n=n: F.fp8_gemm_unscale(
-                ws.gy_q, F.E5M2, sv.w_qT, F.E4M3FN, ws.gy_sc.inv_ptr(), sv.w_sc.inv_ptr(),
-                self.scale, fz, self.gx[n])))
-            out.append((f"{n}_wgrad {L.N}x{L.K}x{L.M}", fl, lambda sv=sv, ws=ws, n=n: F.fp8_gemm_unscale(
-                ws.gy_qT, F.E5M2, sv.x_qT, F.E4M3FN, ws.gy_sc.inv_ptr(), sv.x_sc.inv_ptr(),
-                self.scale, fz, self.gw[n])))
+            if self.transposed:
+                dg = lambda sv=sv, ws=ws, n=n: F.fp8_gemm_unscale(
+                    ws.gy_q, F.E5M2, sv.w_qT, F.E4M3FN, ws.gy_sc.inv_ptr(), sv.w_sc.inv_ptr(),
+                    self.scale, fz, self.gx[n])
+                wg = lambda sv=sv, ws=ws, n=n: F.fp8_gemm_unscale(
+                    ws.gy_qT, F.E5M2, sv.x_qT, F.E4M3FN, ws.gy_sc.inv_ptr(), sv.x_sc.inv_ptr(),
+                    self.scale, fz, self.gw[n])
+            else:  # W codes as B^T for dgrad; gy and x codes as A^T and B^T for wgrad
+                dg = lambda sv=sv, ws=ws, n=n: F.fp8_gemm_kmajor_unscale(
+                    ws.gy_q, F.E5M2, 0, sv.w_q, F.E4M3FN, 1, ws.gy_sc.inv_ptr(), sv.w_sc.inv_ptr(),
+                    self.scale, fz, self.gx[n])
+                wg = lambda sv=sv, ws=ws, n=n: F.fp8_gemm_kmajor_unscale(
+                    ws.gy_q, F.E5M2, 1, sv.x_q, F.E4M3FN, 1, ws.gy_sc.inv_ptr(), sv.x_sc.inv_ptr(),
+                    self.scale, fz, self.gw[n])
+            out.append((f"{n}_dgrad {L.M}x{L.K}x{L.N}", fl, dg))
+            out.append((f"{n}_wgrad {L.N}x{L.K}x{L.M}", fl, wg))
         return out
 
     def casts(self):
-        """The step's eight casts (amax, then quantize with the transposed copy)
-        as (name, elements, call), on fresh records of their own."""
+        """The step's eight casts (amax, then quantize, with the transposed copy
+        when the step keeps them) as (name, elements, call), on fresh records
+        of their own."""
         F, out = self.F, []
         d = self.dev
         for name, t, fmt in (("x", d["x"], F.E4M3FN), ("h", d["h"], F.E4M3FN),
@@ -240,7 +255,8 @@ class MlpStep:
                              ("gy_up", d["gy_up"], F.E5M2), ("gy_down", d["gy_down"], F.E5M2)):
             rec = F.ScaleRec(device=t.device)
             q = self.torch.empty(t.shape, dtype=self.torch.uint8, device=t.device)
-            qT = self.torch.empty((t.shape[1], t.shape[0]), dtype=self.torch.uint8, device=t.device)
+            qT = (self.torch.empty((t.shape[1], t.shape[0]), dtype=self.torch.uint8, device=t.device)
+                  if self.transposed else None)
 
             def call(t=t, fmt=fmt, rec=rec, q=q, qT=qT):
                 F.fp8_amax(t, rec)
@@ -292,7 +308,8 @@ def main():
         print(json.dumps({"square_layer": square_layer(np, torch, F, dev, stream, T, args)}), flush=True)
         return
 
-    mlp = MlpStep(np, torch, F, dev)
+    mlp = MlpStep(np, torch, F, dev, transposed=args.transposed_copies)
+    cast_bpe = 6.0 if mlp.transposed else 5.0  # amax read 2 B; cast read 2 B, write 1 (+1) B
     log(f"timing {args.steps} steps of the MLP block")
     ms_per_step, wall, spread = timed_steps(torch, stream, mlp.step, args.steps, args.warmup)
     gemm_flops = sum(2.0 * L.M * L.N * L.K for L in mlp.lin.values()) * 3
@@ -304,16 +321,16 @@ def main():
     cast = {}
     for name, n, call in mlp.casts():
         us = T.run(call, args.reps)
-        cast[name] = {"elements": n, "amax_plus_cast_T_us": round(us, 2),
-                      "GBps": round(6.0 * n / (us * 1e-6) / 1e9, 1)}
+        cast[name] = {"elements": n, "amax_plus_cast_us": round(us, 2),
+                      "GBps": round(cast_bpe * n / (us * 1e-6) / 1e9, 1)}
     torch.cuda.empty_cache()
     upd_us = T.run(lambda: F.amp_update_scale(mlp.scale, mlp.tracker, mlp.found, 2.0, 0.5, 2000),
                    args.reps)
     sum_gemm = sum(gemm_us.values())
     achieved = sum(gemm_fl.values()) / (sum_gemm * 1e-6) / 1e12
-    cast_bytes = 6.0 * sum(c["elements"] for c in cast.values())
+    cast_bytes = cast_bpe * sum(c["elements"] for c in cast.values())
     # x is cast once per step although gate and up both consume it
-    sum_cast = sum(c["amax_plus_cast_T_us"] for c in cast.values())
+    sum_cast = sum(c["amax_plus_cast_us"] for c in cast.values())
 
     # ---- sampled check of the step's outputs against the oracle (after one
     # step from the initial loss scale, as timed)
@@ -333,6 +350,7 @@ def main():
         side["small_layer"] = small_layer(torch, F, dev, stream, T)
         log("MLP block through the PyTorch layer")
         side["mlp_block_autograd"] = mlp_autograd(torch, F, dev, stream)
+    mlp_transposed = mlp.transposed
     del mlp
     torch.cuda.empty_cache()
 
@@ -358,7 +376,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": "transformer MLP block T=8192 H=4096 F=14336 in FP8: gate, up, "
                                "down linears fwd+dgrad+wgrad (9 GEMMs), per-tensor dynamic "
-                               "scaling of every operand with fused transposed copies, "
+                               "scaling of every operand, " + (
+                                   "fused transposed copies read row-major by dgrad/wgrad, "
+                                   if mlp_transposed else
+                                   "no transposed copies: dgrad/wgrad read the codes "
+                                   "contraction-major, ") +
                                "GradScaler unscale/check fused into the dgrad/wgrad epilogues, "
                                "device-side scale update",
                    "tokens": 8192, "hidden": 4096, "ffn": 14336,
@@ -367,7 +389,7 @@ def main():
                    "formats": "e4m3fn x/h/W, e5m2 gy"},
         "step_pct_of_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
         "step_spread": spread,
-        "step_breakdown_us": {"gemms": round(sum_gemm, 1), "casts_amax_quant_T": round(sum_cast, 1),
+        "step_breakdown_us": {"gemms": round(sum_gemm, 1), "casts_amax_quant": round(sum_cast, 1),
                               "update": round(upd_us, 2),
                               "sum": round(sum_gemm + sum_cast + upd_us, 1),
                               "step": round(1e3 * ms_per_step, 1)},
@@ -415,7 +437,8 @@ def mlp_check(np, torch, F, mlp, n_pts=256):
         pairs.append((ws[n].gy_q, ws[n].gy_qT, ws[n].gy_sc, "gy_" + n, O.E5M2))
     for dq, dqT, rec, key, fmt in pairs:
         assert_codes_equal(fmt, dq.cpu().numpy(), q[key].q, key)
-        assert_codes_equal(fmt, dqT.cpu().numpy(), q[key].qT, key + " T")
+        if dqT is not None:
+            assert_codes_equal(fmt, dqT.cpu().numpy(), q[key].qT, key + " T")
         r = rec.read()
         assert r["amax_bits"] == q[key].sc.amax_bits and r["inv"] == q[key].sc.inv, key
     assert int(mlp.found.item()) == 0
@@ -440,7 +463,8 @@ def mlp_check(np, torch, F, mlp, n_pts=256):
             else:
                 nw = check_gemm_values(g, c_ref, ad, A.shape[1], fmt, f"{n} {what}")
             nw_max = max(nw_max, nw)
-    return {"codes_and_records": "bit-exact (8 casts with transposed copies)",
+    return {"codes_and_records": "bit-exact (8 casts" + (
+                " with transposed copies)" if mlp.transposed else ")"),
             "found_inf": 0, "gemm_samples_per_gemm": n_pts, "gemms": 9, "ok": True,
             "max_abs_err_over_max_abs": float(nw_max)}
 

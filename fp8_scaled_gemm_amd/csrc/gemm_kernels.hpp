@@ -49,6 +49,14 @@ struct GemmCfg {
 
 // byte offset of 16-byte chunk c of row r inside a [rows][128 B] LDS tile
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4); }
+// A contraction-major k-tile row (one k, 128 output rows or columns) of the
+// 128 x 128 kernel: the 16 lanes of a transposed read cover rows 8 apart
+// (8 rows, 32 banks), and the four 16-lane groups rows 32 apart.  Bit 0 of
+// the chunk swap follows bit 5 ^ bit 6 of the row, so any two groups that
+// the LDS serves together fall on opposite bank sets.
+__device__ __forceinline__ int lds_off_t(int r, int c) {
+  return r * kBK + ((c ^ (r & 7) ^ (((r >> 5) ^ (r >> 6)) & 1)) << 4);
+}
 
 // The unscale step fused into an fp16 epilogue: the GradScaler's rounding
 // sequence on the stored value, h = fp16(c), g = fp16(fl32(h) * inv_s), in
@@ -213,12 +221,12 @@ __device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, in
 #pragma unroll
     for (int i = 0; i < Cfg::kLoadsA; ++i) {
       const int c = tid + i * Cfg::kThreads;
-      *reinterpret_cast<uint4*>(a + lds_off(c >> 3, c & 7)) = ra[i];
+      *reinterpret_cast<uint4*>(a + (TA ? lds_off_t(c >> 3, c & 7) : lds_off(c >> 3, c & 7))) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < Cfg::kLoadsB; ++i) {
       const int c = tid + i * Cfg::kThreads;
-      *reinterpret_cast<uint4*>(b + lds_off(c >> 3, c & 7)) = rb[i];
+      *reinterpret_cast<uint4*>(b + (TB ? lds_off_t(c >> 3, c & 7) : lds_off(c >> 3, c & 7))) = rb[i];
     }
   };
 
@@ -243,7 +251,7 @@ __device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, in
     for (int r = 0; r < 4; ++r) {
       const int row = 32 * (lane >> 4) + 8 * r + (frow >> 1);
       const v2i_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (__attribute__((address_space(3))) v2i_t*)(base + lds_off(row, blk) + 8 * (frow & 1)));
+          (__attribute__((address_space(3))) v2i_t*)(base + lds_off_t(row, blk) + 8 * (frow & 1)));
       out[2 * r] = t.x;
       out[2 * r + 1] = t.y;
     }
@@ -478,14 +486,21 @@ __device__ __forceinline__ void tile_of(int nbm, int nbn, int& tm, int& tn) {
 // where the GEMM contracts over its rows -- the backward GEMMs' operands,
 // without a transposed copy.  Such an operand's k-tile is staged as 128 LDS
 // rows (one per k) of 256 bytes (the tile's output rows or columns), 16-byte
-// chunk q of row r at position q ^ (r & 7), and each fragment is gathered
+// chunk q of row r at position q ^ swzT(r), and each fragment is gathered
 // with four ds_read_b64_tr_b8: in every group of 16 lanes the 8-byte reads
 // of lanes 2i and 2i + 1 form row i of an 8 x 16 byte matrix and lane j
 // receives its column j, so lane j of group g, pointing at row
 // 32 g + 8 r + j / 2, chunk half j & 1, receives k = 32 g + 8 r .. + 7 of its
 // output row or column.  Rows past K fall outside the buffer descriptor and
 // read as zero (no ragged-K test); columns past M or N are pointed outside.
+// swzT(r) = (r & 7) | 8 ((r >> 5 ^ r >> 6) & 1): the 16 lanes of a group read
+// 8 rows at 8 chunk positions, one 128-byte half of the 64 banks, and the
+// four groups rows 32 apart; the bit-3 term puts any two groups that the LDS
+// serves together (0 and 1 or 0 and 2, 2 and 3 or 1 and 3) in opposite halves
+// (without it every transposed read took a two-way bank conflict).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int swzT(int r) { return (r & 7) | ((((r >> 5) ^ (r >> 6)) & 1) << 3); }
+
 template <int FA, int FB, int OUT, bool RAGGED_K, bool RW, int BM = 256, bool TR = false,
           bool TA = false, bool TB = false>
 __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
@@ -552,36 +567,46 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
   };
   // A contraction-major operand's stage (128 rows of 256 B) by wave q of a
   // group: 8 loads of 4 rows, rows 32 q + 4 i + l / 16, LDS position l % 16;
-  // the row's swizzle (4 i + l / 16) & 7 takes two values per lane (i even or
-  // odd), so a lane needs two offsets and the rest is scalar.  `ld` is the
-  // stored row length (M or N), `ncols` that of the tile's columns left.
+  // the row's swizzle swzT(32 q + 4 i + l / 16) takes two values per lane (i
+  // even or odd), so a lane needs two offsets and the rest is scalar.  `ld` is
+  // the stored row length (M or N), `ncols` that of the tile's columns left.
   const int lr4 = lane >> 4, lp = lane & 15;
-  auto t_off = [&](int sw, int64_t ld, int64_t ncols) -> uint32_t {
-    const int q = lp ^ sw;
+  auto t_off = [&](int row, int64_t ld, int64_t ncols) -> uint32_t {
+    const int q = lp ^ swzT(row);
     return 16 * q < ncols ? (uint32_t)(lr4 * ld + 16 * q) : 0x7FFFFFF0u;
   };
-  const uint32_t ta0 = TA ? t_off(lr4, M, M - bm) : 0u, ta1 = TA ? t_off(4 + lr4, M, M - bm) : 0u;
-  const uint32_t tb0 = TB ? t_off(lr4, N, N - bn) : 0u, tb1 = TB ? t_off(4 + lr4, N, N - bn) : 0u;
-  // (a load's 4 rows lie all below K or all past it, K being a multiple of
-  // 16; past it the scalar part is the outside offset, so no row offset can
-  // exceed (K - 4) * ld < 2^31)
-  auto issue_t = [&](int kt, uint32_t dst, const i32x4& rs, int64_t ld, uint32_t v0, uint32_t v1) {
+  const int trow = 32 * wq + lr4;
+  const uint32_t ta0 = TA ? t_off(trow, M, M - bm) : 0u, ta1 = TA ? t_off(trow + 4, M, M - bm) : 0u;
+  const uint32_t tb0 = TB ? t_off(trow, N, N - bn) : 0u, tb1 = TB ? t_off(trow + 4, N, N - bn) : 0u;
+  // A load's 4 rows lie all below K or all past it (K is a multiple of 16):
+  // load i is in range while 4 i < K - (128 kt + 32 q); past K its scalar part
+  // is the outside offset, so no row offset exceeds (K - 4) ld < 2^31.  All of
+  // it is 32-bit scalar arithmetic (K, M and N are below 2^31), the row
+  // offset stepped by 4 ld from load to load; 4 ld passes through an empty
+  // asm statement so the compiler does not hoist the eight multiples out of
+  // the k-loop (they spilled scalar registers).
+  const int K32 = (int)K;
+  auto issue_t = [&](int kt, uint32_t dst, const i32x4& rs, uint32_t ld, uint32_t v0, uint32_t v1) {
+    const int r0 = kt * kBK + 32 * wq;
+    const int rem = kt < nk ? K32 - r0 : 0;
+    uint32_t ld4 = 4 * ld;
+    asm volatile("" : "+s"(ld4));
+    uint32_t sb = (uint32_t)r0 * ld;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t row = (int64_t)kt * kBK + 32 * wq + 4 * i;
-      const uint32_t sb = kt < nk && row < K ? (uint32_t)(row * ld) : kOob;
-      lds_dma16_split(dst + (wq * 8 + i) * 1024, (i & 1) ? v1 : v0, sb, rs);
+      lds_dma16_split(dst + (wq * 8 + i) * 1024, (i & 1) ? v1 : v0, 4 * i < rem ? sb : kOob, rs);
+      sb += ld4;
     }
   };
   using LA = std::integral_constant<int, TA ? 8 : kLoadsA>;
   using LB = std::integral_constant<int, kLoads>;
   // this group's loads of operand A (group 0) or B (group 1) for k-tile kt
   auto issue_a = [&](int kt, uint32_t dst) {
-    if constexpr (TA) issue_t(kt, dst, ra, M, ta0, ta1);
+    if constexpr (TA) issue_t(kt, dst, ra, (uint32_t)M, ta0, ta1);
     else issue(LA{}, kt, dst, ra);
   };
   auto issue_b = [&](int kt, uint32_t dst) {
-    if constexpr (TB) issue_t(kt, dst, rb, N, tb0, tb1);
+    if constexpr (TB) issue_t(kt, dst, rb, (uint32_t)N, tb0, tb1);
     else issue(LB{}, kt, dst, rb);
   };
   v4f acc[kTM][kTN];
@@ -600,11 +625,12 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
   };
   // fragment of output block blk (16 rows or columns) from a contraction-major
   // stage: four transposed 8-byte reads (see above).  The lane reads rows
-  // 32 g + 8 r + lp / 2, all with swizzle lp / 2, so its addresses are
-  // t_base + r * 2048 + ((blk ^ lp / 2) << 4).  The XOR differs per block and
-  // lane; `sx` (lp / 2 << 4) is passed through an empty asm statement once per
-  // memory phase so the compiler recomputes the XORs there instead of keeping
-  // one address register per block live across the k-loop.
+  // 32 g + 8 r + lp / 2, all with swizzle swzT(32 g + lp / 2), so its
+  // addresses are t_base + r * 2048 + ((blk ^ swzT(..)) << 4).  The XOR
+  // differs per block and lane; `sx` (swzT(..) << 4) is passed through an
+  // empty asm statement once per memory phase so the compiler recomputes the
+  // XORs there instead of keeping one address register per block live across
+  // the k-loop.
   typedef int v2i_t __attribute__((ext_vector_type(2)));
   const uint32_t t_base = (uint32_t)((32 * lr4 + (lp >> 1)) * 256 + 8 * (lp & 1));
   auto frag_t = [&](const uint8_t* base, int blk, uint32_t sx) {
@@ -652,7 +678,7 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
       const uint32_t da = lds_u32(sa(std::integral_constant<int, (P + 1) % 2>{}));
       const uint32_t db = lds_u32(sb(std::integral_constant<int, (P + 2) % 3>{}));
       if constexpr (LA::value == kLoads && TA == TB) {
-        if constexpr (TA) issue_t(t + 1 + grp, grp ? db : da, grp ? rb : ra, grp ? N : M,
+        if constexpr (TA) issue_t(t + 1 + grp, grp ? db : da, grp ? rb : ra, (uint32_t)(grp ? N : M),
                                   grp ? tb0 : ta0, grp ? tb1 : ta1);
         else issue(LB{}, t + 1 + grp, grp ? db : da, grp ? rb : ra);
       } else {
@@ -660,7 +686,7 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
         else issue_a(t + 1, da);
       }
     }
-    uint32_t sx = (uint32_t)(lp >> 1) << 4;
+    uint32_t sx = (uint32_t)swzT(32 * lr4 + (lp >> 1)) << 4;
     if constexpr (TA || TB) asm volatile("" : "+v"(sx));
 #pragma unroll
     for (int j = 0; j < kTN; ++j) bf[j] = TB ? frag_t(b, rb0 + j, sx) : frag(b, rb0 + j);
