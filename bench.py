@@ -9,9 +9,10 @@ seeded; fp16 AMP with loss scale 65536):
             up), h and the three weights -> y = x W^T (bf16) for gate, up, down
   backward: each linear's gradient (carrying the loss scale) amax -> e5m2
             codes -> dgrad gx = gy W and wgrad gW = gy^T x in fp16, the GEMMs
-            reading W, x and gy codes contraction-major (no transposed copies;
-            --transposed-copies casts them and reads them row-major), unscaled
-            and checked for inf/NaN in the GEMM epilogues
+            reading W, x, gy of down contraction-major and gy of gate and
+            up, h through the transposed copies their casts write (--layout
+            chooses other mixes), unscaled and checked for inf/NaN in the
+            GEMM epilogues
   scaler:   update() of the loss scale on the device
 all through the C ABI on one stream, inputs resident in HBM.
 
@@ -66,9 +67,12 @@ def parse():
                    help="only the HBM-scale passes (for counter runs); prints their figures")
     p.add_argument("--square-only", action="store_true",
                    help="only the square 4096^3 layer's side line (for counter runs)")
-    p.add_argument("--transposed-copies", action="store_true",
-                   help="MLP step with transposed code copies that the backward GEMMs read "
-                        "row-major (default: no copies, the codes read contraction-major)")
+    p.add_argument("--layout", choices=("a-slot", "none", "all"), default="a-slot",
+                   help="which transposed code copies the MLP step's casts write: 'a-slot' "
+                        "(default) those of the weight-gradient GEMMs' first operand (gy of "
+                        "gate and up, h of down), the other operands read contraction-major; "
+                        "'none': every backward operand read contraction-major; 'all': every "
+                        "copy written and read row-major")
     p.add_argument("--copy-reference", action="store_true",
                    help="only copy 1 GiB device-to-device 5 times (calibrates the HBM byte "
                         "counters against a transfer of known size)")
@@ -158,9 +162,18 @@ class MlpStep:
 
     NAMES = ("gate", "up", "down")
 
-    def __init__(self, np, torch, F, dev, transposed=False):
+    # which tensors' casts write a transposed copy, per layout: the weight
+    # gradient's first GEMM operand (gy of gate and up; h for down, whose
+    # weight gradient runs with the operands' roles swapped) is read twice as
+    # often from LDS as the second, so only there does a contraction-major
+    # read cost time
+    LAYOUTS = {"a-slot": {"h", "gy_gate", "gy_up"}, "none": set(),
+               "all": {"x", "h", "w_gate", "w_up", "w_down", "gy_gate", "gy_up", "gy_down"}}
+
+    def __init__(self, np, torch, F, dev, layout="a-slot"):
         from workloads.configs import mlp_linear, MLP_T, MLP_H, MLP_F
-        self.F, self.torch, self.transposed = F, torch, transposed
+        self.F, self.torch, self.layout = F, torch, layout
+        self.tr = self.LAYOUTS[layout]
         self.T, self.H, self.Fd = MLP_T, MLP_H, MLP_F
         self.lin = {n: mlp_linear(n) for n in self.NAMES}
         log("generating the MLP block's inputs")
@@ -177,8 +190,10 @@ class MlpStep:
         self.saved, self.ws, self.y, self.gx, self.gw = {}, {}, {}, {}, {}
         for n in self.NAMES:
             L = self.lin[n]
-            self.saved[n] = F.LinearSaved(L.M, L.N, L.K, device=dev, transposed=transposed)
-            self.ws[n] = F.LinearBwdWs(L.M, L.N, device=dev, transposed=transposed)
+            self.saved[n] = F.LinearSaved(L.M, L.N, L.K, device=dev,
+                                          x_transposed=("h" if n == "down" else "x") in self.tr,
+                                          w_transposed="w_" + n in self.tr)
+            self.ws[n] = F.LinearBwdWs(L.M, L.N, device=dev, transposed="gy_" + n in self.tr)
             self.y[n] = torch.empty((L.M, L.N), **bf)
             self.gx[n] = torch.empty((L.M, L.K), **f16)
             self.gw[n] = torch.empty((L.N, L.K), **f16)
@@ -225,28 +240,24 @@ class MlpStep:
             out.append((f"{n}_fwd {L.M}x{L.N}x{L.K}", fl, lambda sv=sv, n=n: F.fp8_gemm(
                 sv.x_q, F.E4M3FN, sv.w_q, F.E4M3FN, sv.x_sc.inv_ptr(), sv.w_sc.inv_ptr(),
                 self.y[n], F.OUT_BF16)))
-            if self.transposed:
-                dg = lambda sv=sv, ws=ws, n=n: F.fp8_gemm_unscale(
-                    ws.gy_q, F.E5M2, sv.w_qT, F.E4M3FN, ws.gy_sc.inv_ptr(), sv.w_sc.inv_ptr(),
-                    self.scale, fz, self.gx[n])
-                wg = lambda sv=sv, ws=ws, n=n: F.fp8_gemm_unscale(
-                    ws.gy_qT, F.E5M2, sv.x_qT, F.E4M3FN, ws.gy_sc.inv_ptr(), sv.x_sc.inv_ptr(),
-                    self.scale, fz, self.gw[n])
-            else:  # W codes as B^T for dgrad; gy and x codes as A^T and B^T for wgrad
-                dg = lambda sv=sv, ws=ws, n=n: F.fp8_gemm_kmajor_unscale(
-                    ws.gy_q, F.E5M2, 0, sv.w_q, F.E4M3FN, 1, ws.gy_sc.inv_ptr(), sv.w_sc.inv_ptr(),
-                    self.scale, fz, self.gx[n])
-                wg = lambda sv=sv, ws=ws, n=n: F.fp8_gemm_kmajor_unscale(
-                    ws.gy_q, F.E5M2, 1, sv.x_q, F.E4M3FN, 1, ws.gy_sc.inv_ptr(), sv.x_sc.inv_ptr(),
-                    self.scale, fz, self.gw[n])
+            # as the layer's backward: a transposed copy where the cast wrote
+            # one, else the row-major codes read contraction-major (W as B^T
+            # for dgrad; gy as A^T and x as B^T for wgrad)
+            wk, gk, xk = sv.w_qT is None, ws.gy_qT is None, sv.x_qT is None
+            dg = lambda sv=sv, ws=ws, n=n, wk=wk: F.fp8_gemm_kmajor_unscale(
+                ws.gy_q, F.E5M2, 0, sv.w_q if wk else sv.w_qT, F.E4M3FN, wk, ws.gy_sc.inv_ptr(),
+                sv.w_sc.inv_ptr(), self.scale, fz, self.gx[n])
+            wg = lambda sv=sv, ws=ws, n=n, gk=gk, xk=xk: F.fp8_gemm_kmajor_unscale(
+                ws.gy_q if gk else ws.gy_qT, F.E5M2, gk, sv.x_q if xk else sv.x_qT, F.E4M3FN, xk,
+                ws.gy_sc.inv_ptr(), sv.x_sc.inv_ptr(), self.scale, fz, self.gw[n])
             out.append((f"{n}_dgrad {L.M}x{L.K}x{L.N}", fl, dg))
             out.append((f"{n}_wgrad {L.N}x{L.K}x{L.M}", fl, wg))
         return out
 
     def casts(self):
         """The step's eight casts (amax, then quantize, with the transposed copy
-        when the step keeps them) as (name, elements, call), on fresh records
-        of their own."""
+        where the step keeps one) as (name, elements, bytes, call), on fresh
+        records of their own."""
         F, out = self.F, []
         d = self.dev
         for name, t, fmt in (("x", d["x"], F.E4M3FN), ("h", d["h"], F.E4M3FN),
@@ -256,12 +267,13 @@ class MlpStep:
             rec = F.ScaleRec(device=t.device)
             q = self.torch.empty(t.shape, dtype=self.torch.uint8, device=t.device)
             qT = (self.torch.empty((t.shape[1], t.shape[0]), dtype=self.torch.uint8, device=t.device)
-                  if self.transposed else None)
+                  if name in self.tr else None)
 
             def call(t=t, fmt=fmt, rec=rec, q=q, qT=qT):
                 F.fp8_amax(t, rec)
                 F.fp8_quantize(t, fmt, rec, q, qT)
-            out.append((name, t.numel(), call))
+            # amax reads 2 B; the cast reads 2 B and writes 1 B (+1 B transposed)
+            out.append((name, t.numel(), (6 if qT is not None else 5) * t.numel(), call))
         return out
 
 
@@ -308,8 +320,7 @@ def main():
         print(json.dumps({"square_layer": square_layer(np, torch, F, dev, stream, T, args)}), flush=True)
         return
 
-    mlp = MlpStep(np, torch, F, dev, transposed=args.transposed_copies)
-    cast_bpe = 6.0 if mlp.transposed else 5.0  # amax read 2 B; cast read 2 B, write 1 (+1) B
+    mlp = MlpStep(np, torch, F, dev, layout=args.layout)
     log(f"timing {args.steps} steps of the MLP block")
     ms_per_step, wall, spread = timed_steps(torch, stream, mlp.step, args.steps, args.warmup)
     gemm_flops = sum(2.0 * L.M * L.N * L.K for L in mlp.lin.values()) * 3
@@ -319,16 +330,17 @@ def main():
     gemm_us = {name: T.run(call, args.reps) for name, fl, call in mlp.gemms()}
     gemm_fl = {name: fl for name, fl, _ in mlp.gemms()}
     cast = {}
-    for name, n, call in mlp.casts():
+    for name, n, nbytes, call in mlp.casts():
         us = T.run(call, args.reps)
-        cast[name] = {"elements": n, "amax_plus_cast_us": round(us, 2),
-                      "GBps": round(cast_bpe * n / (us * 1e-6) / 1e9, 1)}
+        cast[name] = {"elements": n, "bytes": nbytes, "transposed_copy": nbytes == 6 * n,
+                      "amax_plus_cast_us": round(us, 2),
+                      "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
     torch.cuda.empty_cache()
     upd_us = T.run(lambda: F.amp_update_scale(mlp.scale, mlp.tracker, mlp.found, 2.0, 0.5, 2000),
                    args.reps)
     sum_gemm = sum(gemm_us.values())
     achieved = sum(gemm_fl.values()) / (sum_gemm * 1e-6) / 1e12
-    cast_bytes = cast_bpe * sum(c["elements"] for c in cast.values())
+    cast_bytes = sum(c["bytes"] for c in cast.values())
     # x is cast once per step although gate and up both consume it
     sum_cast = sum(c["amax_plus_cast_us"] for c in cast.values())
 
@@ -350,7 +362,7 @@ def main():
         side["small_layer"] = small_layer(torch, F, dev, stream, T)
         log("MLP block through the PyTorch layer")
         side["mlp_block_autograd"] = mlp_autograd(torch, F, dev, stream)
-    mlp_transposed = mlp.transposed
+    mlp_tr = sorted(mlp.tr)
     del mlp
     torch.cuda.empty_cache()
 
@@ -377,8 +389,10 @@ def main():
         "config": {"workload": "transformer MLP block T=8192 H=4096 F=14336 in FP8: gate, up, "
                                "down linears fwd+dgrad+wgrad (9 GEMMs), per-tensor dynamic "
                                "scaling of every operand, " + (
-                                   "fused transposed copies read row-major by dgrad/wgrad, "
-                                   if mlp_transposed else
+                                   "fused transposed copies of " + ", ".join(mlp_tr) +
+                                   " read row-major by the weight-gradient GEMMs, every other "
+                                   "backward operand read contraction-major, "
+                                   if mlp_tr else
                                    "no transposed copies: dgrad/wgrad read the codes "
                                    "contraction-major, ") +
                                "GradScaler unscale/check fused into the dgrad/wgrad epilogues, "
@@ -463,8 +477,8 @@ def mlp_check(np, torch, F, mlp, n_pts=256):
             else:
                 nw = check_gemm_values(g, c_ref, ad, A.shape[1], fmt, f"{n} {what}")
             nw_max = max(nw_max, nw)
-    return {"codes_and_records": "bit-exact (8 casts" + (
-                " with transposed copies)" if mlp.transposed else ")"),
+    return {"codes_and_records": "bit-exact (8 casts; transposed copies of " + (
+                ", ".join(sorted(mlp.tr)) or "none") + ")",
             "found_inf": 0, "gemm_samples_per_gemm": n_pts, "gemms": 9, "ok": True,
             "max_abs_err_over_max_abs": float(nw_max)}
 

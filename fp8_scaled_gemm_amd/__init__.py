@@ -369,17 +369,21 @@ def fp8_gemm_kmajor_unscale(A: torch.Tensor, fa: int, a_kmajor: bool, B: torch.T
 class LinearSaved:
     """Device buffers the forward pass fills for the backward pass.  With
     transposed=False no transposed copies are kept (x_qT and w_qT are None):
-    the backward GEMMs read x_q and w_q contraction-major."""
+    the backward GEMMs read x_q and w_q contraction-major.  x_transposed /
+    w_transposed choose for one operand alone (default: `transposed`)."""
 
-    def __init__(self, M, N, K, device="cuda", tensors=None, transposed=True):
+    def __init__(self, M, N, K, device="cuda", tensors=None, transposed=True, x_transposed=None,
+                 w_transposed=None):
         if tensors is not None:  # (x_q, x_qT, w_q, w_qT, recs) kept from an earlier forward
             self.x_q, self.x_qT, self.w_q, self.w_qT, self.recs = tensors
         else:
+            xt = transposed if x_transposed is None else x_transposed
+            wt = transposed if w_transposed is None else w_transposed
             u8 = dict(dtype=torch.uint8, device=device)
             self.x_q = torch.empty((M, K), **u8)
-            self.x_qT = torch.empty((K, M), **u8) if transposed else None
+            self.x_qT = torch.empty((K, M), **u8) if xt else None
             self.w_q = torch.empty((N, K), **u8)
-            self.w_qT = torch.empty((K, N), **u8) if transposed else None
+            self.w_qT = torch.empty((K, N), **u8) if wt else None
             self.recs = torch.zeros((2, SCALE_REC_BYTES), **u8)
         self.x_sc = ScaleRec(buf=self.recs[0])
         self.w_sc = ScaleRec(buf=self.recs[1])
@@ -394,8 +398,6 @@ class LinearSaved:
                id(self.w_sc), id(self.x_sc.buf), id(self.w_sc.buf))
         if self.__dict__.get("_ok") == key:
             return
-        if (self.x_qT is None) != (self.w_qT is None):
-            raise Fp8sgError("saved.x_qT and saved.w_qT: both tensors or both None")
         for t, name, shape in ((self.x_q, "saved.x_q", (M, K)), (self.x_qT, "saved.x_qT", (K, M)),
                                (self.w_q, "saved.w_q", (N, K)), (self.w_qT, "saved.w_qT", (K, N))):
             if t is not None or name in ("saved.x_q", "saved.w_q"):
@@ -418,7 +420,7 @@ class LinearSaved:
 
 class LinearBwdWs:
     """The backward's gradient codes; with transposed=False no transposed copy
-    (for a LinearSaved without transposed copies)."""
+    (the weight-gradient GEMM then reads gy_q contraction-major)."""
 
     def __init__(self, M, N, device="cuda", transposed=True):
         u8 = dict(dtype=torch.uint8, device=device)

@@ -54,11 +54,10 @@ fp8sg_status check_gemm(const void* A, int fa, const void* B, int fb, const void
   return FP8SG_OK;
 }
 
-// x_qT and w_qT are both given (the backward GEMMs read the transposed
-// copies) or both null (they read the row-major codes, contraction-major).
+// x_qT and w_qT may each be null: the backward GEMM that would read that
+// transposed copy reads the row-major codes contraction-major instead.
 fp8sg_status check_saved(const fp8_linear_saved* s) {
   if (!s || !s->x_q || !s->w_q || !s->x_sc || !s->w_sc) return FP8SG_ERR_NULL;
-  if (!s->x_qT != !s->w_qT) return FP8SG_ERR_NULL;
   if (!aligned16(s->x_q) || !aligned16(s->x_qT) || !aligned16(s->w_q) || !aligned16(s->w_qT) ||
       !aligned(s->x_sc, 8) || !aligned(s->w_sc, 8))
     return FP8SG_ERR_ALIGN;
@@ -309,10 +308,7 @@ fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64
   if (!gy || !ws || !gx || !gw) return FP8SG_ERR_NULL;
   fp8sg_status st = check_saved(saved);
   if (st != FP8SG_OK) return st;
-  // without transposed copies (saved and workspace alike), the backward GEMMs
-  // read the row-major codes contraction-major
-  const bool kmajor = !saved->x_qT;
-  if (!ws->gy_q || !ws->gy_sc || (!ws->gy_qT != kmajor)) return FP8SG_ERR_NULL;
+  if (!ws->gy_q || !ws->gy_sc) return FP8SG_ERR_NULL;
   if (!out_ok(out)) return FP8SG_ERR_FORMAT;
   if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K) || !gemm_ok(M, N, K))
     return FP8SG_ERR_SHAPE;
@@ -342,19 +338,21 @@ fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64
   }
   if (e != hipSuccess) return FP8SG_ERR_HIP;
 
-  if (kmajor) {
-    // dgrad: gy codes [M, N] x W codes [N, K] (contraction-major B); wgrad:
-    // gy codes as A^T [M, N] x x codes as B^T [M, K]
-    GemmProblem dg{ws->gy_q, saved->w_q, gx, &ws->gy_sc->inv, &saved->w_sc->inv, M, K, N,
-                   amp_scale, found_inf};
-    GemmProblem wg{ws->gy_q, saved->x_q, gw, &ws->gy_sc->inv, &saved->x_sc->inv, N, K, M,
-                   amp_scale, found_inf};
-    return hip_status(launch_gemm_km_pair(dg, wg, amp_scale ? kOutF16Unscale : (int)out, s));
+  // An operand without its transposed copy is read from its row-major codes,
+  // contraction-major: dgrad's W codes [N, K] as B^T, wgrad's gy codes
+  // [M, N] as A^T and x codes [M, K] as B^T.
+  const bool tb_d = !saved->w_qT, ta_w = !ws->gy_qT, tb_w = !saved->x_qT;
+  GemmProblem dg{ws->gy_q, tb_d ? saved->w_q : saved->w_qT, gx, &ws->gy_sc->inv, &saved->w_sc->inv,
+                 M, K, N, amp_scale, found_inf};
+  GemmProblem wg{ta_w ? ws->gy_q : ws->gy_qT, tb_w ? saved->x_q : saved->x_qT, gw, &ws->gy_sc->inv,
+                 &saved->x_sc->inv, N, K, M, amp_scale, found_inf};
+  const int o = amp_scale ? kOutF16Unscale : (int)out;
+  if (tb_d && ta_w && tb_w) return hip_status(launch_gemm_km_pair(dg, wg, o, s));
+  if (tb_d || ta_w || tb_w) {  // some copies kept: one launch per GEMM
+    e = launch_gemm_km(dg, FP8SG_E5M2, FP8SG_E4M3FN, o, false, tb_d, s);
+    if (e != hipSuccess) return FP8SG_ERR_HIP;
+    return hip_status(launch_gemm_km(wg, FP8SG_E5M2, FP8SG_E4M3FN, o, ta_w, tb_w, s));
   }
-  GemmProblem dg{ws->gy_q, saved->w_qT, gx, &ws->gy_sc->inv, &saved->w_sc->inv, M, K, N,
-                 amp_scale, found_inf};
-  GemmProblem wg{ws->gy_qT, saved->x_qT, gw, &ws->gy_sc->inv, &saved->x_sc->inv, N, K, M,
-                 amp_scale, found_inf};
   if (amp_scale)  // fp16 gradients unscaled and checked in the GEMM epilogues
     return hip_status(launch_gemm_unscale_pair(dg, wg, false, s));
   return hip_status(launch_gemm_pair(dg, wg, FP8SG_E5M2, FP8SG_E4M3FN, out, s));

@@ -864,7 +864,9 @@ static hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
     if (cus > 0) {
       const int64_t c256 = tile_rounds_cost(p.M, p.N, 256, cus);
       const int64_t c224 = tile_rounds_cost(p.M, p.N, 224, cus);
-      if constexpr (!RW && TA == TB) {
+      // (not when that would move a contraction-major B into the A slot,
+      // whose fragments take twice the transposed LDS reads of B's)
+      if constexpr (!RW && (TA || !TB)) {
         const int64_t c224t = tile_rounds_cost(p.N, p.M, 224, cus);
         if (c224t * 100 < (c224 < c256 ? c224 : c256) * 95) {
           GemmProblem q = p;

@@ -27,7 +27,13 @@
 // stores the result in its own partial slot of the record (at most
 // FP8SG_AMAX_PARTS blocks per tensor; the tiled blocks then loop over tiles).
 // k_hist_push then reduces those partials into rec->amax and pushes it to the
-// front of the history.  One pass over x instead of two.
+// front of the history.  One pass over x instead of two.  A tensor that needs
+// more blocks than there are slots (more than 16 Mi elements) takes the
+// two-level form: k_parts_clear zeroes the slots first, the cast runs one
+// pass per block like the dynamic cast, and block b folds its maximum into
+// slot b % FP8SG_AMAX_PARTS with an unsigned atomic max (the fp32 bits of
+// non-negative values order like the values, NaN canonical above +inf; a
+// maximum does not depend on the order of the updates).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -105,10 +111,15 @@ __device__ __forceinline__ float self_amax(const QuantJob& job) {
   return __uint_as_float(bits);
 }
 
-// DELAYED: this block's |x| maximum (packed pair max m) into its partial slot.
-template <bool DELAYED>
+// DELAYED: this block's |x| maximum (packed pair max m) into its partial slot
+// (ATOMIC: folded into slot lb % FP8SG_AMAX_PARTS, which k_parts_clear zeroed).
+static_assert((FP8SG_AMAX_PARTS & (FP8SG_AMAX_PARTS - 1)) == 0, "slot index by mask");
+template <bool DELAYED, bool ATOMIC = false>
 __device__ __forceinline__ void store_block_amax(const QuantJob& job, int lb, uint32_t m) {
-  if constexpr (DELAYED) {
+  if constexpr (DELAYED && ATOMIC) {
+    const uint32_t bits = block_max_u32<kQThreads>(absmax_bits(m));
+    if (threadIdx.x == 0) atomicMax(&job.rec->_part[lb & (FP8SG_AMAX_PARTS - 1)], bits);
+  } else if constexpr (DELAYED) {
     const uint32_t bits = block_max_u32<kQThreads>(absmax_bits(m));
     if (threadIdx.x == 0) {
       job.rec->_part[lb] = bits;
@@ -135,7 +146,7 @@ __device__ __forceinline__ void publish_scale(fp8sg_scale_rec* rec, float amax, 
   }
 }
 
-template <int FMT, bool S, int SRC, bool SELF = false, bool F16 = false>
+template <int FMT, bool S, int SRC, bool SELF = false, bool F16 = false, bool ATOMIC = false>
 __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
   static_assert(!F16 || (SRC == kSrcParts && !SELF), "fp16 inputs: dynamic casts only");
   constexpr bool DELAYED = SRC == kSrcHist;
@@ -238,19 +249,20 @@ __global__ __launch_bounds__(kQThreads) void k_quant_tiled(QuantArgs args) {
     }
     if (tile + job.nblocks < ntiles) __syncthreads();  // the next tile reuses lds
   }
-  store_block_amax<DELAYED>(job, lb, am);
+  store_block_amax<DELAYED, ATOMIC>(job, lb, am);
 }
 
 // Row-major codes only, any element count: grid-stride over 16-byte loads.
-// Dynamic scaling gives every block one pass of kFlatUnroll loads per thread
-// (up to kFlatMaxBlocks blocks; 2^28 elements at 6.5 TB/s against 6.1 with
-// 4096 striding blocks); delayed scaling has at most FP8SG_AMAX_PARTS blocks,
-// which stride with 8 loads in flight per thread.
-template <int SRC>
-constexpr int flat_unroll() { return SRC == kSrcHist ? 8 : 4; }
+// Dynamic scaling and the two-level delayed form give every block one pass of
+// kFlatUnroll loads per thread (up to kFlatMaxBlocks blocks; 2^28 elements at
+// 6.5 TB/s against 6.1 with 4096 striding blocks); otherwise delayed scaling
+// has at most FP8SG_AMAX_PARTS blocks, which stride with 8 loads in flight
+// per thread.
+template <int SRC, bool ATOMIC = false>
+constexpr int flat_unroll() { return SRC == kSrcHist && !ATOMIC ? 8 : 4; }
 constexpr int64_t kFlatMaxBlocks = 65536;
 
-template <int FMT, bool S, int SRC, bool F16 = false>
+template <int FMT, bool S, int SRC, bool F16 = false, bool ATOMIC = false>
 __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
   static_assert(!F16 || SRC == kSrcParts, "fp16 inputs: dynamic casts only");
   constexpr bool DELAYED = SRC == kSrcHist;
@@ -265,7 +277,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
   const uint4* const xv = reinterpret_cast<const uint4*>(
       nvec > 0 ? static_cast<const void*>(job.x) : static_cast<const void*>(job.rec));
   uint2* qv = reinterpret_cast<uint2*>(job.q);
-  constexpr int kFlatUnroll = flat_unroll<SRC>();
+  constexpr int kFlatUnroll = flat_unroll<SRC, ATOMIC>();
   const int64_t step = (int64_t)job.nblocks * kQThreads * kFlatUnroll;
   uint4 v[kFlatUnroll];
   // branch-free as in the tiled kernel: past the end a lane loads vector 0
@@ -309,7 +321,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_flat(QuantArgs args) {
     if constexpr (DELAYED) am = pmax(am, (uint32_t)(job.x[i] & 0x7FFFu));
     job.q[i] = quant1<FMT, F16>(job.x[i], sv.s32);
   }
-  store_block_amax<DELAYED>(job, lb, am);
+  store_block_amax<DELAYED, ATOMIC>(job, lb, am);
 }
 
 // Transposed copy of a shape the tiled kernel does not take: one thread per element.
@@ -333,6 +345,15 @@ __global__ __launch_bounds__(kQThreads) void k_quant_elem(QuantArgs args) {
     job.qT[cc * job.rows + r] = c;
   }
   store_block_amax<DELAYED>(job, lb, am);
+}
+
+// Two-level delayed cast, before it: every partial slot of each job's record
+// zeroed (the cast's blocks fold their maxima into them), all slots counted.
+// One block per job.
+__global__ __launch_bounds__(kQThreads) void k_parts_clear(QuantArgs args) {
+  fp8sg_scale_rec* rec = args.job[blockIdx.x].rec;
+  for (int i = threadIdx.x; i < FP8SG_AMAX_PARTS; i += kQThreads) rec->_part[i] = 0;
+  if (threadIdx.x == 0) rec->_nparts = FP8SG_AMAX_PARTS;
 }
 
 // Delayed scaling, after the cast: rec->amax = the current tensor's amax
@@ -372,7 +393,9 @@ static QuantPath path_of(const QuantJob& j) {
   return kPathElem;
 }
 
-static int blocks_of(QuantJob& j, QuantPath p) {
+// Blocks of a job on path p.  atomic: the two-level delayed form (the block
+// count is not bounded by the partial slots).
+static int blocks_of(QuantJob& j, QuantPath p, bool atomic = false) {
   const int64_t n = j.rows * j.cols;
   int64_t b;
   if (p == kPathTiled) {
@@ -381,15 +404,27 @@ static int blocks_of(QuantJob& j, QuantPath p) {
     b = tr * tc;
     if (b > (1 << 20)) b = 1 << 20;  // the blocks stride over the tiles
   } else if (p == kPathFlat) {
-    const int64_t per = (int64_t)kQThreads * (j.hist ? flat_unroll<kSrcHist>() : flat_unroll<kSrcParts>());
+    const int64_t per = (int64_t)kQThreads *
+        (j.hist ? (atomic ? flat_unroll<kSrcHist, true>() : flat_unroll<kSrcHist>()) : flat_unroll<kSrcParts>());
     b = ((n >> 3) + per - 1) / per;
     if (b > kFlatMaxBlocks) b = kFlatMaxBlocks;
   } else {
     b = (n + kQThreads - 1) / kQThreads;
     if (b > 4096) b = 4096;
   }
-  if (j.hist && b > FP8SG_AMAX_PARTS) b = FP8SG_AMAX_PARTS;  // one partial slot per block
+  if (j.hist && !atomic && b > FP8SG_AMAX_PARTS) b = FP8SG_AMAX_PARTS;  // one partial slot per block
   return (int)(b < 1 ? 1 : b);  // one block at least: it writes the scale fields
+}
+
+// Whether a delayed launch on path p takes the two-level form: some job
+// needs more blocks for one pass than there are partial slots.
+static bool two_level(const QuantArgs& a, int j0, int j1, QuantPath p) {
+  if (p == kPathElem) return false;
+  for (int j = j0; j < j1; ++j) {
+    QuantJob jb = a.job[j];
+    if (blocks_of(jb, p, true) > FP8SG_AMAX_PARTS) return true;
+  }
+  return false;
 }
 
 template <int FMT, int SRC, bool F16 = false>
@@ -402,9 +437,11 @@ static hipError_t launch_fmt(QuantArgs a, hipStream_t stream, bool self = false)
     int total = 0;
     int64_t bytes = 0;  // read + written by this launch
     int j = j0;
-    for (; j < a.njobs && path_of(a.job[j]) == p; ++j) {
-      QuantJob jb = a.job[j];
-      jb.nblocks = blocks_of(jb, p);
+    while (j < a.njobs && path_of(a.job[j]) == p) ++j;
+    const bool atomic = DELAYED && two_level(a, j0, j, p);
+    for (int i = j0; i < j; ++i) {
+      QuantJob jb = a.job[i];
+      jb.nblocks = blocks_of(jb, p, atomic);
       if (self) jb.nblocks = 1;  // the block loops over all the tensor's tiles
       jb.block0 = total;
       total += jb.nblocks;
@@ -412,7 +449,24 @@ static hipError_t launch_fmt(QuantArgs a, hipStream_t stream, bool self = false)
       sub.job[sub.njobs++] = jb;
     }
     const bool st = bytes >= kStreamBytes;
-    if (self && p == kPathTiled && SRC == kSrcParts && !F16)
+    if constexpr (DELAYED) {
+      if (atomic) {
+        hipLaunchKernelGGL(k_parts_clear, dim3(sub.njobs), dim3(kQThreads), 0, stream, sub);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (p == kPathTiled && st)
+          hipLaunchKernelGGL((k_quant_tiled<FMT, true, SRC, false, false, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
+        else if (p == kPathTiled)
+          hipLaunchKernelGGL((k_quant_tiled<FMT, false, SRC, false, false, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
+        else if (st)
+          hipLaunchKernelGGL((k_quant_flat<FMT, true, SRC, false, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
+        else
+          hipLaunchKernelGGL((k_quant_flat<FMT, false, SRC, false, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
+      }
+    }
+    if (atomic) {
+      // launched above
+    } else if (self && p == kPathTiled && SRC == kSrcParts && !F16)
       hipLaunchKernelGGL((k_quant_tiled<FMT, false, kSrcParts, true>), dim3(total), dim3(kQThreads), 0, stream, sub);
     else if (p == kPathTiled && st)
       hipLaunchKernelGGL((k_quant_tiled<FMT, true, SRC, false, F16>), dim3(total), dim3(kQThreads), 0, stream, sub);

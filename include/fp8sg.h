@@ -236,12 +236,18 @@ FP8SG_API fp8sg_status fp8_gemm_kmajor_unscale(const uint8_t* A, fp8sg_format fa
 /*
  * What the forward pass saves for the backward pass [FP8-TRAIN §6: the
  * quantized FP8 tensors and their inverse scales, not the bf16 inputs].
- * All pointers are caller-owned device buffers.  x_qT and w_qT are both given
- * or both NULL: NULL means no transposed copies are made, and the backward
- * GEMMs read x_q and w_q contraction-major (fp8_gemm_kmajor); the workspace's
- * gy_qT must then be NULL too (FP8SG_ERR_NULL otherwise).  Both forms give
- * the same results bit for bit; without the copies each cast writes 1 B per
- * element instead of 2 and the buffers are not needed.
+ * All pointers are caller-owned device buffers.  Each transposed copy (x_qT,
+ * w_qT here, gy_qT in the workspace) may be NULL on its own: that copy is not
+ * made, and the backward GEMM that would read it reads the row-major codes
+ * contraction-major instead (fp8_gemm_kmajor).  Every combination gives the
+ * same results bit for bit; a cast without its copy writes 1 B per element
+ * instead of 2.  Speed: a contraction-major operand costs nothing in the
+ * GEMM's second (B) slot and about 8% in the first (A) slot, which takes
+ * twice the fragment reads.  dgrad reads W in the B slot; wgrad gW = gy^T x
+ * puts gy in the A slot, except where the launcher swaps the roles to fit
+ * 224-row tiles along K (then x takes the A slot: the MLP block's
+ * down-projection, N = 4096, K = 14336).  Keeping the copy of the A-slot
+ * operand only is the fastest form where the layer is large.
  */
 typedef struct fp8_linear_saved {
   uint8_t* x_q;         /* [M,K] e4m3 codes of x                */
@@ -255,7 +261,7 @@ typedef struct fp8_linear_saved {
 /* Backward workspace: the quantized gradient and its scale record. */
 typedef struct fp8_linear_bwd_ws {
   uint8_t* gy_q;        /* [M,N] e5m2 codes of gy               */
-  uint8_t* gy_qT;       /* [N,M] transposed copy, or NULL (with the saved copies NULL) */
+  uint8_t* gy_qT;       /* [N,M] transposed copy, or NULL       */
   fp8sg_scale_rec* gy_sc;
 } fp8_linear_bwd_ws;
 

@@ -246,9 +246,9 @@ def test_fused_unscale_validation():
 
 
 def test_kmajor_validation():
-    """The contraction-major GEMMs validate as fp8_gemm does; a linear layer's
-    transposed copies are both given or both NULL, the backward workspace's
-    gy_qT with them."""
+    """The contraction-major GEMMs validate as fp8_gemm does; each of a linear
+    layer's transposed copies (x_qT, w_qT, gy_qT) may be NULL on its own (a
+    bad size after them shows the pointer checks passed, with no launch)."""
     L = F.lib()
     g = L.fp8_gemm_kmajor
     args = [P(A16), 0, 1, P(A16B), 0, 1, P(A16), P(A16), P(A16B), 0, 16, 32, 48, P(0)]
@@ -267,15 +267,19 @@ def test_kmajor_validation():
         P(A16), 1, 1, P(A16B), 0, 1, P(A16), P(A16), P(scale), P(found), P(C), M, 16, 32, P(0))
     assert u(scale=0) == ENULL and u(found=0) == ENULL and u(C=0) == ENULL
     assert u(M=24) == ESHAPE and u(scale=A16 + 1) == EALIGN
-    one = F._Saved(A16, 0, A16, A16, A16, A16)       # x_qT NULL, w_qT given
-    assert L.fp8_scaled_linear_fwd(P(A16), P(A16), 16, 16, 16, ctypes.byref(one), P(A16), 0,
-                                   P(0)) == ENULL
-    none = F._Saved(A16, 0, A16, 0, A16, A16)        # no transposed copies
-    both = F._Saved(A16, A16, A16, A16, A16, A16)
-    ws_t, ws_n = F._BwdWs(A16, A16, A16), F._BwdWs(A16, 0, A16)
-    bwd = lambda s, ws: L.fp8_scaled_linear_bwd(P(A16), ctypes.byref(s), 16, 16, 16,
-                                                ctypes.byref(ws), P(A16), P(A16), 0, P(0))
-    assert bwd(none, ws_t) == ENULL and bwd(both, ws_n) == ENULL
+    fwd = lambda s, M: L.fp8_scaled_linear_fwd(P(A16), P(A16), M, 16, 16, ctypes.byref(s),
+                                               P(A16), 0, P(0))
+    bwd = lambda s, ws, M: L.fp8_scaled_linear_bwd(P(A16), ctypes.byref(s), M, 16, 16,
+                                                   ctypes.byref(ws), P(A16), P(A16), 0, P(0))
+    for xt in (0, A16):
+        for wt in (0, A16):
+            s = F._Saved(A16, xt, A16, wt, A16, A16)
+            assert fwd(s, 24) == ESHAPE
+            for gt in (0, A16):
+                assert bwd(s, F._BwdWs(A16, gt, A16), 24) == ESHAPE
+            assert bwd(s, F._BwdWs(0, A16, A16), 16) == ENULL      # gy_q is required
+    assert fwd(F._Saved(0, A16, A16, A16, A16, A16), 16) == ENULL  # x_q is required
+    assert fwd(F._Saved(A16, MIS, A16, A16, A16, A16), 16) == EALIGN
 
 
 def test_gemm_unscale_validation():

@@ -179,3 +179,27 @@ def test_delayed_record_reused_after_a_larger_tensor(transposed):
         ref = O.to_fp8_delayed(x, O.E4M3FN, hist_h, with_transpose=transposed)
         check_step(rec, hist, q, qT, ref, O.E4M3FN, f"reused record, step {t}")
         hist_h = ref.hist
+
+
+@pytest.mark.parametrize("shape,transposed", [((4224, 4096), True), ((4099, 4097), False)])
+def test_delayed_two_level_over_stale_slots(shape, transposed):
+    """Tensors that need more blocks than there are partial slots (1056 tiles
+    of 128 x 128; 2050 flat blocks with a ragged tail) take the two-level
+    cast, whose blocks fold their maxima into slots cleared first: a record
+    whose slots a tensor of larger amax filled must not leak into the amax
+    pushed to the history."""
+    rec = F.ScaleRec(device=DEV)
+    big = W.normal_bf16(43, 0, (4096, 2048), 1.0, 0.002, 500.0)
+    F.fp8_amax(dev16(big).reshape(big.shape), rec)
+    hist_h = np.array([0.004, 0.002], np.float32)
+    hist = torch.from_numpy(hist_h.copy()).to(DEV)
+    rows, cols = shape
+    q = torch.empty(shape, dtype=torch.uint8, device=DEV)
+    qT = torch.empty((cols, rows), dtype=torch.uint8, device=DEV) if transposed else None
+    for t in range(2):
+        x = W.normal_bf16(43, t + 1, shape, 1e-3)
+        F.fp8_quantize_delayed(dev16(x).reshape(shape), O.E5M2, rec, hist, q, qT)
+        torch.cuda.synchronize()
+        ref = O.to_fp8_delayed(x, O.E5M2, hist_h, with_transpose=transposed)
+        check_step(rec, hist, q, qT, ref, O.E5M2, f"two-level {shape}, step {t}")
+        hist_h = ref.hist

@@ -81,7 +81,7 @@ def test_kmajor_formats_match_oracle(fa, fb, shape):
     assert nw <= 1e-3
 
 
-@pytest.mark.parametrize("ta,tb", [(0, 1), (1, 1)])
+@pytest.mark.parametrize("ta,tb", [(0, 1), (1, 0), (1, 1)])
 @pytest.mark.parametrize("shape", [(144, 272, 400), (4000, 2064, 400), (912, 13072, 400)])
 def test_kmajor_unscale_equals_rowmajor(ta, tb, shape):
     """The fused-unscale epilogue on contraction-major operands: the fp16
@@ -105,8 +105,9 @@ def run_layer(M, N, K, transposed, delayed, seed):
     x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(DEV)
     w = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16).to(DEV)
     gy = (1e-4 * 65536.0 * torch.randn(M, N, generator=g)).to(torch.bfloat16).to(DEV)
-    saved = F.LinearSaved(M, N, K, transposed=transposed)
-    ws = F.LinearBwdWs(M, N, transposed=transposed)
+    xt, wt, gt = transposed if isinstance(transposed, tuple) else (transposed,) * 3
+    saved = F.LinearSaved(M, N, K, x_transposed=xt, w_transposed=wt)
+    ws = F.LinearBwdWs(M, N, transposed=gt)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     gx = torch.empty((M, K), dtype=torch.float16, device=DEV)
     gw = torch.empty((N, K), dtype=torch.float16, device=DEV)
@@ -133,17 +134,23 @@ def run_layer(M, N, K, transposed, delayed, seed):
                 x_q=saved.x_q, w_q=saved.w_q, gy_q=ws.gy_q, found=found, hists=hists, recs=recs)
 
 
+LAYOUTS = [False, (False, False, True), (True, False, False), (False, True, True),
+           (True, True, False)]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("delayed", [False, True])
 @pytest.mark.parametrize("shape", [(64, 256, 128), (1024, 1536, 768), (4096, 4096, 2048),
-                                   (2048, 14336, 4096)])
-def test_linear_without_transposed_copies(shape, delayed):
+                                   (2048, 14336, 4096), (2048, 4096, 14336)])
+def test_linear_without_transposed_copies(shape, delayed, layout):
     """Forward, backward with the fused unscale, and (dynamic) the plain bf16
-    backward: identical with and without transposed copies (the small
-    layer's one-block cast, the 128 x 128 pair launch, the 256 x 256 and
-    224-row forms)."""
+    backward: identical with all transposed copies and with none or some of
+    them (x_qT, w_qT, gy_qT) -- the small layer's one-block cast, the
+    128 x 128 pair launch, the 256 x 256 and 224-row forms, and the
+    down-projection form whose weight gradient swaps the operands' roles."""
     M, N, K = shape
     a = run_layer(M, N, K, True, delayed, M + N + K)
-    b = run_layer(M, N, K, False, delayed, M + N + K)
+    b = run_layer(M, N, K, layout, delayed, M + N + K)
     assert a["recs"] == b["recs"]
     for k in ("y", "gx", "gw", "gx2", "gw2", "x_q", "w_q", "gy_q", "found"):
         if a[k] is None:
