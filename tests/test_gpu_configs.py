@@ -253,18 +253,33 @@ def test_quantize_flat_past_one_pass_per_block(delayed):
     assert_codes_equal(O.E4M3FN, q.cpu().numpy(), ref_q, "flat striding")
 
 
-def _scaler_reference(sizes, injections, values_finite_ok):
-    """Oracle trajectory of (found, scale, tracker) per step."""
+def _scaler_reference(pristine_h, injections):
+    """The oracle's trajectory: per step the scale it runs with, and after its
+    update (found, scale, tracker).  A step's flag is the oracle's
+    unscale_check of that step's data at that scale: the resident tensors
+    (whose flag depends only on the scale, so it is computed once per
+    distinct scale, tensor by tensor) and, on an injected step, the injected
+    tensor with its inf/NaN."""
     inj = {j.step: j for j in injections}
     st = O.ScalerState(np.float32(C.INIT_SCALE), 0)
-    traj = []
+    base = {}
+    before, traj = [], []
     for s in range(C.SCALER_STEPS):
-        found = 1 if s in inj else 0
-        if s not in inj:
-            assert values_finite_ok
+        sc = float(st.scale)
+        if sc not in base:
+            f = 0
+            for g in pristine_h:
+                f = O.unscale_check([g.copy()], sc, f)
+            base[sc] = f
+        found = base[sc]
+        if s in inj:
+            g = pristine_h[inj[s].tensor].copy()
+            g[inj[s].index] = inj[s].bits
+            found = O.unscale_check([g], sc, found)
+        before.append(sc)
         st = O.update_scale(st, found, C.GROWTH, C.BACKOFF, C.SCALER_INTERVAL)
         traj.append((found, float(st.scale), st.tracker))
-    return traj
+    return before, traj
 
 
 def test_gradscaler_200_tensors_1000_steps_full_size():
@@ -273,13 +288,21 @@ def test_gradscaler_200_tensors_1000_steps_full_size():
     growth interval 100.  Each step restores the tensors from a resident copy
     (values N(0,1e-5) * 65536), injects per the schedule, then runs one
     amp_unscale_check over all 200 tensors and amp_update_scale.  The
-    found/scale/tracker trajectory must equal the oracle's over all 1000 steps;
-    unscaled values are compared in full at step 0 and sampled at the first
-    injected and the last step."""
+    found/scale/tracker trajectory must equal the oracle's over all 1000 steps
+    (the oracle runs unscale_check on every step's data, see
+    _scaler_reference); the unscaled values are compared in full at the first
+    step that runs with each distinct scale, and sampled (with the injected
+    element) at the first injected and the last step."""
     sizes = C.scaler_sizes()
     injections = C.injection_schedule(sizes)
     log(f"scaler: {len(sizes)} tensors, {int(sizes.sum())} elements, {len(injections)} injections")
     pristine_h = [C.scaler_grad(t, int(n), C.INIT_SCALE) for t, n in enumerate(sizes)]
+    log("scaler: oracle trajectory")
+    before, traj = _scaler_reference(pristine_h, injections)
+    full_at = {}
+    for s, sc in enumerate(before):
+        full_at.setdefault(sc, s)
+    full_steps = set(full_at.values())
     pristine = [dev16(g, torch.float16) for g in pristine_h]
     work = [torch.empty_like(p) for p in pristine]
     scale = torch.tensor([C.INIT_SCALE], dtype=torch.float32, device=DEV)
@@ -288,7 +311,6 @@ def test_gradscaler_200_tensors_1000_steps_full_size():
     hist = torch.zeros((C.SCALER_STEPS, 3), dtype=torch.float64, device=DEV)
     inj = {j.step: j for j in injections}
     first_inj = injections[0].step if injections else None
-    checks = {}
     inj_bits = torch.tensor([0], dtype=torch.int16, device=DEV)
     for s in range(C.SCALER_STEPS):
         for wv, pv in zip(work, pristine):
@@ -297,47 +319,41 @@ def test_gradscaler_200_tensors_1000_steps_full_size():
             j = inj[s]
             inj_bits.fill_(int(np.array([j.bits], np.uint16).view(np.int16)[0]))
             work[j.tensor].view(torch.int16)[j.index:j.index + 1].copy_(inj_bits)
-        scale_before = float(scale.item()) if s in (0, first_inj, C.SCALER_STEPS - 1) else None
         F.amp_unscale_check(work, scale, found)
         hist[s, 0].copy_(found[0])
         F.amp_update_scale(scale, tracker, found, C.GROWTH, C.BACKOFF, C.SCALER_INTERVAL)
         hist[s, 1].copy_(scale[0])
         hist[s, 2].copy_(tracker[0])
-        if scale_before is not None:
+        if s in full_steps:
             torch.cuda.synchronize()
-            checks[s] = scale_before
-            if s == 0:
-                log("scaler: full element-wise check at step 0")
-                ref = [g.copy() for g in pristine_h]
-                f0 = O.unscale_check(ref, scale_before, 0)
-                assert f0 == 0  # every value is finite after unscaling
-                for t, wv in enumerate(work):
-                    assert_codes_equal(O.F16, host16(wv), ref[t], f"step 0 tensor {t}")
-                del ref
-            else:
-                log(f"scaler: sampled check at step {s}")
-                rng = np.random.default_rng(s)
-                for t in rng.choice(len(sizes), 20, replace=False).tolist() + \
-                        ([inj[s].tensor] if s in inj else []):
-                    n = int(sizes[t])
-                    idx = np.unique(np.concatenate([rng.integers(0, n, 5000),
-                                                    [inj[s].index] if (s in inj and inj[s].tensor == t) else []]).astype(np.int64))
-                    src = pristine_h[t][idx].copy()
-                    if s in inj and inj[s].tensor == t:
-                        src[np.searchsorted(idx, inj[s].index)] = inj[s].bits
-                    O.unscale_check([src], scale_before, 0)
-                    got = host16(work[t])[idx]
-                    assert_codes_equal(O.F16, got, src, f"step {s} tensor {t}")
+            log(f"scaler: full element-wise check at step {s} (scale {before[s]})")
+            for t, wv in enumerate(work):
+                ref = pristine_h[t].copy()
+                if s in inj and inj[s].tensor == t:
+                    ref[inj[s].index] = inj[s].bits
+                O.unscale_check([ref], before[s], 0)
+                assert_codes_equal(O.F16, host16(wv), ref, f"step {s} tensor {t}")
+            del ref
+        elif s in (first_inj, C.SCALER_STEPS - 1):
+            torch.cuda.synchronize()
+            log(f"scaler: sampled check at step {s}")
+            rng = np.random.default_rng(s)
+            for t in rng.choice(len(sizes), 20, replace=False).tolist() + \
+                    ([inj[s].tensor] if s in inj else []):
+                n = int(sizes[t])
+                idx = np.unique(np.concatenate([rng.integers(0, n, 5000),
+                                                [inj[s].index] if (s in inj and inj[s].tensor == t) else []]).astype(np.int64))
+                src = pristine_h[t][idx].copy()
+                if s in inj and inj[s].tensor == t:
+                    src[np.searchsorted(idx, inj[s].index)] = inj[s].bits
+                O.unscale_check([src], before[s], 0)
+                got = host16(work[t])[idx]
+                assert_codes_equal(O.F16, got, src, f"step {s} tensor {t}")
         if s % 100 == 0:
             log(f"scaler: step {s}")
     torch.cuda.synchronize()
-    # the oracle's found flag on the injected tensor at every injected step
-    for j in injections:
-        g = pristine_h[j.tensor].copy()
-        g[j.index] = j.bits
-        assert O.unscale_check([g], C.INIT_SCALE, 0) == 1
-    traj = _scaler_reference(sizes, injections, values_finite_ok=True)
     h = hist.cpu().numpy()
+    assert sum(f for f, _, _ in traj) == len(injections)
     for s in range(C.SCALER_STEPS):
         assert (int(h[s, 0]), float(h[s, 1]), int(h[s, 2])) == traj[s], f"step {s}"
     log(f"scaler: trajectory ok, final scale {traj[-1][1]}, tracker {traj[-1][2]}")
