@@ -67,12 +67,12 @@ def parse():
                    help="only the HBM-scale passes (for counter runs); prints their figures")
     p.add_argument("--square-only", action="store_true",
                    help="only the square 4096^3 layer's side line (for counter runs)")
-    p.add_argument("--layout", choices=("a-slot", "none", "all"), default="a-slot",
-                   help="which transposed code copies the MLP step's casts write: 'a-slot' "
-                        "(default) those of the weight-gradient GEMMs' first operand (gy of "
-                        "gate and up, h of down), the other operands read contraction-major; "
-                        "'none': every backward operand read contraction-major; 'all': every "
-                        "copy written and read row-major")
+    p.add_argument("--layout", choices=("auto", "none", "all"), default="auto",
+                   help="which transposed code copies the MLP step's casts write: 'auto' "
+                        "(default) those fp8_linear_copies picks (the weight-gradient GEMMs' "
+                        "first operand: gy of gate and up, h of down), the other operands read "
+                        "contraction-major; 'none': every backward operand read "
+                        "contraction-major; 'all': every copy written and read row-major")
     p.add_argument("--copy-reference", action="store_true",
                    help="only copy 1 GiB device-to-device 5 times (calibrates the HBM byte "
                         "counters against a transfer of known size)")
@@ -162,20 +162,26 @@ class MlpStep:
 
     NAMES = ("gate", "up", "down")
 
-    # which tensors' casts write a transposed copy, per layout: the weight
-    # gradient's first GEMM operand (gy of gate and up; h for down, whose
-    # weight gradient runs with the operands' roles swapped) is read twice as
-    # often from LDS as the second, so only there does a contraction-major
-    # read cost time
-    LAYOUTS = {"a-slot": {"h", "gy_gate", "gy_up"}, "none": set(),
-               "all": {"x", "h", "w_gate", "w_up", "w_down", "gy_gate", "gy_up", "gy_down"}}
+    # which tensors' casts write a transposed copy: "auto" asks the library
+    # (fp8_linear_copies: the weight gradient's first GEMM operand, read twice
+    # as often from LDS as the second, keeps its copy -- gy of gate and up, h
+    # for down, whose weight gradient runs with the operands' roles swapped)
+    ALL = {"x", "h", "w_gate", "w_up", "w_down", "gy_gate", "gy_up", "gy_down"}
 
-    def __init__(self, np, torch, F, dev, layout="a-slot"):
+    def __init__(self, np, torch, F, dev, layout="auto"):
         from workloads.configs import mlp_linear, MLP_T, MLP_H, MLP_F
         self.F, self.torch, self.layout = F, torch, layout
-        self.tr = self.LAYOUTS[layout]
-        self.T, self.H, self.Fd = MLP_T, MLP_H, MLP_F
         self.lin = {n: mlp_linear(n) for n in self.NAMES}
+        if layout == "auto":
+            self.tr = set()
+            for n, L in self.lin.items():
+                xt, wt, gt = F.fp8_linear_copies(L.M, L.N, L.K)
+                for key, on in ((("h" if n == "down" else "x"), xt), ("w_" + n, wt), ("gy_" + n, gt)):
+                    if on:
+                        self.tr.add(key)
+        else:
+            self.tr = set() if layout == "none" else set(self.ALL)
+        self.T, self.H, self.Fd = MLP_T, MLP_H, MLP_F
         log("generating the MLP block's inputs")
         self.host = {}
         g = self.lin["gate"]

@@ -29,7 +29,7 @@ EXPORTS = ("fp8sg_status_string", "fp8sg_version", "amp_norm_workspace_len", "fp
            "fp8_scaled_linear_bwd_rowwise", "fp8_scaled_linear_bwd_unscale", "fp8_gemm_unscale",
            "fp8_scaled_linear_bwd_delayed_unscale", "fp8_scaled_linear_bwd_rowwise_unscale",
            "fp8_quantize_from_amax", "amp_unscale_check_norm_noalloc", "fp8_amax_f16",
-           "fp8_quantize_f16", "fp8_gemm_kmajor", "fp8_gemm_kmajor_unscale")
+           "fp8_quantize_f16", "fp8_gemm_kmajor", "fp8_gemm_kmajor_unscale", "fp8_linear_copies")
 MAX_HISTORY = 1024
 MAX_DIM = 1 << 29     # largest matrix dimension an entry point takes
 MAX_ELEMS = 1 << 35   # largest tensor, in elements
@@ -84,6 +84,7 @@ def lib():
     L.fp8_quantize_f16.argtypes = [P, i64, i64, i, P, P, P, P]
     L.fp8_gemm.argtypes = [P, i, P, i, P, P, P, i, i64, i64, i64, P]
     L.fp8_gemm_kmajor.argtypes = [P, i, i32, P, i, i32, P, P, P, i, i64, i64, i64, P]
+    L.fp8_linear_copies.argtypes = [i64, i64, i64, P, P, P]
     L.fp8_gemm_kmajor_unscale.argtypes = [P, i, i32, P, i, i32, P, P, P, P, P, i64, i64, i64, P]
     L.fp8_scaled_linear_fwd.argtypes = [P, P, i64, i64, i64, ctypes.POINTER(_Saved), P, i, P]
     L.fp8_scaled_linear_bwd.argtypes = [P, ctypes.POINTER(_Saved), i64, i64, i64,
@@ -364,6 +365,23 @@ def fp8_gemm_kmajor_unscale(A: torch.Tensor, fa: int, a_kmajor: bool, B: torch.T
                                          int(bool(b_kmajor)), ctypes.c_void_p(inv_a_ptr),
                                          ctypes.c_void_p(inv_b_ptr), _ptr(scale), _ptr(found_inf),
                                          _ptr(C), M, N, K, _stream(stream)), "fp8_gemm_kmajor_unscale")
+
+
+_copies_cache = {}
+
+
+def fp8_linear_copies(M: int, N: int, K: int):
+    """(x_T, w_T, gy_T): which transposed copies make the backward of an
+    M x N x K linear layer fastest on the current device (the results are the
+    same bits with any choice).  Cached per device and size."""
+    key = (torch.cuda.current_device() if torch.cuda.is_available() else -1, M, N, K)
+    got = _copies_cache.get(key)
+    if got is None:
+        v = [ctypes.c_int32(0) for _ in range(3)]
+        _check(lib().fp8_linear_copies(M, N, K, *[ctypes.addressof(a) for a in v]),
+               "fp8_linear_copies")
+        got = _copies_cache[key] = tuple(bool(a.value) for a in v)
+    return got
 
 
 class LinearSaved:

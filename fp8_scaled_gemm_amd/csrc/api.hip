@@ -82,6 +82,19 @@ const char* fp8sg_status_string(int status) {
 
 int fp8sg_version(void) { return 100; }
 
+fp8sg_status fp8_linear_copies(int64_t M, int64_t N, int64_t K, int32_t* x_T, int32_t* w_T,
+                               int32_t* gy_T) {
+  if (!x_T || !w_T || !gy_T) return FP8SG_ERR_NULL;
+  if (!dims16_pos(M) || !dims16_pos(N) || !dims16_pos(K) || !gemm_ok(M, N, K))
+    return FP8SG_ERR_SHAPE;
+  bool x = false, w = false, g = false;
+  linear_copies(M, N, K, x, w, g);
+  *x_T = x;
+  *w_T = w;
+  *gy_T = g;
+  return FP8SG_OK;
+}
+
 fp8sg_status fp8_amax(const uint16_t* x, int64_t n, fp8sg_scale_rec* rec, fp8sg_stream stream) {
   if (!rec || (n > 0 && !x)) return FP8SG_ERR_NULL;
   if (n < 0 || n > FP8SG_MAX_ELEMS) return FP8SG_ERR_SHAPE;

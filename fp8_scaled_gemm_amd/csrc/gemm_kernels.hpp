@@ -853,34 +853,45 @@ inline bool big_tiles_fit(const GemmProblem& p) {
   return p.K > 0 && (TA ? p.K * p.M < lim : p.K * 256 < lim) && (TB ? p.K * p.N < lim : p.K * 256 < lim);
 }
 
+// The large-tile kernel's tiling of an M x N output on `cus` CUs: 256 x 256
+// tiles, 224-row tiles along M, or (swap_ok) 224-row tiles along N with the
+// operands' roles swapped, where their rounds over the CUs take clearly
+// (5%) less time.  cus <= 0 (unknown) keeps 256 x 256.
+enum BigTiling { kTile256, kTile224, kTile224Swapped };
+inline BigTiling big_tiling(int64_t M, int64_t N, int cus, bool swap_ok) {
+  if (cus <= 0) return kTile256;
+  const int64_t c256 = tile_rounds_cost(M, N, 256, cus);
+  const int64_t c224 = tile_rounds_cost(M, N, 224, cus);
+  if (swap_ok && tile_rounds_cost(N, M, 224, cus) * 100 < (c224 < c256 ? c224 : c256) * 95)
+    return kTile224Swapped;
+  return c224 * 100 < c256 * 95 ? kTile224 : kTile256;
+}
+// Enough 256 x 256 tiles to fill the chip: the large-tile kernel's range.
+inline bool big_tiles_wanted(int64_t M, int64_t N) {
+  return ((M + 255) / 256) * ((N + 255) / 256) >= 128;
+}
+
 template <int FA, int FB, int OUT, bool RW, bool TA = false, bool TB = false>
 static hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
-  // 256 x 256 tiles once there are enough of them to fill the chip.
-  // 224-row tiles (along M, or along N with the operands' roles swapped)
-  // where their rounds over the CUs take clearly less time.
-  const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (big >= 128 && big_tiles_fit<TA, TB>(p)) {
-    const int cus = device_cus();
-    if (cus > 0) {
-      const int64_t c256 = tile_rounds_cost(p.M, p.N, 256, cus);
-      const int64_t c224 = tile_rounds_cost(p.M, p.N, 224, cus);
-      // (not when that would move a contraction-major B into the A slot,
-      // whose fragments take twice the transposed LDS reads of B's)
-      if constexpr (!RW && (TA || !TB)) {
-        const int64_t c224t = tile_rounds_cost(p.N, p.M, 224, cus);
-        if (c224t * 100 < (c224 < c256 ? c224 : c256) * 95) {
-          GemmProblem q = p;
-          q.A = p.B;
-          q.B = p.A;
-          q.inv_a = p.inv_b;
-          q.inv_b = p.inv_a;
-          q.M = p.N;
-          q.N = p.M;
-          return launch_pingpong<FB, FA, OUT, RW, 224, true, TB, TA>(q, stream);
-        }
+  // The large-tile kernel in the tiling big_tiling picks.  The roles are not
+  // swapped under row-wise scaling, nor where that would move a
+  // contraction-major B into the A slot, whose fragments take twice the
+  // transposed LDS reads of B's.
+  if (big_tiles_wanted(p.M, p.N) && big_tiles_fit<TA, TB>(p)) {
+    const BigTiling t = big_tiling(p.M, p.N, device_cus(), !RW && (TA || !TB));
+    if constexpr (!RW && (TA || !TB)) {
+      if (t == kTile224Swapped) {
+        GemmProblem q = p;
+        q.A = p.B;
+        q.B = p.A;
+        q.inv_a = p.inv_b;
+        q.inv_b = p.inv_a;
+        q.M = p.N;
+        q.N = p.M;
+        return launch_pingpong<FB, FA, OUT, RW, 224, true, TB, TA>(q, stream);
       }
-      if (c224 * 100 < c256 * 95) return launch_pingpong<FA, FB, OUT, RW, 224, false, TA, TB>(p, stream);
     }
+    if (t == kTile224) return launch_pingpong<FA, FB, OUT, RW, 224, false, TA, TB>(p, stream);
     return launch_pingpong<FA, FB, OUT, RW, 256, false, TA, TB>(p, stream);
   }
   return launch_cfg<128, 128, 2, 2, FA, FB, OUT, RW, TA, TB>(p, stream);

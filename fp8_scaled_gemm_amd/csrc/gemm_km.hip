@@ -15,6 +15,19 @@ hipError_t launch_gemm_km01(const GemmProblem& p, int fa, int fb, int out, hipSt
 hipError_t launch_gemm_km10(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);
 hipError_t launch_gemm_km11(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);
 
+void linear_copies(int64_t M, int64_t N, int64_t K, bool& x_t, bool& w_t, bool& gy_t) {
+  // dgrad (M x K over N) reads W in the B slot: a contraction-major read
+  // costs nothing there.  wgrad (N x K over M): the operand in the A slot
+  // keeps its copy -- x where the launcher swaps the roles, else gy -- when
+  // it takes the large-tile kernel; small layers keep none (both backward
+  // GEMMs then share one launch of the 128 x 128 kernel).
+  w_t = false;
+  x_t = gy_t = false;
+  if (!big_tiles_wanted(N, K)) return;
+  if (big_tiling(N, K, device_cus(), true) == kTile224Swapped) x_t = true;
+  else gy_t = true;
+}
+
 hipError_t launch_gemm_km(const GemmProblem& p, int fa, int fb, int out, bool ta, bool tb,
                           hipStream_t stream) {
   if (ta && tb) return launch_gemm_km11(p, fa, fb, out, stream);

@@ -87,6 +87,9 @@ hipError_t launch_gemm_km(const GemmProblem& p, int fa, int fb, int out, bool ta
                           hipStream_t stream);
 hipError_t launch_gemm_km_pair(const GemmProblem& dgrad, const GemmProblem& wgrad, int out,
                                hipStream_t stream);
+// Which transposed copies make the backward of an M x N x K linear layer
+// fastest on the current device (fp8_linear_copies).
+void linear_copies(int64_t M, int64_t N, int64_t K, bool& x_t, bool& w_t, bool& gy_t);
 // Row-wise scaling (gemm_rowwise.hip): inv_a points to M doubles, inv_b to N;
 // element (m, n) is scaled by fl32(inv_a[m] * inv_b[n]).
 hipError_t launch_gemm_rowwise(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);

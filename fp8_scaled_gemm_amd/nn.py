@@ -43,7 +43,8 @@ from torch import nn
 from . import (E4M3FN, E5M2, LinearBwdWs, LinearBwdWsRW, LinearSaved, LinearSavedRW, OUT_BF16,
                OUT_F16, SCALE_REC_BYTES, ScaleRec,
                amp_norm_workspace_len, amp_unscale_check, amp_unscale_check_norm,
-               amp_update_scale, fp8_amax, fp8_amax_f16, fp8_gemm, fp8_gemm_unscale,
+               amp_update_scale, fp8_amax, fp8_amax_f16, fp8_gemm, fp8_gemm_kmajor,
+               fp8_gemm_kmajor_unscale, fp8_linear_copies,
                fp8_quantize_f16, fp8_scaled_linear_bwd, fp8_scaled_linear_bwd_delayed,
                fp8_scaled_linear_bwd_rowwise, fp8_scaled_linear_fwd, fp8_scaled_linear_fwd_delayed,
                fp8_scaled_linear_fwd_rowwise)
@@ -63,27 +64,37 @@ def _seed_history(hist: torch.Tensor, x: torch.Tensor):
 # ---------------------------------------------------------------- custom ops
 # The dynamic-scaling linear as two operators.  The forward returns y and the
 # state the backward needs (codes, transposed codes, the two scale records),
-# all fresh outputs; nothing is mutated.
+# all fresh outputs; nothing is mutated.  Which transposed copies are made
+# follows fp8_linear_copies (the fastest backward on this device); a copy not
+# made travels as an empty tensor.
+
+def _present(t):
+    return t if t is not None and t.numel() > 0 else None
+
 
 @torch.library.custom_op("fp8sg::scaled_linear_fwd", mutates_args=())
 def _op_fwd(x: torch.Tensor, w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor,
                                                          torch.Tensor, torch.Tensor, torch.Tensor]:
     M, K = x.shape
     N = w.shape[0]
-    saved = LinearSaved(M, N, K, device=x.device)
+    xt, wt, _ = fp8_linear_copies(M, N, K)
+    saved = LinearSaved(M, N, K, device=x.device, x_transposed=xt, w_transposed=wt)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     fp8_scaled_linear_fwd(x, w, saved, y, OUT_BF16)
-    return (y, *saved.tensors())
+    empty = torch.empty(0, dtype=torch.uint8, device=x.device)
+    return (y, saved.x_q, saved.x_qT if xt else empty, saved.w_q, saved.w_qT if wt else empty.clone(),
+            saved.recs)
 
 
 @_op_fwd.register_fake
 def _op_fwd_fake(x, w):
     M, K = x.shape
     N = w.shape[0]
+    xt, wt, _ = fp8_linear_copies(M, N, K)
     u8 = dict(dtype=torch.uint8, device=x.device)
     return (x.new_empty((M, N), dtype=torch.bfloat16), x.new_empty((M, K), **u8),
-            x.new_empty((K, M), **u8), x.new_empty((N, K), **u8), x.new_empty((K, N), **u8),
-            x.new_empty((2, SCALE_REC_BYTES), **u8))
+            x.new_empty((K, M) if xt else (0,), **u8), x.new_empty((N, K), **u8),
+            x.new_empty((K, N) if wt else (0,), **u8), x.new_empty((2, SCALE_REC_BYTES), **u8))
 
 
 @torch.library.custom_op("fp8sg::scaled_linear_bwd", mutates_args=())
@@ -91,10 +102,11 @@ def _op_bwd(gy: torch.Tensor, x_q: torch.Tensor, x_qT: torch.Tensor, w_q: torch.
             w_qT: torch.Tensor, recs: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
     M, N = gy.shape
     K = x_q.shape[1]
-    saved = LinearSaved(M, N, K, tensors=(x_q, x_qT, w_q, w_qT, recs))
+    saved = LinearSaved(M, N, K, tensors=(x_q, _present(x_qT), w_q, _present(w_qT), recs))
     gx = torch.empty((M, K), dtype=torch.bfloat16, device=gy.device)
     gw = torch.empty((N, K), dtype=torch.bfloat16, device=gy.device)
-    fp8_scaled_linear_bwd(gy, saved, LinearBwdWs(M, N, device=gy.device), gx, gw, OUT_BF16)
+    ws = LinearBwdWs(M, N, device=gy.device, transposed=fp8_linear_copies(M, N, K)[2])
+    fp8_scaled_linear_bwd(gy, saved, ws, gx, gw, OUT_BF16)
     return gx, gw
 
 
@@ -136,7 +148,8 @@ class _Fp8LinearFn(torch.autograd.Function):
             fp8_scaled_linear_fwd_rowwise(x2d, weight, saved, y, OUT_BF16)
             ctx.save_for_backward(*saved.tensors())
             return y
-        saved = LinearSaved(M, N, K, device=x2d.device)
+        xt, wt, _ = fp8_linear_copies(M, N, K)
+        saved = LinearSaved(M, N, K, device=x2d.device, x_transposed=xt, w_transposed=wt)
         if mod.scaling == "delayed":
             if not mod._seeded_fwd:
                 _seed_history(mod.hist_x, x2d)
@@ -163,7 +176,7 @@ class _Fp8LinearFn(torch.autograd.Function):
                                           gw, OUT_BF16)
             return gx, gw, None
         saved = LinearSaved(M, N, K, tensors=ctx.saved_tensors)
-        ws = mod._bwd_scratch(M, N, gy.device, False)
+        ws = mod._bwd_scratch(M, N, gy.device, False, fp8_linear_copies(M, N, K)[2])
         if mod.scaling == "delayed":
             if not mod._seeded_bwd:
                 _seed_history(mod.hist_gy, gy)
@@ -186,7 +199,8 @@ class _Fp8LinearF16Fn(torch.autograd.Function):
     def forward(ctx, x2d: torch.Tensor, weight: torch.Tensor, mod: "Float8Linear"):
         M, K = x2d.shape
         N = weight.shape[0]
-        saved = LinearSaved(M, N, K, device=x2d.device)
+        xt, wt, _ = fp8_linear_copies(M, N, K)
+        saved = LinearSaved(M, N, K, device=x2d.device, x_transposed=xt, w_transposed=wt)
         fp8_amax_f16(x2d, saved.x_sc)
         fp8_quantize_f16(x2d, E4M3FN, saved.x_sc, saved.x_q, saved.x_qT)
         fp8_amax_f16(weight, saved.w_sc)
@@ -207,21 +221,24 @@ class _Fp8LinearF16Fn(torch.autograd.Function):
             raise TypeError(f"an fp16 Float8Linear expects fp16 output gradients, got {gy.dtype}")
         gy = gy.contiguous()
         saved = LinearSaved(M, N, K, tensors=ctx.saved_tensors)
-        ws = mod._bwd_scratch(M, N, gy.device, False)
+        ws = mod._bwd_scratch(M, N, gy.device, False, fp8_linear_copies(M, N, K)[2])
         fp8_amax_f16(gy, ws.gy_sc)
         fp8_quantize_f16(gy, E5M2, ws.gy_sc, ws.gy_q, ws.gy_qT)
+        # an operand without its transposed copy is read contraction-major
+        wk, gk, xk = saved.w_qT is None, ws.gy_qT is None, saved.x_qT is None
         gx = torch.empty((M, K), dtype=torch.float16, device=gy.device)
-        fp8_gemm(ws.gy_q, E5M2, saved.w_qT, E4M3FN, ws.gy_sc.inv_ptr(), saved.w_sc.inv_ptr(), gx,
-                 OUT_F16)
+        fp8_gemm_kmajor(ws.gy_q, E5M2, False, saved.w_q if wk else saved.w_qT, E4M3FN, wk,
+                        ws.gy_sc.inv_ptr(), saved.w_sc.inv_ptr(), gx, OUT_F16)
         gw = torch.empty((N, K), dtype=torch.float16, device=gy.device)
+        a, b = (ws.gy_q if gk else ws.gy_qT), (saved.x_q if xk else saved.x_qT)
         scaler = mod.grad_scaler
         if scaler is not None:
-            fp8_gemm_unscale(ws.gy_qT, E5M2, saved.x_qT, E4M3FN, ws.gy_sc.inv_ptr(),
-                             saved.x_sc.inv_ptr(), scaler._scale, scaler._found, gw)
+            fp8_gemm_kmajor_unscale(a, E5M2, gk, b, E4M3FN, xk, ws.gy_sc.inv_ptr(),
+                                    saved.x_sc.inv_ptr(), scaler._scale, scaler._found, gw)
             scaler._mark_unscaled(mod.weight)
         else:
-            fp8_gemm(ws.gy_qT, E5M2, saved.x_qT, E4M3FN, ws.gy_sc.inv_ptr(), saved.x_sc.inv_ptr(),
-                     gw, OUT_F16)
+            fp8_gemm_kmajor(a, E5M2, gk, b, E4M3FN, xk, ws.gy_sc.inv_ptr(), saved.x_sc.inv_ptr(),
+                            gw, OUT_F16)
         return gx, gw, None
 
 
@@ -258,13 +275,14 @@ class Float8Linear(nn.Module):
         self._seeded_fwd = self._seeded_bwd = False
         self._ws = None
 
-    def _bwd_scratch(self, M, N, device, rowwise):
+    def _bwd_scratch(self, M, N, device, rowwise, transposed=True):
         """The quantized gradient of the backward pass, kept across steps (its
         contents are written and consumed inside one backward call on the
         current stream, so calls on one stream can share it)."""
-        key = (M, N, str(device), rowwise)
+        key = (M, N, str(device), rowwise, transposed)
         if self._ws is None or self._ws[0] != key:
-            ws = LinearBwdWsRW(M, N, device=device) if rowwise else LinearBwdWs(M, N, device=device)
+            ws = LinearBwdWsRW(M, N, device=device) if rowwise else \
+                LinearBwdWs(M, N, device=device, transposed=transposed)
             self._ws = (key, ws)
         return self._ws[1]
 

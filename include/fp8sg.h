@@ -249,6 +249,22 @@ FP8SG_API fp8sg_status fp8_gemm_kmajor_unscale(const uint8_t* A, fp8sg_format fa
  * down-projection, N = 4096, K = 14336).  Keeping the copy of the A-slot
  * operand only is the fastest form where the layer is large.
  */
+/*
+ * Which transposed copies make the backward of a linear layer with these
+ * sizes fastest on the current device [FP8-TRAIN §4: dgrad and wgrad
+ * contract x, W and gy over their other dimension]; the results are the same
+ * bits with any choice (see fp8_linear_saved below).
+ *   M tokens, N outputs, K inputs: > 0, multiples of 16 (FP8SG_ERR_SHAPE).
+ *   *x_T, *w_T, *gy_T: 1 = make that copy, 0 = read the row-major codes
+ *   contraction-major.  W never needs one (dgrad reads it in the GEMM's
+ *   second slot); of x and gy, the weight gradient's first-slot operand keeps
+ *   its copy when that GEMM takes the 256 x 256 (or 224-row) kernel; small
+ *   layers keep none.  Host-only: queries the device's CU count, launches
+ *   nothing.
+ */
+FP8SG_API fp8sg_status fp8_linear_copies(int64_t M, int64_t N, int64_t K, int32_t* x_T,
+                                         int32_t* w_T, int32_t* gy_T);
+
 typedef struct fp8_linear_saved {
   uint8_t* x_q;         /* [M,K] e4m3 codes of x                */
   uint8_t* x_qT;        /* [K,M] transposed copy, or NULL       */

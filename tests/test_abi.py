@@ -435,3 +435,18 @@ def test_buffer_checks_are_cached_per_buffer_set():
     ws.gy_qT = torch.zeros(N, M, dtype=torch.int8)
     with pytest.raises(TypeError, match="ws.gy_qT"):
         ws.check(M, N)
+
+
+def test_linear_copies_query():
+    """fp8_linear_copies validates like a linear layer's entry points and
+    never asks for W's copy (host-only: no launch)."""
+    L = F.lib()
+    v = [ctypes.c_int32(7) for _ in range(3)]
+    q = lambda M, N, K, ptrs=None: L.fp8_linear_copies(M, N, K, *(ptrs or [ctypes.addressof(a) for a in v]))
+    assert q(64, 256, 24) == ESHAPE and q(0, 256, 128) == ESHAPE and q(-16, 16, 16) == ESHAPE
+    assert q(64, 256, 128, [0, ctypes.addressof(v[1]), ctypes.addressof(v[2])]) == ENULL
+    for shape in ((64, 256, 128), (8192, 14336, 4096), (8192, 4096, 14336), (4096, 4096, 4096)):
+        assert q(*shape) == 0
+        assert v[1].value == 0 and v[0].value in (0, 1) and v[2].value in (0, 1)
+        assert not (v[0].value and v[2].value)
+        assert F.fp8_linear_copies(*shape) == tuple(bool(a.value) for a in v)

@@ -161,3 +161,22 @@ def test_linear_without_transposed_copies(shape, delayed, layout):
         assert torch.equal(ta, tb), (k, shape, delayed)
     for h1, h2 in zip(a["hists"], b["hists"]):
         assert torch.equal(h1, h2)
+
+
+def test_linear_copies_on_the_device():
+    """The fastest layout on MI355X's 256 CUs: the weight gradient's first-slot
+    operand keeps its copy (gy for the MLP block's gate/up, x = h for down,
+    whose weight gradient swaps the roles); small layers keep none; the layer
+    run in that layout equals the one with every copy."""
+    assert torch.cuda.get_device_properties(0).multi_processor_count == 256
+    assert F.fp8_linear_copies(8192, 14336, 4096) == (False, False, True)
+    assert F.fp8_linear_copies(8192, 4096, 14336) == (True, False, False)
+    assert F.fp8_linear_copies(64, 256, 128) == (False, False, False)
+    for M, N, K in ((2048, 4096, 14336), (1024, 1536, 768)):
+        a = run_layer(M, N, K, True, False, M + N)
+        b = run_layer(M, N, K, F.fp8_linear_copies(M, N, K), False, M + N)
+        for k in ("y", "gx", "gw", "gx2", "gw2", "found"):
+            ta, tb = a[k], b[k]
+            if ta.dtype in (torch.bfloat16, torch.float16):
+                ta, tb = ta.view(torch.int16), tb.view(torch.int16)
+            assert torch.equal(ta, tb), (k, M, N, K)
