@@ -629,8 +629,12 @@ def small_layer(torch, F, dev, stream, T, reps=200):
     from workloads.configs import SMALL as S
     import numpy as np
     x, w, gy = (bf16_dev(torch, np, a, dev) for a in (S.x(), S.w(), S.gy()))
-    saved = F.LinearSaved(S.M, S.N, S.K, device=dev)
-    ws = F.LinearBwdWs(S.M, S.N, device=dev)
+    # the copies fp8_linear_copies picks: none for a layer this small, so each
+    # pass runs in one launch (casts fused into the GEMM blocks)
+    xt, wt, gt = F.fp8_linear_copies(S.M, S.N, S.K)
+    saved = F.LinearSaved(S.M, S.N, S.K, device=dev, x_transposed=xt, w_transposed=wt)
+    ws = F.LinearBwdWs(S.M, S.N, device=dev, transposed=gt)
+    one_launch = not (xt or wt or gt)
     y = torch.empty((S.M, S.N), dtype=torch.bfloat16, device=dev)
     gx = torch.empty((S.M, S.K), dtype=torch.float16, device=dev)
     gw = torch.empty((S.N, S.K), dtype=torch.float16, device=dev)
@@ -670,9 +674,14 @@ def small_layer(torch, F, dev, stream, T, reps=200):
            "scaler_step_us": round(T.run(scaler, reps), 2),
            "step_us": round(T.run(step, reps), 2),
            "step_fused_unscale_us": round(T.run(step_fused, reps), 2),
-           # tensors of at most 64 Ki elements are cast by one block each with
-           # their own amax, and the two backward GEMMs share a launch
-           "launches": {"fwd": 2, "bwd": 2, "scaler_step": 2, "step_fused_unscale": 5}}
+           # without transposed copies each pass is one launch (every GEMM
+           # block reduces and casts what it needs); with them, tensors of at
+           # most 64 Ki elements are cast by one block each and the two
+           # backward GEMMs share a launch
+           "transposed_copies": [k for k, v in (("x", xt), ("w", wt), ("gy", gt)) if v],
+           "launches": ({"fwd": 1, "bwd": 1, "scaler_step": 2, "step_fused_unscale": 3}
+                        if one_launch else
+                        {"fwd": 2, "bwd": 2, "scaler_step": 2, "step_fused_unscale": 5})}
     out["step_graph_replay_us"] = replay_us(step)
     out["step_fused_unscale_graph_replay_us"] = replay_us(step_fused)
     out["TFLOPs_eager"] = round(3 * 2.0 * S.M * S.N * S.K / (out["step_us"] * 1e-6) / 1e12, 4)

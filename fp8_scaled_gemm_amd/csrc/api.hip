@@ -289,6 +289,12 @@ fp8sg_status linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t
   }
   hipStream_t s = S(stream);
   hipError_t e;
+  if (!delayed && !saved->x_qT && !saved->w_qT && small_layer_fits(M, N, K)) {
+    // small layer without transposed copies: casts and GEMM in one launch
+    SmallFwdArgs a{x, w, GemmProblem{saved->x_q, saved->w_q, y, nullptr, nullptr, M, N, K},
+                   saved->x_sc, saved->w_sc, saved->x_q, saved->w_q};
+    return hip_status(launch_small_fwd(a, out, s));
+  }
   QuantArgs qa{};
   qa.job[0] = QuantJob{x, M, K, saved->x_sc, saved->x_q, saved->x_qT, 0, 0, 0, hist_x, hist_len};
   qa.job[1] = QuantJob{w, N, K, saved->w_sc, saved->w_q, saved->w_qT, 0, 0, 0, hist_w, hist_len};
@@ -334,6 +340,22 @@ fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64
   }
   hipStream_t s = S(stream);
   hipError_t e;
+  // An operand without its transposed copy is read from its row-major codes,
+  // contraction-major: dgrad's W codes [N, K] as B^T, wgrad's gy codes
+  // [M, N] as A^T and x codes [M, K] as B^T.
+  const bool tb_d = !saved->w_qT, ta_w = !ws->gy_qT, tb_w = !saved->x_qT;
+  const int o = amp_scale ? kOutF16Unscale : (int)out;
+  if (!hist_gy && tb_d && ta_w && tb_w && small_layer_fits(M, N, K)) {
+    // small layer without transposed copies: the cast of gy and both GEMMs
+    // in one launch
+    SmallBwdArgs a{gy, M, N,
+                   GemmProblem{ws->gy_q, saved->w_q, gx, nullptr, &saved->w_sc->inv, M, K, N,
+                               amp_scale, found_inf},
+                   GemmProblem{ws->gy_q, saved->x_q, gw, nullptr, &saved->x_sc->inv, N, K, M,
+                               amp_scale, found_inf},
+                   ws->gy_sc, ws->gy_q};
+    return hip_status(launch_small_bwd(a, o, s));
+  }
   QuantArgs qa{};
   qa.job[0] = QuantJob{gy, M, N, ws->gy_sc, ws->gy_q, ws->gy_qT, 0, 0, 0, hist_gy, hist_len};
   qa.njobs = 1;
@@ -351,15 +373,10 @@ fp8sg_status linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved, int64
   }
   if (e != hipSuccess) return FP8SG_ERR_HIP;
 
-  // An operand without its transposed copy is read from its row-major codes,
-  // contraction-major: dgrad's W codes [N, K] as B^T, wgrad's gy codes
-  // [M, N] as A^T and x codes [M, K] as B^T.
-  const bool tb_d = !saved->w_qT, ta_w = !ws->gy_qT, tb_w = !saved->x_qT;
   GemmProblem dg{ws->gy_q, tb_d ? saved->w_q : saved->w_qT, gx, &ws->gy_sc->inv, &saved->w_sc->inv,
                  M, K, N, amp_scale, found_inf};
   GemmProblem wg{ta_w ? ws->gy_q : ws->gy_qT, tb_w ? saved->x_q : saved->x_qT, gw, &ws->gy_sc->inv,
                  &saved->x_sc->inv, N, K, M, amp_scale, found_inf};
-  const int o = amp_scale ? kOutF16Unscale : (int)out;
   if (tb_d && ta_w && tb_w) return hip_status(launch_gemm_km_pair(dg, wg, o, s));
   if (tb_d || ta_w || tb_w) {  // some copies kept: one launch per GEMM
     e = launch_gemm_km(dg, FP8SG_E5M2, FP8SG_E4M3FN, o, false, tb_d, s);

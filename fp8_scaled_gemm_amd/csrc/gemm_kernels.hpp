@@ -137,6 +137,11 @@ struct Alpha {
       a = (float)(*p.inv_a * *p.inv_b);
     }
   }
+  // per-tensor scaling with the two inverses given as values
+  __device__ Alpha(double inv_a, double inv_b) {
+    static_assert(!RW, "one factor");
+    a = (float)(inv_a * inv_b);
+  }
   // c holds C[m][n .. n+3] of block (i, j)
   __device__ void apply(v4f& c, int i, int j) const {
     if constexpr (RW) {
@@ -151,6 +156,18 @@ struct Alpha {
   }
 };
 
+// A bf16 operand cast to FP8 on its way into LDS (the small layers' one-launch
+// passes, small_layer.hip): each 16-element chunk is quantized by quant8 at
+// the tensor's scale32, the codes the cast kernels write; a block given `q`
+// also stores its chunks' codes there, at the elements' own positions (the
+// operand's stored layout).  x replaces the GEMM problem's code pointer.
+struct CastSrc {
+  const uint16_t* x;
+  float s32;
+  double inv;  // the tensor's inverse scale: the epilogue factor takes it
+  uint8_t* q;
+};
+
 // Small-problem kernel: a BM x BN block tile per workgroup, K consumed 128
 // bytes at a time.  Each k-tile of A and B is fetched with 16-byte global loads
 // into registers while the previous tile is being multiplied, then written to
@@ -161,9 +178,11 @@ struct Alpha {
 // its k-tile is staged as 128 rows of 128 bytes (one per k, the tile's 128
 // output rows or columns) and its fragments are read with ds_read_b64_tr_b8,
 // as in the large-tile kernel below.
+// CA / CB: the operand is a bf16 tensor cast on the fly (CastSrc ca / cb).
 template <int BM, int BN, int WM, int WN, int FA, int FB, int OUT, bool RW, bool TA = false,
-          bool TB = false>
-__device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, int by) {
+          bool TB = false, bool CA = false, bool CB = false>
+__device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, int by,
+                                                CastSrc ca = CastSrc{}, CastSrc cb = CastSrc{}) {
   static_assert(!(TA || TB) || (BM == 128 && BN == 128), "contraction-major: 128 x 128 tiles");
   using Cfg = GemmCfg<BM, BN, WM, WN>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -179,54 +198,104 @@ __device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, in
   const int64_t M = p.M, N = p.N, K = p.K;
   const int nk = (int)((K + kBK - 1) / kBK);
 
-  // global -> register prefetch of one k-tile
-  uint4 ra[Cfg::kLoadsA], rb[Cfg::kLoadsB];
+  // global -> register prefetch of one k-tile (a cast operand's chunk is 16
+  // bf16 values, two 16-byte loads)
+  uint4 ra[Cfg::kLoadsA * (CA ? 2 : 1)], rb[Cfg::kLoadsB * (CB ? 2 : 1)];
   // chunk c of a k-tile: LDS row c / 8, 16-byte chunk c % 8; a row-major
   // operand's row is an output row (column) and the chunk 16 k values, a
-  // contraction-major one's row is a k and the chunk 16 output rows (columns)
+  // contraction-major one's row is a k and the chunk 16 output rows (columns).
+  // The chunk's first element and whether it lies inside the operand:
+  auto chunk_a = [&](int64_t k0, int c, int64_t& idx) {
+    const int r = c >> 3, kc = c & 7;
+    if constexpr (TA) {
+      const int64_t gk = k0 + r, gm = bm + 16 * kc;
+      idx = gk * M + gm;
+      return gk < K && gm < M;
+    } else {
+      const int64_t gr = bm + r, gk = k0 + 16 * kc;
+      idx = gr * K + gk;
+      return gr < M && gk < K;
+    }
+  };
+  auto chunk_b = [&](int64_t k0, int c, int64_t& idx) {
+    const int r = c >> 3, kc = c & 7;
+    if constexpr (TB) {
+      const int64_t gk = k0 + r, gn = bn + 16 * kc;
+      idx = gk * N + gn;
+      return gk < K && gn < N;
+    } else {
+      const int64_t gr = bn + r, gk = k0 + 16 * kc;
+      idx = gr * K + gk;
+      return gr < N && gk < K;
+    }
+  };
+  // (a value, not a named zero: a conditional between two lvalues would select
+  // an address and put the zero in scratch memory)
+  auto zero = []() { return make_uint4(0, 0, 0, 0); };
   auto load_tile = [&](int kt) {
     const int64_t k0 = (int64_t)kt * kBK;
 #pragma unroll
     for (int i = 0; i < Cfg::kLoadsA; ++i) {
-      const int c = tid + i * Cfg::kThreads;
-      const int r = c >> 3, kc = c & 7;
-      if constexpr (TA) {
-        const int64_t gk = k0 + r, gm = bm + 16 * kc;
-        ra[i] = (gk < K && gm < M) ? *reinterpret_cast<const uint4*>(p.A + gk * M + gm)
-                                   : make_uint4(0, 0, 0, 0);
+      int64_t idx;
+      const bool ok = chunk_a(k0, tid + i * Cfg::kThreads, idx);
+      if constexpr (CA) {
+        ra[2 * i] = ok ? *reinterpret_cast<const uint4*>(ca.x + idx) : zero();
+        ra[2 * i + 1] = ok ? *reinterpret_cast<const uint4*>(ca.x + idx + 8) : zero();
       } else {
-        const int64_t gr = bm + r, gk = k0 + 16 * kc;
-        ra[i] = (gr < M && gk < K) ? *reinterpret_cast<const uint4*>(p.A + gr * K + gk)
-                                   : make_uint4(0, 0, 0, 0);
+        ra[i] = ok ? *reinterpret_cast<const uint4*>(p.A + idx) : zero();
       }
     }
 #pragma unroll
     for (int i = 0; i < Cfg::kLoadsB; ++i) {
-      const int c = tid + i * Cfg::kThreads;
-      const int r = c >> 3, kc = c & 7;
-      if constexpr (TB) {
-        const int64_t gk = k0 + r, gn = bn + 16 * kc;
-        rb[i] = (gk < K && gn < N) ? *reinterpret_cast<const uint4*>(p.B + gk * N + gn)
-                                   : make_uint4(0, 0, 0, 0);
+      int64_t idx;
+      const bool ok = chunk_b(k0, tid + i * Cfg::kThreads, idx);
+      if constexpr (CB) {
+        rb[2 * i] = ok ? *reinterpret_cast<const uint4*>(cb.x + idx) : zero();
+        rb[2 * i + 1] = ok ? *reinterpret_cast<const uint4*>(cb.x + idx + 8) : zero();
       } else {
-        const int64_t gr = bn + r, gk = k0 + 16 * kc;
-        rb[i] = (gr < N && gk < K) ? *reinterpret_cast<const uint4*>(p.B + gr * K + gk)
-                                   : make_uint4(0, 0, 0, 0);
+        rb[i] = ok ? *reinterpret_cast<const uint4*>(p.B + idx) : zero();
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  // a cast chunk's 16 codes (zero outside the operand, as the code loads
+  // give); a block with a code buffer also stores them
+  auto cast_chunk = [&](const CastSrc& cs, auto fmt, const uint4& lo, const uint4& hi, bool ok,
+                        int64_t idx) {
+    constexpr int F = decltype(fmt)::value;
+    const uint2 a = quant8<F>(lo, cs.s32), b = quant8<F>(hi, cs.s32);
+    const uint4 q = ok ? make_uint4(a.x, a.y, b.x, b.y) : zero();
+    if (ok && cs.q) *reinterpret_cast<uint4*>(cs.q + idx) = q;
+    return q;
+  };
+  auto store_tile = [&](int buf, int kt) {
     uint8_t* a = As + buf * BM * kBK;
     uint8_t* b = Bs + buf * BN * kBK;
+    const int64_t k0 = (int64_t)kt * kBK;
 #pragma unroll
     for (int i = 0; i < Cfg::kLoadsA; ++i) {
       const int c = tid + i * Cfg::kThreads;
-      *reinterpret_cast<uint4*>(a + (TA ? lds_off_t(c >> 3, c & 7) : lds_off(c >> 3, c & 7))) = ra[i];
+      uint4 v;
+      if constexpr (CA) {
+        int64_t idx;
+        const bool ok = chunk_a(k0, c, idx);
+        v = cast_chunk(ca, std::integral_constant<int, FA>{}, ra[2 * i], ra[2 * i + 1], ok, idx);
+      } else {
+        v = ra[i];
+      }
+      *reinterpret_cast<uint4*>(a + (TA ? lds_off_t(c >> 3, c & 7) : lds_off(c >> 3, c & 7))) = v;
     }
 #pragma unroll
     for (int i = 0; i < Cfg::kLoadsB; ++i) {
       const int c = tid + i * Cfg::kThreads;
-      *reinterpret_cast<uint4*>(b + (TB ? lds_off_t(c >> 3, c & 7) : lds_off(c >> 3, c & 7))) = rb[i];
+      uint4 v;
+      if constexpr (CB) {
+        int64_t idx;
+        const bool ok = chunk_b(k0, c, idx);
+        v = cast_chunk(cb, std::integral_constant<int, FB>{}, rb[2 * i], rb[2 * i + 1], ok, idx);
+      } else {
+        v = rb[i];
+      }
+      *reinterpret_cast<uint4*>(b + (TB ? lds_off_t(c >> 3, c & 7) : lds_off(c >> 3, c & 7))) = v;
     }
   };
 
@@ -260,7 +329,7 @@ __device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, in
 
   if (nk > 0) {
     load_tile(0);
-    store_tile(0);
+    store_tile(0, 0);
   }
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
@@ -296,12 +365,19 @@ __device__ __forceinline__ void gemm_small_tile(const GemmProblem& p, int bx, in
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], FB, FA,
                                                                      0, 0, 0, 0);
     }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
+    if (kt + 1 < nk) store_tile(buf ^ 1, kt + 1);
     __syncthreads();
   }
 
-  // epilogue: lane holds C[m][n..n+3] of each 16x16 block
-  const Alpha<RW, Cfg::kTM, Cfg::kTN> alpha(p, bm + wm * (BM / WM), bn + wn * (BN / WN), lane);
+  // epilogue: lane holds C[m][n..n+3] of each 16x16 block; a cast operand
+  // brings its inverse scale as a value
+  auto make_alpha = [&]() {
+    if constexpr (CA || CB)
+      return Alpha<RW, Cfg::kTM, Cfg::kTN>(CA ? ca.inv : *p.inv_a, CB ? cb.inv : *p.inv_b);
+    else
+      return Alpha<RW, Cfg::kTM, Cfg::kTN>(p, bm + wm * (BM / WM), bn + wn * (BN / WN), lane);
+  };
+  const Alpha<RW, Cfg::kTM, Cfg::kTN> alpha = make_alpha();
   Unscale us;
   if constexpr (OUT == kOutF16Unscale) us.load(p);
 #pragma unroll

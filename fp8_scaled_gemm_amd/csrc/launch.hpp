@@ -90,6 +90,33 @@ hipError_t launch_gemm_km_pair(const GemmProblem& dgrad, const GemmProblem& wgra
 // Which transposed copies make the backward of an M x N x K linear layer
 // fastest on the current device (fp8_linear_copies).
 void linear_copies(int64_t M, int64_t N, int64_t K, bool& x_t, bool& w_t, bool& gy_t);
+
+// Small layers in one launch per pass (small_layer.hip), for layers whose x,
+// W and gy each hold at most kSelfCastMaxElems elements and that keep no
+// transposed copies.  Forward: p is the forward GEMM (A = x_q, B = w_q, C = y;
+// its inverse pointers are not read), x and w the bf16 inputs.  Backward: dg
+// and wg are the dgrad and wgrad problems on contraction-major codes (their
+// inv_b point to the saved records' inverses), gy the bf16 gradient
+// [rows, cols].
+struct SmallFwdArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  GemmProblem p;
+  fp8sg_scale_rec* x_sc;
+  fp8sg_scale_rec* w_sc;
+  uint8_t* x_q;
+  uint8_t* w_q;
+};
+struct SmallBwdArgs {
+  const uint16_t* gy;
+  int64_t rows, cols;
+  GemmProblem dg, wg;
+  fp8sg_scale_rec* gy_sc;
+  uint8_t* gy_q;
+};
+bool small_layer_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_small_fwd(const SmallFwdArgs& a, int out, hipStream_t stream);
+hipError_t launch_small_bwd(const SmallBwdArgs& a, int out, hipStream_t stream);
 // Row-wise scaling (gemm_rowwise.hip): inv_a points to M doubles, inv_b to N;
 // element (m, n) is scaled by fl32(inv_a[m] * inv_b[n]).
 hipError_t launch_gemm_rowwise(const GemmProblem& p, int fa, int fb, int out, hipStream_t stream);
