@@ -283,10 +283,13 @@ typedef struct fp8_linear_bwd_ws {
 
 /*
  * Forward of the FP8 linear layer y = x @ W^T [FP8-TRAIN §4 forward, §6]:
- * amax of x and W, fp64 scales, e4m3 quantize-cast with transposed copies,
- * then the scaled GEMM.
+ * amax of x and W, fp64 scales, e4m3 quantize-cast (with the transposed
+ * copies `saved` asks for), then the scaled GEMM.
  *   x: [M,K] bf16, w: [N,K] bf16 (nn.Linear's [out,in]); y: [M,N] of type
  *   `out` (FP8SG_OUT_BF16 normally).  M, N, K > 0, multiples of 16.
+ * A layer with M*K, N*K and M*N all at most 65536 and no transposed copies
+ * runs in one launch (the GEMM blocks reduce and cast what they need); the
+ * codes, records and y are the same bits as the separate launches give.
  */
 FP8SG_API fp8sg_status fp8_scaled_linear_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
                                    int64_t K, const fp8_linear_saved* saved, void* y,
@@ -294,12 +297,15 @@ FP8SG_API fp8sg_status fp8_scaled_linear_fwd(const uint16_t* x, const uint16_t* 
 
 /*
  * Backward of the FP8 linear layer [FP8-TRAIN §4 backward]: gy quantized to
- * e5m2 (with its transposed copy), then
+ * e5m2 (with its transposed copy when ws has one), then
  *   dgrad gx[M,K] = gy @ W     from gy_q [M,N] and the saved w_qT [K,N],
  *   wgrad gW[N,K] = gy^T @ x   from gy_qT [N,M] and the saved x_qT [K,M],
- * each dequantised by the product of its two inverse scales.
+ * each dequantised by the product of its two inverse scales (a missing
+ * transposed copy is read from the row-major codes, same bits).
  *   gy: [M,N] bf16; gx, gw of type `out` (FP8SG_OUT_F16 feeds fp16 AMP).
  *   `saved` must come from fp8_scaled_linear_fwd with the same M, N, K.
+ * Small layers without transposed copies (as for the forward) run the cast
+ * of gy and both GEMMs in one launch.
  */
 FP8SG_API fp8sg_status fp8_scaled_linear_bwd(const uint16_t* gy, const fp8_linear_saved* saved,
                                    int64_t M, int64_t N, int64_t K, const fp8_linear_bwd_ws* ws,
