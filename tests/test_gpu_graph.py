@@ -19,16 +19,20 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("fused", [False, True])
-def test_step_graph_replay_matches_eager(fused):
-    M, N, K = 512, 768, 384
+@pytest.mark.parametrize("shape,copies", [((512, 768, 384), True), ((512, 768, 384), False),
+                                          ((64, 256, 128), False)])
+def test_step_graph_replay_matches_eager(fused, shape, copies):
+    """With transposed copies; without them (the backward GEMMs read the codes
+    contraction-major); and the small layer's one-launch passes."""
+    M, N, K = shape
     x = torch.from_numpy(W.normal_bf16(41, 0, (M, K), 1.0).view(np.int16)).view(
         torch.bfloat16).to(DEV)
     w = torch.from_numpy(W.normal_bf16(41, 1, (N, K), 0.02).view(np.int16)).view(
         torch.bfloat16).to(DEV)
     gy = torch.from_numpy(W.normal_bf16(41, 2, (M, N), 1e-4 * 65536.0).view(
         np.int16)).view(torch.bfloat16).to(DEV)
-    saved = F.LinearSaved(M, N, K, device=DEV)
-    ws = F.LinearBwdWs(M, N, device=DEV)
+    saved = F.LinearSaved(M, N, K, device=DEV, transposed=copies)
+    ws = F.LinearBwdWs(M, N, device=DEV, transposed=copies)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     gx = torch.empty((M, K), dtype=torch.float16, device=DEV)
     gw = torch.empty((N, K), dtype=torch.float16, device=DEV)
@@ -47,8 +51,8 @@ def test_step_graph_replay_matches_eager(fused):
         # output) stays that of the eager reference step
         F.amp_update_scale(scale, tracker, found, 1.0, 0.5, 3)
 
-    outs = (y, gx, gw, saved.x_q, saved.x_qT, saved.w_q, saved.w_qT, saved.recs, ws.gy_q,
-            ws.gy_qT, ws.gy_sc.buf)
+    outs = [t for t in (y, gx, gw, saved.x_q, saved.x_qT, saved.w_q, saved.w_qT, saved.recs, ws.gy_q,
+                        ws.gy_qT, ws.gy_sc.buf) if t is not None]
     step()
     torch.cuda.synchronize()
     ref = [o.clone() for o in outs]
@@ -64,7 +68,7 @@ def test_step_graph_replay_matches_eager(fused):
         step()  # captured, not run
     expect_scale, expect_tracker = 65536.0, 2
     for r in range(4):
-        for t in (y, gx, gw, saved.x_q, ws.gy_qT):
+        for t in (y, gx, gw, saved.x_q, ws.gy_q):
             t.zero_()
         g.replay()
         torch.cuda.synchronize()
