@@ -7,6 +7,7 @@ import pytest
 import torch
 from torch import nn
 
+import fp8_scaled_gemm_amd as F
 import fp8_scaled_gemm_amd.nn as FN
 import oracle as O
 import workloads as W
@@ -33,8 +34,12 @@ def check_out(got, c_ref, A, fa, B, ia, ib, K, what):
                       O.BF16, what)
 
 
-def test_float8_linear_autograd_matches_oracle():
-    B, T, K, N = 2, 64, 128, 256
+@pytest.mark.parametrize("B,T,K,N", [(2, 64, 128, 256), (2, 1024, 2048, 4096)])
+def test_float8_linear_autograd_matches_oracle(B, T, K, N):
+    """The small layer (each pass one launch, no transposed copies) and a layer
+    whose weight gradient takes the large-tile kernel (only gy's transposed
+    copy kept, x and W read contraction-major), every output against the
+    oracle through autograd."""
     x_h = W.normal_bf16(61, 0, (B * T, K), 1.0)
     w_h = W.normal_bf16(61, 1, (N, K), 0.02)
     gy_h = W.normal_bf16(61, 2, (B * T, N), 1e-3)
@@ -53,6 +58,8 @@ def test_float8_linear_autograd_matches_oracle():
     assert node is not None, "no FP8 linear node in the graph"
     saved = node.saved_tensors
     assert len(saved) == 5 and all(t.dtype == torch.uint8 for t in saved)
+    xt, wt, _ = F.fp8_linear_copies(B * T, N, K)
+    assert (saved[1].numel() > 0, saved[3].numel() > 0) == (xt, wt)
     y.backward(dev_bf16(gy_h).reshape(B, T, N))
     torch.cuda.synchronize()
     fw = O.linear_fwd(x_h, w_h)
