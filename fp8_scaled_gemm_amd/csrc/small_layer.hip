@@ -1,7 +1,7 @@
 // Small linear layers in one launch per pass [FP8-TRAIN §2 (amax, fp64 scale,
-// cast), §4 (the forward, dgrad and wgrad products); the benchmark spec's small
-// layer, B = 64, K = 128, N = 256, where every kernel is mostly launch and
-// dependency latency].
+// cast), §4 (the forward, dgrad and wgrad products)].  At sizes such as
+// B = 64, K = 128, N = 256 every kernel is mostly launch and dependency
+// latency, so the number of launches sets the time.
 //
 // Forward: every block of the forward GEMM reduces |x| and |W| over the whole
 // tensors itself (at most 64 Ki elements each, read from L2), derives both
