@@ -168,7 +168,7 @@ class MlpStep:
     # for down, whose weight gradient runs with the operands' roles swapped)
     ALL = {"x", "h", "w_gate", "w_up", "w_down", "gy_gate", "gy_up", "gy_down"}
 
-    def __init__(self, np, torch, F, dev, layout="auto"):
+    def __init__(self, np, torch, F, dev, layout="auto", inputs=None):
         from workloads.configs import mlp_linear, MLP_T, MLP_H, MLP_F
         self.F, self.torch, self.layout = F, torch, layout
         self.lin = {n: mlp_linear(n) for n in self.NAMES}
@@ -182,15 +182,18 @@ class MlpStep:
         else:
             self.tr = set() if layout == "none" else set(self.ALL)
         self.T, self.H, self.Fd = MLP_T, MLP_H, MLP_F
-        log("generating the MLP block's inputs")
-        self.host = {}
-        g = self.lin["gate"]
-        self.host["x"] = g.x()
-        self.host["h"] = self.lin["down"].x()
-        for n in self.NAMES:
-            self.host["w_" + n] = self.lin[n].w()
-            self.host["gy_" + n] = loss_scaled(np, self.lin[n].gy())
-        self.dev = {k: bf16_dev(torch, np, v, dev) for k, v in self.host.items()}
+        if inputs is not None:  # (host arrays, device tensors) of another MlpStep
+            self.host, self.dev = inputs
+        else:
+            log("generating the MLP block's inputs")
+            self.host = {}
+            g = self.lin["gate"]
+            self.host["x"] = g.x()
+            self.host["h"] = self.lin["down"].x()
+            for n in self.NAMES:
+                self.host["w_" + n] = self.lin[n].w()
+                self.host["gy_" + n] = loss_scaled(np, self.lin[n].gy())
+            self.dev = {k: bf16_dev(torch, np, v, dev) for k, v in self.host.items()}
         bf = dict(dtype=torch.bfloat16, device=dev)
         f16 = dict(dtype=torch.float16, device=dev)
         self.saved, self.ws, self.y, self.gx, self.gw = {}, {}, {}, {}, {}
@@ -369,7 +372,13 @@ def main():
         log("MLP block through the PyTorch layer")
         side["mlp_block_autograd"] = mlp_autograd(torch, F, dev, stream)
     mlp_tr = sorted(mlp.tr)
+    layout_used, inputs = mlp.layout, (mlp.host, mlp.dev)
     del mlp
+    torch.cuda.empty_cache()
+    if not args.no_side:
+        side["mlp_copy_layouts"] = copy_layouts(np, torch, F, dev, stream, T, args, layout_used,
+                                                inputs)
+    del inputs
     torch.cuda.empty_cache()
 
     hbm, hbm_kern = ({}, {}) if args.no_hbm else hbm_passes(np, torch, F, dev, T)
@@ -685,6 +694,25 @@ def small_layer(torch, F, dev, stream, T, reps=200):
     out["step_graph_replay_us"] = replay_us(step)
     out["step_fused_unscale_graph_replay_us"] = replay_us(step_fused)
     out["TFLOPs_eager"] = round(3 * 2.0 * S.M * S.N * S.K / (out["step_us"] * 1e-6) / 1e12, 4)
+    return out
+
+
+def copy_layouts(np, torch, F, dev, stream, T, args, used, inputs):
+    """The MLP step with the other transposed-copy layouts, on the same inputs,
+    for comparison with the headline's: step time and the nine GEMMs' fraction
+    of FP8 peak."""
+    out = {"headline_layout": used}
+    for layout in ("auto", "none", "all"):
+        if layout == used:
+            continue
+        log(f"MLP step with the '{layout}' copy layout")
+        m = MlpStep(np, torch, F, dev, layout=layout, inputs=inputs)
+        ms, _, _ = timed_steps(torch, stream, m.step, args.steps, args.warmup)
+        g = [(fl, T.run(call, args.reps)) for _, fl, call in m.gemms()]
+        frac = sum(fl for fl, _ in g) / (sum(us for _, us in g) * 1e-6) / 1e12 / PEAK_FP8_TFLOPS
+        out[layout] = {"copies": sorted(m.tr), "ms_per_step": round(ms, 4), "gemm_frac": round(frac, 4)}
+        del m
+        torch.cuda.empty_cache()
     return out
 
 

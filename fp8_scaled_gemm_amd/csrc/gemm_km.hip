@@ -19,8 +19,12 @@ void linear_copies(int64_t M, int64_t N, int64_t K, bool& x_t, bool& w_t, bool& 
   // dgrad (M x K over N) reads W in the B slot: a contraction-major read
   // costs nothing there.  wgrad (N x K over M): the operand in the A slot
   // keeps its copy -- x where the launcher swaps the roles, else gy -- when
-  // it takes the large-tile kernel; small layers keep none (both backward
-  // GEMMs then share one launch of the 128 x 128 kernel).
+  // it takes the large-tile kernel (read contraction-major there it makes
+  // that GEMM about 5% slower); small layers keep none (both backward GEMMs
+  // then share one launch of the 128 x 128 kernel, or each pass is one
+  // launch).  The choice is the GEMMs' alone: the copy costs its cast one
+  // more byte per element, which at the MLP block's shapes about cancels
+  // what the GEMM saves.
   w_t = false;
   x_t = gy_t = false;
   if (!big_tiles_wanted(N, K)) return;

@@ -250,10 +250,11 @@ FP8SG_API fp8sg_status fp8_gemm_kmajor_unscale(const uint8_t* A, fp8sg_format fa
  * operand only is the fastest form where the layer is large.
  */
 /*
- * Which transposed copies make the backward of a linear layer with these
- * sizes fastest on the current device [FP8-TRAIN §4: dgrad and wgrad
+ * Which transposed copies make the backward GEMMs of a linear layer with
+ * these sizes fastest on the current device [FP8-TRAIN §4: dgrad and wgrad
  * contract x, W and gy over their other dimension]; the results are the same
- * bits with any choice (see fp8_linear_saved below).
+ * bits with any choice (see fp8_linear_saved below).  A copy costs its cast
+ * one more byte written per element, which this choice does not weigh.
  *   M tokens, N outputs, K inputs: > 0, multiples of 16 (FP8SG_ERR_SHAPE).
  *   *x_T, *w_T, *gy_T: 1 = make that copy, 0 = read the row-major codes
  *   contraction-major.  W never needs one (dgrad reads it in the GEMM's
