@@ -227,3 +227,39 @@ def test_empty_contraction_at_large_tile_sizes(M, N):
     torch.cuda.synchronize()
     assert torch.count_nonzero(C.view(torch.int16)) == 0
     assert int(found.item()) == 0
+
+
+@pytest.mark.parametrize("name", ["gate", "down"])
+def test_mlp_layer_copy_layouts_agree(name):
+    """An MLP linear at full size (gate: 8192 x 14336 x 4096; down: 8192 x 4096
+    x 14336) run as the benchmark runs it -- bf16 forward, backward of the
+    loss-scaled gradient with the unscale fused -- with every transposed copy,
+    with the copies fp8_linear_copies picks, and with none: the codes,
+    records, outputs and the non-finite flag are the same bits (the layer
+    with every copy is checked against the oracle in the config tests)."""
+    from workloads.configs import mlp_linear
+    L = mlp_linear(name)
+    M, N, K = L.M, L.N, L.K
+    x = dev_bf16(L.x()).reshape(M, K)
+    w = dev_bf16(L.w()).reshape(N, K)
+    gy = dev_bf16(L.gy()).reshape(M, N) * 65536.0
+    runs = []
+    for layout in ((True, True, True), F.fp8_linear_copies(M, N, K), (False, False, False)):
+        xt, wt, gt = layout
+        saved = F.LinearSaved(M, N, K, x_transposed=xt, w_transposed=wt)
+        ws = F.LinearBwdWs(M, N, transposed=gt)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        gx = torch.empty((M, K), dtype=torch.float16, device=DEV)
+        gw = torch.empty((N, K), dtype=torch.float16, device=DEV)
+        scale = torch.tensor([65536.0], dtype=torch.float32, device=DEV)
+        found = torch.zeros(1, dtype=torch.int32, device=DEV)
+        F.fp8_scaled_linear_fwd(x, w, saved, y, F.OUT_BF16)
+        F.fp8_scaled_linear_bwd_unscale(gy, saved, ws, scale, found, gx, gw)
+        torch.cuda.synchronize()
+        runs.append((layout, [y.view(torch.int16), gx.view(torch.int16), gw.view(torch.int16),
+                              saved.x_q, saved.w_q, ws.gy_q, saved.recs[:, :32], ws.gy_sc.buf[:32],
+                              found]))
+    ref = runs[0][1]
+    for layout, got in runs[1:]:
+        for k, (a, b) in enumerate(zip(ref, got)):
+            assert torch.equal(a, b), (name, layout, k)
