@@ -203,3 +203,48 @@ def test_delayed_two_level_over_stale_slots(shape, transposed):
         ref = O.to_fp8_delayed(x, O.E5M2, hist_h, with_transpose=transposed)
         check_step(rec, hist, q, qT, ref, O.E5M2, f"two-level {shape}, step {t}")
         hist_h = ref.hist
+
+
+@pytest.mark.parametrize("copies", [True, False])
+def test_delayed_linear_two_level_casts(copies):
+    """A layer whose x, W and gy each need more cast blocks than a record has
+    partial slots (4224 x 4352 x 4096: 1056, 1088 and 1122 tiles), so x and W
+    share one two-level launch (slot clear, one pass per block, atomic slot
+    maxima) and gy takes another; two steps with delayed scaling: codes,
+    scale fields, histories against the oracle bit for bit, GEMM outputs
+    sampled."""
+    M, N, K, H = 4224, 4352, 4096, 4
+    saved = F.LinearSaved(M, N, K, device=DEV, transposed=copies)
+    ws = F.LinearBwdWs(M, N, device=DEV, transposed=copies)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    gx = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    gw = torch.empty((N, K), dtype=torch.bfloat16, device=DEV)
+    hx, hw, hg = (np.full(H, v, np.float32) for v in (3.0, 0.08, 4e-4))
+    dhx, dhw, dhg = (torch.from_numpy(h.copy()).to(DEV) for h in (hx, hw, hg))
+    rng = np.random.default_rng(7)
+    for t in range(2):
+        x = W.normal_bf16(60 + t, 0, (M, K), 1.0 + t)
+        w = W.normal_bf16(60 + t, 1, (N, K), 0.02)
+        gy = W.normal_bf16(60 + t, 2, (M, N), 1e-4)
+        F.fp8_scaled_linear_fwd_delayed(dev16(x), dev16(w), saved, dhx, dhw, y)
+        F.fp8_scaled_linear_bwd_delayed(dev16(gy), saved, ws, dhg, gx, gw)
+        torch.cuda.synchronize()
+        # the oracle's delayed casts (its composite linear functions would also
+        # run the three full GEMMs on the CPU)
+        xq = O.to_fp8_delayed(x, O.E4M3FN, hx)
+        wq = O.to_fp8_delayed(w, O.E4M3FN, hw)
+        gq = O.to_fp8_delayed(gy, O.E5M2, hg)
+        hx, hw, hg = xq.hist, wq.hist, gq.hist
+        check_step(saved.x_sc, dhx, saved.x_q, saved.x_qT, xq, O.E4M3FN, f"x step {t}")
+        check_step(saved.w_sc, dhw, saved.w_q, saved.w_qT, wq, O.E4M3FN, f"w step {t}")
+        check_step(ws.gy_sc, dhg, ws.gy_q, ws.gy_qT, gq, O.E5M2, f"gy step {t}")
+        for got, A, fa, B, ia, ib, kc, what in (
+                (y, xq.q, O.E4M3FN, wq.q, xq.sc.inv, wq.sc.inv, K, "fwd"),
+                (gx, gq.q, O.E5M2, wq.qT, gq.sc.inv, wq.sc.inv, N, "dgrad"),
+                (gw, gq.qT, O.E5M2, xq.qT, gq.sc.inv, xq.sc.inv, M, "wgrad")):
+            R, C = got.shape
+            ii, jj = rng.integers(0, R, 2048), rng.integers(0, C, 2048)
+            c_ref = O.gemm_at(A, fa, B, O.E4M3FN, ia, ib, ii, jj)
+            ad = O.gemm_absdot_at(A, fa, B, O.E4M3FN, ia, ib, ii, jj)
+            check_gemm_values(O.decode(O.BF16, host_u16(got)[ii, jj]), c_ref, ad, kc, O.BF16,
+                              f"{what} step {t}")
