@@ -508,7 +508,10 @@ def square_layer(np, torch, F, dev, stream, T, args):
     x = bf16_dev(torch, np, S.x(), dev)
     w = bf16_dev(torch, np, S.w(), dev)
     gy = bf16_dev(torch, np, loss_scaled(np, S.gy()), dev)
-    saved, ws = F.LinearSaved(M, N, K, device=dev), F.LinearBwdWs(M, N, device=dev)
+    # the transposed copies fp8_linear_copies picks (gy's alone at this size)
+    xt, wt, gt = F.fp8_linear_copies(M, N, K)
+    saved = F.LinearSaved(M, N, K, device=dev, x_transposed=xt, w_transposed=wt)
+    ws = F.LinearBwdWs(M, N, device=dev, transposed=gt)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     gx = torch.empty((M, K), dtype=torch.float16, device=dev)
     gw = torch.empty((N, K), dtype=torch.float16, device=dev)
@@ -524,25 +527,40 @@ def square_layer(np, torch, F, dev, stream, T, args):
     steps = max(args.steps, 20)
     ms, _, _ = timed_steps(torch, stream, step, steps, args.warmup)
     fl = 2.0 * M * N * K
+    # the three GEMMs as the backward runs them: a missing copy's operand read
+    # contraction-major
+    wk, gk, xk = not wt, not gt, not xt
     g = [T.run(lambda: F.fp8_gemm(saved.x_q, F.E4M3FN, saved.w_q, F.E4M3FN, saved.x_sc.inv_ptr(),
                                   saved.w_sc.inv_ptr(), y, F.OUT_BF16), args.reps),
-         T.run(lambda: F.fp8_gemm_unscale(ws.gy_q, F.E5M2, saved.w_qT, F.E4M3FN,
-                                          ws.gy_sc.inv_ptr(), saved.w_sc.inv_ptr(), scale, found,
-                                          gx), args.reps),
-         T.run(lambda: F.fp8_gemm_unscale(ws.gy_qT, F.E5M2, saved.x_qT, F.E4M3FN,
-                                          ws.gy_sc.inv_ptr(), saved.x_sc.inv_ptr(), scale, found,
-                                          gw), args.reps)]
+         T.run(lambda: F.fp8_gemm_kmajor_unscale(
+             ws.gy_q, F.E5M2, 0, saved.w_q if wk else saved.w_qT, F.E4M3FN, wk,
+             ws.gy_sc.inv_ptr(), saved.w_sc.inv_ptr(), scale, found, gx), args.reps),
+         T.run(lambda: F.fp8_gemm_kmajor_unscale(
+             ws.gy_q if gk else ws.gy_qT, F.E5M2, gk, saved.x_q if xk else saved.x_qT, F.E4M3FN, xk,
+             ws.gy_sc.inv_ptr(), saved.x_sc.inv_ptr(), scale, found, gw), args.reps)]
     rec = F.ScaleRec(device=dev)
     q = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    qT = torch.empty((K, M), dtype=torch.uint8, device=dev)
+    qT = torch.empty((K, M), dtype=torch.uint8, device=dev) if xt else None
     c_us = T.run(lambda: (F.fp8_amax(x, rec), F.fp8_quantize(x, F.E4M3FN, rec, q, qT)), args.reps)
     gavg = sum(g) / 3
     out = {"workload": "square linear 4096^3 (x with 0.1% outliers x50), fwd + bwd with fused "
                        "unscale + update",
+           "transposed_copies": [k for k, v in (("x", xt), ("w", wt), ("gy", gt)) if v],
            "ms_per_step": round(ms, 4), "TFLOPs": round(3 * fl / (ms * 1e-3) / 1e12, 1),
            "gemm_us": [round(v, 2) for v in g],
            "gemm_frac": round(fl / (gavg * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
-           "cast_x_amax_quant_T_us": round(c_us, 2)}
+           "cast_x_amax_quant_us": round(c_us, 2)}
+    # the same step with every transposed copy
+    saved_a, ws_a = F.LinearSaved(M, N, K, device=dev), F.LinearBwdWs(M, N, device=dev)
+
+    def step_all_copies():
+        F.fp8_scaled_linear_fwd(x, w, saved_a, y, F.OUT_BF16)
+        F.fp8_scaled_linear_bwd_unscale(gy, saved_a, ws_a, scale, found, gx, gw)
+        F.amp_update_scale(scale, tracker, found, 2.0, 0.5, 2000)
+
+    ms_a, _, _ = timed_steps(torch, stream, step_all_copies, steps, args.warmup)
+    out["all_copies_ms_per_step"] = round(ms_a, 4)
+    del saved_a, ws_a
     # the same step with delayed scaling of x, W and gy (history of 16)
     hx, hw, hg = (torch.ones(16, dtype=torch.float32, device=dev) for _ in range(3))
 
