@@ -41,6 +41,13 @@ __device__ __forceinline__ void st_stream(void* p, uint2 v) {
 // cached accesses: its inputs were usually just written or read by the
 // previous kernel and are still there, and its outputs are read next.
 constexpr int64_t kStreamBytes = 256ll << 20;
+// A GEMM output of this size or more leaves the kernel with non-temporal
+// stores.  The GEMM is bound by its matrix cores and reads its operands at a
+// small fraction of the memory bandwidth, so its output reaches HBM during
+// the GEMM; stored cached, it would stay in the caches as dirty lines that
+// the next memory-bound kernel, reading other tensors, has to write back
+// first.  A smaller output stays cached for the consumer that reads it next.
+constexpr int64_t kStreamOutBytes = 64ll << 20;
 // An empty use of a loaded value (no instruction): the compiler may not sink
 // the load into a later conditional use, where it would be issued only after
 // the work before that use.

@@ -15,7 +15,8 @@
 // accumulators are four consecutive output columns.  LDS tiles hold 16-byte
 // chunks XOR-swizzled by row so the fragment reads hit distinct banks.
 //   - k_gemm_pingpong: 256 x 256 (or 224 x 256) tiles, for problems with at
-//     least 128 of them (fills the chip).
+//     least 128 of them (fills the chip).  A 16-bit output of kStreamOutBytes
+//     or more is stored non-temporally.
 //   - k_gemm: 128 x 128 tiles with register-staged loads, for smaller problems.
 // Each kernel has a per-tensor epilogue (one alpha) and a row-wise one (RW:
 // inverse-scale vectors along M and N); gemm.hip and gemm_rowwise.hip hold the
@@ -866,15 +867,18 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
     // the staged tile, 16-byte chunks of 8 columns: BM rows x 32 chunks, or
     // under TR 256 rows x BM / 8 chunks (28 at BM = 224)
     constexpr int kChunks = TR ? BM / 8 : BN / 8;
+    auto write_tile = [&](auto nt) {
 #pragma unroll
-    for (int pass = 0; pass < BM / 16; ++pass) {
-      const int id = pass * 512 + (int)threadIdx.x;
-      const int r = id / kChunks, cc = id % kChunks;
-      const uint4 v = *reinterpret_cast<const uint4*>(crow(r) + ((cc ^ (r & 31)) << 4));
-      const int64_t m = row0 + r, n = col0 + 8 * cc;
-      if (m < c_rows && n < c_cols)
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + m * c_cols + n) = v;
-    }
+      for (int pass = 0; pass < BM / 16; ++pass) {
+        const int id = pass * 512 + (int)threadIdx.x;
+        const int r = id / kChunks, cc = id % kChunks;
+        const uint4 v = *reinterpret_cast<const uint4*>(crow(r) + ((cc ^ (r & 31)) << 4));
+        const int64_t m = row0 + r, n = col0 + 8 * cc;
+        if (m < c_rows && n < c_cols) st16<decltype(nt)::value>(reinterpret_cast<uint16_t*>(p.C) + m * c_cols + n, v);
+      }
+    };
+    if (2 * c_rows * c_cols >= kStreamOutBytes) write_tile(std::true_type{});
+    else write_tile(std::false_type{});
   }
 }
 
