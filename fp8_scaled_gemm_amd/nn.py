@@ -119,9 +119,15 @@ def _op_bwd_fake(gy, x_q, x_qT, w_q, w_qT, recs):
 
 def _op_setup(ctx, inputs, output):
     ctx.save_for_backward(*output[1:])
+    # the codes and records are state, not differentiable outputs: without
+    # this, autograd passes the backward a zero-filled "gradient" of each (one
+    # fill kernel per code tensor, up to 117 MB each in the MLP block)
+    ctx.set_materialize_grads(False)
 
 
 def _op_backward(ctx, gy, *_unused):
+    if gy is None:  # y took no part in the loss
+        return None, None
     if gy.dtype != torch.bfloat16:
         raise TypeError(f"Float8Linear expects bf16 output gradients, got {gy.dtype}")
     gx, gw = torch.ops.fp8sg.scaled_linear_bwd(gy.contiguous(), *ctx.saved_tensors)

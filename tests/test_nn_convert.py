@@ -126,3 +126,32 @@ def test_dynamo_captures_the_fp8_linear_as_one_op():
     assert len(graphs) == 1
     targets = [str(n.target) for n in graphs[0].graph.nodes if n.op == "call_function"]
     assert sum("fp8sg.scaled_linear_fwd" in t for t in targets) == 2, targets
+
+
+def test_backward_gets_no_zero_filled_code_gradients():
+    """The dynamic-scaling op returns y plus the codes and records the
+    backward needs.  Those are state, not differentiable outputs: the autograd
+    setup turns off gradient materialization, so the backward receives None
+    for them rather than a zero-filled tensor of each code's size (one fill
+    kernel per tensor, up to 117 MB each in the MLP block).  A backward whose
+    y took no part in the loss returns no gradients.  Host logic only: a
+    recording context stands in for autograd's."""
+    import fp8_scaled_gemm_amd.nn as FN
+
+    class Ctx:
+        def __init__(self):
+            self.saved, self.materialize = None, True
+
+        def save_for_backward(self, *t):
+            self.saved = t
+
+        def set_materialize_grads(self, v):
+            self.materialize = v
+
+    ctx = Ctx()
+    outs = (torch.empty(32, 64, dtype=torch.bfloat16),) + tuple(
+        torch.empty(n, dtype=torch.uint8) for n in (2048, 0, 4096, 0, 8))
+    FN._op_setup(ctx, (None, None), outs)
+    assert ctx.materialize is False
+    assert len(ctx.saved) == 5 and all(a is b for a, b in zip(ctx.saved, outs[1:]))
+    assert FN._op_backward(ctx, None, None, None, None, None, None) == (None, None)
