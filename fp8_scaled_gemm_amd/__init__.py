@@ -438,13 +438,14 @@ class LinearSaved:
 
 class LinearBwdWs:
     """The backward's gradient codes; with transposed=False no transposed copy
-    (the weight-gradient GEMM then reads gy_q contraction-major)."""
+    (the weight-gradient GEMM then reads gy_q contraction-major).  gy_sc: the
+    scale record to use (default: a new zeroed one)."""
 
-    def __init__(self, M, N, device="cuda", transposed=True):
+    def __init__(self, M, N, device="cuda", transposed=True, gy_sc=None):
         u8 = dict(dtype=torch.uint8, device=device)
         self.gy_q = torch.empty((M, N), **u8)
         self.gy_qT = torch.empty((N, M), **u8) if transposed else None
-        self.gy_sc = ScaleRec(device=device)
+        self.gy_sc = gy_sc if gy_sc is not None else ScaleRec(device=device)
 
     def check(self, M, N):
         key = (M, N, id(self.gy_q), id(self.gy_qT), id(self.gy_sc), id(self.gy_sc.buf))

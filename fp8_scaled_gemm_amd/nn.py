@@ -78,7 +78,13 @@ def _op_fwd(x: torch.Tensor, w: torch.Tensor) -> tuple[torch.Tensor, torch.Tenso
     M, K = x.shape
     N = w.shape[0]
     xt, wt, _ = fp8_linear_copies(M, N, K)
-    saved = LinearSaved(M, N, K, device=x.device, x_transposed=xt, w_transposed=wt)
+    u8 = dict(dtype=torch.uint8, device=x.device)
+    # uninitialised records: the forward writes every field the backward reads
+    # (a zero fill would cost one more kernel launch per call)
+    saved = LinearSaved(M, N, K, tensors=(
+        torch.empty((M, K), **u8), torch.empty((K, M), **u8) if xt else None,
+        torch.empty((N, K), **u8), torch.empty((K, N), **u8) if wt else None,
+        torch.empty((2, SCALE_REC_BYTES), **u8)))
     y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     fp8_scaled_linear_fwd(x, w, saved, y, OUT_BF16)
     empty = torch.empty(0, dtype=torch.uint8, device=x.device)
@@ -105,7 +111,9 @@ def _op_bwd(gy: torch.Tensor, x_q: torch.Tensor, x_qT: torch.Tensor, w_q: torch.
     saved = LinearSaved(M, N, K, tensors=(x_q, _present(x_qT), w_q, _present(w_qT), recs))
     gx = torch.empty((M, K), dtype=torch.bfloat16, device=gy.device)
     gw = torch.empty((N, K), dtype=torch.bfloat16, device=gy.device)
-    ws = LinearBwdWs(M, N, device=gy.device, transposed=fp8_linear_copies(M, N, K)[2])
+    # the backward writes gy's record before it reads it: no zero fill needed
+    rec = ScaleRec(buf=torch.empty(SCALE_REC_BYTES, dtype=torch.uint8, device=gy.device))
+    ws = LinearBwdWs(M, N, device=gy.device, transposed=fp8_linear_copies(M, N, K)[2], gy_sc=rec)
     fp8_scaled_linear_bwd(gy, saved, ws, gx, gw, OUT_BF16)
     return gx, gw
 

@@ -345,3 +345,35 @@ def test_fp16_two_layer_model_skips_on_overflow():
     assert scaler.state()[2] == 0
     scaler.update()
     assert any(not torch.equal(a, b) for a, b in zip(before, model.parameters()))
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 128), (512, 768, 1024), (2048, 4096, 14336)])
+def test_linear_records_need_no_initialisation(M, N, K):
+    """The layer's op allocates its scale records without zeroing them: the
+    forward and the backward write every field they read.  The linear entry
+    points with records first filled with 0xFF bytes (NaN and garbage in every
+    field and partial slot) give the same outputs and record fields, bit for
+    bit, as with zeroed records: on the one-launch small path (64 x 256 x 128),
+    the general path, and a size whose backward keeps a transposed copy."""
+    g = torch.Generator(device="cpu").manual_seed(M + N + K)
+    x = (torch.randn(M, K, generator=g)).to(torch.bfloat16).to(DEV)
+    w = (torch.randn(N, K, generator=g) * 0.02).to(torch.bfloat16).to(DEV)
+    gy = (torch.randn(M, N, generator=g) * 1e-4).to(torch.bfloat16).to(DEV)
+    xt, wt, gt = F.fp8_linear_copies(M, N, K)
+    runs = []
+    for fill in (0x00, 0xFF):
+        recs = torch.full((2, F.SCALE_REC_BYTES), fill, dtype=torch.uint8, device=DEV)
+        saved = F.LinearSaved(M, N, K, x_transposed=xt, w_transposed=wt)
+        saved = F.LinearSaved(M, N, K, tensors=(saved.x_q, saved.x_qT, saved.w_q, saved.w_qT, recs))
+        gy_rec = F.ScaleRec(buf=torch.full((F.SCALE_REC_BYTES,), fill, dtype=torch.uint8, device=DEV))
+        ws = F.LinearBwdWs(M, N, transposed=gt, gy_sc=gy_rec)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        gx = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+        gw = torch.empty((N, K), dtype=torch.bfloat16, device=DEV)
+        F.fp8_scaled_linear_fwd(x, w, saved, y, F.OUT_BF16)
+        F.fp8_scaled_linear_bwd(gy, saved, ws, gx, gw, F.OUT_BF16)
+        torch.cuda.synchronize()
+        runs.append([y.view(torch.int16), gx.view(torch.int16), gw.view(torch.int16), saved.x_q,
+                     saved.w_q, ws.gy_q, recs[:, :32], gy_rec.buf[:32]])
+    for k, (a, b) in enumerate(zip(*runs)):
+        assert torch.equal(a, b), (M, N, K, k)
