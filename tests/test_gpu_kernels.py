@@ -252,6 +252,50 @@ def test_gemm_matches_oracle(fa, fb, shape, out):
     check_gemm_values(g, c_ref, absdot, K, OUT_FMT[out], f"{shape} {fa}{fb} out{out}")
 
 
+# 224-row tiles along M; 256 x 256 tiles; 224-row tiles along N with the
+# operands' roles swapped (each with ragged edges)
+@pytest.mark.parametrize("shape", [(8208, 4112, 272), (4112, 14000, 144), (4096, 14320, 144)])
+@pytest.mark.parametrize("unscale", [False, True])
+def test_gemm_streamed_output(shape, unscale):
+    """A 16-bit output of 64 MiB or more leaves the large-tile kernel with
+    non-temporal stores: ragged M and N in each of its three tilings, bf16
+    output and the fp16 output with the fused unscale.  Every output against
+    the oracle, the non-finite flag, and the 64 KiB after C untouched."""
+    from tests.parity import check_unscaled_values
+    M, N, K = shape
+    fa = F.E5M2 if unscale else F.E4M3FN
+    rng = np.random.default_rng(M + 3 * N + 7 * K)
+    A = random_codes(rng, fa, (M, K))
+    B = random_codes(rng, F.E4M3FN, (N, K))
+    inv = np.array([2.0 ** -16 / 3.0, 1.0 / 448.0 * 0.37], np.float64)
+    invd = torch.from_numpy(inv).to(DEV)
+    guard = 32768
+    buf = torch.full((M * N + guard,), 0x5A5A, dtype=torch.int16, device=DEV)
+    if unscale:
+        C = buf[:M * N].view(torch.float16).view(M, N)
+        scale = torch.tensor([65536.0], dtype=torch.float32, device=DEV)
+        found = torch.zeros(1, dtype=torch.int32, device=DEV)
+        F.fp8_gemm_unscale(dev_u8(A), fa, dev_u8(B), F.E4M3FN, invd.data_ptr(), invd.data_ptr() + 8,
+                           scale, found, C)
+    else:
+        C = buf[:M * N].view(torch.bfloat16).view(M, N)
+        F.fp8_gemm(dev_u8(A), fa, dev_u8(B), F.E4M3FN, invd.data_ptr(), invd.data_ptr() + 8, C,
+                   F.OUT_BF16)
+    torch.cuda.synchronize()
+    assert 2 * M * N >= 64 << 20
+    assert bool(torch.all(buf[M * N:] == 0x5A5A)), "stores past C"
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ii, jj = ii.reshape(-1), jj.reshape(-1)
+    c_ref = O.gemm_at(A, fa, B, F.E4M3FN, inv[0], inv[1], ii, jj)
+    absdot = O.gemm_absdot_at(A, fa, B, F.E4M3FN, inv[0], inv[1], ii, jj)
+    bits = buf[:M * N].cpu().numpy().view(np.uint16)
+    if unscale:
+        assert int(found.item()) == 0
+        check_unscaled_values(bits, c_ref, absdot, K, 65536.0, f"{shape} unscaled")
+    else:
+        check_gemm_values(decode_out(O.BF16, bits), c_ref, absdot, K, O.BF16, f"{shape} bf16")
+
+
 @pytest.mark.parametrize("shape", [(32, 48, (1 << 20) + 16), (272, 16, 65536 + 48)])
 def test_gemm_long_contraction(shape):
     """A contraction of a million FP8 products (8,192 k-tiles of 128 plus a
