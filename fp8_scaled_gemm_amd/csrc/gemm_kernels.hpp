@@ -72,6 +72,7 @@ struct Unscale {
   uint32_t mx;
   __device__ Unscale() : inv_s(0.f), mx(0u) {}
   __device__ void load(const GemmProblem& p) { inv_s = 1.0f / *p.amp_scale; }
+  __device__ void set(float amp_scale) { inv_s = 1.0f / amp_scale; }
   // two elements: fp16 pair of fp16(fl32(fp16(c) * inv_s)), as packed bits
   __device__ uint32_t pair(f32x2 c) const {
     typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -156,6 +157,15 @@ struct Alpha {
     }
   }
 };
+
+// The epilogue factor from inverse scales loaded earlier (per-tensor), or
+// from the row-wise vectors in memory (RW).
+template <bool RW, int TM, int TN>
+__device__ __forceinline__ Alpha<RW, TM, TN> epilogue_alpha(const GemmProblem& p, int64_t m0, int64_t n0,
+                                                        int lane, double inv_a, double inv_b) {
+  if constexpr (RW) return Alpha<RW, TM, TN>(p, m0, n0, lane);
+  else return Alpha<RW, TM, TN>(inv_a, inv_b);
+}
 
 // A bf16 operand cast to FP8 on its way into LDS (the small layers' one-launch
 // passes, small_layer.hip): each 16-element chunk is quantized by quant8 at
@@ -605,6 +615,17 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int grp = wave >> 2, wq = wave & 3;
   const int64_t M = p.M, N = p.N, K = p.K;
+  // The epilogue's inputs from memory (per-tensor inverse scales, the loss
+  // scale), loaded before the main loop: loaded after it, every tile's
+  // epilogue waited one memory round trip for them.  Uniform, so they stay
+  // in scalar registers through the loop.
+  double inv_a0 = 0.0, inv_b0 = 0.0;
+  float amp0 = 1.0f;
+  if constexpr (!RW) {
+    inv_a0 = *p.inv_a;
+    inv_b0 = *p.inv_b;
+  }
+  if constexpr (OUT == kOutF16Unscale) amp0 = *p.amp_scale;
   const int nbm = (int)((M + BM - 1) / BM), nbn = (int)((N + BN - 1) / BN);
   int tm, tn;
   tile_of(nbm, nbn, tm, tn);
@@ -807,7 +828,7 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
   if (grp == 0) barrier();
 
   const int wr0 = grp * (BM / 2), wc0 = wq * 64;
-  const Alpha<RW, kTM, kTN> alpha(p, bm + wr0, bn + wc0, lane);
+  const Alpha<RW, kTM, kTN> alpha = epilogue_alpha<RW, kTM, kTN>(p, bm + wr0, bn + wc0, lane, inv_a0, inv_b0);
   // Block (i, j) of this lane, in the C tile: row r, columns col .. col + 3.
   // The C tile is BM x 256 (rows along p.M), or 256 x BM under TR (rows along
   // p.N, which is then the original M); C's rows are c_rows long.
@@ -843,7 +864,7 @@ __global__ __launch_bounds__(512) void k_gemm_pingpong(GemmProblem p) {
       return base + (r & 63) * kRowBytes;
     };
     Unscale us;
-    if constexpr (OUT == kOutF16Unscale) us.load(p);
+    if constexpr (OUT == kOutF16Unscale) us.set(amp0);
     __builtin_amdgcn_s_waitcnt(0);  // no load may still be writing a slot
     barrier();
 #pragma unroll
