@@ -48,8 +48,8 @@ GEMM_SRC = os.path.join(ROOT, "fp8_scaled_gemm_amd", "csrc", "gemm_kernels.hpp")
 # device-to-device copy (bench.py --copy-reference: FETCH_SIZE x2.0,
 # WRITE_SIZE x1.0).  Valid only for the GEMM kernel source they were taken on
 # (its hash); bench.py reports null for any other.
-GEMM_TRAFFIC = {"gemm_src_sha256_16": "b3527ba0a3d450c0", "fetch_kib": 355140.5,
-                "write_kib": 137295.0, "fetch_factor": 2.0, "write_factor": 1.0}
+GEMM_TRAFFIC = {"gemm_src_sha256_16": "3cb9b645dee0b52f", "fetch_kib": 355144.4,
+                "write_kib": 137377.3, "fetch_factor": 2.0, "write_factor": 1.0}
 
 
 def parse():
